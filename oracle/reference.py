@@ -1,0 +1,419 @@
+"""Plain numpy oracle of the prefill-only decision path (test infrastructure).
+
+Every function states the passage of the pages it follows.  Page names used:
+  [omni-readme]  System1-Omni README
+  [rfc114]       RFC #114, "Native Rust/CUDA support for OmniJev-4B v1.1"
+  [rfc114-plan]  RFC #114, comment "Plan: native OmniJev-4B v1.1"
+  [sys1rust]     sys1rust README
+  [cua-issue]    "[New Model]: Support Cua-S1 4B 0.2", issue #10
+Readings taken where the pages are silent (tags used below):
+  (R1)  linear attention is the stated stand-in S_t = g_t S_{t-1} + k_t v_t^T,
+        o_t = S_t^T q_t: update first, then read, so o_t sees token t.  No
+        feature map, q/k norm, 1/sqrt(dk), short conv, delta rule or output
+        gate (the pages name Gated DeltaNet but print no equations).
+  (R2)  one decay gate per (token, head): g = sigmoid(u . w_g[h]), no bias.
+  (R3)  the state is zero at a sequence start; a branch starts from its
+        prefix's final state ([rfc114] section 5).
+  (R4)  layer l is full attention iff l % full_every == full_every - 1
+        (3 linear then 1 full; the tiny shape alternates).
+  (R5)  packed sequences are independent.
+  (R6)  pre-norm residual blocks, RMSNorm before the mixer and the FFN, one
+        final RMSNorm before the readout.
+  (R7)  RMSNorm eps 1e-6 everywhere, gains initialised to one.
+  (R8)  grouped-query attention with contiguous groups, scale 1/sqrt(hd),
+        causal mask including the diagonal, no biases.
+  (R9)  rotate-half RoPE over the whole head dim, base 10000; positions
+        restart at 0 per sequence; branch token j sits at position P + j.
+  (R10) SwiGLU FFN, no biases anywhere.
+  (R11) choice ties go to the lowest option index.
+  (R12) score levels are numbered 0..K-1 in caller order.
+  (R13) noul options are ordered [yes, no].
+  (R14) the readout softmax runs over the question's K option logits only, no
+        temperature or bias.
+  (R15) LoRA targets: q, k, v, o of both mixer kinds (+ FFN gate, up, down on
+        the 4B/27B shapes); the decay-gate projection is not adapted.
+"""
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL = 0, 1, 2
+
+
+# --------------------------------------------------------------------------
+# storage formats
+# --------------------------------------------------------------------------
+def bf16_bits_to_float(bits, dtype=np.float64):
+    """Decode bfloat16 bit patterns (uint16): a bf16 value is the top half of
+    the float32 with the same sign, exponent and leading mantissa bits."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(dtype, copy=False)
+
+
+def round_to_bf16_bits(x):
+    """Round float64 values to bfloat16, to nearest with ties to even, in one
+    step (no intermediate float32 rounding).  A float64 keeps 52 explicit
+    mantissa bits and a bf16 keeps 7, so 45 low bits are rounded away on the
+    float64 bit pattern; the 8-significant-bit result is exactly a float32,
+    whose top 16 bits are the bf16 pattern.  Inputs are finite and inside the
+    float32 normal range."""
+    u = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    u = ((u + lsb + np.uint64((1 << 44) - 1)) >> np.uint64(45)) << np.uint64(45)
+    f32 = u.view(np.float64).astype(np.float32)
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# building blocks
+# --------------------------------------------------------------------------
+def rms_norm(x, w, eps):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * w.  (R6, R7):
+    the pages name Qwen3.5-family backbones ([omni-readme], directory table;
+    [cua-issue], model request), whose blocks are pre-norm with RMSNorm."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def rope_rotate_half(a, pos, base):
+    """Rotary position embedding, rotate-half pairing (R9): for i < hd/2 the
+    pair (a_i, a_{i+hd/2}) is rotated by angle pos * base^(-2i/hd).
+    a: [T, H, hd]; pos: [T] integer positions.  Angles are formed in float64."""
+    T, H, hd = a.shape
+    half = hd // 2
+    inv = base ** (-2.0 * np.arange(half, dtype=np.float64) / hd)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+    c = np.cos(ang).astype(a.dtype)[:, None, :]
+    s = np.sin(ang).astype(a.dtype)[:, None, :]
+    a1, a2 = a[..., :half], a[..., half:]
+    return np.concatenate([a1 * c - a2 * s, a2 * c + a1 * s], axis=-1)
+
+
+def la_scan_recurrent(q, k, v, g, S0=None):
+    """Gated linear attention, the recurrence itself, one token at a time:
+        S_t = g_t * S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t
+    per head, with S a [dk, dv] state and g_t a scalar per (token, head) (R1,
+    R2).  The state is float64 here, at least the fp32 the pages require for
+    the recurrent state ([rfc114] section 5).  S0 is the initial state (zero
+    at a sequence start, the prefix's final state for a branch).
+    q, k: [T, H, dk]; v: [T, H, dv]; g: [T, H].  Returns (o [T, H, dv], S_T)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    S = np.zeros((H, dk, dv), dtype=q.dtype) if S0 is None else np.array(S0, dtype=q.dtype)
+    o = np.zeros((T, H, dv), dtype=q.dtype)
+    for t in range(T):
+        S = g[t][:, None, None] * S + k[t][:, :, None] * v[t][:, None, :]
+        o[t] = np.einsum("hkv,hk->hv", S, q[t])
+    return o, S
+
+
+def la_scan_unrolled(q, k, v, g, S0=None):
+    """The same recurrence in closed form (unrolled), computed with matmuls:
+        o_t = sum_{s<=t} exp(G_t - G_s) (q_t . k_s) v_s + exp(G_t) S0^T q_t
+        S_T = sum_s exp(G_{T-1} - G_s) k_s v_s^T + exp(G_{T-1}) S0
+    with G_t = sum_{r<=t} log g_r.  Decays are formed as exp of a difference,
+    never as a ratio of products (products of many gates underflow).  G and the
+    decay factors are formed in float64 in every mode.  Exact reformulation of
+    la_scan_recurrent; the tests check one against the other."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = q.dtype
+    S_init = np.zeros((H, dk, dv), dtype=dt) if S0 is None else np.asarray(S0, dtype=dt)
+    o = np.zeros((T, H, dv), dtype=dt)
+    S_fin = np.array(S_init, copy=True)
+    if T == 0:
+        return o, S_fin
+    # a gate of exactly 0 is clamped to 1e-300 so that every log is finite;
+    # the decays it produces are below 1e-300 and vanish in the sums.
+    G = np.cumsum(np.log(np.maximum(np.asarray(g, dtype=np.float64), 1e-300)), axis=0)
+    tri = np.tril(np.ones((T, T), dtype=bool))
+    for h in range(H):
+        Gh = G[:, h]
+        D = np.where(tri, np.exp(np.minimum(Gh[:, None] - Gh[None, :], 0.0)), 0.0)
+        A = (q[:, h, :] @ k[:, h, :].T) * D.astype(dt)
+        o[:, h, :] = A @ v[:, h, :] + np.exp(Gh).astype(dt)[:, None] * (q[:, h, :] @ S_init[h])
+        w_last = np.exp(Gh[-1] - Gh).astype(dt)                          # [T]
+        S_fin[h] = (k[:, h, :] * w_last[:, None]).T @ v[:, h, :] + np.exp(Gh[-1]).astype(dt) * S_init[h]
+    return o, S_fin
+
+
+def causal_attention(q, k, v, q_pos, k_pos):
+    """Causal softmax attention, the definition: for query head h with kv head
+    h // (Hq / Hkv) (grouped, contiguous groups, R8),
+        o_t = sum_{s : pos_s <= pos_t} softmax_s(q_t . k_s / sqrt(hd)) v_s.
+    The diagonal is included.  q: [Tq, Hq, hd]; k, v: [Tk, Hkv, hd]."""
+    Tq, Hq, hd = q.shape
+    Hkv = k.shape[1]
+    grp = Hq // Hkv
+    o = np.zeros((Tq, Hq, v.shape[2]), dtype=q.dtype)
+    if Tq == 0:
+        return o
+    mask = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+    scale = 1.0 / math.sqrt(hd)
+    for h in range(Hq):
+        kv = h // grp
+        s = (q[:, h, :] @ k[:, kv, :].T) * scale
+        s = np.where(mask, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        o[:, h, :] = p @ v[:, kv, :]
+    return o
+
+
+def swiglu(u, w_gate, w_up, w_down):
+    """SwiGLU FFN (R10): down( silu(u W_gate^T) * (u W_up^T) ), silu(a) = a sigmoid(a)."""
+    a = u @ w_gate.T
+    b = u @ w_up.T
+    return (a * sigmoid(a) * b) @ w_down.T
+
+
+def lora_merge(w, a, b, alpha, rank):
+    """Merged LoRA weight W' = W + (alpha / r) B A ([rfc114] section 3 asks for
+    the merge at load; [cua-issue] first plan comment: merged at load).
+    w: [out, in]; a: [r, in]; b: [out, r]."""
+    return w + (alpha / rank) * (b @ a)
+
+
+def softmax(z):
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def decision_fields(p, qtype):
+    """Answer fields from option probabilities p (caller order), after
+    [sys1rust] "Try it": choice is the most likely option (lowest index on an
+    exact tie, R11); score is the expected level, levels numbered 0..K-1 in
+    caller order (R12), so it can fall between levels; noul is P(yes) with
+    options ordered [yes, no]; answer_confidence is the largest probability;
+    for choice and score, confidence is 1 minus the normalised entropy
+    (0 for an even split, 1 for a one-hot); for noul, confidence equals
+    answer_confidence.  entropy_confidence = 1 - H(p)/ln K for every type.
+    0 ln 0 is taken as 0."""
+    p = np.asarray(p, dtype=np.float64)
+    K = len(p)
+    choice = int(np.argmax(p))
+    score = float(np.dot(np.arange(K, dtype=np.float64), p))
+    noul = float(p[0])
+    ans = float(p.max())
+    nz = p[p > 0]
+    H = float(-(nz * np.log(nz)).sum())
+    ent = float(min(1.0, max(0.0, 1.0 - H / math.log(K))))
+    conf = ans if qtype == QTYPE_NOUL else ent
+    return {"choice": choice, "score": score, "noul": noul,
+            "answer_confidence": ans, "confidence": conf,
+            "entropy_confidence": ent}
+
+
+def readout(h_row, w_final, e_rows, eps, qtype):
+    """Decision readout of one question: final RMSNorm of the marker row,
+    option logits z_k = h . E[opt_k] against the tied embedding rows, softmax
+    over the K option logits only ([cua-issue] first plan comment: one forward
+    pass and a softmax over the answer-letter logits; [rfc114-plan]: the head
+    stays bf16 and is cast to fp32 before the softmax -- here the whole
+    readout runs in the oracle's float type).  Returns (p, fields)."""
+    h = rms_norm(h_row[None, :], w_final, eps)[0]
+    z = e_rows @ h
+    p = softmax(z)
+    return p, decision_fields(p, qtype)
+
+
+# --------------------------------------------------------------------------
+# the hybrid decoder
+# --------------------------------------------------------------------------
+class OracleModel:
+    """Hybrid decoder with merged LoRA, evaluated in `dtype` (float64 default).
+
+    Weights arrive as the generator's raw tensors: bf16 bit patterns (uint16)
+    or float32.  For a bf16 model each LoRA target is merged in float64 and
+    rounded once to bf16, the merged storage the pages describe ([rfc114]
+    section 1: adapter merged into BF16 weights); for an fp32 model the merge
+    is kept exact.  With lora="unmerged" the adapter is applied at run time as
+    W x + (alpha/r) B (A x) on the unrounded base (the comparison [rfc114]
+    section 3 asks for).  Weights are decoded to `dtype` at each use unless
+    keep_decoded=True."""
+
+    def __init__(self, shape, tensors, dtype=np.float64, lora="merged",
+                 keep_decoded=False, threads=0):
+        self.s = shape
+        self.dtype = np.dtype(dtype)
+        self.lora = lora
+        self.bf16 = shape.dtype == "bf16"
+        self.keep = keep_decoded
+        self._raw = tensors
+        self._store = {}
+        self._dec = {}
+        self.scale = shape.lora_alpha / shape.lora_rank
+        targets = [n[:-len(".lora_A")] for n in tensors if n.endswith(".lora_A")]
+        if lora == "merged":
+            def job(name):
+                self._store[name] = self._merge(name)
+            if threads <= 0:
+                threads = 8
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(job, targets))
+        self.targets = set(targets)
+
+    # -- weights ---------------------------------------------------------
+    def _to_float(self, raw, dtype=None):
+        dtype = dtype or self.dtype
+        if raw.dtype == np.uint16:
+            return bf16_bits_to_float(raw, dtype)
+        return raw.astype(dtype, copy=False)
+
+    def _merge(self, name):
+        w = self._to_float(self._raw[name], np.float64)
+        a = self._to_float(self._raw[name + ".lora_A"], np.float64)
+        b = self._to_float(self._raw[name + ".lora_B"], np.float64)
+        m = lora_merge(w, a, b, self.s.lora_alpha, self.s.lora_rank)
+        return round_to_bf16_bits(m) if self.bf16 else m
+
+    def merged_storage(self, name):
+        """The merged weight as stored (bf16 bits or float64)."""
+        return self._store.get(name, self._raw[name])
+
+    def W(self, name):
+        if name in self._dec:
+            return self._dec[name]
+        w = self._to_float(self._store[name] if name in self._store else self._raw[name])
+        if self.keep:
+            self._dec[name] = w
+        return w
+
+    def proj(self, name, u):
+        """u W^T, with the LoRA term added at run time in unmerged mode."""
+        y = u @ self.W(name).T
+        if self.lora == "unmerged" and name in self.targets:
+            a = self._to_float(self._raw[name + ".lora_A"])
+            b = self._to_float(self._raw[name + ".lora_B"])
+            y = y + self.scale * ((u @ a.T) @ b.T)
+        return y
+
+    def embed(self, ids):
+        return self._to_float(self._raw["embed"][np.asarray(ids)])
+
+    # -- mixers ----------------------------------------------------------
+    def _linear(self, l, u, S0):
+        s = self.s
+        T = u.shape[0]
+        p = f"layers.{l}.la"
+        q = self.proj(p + ".q", u).reshape(T, s.la_heads, s.la_dk)
+        k = self.proj(p + ".k", u).reshape(T, s.la_heads, s.la_dk)
+        v = self.proj(p + ".v", u).reshape(T, s.la_heads, s.la_dv)
+        g = sigmoid(self.proj(p + ".g", u))           # (R2) one gate per head
+        o, S = la_scan_unrolled(q, k, v, g, S0)
+        return self.proj(p + ".o", o.reshape(T, s.la_heads * s.la_dv)), S
+
+    def _full(self, l, u, pos, prefix):
+        s = self.s
+        T = u.shape[0]
+        p = f"layers.{l}.fa"
+        q = rope_rotate_half(self.proj(p + ".q", u).reshape(T, s.fa_q_heads, s.fa_head_dim),
+                             pos, s.rope_base)
+        k = rope_rotate_half(self.proj(p + ".k", u).reshape(T, s.fa_kv_heads, s.fa_head_dim),
+                             pos, s.rope_base)
+        v = self.proj(p + ".v", u).reshape(T, s.fa_kv_heads, s.fa_head_dim)
+        if prefix is not None:
+            pk, pv, ppos = prefix
+            k = np.concatenate([pk, k], axis=0)
+            v = np.concatenate([pv, v], axis=0)
+            kpos = np.concatenate([ppos, pos])
+        else:
+            kpos = pos
+        o = causal_attention(q, k, v, pos, kpos)
+        return self.proj(p + ".o", o.reshape(T, s.fa_q_heads * s.fa_head_dim)), (k, v, kpos)
+
+    # -- forward ---------------------------------------------------------
+    def forward(self, ids, start_pos=0, cache=None, want_cache=False, capture_rows=None):
+        """Forward over one sequence.  Returns (x_final [T, d], hidden, cache):
+        hidden[l] = residual stream after the embedding (l = 0) and after
+        layer l (l >= 1) at capture_rows (all rows if None); cache holds each
+        linear layer's final state and each full layer's keys/values, so that
+        a continuation can start from it ([rfc114] section 5: snapshot of the
+        full-attention KV and the recurrent state; every branch starts from
+        the same snapshot)."""
+        s = self.s
+        T = len(ids)
+        pos = start_pos + np.arange(T, dtype=np.int64)
+        x = self.embed(ids)
+        rows = slice(None) if capture_rows is None else np.asarray(capture_rows)
+        hidden = [x[rows].copy()]
+        out_cache = {"la": {}, "fa": {}, "len": start_pos + T}
+        for l in range(s.n_layers):
+            u = rms_norm(x, self.W(f"layers.{l}.attn_norm"), s.rms_eps)
+            if s.is_full(l):
+                prefix = None if cache is None else cache["fa"][l]
+                m, kv = self._full(l, u, pos, prefix)
+                if want_cache:
+                    out_cache["fa"][l] = kv
+            else:
+                S0 = None if cache is None else cache["la"][l]
+                m, S = self._linear(l, u, S0)
+                if want_cache:
+                    out_cache["la"][l] = S
+            y = x + m
+            v = rms_norm(y, self.W(f"layers.{l}.ffn_norm"), s.rms_eps)
+            f = f"layers.{l}.ffn"
+            x = y + self._ffn(f, v)
+            hidden.append(x[rows].copy())
+        return x, hidden, (out_cache if want_cache else None)
+
+    def _ffn(self, f, v):
+        a = self.proj(f + ".gate", v)
+        b = self.proj(f + ".up", v)
+        return self.proj(f + ".down", a * sigmoid(a) * b)
+
+    def decide(self, x_row, qtype, option_ids):
+        e = self.embed(option_ids)
+        return readout(x_row, self.W("final_norm"), e, self.s.rms_eps, qtype)
+
+
+def prefill_decide(model, batch, mode="plain", capture=None, seqs=None):
+    """Answer every question of `batch` (an s1_workloads.Batch).
+
+    Sequences are independent (R5: nothing crosses a sequence boundary).  A
+    branch (prefix_of[i] >= 0) is, by definition, the plain forward over
+    prefix + suffix restricted to its suffix rows (mode="plain");
+    mode="continuation" runs each prefix once and continues every branch from
+    its cache, which [rfc114-plan] states equals the plain forward up to
+    rounding (checked by the tests).  capture maps a sequence index to rows
+    (within that sequence) whose residual stream is returned per layer.
+    seqs restricts the work to the listed sequences (questions elsewhere are
+    skipped).  Returns {"probs": {j: p}, "fields": {j: dict},
+    "hidden": {i: [n_layers + 1, rows, d]}}."""
+    capture = capture or {}
+    todo = range(batch.n_seqs) if seqs is None else seqs
+    probs, fields, hidden = {}, {}, {}
+    prefix_cache = {}
+    for i in todo:
+        ids = batch.tokens_of(i)
+        pidx = int(batch.prefix_of[i])
+        rows = capture.get(i)
+        if pidx < 0:
+            x, hid, _ = model.forward(ids, capture_rows=rows)
+        elif mode == "plain":
+            pids = batch.tokens_of(pidx)
+            P = len(pids)
+            full_rows = None if rows is None else P + np.asarray(rows)
+            if full_rows is None:
+                full_rows = P + np.arange(len(ids))
+            x, hid, _ = model.forward(np.concatenate([pids, ids]), capture_rows=full_rows)
+            x = x[P:]
+        else:
+            if pidx not in prefix_cache:
+                _, _, prefix_cache[pidx] = model.forward(batch.tokens_of(pidx), want_cache=True)
+            c = prefix_cache[pidx]
+            x, hid, _ = model.forward(ids, start_pos=c["len"], cache=c, capture_rows=rows)
+        if i in capture:
+            hidden[i] = np.stack(hid)
+        for j in np.nonzero(batch.q_seq == i)[0]:
+            p, f = model.decide(x[batch.q_marker[j]], int(batch.q_type[j]), batch.options_of(j))
+            probs[int(j)] = p
+            fields[int(j)] = f
+    return {"probs": probs, "fields": fields, "hidden": hidden}

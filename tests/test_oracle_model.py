@@ -1,0 +1,220 @@
+"""Whole-model checks of the CPU oracle on the tiny fp32 shape (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from s1_workloads import make_weights, make_batch, shape_of
+from s1_workloads.batch import random_batch
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    shape = shape_of("tiny-fp32")
+    return shape, make_weights(shape)
+
+
+def test_generator_is_thread_count_independent(tiny):
+    shape, w = tiny
+    w1 = make_weights(shape, threads=1)
+    for n in w.tensors:
+        assert np.array_equal(w.tensors[n], w1.tensors[n]), n
+
+
+def test_workload_batches_are_valid():
+    for name in ("tiny-fp32", "4b-single-512", "4b-varlen-16", "4b-branch-4096x20",
+                 "27b-single-1024"):
+        b = make_batch(name)
+        V = shape_of(name).vocab
+        lens = b.seq_lens
+        assert (b.token_ids >= 0).all() and (b.token_ids < V).all()
+        for j in range(b.n_questions):
+            i = b.q_seq[j]
+            assert 0 <= b.q_marker[j] < lens[i]
+            opts = b.options_of(j)
+            assert len(set(opts.tolist())) == len(opts) >= 2
+            if b.q_type[j] == O.QTYPE_NOUL:
+                assert len(opts) == 2
+    b = make_batch("4b-branch-4096x20")
+    assert b.n_tokens == 4096 + 20 * 64 and (b.prefix_of[1:] == 0).all()
+    b = make_batch("4b-varlen-16")
+    assert b.n_seqs == 16 and (b.seq_lens >= 256).all() and (b.seq_lens <= 2048).all()
+
+
+def _torch_forward(shape, tensors, ids):
+    """An independent formulation of the tiny hybrid in PyTorch CPU ops
+    (F.linear, F.rms_norm, F.scaled_dot_product_attention, a step loop for
+    the recurrence, complex-number RoPE), float64, with LoRA applied unmerged."""
+    F = torch.nn.functional
+    t = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in tensors.items()}
+    s = shape
+    sc = s.lora_alpha / s.lora_rank
+
+    def lin(name, x):
+        y = F.linear(x, t[name])
+        if name + ".lora_A" in t:
+            y = y + sc * F.linear(F.linear(x, t[name + ".lora_A"]), t[name + ".lora_B"])
+        return y
+
+    def rope(a, pos):
+        hd = a.shape[-1]
+        half = hd // 2
+        z = torch.complex(a[..., :half], a[..., half:])
+        th = torch.tensor([s.rope_base ** (-(2 * i) / hd) for i in range(half)], dtype=torch.float64)
+        z = z * torch.polar(torch.ones_like(th), pos[:, None, None].double() * th)
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    T = len(ids)
+    x = t["embed"][torch.from_numpy(ids.astype(np.int64))]
+    pos = torch.arange(T)
+    for l in range(s.n_layers):
+        u = F.rms_norm(x, (s.d_model,), t[f"layers.{l}.attn_norm"], eps=s.rms_eps)
+        if s.is_full(l):
+            p = f"layers.{l}.fa"
+            q = rope(lin(p + ".q", u).view(T, s.fa_q_heads, -1), pos)
+            k = rope(lin(p + ".k", u).view(T, s.fa_kv_heads, -1), pos)
+            v = lin(p + ".v", u).view(T, s.fa_kv_heads, -1)
+            rep = s.fa_q_heads // s.fa_kv_heads
+            k, v = k.repeat_interleave(rep, 1), v.repeat_interleave(rep, 1)
+            o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1),
+                                               v.transpose(0, 1), is_causal=True)
+            m = lin(p + ".o", o.transpose(0, 1).reshape(T, -1))
+        else:
+            p = f"layers.{l}.la"
+            q = lin(p + ".q", u).view(T, s.la_heads, -1)
+            k = lin(p + ".k", u).view(T, s.la_heads, -1)
+            v = lin(p + ".v", u).view(T, s.la_heads, -1)
+            g = torch.sigmoid(lin(p + ".g", u))
+            S = torch.zeros(s.la_heads, s.la_dk, s.la_dv, dtype=torch.float64)
+            outs = []
+            for i in range(T):
+                S = g[i][:, None, None] * S + torch.einsum("hk,hv->hkv", k[i], v[i])
+                outs.append(torch.einsum("hkv,hk->hv", S, q[i]))
+            m = lin(p + ".o", torch.stack(outs).reshape(T, -1))
+        y = x + m
+        w = F.rms_norm(y, (s.d_model,), t[f"layers.{l}.ffn_norm"], eps=s.rms_eps)
+        f = f"layers.{l}.ffn"
+        x = y + lin(f + ".down", F.silu(lin(f + ".gate", w)) * lin(f + ".up", w))
+    return x.numpy()
+
+
+def test_oracle_forward_matches_independent_torch_formulation(tiny):
+    shape, w = tiny
+    b = make_batch("tiny-fp32")
+    ids = b.tokens_of(0)
+    m = O.OracleModel(shape, w.tensors)
+    x, hid, _ = m.forward(ids)
+    ref = _torch_forward(shape, w.tensors, ids)
+    np.testing.assert_allclose(x, ref, rtol=1e-9, atol=1e-10)
+
+
+def test_float32_mode_agrees_with_float64(tiny):
+    shape, w = tiny
+    b = make_batch("tiny-fp32")
+    r64 = O.prefill_decide(O.OracleModel(shape, w.tensors), b, capture={0: np.arange(128)})
+    r32 = O.prefill_decide(O.OracleModel(shape, w.tensors, dtype=np.float32), b,
+                           capture={0: np.arange(128)})
+    h64, h32 = r64["hidden"][0], r32["hidden"][0]
+    for l in range(h64.shape[0]):
+        assert np.linalg.norm(h32[l] - h64[l]) / np.linalg.norm(h64[l]) < 1e-5
+    for j in r64["probs"]:
+        assert np.abs(r32["probs"][j] - r64["probs"][j]).max() < 1e-5
+
+
+def test_merged_equals_unmerged_for_fp32_storage(tiny):
+    shape, w = tiny
+    b = make_batch("tiny-fp32")
+    a = O.prefill_decide(O.OracleModel(shape, w.tensors), b)
+    u = O.prefill_decide(O.OracleModel(shape, w.tensors, lora="unmerged"), b)
+    for j in a["probs"]:
+        np.testing.assert_allclose(a["probs"][j], u["probs"][j], rtol=1e-10, atol=1e-12)
+
+
+def test_branch_continuation_equals_plain_forward(tiny):
+    shape, w = tiny
+    # prefix 100 (not a multiple of 64) + 3 branches of 13, 64, 1 tokens
+    b = random_batch(shape.vocab, [100, 13, 64, 1], seed=7, prefix_of=[-1, 0, 0, 0])
+    m = O.OracleModel(shape, w.tensors)
+    cap = {1: np.arange(13), 2: np.arange(64)}
+    plain = O.prefill_decide(m, b, mode="plain", capture=cap)
+    cont = O.prefill_decide(m, b, mode="continuation", capture=cap)
+    for i in cap:
+        np.testing.assert_allclose(cont["hidden"][i], plain["hidden"][i], rtol=1e-9, atol=1e-10)
+    for j in plain["probs"]:
+        np.testing.assert_allclose(cont["probs"][j], plain["probs"][j], rtol=1e-9, atol=1e-12)
+
+
+def test_varlen_equals_each_request_alone(tiny):
+    shape, w = tiny
+    b = random_batch(shape.vocab, [40, 1, 77], seed=3)
+    m = O.OracleModel(shape, w.tensors)
+    together = O.prefill_decide(m, b)
+    for i in range(3):
+        x, _, _ = m.forward(b.tokens_of(i))
+        for j in np.nonzero(b.q_seq == i)[0]:
+            p, _ = m.decide(x[b.q_marker[j]], int(b.q_type[j]), b.options_of(j))
+            np.testing.assert_array_equal(p, together["probs"][int(j)])
+
+
+def test_bf16_merge_effect_is_small():
+    """The merged-bf16 model against the unmerged adapter on unrounded base
+    weights (the qualification asked for in RFC #114, section 3), on a
+    reduced-depth bf16 shape so that it runs in seconds on the CPU."""
+    from dataclasses import replace
+    shape = replace(shape_of("4b-single-512"), name="bf16-mini", n_layers=4, d_model=256,
+                    ffn=512, vocab=2048, la_heads=2, fa_q_heads=2, fa_kv_heads=1, shape_id=77)
+    w = make_weights(shape)
+    b = random_batch(shape.vocab, [96], seed=11, questions_per_seq=[4])
+    a = O.prefill_decide(O.OracleModel(shape, w.tensors), b)
+    u = O.prefill_decide(O.OracleModel(shape, w.tensors, lora="unmerged"), b)
+    worst = max(np.abs(a["probs"][j] - u["probs"][j]).max() for j in a["probs"])
+    assert worst < 0.05
+
+
+# ------------------------------------------------ planted mistakes (CPU only)
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Each mutation of the oracle makes at least one pin fail."""
+    import tests.test_oracle_pins as P
+
+    def fails(fn, *args):
+        try:
+            fn(*args)
+        except AssertionError:
+            return True
+        return False
+
+    real_rope = O.rope_rotate_half
+    def rope_wrong_sign(a, pos, base):           # rotation in the wrong direction
+        return real_rope(a, -np.asarray(pos), base)
+    monkeypatch.setattr(O, "rope_rotate_half", rope_wrong_sign)
+    monkeypatch.setattr(P.O, "rope_rotate_half", rope_wrong_sign)
+    assert fails(P.test_rope_equals_complex_rotation)
+    monkeypatch.undo()
+
+    real_scan = O.la_scan_recurrent
+    def scan_no_diagonal(q, k, v, g, S0=None):   # o_t reads S_{t-1} instead of S_t
+        o, S = real_scan(q, k, v, g, S0)
+        o2 = np.zeros_like(o)
+        o2[1:] = o[:-1]
+        return o2, S
+    monkeypatch.setattr(P.O, "la_scan_recurrent", scan_no_diagonal)
+    assert fails(P.test_scan_gate_one_is_causal_linear_attention, scan_no_diagonal)
+    monkeypatch.undo()
+
+    real_attn = O.causal_attention
+    def attn_no_scale(q, k, v, qp, kp):          # forgets 1/sqrt(hd)
+        return real_attn(q * math.sqrt(q.shape[-1]), k, v, qp, kp)
+    monkeypatch.setattr(P.O, "causal_attention", attn_no_scale)
+    assert fails(P.test_attention_matches_torch_sdpa)
+    monkeypatch.undo()
+
+    real_fields = O.decision_fields
+    def fields_unnormalised(p, qtype):            # entropy not divided by ln K
+        f = real_fields(p, qtype)
+        if qtype != O.QTYPE_NOUL:
+            f["confidence"] = 1.0 - (1.0 - f["confidence"]) * math.log(len(p))
+        return f
+    monkeypatch.setattr(P.O, "decision_fields", fields_unnormalised)
+    assert fails(P.test_readout_golden_special_cases)
