@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Prefill throughput of the decision path on one MI355X.
+
+A step is one whole prefill-and-decide of the workload's request (embedding,
+every layer, readout) through the library's resident-input plan: token ids
+and metadata already sit in device memory when the timed region starts.
+Prints one JSON line with the throughput (prefill tokens/s), ms per request,
+the dominant kernel's roofline fraction (HIP events recorded by the library
+on the launch stream) and the CPU oracle's throughput on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s and ms/request, 4B-shape hybrid bf16 on 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def requests_in(batch):
+    """A request is a sequence that is not a prefix of another sequence: a
+    prefix and its branches form one request."""
+    import numpy as np
+    prefixes = set(int(p) for p in batch.prefix_of if p >= 0)
+    return sum(1 for i in range(batch.n_seqs) if batch.prefix_of[i] < 0 and i not in prefixes) + len(prefixes)
+
+
+def gemm_flops(shape, T):
+    """Algorithmic flops of each projection GEMM family for T tokens."""
+    d, F = shape.d_model, shape.ffn
+    H, dk, dv = shape.la_heads, shape.la_dk, shape.la_dv
+    Hq, Hkv, hd = shape.fa_q_heads, shape.fa_kv_heads, shape.fa_head_dim
+    return {
+        "gemm_la_in": 2 * T * d * (2 * H * dk + H * dv + H),
+        "gemm_fa_qkv": 2 * T * d * (Hq + 2 * Hkv) * hd,
+        "gemm_o": None,  # mixed K (linear and full layers); not used for the roofline
+        "gemm_gate_up": 2 * T * d * 2 * F,
+        "gemm_down": 2 * T * F * d,
+    }
+
+
+def cpu_baseline(shape, weights, batch, budget_s=30.0):
+    """Time the CPU oracle (float32 mode) on a bounded sample of the request:
+    the first sequence's prefill over as many whole layers as fit the budget,
+    scaled to all layers."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    om = oracle.OracleModel(shape, weights.tensors, dtype=np.float32)
+    ids = batch.tokens_of(0)
+    # time the first n layers, doubling n while the budget allows
+    n_done, t_used, n = 0, 0.0, 1
+    while True:
+        t0 = time.time()
+        om.forward(ids, n_layers=n)
+        n_done, t_used = n, time.time() - t0
+        if n == shape.n_layers or t_used * 2.2 > budget_s:
+            break
+        n = min(shape.n_layers, 2 * n)
+    per_layer = t_used / n_done
+    full = per_layer * shape.n_layers
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": len(ids) / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float32 oracle forward of the {len(ids)}-token request over {n_done} of "
+                      f"{shape.n_layers} layers ({t_used:.1f} s), scaled to all layers; "
+                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="4b-single-512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the decision path has no "
+              "multi-GPU code; see the sharding notes in the design document.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import prefill_only_decision_amd as s1
+    from s1_workloads import make_batch, make_weights, shape_of
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    shape = shape_of(args.workload)
+    batch = make_batch(args.workload)
+    t0 = time.time()
+    w = make_weights(shape)
+    t_gen = time.time() - t0
+    T = batch.n_tokens
+    cfg = s1.make_config(shape, max_tokens=max(T, 1024), max_seqs=max(batch.n_seqs, 4),
+                         max_questions=max(batch.n_questions, 16), max_options=256, max_prefixes=4,
+                         max_positions=max(int(batch.seq_lens.max()) * 2, 8192))
+    t0 = time.time()
+    model = s1.Model(cfg, w.tensors, stream=stream)
+    t_load = time.time() - t0
+    plan = model.plan(batch)
+    dp = torch.zeros(max(plan.n_options, 1), dtype=torch.float32, device="cuda")
+    dd = torch.zeros((max(plan.n_questions, 1), 6), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens = plan.tokens
+    value = tokens / (ms_step / 1e3)
+    reqs = requests_in(batch)
+
+    # per-kernel durations: events recorded by the library after each launch
+    prof = {}
+    for _ in range(max(1, args.profile_steps)):
+        for k, (n, us) in plan.profile(dp.data_ptr(), dd.data_ptr(), sp).items():
+            a, b = prof.get(k, (0, 0.0))
+            prof[k] = (a + n, b + us)
+    steps_p = max(1, args.profile_steps)
+    flops = gemm_flops(shape, tokens)
+    launches, total_us = prof["gemm_gate_up"]
+    avg_us = total_us / launches
+    achieved = flops["gemm_gate_up"] / (avg_us * 1e-6) / 1e12
+    kernels = {k: {"launches_per_step": n // steps_p, "us_per_step": round(us / steps_p, 1),
+                   "us_per_launch": round(us / n, 2)} for k, (n, us) in sorted(prof.items())}
+    gemm_us = sum(prof[k][1] for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+                  if k in prof) / steps_p
+    all_gemm_flops = 2 * tokens * shape.linear_params()
+    roofline = {"bound": "mfma", "kernel": "gemm_gate_up (bf16 MFMA GEMM + SwiGLU epilogue)",
+                "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops["gemm_gate_up"], "us_per_launch": round(avg_us, 2),
+                "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_request": round(ms_step / reqs, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens_per_step": int(tokens), "requests_per_step": reqs,
+                   "questions_per_step": int(batch.n_questions), "layers": shape.n_layers,
+                   "d_model": shape.d_model, "weights": "seeded random init N(0, 0.02), LoRA r32 merged"},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "load_s": round(t_load, 2), "weight_gen_s": round(t_gen, 2),
+        "kernels": kernels, "roofline": roofline,
+    }
+    plan.free()
+    model.free()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, w, batch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

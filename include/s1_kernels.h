@@ -1,0 +1,95 @@
+/*
+ * s1_kernels.h -- per-kernel entry points of the prefill-only decision
+ * library, for parity tests and micro-benchmarks.
+ *
+ * Every function enqueues one kernel family on hip_stream (NULL: the null
+ * stream) and returns without synchronising, except s1k_la_scan and
+ * s1k_attention, which copy their host metadata to temporary device memory
+ * and synchronise the stream before returning.  All array arguments are device
+ * pointers unless marked "host".  dtype is s1_dtype (S1_F32 or S1_BF16) and
+ * selects the element type of the arrays marked "elem" (bf16 arrays hold raw
+ * bfloat16 bit patterns).  Returns S1_OK, S1_EINVAL for shapes the kernel does
+ * not support, or S1_EDEVICE if the launch failed.  Shapes are checked on the
+ * host before launch; the caller guarantees that every buffer holds the
+ * stated number of elements.
+ */
+#ifndef S1_KERNELS_H
+#define S1_KERNELS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[M,N] (fp32, row stride N) = A[M,K] (elem, row stride K) x W[N,K]^T
+ * (elem, row stride K): the projection GEMM with a plain fp32 epilogue.
+ * split_k >= 1 splits the K loop over workgroups and sums the partial tiles
+ * in a fixed order (deterministic).  bf16 needs K % 8 == 0, fp32 K % 4 == 0.
+ * Projection GEMMs of the decoder (RFC #114, section 1: the language-model
+ * projections; the Cua-S1 issue, "mostly GEMMs" comment). */
+int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
+             int32_t K, int32_t split_k, void* hip_stream);
+
+/* out[T,d] (elem) = x / sqrt(mean(x^2) + eps) * w for each row of x[T,d]
+ * (fp32); w[d] fp32.  RMSNorm before each mixer and FFN (pre-norm blocks of
+ * the Qwen3.5-family backbone the System1-Omni README names). */
+int s1k_rmsnorm(int32_t dtype, const float* x, const float* w, void* out, int32_t T,
+                int32_t d, float eps, void* hip_stream);
+
+/* x[T,d] (fp32) = E[ids[t]] (E elem [V,d]); ids int32 in [0, V) (checked by
+ * the caller).  Tied input embedding (RFC #114 section 3: input/output
+ * embedding tying is preserved). */
+int s1k_embed(int32_t dtype, const int32_t* ids, const void* E, float* x, int32_t T,
+              int32_t d, void* hip_stream);
+
+/* out[out_dim,in_dim] (elem) = W + scale * B A, computed in fp32 and rounded
+ * once (round to nearest even for bf16); W elem [out_dim,in_dim], A elem
+ * [rank,in_dim], B elem [out_dim,rank].  A or B NULL: plain copy of W.
+ * LoRA merge at load (RFC #114 section 3). */
+int s1k_lora_merge(int32_t dtype, const void* W, const void* A, const void* B, void* out,
+                   int32_t out_dim, int32_t in_dim, int32_t rank, float scale, void* hip_stream);
+
+/* Gated linear-attention scan over packed sequences:
+ *   S_t = g_t S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t   per (sequence, head)
+ * q, k (elem, [T, H, dk] at row stride ld_qkv elements), v (elem, [T, H, dv]
+ * at row stride ld_qkv), log_g (fp32 [T, H], natural log of the gate),
+ * o (elem [T, H*dv]).  cu_seqlens (host, n_seqs + 1).  s_init (fp32
+ * [n_seqs, H, dk, dv] or NULL = zero start) and s_final (same shape or NULL)
+ * hold each sequence's initial and final state.  bf16 needs dk = dv = 128;
+ * fp32 needs dk, dv <= 128.  The recurrent state stays fp32 (RFC #114
+ * section 5: FP32 recurrent state). */
+int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int32_t ld_qkv,
+                const float* log_g, void* o, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                int32_t n_seqs, const int32_t* cu_seqlens, const float* s_init,
+                float* s_final, void* hip_stream);
+
+/* Causal attention over packed sequences with grouped KV heads:
+ *   o_t = sum_{s: pos_s <= pos_t} softmax_s(q_t . k_s / sqrt(hd)) v_s
+ * q (elem [Tq, Hq, hd]), k, v (elem [Tkv, Hkv, hd]), o (elem [Tq, Hq, hd]).
+ * Sequence i has queries q_row0[i] .. q_row0[i] + q_len[i] - 1; its keys are
+ * kv_pre_len[i] prefix rows starting at kv_pre_row0[i] (positions 0 ..) and
+ * then its own q_len[i] rows starting at kv_row0[i] (positions
+ * kv_pre_len[i] ..); query j has position kv_pre_len[i] + j.  All five
+ * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd <= 128. */
+int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                  int32_t Hq, int32_t Hkv, int32_t hd, int32_t n_seqs, const int32_t* q_row0,
+                  const int32_t* q_len, const int32_t* kv_row0, const int32_t* kv_pre_row0,
+                  const int32_t* kv_pre_len, void* hip_stream);
+
+/* Decision readout for Q questions: h = RMSNorm(x[rows[j]]; w_final),
+ * z_k = h . E[opt_k], p = softmax(z) over the question's options, and the
+ * answer fields (layout of s1_decision in s1.h: int32 choice then 5 floats).
+ * x fp32 [*, d], E elem [V, d], rows/opt_offsets/opt_ids/q_type device;
+ * at most 1024 options per question.
+ * (Cua-S1 issue, first plan comment; sys1rust README, "Try it".) */
+int s1k_readout(int32_t dtype, const float* x, int32_t d, const float* w_final, float eps,
+                const void* E, int32_t Q, const int32_t* rows, const int32_t* opt_offsets,
+                const int32_t* opt_ids, const uint8_t* q_type, float* probs, void* decisions,
+                void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S1_KERNELS_H */

@@ -37,13 +37,13 @@ varlen = independent, continuation = plain forward.
 """
 from .reference import (OracleModel, bf16_bits_to_float, round_to_bf16_bits,
                         rms_norm, rope_rotate_half, la_scan_recurrent,
-                        la_scan_unrolled, causal_attention, swiglu,
+                        la_scan_unrolled, la_scan_segmented, causal_attention, swiglu,
                         lora_merge, softmax, decision_fields, readout,
                         prefill_decide, QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL)
 
 __all__ = [
     "OracleModel", "bf16_bits_to_float", "round_to_bf16_bits", "rms_norm",
-    "rope_rotate_half", "la_scan_recurrent", "la_scan_unrolled",
+    "rope_rotate_half", "la_scan_recurrent", "la_scan_unrolled", "la_scan_segmented",
     "causal_attention", "swiglu", "lora_merge", "softmax", "decision_fields",
     "readout", "prefill_decide", "QTYPE_CHOICE", "QTYPE_SCORE", "QTYPE_NOUL",
 ]

@@ -142,6 +142,23 @@ def la_scan_unrolled(q, k, v, g, S0=None):
     return o, S_fin
 
 
+def la_scan_segmented(q, k, v, g, S0=None, segment=512):
+    """The recurrence over consecutive segments of the sequence, each in the
+    unrolled form, the state at a segment's end being the next segment's
+    initial state -- the state summarises everything before it, which is also
+    what lets a branch continue from a prefix ([rfc114] section 5).  Bounds
+    the unrolled form's T x T decay matrix for long sequences."""
+    T, H, _ = q.shape
+    o = np.zeros((T, H, v.shape[2]), dtype=q.dtype)
+    S = S0
+    if T == 0:
+        return la_scan_unrolled(q, k, v, g, S0)
+    for a in range(0, T, segment):
+        b = min(T, a + segment)
+        o[a:b], S = la_scan_unrolled(q[a:b], k[a:b], v[a:b], g[a:b], S)
+    return o, S
+
+
 def causal_attention(q, k, v, q_pos, k_pos):
     """Causal softmax attention, the definition: for query head h with kv head
     h // (Hq / Hkv) (grouped, contiguous groups, R8),
@@ -307,7 +324,7 @@ class OracleModel:
         k = self.proj(p + ".k", u).reshape(T, s.la_heads, s.la_dk)
         v = self.proj(p + ".v", u).reshape(T, s.la_heads, s.la_dv)
         g = sigmoid(self.proj(p + ".g", u))           # (R2) one gate per head
-        o, S = la_scan_unrolled(q, k, v, g, S0)
+        o, S = la_scan_segmented(q, k, v, g, S0)
         return self.proj(p + ".o", o.reshape(T, s.la_heads * s.la_dv)), S
 
     def _full(self, l, u, pos, prefix):
@@ -330,14 +347,16 @@ class OracleModel:
         return self.proj(p + ".o", o.reshape(T, s.fa_q_heads * s.fa_head_dim)), (k, v, kpos)
 
     # -- forward ---------------------------------------------------------
-    def forward(self, ids, start_pos=0, cache=None, want_cache=False, capture_rows=None):
+    def forward(self, ids, start_pos=0, cache=None, want_cache=False, capture_rows=None,
+                n_layers=None):
         """Forward over one sequence.  Returns (x_final [T, d], hidden, cache):
         hidden[l] = residual stream after the embedding (l = 0) and after
         layer l (l >= 1) at capture_rows (all rows if None); cache holds each
         linear layer's final state and each full layer's keys/values, so that
         a continuation can start from it ([rfc114] section 5: snapshot of the
         full-attention KV and the recurrent state; every branch starts from
-        the same snapshot)."""
+        the same snapshot).  n_layers < all runs only the first layers (used
+        to time a bounded sample)."""
         s = self.s
         T = len(ids)
         pos = start_pos + np.arange(T, dtype=np.int64)
@@ -345,7 +364,7 @@ class OracleModel:
         rows = slice(None) if capture_rows is None else np.asarray(capture_rows)
         hidden = [x[rows].copy()]
         out_cache = {"la": {}, "fa": {}, "len": start_pos + T}
-        for l in range(s.n_layers):
+        for l in range(s.n_layers if n_layers is None else n_layers):
             u = rms_norm(x, self.W(f"layers.{l}.attn_norm"), s.rms_eps)
             if s.is_full(l):
                 prefix = None if cache is None else cache["fa"][l]
@@ -391,12 +410,16 @@ def prefill_decide(model, batch, mode="plain", capture=None, seqs=None):
     todo = range(batch.n_seqs) if seqs is None else seqs
     probs, fields, hidden = {}, {}, {}
     prefix_cache = {}
+    is_prefix = set(int(p) for p in batch.prefix_of if p >= 0)
     for i in todo:
         ids = batch.tokens_of(i)
         pidx = int(batch.prefix_of[i])
         rows = capture.get(i)
         if pidx < 0:
-            x, hid, _ = model.forward(ids, capture_rows=rows)
+            keep = mode != "plain" and i in is_prefix
+            x, hid, c = model.forward(ids, capture_rows=rows, want_cache=keep)
+            if keep:
+                prefix_cache[i] = c
         elif mode == "plain":
             pids = batch.tokens_of(pidx)
             P = len(pids)

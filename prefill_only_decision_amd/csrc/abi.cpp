@@ -1,0 +1,438 @@
+// C ABI of the library: argument validation, error reporting, entry points.
+#include <chrono>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/s1.h"
+#include "../../include/s1_kernels.h"
+#include "internal.h"
+
+namespace s1 {
+
+namespace {
+thread_local std::string g_err;
+}
+
+int set_error(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+std::string hip_msg(hipError_t e, const char* what) {
+  return std::string(what) + ": " + hipGetErrorString(e);
+}
+
+int validate_config(const s1_config* c) {
+  if (!c) return set_error(S1_EINVAL, "config is NULL");
+  if (c->dtype != S1_F32 && c->dtype != S1_BF16) return set_error(S1_EINVAL, "dtype must be S1_F32 or S1_BF16");
+  if (c->n_layers < 1 || c->full_every < 1 || c->d_model < 1 || c->ffn < 1 || c->vocab < 1 ||
+      c->la_heads < 1 || c->la_dk < 1 || c->la_dv < 1 || c->fa_q_heads < 1 || c->fa_kv_heads < 1 ||
+      c->fa_head_dim < 1)
+    return set_error(S1_EINVAL, "every shape field must be positive");
+  if (c->fa_q_heads % c->fa_kv_heads) return set_error(S1_EINVAL, "fa_q_heads must be a multiple of fa_kv_heads");
+  if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return set_error(S1_EINVAL, "rope_base must be > 0 and rms_eps >= 0");
+  if (c->lora_rank < 0 || c->lora_rank > 64 || (c->lora_targets && c->lora_rank < 1))
+    return set_error(S1_EINVAL, "lora_rank must be in [1, 64] when targets are set");
+  if (c->lora_targets & ~0x7Fu) return set_error(S1_EINVAL, "unknown LoRA target bits");
+  if (c->max_tokens < 1 || c->max_seqs < 1 || c->max_questions < 1 || c->max_options < 2 ||
+      c->max_prefixes < 1 || c->max_positions < 1)
+    return set_error(S1_EINVAL, "budgets must be positive (max_options >= 2)");
+  if (c->max_tokens > (1LL << 30) || c->max_positions > (1LL << 24))
+    return set_error(S1_EINVAL, "max_tokens or max_positions too large");
+  if (c->d_model + c->max_options > 16384)
+    return set_error(S1_EINVAL, "d_model + max_options must not exceed 16384 (readout LDS)");
+  if (c->dtype == S1_BF16) {
+    if (c->la_dk != 128 || c->la_dv != 128 || c->fa_head_dim != 128)
+      return set_error(S1_EINVAL, "bf16 models need la_dk = la_dv = fa_head_dim = 128");
+    if (c->d_model % 64 || c->ffn % 64)
+      return set_error(S1_EINVAL, "bf16 models need d_model and ffn to be multiples of 64");
+  } else {
+    if (c->fa_head_dim != 64 && c->fa_head_dim != 128)
+      return set_error(S1_EINVAL, "fp32 models need fa_head_dim 64 or 128");
+    if (c->la_dk > 128 || c->la_dv > 128 || 256 % c->la_dv || c->la_dk % (256 / c->la_dv))
+      return set_error(S1_EINVAL, "fp32 models need la_dv dividing 256 and la_dk <= 128");
+    if (c->d_model % 4 || c->ffn % 4 || (c->la_heads * c->la_dv) % 4)
+      return set_error(S1_EINVAL, "fp32 models need d_model, ffn, la_heads*la_dv multiples of 4");
+  }
+  return S1_OK;
+}
+
+int validate_batch(const s1_config* c, const s1_batch* b) {
+  if (!c || !b) return set_error(S1_EINVAL, "config or batch is NULL");
+  const int n = b->n_seqs;
+  if (n < 0) return set_error(S1_EINVAL, "n_seqs < 0");
+  if (n > c->max_seqs) return set_error(S1_EBUDGET, "more sequences than max_seqs");
+  if (n > 0 && !b->cu_seqlens) return set_error(S1_EINVAL, "cu_seqlens is NULL");
+  if (n > 0 && b->cu_seqlens[0] != 0) return set_error(S1_EINVAL, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < n; ++i)
+    if (b->cu_seqlens[i + 1] < b->cu_seqlens[i]) return set_error(S1_EINVAL, "cu_seqlens must be non-decreasing");
+  const long long T = n > 0 ? b->cu_seqlens[n] : 0;
+  if (T > c->max_tokens) return set_error(S1_EBUDGET, "more tokens than max_tokens");
+  if (T > 0 && !b->token_ids) return set_error(S1_EINVAL, "token_ids is NULL");
+  for (long long t = 0; t < T; ++t)
+    if (b->token_ids[t] < 0 || b->token_ids[t] >= c->vocab)
+      return set_error(S1_EINVAL, "token id out of range at " + std::to_string(t));
+  auto len = [&](int i) { return b->cu_seqlens[i + 1] - b->cu_seqlens[i]; };
+  std::vector<char> is_prefix(n, 0);
+  int n_prefix = 0;
+  for (int i = 0; i < n; ++i) {
+    const int p = b->prefix_of ? b->prefix_of[i] : -1;
+    if (p < -1 || p >= n || p == i) return set_error(S1_EINVAL, "prefix_of[" + std::to_string(i) + "] is invalid");
+    if (p >= 0) {
+      if (b->prefix_of[p] != -1) return set_error(S1_EINVAL, "a prefix must not itself be a branch");
+      if (!is_prefix[p]) ++n_prefix;
+      is_prefix[p] = 1;
+    }
+    const long long positions = (long long)len(i) + (p >= 0 ? len(p) : 0);
+    if (positions > c->max_positions) return set_error(S1_EBUDGET, "sequence longer than max_positions");
+  }
+  if (n_prefix > c->max_prefixes) return set_error(S1_EBUDGET, "more prefix sequences than max_prefixes");
+  const int Q = b->n_questions;
+  if (Q < 0) return set_error(S1_EINVAL, "n_questions < 0");
+  if (Q > c->max_questions) return set_error(S1_EBUDGET, "more questions than max_questions");
+  if (Q > 0 && (!b->q_seq || !b->q_marker || !b->q_type || !b->opt_offsets || !b->opt_ids))
+    return set_error(S1_EINVAL, "question arrays are NULL");
+  if (Q > 0 && b->opt_offsets[0] != 0) return set_error(S1_EINVAL, "opt_offsets[0] must be 0");
+  for (int j = 0; j < Q; ++j) {
+    const std::string at = " (question " + std::to_string(j) + ")";
+    const int s = b->q_seq[j];
+    if (s < 0 || s >= n) return set_error(S1_EINVAL, "q_seq out of range" + at);
+    if (b->q_marker[j] < 0 || b->q_marker[j] >= len(s)) return set_error(S1_EINVAL, "marker outside its sequence" + at);
+    if (b->q_type[j] > S1_NOUL) return set_error(S1_EINVAL, "unknown question type" + at);
+    const int K = b->opt_offsets[j + 1] - b->opt_offsets[j];
+    if (K < 2) return set_error(S1_EINVAL, "a question needs at least 2 options" + at);
+    if (b->q_type[j] == S1_NOUL && K != 2) return set_error(S1_EINVAL, "a noul question needs exactly 2 options" + at);
+    if (K > c->max_options) return set_error(S1_EBUDGET, "more options than max_options" + at);
+    for (int k = b->opt_offsets[j]; k < b->opt_offsets[j + 1]; ++k)
+      if (b->opt_ids[k] < 0 || b->opt_ids[k] >= c->vocab) return set_error(S1_EINVAL, "option id out of range" + at);
+  }
+  return S1_OK;
+}
+
+}  // namespace s1
+
+using namespace s1;
+
+struct s1_model {
+  Model* m;
+};
+struct s1_plan {
+  Plan* p;
+  s1_model* owner;
+};
+
+extern "C" {
+
+const char* s1_last_error(void) { return g_err.c_str(); }
+
+int s1_validate(const s1_config* cfg, const s1_batch* b) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  return validate_batch(cfg, b);
+}
+
+int s1_load_weights(const s1_config* cfg, const s1_tensor* tensors, int32_t n_tensors,
+                    void* hip_stream, s1_model** out) {
+  if (!out) return set_error(S1_EINVAL, "out is NULL");
+  Model* m = nullptr;
+  const int rc = load_model(cfg, tensors, n_tensors, static_cast<hipStream_t>(hip_stream), &m);
+  if (rc) return rc;
+  s1_model* h = new (std::nothrow) s1_model{m};
+  if (!h) {
+    delete m;
+    return set_error(S1_ENOMEM, "host allocation failed");
+  }
+  *out = h;
+  g_err.clear();
+  return S1_OK;
+}
+
+void s1_free(s1_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  delete m->m;
+  delete m;
+}
+
+int s1_plan_create(s1_model* m, const s1_batch* b, s1_plan** out) {
+  if (!m || !out) return set_error(S1_EINVAL, "model or out is NULL");
+  Plan* p = nullptr;
+  const int rc = create_plan(m->m, b, &p);
+  if (rc) return rc;
+  s1_plan* h = new (std::nothrow) s1_plan{p, m};
+  if (!h) {
+    delete p;
+    return set_error(S1_ENOMEM, "host allocation failed");
+  }
+  *out = h;
+  return S1_OK;
+}
+
+void s1_plan_free(s1_plan* p) {
+  if (!p) return;
+  delete p->p;
+  delete p;
+}
+
+int64_t s1_plan_tokens(const s1_plan* p) { return p ? p->p->T : 0; }
+
+int s1_plan_set_capture(s1_plan* p, int32_t n_rows, const int32_t* rows, float* d_hidden) {
+  if (!p) return set_error(S1_EINVAL, "plan is NULL");
+  return set_capture(p->p, n_rows, rows, d_hidden);
+}
+
+int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream) {
+  if (!m || !p) return set_error(S1_EINVAL, "model or plan is NULL");
+  if (p->owner != m) return set_error(S1_EINVAL, "plan belongs to another model");
+  if (p->p->Q > 0 && (!d_probs || !d_out)) return set_error(S1_EINVAL, "output buffers are NULL");
+  hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : m->m->own_stream;
+  const int rc = run_plan(m->m, p->p, d_probs, d_out, s);
+  if (rc) (void)hipStreamSynchronize(s);
+  return rc;
+}
+
+int s1_plan_profile(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream,
+                    s1_kernel_time* out, int32_t max_out, int32_t* n_out) {
+  if (!m || !p || !out || !n_out || max_out < 1) return set_error(S1_EINVAL, "NULL argument");
+  if (p->owner != m) return set_error(S1_EINVAL, "plan belongs to another model");
+  Model* mm = m->m;
+  hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : mm->own_stream;
+  if (!mm->prof) mm->prof = new (std::nothrow) Profiler();
+  if (!mm->prof || mm->prof->reserve(16 * mm->cfg.n_layers + 64) != S1_OK)
+    return set_error(S1_EDEVICE, "profiler events");
+  int rc = run_plan(mm, p->p, d_probs, d_out, s);
+  Profiler* pr = mm->prof;
+  mm->prof = nullptr;
+  const hipError_t se = hipStreamSynchronize(s);
+  mm->prof = pr;
+  if (rc) return rc;
+  if (se != hipSuccess) return set_error(S1_EDEVICE, hip_msg(se, "profiled run"));
+  if (pr->overflow) return set_error(S1_EDEVICE, "profiler ran out of events");
+  double tot[KC_COUNT] = {0};
+  int cnt[KC_COUNT] = {0};
+  for (int i = 1; i < pr->used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr->ev[i - 1], pr->ev[i]) != hipSuccess) return set_error(S1_EDEVICE, "event time");
+    const int c = pr->cls[i];
+    if (c >= 0 && c < KC_COUNT) {
+      tot[c] += ms * 1000.0;
+      cnt[c] += 1;
+    }
+  }
+  int k = 0;
+  for (int c = 0; c < KC_COUNT && k < max_out; ++c) {
+    if (!cnt[c]) continue;
+    std::memset(out[k].name, 0, sizeof(out[k].name));
+    std::strncpy(out[k].name, kernel_class_name(c), sizeof(out[k].name) - 1);
+    out[k].launches = cnt[c];
+    out[k].total_us = tot[c];
+    ++k;
+  }
+  *n_out = k;
+  return S1_OK;
+}
+
+int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision* out,
+                      s1_timing* timing, void* hip_stream) {
+  const auto t0 = std::chrono::steady_clock::now();
+  if (!m) return set_error(S1_EINVAL, "model is NULL");
+  int rc = validate_batch(&m->m->cfg, b);
+  if (rc) return rc;
+  if (b->n_questions > 0 && (!probs || !out)) return set_error(S1_EINVAL, "output arrays are NULL");
+  hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : m->m->own_stream;
+  Plan* p = nullptr;
+  rc = create_plan(m->m, b, &p);
+  if (rc) return rc;
+  const int Q = p->Q, nopt = p->total_opts;
+  void* dout = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  double dev_us = 0.0;
+  const size_t bytes = (size_t)nopt * sizeof(float) + (size_t)Q * sizeof(s1_decision) + 16;
+  auto fail = [&](int code, const std::string& msg) {
+    (void)hipStreamSynchronize(s);
+    if (dout) (void)hipFree(dout);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    delete p;
+    return code == S1_OK ? S1_OK : (msg.empty() ? code : set_error(code, msg));
+  };
+  if (hipMalloc(&dout, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    dout = nullptr;
+    return fail(S1_ENOMEM, "device allocation for results failed");
+  }
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+    return fail(S1_EDEVICE, "event creation failed");
+  float* dprobs = static_cast<float*>(dout);
+  s1_decision* ddec = reinterpret_cast<s1_decision*>(static_cast<char*>(dout) + ((size_t)nopt * 4 + 15) / 16 * 16);
+  if (hipEventRecord(e0, s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
+  rc = run_plan(m->m, p, dprobs, ddec, s);
+  if (rc) return fail(rc, "");
+  if (hipEventRecord(e1, s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
+  if (Q > 0) {
+    if (hipMemcpyAsync(probs, dprobs, (size_t)nopt * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(out, ddec, (size_t)Q * sizeof(s1_decision), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return fail(S1_EDEVICE, "copy results to host failed");
+  }
+  const hipError_t se = hipStreamSynchronize(s);
+  if (se != hipSuccess) return fail(S1_EDEVICE, hip_msg(se, "device work failed"));
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, e0, e1) == hipSuccess) dev_us = ms * 1000.0;
+  const long long T = p->T;
+  fail(S1_OK, "");
+  if (timing) {
+    timing->tokens_processed = T;
+    timing->device_us = dev_us;
+    timing->wall_us =
+        std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  }
+  return S1_OK;
+}
+
+// ----------------------------------------------------------- kernel level
+static hipStream_t strm(void* s) { return static_cast<hipStream_t>(s); }
+static int dev_status(hipError_t e, const char* what) {
+  return e == hipSuccess ? S1_OK : set_error(S1_EDEVICE, hip_msg(e, what));
+}
+
+int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
+             int32_t split_k, void* hip_stream) {
+  const bool bf16 = dtype == S1_BF16;
+  if ((dtype != S1_BF16 && dtype != S1_F32) || M < 0 || N < 0 || K < 1 || split_k < 1 ||
+      K % (bf16 ? 8 : 4) || (split_k > 1 && N % 4) || !A || !W || !C)
+    return set_error(S1_EINVAL, "s1k_gemm: unsupported arguments");
+  GemmArgs g{};
+  g.A = A;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldw = K;
+  g.out0 = C;
+  g.ld0 = N;
+  float* ws = nullptr;
+  if (split_k > 1) {
+    if (hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)split_k * M * N * sizeof(float) + 256, strm(hip_stream)) != hipSuccess)
+      return set_error(S1_ENOMEM, "s1k_gemm: workspace allocation failed");
+  }
+  const hipError_t e = launch_gemm(bf16, EPI_F32, g, split_k, ws, strm(hip_stream));
+  if (ws) (void)hipFreeAsync(ws, strm(hip_stream));
+  return dev_status(e, "s1k_gemm");
+}
+
+int s1k_rmsnorm(int32_t dtype, const float* x, const float* w, void* out, int32_t T, int32_t d, float eps,
+                void* hip_stream) {
+  if ((dtype != S1_BF16 && dtype != S1_F32) || T < 0 || d < 4 || d % 4 || !x || !w || !out)
+    return set_error(S1_EINVAL, "s1k_rmsnorm: unsupported arguments");
+  return dev_status(launch_rmsnorm(dtype == S1_BF16, x, w, out, T, d, eps, strm(hip_stream)), "s1k_rmsnorm");
+}
+
+int s1k_embed(int32_t dtype, const int32_t* ids, const void* E, float* x, int32_t T, int32_t d,
+              void* hip_stream) {
+  if ((dtype != S1_BF16 && dtype != S1_F32) || T < 0 || d < 4 || d % 4 || !ids || !E || !x)
+    return set_error(S1_EINVAL, "s1k_embed: unsupported arguments");
+  return dev_status(launch_embed(dtype == S1_BF16, ids, E, x, T, d, strm(hip_stream)), "s1k_embed");
+}
+
+int s1k_lora_merge(int32_t dtype, const void* W, const void* A, const void* B, void* out, int32_t out_dim,
+                   int32_t in_dim, int32_t rank, float scale, void* hip_stream) {
+  if ((dtype != S1_BF16 && dtype != S1_F32) || out_dim < 0 || in_dim < 0 || !W || !out ||
+      ((A == nullptr) != (B == nullptr)) || (A && (rank < 1 || rank > 64)))
+    return set_error(S1_EINVAL, "s1k_lora_merge: unsupported arguments");
+  return dev_status(launch_merge(dtype == S1_BF16, W, A, B, out, out_dim, in_dim, rank, scale, nullptr,
+                                 strm(hip_stream)),
+                    "s1k_lora_merge");
+}
+
+int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int32_t ld_qkv,
+                const float* log_g, void* o, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t n_seqs,
+                const int32_t* cu_seqlens, const float* s_init, float* s_final, void* hip_stream) {
+  const bool bf16 = dtype == S1_BF16;
+  if ((dtype != S1_BF16 && dtype != S1_F32) || n_seqs < 0 || H < 1 || !cu_seqlens || !q || !k || !v ||
+      !log_g || !o || (bf16 && (dk != 128 || dv != 128)) ||
+      (!bf16 && (dk > 128 || dv > 128 || 256 % dv || dk % (256 / dv))))
+    return set_error(S1_EINVAL, "s1k_la_scan: unsupported arguments");
+  if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T))
+    return set_error(S1_EINVAL, "s1k_la_scan: cu_seqlens out of range");
+  if (n_seqs == 0) return S1_OK;
+  // one state buffer: initial states copied in, final states copied out
+  std::vector<ScanSeq> seqs(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    if (cu_seqlens[i + 1] < cu_seqlens[i]) return set_error(S1_EINVAL, "s1k_la_scan: cu_seqlens decreasing");
+    seqs[i] = {cu_seqlens[i], cu_seqlens[i + 1] - cu_seqlens[i], s_init ? i : -1, -1};
+  }
+  const size_t sbytes = (size_t)n_seqs * H * dk * dv * sizeof(float);
+  float* st = nullptr;
+  ScanSeq* dseq = nullptr;
+  hipStream_t s = strm(hip_stream);
+  if (hipMalloc(&st, sbytes) != hipSuccess || hipMalloc(&dseq, seqs.size() * sizeof(ScanSeq)) != hipSuccess) {
+    (void)hipGetLastError();
+    if (st) (void)hipFree(st);
+    return set_error(S1_ENOMEM, "s1k_la_scan: allocation failed");
+  }
+  // the kernel reads slot s_in and writes slot s_out of the same buffer; with
+  // s_in == s_out == i the read happens before the write in the same workgroup
+  for (auto& q2 : seqs) q2.s_out = s_final ? (int)(&q2 - seqs.data()) : -1;
+  hipError_t e = hipMemcpy(dseq, seqs.data(), seqs.size() * sizeof(ScanSeq), hipMemcpyHostToDevice);
+  if (e == hipSuccess && s_init) e = hipMemcpyAsync(st, s_init, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_scan(bf16, q, k, v, ld_qkv, log_g, H, o, H * dv, dseq, n_seqs, st, H, dk, dv, s);
+  if (e == hipSuccess && s_final) e = hipMemcpyAsync(s_final, st, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(st);
+  (void)hipFree(dseq);
+  return dev_status(e, "s1k_la_scan");
+}
+
+int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o, int32_t Hq, int32_t Hkv,
+                  int32_t hd, int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len,
+                  const int32_t* kv_row0, const int32_t* kv_pre_row0, const int32_t* kv_pre_len,
+                  void* hip_stream) {
+  const bool bf16 = dtype == S1_BF16;
+  if ((dtype != S1_BF16 && dtype != S1_F32) || Hq < 1 || Hkv < 1 || Hq % Hkv || n_seqs < 0 || !q || !k ||
+      !v || !o || (bf16 && hd != 128) || (!bf16 && (hd < 1 || hd > 128)) ||
+      (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)))
+    return set_error(S1_EINVAL, "s1k_attention: unsupported arguments");
+  std::vector<AttnSeq> seqs(n_seqs);
+  std::vector<AttnBlock> blocks;
+  const int bq = attn_block_rows(bf16);
+  for (int i = 0; i < n_seqs; ++i) {
+    if (q_len[i] < 0 || kv_pre_len[i] < 0) return set_error(S1_EINVAL, "s1k_attention: negative length");
+    seqs[i] = {q_row0[i], q_len[i], kv_row0[i], kv_pre_row0[i], kv_pre_len[i]};
+    for (int q0 = 0; q0 < q_len[i]; q0 += bq) blocks.push_back({i, q0});
+  }
+  if (blocks.empty()) return S1_OK;
+  void* dm = nullptr;
+  const size_t b1 = seqs.size() * sizeof(AttnSeq), b2 = blocks.size() * sizeof(AttnBlock);
+  if (hipMalloc(&dm, b1 + b2 + 256) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "s1k_attention: allocation failed");
+  }
+  auto* ds = static_cast<AttnSeq*>(dm);
+  auto* db = reinterpret_cast<AttnBlock*>(static_cast<char*>(dm) + (b1 + 255) / 256 * 256);
+  hipError_t e = hipMemcpy(ds, seqs.data(), b1, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(db, blocks.data(), b2, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = launch_attention(bf16, q, Hq * hd, k, v, Hkv * hd, o, Hq * hd, ds, db, (int)blocks.size(), Hq, Hkv,
+                         hd, strm(hip_stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(strm(hip_stream));
+  (void)hipFree(dm);
+  return dev_status(e, "s1k_attention");
+}
+
+int s1k_readout(int32_t dtype, const float* x, int32_t d, const float* w_final, float eps, const void* E,
+                int32_t Q, const int32_t* rows, const int32_t* opt_offsets, const int32_t* opt_ids,
+                const uint8_t* q_type, float* probs, void* decisions, void* hip_stream) {
+  if ((dtype != S1_BF16 && dtype != S1_F32) || d < 4 || d % 4 || Q < 0 || !x || !w_final || !E ||
+      (Q > 0 && (!rows || !opt_offsets || !opt_ids || !q_type || !probs || !decisions)))
+    return set_error(S1_EINVAL, "s1k_readout: unsupported arguments");
+  // the LDS holds d floats plus the logits of one question (K <= 1024)
+  if (d + 1024 > 16384) return set_error(S1_EINVAL, "s1k_readout: d too large");
+  return dev_status(launch_readout(dtype == S1_BF16, x, d, w_final, eps, E, Q, rows, opt_offsets, opt_ids,
+                                   q_type, probs, decisions, 1024, strm(hip_stream)),
+                    "s1k_readout");
+}
+
+}  // extern "C"

@@ -1,0 +1,656 @@
+// Model loading (copy, LoRA merge, layout), request plans and the layer loop.
+//
+// One prefill pass per request, no decoding (System1-Omni README,
+// introduction).  Sequences are packed without padding; a request with
+// branches runs two passes over the same packed buffers: pass A over every
+// sequence that is not a branch (prefixes write their full-attention keys and
+// values and their final linear-attention state), pass B over the branches,
+// which start from that snapshot (RFC #114 section 5).  The readout then runs
+// only at the questions' marker rows (sys1rust README, "How it works": the
+// head runs only at the positions the answer reads).
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace s1 {
+
+#define S1_TRY(expr, what)                                  \
+  do {                                                      \
+    hipError_t e_ = (expr);                                 \
+    if (e_ != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e_, what)); \
+  } while (0)
+
+const char* kernel_class_name(int c) {
+  static const char* names[KC_COUNT] = {"embed", "rmsnorm", "gemm_la_in", "la_scan", "gemm_fa_qkv",
+                                        "attention", "gemm_o", "gemm_gate_up", "gemm_down", "capture",
+                                        "readout"};
+  return (c >= 0 && c < KC_COUNT) ? names[c] : "?";
+}
+
+Profiler::~Profiler() {
+  for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+}
+
+int Profiler::reserve(int n) {
+  while ((int)ev.size() < n) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return S1_EDEVICE;
+    ev.push_back(e);
+  }
+  cls.resize(ev.size());
+  return S1_OK;
+}
+
+void Profiler::begin(hipStream_t s) {
+  used = 0;
+  overflow = false;
+  mark(-1, s);
+}
+
+void Profiler::mark(int c, hipStream_t s) {
+  if (used >= (int)ev.size()) {
+    overflow = true;
+    return;
+  }
+  (void)hipEventRecord(ev[used], s);
+  cls[used++] = c;
+}
+
+Model::~Model() {
+  delete prof;
+  for (void* p : allocs) (void)hipFree(p);
+  if (own_stream) (void)hipStreamDestroy(own_stream);
+}
+
+void* Model::alloc(size_t bytes) {
+  void* p = nullptr;
+  if (bytes == 0) bytes = 256;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    throw std::bad_alloc();
+  }
+  allocs.push_back(p);
+  return p;
+}
+
+Plan::~Plan() {
+  if (dev) (void)hipFree(dev);
+  if (cap_dev) (void)hipFree(cap_dev);
+}
+
+namespace {
+
+struct TensorTable {
+  std::map<std::string, const s1_tensor*> byname;
+  const s1_tensor* get(const std::string& n) const {
+    auto it = byname.find(n);
+    return it == byname.end() ? nullptr : it->second;
+  }
+};
+
+// Index of dimension i of a rotate-half head after the permutation that puts
+// the partner of each column exactly 32 columns later: within every group of
+// 64 columns, the first 32 hold dims d and the next 32 hold dims d + hd/2.
+int rope_perm(int i, int hd) {
+  const int half = hd / 2;
+  if (i < half) return 64 * (i / 32) + (i % 32);
+  const int j = i - half;
+  return 64 * (j / 32) + 32 + (j % 32);
+}
+
+class Loader {
+ public:
+  Loader(Model* m, const TensorTable& tt, hipStream_t s) : m_(m), tt_(tt), s_(s) {}
+  ~Loader() {
+    for (void* p : scratch_) (void)hipFree(p);
+  }
+
+  // Copy (or reference) tensor `name`, checking its shape.
+  int fetch(const std::string& name, int64_t rows, int64_t cols, const void** dev) {
+    const s1_tensor* t = tt_.get(name);
+    if (!t) return set_error(S1_EINVAL, "missing tensor '" + name + "'");
+    const int64_t r = t->ndim == 1 ? 1 : t->shape[0];
+    const int64_t c = t->ndim == 1 ? t->shape[0] : t->shape[1];
+    const int64_t want_r = cols < 0 ? 1 : rows, want_c = cols < 0 ? rows : cols;
+    if (t->dtype != m_->cfg.dtype || t->ndim < 1 || t->ndim > 2 || r != want_r || c != want_c ||
+        t->data == nullptr)
+      return set_error(S1_EINVAL, "tensor '" + name + "' has the wrong dtype, shape or no data");
+    const size_t bytes = (size_t)(want_r * want_c) * m_->esz;
+    if (t->on_device) {
+      *dev = t->data;
+      return S1_OK;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return set_error(S1_ENOMEM, "device allocation for '" + name + "' failed");
+    }
+    scratch_.push_back(p);
+    S1_TRY(hipMemcpy(p, t->data, bytes, hipMemcpyHostToDevice), "copy weights to device");
+    *dev = p;
+    return S1_OK;
+  }
+
+  // Merge the adapter of `name` (if it is a target) into its rows of dst,
+  // row o of the [out, in] source going to dst row map[o] (or base + o).
+  int projection(const std::string& name, int out_dim, int in_dim, bool target, void* dst,
+                 const std::vector<int>& map) {
+    const void* w = nullptr;
+    const void* a = nullptr;
+    const void* b = nullptr;
+    int rc = fetch(name, out_dim, in_dim, &w);
+    if (rc) return rc;
+    const int r = m_->cfg.lora_rank;
+    if (target) {
+      if ((rc = fetch(name + ".lora_A", r, in_dim, &a))) return rc;
+      if ((rc = fetch(name + ".lora_B", out_dim, r, &b))) return rc;
+    }
+    int* dmap = nullptr;
+    if (!map.empty()) {
+      if (hipMalloc(&dmap, map.size() * sizeof(int)) != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(S1_ENOMEM, "device allocation failed");
+      }
+      scratch_.push_back(dmap);
+      S1_TRY(hipMemcpy(dmap, map.data(), map.size() * sizeof(int), hipMemcpyHostToDevice), "copy row map");
+    }
+    const float scale = target ? m_->cfg.lora_alpha / (float)r : 0.f;
+    S1_TRY(launch_merge(m_->bf16, w, target ? a : nullptr, target ? b : nullptr, dst, out_dim, in_dim,
+                        r, scale, dmap, s_),
+           "LoRA merge");
+    S1_TRY(hipStreamSynchronize(s_), "LoRA merge");
+    release();
+    return S1_OK;
+  }
+
+  int norm(const std::string& name, int d, float** out) {
+    const void* w = nullptr;
+    int rc = fetch(name, d, -1, &w);
+    if (rc) return rc;
+    *out = static_cast<float*>(m_->alloc((size_t)d * sizeof(float)));
+    S1_TRY(launch_to_f32(m_->bf16, w, *out, d, s_), "norm gains");
+    S1_TRY(hipStreamSynchronize(s_), "norm gains");
+    release();
+    return S1_OK;
+  }
+
+  void release() {
+    for (void* p : scratch_) (void)hipFree(p);
+    scratch_.clear();
+  }
+
+ private:
+  Model* m_;
+  const TensorTable& tt_;
+  hipStream_t s_;
+  std::vector<void*> scratch_;
+};
+
+std::vector<int> offset_map(int n, int base) {
+  std::vector<int> v(n);
+  for (int i = 0; i < n; ++i) v[i] = base + i;
+  return v;
+}
+
+int load_layers(Model* m, Loader& ld, hipStream_t s) {
+  const s1_config& c = m->cfg;
+  const int d = c.d_model, F = c.ffn, H = c.la_heads, dk = c.la_dk, dv = c.la_dv;
+  const int Hq = c.fa_q_heads, Hkv = c.fa_kv_heads, hd = c.fa_head_dim;
+  const uint32_t tg = c.lora_targets;
+  int rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerW& L = m->layers[l];
+    const std::string p = "layers." + std::to_string(l);
+    if ((rc = ld.norm(p + ".attn_norm", d, &L.attn_norm))) return rc;
+    if ((rc = ld.norm(p + ".ffn_norm", d, &L.ffn_norm))) return rc;
+    if (!L.full) {
+      const std::string q = p + ".la";
+      L.n_in = 2 * H * dk + H * dv + H;
+      L.w_in = m->alloc((size_t)L.n_in * d * m->esz);
+      if ((rc = ld.projection(q + ".q", H * dk, d, tg & S1_LORA_Q, L.w_in, offset_map(H * dk, 0)))) return rc;
+      if ((rc = ld.projection(q + ".k", H * dk, d, tg & S1_LORA_K, L.w_in, offset_map(H * dk, H * dk)))) return rc;
+      if ((rc = ld.projection(q + ".v", H * dv, d, tg & S1_LORA_V, L.w_in, offset_map(H * dv, 2 * H * dk)))) return rc;
+      if ((rc = ld.projection(q + ".g", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv)))) return rc;
+      L.k_o = H * dv;
+      L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
+      if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
+    } else {
+      const std::string q = p + ".fa";
+      L.n_in = (Hq + 2 * Hkv) * hd;
+      L.w_in = m->alloc((size_t)L.n_in * d * m->esz);
+      std::vector<int> mq(Hq * hd), mk(Hkv * hd);
+      for (int h = 0; h < Hq; ++h)
+        for (int i = 0; i < hd; ++i) mq[h * hd + i] = h * hd + rope_perm(i, hd);
+      for (int h = 0; h < Hkv; ++h)
+        for (int i = 0; i < hd; ++i) mk[h * hd + i] = Hq * hd + h * hd + rope_perm(i, hd);
+      if ((rc = ld.projection(q + ".q", Hq * hd, d, tg & S1_LORA_Q, L.w_in, mq))) return rc;
+      if ((rc = ld.projection(q + ".k", Hkv * hd, d, tg & S1_LORA_K, L.w_in, mk))) return rc;
+      if ((rc = ld.projection(q + ".v", Hkv * hd, d, tg & S1_LORA_V, L.w_in,
+                              offset_map(Hkv * hd, (Hq + Hkv) * hd)))) return rc;
+      L.k_o = Hq * hd;
+      L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
+      if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
+    }
+    const std::string f = p + ".ffn";
+    L.n_gu = 2 * m->ffn_pad;
+    L.w_gu = m->alloc((size_t)L.n_gu * d * m->esz);
+    S1_TRY(hipMemsetAsync(L.w_gu, 0, (size_t)L.n_gu * d * m->esz, s), "clear gate/up");
+    std::vector<int> mg(F), mu(F);
+    for (int i = 0; i < F; ++i) {
+      mg[i] = 64 * (i / 32) + (i % 32);
+      mu[i] = mg[i] + 32;
+    }
+    if ((rc = ld.projection(f + ".gate", F, d, tg & S1_LORA_GATE, L.w_gu, mg))) return rc;
+    if ((rc = ld.projection(f + ".up", F, d, tg & S1_LORA_UP, L.w_gu, mu))) return rc;
+    L.w_down = m->alloc((size_t)d * F * m->esz);
+    if ((rc = ld.projection(f + ".down", d, F, tg & S1_LORA_DOWN, L.w_down, {}))) return rc;
+  }
+  return S1_OK;
+}
+
+int alloc_workspace(Model* m) {
+  const s1_config& c = m->cfg;
+  const long long T = c.max_tokens, d = c.d_model;
+  const int H = c.la_heads, Hq = c.fa_q_heads, Hkv = c.fa_kv_heads, hd = c.fa_head_dim;
+  m->ld_qkv = std::max(2 * H * c.la_dk + H * c.la_dv, Hq * hd);
+  m->ld_att = std::max(H * c.la_dv, Hq * hd);
+  m->x = static_cast<float*>(m->alloc(T * d * sizeof(float)));
+  m->xn = m->alloc(T * d * m->esz);
+  m->qkv = m->alloc(T * m->ld_qkv * m->esz);
+  m->lg = static_cast<float*>(m->alloc(T * H * sizeof(float)));
+  m->att = m->alloc(T * m->ld_att * m->esz);
+  m->hbuf = m->alloc(T * (long long)c.ffn * m->esz);
+  m->kc = m->alloc((size_t)std::max(1, m->n_fa) * T * Hkv * hd * m->esz);
+  m->vc = m->alloc((size_t)std::max(1, m->n_fa) * T * Hkv * hd * m->esz);
+  m->states = static_cast<float*>(m->alloc((size_t)std::max(1, m->n_la) * c.max_prefixes * H *
+                                           c.la_dk * c.la_dv * sizeof(float)));
+  m->split_max_rows = (int)std::min<long long>(T, 2048);
+  m->splitws_elems = 4LL * m->split_max_rows * d;
+  m->splitws = static_cast<float*>(m->alloc(m->splitws_elems * sizeof(float)));
+  m->rope = static_cast<float2*>(m->alloc((size_t)c.max_positions * (hd / 2) * sizeof(float2)));
+  return S1_OK;
+}
+
+}  // namespace
+
+int load_model(const s1_config* cfg, const s1_tensor* tensors, int n, hipStream_t user_stream,
+               Model** out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && tensors == nullptr)) return set_error(S1_EINVAL, "tensor table is NULL");
+  TensorTable tt;
+  for (int i = 0; i < n; ++i) {
+    if (tensors[i].name == nullptr) return set_error(S1_EINVAL, "tensor with a NULL name");
+    tt.byname[tensors[i].name] = &tensors[i];
+  }
+  Model* m = new (std::nothrow) Model();
+  if (!m) return set_error(S1_ENOMEM, "host allocation failed");
+  m->cfg = *cfg;
+  m->bf16 = cfg->dtype == S1_BF16;
+  m->esz = m->bf16 ? 2 : 4;
+  m->ffn_pad = (cfg->ffn + 31) / 32 * 32;
+  if (hipGetDevice(&m->device) != hipSuccess) {
+    delete m;
+    return set_error(S1_EDEVICE, "no HIP device");
+  }
+  if (hipStreamCreateWithFlags(&m->own_stream, hipStreamNonBlocking) != hipSuccess) {
+    delete m;
+    return set_error(S1_EDEVICE, "stream creation failed");
+  }
+  hipStream_t s = user_stream ? user_stream : m->own_stream;
+  m->layers.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    LayerW& L = m->layers[l];
+    L.full = (l % cfg->full_every) == cfg->full_every - 1;
+    if (L.full) L.fa_idx = m->n_fa++;
+    else L.la_idx = m->n_la++;
+  }
+  try {
+    Loader ld(m, tt, s);
+    const void* e = nullptr;
+    rc = ld.fetch("embed", cfg->vocab, cfg->d_model, &e);
+    if (!rc) {
+      const size_t bytes = (size_t)cfg->vocab * cfg->d_model * m->esz;
+      m->embed = m->alloc(bytes);
+      if (hipMemcpyAsync(m->embed, e, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        rc = set_error(S1_EDEVICE, "copy embedding");
+      ld.release();
+    }
+    if (!rc) rc = ld.norm("final_norm", cfg->d_model, &m->final_norm);
+    if (!rc) rc = load_layers(m, ld, s);
+    if (!rc) rc = alloc_workspace(m);
+    if (!rc) {
+      if (launch_rope_table(m->rope, (int)cfg->max_positions, cfg->fa_head_dim, cfg->rope_base, s) !=
+              hipSuccess ||
+          hipStreamSynchronize(s) != hipSuccess)
+        rc = set_error(S1_EDEVICE, "rope table");
+    }
+  } catch (const std::bad_alloc&) {
+    rc = set_error(S1_ENOMEM, "device allocation failed while loading the model");
+  }
+  if (rc) {
+    (void)hipStreamSynchronize(s);
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return S1_OK;
+}
+
+// ------------------------------------------------------------------ plans
+int create_plan(Model* m, const s1_batch* b, Plan** out) {
+  int rc = validate_batch(&m->cfg, b);
+  if (rc) return rc;
+  Plan* p = new (std::nothrow) Plan();
+  if (!p) return set_error(S1_ENOMEM, "host allocation failed");
+  p->m = m;
+  const int n = b->n_seqs;
+  p->n_seqs = n;
+  p->T = n > 0 ? b->cu_seqlens[n] : 0;
+  p->Q = b->n_questions;
+  p->total_opts = p->Q > 0 ? b->opt_offsets[p->Q] : 0;
+  for (int j = 0; j < p->Q; ++j) p->max_k = std::max(p->max_k, b->opt_offsets[j + 1] - b->opt_offsets[j]);
+
+  auto pre = [&](int i) { return b->prefix_of ? b->prefix_of[i] : -1; };
+  std::vector<int> slot(n, -1);
+  int n_slots = 0;
+  for (int i = 0; i < n; ++i)
+    if (pre(i) >= 0 && slot[pre(i)] < 0) slot[pre(i)] = n_slots++;
+  // internal order: pass A (non-branches) then pass B (branches)
+  std::vector<int> order[2];
+  for (int i = 0; i < n; ++i) order[pre(i) >= 0 ? 1 : 0].push_back(i);
+  std::vector<int> row0(n, 0);
+  p->row_of.assign(p->T, 0);
+  p->pass_of_row.assign(p->T, 0);
+  std::vector<int32_t> ids(p->T), pos(p->T);
+  int r = 0;
+  p->n_passes = order[1].empty() ? 1 : 2;
+  for (int ps = 0; ps < 2; ++ps) {
+    p->pass[ps].r0 = r;
+    for (int i : order[ps]) {
+      row0[i] = r;
+      const int len = b->cu_seqlens[i + 1] - b->cu_seqlens[i];
+      const int P = pre(i) >= 0 ? b->cu_seqlens[pre(i) + 1] - b->cu_seqlens[pre(i)] : 0;
+      for (int t = 0; t < len; ++t) {
+        p->row_of[b->cu_seqlens[i] + t] = r + t;
+        p->pass_of_row[r + t] = ps;
+        ids[r + t] = b->token_ids[b->cu_seqlens[i] + t];
+        pos[r + t] = P + t;
+      }
+      r += len;
+    }
+    p->pass[ps].T = r - p->pass[ps].r0;
+    p->pass[ps].n_seqs = (int)order[ps].size();
+  }
+  std::vector<ScanSeq> scan[2];
+  std::vector<AttnSeq> attn[2];
+  std::vector<AttnBlock> blocks[2];
+  const int bq = attn_block_rows(m->bf16);
+  for (int ps = 0; ps < 2; ++ps)
+    for (size_t k = 0; k < order[ps].size(); ++k) {
+      const int i = order[ps][k];
+      const int len = b->cu_seqlens[i + 1] - b->cu_seqlens[i];
+      const int pi = pre(i);
+      const int P = pi >= 0 ? b->cu_seqlens[pi + 1] - b->cu_seqlens[pi] : 0;
+      scan[ps].push_back({row0[i], len, pi >= 0 ? slot[pi] : -1, slot[i]});
+      attn[ps].push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
+      for (int q0 = 0; q0 < len; q0 += bq) blocks[ps].push_back({(int)k, q0});
+    }
+  std::vector<int32_t> qrow(p->Q);
+  for (int j = 0; j < p->Q; ++j) qrow[j] = row0[b->q_seq[j]] + b->q_marker[j];
+
+  // one device block for every array of the plan
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_ids = take(p->T * 4), o_pos = take(p->T * 4), o_qrow = take(p->Q * 4);
+  const size_t o_off = take((p->Q + 1) * 4), o_opt = take(p->total_opts * 4), o_qt = take(p->Q);
+  size_t o_scan[2], o_attn[2], o_blk[2];
+  for (int ps = 0; ps < 2; ++ps) {
+    o_scan[ps] = take(scan[ps].size() * sizeof(ScanSeq));
+    o_attn[ps] = take(attn[ps].size() * sizeof(AttnSeq));
+    o_blk[ps] = take(blocks[ps].size() * sizeof(AttnBlock));
+  }
+  std::vector<char> host(off, 0);
+  auto put = [&](size_t o, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(host.data() + o, src, bytes);
+  };
+  put(o_ids, ids.data(), p->T * 4);
+  put(o_pos, pos.data(), p->T * 4);
+  put(o_qrow, qrow.data(), p->Q * 4);
+  if (p->Q > 0) {
+    put(o_off, b->opt_offsets, (p->Q + 1) * 4);
+    put(o_opt, b->opt_ids, p->total_opts * 4);
+    put(o_qt, b->q_type, p->Q);
+  }
+  for (int ps = 0; ps < 2; ++ps) {
+    put(o_scan[ps], scan[ps].data(), scan[ps].size() * sizeof(ScanSeq));
+    put(o_attn[ps], attn[ps].data(), attn[ps].size() * sizeof(AttnSeq));
+    put(o_blk[ps], blocks[ps].data(), blocks[ps].size() * sizeof(AttnBlock));
+  }
+  if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return set_error(S1_ENOMEM, "device allocation for the plan failed");
+  }
+  if (hipMemcpy(p->dev, host.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
+    delete p;
+    return set_error(S1_EDEVICE, "copy plan to device");
+  }
+  char* dv = static_cast<char*>(p->dev);
+  p->ids = reinterpret_cast<int32_t*>(dv + o_ids);
+  p->pos = reinterpret_cast<int32_t*>(dv + o_pos);
+  p->q_row = reinterpret_cast<int32_t*>(dv + o_qrow);
+  p->opt_off = reinterpret_cast<int32_t*>(dv + o_off);
+  p->opt_ids = reinterpret_cast<int32_t*>(dv + o_opt);
+  p->q_type = reinterpret_cast<uint8_t*>(dv + o_qt);
+  for (int ps = 0; ps < 2; ++ps) {
+    p->pass[ps].scan = reinterpret_cast<ScanSeq*>(dv + o_scan[ps]);
+    p->pass[ps].attn = reinterpret_cast<AttnSeq*>(dv + o_attn[ps]);
+    p->pass[ps].blocks = reinterpret_cast<AttnBlock*>(dv + o_blk[ps]);
+    p->pass[ps].n_blocks = (int)blocks[ps].size();
+  }
+  *out = p;
+  return S1_OK;
+}
+
+int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
+  if (p->cap_dev) {
+    (void)hipFree(p->cap_dev);
+    p->cap_dev = nullptr;
+  }
+  p->n_cap = 0;
+  p->cap_out = nullptr;
+  for (auto& ps : p->pass) ps.n_cap = 0;
+  if (n_rows <= 0) return S1_OK;
+  if (rows == nullptr || d_hidden == nullptr) return set_error(S1_EINVAL, "capture rows or buffer is NULL");
+  std::vector<int32_t> lists[2][2];   // [pass][rows | dst]
+  for (int j = 0; j < n_rows; ++j) {
+    if (rows[j] < 0 || rows[j] >= p->T) return set_error(S1_EINVAL, "capture row out of range");
+    const int r = p->row_of[rows[j]];
+    const int ps = p->pass_of_row[r];
+    lists[ps][0].push_back(r);
+    lists[ps][1].push_back(j);
+  }
+  if (hipMalloc(&p->cap_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "device allocation for capture failed");
+  }
+  int32_t* d = static_cast<int32_t*>(p->cap_dev);
+  for (int ps = 0; ps < 2; ++ps) {
+    const int k = (int)lists[ps][0].size();
+    if (k) {
+      if (hipMemcpy(d, lists[ps][0].data(), 4 * k, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(d + k, lists[ps][1].data(), 4 * k, hipMemcpyHostToDevice) != hipSuccess)
+        return set_error(S1_EDEVICE, "copy capture rows");
+    }
+    p->pass[ps].cap_rows = d;
+    p->pass[ps].cap_dst = d + k;
+    p->pass[ps].n_cap = k;
+    d += 2 * k;
+  }
+  p->n_cap = n_rows;
+  p->cap_out = d_hidden;
+  return S1_OK;
+}
+
+// ---------------------------------------------------------------- forward
+#define MARK(cls)                            \
+  do {                                       \
+    if (m->prof) m->prof->mark((cls), s);    \
+  } while (0)
+
+namespace {
+
+int choose_split(const Model* m, int M, int N, int K) {
+  if (M > m->split_max_rows) return 1;
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int split = 1;
+  while (split < 4 && tiles * (split + 1) <= 320 && K / (64 * (split + 1)) >= 4) ++split;
+  return split;
+}
+
+int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
+  const s1_config& c = m->cfg;
+  const int d = c.d_model, H = c.la_heads, dk = c.la_dk, dv = c.la_dv;
+  const int Hq = c.fa_q_heads, Hkv = c.fa_kv_heads, hd = c.fa_head_dim;
+  const int T = ps.T, r0 = ps.r0;
+  if (T == 0) return S1_OK;
+  const size_t es = m->esz;
+  char* xn = static_cast<char*>(m->xn) + (size_t)r0 * d * es;
+  float* x = m->x + (size_t)r0 * d;
+  char* qkv = static_cast<char*>(m->qkv);
+  char* att = static_cast<char*>(m->att);
+  const long long kvld = (long long)Hkv * hd;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = m->layers[l];
+    S1_TRY(launch_rmsnorm(m->bf16, x, L.attn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+    MARK(KC_RMSNORM);
+    GemmArgs g{};
+    g.A = xn;
+    g.M = T;
+    g.K = d;
+    g.lda = d;
+    g.ldw = d;
+    g.W = L.w_in;
+    g.N = L.n_in;
+    if (!L.full) {
+      g.out0 = qkv + (size_t)r0 * m->ld_qkv * es;
+      g.ld0 = m->ld_qkv;
+      g.out1 = m->lg + (size_t)r0 * H;
+      g.ld1 = H;
+      g.nsplit = 2 * H * dk + H * dv;
+      S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s), "linear-attention in-projection");
+      MARK(KC_GEMM_LA_IN);
+      float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
+      S1_TRY(launch_scan(m->bf16, qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es,
+                         m->ld_qkv, m->lg, H, att, m->ld_att, ps.scan, ps.n_seqs, states, H, dk, dv, s),
+             "linear-attention scan");
+      MARK(KC_LA_SCAN);
+    } else {
+      char* kc = static_cast<char*>(m->kc) + (size_t)L.fa_idx * c.max_tokens * kvld * es;
+      char* vc = static_cast<char*>(m->vc) + (size_t)L.fa_idx * c.max_tokens * kvld * es;
+      g.out0 = qkv + (size_t)r0 * m->ld_qkv * es;
+      g.ld0 = m->ld_qkv;
+      g.out1 = kc + (size_t)r0 * kvld * es;
+      g.ld1 = (int)kvld;
+      g.out2 = vc + (size_t)r0 * kvld * es;
+      g.ld2 = (int)kvld;
+      g.nsplit = Hq * hd;
+      g.nsplit2 = (Hq + Hkv) * hd;
+      g.head_dim = hd;
+      g.pos = p->pos + r0;
+      g.rope = m->rope;
+      S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s), "attention QKV projection");
+      MARK(KC_GEMM_FA_QKV);
+      S1_TRY(launch_attention(m->bf16, qkv, m->ld_qkv, kc, vc, (int)kvld, att, m->ld_att, ps.attn,
+                              ps.blocks, ps.n_blocks, Hq, Hkv, hd, s),
+             "attention");
+      MARK(KC_ATTENTION);
+    }
+    GemmArgs go{};
+    go.A = att + (size_t)r0 * m->ld_att * es;
+    go.lda = m->ld_att;
+    go.W = L.w_o;
+    go.ldw = L.k_o;
+    go.M = T;
+    go.N = d;
+    go.K = L.k_o;
+    go.out0 = x;
+    go.ld0 = d;
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, choose_split(m, T, d, L.k_o), m->splitws, s),
+           "mixer out-projection");
+    MARK(KC_GEMM_O);
+    S1_TRY(launch_rmsnorm(m->bf16, x, L.ffn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+    MARK(KC_RMSNORM);
+    GemmArgs gu{};
+    gu.A = xn;
+    gu.lda = d;
+    gu.W = L.w_gu;
+    gu.ldw = d;
+    gu.M = T;
+    gu.N = L.n_gu;
+    gu.K = d;
+    gu.out0 = static_cast<char*>(m->hbuf) + (size_t)r0 * c.ffn * es;
+    gu.ld0 = c.ffn;
+    gu.n_valid = c.ffn;
+    S1_TRY(launch_gemm(m->bf16, EPI_SWIGLU, gu, 1, nullptr, s), "FFN gate/up");
+    MARK(KC_GEMM_GATE_UP);
+    GemmArgs gd{};
+    gd.A = gu.out0;
+    gd.lda = c.ffn;
+    gd.W = L.w_down;
+    gd.ldw = c.ffn;
+    gd.M = T;
+    gd.N = d;
+    gd.K = c.ffn;
+    gd.out0 = x;
+    gd.ld0 = d;
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, choose_split(m, T, d, c.ffn), m->splitws, s),
+           "FFN down");
+    MARK(KC_GEMM_DOWN);
+    if (ps.n_cap) {
+      S1_TRY(launch_gather_rows(m->x, d, ps.cap_rows, ps.cap_dst, ps.n_cap,
+                                p->cap_out + (size_t)(l + 1) * p->n_cap * d, s),
+             "capture");
+      MARK(KC_CAPTURE);
+    }
+  }
+  return S1_OK;
+}
+
+}  // namespace
+
+int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
+  const s1_config& c = m->cfg;
+  if (p->T == 0) return S1_OK;
+  if (m->prof) m->prof->begin(s);
+  S1_TRY(launch_embed(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, s), "embedding");
+  MARK(KC_EMBED);
+  for (int ps = 0; ps < p->n_passes; ++ps)
+    if (p->pass[ps].n_cap)
+      S1_TRY(launch_gather_rows(m->x, c.d_model, p->pass[ps].cap_rows, p->pass[ps].cap_dst,
+                                p->pass[ps].n_cap, p->cap_out, s),
+             "capture");
+  for (int ps = 0; ps < p->n_passes; ++ps) {
+    const int rc = run_pass(m, p, p->pass[ps], s);
+    if (rc) return rc;
+  }
+  if (p->Q > 0)
+    S1_TRY(launch_readout(m->bf16, m->x, c.d_model, m->final_norm, c.rms_eps, m->embed, p->Q, p->q_row,
+                          p->opt_off, p->opt_ids, p->q_type, d_probs, d_dec, p->max_k, s),
+           "readout");
+  if (p->Q > 0) MARK(KC_READOUT);
+  return S1_OK;
+}
+
+}  // namespace s1

@@ -1,0 +1,126 @@
+// Host-side model and plan structures of the library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/s1.h"
+#include "kernels.h"
+
+namespace s1 {
+
+// Thread-local error reporting for the C ABI.
+int set_error(int code, const std::string& msg);
+std::string hip_msg(hipError_t e, const char* what);
+
+struct LayerW {
+  bool full = false;
+  int la_idx = -1, fa_idx = -1;
+  float* attn_norm = nullptr;   // fp32 [d]
+  float* ffn_norm = nullptr;    // fp32 [d]
+  void* w_in = nullptr;         // LA: [q | k | v | g] rows; FA: [q | k | v], q/k rows RoPE-permuted
+  int n_in = 0;
+  void* w_o = nullptr;          // [d, heads * head_dim]
+  int k_o = 0;
+  void* w_gu = nullptr;         // gate/up interleaved in blocks of 32 rows, [2 * ffn_pad, d]
+  int n_gu = 0;
+  void* w_down = nullptr;       // [d, ffn]
+};
+
+// Kernel families timed by s1_plan_profile.
+enum KernelClass {
+  KC_EMBED = 0, KC_RMSNORM, KC_GEMM_LA_IN, KC_LA_SCAN, KC_GEMM_FA_QKV, KC_ATTENTION, KC_GEMM_O,
+  KC_GEMM_GATE_UP, KC_GEMM_DOWN, KC_CAPTURE, KC_READOUT, KC_COUNT
+};
+const char* kernel_class_name(int c);
+
+// Events recorded after each launch while profiling.
+struct Profiler {
+  std::vector<hipEvent_t> ev;
+  std::vector<int> cls;
+  int used = 0;
+  bool overflow = false;
+  ~Profiler();
+  int reserve(int n);
+  void begin(hipStream_t s);
+  void mark(int c, hipStream_t s);
+};
+
+struct Model {
+  s1_config cfg{};
+  bool bf16 = true;
+  size_t esz = 2;
+  int device = 0;
+  hipStream_t own_stream = nullptr;
+  int ffn_pad = 0;
+  int n_la = 0, n_fa = 0;
+
+  void* embed = nullptr;        // [V, d]
+  float* final_norm = nullptr;  // fp32 [d]
+  std::vector<LayerW> layers;
+  float2* rope = nullptr;       // [max_positions, head_dim / 2]
+
+  // workspace, sized for cfg budgets
+  float* x = nullptr;           // residual stream fp32 [T, d]
+  void* xn = nullptr;           // normalised activations [T, d]
+  void* qkv = nullptr;          // LA: q | k | v; FA: q          [T, ld_qkv]
+  int ld_qkv = 0;
+  float* lg = nullptr;          // log decay gate fp32 [T, H]
+  void* att = nullptr;          // mixer output [T, ld_att]
+  int ld_att = 0;
+  void* hbuf = nullptr;         // SwiGLU output [T, ffn]
+  void* kc = nullptr;           // [n_fa][T][Hkv * hd]
+  void* vc = nullptr;
+  float* states = nullptr;      // [n_la][max_prefixes][H][dk][dv] fp32
+  float* splitws = nullptr;     // split-K partials
+  long long splitws_elems = 0;
+  int split_max_rows = 0;
+
+  Profiler* prof = nullptr;     // set only during s1_plan_profile
+  std::vector<void*> allocs;
+  ~Model();
+  void* alloc(size_t bytes);    // throws std::bad_alloc on failure
+};
+
+struct PassPlan {
+  int r0 = 0, T = 0;
+  int n_seqs = 0;
+  ScanSeq* scan = nullptr;      // device [n_seqs]
+  AttnSeq* attn = nullptr;      // device [n_seqs]
+  AttnBlock* blocks = nullptr;  // device [n_blocks]
+  int n_blocks = 0;
+  int32_t* cap_rows = nullptr;  // device [n_cap]: rows captured in this pass
+  int32_t* cap_dst = nullptr;   // device [n_cap]: index in the capture list
+  int n_cap = 0;
+};
+
+struct Plan {
+  Model* m = nullptr;
+  int T = 0, n_seqs = 0, Q = 0, total_opts = 0, max_k = 0;
+  int n_passes = 0;
+  PassPlan pass[2];
+  int32_t* ids = nullptr;       // device [T] (internal row order)
+  int32_t* pos = nullptr;       // device [T]
+  int32_t* q_row = nullptr;     // device [Q]
+  int32_t* opt_off = nullptr;   // device [Q + 1]
+  int32_t* opt_ids = nullptr;   // device [sum K]
+  uint8_t* q_type = nullptr;    // device [Q]
+  std::vector<int> row_of;      // caller packed row -> internal row
+  std::vector<int> pass_of_row; // internal row -> pass
+  float* cap_out = nullptr;     // device [(n_layers + 1) * n_cap * d]
+  int n_cap = 0;
+  void* dev = nullptr;          // one device block for the arrays above
+  void* cap_dev = nullptr;      // device block for capture row lists
+  ~Plan();
+};
+
+int validate_config(const s1_config* c);
+int validate_batch(const s1_config* c, const s1_batch* b);
+int load_model(const s1_config* cfg, const s1_tensor* t, int n, hipStream_t s, Model** out);
+int create_plan(Model* m, const s1_batch* b, Plan** out);
+int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
+int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden);
+
+}  // namespace s1

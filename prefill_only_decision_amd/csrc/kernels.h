@@ -1,0 +1,103 @@
+// Host-side launch interface of the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s1 {
+
+// ---------------------------------------------------------------- GEMM
+// C = A[M,K] x W[N,K]^T with a fused epilogue.
+enum Epi {
+  EPI_F32 = 0,   // out0 fp32 [M, ld0]
+  EPI_RESID,     // out0 fp32 [M, ld0] += C            (residual add)
+  EPI_GATE,      // cols < nsplit: out0 elem [M, ld0]; cols >= nsplit:
+                 //   out1 fp32 [M, ld1] = log(sigmoid(C))   (decay gate)
+  EPI_SWIGLU,    // column groups of 64 = [32 gate | 32 up]:
+                 //   out0 elem [M, ld0][f] = silu(gate) * up, f < n_valid
+  EPI_QKV,       // cols < nsplit: q (rope) -> out0; < nsplit2: k (rope) ->
+                 //   out1; else v -> out2.  Head dims permuted (see executor)
+  EPI_PARTIAL,   // out0 fp32 slab per K split (split-K partial sums)
+  EPI_COUNT
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* W;
+  int M, N, K;
+  int lda, ldw;          // row strides in elements
+  int k_split;           // K elements per split (multiple of the K tile)
+  void* out0;
+  void* out1;
+  void* out2;
+  int ld0, ld1, ld2;
+  int nsplit, nsplit2;
+  int n_valid;
+  int head_dim;
+  const int* pos;        // EPI_QKV: position of each row
+  const float2* rope;    // EPI_QKV: (cos, sin) [max_pos][head_dim / 2]
+  long long split_stride;  // EPI_PARTIAL: elements between split slabs
+};
+
+// Runs the GEMM; for epilogues other than EPI_F32 / EPI_RESID split must be
+// 1.  With split > 1 (EPI_F32 or EPI_RESID) partial tiles go to `ws`
+// (split * M * N floats) and a reduction kernel applies the epilogue.
+hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
+                       hipStream_t s);
+// The K tile (elements) of the GEMM for the given element type.
+int gemm_k_tile(bool bf16);
+
+// ------------------------------------------------------------ elementwise
+hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
+                        hipStream_t s);
+hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
+                          float eps, hipStream_t s);
+// out[dst_row(o)] = W[o] + scale * B[o] A ; row_map may be NULL (identity);
+// dst rows are out_ld elements apart.  W, A, B may be fp32 or bf16 (same as
+// out); A == NULL means no adapter.
+hipError_t launch_merge(bool bf16, const void* W, const void* A, const void* B, void* out,
+                        int out_dim, int in_dim, int rank, float scale, const int* row_map,
+                        hipStream_t s);
+hipError_t launch_to_f32(bool bf16, const void* in, float* out, long long n, hipStream_t s);
+hipError_t launch_rope_table(float2* table, int max_pos, int head_dim, double base,
+                             hipStream_t s);
+// out[dst[j]] = x[rows[j]] for j < n_rows (rows of d floats); dst may be NULL.
+hipError_t launch_gather_rows(const float* x, int d, const int32_t* rows, const int32_t* dst,
+                              int n_rows, float* out, hipStream_t s);
+
+// ------------------------------------------------------------------- scan
+struct ScanSeq {
+  int row0;   // first row (in the q/k/v/o/log_g arrays)
+  int len;
+  int s_in;   // initial state slot, or -1 (zero)
+  int s_out;  // final state slot, or -1
+};
+hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
+                       const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
+                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s);
+
+// -------------------------------------------------------------- attention
+struct AttnSeq {
+  int q_row0;       // first query row (q and o arrays)
+  int len;          // queries (= own keys)
+  int kv_row0;      // first own key row (k, v arrays)
+  int kv_pre_row0;  // first prefix key row
+  int kv_pre_len;   // prefix keys (positions 0 ..); queries start at this position
+};
+struct AttnBlock {
+  int seq;
+  int q0;           // first query (within the sequence) of this block
+};
+int attn_block_rows(bool bf16);   // queries per workgroup
+hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, const void* v,
+                            int ld_kv, void* o, int ld_o, const AttnSeq* seqs,
+                            const AttnBlock* blocks, int n_blocks, int Hq, int Hkv, int hd,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------- readout
+hipError_t launch_readout(bool bf16, const float* x, int d, const float* w_final, float eps,
+                          const void* E, int Q, const int32_t* rows, const int32_t* opt_offsets,
+                          const int32_t* opt_ids, const uint8_t* q_type, float* probs,
+                          void* decisions, int max_k, hipStream_t s);
+
+}  // namespace s1

@@ -1,0 +1,304 @@
+// Chunked gated linear-attention scan (the recurrence S_t = g_t S_{t-1} +
+// k_t v_t^T, o_t = S_t^T q_t, one scalar gate per token and head; the pages
+// name Gated DeltaNet without printing its equations, and this is the stated
+// stand-in).  The state stays fp32 (RFC #114 section 5: FP32 recurrent state;
+// a branch starts from its prefix's final state).
+//
+// Chunks of C = 64 tokens are processed in order; inside a chunk, with
+// G_t = sum_{r <= t} log g_r (chunk-local),
+//   O = (QK^T . D) V + diag(exp G) Q S0,   D[t][s] = exp(G_t - G_s) for s <= t
+//   S = exp(G_last) S0 + (K . exp(G_last - G))^T V
+// Decays are always exponentials of differences, never ratios of products.
+// All four products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+// the state lives in accumulator registers across chunks.  A wave owns 32
+// value columns of one head; NW waves share the chunk's Q, K, K^T and V^T
+// tiles in LDS.  The intra-chunk score tile is computed as K Q^T so that its
+// accumulator layout is directly the A operand of (QK^T . D) V, and the state
+// accumulator layout is directly the B operand of Q S0: both use the same
+// permutation of the contraction index, which Q and V^T are read with.
+#include "common.h"
+#include "kernels.h"
+
+namespace s1 {
+
+namespace {
+
+constexpr int C = 64, DK = 128, DV = 128;
+constexpr int QP = DK * 2 + 16;   // bytes per Q / K row in LDS
+constexpr int TP = C * 2 + 16;    // bytes per K^T / V^T row in LDS
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                 const bf16_t* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
+                 bf16_t* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
+                 float* __restrict__ states, int H) {
+  constexpr int NT = NW * 64;
+  constexpr int DVG = 32 * NW;        // value columns per workgroup
+  constexpr int NDVG = DV / DVG;      // workgroups per (sequence, head)
+  __shared__ __attribute__((aligned(16))) char sQ[C * QP];
+  __shared__ __attribute__((aligned(16))) char sK[C * QP];
+  __shared__ __attribute__((aligned(16))) char sKt[DK * TP];
+  __shared__ __attribute__((aligned(16))) char sVt[DVG * TP];
+  __shared__ float sG[C];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane >> 5, cl = lane & 31;
+  const int seq = blockIdx.x / NDVG, dvg = blockIdx.x % NDVG, h = blockIdx.y;
+  const ScanSeq sq = seqs[seq];
+  const int dvw = dvg * DVG;          // first value column of the workgroup
+  const int dv0 = dvw + wave * 32;    // first value column of this wave
+
+  floatx16 S[DK / 32];                // S[a][r] = S[32a + acc_row(r)][dv0 + cl]
+#pragma unroll
+  for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      S[a][r] = sq.s_in >= 0
+                    ? states[(((long long)sq.s_in * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl]
+                    : 0.f;
+
+  for (int c0 = 0; c0 < sq.len; c0 += C) {
+    const int n = min(C, sq.len - c0);
+    const long long base = (long long)sq.row0 + c0;
+    // chunk-local cumulative log-gate, redundantly in every wave
+    float G = lane < n ? lg[(base + lane) * ldg + h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_up(G, off, 64);
+      if (lane >= off) G += t;
+    }
+    const float Glast = __shfl(G, 63, 64);
+    const float wK = __expf(Glast - G);   // decay from token `lane` to the chunk end
+
+    __syncthreads();                      // previous chunk's reads of LDS are done
+    if (wave == 0) sG[lane] = G;
+    // Q rows: straight copy
+    for (int c = tid; c < C * 16; c += NT) {
+      const int s = c >> 4, ch = c & 15;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (s < n) val = *reinterpret_cast<const uint4*>(q + (base + s) * ldqkv + h * DK + ch * 8);
+      *reinterpret_cast<uint4*>(sQ + s * QP + ch * 16) = val;
+    }
+    // K rows (row-major copy) and K^T scaled by the decay to the chunk end
+    for (int c = tid; c < (C / 2) * 16; c += NT) {
+      const int p = c >> 4, ch = c & 15, s0 = 2 * p, s1 = s0 + 1;
+      uint4 ka = make_uint4(0, 0, 0, 0), kb = make_uint4(0, 0, 0, 0);
+      if (s0 < n) ka = *reinterpret_cast<const uint4*>(k + (base + s0) * ldqkv + h * DK + ch * 8);
+      if (s1 < n) kb = *reinterpret_cast<const uint4*>(k + (base + s1) * ldqkv + h * DK + ch * 8);
+      *reinterpret_cast<uint4*>(sK + s0 * QP + ch * 16) = ka;
+      *reinterpret_cast<uint4*>(sK + s1 * QP + ch * 16) = kb;
+      const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
+      const uint32_t a[4] = {ka.x, ka.y, ka.z, ka.w}, b[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d0 = ch * 8 + 2 * e;
+        const float alo = __uint_as_float(a[e] << 16), ahi = __uint_as_float(a[e] & 0xFFFF0000u);
+        const float blo = __uint_as_float(b[e] << 16), bhi = __uint_as_float(b[e] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = pack_bf2(alo * w0, blo * w1);
+        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = pack_bf2(ahi * w0, bhi * w1);
+      }
+    }
+    // V^T for this workgroup's value columns
+    for (int c = tid; c < (C / 2) * (DVG / 8); c += NT) {
+      const int p = c / (DVG / 8), ch = c % (DVG / 8), s0 = 2 * p, s1 = s0 + 1;
+      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+      const long long col = (long long)h * DV + dvw + ch * 8;
+      if (s0 < n) va = *reinterpret_cast<const uint4*>(v + (base + s0) * ldqkv + col);
+      if (s1 < n) vb = *reinterpret_cast<const uint4*>(v + (base + s1) * ldqkv + col);
+      const uint32_t a[4] = {va.x, va.y, va.z, va.w}, b[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d0 = ch * 8 + 2 * e;
+        *reinterpret_cast<uint32_t*>(sVt + d0 * TP + 4 * p) = (a[e] & 0xFFFFu) | (b[e] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + (d0 + 1) * TP + 4 * p) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+
+    // (a) score tiles A^T[s][t] = k_s . q_t for s-tile st <= t-tile tt
+    floatx16 At[3];   // (0,0), (0,1), (1,1)
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) At[x][r] = 0.f;
+      const char* kr = sK + (32 * st + cl) * QP + 16 * hi;
+      const char* qr = sQ + (32 * tt + cl) * QP + 16 * hi;
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks)
+        mfma32(At[x], as_frag(*reinterpret_cast<const uint4*>(kr + 32 * ks)),
+               as_frag(*reinterpret_cast<const uint4*>(qr + 32 * ks)));
+    }
+    // causal mask and decay exp(G_t - G_s), s <= t
+    const float Gt0 = sG[cl], Gt1 = sG[32 + cl];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
+      const int t = 32 * tt + cl;
+      const float Gt = tt ? Gt1 : Gt0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int s = 32 * st + acc_row(r, lane);
+        At[x][r] = s <= t ? At[x][r] * __expf(Gt - sG[s]) : 0.f;
+      }
+    }
+
+    // (b) O = (A . D) V + exp(G_t) Q S0 for both t-tiles
+    bf16x8 Sf[DK / 32][2];
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = S[a][8 * hf + e];
+        Sf[a][hf] = frag_from_f(sv);
+      }
+    const char* vrow = sVt + (wave * 32 + cl) * TP;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      floatx16 O1, O2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        O1[r] = 0.f;
+        O2[r] = 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st <= tt; ++st) {
+        const int x = tt == 0 ? 0 : (st == 0 ? 1 : 2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float av[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) av[e] = At[x][8 * hf + e];
+          const char* vp = vrow + (32 * st + 16 * hf + 4 * hi) * 2;
+          mfma32(O1, frag_from_f(av),
+                 frag_from_halves(*reinterpret_cast<const uint2*>(vp), *reinterpret_cast<const uint2*>(vp + 16)));
+        }
+      }
+      const char* qrow = sQ + (32 * tt + cl) * QP;
+#pragma unroll
+      for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const char* qp = qrow + (32 * a + 16 * hf + 4 * hi) * 2;
+          mfma32(O2, frag_from_halves(*reinterpret_cast<const uint2*>(qp), *reinterpret_cast<const uint2*>(qp + 16)),
+                 Sf[a][hf]);
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * tt + acc_row(r, lane);
+        if (t < n) {
+          const float val = O1[r] + __expf(sG[t]) * O2[r];
+          o[(base + t) * ldo + (long long)h * DV + dv0 + cl] = f2bf(val);
+        }
+      }
+    }
+
+    // (c) S = exp(G_last) S + (K . w)^T V
+    const float dec = __expf(Glast);
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[a][r] *= dec;
+      const char* kt = sKt + (32 * a + cl) * TP + 16 * hi;
+      const char* vt = vrow + 16 * hi;
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks)
+        mfma32(S[a], as_frag(*reinterpret_cast<const uint4*>(kt + 32 * ks)),
+               as_frag(*reinterpret_cast<const uint4*>(vt + 32 * ks)));
+    }
+  }
+
+  if (sq.s_out >= 0) {
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        states[(((long long)sq.s_out * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl] = S[a][r];
+  }
+}
+
+// fp32 path (small models): the recurrence token by token.  One workgroup
+// per (sequence, head); each thread owns state elements of one value column.
+__global__ void __launch_bounds__(256)
+scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                const float* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
+                float* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
+                float* __restrict__ states, int H, int dk, int dv) {
+  __shared__ float sq_[128], sk_[128], sv_[128], part[256];
+  __shared__ float sg;
+  const int tid = threadIdx.x, seq = blockIdx.x, h = blockIdx.y;
+  const ScanSeq sq = seqs[seq];
+  const int j = tid % dv, i0 = tid / dv, istep = 256 / dv, ni = dk / istep;
+  float Sr[128];
+  for (int u = 0; u < ni; ++u) {
+    const int i = i0 + u * istep;
+    Sr[u] = sq.s_in >= 0 ? states[(((long long)sq.s_in * H + h) * dk + i) * dv + j] : 0.f;
+  }
+  for (int t = 0; t < sq.len; ++t) {
+    const long long row = (long long)sq.row0 + t;
+    __syncthreads();
+    if (tid < dk) {
+      sq_[tid] = q[row * ldqkv + h * dk + tid];
+      sk_[tid] = k[row * ldqkv + h * dk + tid];
+    }
+    if (tid < dv) sv_[tid] = v[row * ldqkv + h * dv + tid];
+    if (tid == 0) sg = __expf(lg[row * ldg + h]);
+    __syncthreads();
+    float acc = 0.f;
+    const float g = sg, vj = sv_[j];
+    for (int u = 0; u < ni; ++u) {
+      const int i = i0 + u * istep;
+      Sr[u] = g * Sr[u] + sk_[i] * vj;
+      acc += Sr[u] * sq_[i];
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < dv) {
+      float s = 0.f;
+      for (int x = 0; x < istep; ++x) s += part[x * dv + tid];
+      o[row * ldo + h * dv + tid] = s;
+    }
+  }
+  if (sq.s_out >= 0)
+    for (int u = 0; u < ni; ++u) {
+      const int i = i0 + u * istep;
+      states[(((long long)sq.s_out * H + h) * dk + i) * dv + j] = Sr[u];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
+                       const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
+                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s) {
+  if (n_seqs <= 0 || H <= 0) return hipSuccess;
+  if (bf16) {
+    if (dk != DK || dv != DV) return hipErrorInvalidValue;
+    const long long chains = (long long)n_seqs * H;
+    const auto* qq = reinterpret_cast<const bf16_t*>(q);
+    const auto* kk = reinterpret_cast<const bf16_t*>(k);
+    const auto* vv = reinterpret_cast<const bf16_t*>(v);
+    auto* oo = reinterpret_cast<bf16_t*>(o);
+    if (chains >= 256)
+      hipLaunchKernelGGL(scan_bf16_kernel<4>, dim3(n_seqs * 1, H), dim3(256), 0, s, qq, kk, vv,
+                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
+    else if (chains >= 128)
+      hipLaunchKernelGGL(scan_bf16_kernel<2>, dim3(n_seqs * 2, H), dim3(128), 0, s, qq, kk, vv,
+                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
+    else
+      hipLaunchKernelGGL(scan_bf16_kernel<1>, dim3(n_seqs * 4, H), dim3(64), 0, s, qq, kk, vv,
+                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
+  } else {
+    if (dk > 128 || dv > 128 || 256 % dv != 0 || dk % (256 / dv) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scan_f32_kernel, dim3(n_seqs, H), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
+                       reinterpret_cast<const float*>(v), ld_qkv, log_g, ld_g,
+                       reinterpret_cast<float*>(o), ld_o, seqs, states, H, dk, dv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace s1

@@ -1,0 +1,146 @@
+"""C-ABI contract on the CPU: the library loads without a GPU, exports every
+function the headers declare, and rejects malformed requests with the right
+error code before any device work (host-only validation)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from s1_workloads import make_batch, shape_of
+from s1_workloads.batch import random_batch
+
+s1 = pytest.importorskip("prefill_only_decision_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return s1.load_library()
+    except RuntimeError as e:
+        pytest.fail(str(e))
+
+
+def _declared():
+    names = set()
+    for h in ("s1.h", "s1_kernels.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"\b(s1k?_[a-z_]+)\s*\(", src):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert len(declared) >= 15
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+    assert declared == set(s1.binding.EXPORTS)
+
+
+def test_free_null_is_noop(lib):
+    lib.s1_free(None)
+    lib.s1_plan_free(None)
+
+
+def _cfg(name="4b-single-512", **kw):
+    return s1.make_config(shape_of(name), **kw)
+
+
+def _mutate(b, **changes):
+    import copy
+    c = copy.deepcopy(b)
+    for k, v in changes.items():
+        setattr(c, k, v)
+    return c
+
+
+def _one_question(qtype, opts):
+    from s1_workloads import Batch
+    return Batch(cu_seqlens=np.array([0, 30], np.int32), token_ids=np.arange(30, dtype=np.int32),
+                 prefix_of=np.array([-1], np.int32), q_seq=np.array([0], np.int32),
+                 q_marker=np.array([29], np.int32), q_type=np.array([qtype], np.uint8),
+                 opt_offsets=np.array([0, len(opts)], np.int32), opt_ids=np.array(opts, np.int32))
+
+
+def test_valid_workloads_pass_validation():
+    for name, kw in (("tiny-fp32", {}), ("4b-single-512", {}),
+                     ("4b-varlen-16", dict(max_tokens=32768, max_positions=4096)),
+                     ("4b-branch-4096x20", dict(max_tokens=8192)),
+                     ("27b-single-1024", {})):
+        assert s1.validate(_cfg(name, **kw), make_batch(name)) == s1.binding.S1_OK, s1.binding.last_error()
+
+
+def test_empty_request_is_valid():
+    b = random_batch(4096, [], seed=1)
+    assert s1.validate(_cfg("tiny-fp32"), b) == 0
+
+
+@pytest.mark.parametrize("case,code,needle", [
+    ("k_lt_2", -1, "at least 2 options"),
+    ("noul_k3", -1, "exactly 2 options"),
+    ("marker_oob", -1, "marker outside"),
+    ("bad_type", -1, "question type"),
+    ("token_oob", -1, "token id out of range"),
+    ("option_oob", -1, "option id out of range"),
+    ("cu_decreasing", -1, "non-decreasing"),
+    ("cu_start", -1, "cu_seqlens[0]"),
+    ("too_many_tokens", -4, "max_tokens"),
+    ("too_many_options", -4, "max_options"),
+    ("prefix_chain", -1, "must not itself be a branch"),
+    ("prefix_self", -1, "is invalid"),
+    ("too_many_prefixes", -4, "max_prefixes"),
+    ("q_seq_oob", -1, "q_seq out of range"),
+])
+def test_validation_errors(case, code, needle):
+    cfg = _cfg("tiny-fp32", max_tokens=1024, max_options=16, max_prefixes=1)
+    b = random_batch(4096, [30, 20, 10], seed=5, questions_per_seq=[2, 1, 1])
+    if case == "k_lt_2":
+        b.opt_offsets = b.opt_offsets.copy()
+        b.opt_offsets[1:] = b.opt_offsets[1:] - (b.opt_offsets[1] - 1)
+        b.opt_offsets[0] = 0
+        b.opt_ids = b.opt_ids[-b.opt_offsets[-1]:] if b.opt_offsets[-1] > 0 else b.opt_ids
+    elif case == "noul_k3":
+        b = _one_question(2, [5, 6, 7])
+    elif case == "marker_oob":
+        b.q_marker = b.q_marker.copy()
+        b.q_marker[0] = 30
+    elif case == "bad_type":
+        b.q_type = b.q_type.copy()
+        b.q_type[0] = 3
+    elif case == "token_oob":
+        b.token_ids = b.token_ids.copy()
+        b.token_ids[5] = 4096
+    elif case == "option_oob":
+        b.opt_ids = b.opt_ids.copy()
+        b.opt_ids[0] = -1
+    elif case == "cu_decreasing":
+        b.cu_seqlens = np.array([0, 30, 20, 60], np.int32)
+    elif case == "cu_start":
+        b.cu_seqlens = b.cu_seqlens + 1
+    elif case == "too_many_tokens":
+        b = random_batch(4096, [1000, 100], seed=5)
+    elif case == "too_many_options":
+        b = _one_question(0, list(range(100, 120)))
+    elif case == "prefix_chain":
+        b.prefix_of = np.array([-1, 0, 1], np.int32)
+    elif case == "prefix_self":
+        b.prefix_of = np.array([-1, 1, -1], np.int32)
+    elif case == "too_many_prefixes":
+        b = random_batch(4096, [30, 20, 10, 5], seed=5, prefix_of=[-1, 0, -1, 2])
+    elif case == "q_seq_oob":
+        b.q_seq = b.q_seq.copy()
+        b.q_seq[0] = 3
+    rc = s1.validate(cfg, b)
+    assert rc == code, (rc, s1.binding.last_error())
+    assert needle in s1.binding.last_error()
+
+
+def test_bad_config_rejected():
+    cfg = _cfg("4b-single-512")
+    cfg.la_dk = 64
+    b = make_batch("4b-single-512")
+    assert s1.validate(cfg, b) == -1
+    assert "128" in s1.binding.last_error()

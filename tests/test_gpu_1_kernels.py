@@ -1,0 +1,291 @@
+"""Kernel-level parity: each HIP kernel family through its C-ABI entry point,
+against the oracle's building blocks on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from s1_workloads import f32_to_bf16_bits
+from tests.gpu_util import dev, dev_bits, host_bits, log, rel_l2, require_gpu, stream_ptr
+
+pytestmark = pytest.mark.gpu
+
+import prefill_only_decision_amd as s1  # noqa: E402
+from prefill_only_decision_amd import binding as B  # noqa: E402
+
+
+def _bits(rng, shape, scale=1.0):
+    return f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,split", [
+    (1, 64, 64, 1), (77, 130, 520, 1), (512, 6160, 2560, 1), (512, 2560, 9728, 3),
+    (1000, 2560, 2048, 2), (129, 19456, 2560, 1), (2048, 3072, 2560, 1),
+])
+def test_gemm_bf16(M, N, K, split):
+    torch = require_gpu()
+    log(f"gemm bf16 M={M} N={N} K={K} split={split}")
+    rng = np.random.default_rng([M, N, K])
+    A, W = _bits(rng, (M, K)), _bits(rng, (N, K), 0.05)
+    dA, dW = dev_bits(A), dev_bits(W)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.gemm(B.S1_BF16, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, split, stream_ptr())
+    torch.cuda.synchronize()
+    ref = O.bf16_bits_to_float(A) @ O.bf16_bits_to_float(W).T
+    C = dC.cpu().numpy()
+    assert np.isfinite(C).all()
+    assert rel_l2(C, ref) < 1e-5
+    assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 1408, 256), (100, 256, 688), (5, 772, 256)])
+def test_gemm_f32(M, N, K):
+    torch = require_gpu()
+    log(f"gemm f32 M={M} N={N} K={K}")
+    rng = np.random.default_rng([M, N, K, 32])
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dA, dW = dev(A), dev(W)
+    B.gemm(B.S1_F32, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, 1, stream_ptr())
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    assert rel_l2(dC.cpu().numpy(), ref) < 1e-5
+
+
+def test_gemm_split_is_deterministic():
+    torch = require_gpu()
+    rng = np.random.default_rng(9)
+    M, N, K = 512, 2560, 9728
+    dA, dW = dev_bits(_bits(rng, (M, K))), dev_bits(_bits(rng, (N, K), 0.05))
+    outs = []
+    for _ in range(3):
+        dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        B.gemm(B.S1_BF16, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, 3, stream_ptr())
+        torch.cuda.synchronize()
+        outs.append(dC.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("dtype", [B.S1_BF16, B.S1_F32])
+def test_rmsnorm_and_embed(dtype):
+    torch = require_gpu()
+    rng = np.random.default_rng(dtype + 3)
+    T, d, V = 37, 2560, 1000
+    x = (rng.standard_normal((T, d)) * 3).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    out = torch.empty((T, d), dtype=torch.int16 if dtype == B.S1_BF16 else torch.float32, device="cuda")
+    dx, dw = dev(x), dev(w)
+    B.rmsnorm(dtype, dx.data_ptr(), dw.data_ptr(), out.data_ptr(), T, d, 1e-6, stream_ptr())
+    torch.cuda.synchronize()
+    ref = O.rms_norm(x.astype(np.float64), w.astype(np.float64), 1e-6)
+    got = O.bf16_bits_to_float(host_bits(out)) if dtype == B.S1_BF16 else out.cpu().numpy()
+    tol = 2.0 ** -8 if dtype == B.S1_BF16 else 1e-6
+    assert (np.abs(got - ref) <= tol * np.abs(ref) + 1e-7).all()
+    # embedding gather is a copy: exact
+    if dtype == B.S1_BF16:
+        E = _bits(rng, (V, d), 0.02)
+        dE = dev_bits(E)
+        Ef = O.bf16_bits_to_float(E)
+    else:
+        Ef = (rng.standard_normal((V, d)) * 0.02).astype(np.float32)
+        dE = dev(Ef)
+    ids = rng.integers(0, V, T).astype(np.int32)
+    dx2 = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    dids = dev(ids)
+    B.embed(dtype, dids.data_ptr(), dE.data_ptr(), dx2.data_ptr(), T, d, stream_ptr())
+    torch.cuda.synchronize()
+    assert np.array_equal(dx2.cpu().numpy(), np.asarray(Ef)[ids].astype(np.float32))
+
+
+def test_lora_merge_bf16():
+    torch = require_gpu()
+    rng = np.random.default_rng(11)
+    out_dim, in_dim, r = 300, 2560, 32
+    W, A, Bm = _bits(rng, (out_dim, in_dim), 0.02), _bits(rng, (r, in_dim), 0.02), _bits(rng, (out_dim, r), 0.02)
+    dW, dA, dB = dev_bits(W), dev_bits(A), dev_bits(Bm)
+    dO = torch.empty((out_dim, in_dim), dtype=torch.int16, device="cuda")
+    B.lora_merge(B.S1_BF16, dW.data_ptr(), dA.data_ptr(), dB.data_ptr(), dO.data_ptr(), out_dim, in_dim, r,
+                 2.0, stream_ptr())
+    torch.cuda.synchronize()
+    got = host_bits(dO).astype(np.int64)
+    f = O.bf16_bits_to_float
+    ref = O.round_to_bf16_bits(O.lora_merge(f(W), f(A), f(Bm), 64.0, 32)).astype(np.int64)
+    diff = np.abs(got - ref)
+    assert diff.max() <= 1, diff.max()
+    assert (diff > 0).mean() < 1e-3
+    # no adapter: exact copy
+    B.lora_merge(B.S1_BF16, dW.data_ptr(), 0, 0, dO.data_ptr(), out_dim, in_dim, r, 2.0, stream_ptr())
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dO), W)
+
+
+def _scan_case(H, lens, seed, with_init=True):
+    torch = require_gpu()
+    rng = np.random.default_rng(seed)
+    T, dk = int(sum(lens)), 128
+    qkv = _bits(rng, (T, 3 * H * dk), 1.0)
+    lg = np.log(1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = len(lens)
+    s0 = (rng.standard_normal((n, H, dk, dk)) * 0.1).astype(np.float32) if with_init else None
+    d_qkv, d_lg = dev_bits(qkv), dev(lg)
+    d_o = torch.zeros((T, H * dk), dtype=torch.int16, device="cuda")
+    d_s0 = dev(s0) if with_init else None
+    d_sf = torch.zeros((n, H, dk, dk), dtype=torch.float32, device="cuda")
+    base = d_qkv.data_ptr()
+    B.la_scan(B.S1_BF16, base, base + 2 * H * dk, base + 4 * H * dk, 3 * H * dk, d_lg.data_ptr(),
+              d_o.data_ptr(), T, H, dk, dk, cu, d_s0.data_ptr() if with_init else None,
+              d_sf.data_ptr(), stream_ptr())
+    torch.cuda.synchronize()
+    o = O.bf16_bits_to_float(host_bits(d_o)).reshape(T, H, dk)
+    sf = d_sf.cpu().numpy()
+    qkvf = O.bf16_bits_to_float(qkv).reshape(T, 3, H, dk)
+    worst_o = worst_s = 0.0
+    for i in range(n):
+        a, b = cu[i], cu[i + 1]
+        ro, rs = O.la_scan_unrolled(qkvf[a:b, 0], qkvf[a:b, 1], qkvf[a:b, 2], np.exp(lg[a:b].astype(np.float64)),
+                                    s0[i].astype(np.float64) if with_init else None)
+        if b > a:
+            worst_o = max(worst_o, rel_l2(o[a:b], ro))
+        worst_s = max(worst_s, rel_l2(sf[i], rs))
+    log(f"scan H={H} lens={lens}: rel L2 o {worst_o:.2e} state {worst_s:.2e}")
+    assert worst_o < 1e-2 and worst_s < 1e-2
+
+
+@pytest.mark.parametrize("H,lens", [
+    (16, [1, 63, 64, 65, 200]),            # 80 chains: 1 wave per workgroup
+    (32, [130, 7, 64, 255]),               # 128 chains: 2 waves
+    (64, [1, 100, 64, 300]),               # 256 chains: 4 waves
+])
+def test_scan_bf16(H, lens):
+    _scan_case(H, lens, seed=H)
+
+
+def test_scan_bf16_zero_init_and_empty_sequence():
+    _scan_case(16, [0, 40, 0, 129], seed=5, with_init=False)
+
+
+def test_scan_f32():
+    torch = require_gpu()
+    rng = np.random.default_rng(21)
+    H, dk, lens = 4, 64, [1, 50, 77]
+    T = sum(lens)
+    qkv = rng.standard_normal((T, 3 * H * dk)).astype(np.float32)
+    lg = np.log(1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    s0 = rng.standard_normal((3, H, dk, dk)).astype(np.float32)
+    d_qkv, d_lg, d_s0 = dev(qkv), dev(lg), dev(s0)
+    d_o = torch.zeros((T, H * dk), dtype=torch.float32, device="cuda")
+    d_sf = torch.zeros_like(d_s0)
+    base = d_qkv.data_ptr()
+    B.la_scan(B.S1_F32, base, base + 4 * H * dk, base + 8 * H * dk, 3 * H * dk, d_lg.data_ptr(), d_o.data_ptr(),
+              T, H, dk, dk, cu, d_s0.data_ptr(), d_sf.data_ptr(), stream_ptr())
+    torch.cuda.synchronize()
+    q = qkv.reshape(T, 3, H, dk).astype(np.float64)
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        ro, rs = O.la_scan_recurrent(q[a:b, 0], q[a:b, 1], q[a:b, 2], np.exp(lg[a:b].astype(np.float64)),
+                                     s0[i].astype(np.float64))
+        assert rel_l2(d_o.cpu().numpy()[a:b].reshape(-1, H, dk), ro) < 1e-5
+        assert rel_l2(d_sf.cpu().numpy()[i], rs) < 1e-5
+
+
+def _attn_case(dtype, Hq, Hkv, hd, seqs, seed):
+    """seqs: list of (q_len, prefix_len)."""
+    torch = require_gpu()
+    rng = np.random.default_rng(seed)
+    Tq = sum(s[0] for s in seqs)
+    Tp = sum(s[1] for s in seqs)
+    Tkv = Tq + Tp
+    if dtype == B.S1_BF16:
+        q, k, v = _bits(rng, (Tq, Hq, hd)), _bits(rng, (Tkv, Hkv, hd)), _bits(rng, (Tkv, Hkv, hd))
+        dq, dk_, dv_ = dev_bits(q), dev_bits(k), dev_bits(v)
+        qf, kf, vf = (O.bf16_bits_to_float(a) for a in (q, k, v))
+        do = torch.zeros((Tq, Hq, hd), dtype=torch.int16, device="cuda")
+    else:
+        qf, kf, vf = (rng.standard_normal(s).astype(np.float32) for s in ((Tq, Hq, hd), (Tkv, Hkv, hd), (Tkv, Hkv, hd)))
+        dq, dk_, dv_ = dev(qf), dev(kf), dev(vf)
+        do = torch.zeros((Tq, Hq, hd), dtype=torch.float32, device="cuda")
+    q_row0, q_len, kv_row0, pre_row0, pre_len = [], [], [], [], []
+    rq, rp = 0, Tq
+    for (L, P) in seqs:
+        q_row0.append(rq); q_len.append(L); kv_row0.append(rq); pre_row0.append(rp); pre_len.append(P)
+        rq += L
+        rp += P
+    B.attention(dtype, dq.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), do.data_ptr(), Hq, Hkv, hd,
+                q_row0, q_len, kv_row0, pre_row0, pre_len, stream_ptr())
+    torch.cuda.synchronize()
+    got = O.bf16_bits_to_float(host_bits(do)) if dtype == B.S1_BF16 else do.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for i, (L, P) in enumerate(seqs):
+        if L == 0:
+            continue
+        a = q_row0[i]
+        kk = np.concatenate([kf[pre_row0[i]:pre_row0[i] + P], kf[a:a + L]]).astype(np.float64)
+        vv = np.concatenate([vf[pre_row0[i]:pre_row0[i] + P], vf[a:a + L]]).astype(np.float64)
+        ref = O.causal_attention(qf[a:a + L].astype(np.float64), kk, vv, P + np.arange(L), np.arange(P + L))
+        worst = max(worst, rel_l2(got[a:a + L], ref))
+    log(f"attention dtype={dtype} seqs={seqs}: rel L2 {worst:.2e}")
+    return worst
+
+
+@pytest.mark.parametrize("seqs", [
+    [(1, 0), (100, 0), (128, 0), (129, 0), (300, 0)],
+    [(64, 200), (1, 70), (130, 4096)],
+])
+def test_attention_bf16(seqs):
+    assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=len(seqs)) < 1e-2
+
+
+def test_attention_bf16_gqa5():
+    # 40 query heads over 8 kv heads (groups of 5)
+    assert _attn_case(B.S1_BF16, 40, 8, 128, [(200, 0), (33, 17)], seed=40) < 1e-2
+
+
+def test_attention_f32():
+    assert _attn_case(B.S1_F32, 4, 4, 64, [(1, 0), (70, 0), (20, 30)], seed=3) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [B.S1_BF16, B.S1_F32])
+def test_readout(dtype):
+    torch = require_gpu()
+    rng = np.random.default_rng(31 + dtype)
+    d, V, R = 2560, 1000, 20
+    x = (rng.standard_normal((R, d)) * 5).astype(np.float32)
+    w = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    if dtype == B.S1_BF16:
+        E = _bits(rng, (V, d), 0.02)
+        dE = dev_bits(E)
+        Ef = O.bf16_bits_to_float(E)
+    else:
+        Ef = (rng.standard_normal((V, d)) * 0.02).astype(np.float32)
+        dE = dev(Ef)
+    Q = 40
+    Ks = rng.integers(2, 41, Q)
+    types = rng.integers(0, 3, Q).astype(np.uint8)
+    Ks[types == 2] = 2
+    Ks[0], types[0] = 300, 0                       # one wide question
+    offs = np.concatenate([[0], np.cumsum(Ks)]).astype(np.int32)
+    ids = np.concatenate([rng.choice(V, k, replace=False) for k in Ks]).astype(np.int32)
+    ids[offs[5]:offs[6]] = ids[offs[5]]            # duplicate options: exact tie
+    rows = rng.integers(0, R, Q).astype(np.int32)
+    dx, dw = dev(x), dev(w)
+    drows, doffs, dids, dtypes = dev(rows), dev(offs), dev(ids), dev(types)
+    dp = torch.zeros(int(offs[-1]), dtype=torch.float32, device="cuda")
+    dd = torch.zeros((Q, 6), dtype=torch.float32, device="cuda")
+    B.readout(dtype, dx.data_ptr(), d, dw.data_ptr(), 1e-6, dE.data_ptr(), Q, drows.data_ptr(), doffs.data_ptr(),
+              dids.data_ptr(), dtypes.data_ptr(), dp.data_ptr(), dd.data_ptr(), stream_ptr())
+    torch.cuda.synchronize()
+    p = dp.cpu().numpy()
+    dec = dd.cpu().numpy().copy().view(np.uint8).view(s1.DECISION_DTYPE).reshape(Q)
+    for j in range(Q):
+        rp, f = O.readout(x[rows[j]].astype(np.float64), w.astype(np.float64),
+                          np.asarray(Ef, np.float64)[ids[offs[j]:offs[j + 1]]], 1e-6, int(types[j]))
+        assert np.abs(p[offs[j]:offs[j + 1]] - rp).max() < 1e-4
+        srt = np.sort(rp)
+        if srt[-1] - srt[-2] > 1e-4 or j == 5:
+            assert dec[j]["choice"] == f["choice"], j
+        for key in ("score", "noul", "answer_confidence", "confidence", "entropy_confidence"):
+            assert abs(float(dec[j][key]) - f[key]) < 1e-3 * max(1.0, abs(f[key])), (j, key)

@@ -166,6 +166,16 @@ def test_scan_continuation(P):
     np.testing.assert_allclose(Sb, S_full, rtol=1e-10, atol=1e-10)
 
 
+def test_scan_segmented_equals_recurrence():
+    q, k, v, g = _qkvg(1100, H=2, dk=5, dv=3)
+    S0 = rng.standard_normal((2, 5, 3))
+    o1, S1 = O.la_scan_recurrent(q, k, v, g, S0)
+    for seg in (1, 64, 512, 2000):
+        o2, S2 = O.la_scan_segmented(q, k, v, g, S0, segment=seg)
+        np.testing.assert_allclose(o2, o1, rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(S2, S1, rtol=1e-10, atol=1e-10)
+
+
 def test_scan_strong_decay_no_overflow():
     # gates ~0.02 over 2000 tokens: products underflow; differences must not
     q, k, v, _ = _qkvg(2000, H=1, dk=4, dv=4)
