@@ -257,9 +257,14 @@ class OracleModel:
     keep_decoded=True."""
 
     def __init__(self, shape, tensors, dtype=np.float64, lora="merged",
-                 keep_decoded=False, threads=0):
+                 keep_decoded=False, threads=0, act="exact"):
         self.s = shape
         self.dtype = np.dtype(dtype)
+        # act="bf16": the operands of every matrix product the method runs in
+        # bf16 are bf16 values (see `_a`); act="exact": no activation rounding.
+        if act not in ("exact", "bf16"):
+            raise ValueError(act)
+        self.act = act
         self.lora = lora
         self.bf16 = shape.dtype == "bf16"
         self.keep = keep_decoded
@@ -303,6 +308,20 @@ class OracleModel:
             self._dec[name] = w
         return w
 
+    def _a(self, x):
+        """Activation operand of a bf16 matrix product.  The pages fix the
+        method's precision as BF16 inference ([rfc114] section 1; [cua-issue]
+        timing comments, bfloat16) with an FP32 recurrent state ([rfc114]
+        section 5) and an FP32 head ([rfc114-plan]).  In act="bf16" mode the
+        operands of the bf16 matrix products -- the input of every projection
+        (normalised activations, mixer output, SwiGLU output) and the q, k, v
+        operands of attention and of the recurrence -- are rounded to bf16
+        (nearest, ties to even); accumulation, norms, the residual stream, the
+        state, the softmax and the readout stay in the oracle's float type."""
+        if self.act != "bf16":
+            return x
+        return bf16_bits_to_float(round_to_bf16_bits(x), x.dtype)
+
     def proj(self, name, u):
         """u W^T, with the LoRA term added at run time in unmerged mode."""
         y = u @ self.W(name).T
@@ -320,22 +339,24 @@ class OracleModel:
         s = self.s
         T = u.shape[0]
         p = f"layers.{l}.la"
-        q = self.proj(p + ".q", u).reshape(T, s.la_heads, s.la_dk)
-        k = self.proj(p + ".k", u).reshape(T, s.la_heads, s.la_dk)
-        v = self.proj(p + ".v", u).reshape(T, s.la_heads, s.la_dv)
+        u = self._a(u)
+        q = self._a(self.proj(p + ".q", u).reshape(T, s.la_heads, s.la_dk))
+        k = self._a(self.proj(p + ".k", u).reshape(T, s.la_heads, s.la_dk))
+        v = self._a(self.proj(p + ".v", u).reshape(T, s.la_heads, s.la_dv))
         g = sigmoid(self.proj(p + ".g", u))           # (R2) one gate per head
         o, S = la_scan_segmented(q, k, v, g, S0)
-        return self.proj(p + ".o", o.reshape(T, s.la_heads * s.la_dv)), S
+        return self.proj(p + ".o", self._a(o.reshape(T, s.la_heads * s.la_dv))), S
 
     def _full(self, l, u, pos, prefix):
         s = self.s
         T = u.shape[0]
         p = f"layers.{l}.fa"
-        q = rope_rotate_half(self.proj(p + ".q", u).reshape(T, s.fa_q_heads, s.fa_head_dim),
-                             pos, s.rope_base)
-        k = rope_rotate_half(self.proj(p + ".k", u).reshape(T, s.fa_kv_heads, s.fa_head_dim),
-                             pos, s.rope_base)
-        v = self.proj(p + ".v", u).reshape(T, s.fa_kv_heads, s.fa_head_dim)
+        u = self._a(u)
+        q = self._a(rope_rotate_half(self.proj(p + ".q", u).reshape(T, s.fa_q_heads, s.fa_head_dim),
+                                     pos, s.rope_base))
+        k = self._a(rope_rotate_half(self.proj(p + ".k", u).reshape(T, s.fa_kv_heads, s.fa_head_dim),
+                                     pos, s.rope_base))
+        v = self._a(self.proj(p + ".v", u).reshape(T, s.fa_kv_heads, s.fa_head_dim))
         if prefix is not None:
             pk, pv, ppos = prefix
             k = np.concatenate([pk, k], axis=0)
@@ -344,7 +365,7 @@ class OracleModel:
         else:
             kpos = pos
         o = causal_attention(q, k, v, pos, kpos)
-        return self.proj(p + ".o", o.reshape(T, s.fa_q_heads * s.fa_head_dim)), (k, v, kpos)
+        return self.proj(p + ".o", self._a(o.reshape(T, s.fa_q_heads * s.fa_head_dim))), (k, v, kpos)
 
     # -- forward ---------------------------------------------------------
     def forward(self, ids, start_pos=0, cache=None, want_cache=False, capture_rows=None,
@@ -384,9 +405,10 @@ class OracleModel:
         return x, hidden, (out_cache if want_cache else None)
 
     def _ffn(self, f, v):
+        v = self._a(v)
         a = self.proj(f + ".gate", v)
         b = self.proj(f + ".up", v)
-        return self.proj(f + ".down", a * sigmoid(a) * b)
+        return self.proj(f + ".down", self._a(a * sigmoid(a) * b))
 
     def decide(self, x_row, qtype, option_ids):
         e = self.embed(option_ids)

@@ -44,6 +44,22 @@ __device__ __forceinline__ bf16x8 frag_from_f(const float* v) {
   u.w = pack_bf2(v[6], v[7]);
   return as_frag(u);
 }
+// Split eight floats into hi + lo bf16 operands with v = hi + lo up to
+// 2^-16 relative: hi = rne(v), lo = rne(v - hi) (the difference is exact).
+__device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& lo) {
+  float r[8];
+  uint32_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16_t a = f2bf(v[2 * e]), b = f2bf(v[2 * e + 1]);
+    h[e] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+    r[2 * e] = v[2 * e] - bf2f(a);
+    r[2 * e + 1] = v[2 * e + 1] - bf2f(b);
+  }
+  hi = as_frag(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = frag_from_f(r);
+}
+
 // Two 8-byte halves (4 bf16 each) -> one operand.
 __device__ __forceinline__ bf16x8 frag_from_halves(uint2 a, uint2 b) {
   return as_frag(make_uint4(a.x, a.y, b.x, b.y));

@@ -10,7 +10,10 @@
 //   S = exp(G_last) S0 + (K . exp(G_last - G))^T V
 // Decays are always exponentials of differences, never ratios of products.
 // All four products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
-// the state lives in accumulator registers across chunks.  A wave owns 32
+// the state lives in accumulator registers across chunks.  q, k, v arrive as
+// bf16; the operands formed inside the kernel (decayed scores, the state,
+// decayed keys) are split into hi + lo bf16 parts and multiplied twice, so
+// the scan adds no rounding beyond fp32 accumulation to its bf16 inputs.  A wave owns 32
 // value columns of one head; NW waves share the chunk's Q, K, K^T and V^T
 // tiles in LDS.  The intra-chunk score tile is computed as K Q^T so that its
 // accumulator layout is directly the A operand of (QK^T . D) V, and the state
@@ -38,7 +41,8 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int NDVG = DV / DVG;      // workgroups per (sequence, head)
   __shared__ __attribute__((aligned(16))) char sQ[C * QP];
   __shared__ __attribute__((aligned(16))) char sK[C * QP];
-  __shared__ __attribute__((aligned(16))) char sKt[DK * TP];
+  __shared__ __attribute__((aligned(16))) char sKt[DK * TP];     // decayed K^T, hi part
+  __shared__ __attribute__((aligned(16))) char sKl[DK * TP];     // decayed K^T, lo part
   __shared__ __attribute__((aligned(16))) char sVt[DVG * TP];
   __shared__ float sG[C];
 
@@ -93,10 +97,14 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d0 = ch * 8 + 2 * e;
-        const float alo = __uint_as_float(a[e] << 16), ahi = __uint_as_float(a[e] & 0xFFFF0000u);
-        const float blo = __uint_as_float(b[e] << 16), bhi = __uint_as_float(b[e] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = pack_bf2(alo * w0, blo * w1);
-        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = pack_bf2(ahi * w0, bhi * w1);
+        // element d0 of tokens s0, s1 and element d0 + 1 of both
+        const float x00 = __uint_as_float(a[e] << 16) * w0, x01 = __uint_as_float(b[e] << 16) * w1;
+        const float x10 = __uint_as_float(a[e] & 0xFFFF0000u) * w0, x11 = __uint_as_float(b[e] & 0xFFFF0000u) * w1;
+        const bf16_t h00 = f2bf(x00), h01 = f2bf(x01), h10 = f2bf(x10), h11 = f2bf(x11);
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h00 | ((uint32_t)h01 << 16);
+        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h10 | ((uint32_t)h11 << 16);
+        *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) = pack_bf2(x00 - bf2f(h00), x01 - bf2f(h01));
+        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) = pack_bf2(x10 - bf2f(h10), x11 - bf2f(h11));
       }
     }
     // V^T for this workgroup's value columns
@@ -145,7 +153,16 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
 
     // (b) O = (A . D) V + exp(G_t) Q S0 for both t-tiles
-    bf16x8 Sf[DK / 32][2];
+    floatx16 O1[2], O2[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        O1[tt][r] = 0.f;
+        O2[tt][r] = 0.f;
+      }
+    // Q S0: the state accumulator layout is the B operand, with the
+    // contraction index permuted as acc_row; Q is read with that permutation
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
@@ -153,48 +170,46 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[e] = S[a][8 * hf + e];
-        Sf[a][hf] = frag_from_f(sv);
+        bf16x8 shi, slo;
+        split_frag(sv, shi, slo);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const char* qp = sQ + (32 * tt + cl) * QP + (32 * a + 16 * hf + 4 * hi) * 2;
+          const bf16x8 qf = frag_from_halves(*reinterpret_cast<const uint2*>(qp),
+                                             *reinterpret_cast<const uint2*>(qp + 16));
+          mfma32(O2[tt], qf, shi);
+          mfma32(O2[tt], qf, slo);
+        }
       }
+    // (A . D) V: the score accumulator layout is the A operand
     const char* vrow = sVt + (wave * 32 + cl) * TP;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      floatx16 O1, O2;
+    for (int x = 0; x < 3; ++x) {
+      const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        O1[r] = 0.f;
-        O2[r] = 0.f;
+      for (int hf = 0; hf < 2; ++hf) {
+        float av[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = At[x][8 * hf + e];
+        bf16x8 ahi, alo;
+        split_frag(av, ahi, alo);
+        const char* vp = vrow + (32 * st + 16 * hf + 4 * hi) * 2;
+        const bf16x8 vf = frag_from_halves(*reinterpret_cast<const uint2*>(vp),
+                                           *reinterpret_cast<const uint2*>(vp + 16));
+        mfma32(O1[tt], ahi, vf);
+        mfma32(O1[tt], alo, vf);
       }
+    }
 #pragma unroll
-      for (int st = 0; st <= tt; ++st) {
-        const int x = tt == 0 ? 0 : (st == 0 ? 1 : 2);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float av[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) av[e] = At[x][8 * hf + e];
-          const char* vp = vrow + (32 * st + 16 * hf + 4 * hi) * 2;
-          mfma32(O1, frag_from_f(av),
-                 frag_from_halves(*reinterpret_cast<const uint2*>(vp), *reinterpret_cast<const uint2*>(vp + 16)));
-        }
-      }
-      const char* qrow = sQ + (32 * tt + cl) * QP;
-#pragma unroll
-      for (int a = 0; a < DK / 32; ++a)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const char* qp = qrow + (32 * a + 16 * hf + 4 * hi) * 2;
-          mfma32(O2, frag_from_halves(*reinterpret_cast<const uint2*>(qp), *reinterpret_cast<const uint2*>(qp + 16)),
-                 Sf[a][hf]);
-        }
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * tt + acc_row(r, lane);
         if (t < n) {
-          const float val = O1[r] + __expf(sG[t]) * O2[r];
+          const float val = O1[tt][r] + __expf(sG[t]) * O2[tt][r];
           o[(base + t) * ldo + (long long)h * DV + dv0 + cl] = f2bf(val);
         }
       }
-    }
 
     // (c) S = exp(G_last) S + (K . w)^T V
     const float dec = __expf(Glast);
@@ -203,11 +218,14 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[a][r] *= dec;
       const char* kt = sKt + (32 * a + cl) * TP + 16 * hi;
+      const char* kl = sKl + (32 * a + cl) * TP + 16 * hi;
       const char* vt = vrow + 16 * hi;
 #pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks)
-        mfma32(S[a], as_frag(*reinterpret_cast<const uint4*>(kt + 32 * ks)),
-               as_frag(*reinterpret_cast<const uint4*>(vt + 32 * ks)));
+      for (int ks = 0; ks < C / 16; ++ks) {
+        const bf16x8 vf = as_frag(*reinterpret_cast<const uint4*>(vt + 32 * ks));
+        mfma32(S[a], as_frag(*reinterpret_cast<const uint4*>(kt + 32 * ks)), vf);
+        mfma32(S[a], as_frag(*reinterpret_cast<const uint4*>(kl + 32 * ks)), vf);
+      }
     }
   }
 

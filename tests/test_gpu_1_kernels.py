@@ -142,16 +142,20 @@ def _scan_case(H, lens, seed, with_init=True):
     o = O.bf16_bits_to_float(host_bits(d_o)).reshape(T, H, dk)
     sf = d_sf.cpu().numpy()
     qkvf = O.bf16_bits_to_float(qkv).reshape(T, 3, H, dk)
-    worst_o = worst_s = 0.0
+    worst_o = worst_s = worst_raw = 0.0
     for i in range(n):
         a, b = cu[i], cu[i + 1]
         ro, rs = O.la_scan_unrolled(qkvf[a:b, 0], qkvf[a:b, 1], qkvf[a:b, 2], np.exp(lg[a:b].astype(np.float64)),
                                     s0[i].astype(np.float64) if with_init else None)
         if b > a:
-            worst_o = max(worst_o, rel_l2(o[a:b], ro))
+            # the kernel rounds o once to bf16 at the end; everything before is
+            # exact products with fp32 accumulation
+            worst_o = max(worst_o, rel_l2(o[a:b], O.bf16_bits_to_float(O.round_to_bf16_bits(ro))))
+            worst_raw = max(worst_raw, rel_l2(o[a:b], ro))
         worst_s = max(worst_s, rel_l2(sf[i], rs))
-    log(f"scan H={H} lens={lens}: rel L2 o {worst_o:.2e} state {worst_s:.2e}")
-    assert worst_o < 1e-2 and worst_s < 1e-2
+    log(f"scan H={H} lens={lens}: rel L2 o vs rounded oracle {worst_o:.2e} (vs unrounded {worst_raw:.2e}), "
+        f"state {worst_s:.2e}")
+    assert worst_o < 1e-3 and worst_s < 1e-5
 
 
 @pytest.mark.parametrize("H,lens", [

@@ -24,22 +24,28 @@ _models = {}
 
 
 def _model(shape):
+    """(GPU model, oracle in the path's precision, exact oracle or None)."""
     require_gpu()
     if shape.name not in _models:
         w = make_weights(shape)
         cfg = s1.make_config(shape, max_tokens=4096, max_seqs=16, max_questions=64, max_options=64,
                              max_prefixes=2, max_positions=4096)
-        _models[shape.name] = (s1.Model(cfg, w.tensors), O.OracleModel(shape, w.tensors), w)
+        bf16 = shape.dtype == "bf16"
+        om = O.OracleModel(shape, w.tensors, act="bf16" if bf16 else "exact")
+        ox = O.OracleModel(shape, w.tensors) if bf16 else None
+        _models[shape.name] = (s1.Model(cfg, w.tensors), om, ox)
     return _models[shape.name]
 
 
 def _full_check(shape, batch, label, mode="plain"):
-    model, om, _ = _model(shape)
+    model, om, ox = _model(shape)
     capture = {i: np.arange(int(batch.seq_lens[i])) for i in range(batch.n_seqs) if batch.seq_lens[i] > 0}
     rows = oracle_rows(batch, capture)
     probs, dec, hid = run_gpu(model, batch, rows, shape.n_layers, shape.d_model)
     ref = O.prefill_decide(om, batch, mode=mode, capture=capture)
-    return compare(batch, probs, dec, ref, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture), label=label)
+    rx = O.prefill_decide(ox, batch, mode=mode) if ox is not None else None
+    return compare(batch, probs, dec, ref, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture), label=label,
+                   ref_exact=rx)
 
 
 def test_tiny_workload():

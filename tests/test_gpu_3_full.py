@@ -11,12 +11,12 @@ import pytest
 import oracle as O
 from s1_workloads import make_batch, make_weights, shape_of
 from tests.gpu_util import log, require_gpu
-from tests.parity import compare, oracle_rows, run_gpu, stack_ref_hidden
+from tests.parity import compare_full_depth, oracle_rows, run_gpu, stack_ref_hidden
 
 pytestmark = pytest.mark.gpu
 
 
-def test_4b_single_512(gpu_model_4b, oracle_4b):
+def test_4b_single_512(gpu_model_4b, oracle_4b, oracle_4b_exact):
     shape = shape_of("4b-single-512")
     b = make_batch("4b-single-512")
     capture = {0: np.arange(512)}
@@ -24,10 +24,12 @@ def test_4b_single_512(gpu_model_4b, oracle_4b):
     t0 = time.time()
     ref = O.prefill_decide(oracle_4b, b, capture=capture)
     log(f"oracle 4b-single-512: {time.time() - t0:.1f} s")
-    compare(b, probs, dec, ref, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture), label="4b-single-512")
+    rx = O.prefill_decide(oracle_4b_exact, b, capture=capture)
+    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
+                       stack_ref_hidden(rx, capture), label="4b-single-512")
 
 
-def test_4b_varlen_16_sampled(gpu_model_4b, oracle_4b):
+def test_4b_varlen_16_sampled(gpu_model_4b, oracle_4b, oracle_4b_exact):
     shape = shape_of("4b-varlen-16")
     b = make_batch("4b-varlen-16")
     sample = [9, 4, 15]          # 256, 694 and 826 tokens; 15 is the last in the pack
@@ -41,16 +43,17 @@ def test_4b_varlen_16_sampled(gpu_model_4b, oracle_4b):
     t0 = time.time()
     ref = O.prefill_decide(oracle_4b, b, capture=capture, seqs=sample)
     log(f"oracle 4b-varlen-16 (3 sequences): {time.time() - t0:.1f} s")
+    rx = O.prefill_decide(oracle_4b_exact, b, capture=capture, seqs=sample)
     qs = [j for j in range(b.n_questions) if b.q_seq[j] in sample]
-    compare(b, probs, dec, ref, questions=qs, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture),
-            label="4b-varlen-16 sampled")
+    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
+                       stack_ref_hidden(rx, capture), questions=qs, label="4b-varlen-16 sampled")
     # every question: a probability vector with consistent fields
     for j in range(b.n_questions):
         lo, hi = b.opt_offsets[j], b.opt_offsets[j + 1]
         assert abs(probs[lo:hi].sum() - 1.0) < 1e-5 and (probs[lo:hi] >= 0).all()
 
 
-def test_4b_branch_4096x20(gpu_model_4b, oracle_4b):
+def test_4b_branch_4096x20(gpu_model_4b, oracle_4b, oracle_4b_exact):
     shape = shape_of("4b-branch-4096x20")
     b = make_batch("4b-branch-4096x20")
     capture = {0: np.array([0, 1, 2047, 4095])}
@@ -60,8 +63,9 @@ def test_4b_branch_4096x20(gpu_model_4b, oracle_4b):
     t0 = time.time()
     ref = O.prefill_decide(oracle_4b, b, mode="continuation", capture=capture)
     log(f"oracle 4b-branch-4096x20: {time.time() - t0:.1f} s")
-    compare(b, probs, dec, ref, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture),
-            label="4b-branch-4096x20")
+    rx = O.prefill_decide(oracle_4b_exact, b, mode="continuation", capture=capture)
+    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
+                       stack_ref_hidden(rx, capture), label="4b-branch-4096x20")
 
 
 @pytest.mark.slow
@@ -81,7 +85,10 @@ def test_27b_single_1024():
     probs, dec, hid = run_gpu(model, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
     model.free()
     t0 = time.time()
-    om = O.OracleModel(shape, w.tensors, dtype=np.float32)
+    om = O.OracleModel(shape, w.tensors, dtype=np.float32, act="bf16")
     ref = O.prefill_decide(om, b, capture=capture)
     log(f"oracle 27b-single-1024: {time.time() - t0:.1f} s")
-    compare(b, probs, dec, ref, hidden=hid, ref_hidden=stack_ref_hidden(ref, capture), label="27b-single-1024")
+    om.act = "exact"
+    rx = O.prefill_decide(om, b, capture=capture)
+    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
+                       stack_ref_hidden(rx, capture), label="27b-single-1024")

@@ -218,3 +218,23 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         return f
     monkeypatch.setattr(P.O, "decision_fields", fields_unnormalised)
     assert fails(P.test_readout_golden_special_cases)
+
+
+def test_bf16_activation_mode():
+    """act='bf16' rounds matrix-product operands to bf16 (RFC #114 section 1:
+    BF16 inference); its drift from exact arithmetic is of bf16 size -- not
+    zero, and far below O(1)."""
+    from dataclasses import replace
+    shape = replace(shape_of("4b-single-512"), name="bf16-mini", n_layers=4, d_model=256,
+                    ffn=512, vocab=2048, la_heads=2, fa_q_heads=2, fa_kv_heads=1, shape_id=78)
+    w = make_weights(shape)
+    om = O.OracleModel(shape, w.tensors, act="bf16")
+    x = np.array([1 + 2.0 ** -8 + 2.0 ** -30, 0.02, -3.3])
+    np.testing.assert_array_equal(om._a(x), O.bf16_bits_to_float(O.round_to_bf16_bits(x)))
+    assert O.OracleModel(shape, w.tensors)._a(x) is x
+    b = random_batch(shape.vocab, [80], seed=2, questions_per_seq=[3])
+    cap = {0: np.arange(80)}
+    hb = O.prefill_decide(om, b, capture=cap)["hidden"][0]
+    hx = O.prefill_decide(O.OracleModel(shape, w.tensors), b, capture=cap)["hidden"][0]
+    drift = [np.linalg.norm(hb[l] - hx[l]) / np.linalg.norm(hx[l]) for l in range(1, 5)]
+    assert all(1e-4 < d < 3e-2 for d in drift), drift
