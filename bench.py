@@ -95,7 +95,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()      # a real stream: events and kernels on the same queue
     shape = shape_of(args.workload)
     batch = make_batch(args.workload)
     t0 = time.time()
@@ -113,24 +113,29 @@ def main():
     dd = torch.zeros((max(plan.n_questions, 1), 6), dtype=torch.float32, device="cuda")
     sp = stream.cuda_stream
 
-    for _ in range(args.warmup):
-        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    def timed(graph):
+        plan.set_graph(graph)
+        for _ in range(args.warmup):
+            plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - w0) / args.steps
+
+    ms_eager, wall_eager = timed(False)
+    ms_step, wall = timed(True)          # the plan replayed as one HIP graph
+    wall *= args.steps
     tokens = plan.tokens
     value = tokens / (ms_step / 1e3)
     reqs = requests_in(batch)
 
     # per-kernel durations: events recorded by the library after each launch
+    plan.set_graph(False)
     prof = {}
     for _ in range(max(1, args.profile_steps)):
         for k, (n, us) in plan.profile(dp.data_ptr(), dd.data_ptr(), sp).items():
@@ -161,6 +166,8 @@ def main():
                    "questions_per_step": int(batch.n_questions), "layers": shape.n_layers,
                    "d_model": shape.d_model, "weights": "seeded random init N(0, 0.02), LoRA r32 merged"},
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "execution": "HIP graph replay of the plan",
+        "ms_per_step_eager_launches": round(ms_eager, 4),
         "load_s": round(t_load, 2), "weight_gen_s": round(t_gen, 2),
         "kernels": kernels, "roofline": roofline,
     }

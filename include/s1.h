@@ -202,6 +202,13 @@ int s1_plan_create(s1_model* m, const s1_batch* b, s1_plan** out);
 int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream);
 void s1_plan_free(s1_plan* p);
 
+/* Replay the plan as one HIP graph (enable != 0) instead of issuing every
+ * kernel launch from the host.  The graph is captured on the first run and
+ * captured again when the output or capture pointers change; the stream must
+ * not be the null stream (NULL selects the library's own stream, which is
+ * fine).  Default: off.  Profiling always runs launch by launch. */
+int s1_plan_set_graph(s1_plan* p, int32_t enable);
+
 /* Tokens the plan processes (each prefix once plus every other sequence). */
 int64_t s1_plan_tokens(const s1_plan* p);
 

@@ -187,9 +187,17 @@ int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, voi
   if (p->owner != m) return set_error(S1_EINVAL, "plan belongs to another model");
   if (p->p->Q > 0 && (!d_probs || !d_out)) return set_error(S1_EINVAL, "output buffers are NULL");
   hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : m->m->own_stream;
-  const int rc = run_plan(m->m, p->p, d_probs, d_out, s);
+  const int rc = p->p->use_graph ? run_plan_graph(m->m, p->p, d_probs, d_out, s)
+                                 : run_plan(m->m, p->p, d_probs, d_out, s);
   if (rc) (void)hipStreamSynchronize(s);
   return rc;
+}
+
+int s1_plan_set_graph(s1_plan* p, int32_t enable) {
+  if (!p) return set_error(S1_EINVAL, "plan is NULL");
+  p->p->use_graph = enable != 0;
+  if (!enable) p->p->drop_graph();
+  return S1_OK;
 }
 
 int s1_plan_profile(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream,

@@ -78,7 +78,15 @@ void* Model::alloc(size_t bytes) {
   return p;
 }
 
+void Plan::drop_graph() {
+  if (gexec) (void)hipGraphExecDestroy(gexec);
+  if (graph) (void)hipGraphDestroy(graph);
+  gexec = nullptr;
+  graph = nullptr;
+}
+
 Plan::~Plan() {
+  drop_graph();
   if (dev) (void)hipFree(dev);
   if (cap_dev) (void)hipFree(cap_dev);
 }
@@ -464,6 +472,7 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
 }
 
 int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
+  p->drop_graph();
   if (p->cap_dev) {
     (void)hipFree(p->cap_dev);
     p->cap_dev = nullptr;
@@ -650,6 +659,42 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
                           p->opt_off, p->opt_ids, p->q_type, d_probs, d_dec, p->max_k, s),
            "readout");
   if (p->Q > 0) MARK(KC_READOUT);
+  return S1_OK;
+}
+
+}  // namespace s1
+
+namespace s1 {
+
+// Capture the forward of a plan into a HIP graph on stream s (it must not be
+// the null stream) and replay it.  Only kernel launches are recorded.
+int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
+  if (p->gexec && (p->g_probs != d_probs || p->g_dec != d_dec || p->g_cap != p->cap_out)) p->drop_graph();
+  if (!p->gexec) {
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "begin graph capture"));
+    const int rc = run_plan(m, p, d_probs, d_dec, s);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);
+    if (rc) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "end graph capture"));
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      return set_error(S1_EDEVICE, hip_msg(e, "instantiate graph"));
+    }
+    p->graph = g;
+    p->gexec = x;
+    p->g_probs = d_probs;
+    p->g_dec = d_dec;
+    p->g_cap = p->cap_out;
+  }
+  const hipError_t e = hipGraphLaunch(p->gexec, s);
+  if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "graph launch"));
   return S1_OK;
 }
 

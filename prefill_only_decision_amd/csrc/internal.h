@@ -113,6 +113,15 @@ struct Plan {
   int n_cap = 0;
   void* dev = nullptr;          // one device block for the arrays above
   void* cap_dev = nullptr;      // device block for capture row lists
+  // HIP graph of the whole forward, replayed by s1_plan_run when enabled;
+  // re-captured when the output or capture pointers change
+  bool use_graph = false;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  float* g_probs = nullptr;
+  void* g_dec = nullptr;
+  float* g_cap = nullptr;
+  void drop_graph();
   ~Plan();
 };
 
@@ -122,5 +131,6 @@ int load_model(const s1_config* cfg, const s1_tensor* t, int n, hipStream_t s, M
 int create_plan(Model* m, const s1_batch* b, Plan** out);
 int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden);
+int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 
 }  // namespace s1

@@ -107,34 +107,39 @@ def compare_full_depth(batch, probs, dec, ref, ref_exact, hidden, ref_hidden, ex
     So: the per-layer 1e-2 gate on the first STRICT_LAYERS layers; at every
     layer, this path's distance from the exact oracle at most DRIFT_FACTOR
     times the bf16 oracle's own distance from it (+2e-3); probabilities within
-    the pages' bf16-vs-float32 allowance of both oracles; identical choice
-    wherever the exact oracle's margin exceeds twice that allowance (a
-    probability error within the allowance cannot flip such a choice);
+    an allowance of both oracles -- the pages' bf16-vs-float32 allowance, or
+    DRIFT_FACTOR times the bf16 oracle's own probability drift (+5e-3) if that
+    is larger; identical choice wherever the exact oracle's margin exceeds
+    twice the allowance (an error within it cannot flip such a choice);
     answer fields consistent with this path's probabilities."""
     qs = range(batch.n_questions) if questions is None else list(questions)
     L = hidden.shape[0]
     g_b = [rel_l2(hidden[l], ref_hidden[l]) for l in range(L)]
     g_x = [rel_l2(hidden[l], exact_hidden[l]) for l in range(L)]
     b_x = [rel_l2(ref_hidden[l], exact_hidden[l]) for l in range(L)]
-    dp_b = dp_x = 0.0
-    flips_02 = flips_wide = checked = 0
+    dp_b = dp_x = dp_bx = 0.0
     for j in qs:
         lo, hi = batch.opt_offsets[j], batch.opt_offsets[j + 1]
         dp_b = max(dp_b, float(np.abs(probs[lo:hi] - ref["probs"][j]).max()))
         dp_x = max(dp_x, float(np.abs(probs[lo:hi] - ref_exact["probs"][j]).max()))
+        dp_bx = max(dp_bx, float(np.abs(ref["probs"][j] - ref_exact["probs"][j]).max()))
+        f = O.decision_fields(probs[lo:hi].astype(np.float64), int(batch.q_type[j]))
+        for key in ("score", "noul", "answer_confidence", "confidence", "entropy_confidence"):
+            assert abs(float(dec[j][key]) - f[key]) <= 2e-5 * max(1.0, abs(f[key])), (j, key)
+    allow = max(EXACT_PROB_TOL, DRIFT_FACTOR * dp_bx + 5e-3)
+    flips_02 = flips_wide = checked = 0
+    for j in qs:
         srt = np.sort(ref_exact["probs"][j])
         margin = srt[-1] - srt[-2]
         flip = int(dec[j]["choice"]) != ref_exact["fields"][j]["choice"]
         if margin >= MARGIN:
             checked += 1
             flips_02 += flip
-        if margin > 2 * EXACT_PROB_TOL:
+        if margin > 2 * allow:
             flips_wide += flip
-        f = O.decision_fields(probs[lo:hi].astype(np.float64), int(batch.q_type[j]))
-        for key in ("score", "noul", "answer_confidence", "confidence", "entropy_confidence"):
-            assert abs(float(dec[j][key]) - f[key]) <= 2e-5 * max(1.0, abs(f[key])), (j, key)
     fmt = lambda v: " ".join(f"{x:.1e}" for x in v)
-    log(f"{label}: vs bf16 oracle max|dp| {dp_b:.2e}; vs exact oracle max|dp| {dp_x:.2e}; "
+    log(f"{label}: vs bf16 oracle max|dp| {dp_b:.2e}; vs exact oracle max|dp| {dp_x:.2e} "
+        f"(bf16 oracle vs exact {dp_bx:.2e}, allowance {allow:.3f}); "
         f"choices with margin >= 0.02: {checked}, flips {flips_02}; flips beyond the allowance band {flips_wide}\n"
         f"  per layer, path vs bf16 oracle:  {fmt(g_b)}\n"
         f"  per layer, path vs exact oracle: {fmt(g_x)}\n"
@@ -142,6 +147,7 @@ def compare_full_depth(batch, probs, dec, ref, ref_exact, hidden, ref_hidden, ex
     assert max(g_b[:STRICT_LAYERS + 1]) <= HIDDEN_TOL, g_b[:STRICT_LAYERS + 1]
     for l in range(L):
         assert g_x[l] <= DRIFT_FACTOR * b_x[l] + 2e-3, (l, g_x[l], b_x[l])
-    assert dp_x <= EXACT_PROB_TOL and dp_b <= EXACT_PROB_TOL, (dp_x, dp_b)
+    assert dp_x <= allow and dp_b <= allow, (dp_x, dp_b, allow)
     assert flips_wide == 0
-    return {"dp_bf16": dp_b, "dp_exact": dp_x, "flips_02": flips_02, "layers_vs_bf16": g_b, "layers_vs_exact": g_x}
+    return {"dp_bf16": dp_b, "dp_exact": dp_x, "flips_02": flips_02, "layers_vs_bf16": g_b,
+            "layers_vs_exact": g_x}

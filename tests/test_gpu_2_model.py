@@ -163,3 +163,31 @@ def test_varlen_matches_each_request_alone():
         pa, _, _ = run_gpu(model, alone)
         ref = np.concatenate([p[b.opt_offsets[j]:b.opt_offsets[j + 1]] for j in qs])
         assert np.abs(pa - ref).max() < 2e-3
+
+
+def test_graph_replay_matches_eager():
+    """Every replay of the captured plan equals the eager run bit for bit,
+    with eager work and synchronisations between replays; changing the
+    output buffers re-captures."""
+    import torch
+    from tests.gpu_util import stream_ptr
+    model, _, _ = _model(MINI)
+    b = random_batch(MINI.vocab, [200, 64, 9, 130], seed=19, prefix_of=[-1, 0, -1, -1])
+    p_ref, d_ref, _ = run_gpu(model, b)
+    plan = model.plan(b)
+    plan.set_graph(True)
+    stream = torch.cuda.Stream()
+    for rep in range(4):
+        dp = torch.full((plan.n_options,), -1.0, dtype=torch.float32, device="cuda")
+        dd = torch.zeros((plan.n_questions, 6), dtype=torch.float32, device="cuda")
+        if rep == 3:   # other output buffers: a new capture
+            dp, dd = dp.clone(), dd.clone()
+        with torch.cuda.stream(stream):
+            plan.run(dp.data_ptr(), dd.data_ptr(), stream.cuda_stream)
+        torch.cuda.synchronize()
+        got = dp.cpu().numpy()
+        assert np.array_equal(got, p_ref), rep
+        dec = dd.cpu().numpy().copy().view(np.uint8).view(s1.DECISION_DTYPE).reshape(-1)
+        assert np.array_equal(dec, d_ref), rep
+        run_gpu(model, random_batch(MINI.vocab, [50], seed=rep))   # eager work in between
+    plan.free()
