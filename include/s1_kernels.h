@@ -31,6 +31,12 @@ extern "C" {
 int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
              int32_t K, int32_t split_k, void* hip_stream);
 
+/* s1k_gemm with an explicit workgroup tile configuration (0 is the default
+ * used by the decoder; 1..5 are other tile shapes of the same kernel, bf16
+ * only, for shape comparisons).  Invalid configurations return S1_EINVAL. */
+int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
+                 int32_t K, int32_t split_k, int32_t tile_cfg, void* hip_stream);
+
 /* out[T,d] (elem) = x / sqrt(mean(x^2) + eps) * w for each row of x[T,d]
  * (fp32); w[d] fp32.  RMSNorm before each mixer and FFN (pre-norm blocks of
  * the Qwen3.5-family backbone the System1-Omni README names). */
@@ -63,6 +69,16 @@ int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int3
                 const float* log_g, void* o, int32_t T, int32_t H, int32_t dk, int32_t dv,
                 int32_t n_seqs, const int32_t* cu_seqlens, const float* s_init,
                 float* s_final, void* hip_stream);
+
+/* The same scan (bf16, dk = dv = 128) in its chunk-parallel form, used when a
+ * request has few (sequence, head) chains: every 64-token chunk's state
+ * contribution in parallel, an elementwise scan of chunk states across
+ * chunks, then every chunk's outputs in parallel from the state entering it.
+ * Arguments as s1k_la_scan (bf16 implied).  Synchronises the stream. */
+int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_qkv,
+                        const float* log_g, void* o, int32_t T, int32_t H, int32_t n_seqs,
+                        const int32_t* cu_seqlens, const float* s_init, float* s_final,
+                        void* hip_stream);
 
 /* Causal attention over packed sequences with grouped KV heads:
  *   o_t = sum_{s: pos_s <= pos_t} softmax_s(q_t . k_s / sqrt(hd)) v_s

@@ -24,7 +24,8 @@ EXPORTS = (
     "s1_load_weights", "s1_prefill_decide", "s1_free", "s1_last_error", "s1_validate",
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
     "s1_plan_profile", "s1_plan_set_graph",
-    "s1k_gemm", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
+    "s1k_gemm", "s1k_gemm_cfg", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
+    "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout",
 )
 
@@ -110,10 +111,12 @@ def load_library(path=LIB_PATH):
         "s1_plan_set_graph": (C.c_int, [vp, i32]),
         "s1_plan_profile": (C.c_int, [vp, vp, vp, vp, vp, C.POINTER(KernelTime), i32, C.POINTER(i32)]),
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
+        "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_rmsnorm": (C.c_int, [i32, vp, vp, vp, i32, i32, f32, vp]),
         "s1k_embed": (C.c_int, [i32, vp, vp, vp, i32, i32, vp]),
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
         "s1k_la_scan": (C.c_int, [i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "s1k_la_scan_chunked": (C.c_int, [vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
         "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "s1k_readout": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
     }
@@ -345,6 +348,11 @@ def gemm(dtype, A, W, Cout, M, N, K, split_k=1, stream=None):
     return _k("s1k_gemm", dtype, C.c_void_p(A), C.c_void_p(W), C.c_void_p(Cout), M, N, K, split_k, _stream(stream))
 
 
+def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
+    return _k("s1k_gemm_cfg", dtype, C.c_void_p(A), C.c_void_p(W), C.c_void_p(Cout), M, N, K, split_k, cfg,
+              _stream(stream))
+
+
 def rmsnorm(dtype, x, w, out, T, d, eps, stream=None):
     return _k("s1k_rmsnorm", dtype, C.c_void_p(x), C.c_void_p(w), C.c_void_p(out), T, d, C.c_float(eps), _stream(stream))
 
@@ -366,6 +374,13 @@ def la_scan(dtype, q, k, v, ld_qkv, log_g, o, T, H, dk, dv, cu_seqlens, s_init=N
               C.c_void_p(log_g), C.c_void_p(o), T, H, dk, dv, len(cu) - 1, cu,
               C.c_void_p(s_init) if s_init else None, C.c_void_p(s_final) if s_final else None,
               _stream(stream))
+
+
+def la_scan_chunked(q, k, v, ld_qkv, log_g, o, T, H, cu_seqlens, s_init=None, s_final=None, stream=None):
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    return _k("s1k_la_scan_chunked", C.c_void_p(q), C.c_void_p(k), C.c_void_p(v), ld_qkv, C.c_void_p(log_g),
+              C.c_void_p(o), T, H, len(cu) - 1, cu, C.c_void_p(s_init) if s_init else None,
+              C.c_void_p(s_final) if s_final else None, _stream(stream))
 
 
 def attention(dtype, q, k, v, o, Hq, Hkv, hd, q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len,

@@ -306,9 +306,15 @@ static int dev_status(hipError_t e, const char* what) {
 
 int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
              int32_t split_k, void* hip_stream) {
+  return s1k_gemm_cfg(dtype, A, W, C, M, N, K, split_k, 0, hip_stream);
+}
+
+int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
+                 int32_t split_k, int32_t tile_cfg, void* hip_stream) {
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || M < 0 || N < 0 || K < 1 || split_k < 1 ||
-      K % (bf16 ? 8 : 4) || (split_k > 1 && N % 4) || !A || !W || !C)
+      K % (bf16 ? 8 : 4) || (split_k > 1 && N % 4) || !A || !W || !C || tile_cfg < 0 ||
+      tile_cfg >= gemm_tile_configs())
     return set_error(S1_EINVAL, "s1k_gemm: unsupported arguments");
   GemmArgs g{};
   g.A = A;
@@ -325,7 +331,7 @@ int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, i
     if (hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)split_k * M * N * sizeof(float) + 256, strm(hip_stream)) != hipSuccess)
       return set_error(S1_ENOMEM, "s1k_gemm: workspace allocation failed");
   }
-  const hipError_t e = launch_gemm(bf16, EPI_F32, g, split_k, ws, strm(hip_stream));
+  const hipError_t e = launch_gemm(bf16, EPI_F32, g, split_k, ws, strm(hip_stream), tile_cfg);
   if (ws) (void)hipFreeAsync(ws, strm(hip_stream));
   return dev_status(e, "s1k_gemm");
 }
@@ -392,6 +398,55 @@ int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int3
   (void)hipFree(st);
   (void)hipFree(dseq);
   return dev_status(e, "s1k_la_scan");
+}
+
+int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_qkv, const float* log_g, void* o,
+                        int32_t T, int32_t H, int32_t n_seqs, const int32_t* cu_seqlens, const float* s_init,
+                        float* s_final, void* hip_stream) {
+  if (n_seqs < 0 || H < 1 || !cu_seqlens || !q || !k || !v || !log_g || !o)
+    return set_error(S1_EINVAL, "s1k_la_scan_chunked: unsupported arguments");
+  if (n_seqs == 0) return S1_OK;
+  if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T) return set_error(S1_EINVAL, "s1k_la_scan_chunked: cu_seqlens out of range");
+  std::vector<ScanSeq> chunks;
+  std::vector<ChunkSeq> cseqs;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (len < 0) return set_error(S1_EINVAL, "s1k_la_scan_chunked: cu_seqlens decreasing");
+    ChunkSeq cs{(int)chunks.size(), 0, s_init ? i : -1, s_final ? i : -1};
+    for (int t0 = 0; t0 < len; t0 += 64) {
+      const int id = (int)chunks.size();
+      chunks.push_back({cu_seqlens[i] + t0, std::min(64, len - t0), id, id});
+      ++cs.nc;
+    }
+    cseqs.push_back(cs);
+  }
+  const size_t E = 128 * 128;
+  const size_t nc = std::max<size_t>(1, chunks.size());
+  const size_t bytes = nc * H * E * 4 + nc * H * 4 + (size_t)n_seqs * H * E * 4 +
+                       nc * sizeof(ScanSeq) + cseqs.size() * sizeof(ChunkSeq) + 1024;
+  char* buf = nullptr;
+  hipStream_t s = strm(hip_stream);
+  if (hipMalloc(&buf, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "s1k_la_scan_chunked: allocation failed");
+  }
+  float* cst = reinterpret_cast<float*>(buf);
+  float* gam = cst + nc * H * E;
+  float* st = gam + nc * H + 64;
+  st = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(st) + 255) & ~uintptr_t(255));
+  ScanSeq* dch = reinterpret_cast<ScanSeq*>(st + (size_t)n_seqs * H * E);
+  ChunkSeq* dcs = reinterpret_cast<ChunkSeq*>(dch + nc);
+  hipError_t e = hipMemcpy(dch, chunks.data(), chunks.size() * sizeof(ScanSeq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(dcs, cseqs.data(), cseqs.size() * sizeof(ChunkSeq), hipMemcpyHostToDevice);
+  const size_t sbytes = (size_t)n_seqs * H * E * 4;
+  if (e == hipSuccess && s_init) e = hipMemcpyAsync(st, s_init, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_scan_chunked(q, k, v, ld_qkv, log_g, H, o, H * 128, dch, (int)chunks.size(), dcs, n_seqs, cst,
+                            gam, st, H, s);
+  if (e == hipSuccess && s_final) e = hipMemcpyAsync(s_final, st, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(buf);
+  return dev_status(e, "s1k_la_scan_chunked");
 }
 
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o, int32_t Hq, int32_t Hkv,

@@ -277,6 +277,12 @@ int alloc_workspace(Model* m) {
   m->vc = m->alloc((size_t)std::max(1, m->n_fa) * T * Hkv * hd * m->esz);
   m->states = static_cast<float*>(m->alloc((size_t)std::max(1, m->n_la) * c.max_prefixes * H *
                                            c.la_dk * c.la_dv * sizeof(float)));
+  if (m->bf16) {
+    // chunk-parallel scan workspace, shared by all linear layers (one layer at a time)
+    m->max_chunks = (int)((T + 63) / 64) + c.max_seqs;
+    m->cstates = static_cast<float*>(m->alloc((size_t)m->max_chunks * H * c.la_dk * c.la_dv * sizeof(float)));
+    m->gamma = static_cast<float*>(m->alloc((size_t)m->max_chunks * H * sizeof(float)));
+  }
   m->split_max_rows = (int)std::min<long long>(T, 2048);
   m->splitws_elems = 4LL * m->split_max_rows * d;
   m->splitws = static_cast<float*>(m->alloc(m->splitws_elems * sizeof(float)));
@@ -410,6 +416,24 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
       attn[ps].push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
       for (int q0 = 0; q0 < len; q0 += bq) blocks[ps].push_back({(int)k, q0});
     }
+  // chunk-parallel scan when a pass has few (sequence, head) chains
+  std::vector<ScanSeq> chunks[2];
+  std::vector<ChunkSeq> cseqs[2];
+  for (int ps = 0; ps < 2; ++ps) {
+    const long long chains = (long long)order[ps].size() * m->cfg.la_heads;
+    p->pass[ps].chunked = m->bf16 && !order[ps].empty() && chains < 192;
+    if (!p->pass[ps].chunked) continue;
+    for (size_t k = 0; k < order[ps].size(); ++k) {
+      const ScanSeq& sq = scan[ps][k];
+      ChunkSeq cs{(int)chunks[ps].size(), 0, sq.s_in, sq.s_out};
+      for (int t0 = 0; t0 < sq.len; t0 += 64) {
+        const int id = (int)chunks[ps].size();
+        chunks[ps].push_back({sq.row0 + t0, std::min(64, sq.len - t0), id, id});
+        ++cs.nc;
+      }
+      cseqs[ps].push_back(cs);
+    }
+  }
   std::vector<int32_t> qrow(p->Q);
   for (int j = 0; j < p->Q; ++j) qrow[j] = row0[b->q_seq[j]] + b->q_marker[j];
 
@@ -422,11 +446,13 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
   };
   const size_t o_ids = take(p->T * 4), o_pos = take(p->T * 4), o_qrow = take(p->Q * 4);
   const size_t o_off = take((p->Q + 1) * 4), o_opt = take(p->total_opts * 4), o_qt = take(p->Q);
-  size_t o_scan[2], o_attn[2], o_blk[2];
+  size_t o_scan[2], o_attn[2], o_blk[2], o_chk[2], o_cseq[2];
   for (int ps = 0; ps < 2; ++ps) {
     o_scan[ps] = take(scan[ps].size() * sizeof(ScanSeq));
     o_attn[ps] = take(attn[ps].size() * sizeof(AttnSeq));
     o_blk[ps] = take(blocks[ps].size() * sizeof(AttnBlock));
+    o_chk[ps] = take(chunks[ps].size() * sizeof(ScanSeq));
+    o_cseq[ps] = take(cseqs[ps].size() * sizeof(ChunkSeq));
   }
   std::vector<char> host(off, 0);
   auto put = [&](size_t o, const void* src, size_t bytes) {
@@ -444,6 +470,8 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
     put(o_scan[ps], scan[ps].data(), scan[ps].size() * sizeof(ScanSeq));
     put(o_attn[ps], attn[ps].data(), attn[ps].size() * sizeof(AttnSeq));
     put(o_blk[ps], blocks[ps].data(), blocks[ps].size() * sizeof(AttnBlock));
+    put(o_chk[ps], chunks[ps].data(), chunks[ps].size() * sizeof(ScanSeq));
+    put(o_cseq[ps], cseqs[ps].data(), cseqs[ps].size() * sizeof(ChunkSeq));
   }
   if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
     (void)hipGetLastError();
@@ -466,6 +494,14 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
     p->pass[ps].attn = reinterpret_cast<AttnSeq*>(dv + o_attn[ps]);
     p->pass[ps].blocks = reinterpret_cast<AttnBlock*>(dv + o_blk[ps]);
     p->pass[ps].n_blocks = (int)blocks[ps].size();
+    p->pass[ps].chunks = reinterpret_cast<ScanSeq*>(dv + o_chk[ps]);
+    p->pass[ps].n_chunks = (int)chunks[ps].size();
+    p->pass[ps].cseqs = reinterpret_cast<ChunkSeq*>(dv + o_cseq[ps]);
+  }
+  if (p->pass[0].n_chunks + p->pass[1].n_chunks > 0 &&
+      std::max(p->pass[0].n_chunks, p->pass[1].n_chunks) > m->max_chunks) {
+    delete p;
+    return set_error(S1_EBUDGET, "request needs more scan chunks than the workspace holds");
   }
   *out = p;
   return S1_OK;
@@ -561,9 +597,15 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
       S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s), "linear-attention in-projection");
       MARK(KC_GEMM_LA_IN);
       float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
-      S1_TRY(launch_scan(m->bf16, qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es,
-                         m->ld_qkv, m->lg, H, att, m->ld_att, ps.scan, ps.n_seqs, states, H, dk, dv, s),
-             "linear-attention scan");
+      if (ps.chunked)
+        S1_TRY(launch_scan_chunked(qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es, m->ld_qkv,
+                                   m->lg, H, att, m->ld_att, ps.chunks, ps.n_chunks, ps.cseqs, ps.n_seqs,
+                                   m->cstates, m->gamma, states, H, s),
+               "linear-attention scan (chunk-parallel)");
+      else
+        S1_TRY(launch_scan(m->bf16, qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es,
+                           m->ld_qkv, m->lg, H, att, m->ld_att, ps.scan, ps.n_seqs, states, H, dk, dv, s),
+               "linear-attention scan");
       MARK(KC_LA_SCAN);
     } else {
       char* kc = static_cast<char*>(m->kc) + (size_t)L.fa_idx * c.max_tokens * kvld * es;

@@ -74,6 +74,9 @@ struct Model {
   void* kc = nullptr;           // [n_fa][T][Hkv * hd]
   void* vc = nullptr;
   float* states = nullptr;      // [n_la][max_prefixes][H][dk][dv] fp32
+  float* cstates = nullptr;     // chunk states of the chunk-parallel scan [max_chunks][H][dk][dv]
+  float* gamma = nullptr;       // chunk log-decays [max_chunks][H]
+  int max_chunks = 0;
   float* splitws = nullptr;     // split-K partials
   long long splitws_elems = 0;
   int split_max_rows = 0;
@@ -91,6 +94,10 @@ struct PassPlan {
   AttnSeq* attn = nullptr;      // device [n_seqs]
   AttnBlock* blocks = nullptr;  // device [n_blocks]
   int n_blocks = 0;
+  bool chunked = false;         // scan runs chunk-parallel (few chains)
+  ScanSeq* chunks = nullptr;    // device [n_chunks]
+  int n_chunks = 0;
+  ChunkSeq* cseqs = nullptr;    // device [n_seqs]
   int32_t* cap_rows = nullptr;  // device [n_cap]: rows captured in this pass
   int32_t* cap_dst = nullptr;   // device [n_cap]: index in the capture list
   int n_cap = 0;

@@ -43,7 +43,9 @@ struct GemmArgs {
 // 1.  With split > 1 (EPI_F32 or EPI_RESID) partial tiles go to `ws`
 // (split * M * N floats) and a reduction kernel applies the epilogue.
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
-                       hipStream_t s);
+                       hipStream_t s, int tile_cfg = 0);
+// Number of tile configurations selectable for EPI_F32 / split-K (bf16).
+int gemm_tile_configs();
 // The K tile (elements) of the GEMM for the given element type.
 int gemm_k_tile(bool bf16);
 
@@ -75,6 +77,20 @@ struct ScanSeq {
 hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
                        const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
                        int n_seqs, float* states, int H, int dk, int dv, hipStream_t s);
+// Chunk-parallel form for few (sequence, head) chains (bf16, dk = dv = 128):
+// `chunks` lists every chunk of up to 64 tokens (its s_in / s_out are its own
+// index); `cseqs` gives each sequence's chunk range and its initial / final
+// state slots in `states`.  cstates [n_chunks][H][128][128] and gamma
+// [n_chunks][H] are workspace.
+struct ChunkSeq {
+  int c0, nc;    // chunk range
+  int s_in;      // initial state slot in `states`, or -1
+  int s_out;     // final state slot, or -1
+};
+hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
+                               int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
+                               const ChunkSeq* cseqs, int n_cseqs, float* cstates, float* gamma,
+                               float* states, int H, hipStream_t s);
 
 // -------------------------------------------------------------- attention
 struct AttnSeq {

@@ -30,12 +30,18 @@ constexpr int C = 64, DK = 128, DV = 128;
 constexpr int QP = DK * 2 + 16;   // bytes per Q / K row in LDS
 constexpr int TP = C * 2 + 16;    // bytes per K^T / V^T row in LDS
 
-template <int NW>
+// MODE_FULL: the recurrence over whole sequences.  MODE_SUMMARY: one chunk
+// per entry from a zero state; writes only the chunk's state contribution and
+// its total log-decay.  MODE_OUTPUT: one chunk per entry from the state
+// entering it; writes only the outputs.
+enum { MODE_FULL = 0, MODE_SUMMARY = 1, MODE_OUTPUT = 2 };
+
+template <int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64)
 scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                  const bf16_t* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
                  bf16_t* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
-                 float* __restrict__ states, int H) {
+                 float* __restrict__ states, int H, float* __restrict__ gamma) {
   constexpr int NT = NW * 64;
   constexpr int DVG = 32 * NW;        // value columns per workgroup
   constexpr int NDVG = DV / DVG;      // workgroups per (sequence, head)
@@ -58,7 +64,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      S[a][r] = sq.s_in >= 0
+      S[a][r] = (MODE != MODE_SUMMARY && sq.s_in >= 0)
                     ? states[(((long long)sq.s_in * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl]
                     : 0.f;
 
@@ -77,8 +83,9 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     __syncthreads();                      // previous chunk's reads of LDS are done
     if (wave == 0) sG[lane] = G;
+    if (MODE == MODE_SUMMARY && tid == 0 && dvg == 0) gamma[(long long)seq * H + h] = Glast;
     // Q rows: straight copy
-    for (int c = tid; c < C * 16; c += NT) {
+    for (int c = tid; c < C * 16 && MODE != MODE_SUMMARY; c += NT) {
       const int s = c >> 4, ch = c & 15;
       uint4 val = make_uint4(0, 0, 0, 0);
       if (s < n) val = *reinterpret_cast<const uint4*>(q + (base + s) * ldqkv + h * DK + ch * 8);
@@ -93,6 +100,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       *reinterpret_cast<uint4*>(sK + s0 * QP + ch * 16) = ka;
       *reinterpret_cast<uint4*>(sK + s1 * QP + ch * 16) = kb;
       const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
+      if (MODE == MODE_OUTPUT) continue;
       const uint32_t a[4] = {ka.x, ka.y, ka.z, ka.w}, b[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -124,6 +132,8 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
     __syncthreads();
 
+    const char* vrow = sVt + (wave * 32 + cl) * TP;
+    if constexpr (MODE != MODE_SUMMARY) {
     // (a) score tiles A^T[s][t] = k_s . q_t for s-tile st <= t-tile tt
     floatx16 At[3];   // (0,0), (0,1), (1,1)
 #pragma unroll
@@ -182,7 +192,6 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
       }
     // (A . D) V: the score accumulator layout is the A operand
-    const char* vrow = sVt + (wave * 32 + cl) * TP;
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
       const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
@@ -211,6 +220,8 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
       }
 
+    }  // MODE != MODE_SUMMARY
+    if constexpr (MODE != MODE_OUTPUT) {
     // (c) S = exp(G_last) S + (K . w)^T V
     const float dec = __expf(Glast);
 #pragma unroll
@@ -227,9 +238,10 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         mfma32(S[a], as_frag(*reinterpret_cast<const uint4*>(kl + 32 * ks)), vf);
       }
     }
+    }  // MODE != MODE_OUTPUT
   }
 
-  if (sq.s_out >= 0) {
+  if (MODE != MODE_OUTPUT && sq.s_out >= 0) {
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
@@ -287,7 +299,67 @@ scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// Scan of chunk states across the chunks of each sequence, elementwise over
+// the [dk, dv] state: S_enter[c] = exp(gamma[c-1]) S_enter[c-1] + dS[c-1],
+// starting from the sequence's initial state.  cstates holds dS[c] on entry
+// and S_enter[c] on exit; the final state goes to the sequence's slot.
+__global__ void __launch_bounds__(256)
+chunk_state_scan_kernel(const ChunkSeq* __restrict__ cseqs, const float* __restrict__ gamma,
+                        float* __restrict__ cstates, float* __restrict__ states, int H) {
+  const int sidx = blockIdx.y / H, h = blockIdx.y % H;
+  const ChunkSeq cs = cseqs[sidx];
+  constexpr int E = DK * DV;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  float sv = cs.s_in >= 0 ? states[((long long)cs.s_in * H + h) * E + e] : 0.f;
+  for (int c = cs.c0; c < cs.c0 + cs.nc; ++c) {
+    float* slot = cstates + ((long long)c * H + h) * E + e;
+    const float d = *slot;
+    *slot = sv;
+    sv = __expf(gamma[(long long)c * H + h]) * sv + d;
+  }
+  if (cs.s_out >= 0) states[((long long)cs.s_out * H + h) * E + e] = sv;
+}
+
+template <int MODE>
+hipError_t launch_mode(const bf16_t* qq, const bf16_t* kk, const bf16_t* vv, int ld_qkv, const float* log_g,
+                       int ld_g, bf16_t* oo, int ld_o, const ScanSeq* seqs, int n_seqs, float* states, int H,
+                       float* gamma, int nw, hipStream_t s) {
+  if (nw == 4)
+    hipLaunchKernelGGL((scan_bf16_kernel<4, MODE>), dim3(n_seqs * 1, H), dim3(256), 0, s, qq, kk, vv, ld_qkv,
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+  else if (nw == 2)
+    hipLaunchKernelGGL((scan_bf16_kernel<2, MODE>), dim3(n_seqs * 2, H), dim3(128), 0, s, qq, kk, vv, ld_qkv,
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+  else
+    hipLaunchKernelGGL((scan_bf16_kernel<1, MODE>), dim3(n_seqs * 4, H), dim3(64), 0, s, qq, kk, vv, ld_qkv,
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
+                               int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
+                               const ChunkSeq* cseqs, int n_cseqs, float* cstates, float* gamma,
+                               float* states, int H, hipStream_t s) {
+  if (n_chunks <= 0 || H <= 0) return hipSuccess;
+  const auto* qq = reinterpret_cast<const bf16_t*>(q);
+  const auto* kk = reinterpret_cast<const bf16_t*>(k);
+  const auto* vv = reinterpret_cast<const bf16_t*>(v);
+  auto* oo = reinterpret_cast<bf16_t*>(o);
+  // one wave per (chunk, head, 32 value columns): enough workgroups to fill the chip
+  const long long units = (long long)n_chunks * H;
+  const int nw = units >= 1024 ? 4 : (units >= 256 ? 2 : 1);
+  hipError_t e = launch_mode<MODE_SUMMARY>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates,
+                                           H, gamma, nw, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_state_scan_kernel, dim3(DK * DV / 256, n_cseqs * H), dim3(256), 0, s, cseqs, gamma,
+                     cstates, states, H);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_mode<MODE_OUTPUT>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates, H,
+                                  gamma, nw, s);
+}
 
 hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
                        const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
@@ -300,15 +372,8 @@ hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, i
     const auto* kk = reinterpret_cast<const bf16_t*>(k);
     const auto* vv = reinterpret_cast<const bf16_t*>(v);
     auto* oo = reinterpret_cast<bf16_t*>(o);
-    if (chains >= 256)
-      hipLaunchKernelGGL(scan_bf16_kernel<4>, dim3(n_seqs * 1, H), dim3(256), 0, s, qq, kk, vv,
-                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
-    else if (chains >= 128)
-      hipLaunchKernelGGL(scan_bf16_kernel<2>, dim3(n_seqs * 2, H), dim3(128), 0, s, qq, kk, vv,
-                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
-    else
-      hipLaunchKernelGGL(scan_bf16_kernel<1>, dim3(n_seqs * 4, H), dim3(64), 0, s, qq, kk, vv,
-                         ld_qkv, log_g, ld_g, oo, ld_o, seqs, states, H);
+    return launch_mode<MODE_FULL>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, seqs, n_seqs, states, H, nullptr,
+                                  chains >= 256 ? 4 : (chains >= 128 ? 2 : 1), s);
   } else {
     if (dk > 128 || dv > 128 || 256 % dv != 0 || dk % (256 / dv) != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(scan_f32_kernel, dim3(n_seqs, H), dim3(256), 0, s,

@@ -121,7 +121,7 @@ def test_lora_merge_bf16():
     assert np.array_equal(host_bits(dO), W)
 
 
-def _scan_case(H, lens, seed, with_init=True):
+def _scan_case(H, lens, seed, with_init=True, chunked=False):
     torch = require_gpu()
     rng = np.random.default_rng(seed)
     T, dk = int(sum(lens)), 128
@@ -135,9 +135,14 @@ def _scan_case(H, lens, seed, with_init=True):
     d_s0 = dev(s0) if with_init else None
     d_sf = torch.zeros((n, H, dk, dk), dtype=torch.float32, device="cuda")
     base = d_qkv.data_ptr()
-    B.la_scan(B.S1_BF16, base, base + 2 * H * dk, base + 4 * H * dk, 3 * H * dk, d_lg.data_ptr(),
-              d_o.data_ptr(), T, H, dk, dk, cu, d_s0.data_ptr() if with_init else None,
-              d_sf.data_ptr(), stream_ptr())
+    if chunked:
+        B.la_scan_chunked(base, base + 2 * H * dk, base + 4 * H * dk, 3 * H * dk, d_lg.data_ptr(),
+                          d_o.data_ptr(), T, H, cu, d_s0.data_ptr() if with_init else None,
+                          d_sf.data_ptr(), stream_ptr())
+    else:
+        B.la_scan(B.S1_BF16, base, base + 2 * H * dk, base + 4 * H * dk, 3 * H * dk, d_lg.data_ptr(),
+                  d_o.data_ptr(), T, H, dk, dk, cu, d_s0.data_ptr() if with_init else None,
+                  d_sf.data_ptr(), stream_ptr())
     torch.cuda.synchronize()
     o = O.bf16_bits_to_float(host_bits(d_o)).reshape(T, H, dk)
     sf = d_sf.cpu().numpy()
@@ -153,7 +158,7 @@ def _scan_case(H, lens, seed, with_init=True):
             worst_o = max(worst_o, rel_l2(o[a:b], O.bf16_bits_to_float(O.round_to_bf16_bits(ro))))
             worst_raw = max(worst_raw, rel_l2(o[a:b], ro))
         worst_s = max(worst_s, rel_l2(sf[i], rs))
-    log(f"scan H={H} lens={lens}: rel L2 o vs rounded oracle {worst_o:.2e} (vs unrounded {worst_raw:.2e}), "
+    log(f"scan{' (chunked)' if chunked else ''} H={H} lens={lens}: rel L2 o vs rounded oracle {worst_o:.2e} (vs unrounded {worst_raw:.2e}), "
         f"state {worst_s:.2e}")
     assert worst_o < 1e-3 and worst_s < 1e-5
 
@@ -169,6 +174,13 @@ def test_scan_bf16(H, lens):
 
 def test_scan_bf16_zero_init_and_empty_sequence():
     _scan_case(16, [0, 40, 0, 129], seed=5, with_init=False)
+
+
+@pytest.mark.parametrize("H,lens,init", [
+    (16, [512], True), (16, [1, 63, 64, 65, 200, 0], True), (4, [4096], False), (40, [300, 33], True),
+])
+def test_scan_bf16_chunk_parallel(H, lens, init):
+    _scan_case(H, lens, seed=H + len(lens), with_init=init, chunked=True)
 
 
 def test_scan_f32():
