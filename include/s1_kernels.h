@@ -23,19 +23,26 @@ extern "C" {
 #endif
 
 /* C[M,N] (fp32, row stride N) = A[M,K] (elem, row stride K) x W[N,K]^T
- * (elem, row stride K): the projection GEMM with a plain fp32 epilogue.
- * split_k >= 1 splits the K loop over workgroups and sums the partial tiles
- * in a fixed order (deterministic).  bf16 needs K % 8 == 0, fp32 K % 4 == 0.
- * Projection GEMMs of the decoder (RFC #114, section 1: the language-model
- * projections; the Cua-S1 issue, "mostly GEMMs" comment). */
+ * (elem, row stride K): the projection GEMM with a plain fp32 epilogue, tile
+ * configuration chosen by shape as in the decoder.  split_k >= 1 is the
+ * largest K split allowed: split partial tiles are summed in a fixed order
+ * (deterministic).  bf16 needs K % 8 == 0, fp32 K % 4 == 0.  Projection
+ * GEMMs of the decoder (RFC #114, section 1: the language-model projections;
+ * the Cua-S1 issue, "mostly GEMMs" comment). */
 int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
              int32_t K, int32_t split_k, void* hip_stream);
 
-/* s1k_gemm with an explicit workgroup tile configuration (0 is the default
- * used by the decoder; 1..5 are other tile shapes of the same kernel, bf16
- * only, for shape comparisons).  Invalid configurations return S1_EINVAL. */
+/* s1k_gemm with an explicit tile configuration, 0 <= tile_cfg <
+ * s1k_gemm_tile_configs(), and exactly split_k K splits (fewer when K has
+ * fewer K tiles).  0 is the register-staged kernel (any element type and
+ * shape); 1..5 are the bf16 LDS-DMA kernels (128x128 three stages,
+ * 128x128 two stages, 128x64, 64x128, 256x256), used when K % 64 == 0 and
+ * falling back to 0 otherwise.  Invalid arguments return S1_EINVAL. */
 int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
                  int32_t K, int32_t split_k, int32_t tile_cfg, void* hip_stream);
+
+/* Number of GEMM tile configurations (host-only, no device work). */
+int s1k_gemm_tile_configs(void);
 
 /* out[T,d] (elem) = x / sqrt(mean(x^2) + eps) * w for each row of x[T,d]
  * (fp32); w[d] fp32.  RMSNorm before each mixer and FFN (pre-norm blocks of

@@ -24,7 +24,7 @@ EXPORTS = (
     "s1_load_weights", "s1_prefill_decide", "s1_free", "s1_last_error", "s1_validate",
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
     "s1_plan_profile", "s1_plan_set_graph",
-    "s1k_gemm", "s1k_gemm_cfg", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
+    "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout",
 )
@@ -112,6 +112,7 @@ def load_library(path=LIB_PATH):
         "s1_plan_profile": (C.c_int, [vp, vp, vp, vp, vp, C.POINTER(KernelTime), i32, C.POINTER(i32)]),
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "s1k_gemm_tile_configs": (C.c_int, []),
         "s1k_rmsnorm": (C.c_int, [i32, vp, vp, vp, i32, i32, f32, vp]),
         "s1k_embed": (C.c_int, [i32, vp, vp, vp, i32, i32, vp]),
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
@@ -351,6 +352,10 @@ def gemm(dtype, A, W, Cout, M, N, K, split_k=1, stream=None):
 def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
     return _k("s1k_gemm_cfg", dtype, C.c_void_p(A), C.c_void_p(W), C.c_void_p(Cout), M, N, K, split_k, cfg,
               _stream(stream))
+
+
+def gemm_tile_configs():
+    return load_library().s1k_gemm_tile_configs()
 
 
 def rmsnorm(dtype, x, w, out, T, d, eps, stream=None):

@@ -304,16 +304,12 @@ static int dev_status(hipError_t e, const char* what) {
   return e == hipSuccess ? S1_OK : set_error(S1_EDEVICE, hip_msg(e, what));
 }
 
-int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
-             int32_t split_k, void* hip_stream) {
-  return s1k_gemm_cfg(dtype, A, W, C, M, N, K, split_k, 0, hip_stream);
-}
-
-int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
-                 int32_t split_k, int32_t tile_cfg, void* hip_stream) {
+namespace {
+int gemm_entry(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
+               int32_t split_k, int32_t tile_cfg, void* hip_stream) {
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || M < 0 || N < 0 || K < 1 || split_k < 1 ||
-      K % (bf16 ? 8 : 4) || (split_k > 1 && N % 4) || !A || !W || !C || tile_cfg < 0 ||
+      K % (bf16 ? 8 : 4) || (split_k > 1 && N % 4) || !A || !W || !C || tile_cfg < GEMM_AUTO ||
       tile_cfg >= gemm_tile_configs())
     return set_error(S1_EINVAL, "s1k_gemm: unsupported arguments");
   GemmArgs g{};
@@ -335,6 +331,20 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
   if (ws) (void)hipFreeAsync(ws, strm(hip_stream));
   return dev_status(e, "s1k_gemm");
 }
+}  // namespace
+
+int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
+             int32_t split_k, void* hip_stream) {
+  return gemm_entry(dtype, A, W, C, M, N, K, split_k, GEMM_AUTO, hip_stream);
+}
+
+int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N, int32_t K,
+                 int32_t split_k, int32_t tile_cfg, void* hip_stream) {
+  if (tile_cfg < 0) return set_error(S1_EINVAL, "s1k_gemm_cfg: tile_cfg must be >= 0");
+  return gemm_entry(dtype, A, W, C, M, N, K, split_k, tile_cfg, hip_stream);
+}
+
+int s1k_gemm_tile_configs(void) { return gemm_tile_configs(); }
 
 int s1k_rmsnorm(int32_t dtype, const float* x, const float* w, void* out, int32_t T, int32_t d, float eps,
                 void* hip_stream) {

@@ -556,13 +556,9 @@ int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
 
 namespace {
 
-int choose_split(const Model* m, int M, int N, int K) {
-  if (M > m->split_max_rows) return 1;
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int split = 1;
-  while (split < 4 && tiles * (split + 1) <= 320 && K / (64 * (split + 1)) >= 4) ++split;
-  return split;
-}
+// Largest K split the workspace allows for an M-row GEMM with a d-wide
+// output (the GEMM picks the split it uses, up to this).
+int max_split(const Model* m, int M) { return M <= m->split_max_rows ? 4 : 1; }
 
 int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
   const s1_config& c = m->cfg;
@@ -638,7 +634,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     go.K = L.k_o;
     go.out0 = x;
     go.ld0 = d;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, choose_split(m, T, d, L.k_o), m->splitws, s),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, T), m->splitws, s),
            "mixer out-projection");
     MARK(KC_GEMM_O);
     S1_TRY(launch_rmsnorm(m->bf16, x, L.ffn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
@@ -666,7 +662,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     gd.K = c.ffn;
     gd.out0 = x;
     gd.ld0 = d;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, choose_split(m, T, d, c.ffn), m->splitws, s),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, T), m->splitws, s),
            "FFN down");
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {

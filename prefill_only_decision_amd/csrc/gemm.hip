@@ -53,6 +53,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
                                          int cn0, int lane, int split_idx) {
   const int cl = lane & 31;
   if constexpr (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+    static_assert(TN % 2 == 0, "pair epilogues need both MFMA tiles of a 64-column block in the wave");
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
       const int cb = cn0 + 32 * j;                    // multiple of 64
@@ -280,6 +281,363 @@ gemm_kernel(GemmArgs g) {
   epilogue<T, EPI, S::TM, S::TN>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
 }
 
+// ------------------------------------------------------- bf16 LDS-DMA kernel
+// Operand tiles travel from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: lane l writes 16 bytes at M0 + 16 l), NS
+// stages deep, one barrier per K tile.  An LDS row holds BK bf16 (RB bytes)
+// without padding; 16-byte chunk c of row r is stored at chunk position
+// c ^ ((r >> SH) & (CH - 1)), which spreads the 16 rows that one
+// ds_read_b128 phase reads (same chunk, consecutive rows) over all 64 LDS
+// banks.  Rows past M or N read as zero through the buffer range check, so
+// no load is predicated.  The K range must be a whole number of K tiles.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_>
+struct L3 {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int NWAVE = WM * WN, NT = NWAVE * 64;
+  static constexpr int RB = BK * 2, CH = RB / 16, RPI = 1024 / RB;
+  static constexpr int SH = RB >= 256 ? 0 : (RB == 128 ? 1 : 2);
+  static constexpr int A_BYTES = BM * RB, STAGE = (BM + BN) * RB;
+  static constexpr int A_INS = BM * RB / 1024 / NWAVE, B_INS = BN * RB / 1024 / NWAVE;
+  static constexpr int INS = A_INS + B_INS;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  static constexpr int KS = BK / 16;
+  // workgroups per CU the LDS allows (at most 2 are asked for)
+  static constexpr int OCC = NS * STAGE * 2 <= 160 * 1024 ? 2 : 1;
+  static_assert(A_INS * NWAVE * 1024 == BM * RB && B_INS * NWAVE * 1024 == BN * RB, "tile/wave mismatch");
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(INS * (NS - 1) < 64, "vmcnt range");
+  static_assert(KS % 2 == 0, "operand double buffer alternates per k-step");
+};
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Buffer resource over `bytes` bytes from `base` (raw buffer, no stride):
+// offsets at or past `bytes` read as zero.
+__device__ __forceinline__ int32x4 buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4 r;
+  r.x = static_cast<int>(static_cast<uint32_t>(a));
+  r.y = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
+  r.z = bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
+// land at lds + 16 l.  Written as inline assembly so that the compiler does
+// not treat later LDS reads as dependent on it (it would wait for every
+// outstanding load before each of them); completion is awaited explicitly
+// with vmcnt before the barrier that publishes the stage.  m0 is written
+// here and is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(int32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+
+// The epilogue's arguments, loaded into SGPRs at kernel entry.  Left to the
+// compiler, these kernel-argument loads are placed just before the main loop
+// and are still outstanding when it starts; the waitcnt pass then has to
+// assume the worst at the loop head and waits for every LDS read there.
+template <typename T>
+__device__ __forceinline__ T pin_sgpr(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ GemmArgs pin_epilogue_args(const GemmArgs& g) {
+  GemmArgs e = g;
+  e.M = pin_sgpr(g.M);
+  e.N = pin_sgpr(g.N);
+  e.out0 = pin_sgpr(g.out0);
+  e.out1 = pin_sgpr(g.out1);
+  e.out2 = pin_sgpr(g.out2);
+  e.ld0 = pin_sgpr(g.ld0);
+  e.ld1 = pin_sgpr(g.ld1);
+  e.ld2 = pin_sgpr(g.ld2);
+  e.nsplit = pin_sgpr(g.nsplit);
+  e.nsplit2 = pin_sgpr(g.nsplit2);
+  e.n_valid = pin_sgpr(g.n_valid);
+  e.head_dim = pin_sgpr(g.head_dim);
+  e.pos = pin_sgpr(g.pos);
+  e.rope = pin_sgpr(g.rope);
+  e.split_stride = pin_sgpr(g.split_stride);
+  return e;
+}
+
+// s_waitcnt with vmcnt(vm), lgkmcnt(0), expcnt untouched.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | ((VM >> 4) << 14));
+}
+
+// Tile index -> (tile row, tile column): column-major inside groups of GM
+// tile rows, so that the tiles running at the same time on one XCD share a
+// few A row blocks and W column blocks.
+template <int GM>
+__device__ __forceinline__ void tile_coords(int t, int nbm, int nbn, int& tm, int& tn) {
+  const int group = GM * nbn;
+  const int first = (t / group) * GM;
+  const int gsz = min(nbm - first, GM);
+  const int u = t - (t / group) * group;
+  tm = first + u % gsz;
+  tn = u / gsz;
+}
+
+template <typename S>
+__device__ __forceinline__ int dma_voffset(int b, int lane, int ld) {
+  const int r = b * S::RPI + lane / S::CH;
+  const int c = (lane % S::CH) ^ ((r >> S::SH) & (S::CH - 1));
+  return r * ld * 2 + c * 16;
+}
+
+template <typename S, int EPI>
+__global__ void __launch_bounds__(S::NT)
+__attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
+gemm_lds_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  const GemmArgs e = pin_epilogue_args(g);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / S::WN, wn = wave % S::WN;
+  const int nbm = (g.M + S::BM - 1) / S::BM, nbn = (g.N + S::BN - 1) / S::BN;
+  int tm, tn;
+  tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
+  const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const int kb = blockIdx.y * g.k_split;
+  const int ke = min(g.K, kb + g.k_split);
+  const int nk = ke > kb ? (ke - kb) / S::BK : 0;
+
+  const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
+  const char* wbase = reinterpret_cast<const char*>(g.W) + (long long)n0 * g.ldw * 2;
+  const int32x4 ra = buffer_rsrc(abase, (g.M - m0) * g.lda * 2);
+  const int32x4 rw = buffer_rsrc(wbase, (g.N - n0) * g.ldw * 2);
+  const uint32_t lds0 = lds_addr(smem);
+  int va[S::A_INS], vw[S::B_INS];
+#pragma unroll
+  for (int i = 0; i < S::A_INS; ++i) va[i] = dma_voffset<S>(wave * S::A_INS + i, lane, g.lda);
+#pragma unroll
+  for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
+    const int so = (kb + kt * S::BK) * 2;
+#pragma unroll
+    for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
+#pragma unroll
+    for (int i = 0; i < S::B_INS; ++i) dma16(rw, st + S::A_BYTES + (wave * S::B_INS + i) * 1024, vw[i], so);
+  };
+
+  // per-lane LDS offsets of the MFMA operands for each k-step of a K tile
+  const int l32 = lane & 31, h = lane >> 5;
+  const int sw = (l32 >> S::SH) & (S::CH - 1);
+  int oa[S::KS], ob[S::KS];
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s) {
+    const int pos = ((2 * s + h) ^ sw) * 16;
+    oa[s] = (wm * S::WTM + l32) * S::RB + pos;
+    ob[s] = S::A_BYTES + (wn * S::WTN + l32) * S::RB + pos;
+  }
+
+  floatx16 acc[S::TM][S::TN];
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // All NS stages start full (tiles 0 .. NS-1); at the end of K tile kt its
+  // stage is refilled with tile kt + NS.  Operands are read one k-step
+  // ahead, and the barrier that publishes tile kt + 1 sits between the
+  // reads for the last k-step of tile kt and that k-step's MFMAs, so the
+  // matrix pipeline keeps running across it.
+  bf16x8 fa[2][S::TM], fb[2][S::TN];
+  auto read_ops = [&](int buf, const char* st, int s) {
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i)
+      fa[buf][i] = as_frag(*reinterpret_cast<const uint4*>(st + oa[s] + i * 32 * S::RB));
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+      fb[buf][j] = as_frag(*reinterpret_cast<const uint4*>(st + ob[s] + j * 32 * S::RB));
+  };
+  // The host guarantees at least one K tile per split.
+#pragma unroll
+  for (int p = 0; p < S::NS; ++p)
+    if (p < nk) issue(p);
+  if (S::NS - 1 < nk) wait_vm_lgkm0<(S::NS - 1) * S::INS>();
+  else wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_ops(0, smem, 0);
+  // nothing else (kernel-argument loads included) may be outstanding on
+  // lgkmcnt when the loop is entered, or every iteration waits for all
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  // The last K tile is peeled so that the loop body is straight-line code
+  // around the barrier: the compiler then sees the last k-step's operands
+  // as complete (explicit lgkmcnt(0)) and does not hold its MFMAs until the
+  // next tile's reads return.
+  auto tile = [&](int kt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const char* st = smem + (kt % S::NS) * S::STAGE;
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+      // reads for the next k-step are issued before this k-step's MFMAs
+      // (sched_barrier keeps the scheduler from sinking them)
+      if (s + 1 < S::KS) {
+        read_ops((s + 1) & 1, st, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (!LAST) {
+        // tile kt + 1 landed (own loads) and own reads of tile kt done
+        if (kt + S::NS - 1 < nk) wait_vm_lgkm0<(S::NS - 2) * S::INS>();
+        else wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + S::NS < nk) issue(kt + S::NS);
+        read_ops((s + 1) & 1, smem + ((kt + 1) % S::NS) * S::STAGE, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) mfma32(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
+    }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
+  if (nk > 0) tile(nk - 1, std::true_type{});
+  epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
+}
+
+// ------------------------------------------------- bf16 wide-wave kernel
+// Every wave owns a 128 x 128 block of the output (4 x 4 MFMA tiles), which
+// halves the LDS bytes read per MFMA against 64 x 64 waves: 8 KB of operands
+// feed 16 MFMAs.  Four waves, WM x WN, make the workgroup tile.  Operands
+// travel global -> LDS as in the kernel above (same swizzle, same buffer
+// range checks, same read-ahead and barrier placement).
+template <int WM_, int WN_, int BK_, int NS_>
+struct W4 {
+  static constexpr int WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int NWAVE = WM * WN, NT = NWAVE * 64;
+  static constexpr int TM = 4, TN = 4, WTM = 128, WTN = 128;
+  static constexpr int BM = WM * WTM, BN = WN * WTN;
+  static constexpr int RB = BK * 2, CH = RB / 16, RPI = 1024 / RB;
+  static constexpr int SH = RB >= 256 ? 0 : (RB == 128 ? 1 : 2);
+  static constexpr int A_BYTES = BM * RB, STAGE = (BM + BN) * RB;
+  static constexpr int A_INS = BM * RB / 1024 / NWAVE, B_INS = BN * RB / 1024 / NWAVE;
+  static constexpr int INS = A_INS + B_INS;
+  static constexpr int KS = BK / 16;
+  static_assert(KS % 2 == 0, "operand double buffer alternates per k-step");
+  static_assert(A_INS * NWAVE * 1024 == BM * RB && B_INS * NWAVE * 1024 == BN * RB, "tile/wave mismatch");
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(INS * (NS - 1) < 64, "vmcnt range");
+};
+
+template <typename S, int EPI>
+__global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_wide_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  const GemmArgs e = pin_epilogue_args(g);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / S::WN, wn = wave % S::WN;
+  const int nbm = (g.M + S::BM - 1) / S::BM, nbn = (g.N + S::BN - 1) / S::BN;
+  int tm, tn;
+  tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
+  const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const int kb = blockIdx.y * g.k_split;
+  const int ke = min(g.K, kb + g.k_split);
+  const int nk = (ke - kb) / S::BK;   // >= 1: the host gives every split a K tile
+
+  const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
+  const char* wbase = reinterpret_cast<const char*>(g.W) + (long long)n0 * g.ldw * 2;
+  const int32x4 ra = buffer_rsrc(abase, (g.M - m0) * g.lda * 2);
+  const int32x4 rw = buffer_rsrc(wbase, (g.N - n0) * g.ldw * 2);
+  const uint32_t lds0 = lds_addr(smem);
+  int va[S::A_INS], vw[S::B_INS];
+#pragma unroll
+  for (int i = 0; i < S::A_INS; ++i) va[i] = dma_voffset<S>(wave * S::A_INS + i, lane, g.lda);
+#pragma unroll
+  for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
+    const int so = (kb + kt * S::BK) * 2;
+#pragma unroll
+    for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
+#pragma unroll
+    for (int i = 0; i < S::B_INS; ++i) dma16(rw, st + S::A_BYTES + (wave * S::B_INS + i) * 1024, vw[i], so);
+  };
+
+  const int l32 = lane & 31, h = lane >> 5;
+  const int sw = (l32 >> S::SH) & (S::CH - 1);
+  int oa[S::KS], ob[S::KS];
+#pragma unroll
+  for (int u = 0; u < S::KS; ++u) {
+    const int pos = ((2 * u + h) ^ sw) * 16;
+    oa[u] = (wm * S::WTM + l32) * S::RB + pos;
+    ob[u] = S::A_BYTES + (wn * S::WTN + l32) * S::RB + pos;
+  }
+
+  floatx16 acc[S::TM][S::TN];
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8 fa[2][S::TM], fb[2][S::TN];
+  auto read_ops = [&](int buf, const char* st, int u) {
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) fa[buf][i] = as_frag(*reinterpret_cast<const uint4*>(st + oa[u] + i * 32 * S::RB));
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) fb[buf][j] = as_frag(*reinterpret_cast<const uint4*>(st + ob[u] + j * 32 * S::RB));
+  };
+#pragma unroll
+  for (int p = 0; p < S::NS; ++p)
+    if (p < nk) issue(p);
+  if (S::NS - 1 < nk) wait_vm_lgkm0<(S::NS - 1) * S::INS>();
+  else wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_ops(0, smem, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): nothing outstanding entering the loop
+
+  auto tile = [&](int kt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const char* st = smem + (kt % S::NS) * S::STAGE;
+#pragma unroll
+    for (int u = 0; u < S::KS; ++u) {
+      if (u + 1 < S::KS) {
+        read_ops((u + 1) & 1, st, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (!LAST) {
+        if (kt + S::NS - 1 < nk) wait_vm_lgkm0<(S::NS - 2) * S::INS>();
+        else wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + S::NS < nk) issue(kt + S::NS);
+        read_ops((u + 1) & 1, smem + ((kt + 1) % S::NS) * S::STAGE, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) mfma32(acc[i][j], fa[u & 1][i], fb[u & 1][j]);
+    }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
+  tile(nk - 1, std::true_type{});
+  epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
+}
+
 // Sum of split-K partial slabs in a fixed order, then the epilogue.
 template <bool RESID>
 __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, long long stride,
@@ -305,45 +663,64 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, lo
   }
 }
 
-template <int BM, int BN, int WM, int WN>
-struct Tile {
-  static constexpr int bm = BM, bn = BN, wm = WM, wn = WN;
-};
-// Tile shapes (rows x cols per workgroup, waves as rows x cols).  Config 0
-// runs every epilogue; the others are compiled for the plain and split-K
-// epilogues so that shapes can be compared on the same operands.
-using Tile0 = Tile<128, 128, 2, 2>;
-using Tile1 = Tile<128, 64, 2, 1>;
-using Tile2 = Tile<256, 128, 2, 2>;
-using Tile3 = Tile<128, 256, 2, 2>;
-using Tile4 = Tile<256, 256, 2, 2>;
-using Tile5 = Tile<64, 128, 1, 2>;
-constexpr int N_TILE_CFG = 6;
-
-template <typename T, typename TL, int EPI>
-hipError_t run(const GemmArgs& a, int split, hipStream_t s) {
-  const int nbm = (a.M + TL::bm - 1) / TL::bm, nbn = (a.N + TL::bn - 1) / TL::bn;
-  dim3 grid(nbm * nbn, split);
-  hipLaunchKernelGGL((gemm_kernel<T, TL::bm, TL::bn, TL::wm, TL::wn, EPI>), grid, dim3(TL::wm * TL::wn * 64), 0,
-                     s, a);
+template <typename T, int EPI>
+hipError_t run_reg(const GemmArgs& a, int split, hipStream_t s) {
+  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+  const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI>), dim3(nbm * nbn, split), dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename S, int EPI>
+hipError_t run_lds(const GemmArgs& a, int split, hipStream_t s) {
+  const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  hipLaunchKernelGGL((gemm_lds_kernel<S, EPI>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename S, int EPI>
+hipError_t run_wide(const GemmArgs& a, int split, hipStream_t s) {
+  const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  hipLaunchKernelGGL((gemm_wide_kernel<S, EPI>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+// Tile configurations.  0: register-staged 128 x 128 (every element type
+// and shape); 1-5 (bf16, LDS-DMA): rows x cols, waves, K tile, stages.
+using Cfg1 = L3<128, 128, 2, 2, 64, 3>;
+using Cfg2 = L3<128, 128, 2, 2, 64, 2>;   // small enough for two workgroups per CU
+using Cfg3 = L3<128, 64, 2, 2, 64, 4>;    // one 32-column MFMA tile per wave: no pair epilogues
+using Cfg4 = L3<64, 128, 2, 2, 64, 4>;
+using Cfg5 = W4<2, 2, 64, 2>;             // 256 x 256, 128 x 128 per wave
+constexpr int N_CFG = 6;
+
+// The LDS-DMA kernels need 16-byte aligned rows, a K range made of whole
+// 64-element tiles and operands whose byte offsets fit the 32-bit buffer
+// offsets.
+inline bool lds_ok(const GemmArgs& a) {
+  const long long abytes = (long long)a.M * a.lda * 2, wbytes = (long long)a.N * a.ldw * 2;
+  return a.lda % 8 == 0 && a.ldw % 8 == 0 && a.K % 64 == 0 && a.k_split % 64 == 0 &&
+         abytes < (1LL << 31) && wbytes < (1LL << 31);
 }
 
 template <typename T, int EPI>
 hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
-  if constexpr (EPI == EPI_F32 || EPI == EPI_PARTIAL) {
-    if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2) {
+    constexpr bool PAIR = EPI == EPI_SWIGLU || EPI == EPI_QKV;
+    if (cfg > 0 && lds_ok(a)) {
       switch (cfg) {
-        case 1: return run<T, Tile1, EPI>(a, split, s);
-        case 2: return run<T, Tile2, EPI>(a, split, s);
-        case 3: return run<T, Tile3, EPI>(a, split, s);
-        case 4: return run<T, Tile4, EPI>(a, split, s);
-        case 5: return run<T, Tile5, EPI>(a, split, s);
+        case 1: return run_lds<Cfg1, EPI>(a, split, s);
+        case 2: return run_lds<Cfg2, EPI>(a, split, s);
+        case 3:
+          if constexpr (!PAIR) return run_lds<Cfg3, EPI>(a, split, s);
+          break;
+        case 4: return run_lds<Cfg4, EPI>(a, split, s);
+        case 5: return run_wide<Cfg5, EPI>(a, split, s);
         default: break;
       }
     }
   }
-  return run<T, Tile0, EPI>(a, split, s);
+  return run_reg<T, EPI>(a, split, s);
 }
 
 template <typename T>
@@ -368,11 +745,42 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
   }
   switch (epi) {
     case EPI_F32: return run_cfg<T, EPI_F32>(a, 1, cfg, s);
-    case EPI_RESID: return run<T, Tile0, EPI_RESID>(a, 1, s);
-    case EPI_GATE: return run<T, Tile0, EPI_GATE>(a, 1, s);
-    case EPI_SWIGLU: return run<T, Tile0, EPI_SWIGLU>(a, 1, s);
-    case EPI_QKV: return run<T, Tile0, EPI_QKV>(a, 1, s);
+    case EPI_RESID: return run_cfg<T, EPI_RESID>(a, 1, cfg, s);
+    case EPI_GATE: return run_cfg<T, EPI_GATE>(a, 1, cfg, s);
+    case EPI_SWIGLU: return run_cfg<T, EPI_SWIGLU>(a, 1, cfg, s);
+    case EPI_QKV: return run_cfg<T, EPI_QKV>(a, 1, cfg, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Configuration and K split chosen by shape (bf16), from timings of the 4B
+// projection shapes at 512, 2,048 and 16,925 rows on MI355X: 256 x 256
+// tiles once there are rows enough to fill the chip with them; below that
+// 128 x 128 tiles (two workgroups per CU when there are several waves of
+// tiles), narrower tiles when there are fewer than 192 tiles, and a K split
+// for long reductions with few output tiles.
+void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, int& split) {
+  const long long t128 = (long long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  const bool can_split = max_split > 1 && (epi == EPI_F32 || epi == EPI_RESID);
+  split = 1;
+  if (!bf16) {
+    cfg = 0;
+    if (can_split)
+      while (split < max_split && t128 * (split + 1) <= 320 && a.K / (32 * (split + 1)) >= 4) ++split;
+    return;
+  }
+  if (a.M >= 4096) {
+    cfg = 5;
+  } else if (a.K >= 6144 && can_split) {
+    cfg = 2;
+    split = t128 >= 256 ? 3 : (int)std::min<long long>(4, (256 + t128 - 1) / t128);
+    split = std::min(split, max_split);
+  } else if (t128 >= 300) {
+    cfg = 2;
+  } else if (t128 >= 192) {
+    cfg = 1;
+  } else {
+    cfg = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 4 : 3;
   }
 }
 
@@ -380,14 +788,15 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
 
 int gemm_k_tile(bool bf16) { return bf16 ? 64 : 32; }
 
-int gemm_tile_configs() { return N_TILE_CFG; }
+int gemm_tile_configs() { return N_CFG; }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws, hipStream_t s,
                        int cfg) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   GemmArgs g = a;
-  const int bk = gemm_k_tile(bf16);
   if (split < 1) split = 1;
+  if (cfg < 0) auto_plan(bf16, epi, a, ws ? split : 1, cfg, split);
+  const int bk = gemm_k_tile(bf16);
   // K range per split: a whole number of K tiles
   const int tiles = (a.K + bk - 1) / bk;
   if (split > tiles) split = tiles > 0 ? tiles : 1;

@@ -39,14 +39,18 @@ struct GemmArgs {
   long long split_stride;  // EPI_PARTIAL: elements between split slabs
 };
 
-// Runs the GEMM; for epilogues other than EPI_F32 / EPI_RESID split must be
-// 1.  With split > 1 (EPI_F32 or EPI_RESID) partial tiles go to `ws`
-// (split * M * N floats) and a reduction kernel applies the epilogue.
+// Runs the GEMM.  tile_cfg >= 0 picks a tile configuration (0 .. 
+// gemm_tile_configs() - 1; configurations the shape cannot use fall back to
+// 0) and `split` is the K split; GEMM_AUTO picks both by shape, with `split`
+// the largest K split allowed (1 without a workspace).  With split > 1
+// (EPI_F32 or EPI_RESID only) partial tiles go to `ws` (split * M * N
+// floats) and a reduction kernel applies the epilogue in a fixed order.
+constexpr int GEMM_AUTO = -1;
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
-                       hipStream_t s, int tile_cfg = 0);
-// Number of tile configurations selectable for EPI_F32 / split-K (bf16).
+                       hipStream_t s, int tile_cfg = GEMM_AUTO);
+// Number of tile configurations.
 int gemm_tile_configs();
-// The K tile (elements) of the GEMM for the given element type.
+// The K tile (elements) of the register-staged GEMM for the element type.
 int gemm_k_tile(bool bf16);
 
 // ------------------------------------------------------------ elementwise

@@ -45,6 +45,16 @@ def test_free_null_is_noop(lib):
     lib.s1_plan_free(None)
 
 
+def test_gemm_config_count_and_validation(lib):
+    n = s1.binding.gemm_tile_configs()
+    assert n == 6
+    # invalid configurations are rejected before any device work
+    for cfg in (-1, n):
+        with pytest.raises(s1.binding.S1Error) as e:
+            s1.binding.gemm_cfg(s1.binding.S1_BF16, 16, 16, 16, 4, 4, 64, 1, cfg)
+        assert e.value.code == -1   # S1_EINVAL
+
+
 def _cfg(name="4b-single-512", **kw):
     return s1.make_config(shape_of(name), **kw)
 

@@ -39,6 +39,29 @@ def test_gemm_bf16(M, N, K, split):
     assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
 
 
+@pytest.mark.parametrize("M,N,K,split", [
+    (1, 64, 64, 1), (300, 520, 640, 1), (300, 520, 640, 3), (4100, 264, 128, 1), (130, 2560, 9728, 4),
+])
+def test_gemm_bf16_every_tile_config(M, N, K, split):
+    """Each tile configuration, on ragged M and N (partial tiles in both),
+    several K tiles and K splits, against float64 products of the same bf16
+    operands."""
+    torch = require_gpu()
+    rng = np.random.default_rng([M, N, K, 7])
+    A, W = _bits(rng, (M, K)), _bits(rng, (N, K), 0.05)
+    dA, dW = dev_bits(A), dev_bits(W)
+    ref = O.bf16_bits_to_float(A) @ O.bf16_bits_to_float(W).T
+    for cfg in range(B.gemm_tile_configs()):
+        log(f"gemm bf16 cfg={cfg} M={M} N={N} K={K} split={split}")
+        dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        B.gemm_cfg(B.S1_BF16, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, split, cfg, stream_ptr())
+        torch.cuda.synchronize()
+        C = dC.cpu().numpy()
+        assert np.isfinite(C).all(), cfg
+        assert rel_l2(C, ref) < 1e-5, cfg
+        assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6, cfg
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 1408, 256), (100, 256, 688), (5, 772, 256)])
 def test_gemm_f32(M, N, K):
     torch = require_gpu()
