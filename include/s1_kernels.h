@@ -35,9 +35,10 @@ int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, i
 /* s1k_gemm with an explicit tile configuration, 0 <= tile_cfg <
  * s1k_gemm_tile_configs(), and exactly split_k K splits (fewer when K has
  * fewer K tiles).  0 is the register-staged kernel (any element type and
- * shape); 1..5 are the bf16 LDS-DMA kernels (128x128 three stages,
- * 128x128 two stages, 128x64, 64x128, 256x256), used when K % 64 == 0 and
- * falling back to 0 otherwise.  Invalid arguments return S1_EINVAL. */
+ * shape); 1..6 are the bf16 LDS-DMA kernels (128x128 three stages,
+ * 128x128 two stages, 128x64, 64x128, 256x256, 256x192), used when
+ * K % 64 == 0 and falling back to 0 otherwise.  Invalid arguments return
+ * S1_EINVAL. */
 int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
                  int32_t K, int32_t split_k, int32_t tile_cfg, void* hip_stream);
 

@@ -427,9 +427,15 @@ gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
 
+  // Each tile walks its K tiles from a tile-dependent start (wrapping
+  // around), so that the workgroups running together do not all read the
+  // same K offset, whose rows fall on few L2 channels.  The order is fixed
+  // per tile, so results stay deterministic.
+  const int rot = (int)((7LL * blockIdx.x) % (nk > 0 ? nk : 1));
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
-    const int so = (kb + kt * S::BK) * 2;
+    const int kr = kt + rot;
+    const int so = (kb + (kr >= nk ? kr - nk : kr) * S::BK) * 2;
 #pragma unroll
     for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
 #pragma unroll
@@ -517,16 +523,17 @@ gemm_lds_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------- bf16 wide-wave kernel
-// Every wave owns a 128 x 128 block of the output (4 x 4 MFMA tiles), which
-// halves the LDS bytes read per MFMA against 64 x 64 waves: 8 KB of operands
-// feed 16 MFMAs.  Four waves, WM x WN, make the workgroup tile.  Operands
-// travel global -> LDS as in the kernel above (same swizzle, same buffer
-// range checks, same read-ahead and barrier placement).
-template <int WM_, int WN_, int BK_, int NS_>
+// Every wave owns a TM x TN block of 32 x 32 MFMA tiles (128 x 128, or
+// 64 x 192), which cuts the LDS bytes read per MFMA against 64 x 64 waves:
+// 8 KB of operands feed 12 or 16 MFMAs.  Four waves, WM x WN, make the
+// workgroup tile.  Operands travel global -> LDS as in the kernel above
+// (same swizzle, same buffer range checks, same read-ahead and barrier
+// placement).
+template <int WM_, int WN_, int TM_, int TN_, int BK_, int NS_>
 struct W4 {
   static constexpr int WM = WM_, WN = WN_, BK = BK_, NS = NS_;
   static constexpr int NWAVE = WM * WN, NT = NWAVE * 64;
-  static constexpr int TM = 4, TN = 4, WTM = 128, WTN = 128;
+  static constexpr int TM = TM_, TN = TN_, WTM = 32 * TM, WTN = 32 * TN;
   static constexpr int BM = WM * WTM, BN = WN * WTN;
   static constexpr int RB = BK * 2, CH = RB / 16, RPI = 1024 / RB;
   static constexpr int SH = RB >= 256 ? 0 : (RB == 128 ? 1 : 2);
@@ -566,9 +573,15 @@ gemm_wide_kernel(GemmArgs g) {
   for (int i = 0; i < S::A_INS; ++i) va[i] = dma_voffset<S>(wave * S::A_INS + i, lane, g.lda);
 #pragma unroll
   for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
+  // Each tile walks its K tiles from a tile-dependent start (wrapping
+  // around), so that the workgroups running together do not all read the
+  // same K offset, whose rows fall on few L2 channels.  The order is fixed
+  // per tile, so results stay deterministic.
+  const int rot = (int)((7LL * blockIdx.x) % (nk > 0 ? nk : 1));
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
-    const int so = (kb + kt * S::BK) * 2;
+    const int kr = kt + rot;
+    const int so = (kb + (kr >= nk ? kr - nk : kr) * S::BK) * 2;
 #pragma unroll
     for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
 #pragma unroll
@@ -691,8 +704,9 @@ using Cfg1 = L3<128, 128, 2, 2, 64, 3>;
 using Cfg2 = L3<128, 128, 2, 2, 64, 2>;   // small enough for two workgroups per CU
 using Cfg3 = L3<128, 64, 2, 2, 64, 4>;    // one 32-column MFMA tile per wave: no pair epilogues
 using Cfg4 = L3<64, 128, 2, 2, 64, 4>;
-using Cfg5 = W4<2, 2, 64, 2>;             // 256 x 256, 128 x 128 per wave
-constexpr int N_CFG = 6;
+using Cfg5 = W4<2, 2, 4, 4, 64, 2>;       // 256 x 256, 128 x 128 per wave
+using Cfg6 = W4<4, 1, 2, 6, 64, 2>;       // 256 x 192, 64 x 192 per wave
+constexpr int N_CFG = 7;
 
 // The LDS-DMA kernels need 16-byte aligned rows, a K range made of whole
 // 64-element tiles and operands whose byte offsets fit the 32-bit buffer
@@ -716,6 +730,7 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
           break;
         case 4: return run_lds<Cfg4, EPI>(a, split, s);
         case 5: return run_wide<Cfg5, EPI>(a, split, s);
+        case 6: return run_wide<Cfg6, EPI>(a, split, s);
         default: break;
       }
     }
@@ -754,11 +769,13 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
 }
 
 // Configuration and K split chosen by shape (bf16), from timings of the 4B
-// projection shapes at 512, 2,048 and 16,925 rows on MI355X: 256 x 256
-// tiles once there are rows enough to fill the chip with them; below that
-// 128 x 128 tiles (two workgroups per CU when there are several waves of
-// tiles), narrower tiles when there are fewer than 192 tiles, and a K split
-// for long reductions with few output tiles.
+// projection shapes at 512, 2,048 and 16,925 rows on MI355X with weights
+// not in cache: 256 x 256 tiles once there are rows enough to fill the chip
+// with them; 256 x 192 for wide outputs of few rows (204 tiles for the FFN
+// gate/up at 512 rows, against 152 of 256 x 256); else 128 x 128 tiles (two
+// workgroups per CU when there are several waves of tiles), narrower tiles
+// when there are fewer than 192 tiles, and a K split for long reductions
+// with few output tiles.
 void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, int& split) {
   const long long t128 = (long long)((a.M + 127) / 128) * ((a.N + 127) / 128);
   const bool can_split = max_split > 1 && (epi == EPI_F32 || epi == EPI_RESID);
@@ -771,6 +788,8 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
   }
   if (a.M >= 4096) {
     cfg = 5;
+  } else if (a.M <= 1024 && t128 >= 384) {
+    cfg = 6;
   } else if (a.K >= 6144 && can_split) {
     cfg = 2;
     split = t128 >= 256 ? 3 : (int)std::min<long long>(4, (256 + t128 - 1) / t128);

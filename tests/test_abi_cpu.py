@@ -47,7 +47,7 @@ def test_free_null_is_noop(lib):
 
 def test_gemm_config_count_and_validation(lib):
     n = s1.binding.gemm_tile_configs()
-    assert n == 6
+    assert n == 7
     # invalid configurations are rejected before any device work
     for cfg in (-1, n):
         with pytest.raises(s1.binding.S1Error) as e:
