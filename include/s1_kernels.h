@@ -95,11 +95,13 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
  * kv_pre_len[i] prefix rows starting at kv_pre_row0[i] (positions 0 ..) and
  * then its own q_len[i] rows starting at kv_row0[i] (positions
  * kv_pre_len[i] ..); query j has position kv_pre_len[i] + j.  All five
- * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd <= 128. */
+ * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd <= 128.
+ * block_rows: queries per workgroup, 0 to choose by size as the decoder
+ * does; bf16 accepts 32, 64 or 128, fp32 64. */
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o,
                   int32_t Hq, int32_t Hkv, int32_t hd, int32_t n_seqs, const int32_t* q_row0,
                   const int32_t* q_len, const int32_t* kv_row0, const int32_t* kv_pre_row0,
-                  const int32_t* kv_pre_len, void* hip_stream);
+                  const int32_t* kv_pre_len, int32_t block_rows, void* hip_stream);
 
 /* Decision readout for Q questions: h = RMSNorm(x[rows[j]]; w_final),
  * z_k = h . E[opt_k], p = softmax(z) over the question's options, and the

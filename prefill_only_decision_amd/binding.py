@@ -118,7 +118,7 @@ def load_library(path=LIB_PATH):
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
         "s1k_la_scan": (C.c_int, [i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
         "s1k_la_scan_chunked": (C.c_int, [vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
-        "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]),
         "s1k_readout": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -389,10 +389,10 @@ def la_scan_chunked(q, k, v, ld_qkv, log_g, o, T, H, cu_seqlens, s_init=None, s_
 
 
 def attention(dtype, q, k, v, o, Hq, Hkv, hd, q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len,
-              stream=None):
+              stream=None, block_rows=0):
     arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len)]
     return _k("s1k_attention", dtype, C.c_void_p(q), C.c_void_p(k), C.c_void_p(v), C.c_void_p(o),
-              Hq, Hkv, hd, len(arrs[0]), *arrs, _stream(stream))
+              Hq, Hkv, hd, len(arrs[0]), *arrs, block_rows, _stream(stream))
 
 
 def readout(dtype, x, d, w_final, eps, E, Q, rows, opt_offsets, opt_ids, q_type, probs, decisions,

@@ -462,17 +462,19 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o, int32_t Hq, int32_t Hkv,
                   int32_t hd, int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len,
                   const int32_t* kv_row0, const int32_t* kv_pre_row0, const int32_t* kv_pre_len,
-                  void* hip_stream) {
+                  int32_t block_rows, void* hip_stream) {
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || Hq < 1 || Hkv < 1 || Hq % Hkv || n_seqs < 0 || !q || !k ||
       !v || !o || (bf16 && hd != 128) || (!bf16 && (hd < 1 || hd > 128)) ||
-      (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)))
+      (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)) ||
+      (block_rows != 0 && !attn_block_rows_valid(bf16, block_rows)))
     return set_error(S1_EINVAL, "s1k_attention: unsupported arguments");
+  for (int i = 0; i < n_seqs; ++i)
+    if (q_len[i] < 0 || kv_pre_len[i] < 0) return set_error(S1_EINVAL, "s1k_attention: negative length");
   std::vector<AttnSeq> seqs(n_seqs);
   std::vector<AttnBlock> blocks;
-  const int bq = attn_block_rows(bf16);
+  const int bq = block_rows ? block_rows : attn_block_rows(bf16, q_len, n_seqs, Hq);
   for (int i = 0; i < n_seqs; ++i) {
-    if (q_len[i] < 0 || kv_pre_len[i] < 0) return set_error(S1_EINVAL, "s1k_attention: negative length");
     seqs[i] = {q_row0[i], q_len[i], kv_row0[i], kv_pre_row0[i], kv_pre_len[i]};
     for (int q0 = 0; q0 < q_len[i]; q0 += bq) blocks.push_back({i, q0});
   }
@@ -489,7 +491,7 @@ int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, vo
   if (e == hipSuccess) e = hipMemcpy(db, blocks.data(), b2, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = launch_attention(bf16, q, Hq * hd, k, v, Hkv * hd, o, Hq * hd, ds, db, (int)blocks.size(), Hq, Hkv,
-                         hd, strm(hip_stream));
+                         hd, bq, strm(hip_stream));
   if (e == hipSuccess) e = hipStreamSynchronize(strm(hip_stream));
   (void)hipFree(dm);
   return dev_status(e, "s1k_attention");

@@ -93,10 +93,45 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over a workgroup of NW waves (every thread gets the total).
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += red[i];
+  return t;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// RMSNorm of one row held as float4 pieces v[k] (columns 4 (k * NT + tid)
+// ...): out = v * r * w with r = 1 / sqrt(ss / d + eps), ss the row's sum of
+// squares.
+template <typename T, int NT, int MAXV>
+__device__ __forceinline__ void write_normed_row(const float4 (&v)[MAXV], float ss, int d, float eps,
+                                                 const float* __restrict__ w, T* __restrict__ o) {
+  const float r = rsqrtf(ss / d + eps);
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int c = (k * NT + (int)threadIdx.x) * 4;
+    if (c >= d) break;
+    const float4 g = *reinterpret_cast<const float4*>(w + c);
+    const float4 x = v[k];
+    if constexpr (sizeof(T) == 2) {
+      uint2 u;
+      u.x = pack_bf2(x.x * r * g.x, x.y * r * g.y);
+      u.y = pack_bf2(x.z * r * g.z, x.w * r * g.w);
+      *reinterpret_cast<uint2*>(o + c) = u;
+    } else {
+      *reinterpret_cast<float4*>(o + c) = make_float4(x.x * r * g.x, x.y * r * g.y, x.z * r * g.z, x.w * r * g.w);
+    }
+  }
 }
 
 }  // namespace s1

@@ -405,17 +405,21 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
   std::vector<ScanSeq> scan[2];
   std::vector<AttnSeq> attn[2];
   std::vector<AttnBlock> blocks[2];
-  const int bq = attn_block_rows(m->bf16);
-  for (int ps = 0; ps < 2; ++ps)
+  for (int ps = 0; ps < 2; ++ps) {
+    std::vector<int> lens;
+    for (const int i : order[ps]) lens.push_back(b->cu_seqlens[i + 1] - b->cu_seqlens[i]);
+    const int bq = attn_block_rows(m->bf16, lens.data(), (int)lens.size(), m->cfg.fa_q_heads);
+    p->pass[ps].attn_rows = bq;
     for (size_t k = 0; k < order[ps].size(); ++k) {
       const int i = order[ps][k];
-      const int len = b->cu_seqlens[i + 1] - b->cu_seqlens[i];
+      const int len = lens[k];
       const int pi = pre(i);
       const int P = pi >= 0 ? b->cu_seqlens[pi + 1] - b->cu_seqlens[pi] : 0;
       scan[ps].push_back({row0[i], len, pi >= 0 ? slot[pi] : -1, slot[i]});
       attn[ps].push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
       for (int q0 = 0; q0 < len; q0 += bq) blocks[ps].push_back({(int)k, q0});
     }
+  }
   // chunk-parallel scan when a pass has few (sequence, head) chains
   std::vector<ScanSeq> chunks[2];
   std::vector<ChunkSeq> cseqs[2];
@@ -572,10 +576,13 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
   char* qkv = static_cast<char*>(m->qkv);
   char* att = static_cast<char*>(m->att);
   const long long kvld = (long long)Hkv * hd;
+  bool xn_ready = false;   // xn already holds this layer's normalised input
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
-    S1_TRY(launch_rmsnorm(m->bf16, x, L.attn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
-    MARK(KC_RMSNORM);
+    if (!xn_ready) {
+      S1_TRY(launch_rmsnorm(m->bf16, x, L.attn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+      MARK(KC_RMSNORM);
+    }
     GemmArgs g{};
     g.A = xn;
     g.M = T;
@@ -620,7 +627,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
       S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s), "attention QKV projection");
       MARK(KC_GEMM_FA_QKV);
       S1_TRY(launch_attention(m->bf16, qkv, m->ld_qkv, kc, vc, (int)kvld, att, m->ld_att, ps.attn,
-                              ps.blocks, ps.n_blocks, Hq, Hkv, hd, s),
+                              ps.blocks, ps.n_blocks, Hq, Hkv, hd, ps.attn_rows, s),
              "attention");
       MARK(KC_ATTENTION);
     }
@@ -634,11 +641,17 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     go.K = L.k_o;
     go.out0 = x;
     go.ld0 = d;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, T), m->splitws, s),
+    go.norm_w = L.ffn_norm;
+    go.norm_out = xn;
+    go.norm_eps = c.rms_eps;
+    bool normed = false;
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, T), m->splitws, s, GEMM_AUTO, &normed),
            "mixer out-projection");
     MARK(KC_GEMM_O);
-    S1_TRY(launch_rmsnorm(m->bf16, x, L.ffn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
-    MARK(KC_RMSNORM);
+    if (!normed) {
+      S1_TRY(launch_rmsnorm(m->bf16, x, L.ffn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+      MARK(KC_RMSNORM);
+    }
     GemmArgs gu{};
     gu.A = xn;
     gu.lda = d;
@@ -662,7 +675,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     gd.K = c.ffn;
     gd.out0 = x;
     gd.ld0 = d;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, T), m->splitws, s),
+    if (l + 1 < c.n_layers) {   // the next layer's input norm, fused when the GEMM splits K
+      gd.norm_w = m->layers[l + 1].attn_norm;
+      gd.norm_out = xn;
+      gd.norm_eps = c.rms_eps;
+    }
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, T), m->splitws, s, GEMM_AUTO, &xn_ready),
            "FFN down");
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {

@@ -676,6 +676,38 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, lo
   }
 }
 
+// Split-K reduction into a residual row, fused with the RMSNorm of the
+// updated row: one workgroup per row, partial slabs summed in a fixed order.
+constexpr int RN_MAXV = 16;   // N <= 4 * 256 * RN_MAXV
+template <typename T>
+__global__ void __launch_bounds__(256)
+splitk_resid_norm_kernel(const float* __restrict__ ws, int split, long long stride, float* __restrict__ out,
+                         int N, int ld, const float* __restrict__ w, T* __restrict__ nout, float eps) {
+  __shared__ float red[4];
+  const long long row = blockIdx.x;
+  float4 v[RN_MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < RN_MAXV; ++k) {
+    const int c = (k * 256 + (int)threadIdx.x) * 4;
+    if (c >= N) break;
+    const long long src = row * N + c;
+    float4 t = *reinterpret_cast<const float4*>(ws + src);
+    for (int z = 1; z < split; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(ws + z * stride + src);
+      t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
+    }
+    float4* d = reinterpret_cast<float4*>(out + row * ld + c);
+    float4 o = *d;
+    o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+    *d = o;
+    v[k] = o;
+    ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+  }
+  ss = block_sum<4>(ss, red);
+  write_normed_row<T, 256, RN_MAXV>(v, ss, N, eps, w, nout + row * N);
+}
+
 template <typename T, int EPI>
 hipError_t run_reg(const GemmArgs& a, int split, hipStream_t s) {
   constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
@@ -739,7 +771,7 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, hipStream_t s) {
+hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, hipStream_t s, bool* normed) {
   if (split > 1) {
     if (epi != EPI_F32 && epi != EPI_RESID) return hipErrorInvalidValue;
     GemmArgs p = a;
@@ -748,6 +780,13 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
     p.split_stride = (long long)a.M * a.N;
     hipError_t e = run_cfg<T, EPI_PARTIAL>(p, split, cfg, s);
     if (e != hipSuccess) return e;
+    if (epi == EPI_RESID && a.norm_w && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV) {
+      hipLaunchKernelGGL(splitk_resid_norm_kernel<T>, dim3(a.M), dim3(256), 0, s, ws, split, p.split_stride,
+                         reinterpret_cast<float*>(a.out0), a.N, a.ld0, a.norm_w,
+                         reinterpret_cast<T*>(a.norm_out), a.norm_eps);
+      if (normed) *normed = true;
+      return hipGetLastError();
+    }
     const long long n4 = (long long)a.M * (a.N / 4);
     const int blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
     if (epi == EPI_RESID)
@@ -810,7 +849,8 @@ int gemm_k_tile(bool bf16) { return bf16 ? 64 : 32; }
 int gemm_tile_configs() { return N_CFG; }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws, hipStream_t s,
-                       int cfg) {
+                       int cfg, bool* normed) {
+  if (normed) *normed = false;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   GemmArgs g = a;
   if (split < 1) split = 1;
@@ -822,7 +862,8 @@ hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* 
   g.k_split = ((tiles + split - 1) / split) * bk;
   split = (a.K + g.k_split - 1) / g.k_split;
   if (split < 1) split = 1;
-  return bf16 ? dispatch<bf16_t>(epi, g, split, ws, cfg, s) : dispatch<float>(epi, g, split, ws, cfg, s);
+  return bf16 ? dispatch<bf16_t>(epi, g, split, ws, cfg, s, normed)
+              : dispatch<float>(epi, g, split, ws, cfg, s, normed);
 }
 
 }  // namespace s1

@@ -94,6 +94,7 @@ struct PassPlan {
   AttnSeq* attn = nullptr;      // device [n_seqs]
   AttnBlock* blocks = nullptr;  // device [n_blocks]
   int n_blocks = 0;
+  int attn_rows = 0;            // queries per attention workgroup
   bool chunked = false;         // scan runs chunk-parallel (few chains)
   ScanSeq* chunks = nullptr;    // device [n_chunks]
   int n_chunks = 0;

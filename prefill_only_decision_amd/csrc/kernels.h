@@ -37,6 +37,12 @@ struct GemmArgs {
   const int* pos;        // EPI_QKV: position of each row
   const float2* rope;    // EPI_QKV: (cos, sin) [max_pos][head_dim / 2]
   long long split_stride;  // EPI_PARTIAL: elements between split slabs
+  // EPI_RESID run with a K split: when norm_w is set, the reduction also
+  // writes RMSNorm(updated row) * norm_w (epsilon norm_eps) to norm_out
+  // (elem, row stride N).
+  const float* norm_w;
+  void* norm_out;
+  float norm_eps;
 };
 
 // Runs the GEMM.  tile_cfg >= 0 picks a tile configuration (0 .. 
@@ -45,9 +51,10 @@ struct GemmArgs {
 // the largest K split allowed (1 without a workspace).  With split > 1
 // (EPI_F32 or EPI_RESID only) partial tiles go to `ws` (split * M * N
 // floats) and a reduction kernel applies the epilogue in a fixed order.
+// `normed` (optional) reports whether the fused RMSNorm ran.
 constexpr int GEMM_AUTO = -1;
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
-                       hipStream_t s, int tile_cfg = GEMM_AUTO);
+                       hipStream_t s, int tile_cfg = GEMM_AUTO, bool* normed = nullptr);
 // Number of tile configurations.
 int gemm_tile_configs();
 // The K tile (elements) of the register-staged GEMM for the element type.
@@ -108,10 +115,14 @@ struct AttnBlock {
   int seq;
   int q0;           // first query (within the sequence) of this block
 };
-int attn_block_rows(bool bf16);   // queries per workgroup
+// Queries per attention workgroup for sequences of these lengths: bf16 takes
+// the largest of 128, 64, 32 that still gives 512 workgroups over Hq heads
+// (else 32); fp32 uses 64.
+int attn_block_rows(bool bf16, const int* lens, int n, int Hq);
+bool attn_block_rows_valid(bool bf16, int rows);
 hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, const void* v,
                             int ld_kv, void* o, int ld_o, const AttnSeq* seqs,
-                            const AttnBlock* blocks, int n_blocks, int Hq, int Hkv, int hd,
+                            const AttnBlock* blocks, int n_blocks, int Hq, int Hkv, int hd, int block_rows,
                             hipStream_t s);
 
 // ---------------------------------------------------------------- readout

@@ -31,35 +31,27 @@ __global__ void embed_kernel(const int32_t* __restrict__ ids, const T* __restric
 }
 
 // -------------------------------------------------------------- rmsnorm
-// out = x / sqrt(mean(x^2) + eps) * w, one wave per row.
+// out = x / sqrt(mean(x^2) + eps) * w, one workgroup of 256 threads per row;
+// the row stays in registers between the sum of squares and the scaling
+// (d <= 4 * 256 * RMS_MAXV).
+constexpr int RMS_MAXV = 16;
 template <typename T>
-__global__ void rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                               T* __restrict__ out, int T_, int d, float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= T_) return;
-  const float* xr = x + (long long)row * d;
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                      T* __restrict__ out, int d, float eps) {
+  __shared__ float red[4];
+  const long long row = blockIdx.x;
+  const float* xr = x + row * d;
+  float4 v[RMS_MAXV];
   float ss = 0.f;
-  for (int i = lane * 4; i < d; i += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int k = 0; k < RMS_MAXV; ++k) {
+    const int c = (k * 256 + (int)threadIdx.x) * 4;
+    if (c >= d) break;
+    v[k] = *reinterpret_cast<const float4*>(xr + c);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
-  ss = wave_sum(ss);
-  const float r = rsqrtf(ss / d + eps);
-  T* o = out + (long long)row * d;
-  for (int i = lane * 4; i < d; i += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + i);
-    const float4 g = *reinterpret_cast<const float4*>(w + i);
-    if constexpr (sizeof(T) == 2) {
-      uint2 u;
-      u.x = pack_bf2(v.x * r * g.x, v.y * r * g.y);
-      u.y = pack_bf2(v.z * r * g.z, v.w * r * g.w);
-      *reinterpret_cast<uint2*>(o + i) = u;
-    } else {
-      *reinterpret_cast<float4*>(o + i) =
-          make_float4(v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w);
-    }
-  }
+  ss = block_sum<4>(ss, red);
+  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, out + row * d);
 }
 
 // ---------------------------------------------------------------- merge
@@ -226,13 +218,13 @@ hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, 
 hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
                           float eps, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((T + 3) / 4);
+  if (d % 4 || d > 4 * 256 * RMS_MAXV) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, x, w,
-                       reinterpret_cast<bf16_t*>(out), T, d, eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, s, x, w,
+                       reinterpret_cast<bf16_t*>(out), d, eps);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, x, w,
-                       reinterpret_cast<float*>(out), T, d, eps);
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, s, x, w,
+                       reinterpret_cast<float*>(out), d, eps);
   return hipGetLastError();
 }
 

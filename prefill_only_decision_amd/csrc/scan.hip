@@ -347,9 +347,10 @@ hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int 
   const auto* kk = reinterpret_cast<const bf16_t*>(k);
   const auto* vv = reinterpret_cast<const bf16_t*>(v);
   auto* oo = reinterpret_cast<bf16_t*>(o);
-  // one wave per (chunk, head, 32 value columns): enough workgroups to fill the chip
-  const long long units = (long long)n_chunks * H;
-  const int nw = units >= 1024 ? 4 : (units >= 256 ? 2 : 1);
+  // four waves per (chunk, head), one per 32 value columns, sharing the
+  // chunk's Q / K / K^T tiles (measured faster than one-wave workgroups that
+  // each stage them, also at 8 chunks x 16 heads)
+  const int nw = 4;
   hipError_t e = launch_mode<MODE_SUMMARY>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates,
                                            H, gamma, nw, s);
   if (e != hipSuccess) return e;

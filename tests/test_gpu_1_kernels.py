@@ -231,7 +231,7 @@ def test_scan_f32():
         assert rel_l2(d_sf.cpu().numpy()[i], rs) < 1e-5
 
 
-def _attn_case(dtype, Hq, Hkv, hd, seqs, seed):
+def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0):
     """seqs: list of (q_len, prefix_len)."""
     torch = require_gpu()
     rng = np.random.default_rng(seed)
@@ -254,7 +254,7 @@ def _attn_case(dtype, Hq, Hkv, hd, seqs, seed):
         rq += L
         rp += P
     B.attention(dtype, dq.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), do.data_ptr(), Hq, Hkv, hd,
-                q_row0, q_len, kv_row0, pre_row0, pre_len, stream_ptr())
+                q_row0, q_len, kv_row0, pre_row0, pre_len, stream_ptr(), block_rows=block_rows)
     torch.cuda.synchronize()
     got = O.bf16_bits_to_float(host_bits(do)) if dtype == B.S1_BF16 else do.cpu().numpy().astype(np.float64)
     worst = 0.0
@@ -266,16 +266,17 @@ def _attn_case(dtype, Hq, Hkv, hd, seqs, seed):
         vv = np.concatenate([vf[pre_row0[i]:pre_row0[i] + P], vf[a:a + L]]).astype(np.float64)
         ref = O.causal_attention(qf[a:a + L].astype(np.float64), kk, vv, P + np.arange(L), np.arange(P + L))
         worst = max(worst, rel_l2(got[a:a + L], ref))
-    log(f"attention dtype={dtype} seqs={seqs}: rel L2 {worst:.2e}")
+    log(f"attention dtype={dtype} rows/workgroup={block_rows or 'auto'} seqs={seqs}: rel L2 {worst:.2e}")
     return worst
 
 
+@pytest.mark.parametrize("block_rows", [0, 32, 64, 128])
 @pytest.mark.parametrize("seqs", [
     [(1, 0), (100, 0), (128, 0), (129, 0), (300, 0)],
     [(64, 200), (1, 70), (130, 4096)],
 ])
-def test_attention_bf16(seqs):
-    assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=len(seqs)) < 1e-2
+def test_attention_bf16(seqs, block_rows):
+    assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=len(seqs), block_rows=block_rows) < 1e-2
 
 
 def test_attention_bf16_gqa5():
