@@ -427,15 +427,9 @@ gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
 
-  // Each tile walks its K tiles from a tile-dependent start (wrapping
-  // around), so that the workgroups running together do not all read the
-  // same K offset, whose rows fall on few L2 channels.  The order is fixed
-  // per tile, so results stay deterministic.
-  const int rot = (int)((7LL * blockIdx.x) % (nk > 0 ? nk : 1));
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
-    const int kr = kt + rot;
-    const int so = (kb + (kr >= nk ? kr - nk : kr) * S::BK) * 2;
+    const int so = (kb + kt * S::BK) * 2;
 #pragma unroll
     for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
 #pragma unroll
@@ -573,15 +567,9 @@ gemm_wide_kernel(GemmArgs g) {
   for (int i = 0; i < S::A_INS; ++i) va[i] = dma_voffset<S>(wave * S::A_INS + i, lane, g.lda);
 #pragma unroll
   for (int i = 0; i < S::B_INS; ++i) vw[i] = dma_voffset<S>(wave * S::B_INS + i, lane, g.ldw);
-  // Each tile walks its K tiles from a tile-dependent start (wrapping
-  // around), so that the workgroups running together do not all read the
-  // same K offset, whose rows fall on few L2 channels.  The order is fixed
-  // per tile, so results stay deterministic.
-  const int rot = (int)((7LL * blockIdx.x) % (nk > 0 ? nk : 1));
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
-    const int kr = kt + rot;
-    const int so = (kb + (kr >= nk ? kr - nk : kr) * S::BK) * 2;
+    const int so = (kb + kt * S::BK) * 2;
 #pragma unroll
     for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
 #pragma unroll
@@ -808,16 +796,21 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
 }
 
 // Configuration and K split chosen by shape (bf16), from timings of the 4B
-// projection shapes at 512, 2,048 and 16,925 rows on MI355X with weights
-// not in cache: 256 x 256 tiles once there are rows enough to fill the chip
-// with them; 256 x 192 for wide outputs of few rows (204 tiles for the FFN
-// gate/up at 512 rows, against 152 of 256 x 256); else 128 x 128 tiles (two
-// workgroups per CU when there are several waves of tiles), narrower tiles
-// when there are fewer than 192 tiles, and a K split for long reductions
-// with few output tiles.
+// projection shapes at 512 and 2,048 rows on MI355X with weights not in
+// cache (rotated through more than the 256 MB last-level cache, as in a
+// forward pass):
+//   from 1,024 rows, 256 x 256 tiles when there are 192 of them, with a K
+//   split for long reductions that have fewer;
+//   below that, 256 x 192 tiles for wide outputs (204 tiles for the FFN
+//   gate/up at 512 rows against 152 of 256 x 256), 128 x 128 tiles with a
+//   K split for long reductions, 128 x 128 (three stages; two workgroups
+//   per CU when there are several waves of tiles) down to 192 tiles, and
+//   narrower tiles below that.
 void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, int& split) {
   const long long t128 = (long long)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  const long long t256 = (long long)((a.M + 255) / 256) * ((a.N + 255) / 256);
   const bool can_split = max_split > 1 && (epi == EPI_F32 || epi == EPI_RESID);
+  const bool long_k = a.K >= 6144 && can_split;
   split = 1;
   if (!bf16) {
     cfg = 0;
@@ -825,16 +818,25 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
       while (split < max_split && t128 * (split + 1) <= 320 && a.K / (32 * (split + 1)) >= 4) ++split;
     return;
   }
-  if (a.M >= 4096) {
-    cfg = 5;
-  } else if (a.M <= 1024 && t128 >= 384) {
+  auto split_for = [&](long long tiles, long long target) {
+    int sp = 1;
+    while (sp < max_split && tiles * sp < target) ++sp;
+    return sp;
+  };
+  if (a.M >= 1024) {
+    if (t256 >= 192) {
+      cfg = 5;
+    } else if (long_k) {
+      cfg = 5;
+      split = split_for(t256, 192);
+    } else {
+      cfg = t128 >= 300 ? 2 : 1;
+    }
+  } else if (t128 >= 384) {
     cfg = 6;
-  } else if (a.K >= 6144 && can_split) {
-    cfg = 2;
-    split = t128 >= 256 ? 3 : (int)std::min<long long>(4, (256 + t128 - 1) / t128);
-    split = std::min(split, max_split);
-  } else if (t128 >= 300) {
-    cfg = 2;
+  } else if (long_k) {
+    cfg = 1;
+    split = split_for(t128, 240);
   } else if (t128 >= 192) {
     cfg = 1;
   } else {
