@@ -73,7 +73,74 @@ def cpu_baseline(shape, weights, batch, budget_s=30.0):
                       f"{len(os.sched_getaffinity(0))} host cores visible"}
 
 
+GEMM_SOURCE = os.path.join(ROOT, "prefill_only_decision_amd", "csrc", "gemm.hip")
+COPY_BYTES = 1 << 30   # the calibration copy reads and writes this many bytes
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_gemm_gate_up_{workload}.json")
+
+
+def source_digest():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of the FFN gate/up GEMM (the epilogue-3 GEMM
+    kernel) from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    1 GiB copy that --calibrate-copy adds to the run."""
+    import csv
+    import re
+    import statistics
+
+    def per_kernel(path, counter):
+        gemm, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, kib = r["Kernel_Name"], float(r["Counter_Value"])
+            if re.search(r"gemm_\w+_kernel<.*, 3>\(s1::GemmArgs\)", name):
+                gemm.append(kib * 1024)
+            elif "elementwise" in name and kib * 1024 > COPY_BYTES / 2:
+                copy.append(kib * 1024)
+        if not gemm or not copy:
+            raise SystemExit(f"{path}: no {counter} values for the gate/up GEMM or the calibration copy")
+        return statistics.median(gemm), statistics.median(copy)
+
+    g_f, c_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    g_w, c_w = per_kernel(write_csv, "WRITE_SIZE")
+    rec = {"kernel": "gemm_gate_up (epilogue 3, SwiGLU)", "workload": workload,
+           "fetch_bytes_per_launch": round(g_f * COPY_BYTES / c_f),
+           "write_bytes_per_launch": round(g_w * COPY_BYTES / c_w),
+           "raw_fetch_bytes": round(g_f), "raw_write_bytes": round(g_w),
+           "copy_bytes": COPY_BYTES, "copy_fetch_bytes": round(c_f), "copy_write_bytes": round(c_w),
+           "gemm_source_sha256": source_digest(),
+           "commands": [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.lower()} -o run -f csv -- python3 bench.py "
+                        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --profile-steps 1 --calibrate-copy"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    with open(traffic_file(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def stored_traffic(workload):
+    """Counter-measured HBM bytes per gate/up launch, or None when missing or
+    taken on another version of the GEMM source."""
+    try:
+        rec = json.load(open(traffic_file(workload)))
+    except (OSError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("gemm_source_sha256") == source_digest() else None
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-from":
+        traffic_from_counters(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else "4b-single-512")
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -81,6 +148,8 @@ def main():
     ap.add_argument("--workload", default="4b-single-512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB elementwise copy kernel (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the decision path has no "
@@ -153,7 +222,8 @@ def main():
     all_gemm_flops = 2 * tokens * shape.linear_params()
     roofline = {"bound": "mfma", "kernel": "gemm_gate_up (bf16 MFMA GEMM + SwiGLU epilogue)",
                 "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(args.workload),
+                "traffic_unit": "bytes per launch (HBM, counter-measured)",
                 "flops_per_launch": flops["gemm_gate_up"], "us_per_launch": round(avg_us, 2),
                 "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1)}
 
@@ -173,6 +243,14 @@ def main():
     }
     plan.free()
     model.free()
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                torch.mul(src, 1.0, out=dst)   # an elementwise kernel (a plain copy may go to the DMA engines)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, w, batch)
     print(json.dumps(out), flush=True)
