@@ -26,6 +26,9 @@ def _compile(src):
 
 
 def build(verbose=False):
+    # a failed build must not leave the previous library behind to be loaded
+    if os.path.exists(LIB):
+        os.remove(LIB)
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))

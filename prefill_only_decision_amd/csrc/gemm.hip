@@ -48,6 +48,25 @@ __device__ __forceinline__ float log_sigmoid(float z) {
 }
 __device__ __forceinline__ float silu(float a) { return a / (1.f + __expf(-a)); }
 
+// Global-memory views of the epilogue's pointers: through the generic
+// pointers of GemmArgs the compiler emits flat accesses, whose results it
+// must wait for with vmcnt(0) and lgkmcnt(0) (flat operations may complete
+// out of order), one element at a time.
+template <typename T>
+using gmem = __attribute__((address_space(1))) T;
+template <typename T>
+__device__ __forceinline__ gmem<T>* gptr(void* p) {
+  return (gmem<T>*)p;
+}
+template <typename T>
+__device__ __forceinline__ const gmem<T>* gptr(const void* p) {
+  return (const gmem<T>*)p;
+}
+
+// Loads an epilogue needs (the residual, positions, RoPE factors) are issued
+// for a whole 32-row MFMA tile before its stores: a store to the output may
+// alias a later load as far as the compiler knows, so element-by-element
+// read-modify-write would wait for the memory latency once per element.
 template <typename T, int EPI, int TM, int TN>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0,
                                          int cn0, int lane, int split_idx) {
@@ -60,40 +79,58 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
       if (cb >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
+        const int rb = rm0 + 32 * i;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const int f = (cb >> 1) + cl;
+          if (f >= g.n_valid) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rm0 + 32 * i + acc_row(r, lane);
-          if (row >= g.M) continue;
-          const float a1 = acc[i][j][r], a2 = acc[i][j + 1][r];
-          if constexpr (EPI == EPI_SWIGLU) {
-            const int f = (cb >> 1) + cl;
-            if (f < g.n_valid)
-              reinterpret_cast<T*>(g.out0)[(long long)row * g.ld0 + f] = from_f<T>(silu(a1) * a2);
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (row < g.M)
+              gptr<T>(g.out0)[(long long)row * g.ld0 + f] = from_f<T>(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+          }
+        } else if (cb < g.nsplit2) {
+          // rotate-half pair (d, d + hd/2): permuted to columns (cb+cl, cb+32+cl)
+          const int hc = cb % g.head_dim;
+          const int dim = 32 * (hc >> 6) + cl;
+          float2 cs[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = min(rb + acc_row(r, lane), g.M - 1);
+            const unsigned long long bits =
+                gptr<unsigned long long>(g.rope)[(long long)gptr<int>(g.pos)[row] * (g.head_dim >> 1) + dim];
+            cs[r] = __builtin_bit_cast(float2, bits);
+          }
+          gmem<T>* dst;
+          long long base;
+          int ld;
+          if (cb < g.nsplit) {
+            dst = gptr<T>(g.out0);
+            base = cb;
+            ld = g.ld0;
           } else {
-            if (cb < g.nsplit2) {
-              // rotate-half pair (d, d + hd/2): permuted to columns (cb+cl, cb+32+cl)
-              const int hc = cb % g.head_dim;
-              const int dim = 32 * (hc >> 6) + cl;
-              const float2 cs = g.rope[(long long)g.pos[row] * (g.head_dim >> 1) + dim];
-              const float r1 = a1 * cs.x - a2 * cs.y;
-              const float r2 = a2 * cs.x + a1 * cs.y;
-              T* dst;
-              long long off;
-              if (cb < g.nsplit) {
-                dst = reinterpret_cast<T*>(g.out0);
-                off = (long long)row * g.ld0 + cb;
-              } else {
-                dst = reinterpret_cast<T*>(g.out1);
-                off = (long long)row * g.ld1 + (cb - g.nsplit);
-              }
-              dst[off + cl] = from_f<T>(r1);
-              dst[off + 32 + cl] = from_f<T>(r2);
-            } else {
-              T* dst = reinterpret_cast<T*>(g.out2);
-              const long long off = (long long)row * g.ld2 + (cb - g.nsplit2);
-              dst[off + cl] = from_f<T>(a1);
-              if (cb + 32 < g.N) dst[off + 32 + cl] = from_f<T>(a2);
-            }
+            dst = gptr<T>(g.out1);
+            base = cb - g.nsplit;
+            ld = g.ld1;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (row >= g.M) continue;
+            const float a1 = acc[i][j][r], a2 = acc[i][j + 1][r];
+            const long long off = (long long)row * ld + base;
+            dst[off + cl] = from_f<T>(a1 * cs[r].x - a2 * cs[r].y);
+            dst[off + 32 + cl] = from_f<T>(a2 * cs[r].x + a1 * cs[r].y);
+          }
+        } else {
+          gmem<T>* dst = gptr<T>(g.out2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (row >= g.M) continue;
+            const long long off = (long long)row * g.ld2 + (cb - g.nsplit2);
+            dst[off + cl] = from_f<T>(acc[i][j][r]);
+            if (cb + 32 < g.N) dst[off + 32 + cl] = from_f<T>(acc[i][j + 1][r]);
           }
         }
       }
@@ -105,22 +142,36 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
       if (col >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
+        const int rb = rm0 + 32 * i;
+        if constexpr (EPI == EPI_RESID) {
+          gmem<float>* out = gptr<float>(g.out0);
+          float prev[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rm0 + 32 * i + acc_row(r, lane);
-          if (row >= g.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (EPI == EPI_F32) {
-            reinterpret_cast<float*>(g.out0)[(long long)row * g.ld0 + col] = v;
-          } else if constexpr (EPI == EPI_RESID) {
-            reinterpret_cast<float*>(g.out0)[(long long)row * g.ld0 + col] += v;
-          } else if constexpr (EPI == EPI_PARTIAL) {
-            reinterpret_cast<float*>(g.out0)[split_idx * g.split_stride + (long long)row * g.ld0 + col] = v;
-          } else if constexpr (EPI == EPI_GATE) {
-            if (col < g.nsplit)
-              reinterpret_cast<T*>(g.out0)[(long long)row * g.ld0 + col] = from_f<T>(v);
-            else
-              reinterpret_cast<float*>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = log_sigmoid(v);
+          for (int r = 0; r < 16; ++r) {
+            const int row = min(rb + acc_row(r, lane), g.M - 1);
+            prev[r] = out[(long long)row * g.ld0 + col];
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (row < g.M) out[(long long)row * g.ld0 + col] = prev[r] + acc[i][j][r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (row >= g.M) continue;
+            const float v = acc[i][j][r];
+            if constexpr (EPI == EPI_F32) {
+              gptr<float>(g.out0)[(long long)row * g.ld0 + col] = v;
+            } else if constexpr (EPI == EPI_PARTIAL) {
+              gptr<float>(g.out0)[split_idx * g.split_stride + (long long)row * g.ld0 + col] = v;
+            } else if constexpr (EPI == EPI_GATE) {
+              if (col < g.nsplit)
+                gptr<T>(g.out0)[(long long)row * g.ld0 + col] = from_f<T>(v);
+              else
+                gptr<float>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = log_sigmoid(v);
+            }
           }
         }
       }
@@ -317,9 +368,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 __device__ __forceinline__ int32x4 buffer_rsrc(const void* base, int bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   int32x4 r;
-  r.x = static_cast<int>(static_cast<uint32_t>(a));
-  r.y = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
-  r.z = bytes;
+  // readfirstlane: the values are wave-uniform; saying so keeps them in
+  // scalar registers, which the buffer instructions require
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
   r.w = 0x00020000;
   return r;
 }
@@ -352,8 +405,13 @@ __device__ __forceinline__ T pin_sgpr(T v) {
   asm volatile("" : "+s"(v));
   return v;
 }
+// The RoPE/KV epilogue needs the most arguments; pinned, they can leave too
+// few scalar registers for the 128-bit buffer resource of the operand loads,
+// so that epilogue reads its arguments where it uses them.
+template <int EPI>
 __device__ __forceinline__ GemmArgs pin_epilogue_args(const GemmArgs& g) {
   GemmArgs e = g;
+  if constexpr (EPI == EPI_QKV) return e;
   e.M = pin_sgpr(g.M);
   e.N = pin_sgpr(g.N);
   e.out0 = pin_sgpr(g.out0);
@@ -404,7 +462,7 @@ __global__ void __launch_bounds__(S::NT)
 __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 gemm_lds_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  const GemmArgs e = pin_epilogue_args(g);
+  const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN, wn = wave % S::WN;
@@ -545,7 +603,7 @@ template <typename S, int EPI>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wide_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  const GemmArgs e = pin_epilogue_args(g);
+  const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / S::WN, wn = wave % S::WN;
