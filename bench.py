@@ -214,7 +214,10 @@ def main():
     flops = gemm_flops(shape, tokens)
     launches, total_us = prof["gemm_gate_up"]
     avg_us = total_us / launches
-    achieved = flops["gemm_gate_up"] / (avg_us * 1e-6) / 1e12
+    # flops of the whole step over the kernel's time per step: a branched
+    # request runs the layer once per pass (prefix, then branches)
+    step_flops = flops["gemm_gate_up"] * shape.n_layers     # every layer, every token
+    achieved = step_flops / (total_us / steps_p * 1e-6) / 1e12
     kernels = {k: {"launches_per_step": n // steps_p, "us_per_step": round(us / steps_p, 1),
                    "us_per_launch": round(us / n, 2)} for k, (n, us) in sorted(prof.items())}
     gemm_us = sum(prof[k][1] for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
@@ -224,7 +227,8 @@ def main():
                 "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": stored_traffic(args.workload),
                 "traffic_unit": "bytes per launch (HBM, counter-measured)",
-                "flops_per_launch": flops["gemm_gate_up"], "us_per_launch": round(avg_us, 2),
+                "flops_per_step": step_flops, "launches_per_step": launches // steps_p,
+                "us_per_launch": round(avg_us, 2),
                 "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1)}
 
     out = {
