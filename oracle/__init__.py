@@ -25,6 +25,10 @@ or fusion:
   question's marker position (Cua-S1 issue, first plan comment), and the
   answer fields (sys1rust README, "Try it": answer types and the two
   confidence numbers);
+* language-model features: token log-probabilities normalised over the full
+  vocabulary, computed chunk by chunk, and a candidate score normalised across
+  the candidates of a question (RFC #114, section 4, note under the semantics
+  table);
 * branches: a branch is the plain forward of prefix + suffix (RFC #114,
   section 4 "Branching" row and the "Plan: native OmniJev-4B v1.1" comment,
   which states a continuation equals the plain forward up to rounding).
@@ -39,11 +43,11 @@ from .reference import (OracleModel, bf16_bits_to_float, round_to_bf16_bits,
                         rms_norm, rope_rotate_half, la_scan_recurrent,
                         la_scan_unrolled, la_scan_segmented, causal_attention, swiglu,
                         lora_merge, softmax, decision_fields, readout,
-                        prefill_decide, QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL)
+                        vocab_log_probs, candidate_log_probs, prefill_decide, QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL)
 
 __all__ = [
     "OracleModel", "bf16_bits_to_float", "round_to_bf16_bits", "rms_norm",
     "rope_rotate_half", "la_scan_recurrent", "la_scan_unrolled", "la_scan_segmented",
     "causal_attention", "swiglu", "lora_merge", "softmax", "decision_fields",
-    "readout", "prefill_decide", "QTYPE_CHOICE", "QTYPE_SCORE", "QTYPE_NOUL",
+    "readout", "vocab_log_probs", "candidate_log_probs", "prefill_decide", "QTYPE_CHOICE", "QTYPE_SCORE", "QTYPE_NOUL",
 ]

@@ -32,6 +32,9 @@ Readings taken where the pages are silent (tags used below):
         temperature or bias.
   (R15) LoRA targets: q, k, v, o of both mixer kinds (+ FFN gate, up, down on
         the 4B/27B shapes); the decay-gate projection is not adapted.
+  (R21) a feature candidate scores the sum of its tokens' full-vocabulary
+        log-probabilities, normalised by a log-softmax across the candidates
+        of its question (the six-feature composition on top is not built).
 """
 import math
 from concurrent.futures import ThreadPoolExecutor
@@ -241,6 +244,60 @@ def readout(h_row, w_final, e_rows, eps, qtype):
     return p, decision_fields(p, qtype)
 
 
+def vocab_log_probs(h_rows, w_final, embed, eps, rows, tokens, dtype=np.float64, chunk=16384):
+    """Full-vocabulary token log-probabilities (the language-model features of
+    [rfc114] section 4, note under the semantics table: token log-probabilities
+    normalised over the whole vocabulary, with the vocabulary work done in
+    bounded chunks; [rfc114-plan]: the log-softmax runs over every row of the
+    tied embedding, with the head's logits taken to fp32 first -- here the
+    oracle's float type).
+
+    h_rows [R, d]: residual-stream rows before the final norm.  embed: the raw
+    tied embedding [V, d] (bf16 bit patterns or floats), decoded `chunk` rows
+    at a time so that no [V, d] float copy is held.  Target n is token
+    tokens[n] read from row rows[n].  With hn = RMSNorm(h; w_final) and
+    z[r, v] = hn[r] . E[v] for every v in [0, V):
+        lse[r]  = log sum_v exp(z[r, v])
+        logp[n] = z[rows[n], tokens[n]] - lse[rows[n]]
+    (the log-sum-exp is evaluated as m + log sum exp(z - m) with m the row
+    maximum, the same number).  Returns (logp [n], lse [R])."""
+    hn = rms_norm(np.asarray(h_rows, dtype=dtype), np.asarray(w_final, dtype=dtype), eps)
+    V = embed.shape[0]
+    z = np.empty((hn.shape[0], V), dtype=dtype)
+    for v0 in range(0, V, chunk):
+        e = embed[v0:v0 + chunk]
+        e = bf16_bits_to_float(e, dtype) if e.dtype == np.uint16 else e.astype(dtype)
+        z[:, v0:v0 + e.shape[0]] = hn @ e.T
+    m = z.max(axis=1)
+    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    rows = np.asarray(rows, dtype=np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    return z[rows, tokens] - lse[rows], lse
+
+
+def candidate_log_probs(logp, cand_offsets, cand_group):
+    """Candidate scores and their normalisation across the candidates of one
+    question ([rfc114] section 4, note under the semantics table: the token
+    log-probabilities are normalised over the vocabulary and then again across
+    the candidates of the same question).  Reading (R21): a candidate owns the
+    targets cand_offsets[c] .. cand_offsets[c+1]-1 and scores the sum of their
+    log-probabilities (the log-probability of its whole token string; an empty
+    candidate scores 0); candidates with equal cand_group form one question,
+    normalised as  norm[c] = lp[c] - log sum_{c' in group(c)} exp(lp[c']).
+    Returns (lp [C], norm [C])."""
+    logp = np.asarray(logp, dtype=np.float64)
+    off = np.asarray(cand_offsets, dtype=np.int64)
+    grp = np.asarray(cand_group, dtype=np.int64)
+    C = len(grp)
+    lp = np.array([logp[off[c]:off[c + 1]].sum() for c in range(C)], dtype=np.float64)
+    norm = np.empty(C, dtype=np.float64)
+    for g in np.unique(grp):
+        sel = np.nonzero(grp == g)[0]
+        m = lp[sel].max()
+        norm[sel] = lp[sel] - (m + math.log(np.exp(lp[sel] - m).sum()))
+    return lp, norm
+
+
 # --------------------------------------------------------------------------
 # the hybrid decoder
 # --------------------------------------------------------------------------
@@ -413,6 +470,12 @@ class OracleModel:
     def decide(self, x_row, qtype, option_ids):
         e = self.embed(option_ids)
         return readout(x_row, self.W("final_norm"), e, self.s.rms_eps, qtype)
+
+    def token_log_probs(self, x_rows, rows, tokens):
+        """vocab_log_probs over this model's final norm and tied embedding;
+        x_rows are final residual-stream rows.  Returns (logp, lse)."""
+        return vocab_log_probs(x_rows, self.W("final_norm"), self._raw["embed"], self.s.rms_eps,
+                               rows, tokens, dtype=self.dtype)
 
 
 def prefill_decide(model, batch, mode="plain", capture=None, seqs=None):

@@ -218,6 +218,32 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         return f
     monkeypatch.setattr(P.O, "decision_fields", fields_unnormalised)
     assert fails(P.test_readout_golden_special_cases)
+    monkeypatch.undo()
+
+    real_vlp = O.vocab_log_probs
+    def vlp_last_chunk_dropped(h, w, E, eps, rows, toks, dtype=np.float64, chunk=16384):
+        V = E.shape[0]                           # the denominator loses the ragged last chunk
+        keep = V - (V % chunk) if V % chunk else V
+        logp, lse = real_vlp(h, w, E, eps, rows, toks, dtype, chunk)
+        _, short = real_vlp(h, w, E[:keep], eps, [0], [0], dtype, chunk)
+        r = np.asarray(rows)
+        return logp + lse[r] - short[r], short
+    monkeypatch.setattr(P.O, "vocab_log_probs", vlp_last_chunk_dropped)
+    assert fails(P.test_vocab_log_probs_normalise_over_the_whole_vocabulary)
+    monkeypatch.undo()
+
+    def vlp_no_final_norm(h, w, E, eps, rows, toks, dtype=np.float64, chunk=16384):
+        hn = np.asarray(h, dtype=np.float64) * np.asarray(w)  # gain kept, 1/rms lost
+        return real_vlp(hn * 1e6, np.ones(len(w)), E, 0.0, rows, toks, dtype, chunk)
+    monkeypatch.setattr(P.O, "vocab_log_probs", vlp_no_final_norm)
+    assert fails(P.test_vocab_log_probs_brute_force_loops)
+    monkeypatch.undo()
+
+    real_cand = O.candidate_log_probs
+    def cand_over_all_groups(logp, off, grp):     # normalises across questions
+        return real_cand(logp, off, np.zeros(len(grp), dtype=np.int64))
+    monkeypatch.setattr(P.O, "candidate_log_probs", cand_over_all_groups)
+    assert fails(P.test_candidate_log_probs_hand_values)
 
 
 def test_bf16_activation_mode():
@@ -238,3 +264,21 @@ def test_bf16_activation_mode():
     hx = O.prefill_decide(O.OracleModel(shape, w.tensors), b, capture=cap)["hidden"][0]
     drift = [np.linalg.norm(hb[l] - hx[l]) / np.linalg.norm(hx[l]) for l in range(1, 5)]
     assert all(1e-4 < d < 3e-2 for d in drift), drift
+
+
+def test_token_log_probs_match_torch_log_softmax(tiny):
+    """The model-level features against torch's log_softmax over the full
+    tied-embedding logits of the independent torch formulation's rows."""
+    shape, w = tiny
+    ids = make_batch("tiny-fp32").tokens_of(0)
+    m = O.OracleModel(shape, w.tensors)
+    x, _, _ = m.forward(ids)
+    F = torch.nn.functional
+    xt = torch.from_numpy(_torch_forward(shape, w.tensors, ids))
+    hn = F.rms_norm(xt, (shape.d_model,), torch.from_numpy(w.tensors["final_norm"].astype(np.float64)),
+                    eps=shape.rms_eps)
+    ref = F.log_softmax(hn @ torch.from_numpy(w.tensors["embed"].astype(np.float64)).T, dim=-1).numpy()
+    rows = np.arange(len(ids) - 1)
+    logp, lse = m.token_log_probs(x, rows, ids[1:])
+    np.testing.assert_allclose(logp, ref[rows, ids[1:]], rtol=1e-9, atol=1e-9)
+    assert lse.shape == (len(ids),)

@@ -330,3 +330,110 @@ def test_readout_applies_final_norm_and_tied_rows():
     z = [float(np.dot(E[i], hn)) for i in range(3)]
     Z = sum(math.exp(t) for t in z)
     np.testing.assert_allclose(p, [math.exp(t) / Z for t in z], rtol=1e-12)
+
+
+# ---------------------------------------------- full-vocabulary log-probs
+def _loop_log_probs(h, w, E, eps, rows, tokens):
+    """Brute force with scalar loops: final norm, every logit, log-sum-exp."""
+    out = []
+    for r, t in zip(rows, tokens):
+        x = h[r]
+        ms = sum(float(v) * float(v) for v in x) / len(x)
+        hn = [float(x[i]) / math.sqrt(ms + eps) * float(w[i]) for i in range(len(x))]
+        z = [sum(float(E[v][i]) * hn[i] for i in range(len(x))) for v in range(len(E))]
+        out.append(z[t] - math.log(sum(math.exp(zv) for zv in z)))
+    return out
+
+
+def test_vocab_log_probs_brute_force_loops():
+    R, V, d = 3, 37, 8
+    h = rng.standard_normal((R, d)) * 2
+    w = rng.standard_normal(d)
+    E = rng.standard_normal((V, d))
+    rows = [0, 2, 1, 2, 0]
+    toks = [5, 36, 0, 17, 5]
+    logp, lse = O.vocab_log_probs(h, w, E, 1e-6, rows, toks, chunk=10)
+    np.testing.assert_allclose(logp, _loop_log_probs(h, w, E, 1e-6, rows, toks), rtol=1e-12)
+    assert lse.shape == (R,)
+
+
+def test_vocab_log_probs_normalise_over_the_whole_vocabulary():
+    R, V, d = 4, 50, 16
+    h = rng.standard_normal((R, d))
+    w = rng.uniform(0.5, 1.5, d)
+    E = rng.standard_normal((V, d)) * 3
+    rows = np.repeat(np.arange(R), V)
+    toks = np.tile(np.arange(V), R)
+    logp, _ = O.vocab_log_probs(h, w, E, 1e-6, rows, toks, chunk=7)
+    np.testing.assert_allclose(np.exp(logp).reshape(R, V).sum(axis=1), 1.0, rtol=1e-12)
+    assert (logp < 0).all()
+
+
+def test_vocab_log_probs_library_log_softmax_identity_head():
+    # E = s * I (V = d), unit gains and rows of mean square 1: the logits are
+    # s * h / sqrt(1 + eps), so the features are scipy's log_softmax of them,
+    # also at logits far beyond float64's exp range.
+    from scipy.special import log_softmax
+    d, eps = 24, 1e-6
+    for s in (1.0, 40.0, 2000.0):
+        h = rng.standard_normal((2, d))
+        h /= np.sqrt(np.mean(h * h, axis=1, keepdims=True))
+        rows = np.repeat([0, 1], d)
+        toks = np.tile(np.arange(d), 2)
+        logp, lse = O.vocab_log_probs(h, np.ones(d), s * np.eye(d), eps, rows, toks, chunk=5)
+        ref = log_softmax(s * h / math.sqrt(1 + eps), axis=1).reshape(-1)
+        assert np.isfinite(logp).all() and np.isfinite(lse).all()
+        np.testing.assert_allclose(logp, ref, rtol=1e-12, atol=1e-12 * s)
+
+
+def test_vocab_log_probs_identical_rows_give_minus_log_v():
+    V, d = 1000, 12
+    E = np.tile(rng.standard_normal(d), (V, 1))
+    h = rng.standard_normal((2, d)) * 5
+    logp, _ = O.vocab_log_probs(h, rng.standard_normal(d), E, 1e-6, [0, 1, 1], [0, 999, 512])
+    np.testing.assert_allclose(logp, -math.log(V), rtol=1e-13)
+
+
+def test_vocab_log_probs_bf16_embedding_and_chunking():
+    # bf16 bit patterns decode per chunk; every chunk size (including one that
+    # leaves a ragged last chunk) gives the same numbers as the decoded matrix.
+    V, d = 301, 32
+    Ef = rng.standard_normal((V, d)) * 0.5
+    bits = O.round_to_bf16_bits(Ef)
+    h = rng.standard_normal((3, d))
+    w = rng.standard_normal(d)
+    rows, toks = [0, 1, 2, 2], [300, 0, 150, 7]
+    ref, ref_lse = O.vocab_log_probs(h, w, O.bf16_bits_to_float(bits), 1e-6, rows, toks, chunk=V)
+    for chunk in (1, 64, 100, 301, 4096):
+        got, lse = O.vocab_log_probs(h, w, bits, 1e-6, rows, toks, chunk=chunk)
+        np.testing.assert_allclose(got, ref, rtol=1e-13)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+
+
+def test_vocab_log_probs_option_softmax_equals_readout():
+    # Normalising the options' full-vocabulary log-probabilities across the
+    # options gives back the readout's option softmax: the vocabulary
+    # denominator cancels.
+    V, d = 200, 16
+    E = rng.standard_normal((V, d))
+    h = rng.standard_normal(d)
+    w = rng.standard_normal(d)
+    opts = [17, 3, 150, 88]
+    p, _ = O.readout(h, w, E[opts], 1e-6, O.QTYPE_CHOICE)
+    logp, _ = O.vocab_log_probs(h[None], w, E, 1e-6, [0] * 4, opts)
+    _, norm = O.candidate_log_probs(logp, [0, 1, 2, 3, 4], [0, 0, 0, 0])
+    np.testing.assert_allclose(np.exp(norm), p, rtol=1e-12)
+    assert (logp < np.log(p)).all()     # the vocabulary holds other tokens too
+
+
+def test_candidate_log_probs_hand_values():
+    logp = np.log([0.5, 0.25, 0.1, 0.2, 0.4])
+    # group 7: candidate 0 = tokens 0, 1 (prob 0.125), candidate 2 = token 4 (0.4)
+    # group 3: candidate 1 = tokens 2, 3 (0.02), candidate 3 = nothing (score 0)
+    lp, norm = O.candidate_log_probs(logp, [0, 2, 4, 5, 5], [7, 3, 7, 3])
+    np.testing.assert_allclose(lp, np.log([0.125, 0.02, 0.4, 1.0]), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(np.exp(norm), [0.125 / 0.525, 0.02 / 1.02, 0.4 / 0.525, 1 / 1.02],
+                               rtol=1e-13)
+    # a question with one candidate normalises to log 1 = 0
+    _, n1 = O.candidate_log_probs([-3.0, -4.0], [0, 2], [5])
+    assert n1[0] == 0.0
