@@ -221,10 +221,46 @@ int64_t s1_plan_tokens(const s1_plan* p);
 int s1_plan_set_capture(s1_plan* p, int32_t n_rows, const int32_t* rows, float* d_hidden);
 
 /*
+ * Full-vocabulary language-model features (RFC #114, section 4, note under
+ * the semantics table: token log-probabilities normalised over the whole
+ * vocabulary, then across the candidates of the same question; RFC #114
+ * comment "Plan: native OmniJev-4B v1.1": the log-softmax runs over every
+ * row of the tied embedding, in fp32).  Target n reads the final hidden state
+ * of packed token rows[n] (0-based index into the request's token_ids) and
+ * scores token tokens[n] in [0, vocab):
+ *   h = RMSNorm(x_final[rows[n]]; final_norm), z_v = h . E[v] for every v,
+ *   logp[n] = z_tokens[n] - log sum_v exp(z_v).
+ * Candidate c owns targets cand_offsets[c] .. cand_offsets[c+1]-1
+ * (non-decreasing offsets, last <= n_targets) and scores the sum of their
+ * logp (0 when it owns none); candidates with equal cand_group form one
+ * question and cand_norm[c] = cand_logp[c] - log sum over its question of
+ * exp(cand_logp).  Host arrays, copied during the call.
+ */
+typedef struct {
+  int32_t n_targets;
+  const int32_t* rows;
+  const int32_t* tokens;
+  int32_t n_cands;
+  const int32_t* cand_offsets;   /* [n_cands + 1] */
+  const int32_t* cand_group;     /* [n_cands] */
+} s1_features;
+
+/* Compute the features on every following s1_plan_run, after the readout, on
+ * the same stream: d_logp[n_targets], d_cand_logp[n_cands] and
+ * d_cand_norm[n_cands] are device memory (the candidate buffers may be NULL
+ * when n_cands = 0).  f = NULL or n_targets = 0 switches them off.  The plan
+ * allocates the feature workspace here (about 8 * 32 * ceil(vocab / 128)
+ * bytes per 32 distinct rows plus 8 * d_model bytes per row).  bf16 models
+ * need d_model % 128 == 0.  Errors: S1_EINVAL (ranges, offsets, NULL
+ * outputs), S1_ENOMEM, S1_EDEVICE. */
+int s1_plan_set_features(s1_plan* p, const s1_features* f, float* d_logp, float* d_cand_logp,
+                         float* d_cand_norm);
+
+/*
  * Per-kernel timing.  Runs the plan once like s1_plan_run, with a HIP event
  * recorded on hip_stream after every kernel launch, synchronises, and returns
  * the time between consecutive events summed per kernel family (names such as
- * "gemm_gate_up", "la_scan", "attention", "readout"), with the number of
+ * "gemm_gate_up", "la_scan", "attention", "readout", "vocab_lse"), with the number of
  * launches.  out has room for max_out entries; *n_out receives the count.
  */
 typedef struct {

@@ -114,6 +114,27 @@ int s1k_readout(int32_t dtype, const float* x, int32_t d, const float* w_final, 
                 const int32_t* opt_ids, const uint8_t* q_type, float* probs, void* decisions,
                 void* hip_stream);
 
+/* Full-vocabulary log-sum-exp of R rows of x (fp32 [*, d]) after the final
+ * RMSNorm: lse[r] = log sum_v exp(h_r . E[v]), h_r = RMSNorm(x[rows[r]];
+ * w_final), over all V rows of E (elem [V, d]); rows device int32 [R], lse
+ * device fp32 [R].  bf16: the logits are formed on MFMA from h split into a
+ * bf16 pair hi + lo (|h - hi - lo| <= 2^-17 |h|) with fp32 accumulation and
+ * need d % 128 == 0; fp32: d % 4 == 0.  Allocates its workspace on the stream
+ * (stream-ordered) and returns without synchronising.  (RFC #114, section 4,
+ * note under the semantics table: vocabulary work in bounded chunks.) */
+int s1k_vocab_lse(int32_t dtype, const float* x, int32_t d, const float* w_final, float eps, const void* E,
+                  int32_t V, int32_t R, const int32_t* rows, float* lse, void* hip_stream);
+
+/* Token log-probabilities and candidate normalisation over rows of x (fp32
+ * [n_rows, d]), as s1_plan_set_features in s1.h describes, with rows[] indexing
+ * x directly.  rows, tokens, cand_offsets and cand_group are host arrays;
+ * logp [n_targets], cand_logp and cand_norm [n_cands] device fp32.
+ * Synchronises the stream before returning. */
+int s1k_token_logprobs(int32_t dtype, const float* x, int32_t n_rows, int32_t d, const float* w_final, float eps,
+                       const void* E, int32_t V, int32_t n_targets, const int32_t* rows, const int32_t* tokens,
+                       int32_t n_cands, const int32_t* cand_offsets, const int32_t* cand_group, float* logp,
+                       float* cand_logp, float* cand_norm, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,10 +23,10 @@ LORA_BITS = {"q": 1, "k": 2, "v": 4, "o": 8, "gate": 16, "up": 32, "down": 64}
 EXPORTS = (
     "s1_load_weights", "s1_prefill_decide", "s1_free", "s1_last_error", "s1_validate",
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
-    "s1_plan_profile", "s1_plan_set_graph",
+    "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
-    "s1k_attention", "s1k_readout",
+    "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs",
 )
 
 
@@ -76,6 +76,12 @@ DECISION_DTYPE = np.dtype([("choice", np.int32), ("score", np.float32), ("noul",
                            ("entropy_confidence", np.float32)])
 
 
+class Features(C.Structure):
+    _fields_ = [("n_targets", C.c_int32), ("rows", C.POINTER(C.c_int32)), ("tokens", C.POINTER(C.c_int32)),
+                ("n_cands", C.c_int32), ("cand_offsets", C.POINTER(C.c_int32)),
+                ("cand_group", C.POINTER(C.c_int32))]
+
+
 class KernelTime(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("launches", C.c_int32), ("total_us", C.c_double)]
 
@@ -109,6 +115,7 @@ def load_library(path=LIB_PATH):
         "s1_plan_tokens": (i64, [vp]),
         "s1_plan_set_capture": (C.c_int, [vp, i32, vp, vp]),
         "s1_plan_set_graph": (C.c_int, [vp, i32]),
+        "s1_plan_set_features": (C.c_int, [vp, C.POINTER(Features), vp, vp, vp]),
         "s1_plan_profile": (C.c_int, [vp, vp, vp, vp, vp, C.POINTER(KernelTime), i32, C.POINTER(i32)]),
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
@@ -120,6 +127,9 @@ def load_library(path=LIB_PATH):
         "s1k_la_scan_chunked": (C.c_int, [vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
         "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]),
         "s1k_readout": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "s1k_vocab_lse": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, i32, vp, vp, vp]),
+        "s1k_token_logprobs": (C.c_int, [i32, vp, i32, i32, vp, f32, vp, i32, i32, vp, vp, i32, vp, vp,
+                                         vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -198,6 +208,24 @@ def make_batch(b):
     cb.opt_offsets = _ptr(keep.i32(b.opt_offsets), C.c_int32)
     cb.opt_ids = _ptr(keep.i32(b.opt_ids), C.c_int32)
     return cb, keep
+
+
+def make_features(rows, tokens, cand_offsets=None, cand_group=None):
+    """s1_features from target rows / tokens and candidate spans / groups."""
+    keep = _Arrays()
+    f = Features()
+    r = keep.i32(rows)
+    f.n_targets = len(r)
+    f.rows = _ptr(r, C.c_int32)
+    f.tokens = _ptr(keep.i32(tokens), C.c_int32)
+    if cand_group is not None and len(cand_group):
+        g = keep.i32(cand_group)
+        f.n_cands = len(g)
+        f.cand_offsets = _ptr(keep.i32(cand_offsets), C.c_int32)
+        f.cand_group = _ptr(g, C.c_int32)
+    else:
+        f.n_cands = 0
+    return f, keep
 
 
 def validate(config, batch):
@@ -312,6 +340,16 @@ class Plan:
                                                  rows.ctypes.data_as(C.c_void_p),
                                                  C.c_void_p(d_hidden_ptr)))
 
+    def set_features(self, rows, tokens, cand_offsets, cand_group, d_logp_ptr, d_cand_logp_ptr=0,
+                     d_cand_norm_ptr=0):
+        """Full-vocabulary log-probabilities of (rows[n], tokens[n]) and the
+        candidate scores, written by every following run; empty rows switch
+        them off."""
+        f, keep = make_features(rows, tokens, cand_offsets, cand_group)
+        check(load_library().s1_plan_set_features(self.handle, C.byref(f), C.c_void_p(d_logp_ptr),
+                                                  C.c_void_p(d_cand_logp_ptr or None),
+                                                  C.c_void_p(d_cand_norm_ptr or None)))
+
     def free(self):
         if self.handle:
             load_library().s1_plan_free(self.handle)
@@ -400,3 +438,19 @@ def readout(dtype, x, d, w_final, eps, E, Q, rows, opt_offsets, opt_ids, q_type,
     return _k("s1k_readout", dtype, C.c_void_p(x), d, C.c_void_p(w_final), C.c_float(eps), C.c_void_p(E), Q,
               C.c_void_p(rows), C.c_void_p(opt_offsets), C.c_void_p(opt_ids), C.c_void_p(q_type),
               C.c_void_p(probs), C.c_void_p(decisions), _stream(stream))
+
+
+def vocab_lse(dtype, x, d, w_final, eps, E, V, R, rows, lse, stream=None):
+    return _k("s1k_vocab_lse", dtype, C.c_void_p(x), d, C.c_void_p(w_final), C.c_float(eps), C.c_void_p(E), V, R,
+              C.c_void_p(rows), C.c_void_p(lse), _stream(stream))
+
+
+def token_logprobs(dtype, x, n_rows, d, w_final, eps, E, V, rows, tokens, cand_offsets, cand_group, logp,
+                   cand_logp=0, cand_norm=0, stream=None):
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    g = np.ascontiguousarray(cand_group if cand_group is not None else [], dtype=np.int32)
+    off = np.ascontiguousarray(cand_offsets if cand_offsets is not None else [0], dtype=np.int32)
+    return _k("s1k_token_logprobs", dtype, C.c_void_p(x), n_rows, d, C.c_void_p(w_final), C.c_float(eps),
+              C.c_void_p(E), V, len(rows), rows, tokens, len(g), off, g, C.c_void_p(logp),
+              C.c_void_p(cand_logp or None), C.c_void_p(cand_norm or None), _stream(stream))

@@ -182,6 +182,12 @@ int s1_plan_set_capture(s1_plan* p, int32_t n_rows, const int32_t* rows, float* 
   return set_capture(p->p, n_rows, rows, d_hidden);
 }
 
+int s1_plan_set_features(s1_plan* p, const s1_features* f, float* d_logp, float* d_cand_logp,
+                         float* d_cand_norm) {
+  if (!p) return set_error(S1_EINVAL, "plan is NULL");
+  return set_features(p->p, f, d_logp, d_cand_logp, d_cand_norm);
+}
+
 int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream) {
   if (!m || !p) return set_error(S1_EINVAL, "model or plan is NULL");
   if (p->owner != m) return set_error(S1_EINVAL, "plan belongs to another model");
@@ -508,6 +514,60 @@ int s1k_readout(int32_t dtype, const float* x, int32_t d, const float* w_final, 
   return dev_status(launch_readout(dtype == S1_BF16, x, d, w_final, eps, E, Q, rows, opt_offsets, opt_ids,
                                    q_type, probs, decisions, 1024, strm(hip_stream)),
                     "s1k_readout");
+}
+
+int s1k_vocab_lse(int32_t dtype, const float* x, int32_t d, const float* w_final, float eps, const void* E,
+                  int32_t V, int32_t R, const int32_t* rows, float* lse, void* hip_stream) {
+  const bool bf16 = dtype == S1_BF16;
+  if ((dtype != S1_BF16 && dtype != S1_F32) || !feat_shape_ok(bf16, d) || V < 1 || R < 0 || !x || !w_final ||
+      !E || (R > 0 && (!rows || !lse)))
+    return set_error(S1_EINVAL, "s1k_vocab_lse: unsupported arguments");
+  if (R == 0) return S1_OK;
+  hipStream_t s = strm(hip_stream);
+  const FeatWs w = feat_ws_layout(bf16, R, V, d);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, w.bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "s1k_vocab_lse: allocation failed");
+  }
+  hipError_t e = launch_feat_norm(bf16, x, d, rows, R, w_final, eps, V, ws, s);
+  if (e == hipSuccess) e = launch_vocab_lse(bf16, E, V, d, R, ws, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(lse, static_cast<char*>(ws) + w.lse, 4 * (size_t)R, hipMemcpyDeviceToDevice, s);
+  (void)hipFreeAsync(ws, s);
+  return dev_status(e, "s1k_vocab_lse");
+}
+
+int s1k_token_logprobs(int32_t dtype, const float* x, int32_t n_rows, int32_t d, const float* w_final, float eps,
+                       const void* E, int32_t V, int32_t n_targets, const int32_t* rows, const int32_t* tokens,
+                       int32_t n_cands, const int32_t* cand_offsets, const int32_t* cand_group, float* logp,
+                       float* cand_logp, float* cand_norm, void* hip_stream) {
+  const bool bf16 = dtype == S1_BF16;
+  if ((dtype != S1_BF16 && dtype != S1_F32) || !feat_shape_ok(bf16, d) || V < 1 || n_rows < 0 || !x ||
+      !w_final || !E || (n_targets > 0 && !logp) || (n_cands > 0 && (!cand_logp || !cand_norm)))
+    return set_error(S1_EINVAL, "s1k_token_logprobs: unsupported arguments");
+  FeatHost h;
+  const int rc = build_features(n_rows, nullptr, V, n_targets, rows, tokens, n_cands, cand_offsets, cand_group,
+                                "s1k_token_logprobs", &h);
+  if (rc) return rc;
+  if (n_targets == 0) return S1_OK;
+  hipStream_t s = strm(hip_stream);
+  const FeatWs w = feat_ws_layout(bf16, (int)h.rows.size(), V, d);
+  const size_t meta = h.meta_bytes();
+  void* dm = nullptr;
+  if (hipMalloc(&dm, meta + w.bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "s1k_token_logprobs: allocation failed");
+  }
+  FeatArgs a;
+  hipError_t e = h.upload(dm, &a, s);
+  if (e == hipSuccess)
+    e = launch_features(bf16, x, d, w_final, eps, E, V, a, logp, cand_logp, cand_norm,
+                        static_cast<char*>(dm) + meta, s);
+  const hipError_t se = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = se;
+  (void)hipFree(dm);
+  return dev_status(e, "s1k_token_logprobs");
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ namespace s1 {
 const char* kernel_class_name(int c) {
   static const char* names[KC_COUNT] = {"embed", "rmsnorm", "gemm_la_in", "la_scan", "gemm_fa_qkv",
                                         "attention", "gemm_o", "gemm_gate_up", "gemm_down", "capture",
-                                        "readout"};
+                                        "readout", "vocab_lse", "features"};
   return (c >= 0 && c < KC_COUNT) ? names[c] : "?";
 }
 
@@ -89,6 +89,7 @@ Plan::~Plan() {
   drop_graph();
   if (dev) (void)hipFree(dev);
   if (cap_dev) (void)hipFree(cap_dev);
+  if (feat_dev) (void)hipFree(feat_dev);
 }
 
 namespace {
@@ -552,6 +553,119 @@ int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
   return S1_OK;
 }
 
+// --------------------------------------------------------------- features
+namespace {
+size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+}  // namespace
+
+size_t FeatHost::meta_bytes() const {
+  return al256(4 * rows.size()) + al256(4 * t_ri.size()) + al256(4 * t_tok.size()) + al256(4 * cand_off.size()) +
+         al256(4 * grp_off.size()) + al256(4 * grp_cands.size());
+}
+
+hipError_t FeatHost::upload(void* dst, FeatArgs* a, hipStream_t s) const {
+  char* d = static_cast<char*>(dst);
+  const std::vector<int32_t>* v[6] = {&rows, &t_ri, &t_tok, &cand_off, &grp_off, &grp_cands};
+  const int32_t* ptr[6];
+  for (int i = 0; i < 6; ++i) {
+    ptr[i] = reinterpret_cast<const int32_t*>(d);
+    if (!v[i]->empty()) {
+      const hipError_t e = hipMemcpyAsync(d, v[i]->data(), 4 * v[i]->size(), hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return e;
+    }
+    d += al256(4 * v[i]->size());
+  }
+  a->R = (int)rows.size();
+  a->n_targets = (int)t_tok.size();
+  a->n_groups = grp_off.empty() ? 0 : (int)grp_off.size() - 1;
+  a->rows = ptr[0];
+  a->t_ri = ptr[1];
+  a->t_tok = ptr[2];
+  a->cand_off = ptr[3];
+  a->grp_off = ptr[4];
+  a->grp_cands = ptr[5];
+  return hipSuccess;
+}
+
+int build_features(int n_rows, const std::vector<int>* row_map, int V, int n_targets, const int32_t* rows,
+                   const int32_t* tokens, int n_cands, const int32_t* cand_offsets, const int32_t* cand_group,
+                   const char* who, FeatHost* out) {
+  const std::string w(who);
+  if (n_targets < 0 || n_cands < 0) return set_error(S1_EINVAL, w + ": negative count");
+  if (n_targets > 0 && (!rows || !tokens)) return set_error(S1_EINVAL, w + ": target arrays are NULL");
+  if (n_cands > 0 && (!cand_offsets || !cand_group)) return set_error(S1_EINVAL, w + ": candidate arrays are NULL");
+  FeatHost h;
+  std::vector<int32_t> mapped(n_targets);
+  for (int t = 0; t < n_targets; ++t) {
+    if (rows[t] < 0 || rows[t] >= n_rows) return set_error(S1_EINVAL, w + ": target row out of range");
+    if (tokens[t] < 0 || tokens[t] >= V) return set_error(S1_EINVAL, w + ": target token out of range");
+    mapped[t] = row_map ? (*row_map)[rows[t]] : rows[t];
+  }
+  h.rows = mapped;
+  std::sort(h.rows.begin(), h.rows.end());
+  h.rows.erase(std::unique(h.rows.begin(), h.rows.end()), h.rows.end());
+  h.t_ri.resize(n_targets);
+  for (int t = 0; t < n_targets; ++t)
+    h.t_ri[t] = (int32_t)(std::lower_bound(h.rows.begin(), h.rows.end(), mapped[t]) - h.rows.begin());
+  h.t_tok.assign(tokens, tokens + n_targets);
+  if (n_cands > 0) {
+    if (cand_offsets[0] < 0) return set_error(S1_EINVAL, w + ": candidate offsets must start at >= 0");
+    for (int c = 0; c < n_cands; ++c)
+      if (cand_offsets[c + 1] < cand_offsets[c]) return set_error(S1_EINVAL, w + ": candidate offsets decrease");
+    if (cand_offsets[n_cands] > n_targets) return set_error(S1_EINVAL, w + ": candidate offsets exceed the targets");
+    h.cand_off.assign(cand_offsets, cand_offsets + n_cands + 1);
+    std::vector<int32_t> order(n_cands);
+    for (int c = 0; c < n_cands; ++c) order[c] = c;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cand_group[a] < cand_group[b]; });
+    h.grp_cands = order;
+    h.grp_off.push_back(0);
+    for (int i = 1; i <= n_cands; ++i)
+      if (i == n_cands || cand_group[order[i]] != cand_group[order[i - 1]]) h.grp_off.push_back(i);
+  }
+  h.n_cands = n_cands;
+  *out = std::move(h);
+  return S1_OK;
+}
+
+int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp, float* d_cand_norm) {
+  p->drop_graph();
+  if (p->feat_dev) {
+    (void)hipFree(p->feat_dev);
+    p->feat_dev = nullptr;
+  }
+  p->feat = FeatArgs();
+  p->feat_ws = nullptr;
+  p->feat_logp = p->feat_cand_lp = p->feat_cand_norm = nullptr;
+  if (!f || f->n_targets == 0) return S1_OK;
+  const Model* m = p->m;
+  const s1_config& c = m->cfg;
+  if (!feat_shape_ok(m->bf16, c.d_model))
+    return set_error(S1_EINVAL, "features: d_model must be a multiple of 128 (bf16) or 4 (fp32)");
+  if (!d_logp || (f->n_cands > 0 && (!d_cand_lp || !d_cand_norm)))
+    return set_error(S1_EINVAL, "features: output buffers are NULL");
+  FeatHost h;
+  int rc = build_features(p->T, &p->row_of, c.vocab, f->n_targets, f->rows, f->tokens, f->n_cands,
+                          f->cand_offsets, f->cand_group, "features", &h);
+  if (rc) return rc;
+  const FeatWs w = feat_ws_layout(m->bf16, (int)h.rows.size(), c.vocab, c.d_model);
+  const size_t meta = h.meta_bytes();
+  if (hipMalloc(&p->feat_dev, meta + w.bytes + 256) != hipSuccess) {
+    (void)hipGetLastError();
+    p->feat_dev = nullptr;
+    return set_error(S1_ENOMEM, "device allocation for features failed");
+  }
+  FeatArgs a;
+  hipError_t e = h.upload(p->feat_dev, &a, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "copy feature metadata"));
+  p->feat = a;
+  p->feat_ws = static_cast<char*>(p->feat_dev) + meta;
+  p->feat_logp = d_logp;
+  p->feat_cand_lp = d_cand_lp;
+  p->feat_cand_norm = d_cand_norm;
+  return S1_OK;
+}
+
 // ---------------------------------------------------------------- forward
 #define MARK(cls)                            \
   do {                                       \
@@ -715,6 +829,17 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
                           p->opt_off, p->opt_ids, p->q_type, d_probs, d_dec, p->max_k, s),
            "readout");
   if (p->Q > 0) MARK(KC_READOUT);
+  if (p->feat.n_targets > 0) {
+    S1_TRY(launch_feat_norm(m->bf16, m->x, c.d_model, p->feat.rows, p->feat.R, m->final_norm, c.rms_eps,
+                            c.vocab, p->feat_ws, s),
+           "feature rows");
+    S1_TRY(launch_vocab_lse(m->bf16, m->embed, c.vocab, c.d_model, p->feat.R, p->feat_ws, s), "vocabulary lse");
+    MARK(KC_VOCAB_LSE);
+    S1_TRY(launch_feat_targets(m->bf16, c.d_model, m->embed, c.vocab, p->feat, p->feat_logp, p->feat_cand_lp,
+                               p->feat_cand_norm, p->feat_ws, s),
+           "feature targets");
+    MARK(KC_FEATURES);
+  }
   return S1_OK;
 }
 

@@ -32,7 +32,7 @@ struct LayerW {
 // Kernel families timed by s1_plan_profile.
 enum KernelClass {
   KC_EMBED = 0, KC_RMSNORM, KC_GEMM_LA_IN, KC_LA_SCAN, KC_GEMM_FA_QKV, KC_ATTENTION, KC_GEMM_O,
-  KC_GEMM_GATE_UP, KC_GEMM_DOWN, KC_CAPTURE, KC_READOUT, KC_COUNT
+  KC_GEMM_GATE_UP, KC_GEMM_DOWN, KC_CAPTURE, KC_READOUT, KC_VOCAB_LSE, KC_FEATURES, KC_COUNT
 };
 const char* kernel_class_name(int c);
 
@@ -104,6 +104,23 @@ struct PassPlan {
   int n_cap = 0;
 };
 
+// Host form of a feature request, validated: distinct rows (internal row
+// order), per-target row index and token, candidate spans and the
+// candidates of each group (ascending candidate index).
+struct FeatHost {
+  std::vector<int32_t> rows, t_ri, t_tok, cand_off, grp_off, grp_cands;
+  int n_cands = 0;
+  size_t meta_bytes() const;
+  // copy the metadata to device memory dst (meta_bytes() bytes, 256-aligned)
+  // and fill a with device pointers into it
+  hipError_t upload(void* dst, FeatArgs* a, hipStream_t s) const;
+};
+// Validate and build a feature request.  rows[] index 0 .. n_rows-1 and are
+// mapped through row_map when it is not NULL.
+int build_features(int n_rows, const std::vector<int>* row_map, int V, int n_targets, const int32_t* rows,
+                   const int32_t* tokens, int n_cands, const int32_t* cand_offsets, const int32_t* cand_group,
+                   const char* who, FeatHost* out);
+
 struct Plan {
   Model* m = nullptr;
   int T = 0, n_seqs = 0, Q = 0, total_opts = 0, max_k = 0;
@@ -129,6 +146,14 @@ struct Plan {
   float* g_probs = nullptr;
   void* g_dec = nullptr;
   float* g_cap = nullptr;
+  // full-vocabulary log-probability features, computed after the readout by
+  // every run when set
+  void* feat_dev = nullptr;     // metadata + workspace
+  FeatArgs feat;
+  void* feat_ws = nullptr;
+  float* feat_logp = nullptr;
+  float* feat_cand_lp = nullptr;
+  float* feat_cand_norm = nullptr;
   void drop_graph();
   ~Plan();
 };
@@ -139,6 +164,7 @@ int load_model(const s1_config* cfg, const s1_tensor* t, int n, hipStream_t s, M
 int create_plan(Model* m, const s1_batch* b, Plan** out);
 int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden);
+int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp, float* d_cand_norm);
 int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 
 }  // namespace s1

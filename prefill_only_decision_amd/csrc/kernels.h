@@ -131,4 +131,46 @@ hipError_t launch_readout(bool bf16, const float* x, int d, const float* w_final
                           const int32_t* opt_ids, const uint8_t* q_type, float* probs,
                           void* decisions, int max_k, hipStream_t s);
 
+// ------------------------------------------- full-vocabulary log-probs
+// Workspace of the feature kernels for R distinct rows (byte offsets into
+// one device block): normalised rows hn fp32 [Rp, d], their bf16 hi / lo
+// split [Rp, d] each (bf16 models), per-block partial (max, sum) pairs
+// [nb, Rp] and lse [Rp]; Rp = R rounded up to 32.
+struct FeatWs {
+  int Rp = 0, nb = 0;
+  size_t hn = 0, hi = 0, lo = 0, part = 0, lse = 0, bytes = 0;
+};
+FeatWs feat_ws_layout(bool bf16, int R, int V, int d);
+// Shapes the feature kernels take: bf16 d % 128 == 0, fp32 d % 4 == 0.
+bool feat_shape_ok(bool bf16, int d);
+
+// Device metadata of a feature request: R distinct rows of x (rows[R]);
+// target t reads row rows[t_ri[t]] and scores token t_tok[t]; candidate c
+// owns targets cand_off[c] .. cand_off[c+1]-1; group g lists its
+// candidates grp_cands[grp_off[g] .. grp_off[g+1]-1].
+struct FeatArgs {
+  int R = 0, n_targets = 0, n_groups = 0;
+  const int32_t* rows = nullptr;
+  const int32_t* t_ri = nullptr;
+  const int32_t* t_tok = nullptr;
+  const int32_t* cand_off = nullptr;
+  const int32_t* grp_off = nullptr;
+  const int32_t* grp_cands = nullptr;
+};
+// Final RMSNorm of the R rows into the workspace (hn, and hi / lo for bf16).
+hipError_t launch_feat_norm(bool bf16, const float* x, int d, const int32_t* rows, int R, const float* w_final,
+                            float eps, int V, void* ws, hipStream_t s);
+// lse[r] = log sum_v exp(hn[r] . E[v]) over the V rows of E, from the
+// workspace's normalised rows into its lse array.
+hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void* ws, hipStream_t s);
+// Per-target logp = hn . E[token] - lse, then the candidate scores and
+// their normalisation per group (after launch_vocab_lse).
+hipError_t launch_feat_targets(bool bf16, int d, const void* E, int V, const FeatArgs& f, float* logp,
+                               float* cand_lp, float* cand_norm, void* ws, hipStream_t s);
+// The whole feature computation: logp[n_targets], cand_lp and cand_norm
+// [number of candidates].
+hipError_t launch_features(bool bf16, const float* x, int d, const float* w_final, float eps, const void* E,
+                           int V, const FeatArgs& f, float* logp, float* cand_lp, float* cand_norm, void* ws,
+                           hipStream_t s);
+
 }  // namespace s1

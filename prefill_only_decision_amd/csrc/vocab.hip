@@ -1,0 +1,402 @@
+// Full-vocabulary token log-probabilities and their normalisation across the
+// candidates of a question (RFC #114 "Native Rust/CUDA support for
+// OmniJev-4B v1.1", section 4, note under the semantics table: the language-
+// model features use log-probabilities over the whole vocabulary, computed in
+// bounded chunks; comment "Plan: native OmniJev-4B v1.1": the log-softmax
+// runs over every row of the tied embedding, logits in fp32).
+//
+// Steps, all on the stream given:
+//   1. feat_norm: gather the distinct rows the targets read, final RMSNorm
+//      (fp32), and for bf16 models split each normalised value into a bf16
+//      pair hi + lo (hi = rne(v), lo = rne(v - hi), |v - hi - lo| <= 2^-17 |v|).
+//   2. vocab_lse: the hot kernel.  Every workgroup owns 128 consecutive
+//      vocabulary rows (32 per wave), streams them once from HBM and forms
+//      their logits against all rows of the group on MFMA (E x hi + E x lo,
+//      fp32 accumulation), then reduces them to one (max, sum exp(z - max))
+//      pair per row: no logit is written.  The normalised rows are staged
+//      through LDS per 128-wide k chunk and shared by the four waves.
+//   3. lse_merge: per row, the partial pairs of every vocabulary block merged
+//      in a fixed order, lse = m + log s (deterministic).
+//   4. target_logp: one wave per target, z = hn . E[token] in fp32, logp =
+//      z - lse.
+//   5. cand_norm: one thread per question group, candidate score = sum of
+//      its targets' logp, then score - logsumexp over the group.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace s1 {
+namespace {
+
+constexpr int VL_WAVES = 4;                 // waves per workgroup
+constexpr int VL_ROWS = 32 * VL_WAVES;      // vocabulary rows per workgroup
+constexpr int VL_KC = 128;                  // k per staged chunk
+constexpr int VL_UNITS = VL_KC / 8;         // 16-byte units per row and chunk
+
+// 1. One workgroup per padded row; rows >= R are zero (so padded columns
+// contribute logits of 0 that the caller never reads).
+template <bool SPLIT>
+__global__ void __launch_bounds__(256)
+feat_norm_kernel(const float* __restrict__ x, int d, const int32_t* __restrict__ rows, int R,
+                 const float* __restrict__ w, float eps, float* __restrict__ hn,
+                 bf16_t* __restrict__ hi, bf16_t* __restrict__ lo) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const long long o = (long long)r * d;
+  if (r >= R) {
+    for (int i = threadIdx.x; i < d; i += 256) {
+      hn[o + i] = 0.f;
+      if constexpr (SPLIT) {
+        hi[o + i] = 0;
+        lo[o + i] = 0;
+      }
+    }
+    return;
+  }
+  const float* xr = x + (long long)rows[r] * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss += xr[i] * xr[i];
+  const float rs = rsqrtf(block_sum<4>(ss, red) / d + eps);
+  for (int i = threadIdx.x; i < d; i += 256) {
+    const float v = xr[i] * rs * w[i];
+    hn[o + i] = v;
+    if constexpr (SPLIT) {
+      const bf16_t h = f2bf(v);
+      hi[o + i] = h;
+      lo[o + i] = f2bf(v - bf2f(h));
+    }
+  }
+}
+
+// Merge of two (max, sum exp(z - max)) pairs; an empty pair has s = 0.
+__device__ __forceinline__ float2 lse_pair(float2 a, float2 b) {
+  if (a.y == 0.f) return b;
+  if (b.y == 0.f) return a;
+  const float m = fmaxf(a.x, b.x);
+  return make_float2(m, a.y * __expf(a.x - m) + b.y * __expf(b.x - m));
+}
+
+// 2. Vocabulary log-sum-exp partials, bf16 tied embedding.  Workgroup b owns
+// vocabulary rows [128 b, 128 b + 128); wave w the 32 rows from 128 b + 32 w.
+// NT = 1 or 2 tiles of 32 normalised rows (columns col0 .. col0 + 32 NT - 1).
+//
+// The contraction over k may visit k in any order as long as both operands
+// use the same one: lane l of a wave loads 64 consecutive bf16 of its
+// vocabulary row (k = kb + 64 (l / 32) .. + 63, 128 contiguous bytes) and
+// feeds them as eight MFMA steps; step j takes elements 8 j .. 8 j + 7, so
+// the B operand of lane l at step j is hn[col][kb + 64 (l / 32) + 8 j ..].
+// LDS holds a chunk as [row][hi | lo][16 units of 16 B] with unit u stored
+// at u ^ (row & 15): the 16 lanes of each ds_read_b128 phase (16 rows, one
+// unit) then hit 16 distinct 16-byte bank groups.
+template <int NT>
+__global__ void __launch_bounds__(256)
+vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* __restrict__ hi,
+                      const bf16_t* __restrict__ lo, int col0, int ld_part, float2* __restrict__ part) {
+  constexpr int NR = 32 * NT;                        // normalised rows staged
+  constexpr int BITEMS = NR * 2 * VL_UNITS / 256;    // 16-byte items per thread and chunk
+  __shared__ uint4 bs[2][NR][2][VL_UNITS];
+  __shared__ float2 red[VL_WAVES][NR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v0 = blockIdx.x * VL_ROWS + wave * 32;
+  // clamp the row of lanes past the vocabulary end: they load valid memory
+  // and their logits are masked out below
+  const int my_row = min(v0 + (lane & 31), V - 1);
+  const uint4* arow = reinterpret_cast<const uint4*>(E + (long long)my_row * d + 64 * (lane >> 5));
+  const int nk = d / VL_KC;
+
+  auto load_b = [&](int c, uint4 (&breg)[BITEMS]) {
+#pragma unroll
+    for (int i = 0; i < BITEMS; ++i) {
+      const int f = tid + 256 * i;
+      const int row = f / (2 * VL_UNITS), half = (f / VL_UNITS) & 1, u = f % VL_UNITS;
+      const bf16_t* src = (half ? lo : hi) + (long long)(col0 + row) * d + c * VL_KC + 8 * u;
+      breg[i] = *reinterpret_cast<const uint4*>(src);
+    }
+  };
+  auto store_b = [&](int buf, const uint4 (&breg)[BITEMS]) {
+#pragma unroll
+    for (int i = 0; i < BITEMS; ++i) {
+      const int f = tid + 256 * i;
+      const int row = f / (2 * VL_UNITS), half = (f / VL_UNITS) & 1, u = f % VL_UNITS;
+      bs[buf][row][half][u ^ (row & 15)] = breg[i];
+    }
+  };
+
+  floatx16 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+
+  uint4 a_cur[8], a_nxt[8], b_nxt[BITEMS];
+  {
+    load_b(0, b_nxt);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a_cur[j] = arow[j];
+    store_b(0, b_nxt);
+  }
+  __syncthreads();
+  for (int c = 0; c < nk; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nk;
+    if (more) {
+      load_b(c + 1, b_nxt);
+      const uint4* an = arow + (c + 1) * (VL_KC / 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a_nxt[j] = an[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 a = as_frag(a_cur[j]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int row = 32 * n + (lane & 31);
+        const int u = (8 * (lane >> 5) + j) ^ (row & 15);
+        mfma32(acc[n], a, as_frag(bs[buf][row][0][u]));
+        mfma32(acc[n], a, as_frag(bs[buf][row][1][u]));
+      }
+    }
+    if (more) {
+      store_b(buf ^ 1, b_nxt);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a_cur[j] = a_nxt[j];
+    }
+    __syncthreads();
+  }
+
+  // per column: max and sum of exp over this wave's 32 vocabulary rows
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (v0 + acc_row(r, lane) < V) m = fmaxf(m, acc[n][r]);
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (v0 + acc_row(r, lane) < V) s += __expf(acc[n][r] - m);
+    }
+    s += __shfl_xor(s, 32, 64);
+    if (lane < 32) red[wave][32 * n + lane] = make_float2(m, s);
+  }
+  __syncthreads();
+  if (tid < NR) {
+    float2 t = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < VL_WAVES; ++w) t = lse_pair(t, red[w][tid]);
+    part[(long long)blockIdx.x * ld_part + col0 + tid] = t;
+  }
+}
+
+// 2'. The same partials for fp32 models: thread t of block b owns vocabulary
+// row 256 b + t and loops over the rows (fp32 dot products; these models are
+// small).
+__global__ void __launch_bounds__(256)
+vocab_lse_f32_kernel(const float* __restrict__ E, int V, int d, const float* __restrict__ hn, int R,
+                     int ld_part, float2* __restrict__ part) {
+  __shared__ float2 red[4];
+  const int v = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* e = E + (long long)min(v, V - 1) * d;
+  for (int r = 0; r < R; ++r) {
+    const float* h = hn + (long long)r * d;
+    float z = 0.f;
+    for (int i = 0; i < d; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(e + i);
+      const float4 b = *reinterpret_cast<const float4*>(h + i);
+      z += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    }
+    float2 t = v < V ? make_float2(z, 1.f) : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float2 u;
+      u.x = __shfl_xor(t.x, o, 64);
+      u.y = __shfl_xor(t.y, o, 64);
+      t = lse_pair(t, u);
+    }
+    if (lane == 0) red[wave] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float2 s = red[0];
+      for (int w = 1; w < 4; ++w) s = lse_pair(s, red[w]);
+      part[(long long)blockIdx.x * ld_part + r] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// 3. One workgroup per row: merge the nb partial pairs.  Thread t folds
+// blocks t, t + 256, ... in order, then a fixed butterfly and a fixed
+// cross-wave order finish; the result does not depend on timing.
+__global__ void __launch_bounds__(256)
+lse_merge_kernel(const float2* __restrict__ part, int nb, int ld_part, float* __restrict__ lse) {
+  __shared__ float2 red[4];
+  const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float2 t = make_float2(0.f, 0.f);
+  for (int b = threadIdx.x; b < nb; b += 256) t = lse_pair(t, part[(long long)b * ld_part + r]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float2 u;
+    u.x = __shfl_xor(t.x, o, 64);
+    u.y = __shfl_xor(t.y, o, 64);
+    t = lse_pair(t, u);
+  }
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float2 s = red[0];
+    for (int w = 1; w < 4; ++w) s = lse_pair(s, red[w]);
+    lse[r] = s.x + __logf(s.y);
+  }
+}
+
+// 4. One wave per target.
+template <typename T>
+__global__ void __launch_bounds__(256)
+target_logp_kernel(const float* __restrict__ hn, int d, const T* __restrict__ E,
+                   const int32_t* __restrict__ t_ri, const int32_t* __restrict__ t_tok, int n,
+                   const float* __restrict__ lse, float* __restrict__ logp) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= n) return;
+  const int ri = t_ri[t];
+  const float* h = hn + (long long)ri * d;
+  const T* e = E + (long long)t_tok[t] * d;
+  float z = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 ev;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(e + i);
+      ev = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    } else {
+      ev = *reinterpret_cast<const float4*>(e + i);
+    }
+    const float4 hv = *reinterpret_cast<const float4*>(h + i);
+    z += ev.x * hv.x + ev.y * hv.y + ev.z * hv.z + ev.w * hv.w;
+  }
+  z = wave_sum(z);
+  if (lane == 0) logp[t] = z - lse[ri];
+}
+
+// 5. One thread per group: each member candidate's score (sum of its
+// targets' logp, in target order), then score - logsumexp over the group.
+__global__ void __launch_bounds__(256)
+cand_norm_kernel(const float* __restrict__ logp, const int32_t* __restrict__ cand_off,
+                 const int32_t* __restrict__ grp_off, const int32_t* __restrict__ grp_cands, int G,
+                 float* __restrict__ cand_lp, float* __restrict__ cand_norm) {
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= G) return;
+  const int c0 = grp_off[g], c1 = grp_off[g + 1];
+  float m = -INFINITY;
+  for (int i = c0; i < c1; ++i) {
+    const int c = grp_cands[i];
+    float s = 0.f;
+    for (int t = cand_off[c]; t < cand_off[c + 1]; ++t) s += logp[t];
+    cand_lp[c] = s;
+    m = fmaxf(m, s);
+  }
+  float se = 0.f;
+  for (int i = c0; i < c1; ++i) se += __expf(cand_lp[grp_cands[i]] - m);
+  const float l = m + __logf(se);
+  for (int i = c0; i < c1; ++i) {
+    const int c = grp_cands[i];
+    cand_norm[c] = cand_lp[c] - l;
+  }
+}
+
+}  // namespace
+
+FeatWs feat_ws_layout(bool bf16, int R, int V, int d) {
+  FeatWs w;
+  w.Rp = std::max(32, (R + 31) / 32 * 32);
+  w.nb = bf16 ? (V + VL_ROWS - 1) / VL_ROWS : (V + 255) / 256;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.hn = take((size_t)w.Rp * d * 4);
+  w.hi = bf16 ? take((size_t)w.Rp * d * 2) : 0;
+  w.lo = bf16 ? take((size_t)w.Rp * d * 2) : 0;
+  w.part = take((size_t)w.nb * w.Rp * 8);
+  w.lse = take((size_t)w.Rp * 4);
+  w.bytes = off;
+  return w;
+}
+
+bool feat_shape_ok(bool bf16, int d) {
+  return bf16 ? (d >= VL_KC && d % VL_KC == 0) : (d >= 4 && d % 4 == 0);
+}
+
+hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void* ws, hipStream_t s) {
+  const FeatWs w = feat_ws_layout(bf16, R, V, d);
+  char* base = static_cast<char*>(ws);
+  auto* part = reinterpret_cast<float2*>(base + w.part);
+  if (bf16) {
+    const auto* hi = reinterpret_cast<const bf16_t*>(base + w.hi);
+    const auto* lo = reinterpret_cast<const bf16_t*>(base + w.lo);
+    for (int c0 = 0; c0 < w.Rp; c0 += 64) {
+      if (w.Rp - c0 >= 64)
+        hipLaunchKernelGGL(vocab_lse_bf16_kernel<2>, dim3(w.nb), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo, c0, w.Rp, part);
+      else
+        hipLaunchKernelGGL(vocab_lse_bf16_kernel<1>, dim3(w.nb), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo, c0, w.Rp, part);
+    }
+  } else {
+    hipLaunchKernelGGL(vocab_lse_f32_kernel, dim3(w.nb), dim3(256), 0, s, reinterpret_cast<const float*>(E), V,
+                       d, reinterpret_cast<const float*>(base + w.hn), R, w.Rp, part);
+  }
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(R), dim3(256), 0, s, part, w.nb, w.Rp,
+                     reinterpret_cast<float*>(base + w.lse));
+  return hipGetLastError();
+}
+
+hipError_t launch_feat_norm(bool bf16, const float* x, int d, const int32_t* rows, int R, const float* w_final,
+                            float eps, int V, void* ws, hipStream_t s) {
+  const FeatWs w = feat_ws_layout(bf16, R, V, d);
+  char* base = static_cast<char*>(ws);
+  if (bf16)
+    hipLaunchKernelGGL(feat_norm_kernel<true>, dim3(w.Rp), dim3(256), 0, s, x, d, rows, R, w_final, eps,
+                       reinterpret_cast<float*>(base + w.hn), reinterpret_cast<bf16_t*>(base + w.hi),
+                       reinterpret_cast<bf16_t*>(base + w.lo));
+  else
+    hipLaunchKernelGGL(feat_norm_kernel<false>, dim3(w.Rp), dim3(256), 0, s, x, d, rows, R, w_final, eps,
+                       reinterpret_cast<float*>(base + w.hn), nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_feat_targets(bool bf16, int d, const void* E, int V, const FeatArgs& f, float* logp,
+                               float* cand_lp, float* cand_norm, void* ws, hipStream_t s) {
+  if (f.n_targets <= 0) return hipSuccess;
+  const FeatWs w = feat_ws_layout(bf16, f.R, V, d);
+  char* base = static_cast<char*>(ws);
+  const auto* hn = reinterpret_cast<const float*>(base + w.hn);
+  const auto* lse = reinterpret_cast<const float*>(base + w.lse);
+  const dim3 g((f.n_targets + 3) / 4);
+  if (bf16)
+    hipLaunchKernelGGL(target_logp_kernel<bf16_t>, g, dim3(256), 0, s, hn, d,
+                       reinterpret_cast<const bf16_t*>(E), f.t_ri, f.t_tok, f.n_targets, lse, logp);
+  else
+    hipLaunchKernelGGL(target_logp_kernel<float>, g, dim3(256), 0, s, hn, d, reinterpret_cast<const float*>(E),
+                       f.t_ri, f.t_tok, f.n_targets, lse, logp);
+  if (f.n_groups > 0)
+    hipLaunchKernelGGL(cand_norm_kernel, dim3((f.n_groups + 255) / 256), dim3(256), 0, s, logp, f.cand_off,
+                       f.grp_off, f.grp_cands, f.n_groups, cand_lp, cand_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_features(bool bf16, const float* x, int d, const float* w_final, float eps, const void* E,
+                           int V, const FeatArgs& f, float* logp, float* cand_lp, float* cand_norm, void* ws,
+                           hipStream_t s) {
+  if (f.n_targets <= 0 || f.R <= 0) return hipSuccess;
+  hipError_t e = launch_feat_norm(bf16, x, d, f.rows, f.R, w_final, eps, V, ws, s);
+  if (e == hipSuccess) e = launch_vocab_lse(bf16, E, V, d, f.R, ws, s);
+  if (e == hipSuccess) e = launch_feat_targets(bf16, d, E, V, f, logp, cand_lp, cand_norm, ws, s);
+  return e;
+}
+
+}  // namespace s1

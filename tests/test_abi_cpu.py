@@ -154,3 +154,25 @@ def test_bad_config_rejected():
     b = make_batch("4b-single-512")
     assert s1.validate(cfg, b) == -1
     assert "128" in s1.binding.last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(tokens=[0, 4096]), "token out of range"),
+    (dict(rows=[0, 8]), "row out of range"),
+    (dict(rows=[-1, 0]), "row out of range"),
+    (dict(cand_offsets=[0, 2, 1], cand_group=[0, 0]), "decrease"),
+    (dict(cand_offsets=[0, 1, 3], cand_group=[0, 0]), "exceed"),
+    (dict(cand_offsets=[-1, 1], cand_group=[0]), "start"),
+    (dict(d=102), "unsupported"),
+    (dict(dtype=s1.binding.S1_BF16, d=256 + 64), "unsupported"),
+])
+def test_feature_request_validation(lib, kw, needle):
+    """Malformed feature requests fail with S1_EINVAL on the host, before
+    any device memory is touched (the pointers here are never dereferenced)."""
+    a = dict(dtype=s1.binding.S1_F32, d=256, rows=[0, 7], tokens=[5, 9], cand_offsets=[0, 1, 2],
+             cand_group=[3, 3])
+    a.update(kw)
+    with pytest.raises(s1.binding.S1Error) as e:
+        s1.binding.token_logprobs(a["dtype"], 64, 8, a["d"], 64, 1e-6, 64, 4096, a["rows"], a["tokens"],
+                                  a["cand_offsets"], a["cand_group"], 64, 64, 64)
+    assert e.value.code == -1 and needle in str(e.value)
