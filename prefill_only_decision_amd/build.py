@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libs1.so")
 SOURCES = ["abi.cpp", "executor.cpp", "gemm.hip", "attention.hip", "scan.hip", "misc.hip", "vocab.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled for all device code.
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 

@@ -14,7 +14,7 @@
 //      their logits against all rows of the group on MFMA (E x hi + E x lo,
 //      fp32 accumulation), then reduces them to one (max, sum exp(z - max))
 //      pair per row: no logit is written.  The normalised rows are staged
-//      through LDS per 128-wide k chunk and shared by the four waves.
+//      through LDS chunk by chunk and shared by the four waves.
 //   3. lse_merge: per row, the partial pairs of every vocabulary block merged
 //      in a fixed order, lse = m + log s (deterministic).
 //   4. target_logp: one wave per target, z = hn . E[token] in fp32, logp =
@@ -25,6 +25,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <utility>
 
 namespace s1 {
 namespace {
@@ -32,7 +33,6 @@ namespace {
 constexpr int VL_WAVES = 4;                 // waves per workgroup
 constexpr int VL_ROWS = 32 * VL_WAVES;      // vocabulary rows per workgroup
 constexpr int VL_KC = 128;                  // k per staged chunk
-constexpr int VL_UNITS = VL_KC / 8;         // 16-byte units per row and chunk
 
 // 1. One workgroup per padded row; rows >= R are zero (so padded columns
 // contribute logits of 0 that the caller never reads).
@@ -77,93 +77,163 @@ __device__ __forceinline__ float2 lse_pair(float2 a, float2 b) {
   return make_float2(m, a.y * __expf(a.x - m) + b.y * __expf(b.x - m));
 }
 
-// 2. Vocabulary log-sum-exp partials, bf16 tied embedding.  Workgroup b owns
-// vocabulary rows [128 b, 128 b + 128); wave w the 32 rows from 128 b + 32 w.
-// NT = 1 or 2 tiles of 32 normalised rows (columns col0 .. col0 + 32 NT - 1).
+// 2. Vocabulary log-sum-exp partials, bf16 tied embedding.
 //
-// The contraction over k may visit k in any order as long as both operands
-// use the same one: lane l of a wave loads 64 consecutive bf16 of its
-// vocabulary row (k = kb + 64 (l / 32) .. + 63, 128 contiguous bytes) and
-// feeds them as eight MFMA steps; step j takes elements 8 j .. 8 j + 7, so
-// the B operand of lane l at step j is hn[col][kb + 64 (l / 32) + 8 j ..].
-// LDS holds a chunk as [row][hi | lo][16 units of 16 B] with unit u stored
-// at u ^ (row & 15): the 16 lanes of each ds_read_b128 phase (16 rows, one
-// unit) then hit 16 distinct 16-byte bank groups.
-template <int NT>
-__global__ void __launch_bounds__(256)
-vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* __restrict__ hi,
-                      const bf16_t* __restrict__ lo, int col0, int ld_part, float2* __restrict__ part) {
-  constexpr int NR = 32 * NT;                        // normalised rows staged
-  constexpr int BITEMS = NR * 2 * VL_UNITS / 256;    // 16-byte items per thread and chunk
-  __shared__ uint4 bs[2][NR][2][VL_UNITS];
+// Workgroup b owns vocabulary rows [128 b, 128 b + 128), wave w the 32 rows
+// from 128 b + 32 w (one MFMA row tile), and NT tiles of 32 normalised rows
+// (columns col0 .. col0 + 32 NT - 1).  The kernel is bound by streaming E
+// from HBM, and HBM only delivers its bandwidth with a few hundred KB of
+// loads in flight per CU; so the vocabulary rows stream through a ring of D
+// register buffers per lane (D - 1 chunks of KC k-values in flight while one
+// is multiplied), and the normalised rows -- identical for all waves --
+// through a ring of D LDS buffers filled by buffer-to-LDS DMA, issued
+// together with the vocabulary chunk of the same k range.
+//
+// Vector-memory completions are counted in issue order (vmcnt), so every
+// chunk's loads (E into registers, hn into LDS) are issued as one group and
+// a wait for "all but the last D - 2 groups" covers exactly the chunk about to
+// be used.  Both kinds of load are written as inline assembly: a
+// compiler-visible LDS DMA makes the compiler wait for every outstanding load
+// before any LDS read, which would empty the ring.  The wait names the
+// chunk's registers as operands, so nothing that uses them can be scheduled
+// before it; chunks past the end load from beyond the buffer's range, which
+// reads zeros without touching memory, so every group has the same size.
+//
+// k order: the contraction may visit k in any order as long as both operands
+// use the same one.  Lane l (half h = l / 32) feeds MFMA step j with the
+// eight vocabulary values at k = 16 j + 8 h of the chunk, and the B operand
+// of lane l at step j is hn[col][16 j + 8 h ..].  Each LDS chunk holds, per
+// normalised row, 2 U 16-byte slots (U = KC / 8 of hi, then U of lo), slot s
+// stored at s ^ (row & 15): the 16 lanes of a ds_read_b128 phase (16 rows,
+// one slot) then hit 16 distinct 16-byte bank groups.
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Raw buffer resource over `bytes` bytes from base; offsets at or past
+// `bytes` read as zero.  The fields are wave-uniform (readfirstlane keeps
+// them in the scalar registers the buffer instructions take).
+__device__ __forceinline__ int32x4 raw_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
+__device__ __forceinline__ void vl_dma16(int32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+// 16 bytes per lane into registers; complete only after a vl_wait.
+__device__ __forceinline__ u32x4 vl_load16(int32x4 rsrc, int voff) {
+  u32x4 v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voff), "s"(rsrc) : "memory");
+  return v;
+}
+#pragma clang diagnostic pop
+
+// Wait until at most VM vector-memory loads are outstanding; the J
+// registers of the chunk are tied to the wait.
+template <int VM, int J>
+__device__ __forceinline__ void vl_wait(u32x4 (&a)[J]) {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  if constexpr (J == 8)
+    asm volatile("s_waitcnt vmcnt(%8)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]),
+                 "+v"(a[5]), "+v"(a[6]), "+v"(a[7]) : "n"(VM) : "memory");
+  else if constexpr (J == 4)
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(VM) : "memory");
+  else
+    static_assert(J == 8 || J == 4, "chunk register count");
+}
+
+template <int NT, int KC, int D>
+__global__ void __launch_bounds__(256, 2)
+vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* __restrict__ hi, int lo_delta,
+                      int col0, int ld_part, float2* __restrict__ part) {
+  constexpr int U = KC / 8, J = KC / 16, NR = 32 * NT;
+  constexpr int ROWB = 32 * U;            // LDS bytes per normalised row and chunk (hi + lo)
+  constexpr int CHB = NR * ROWB;          // LDS bytes per chunk
+  constexpr int IPW = CHB / 4096;         // 1 KB DMA instructions per wave and chunk
+  static_assert(IPW >= 1 && CHB % 4096 == 0 && 2 * U >= 16, "chunk layout");
+  static_assert(D >= 3, "ring depth");
+  __shared__ __attribute__((aligned(16))) char ring[D][CHB];
   __shared__ float2 red[VL_WAVES][NR];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int v0 = blockIdx.x * VL_ROWS + wave * 32;
-  // clamp the row of lanes past the vocabulary end: they load valid memory
-  // and their logits are masked out below
-  const int my_row = min(v0 + (lane & 31), V - 1);
-  const uint4* arow = reinterpret_cast<const uint4*>(E + (long long)my_row * d + 64 * (lane >> 5));
-  const int nk = d / VL_KC;
-
-  auto load_b = [&](int c, uint4 (&breg)[BITEMS]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int vb = blockIdx.x * VL_ROWS;
+  const int v0 = vb + wave * 32;
+  // this workgroup's vocabulary rows; rows past V read as zero
+  const int32x4 ra = raw_rsrc(E + (long long)vb * d, (int)(min(V - vb, VL_ROWS) * (long long)d * 2));
+  const int a_base = (wave * 32 + (lane & 31)) * d * 2;
+  // hi rows col0 .. col0 + NR - 1, lo rows lo_delta bytes further on
+  const bf16_t* hb = hi + (long long)col0 * d;
+  const int32x4 rb = raw_rsrc(hb, lo_delta + NR * d * 2);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)&ring[0][0]));
+  int b_off[IPW];
 #pragma unroll
-    for (int i = 0; i < BITEMS; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f / (2 * VL_UNITS), half = (f / VL_UNITS) & 1, u = f % VL_UNITS;
-      const bf16_t* src = (half ? lo : hi) + (long long)(col0 + row) * d + c * VL_KC + 8 * u;
-      breg[i] = *reinterpret_cast<const uint4*>(src);
-    }
-  };
-  auto store_b = [&](int buf, const uint4 (&breg)[BITEMS]) {
-#pragma unroll
-    for (int i = 0; i < BITEMS; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f / (2 * VL_UNITS), half = (f / VL_UNITS) & 1, u = f % VL_UNITS;
-      bs[buf][row][half][u ^ (row & 15)] = breg[i];
-    }
-  };
-
+  for (int i = 0; i < IPW; ++i) {
+    const int byte = 1024 * (wave * IPW + i) + 16 * lane;   // where this lane's DMA lands in the chunk
+    const int row = byte / ROWB;
+    const int hu = ((byte % ROWB) / 16) ^ (row & 15);       // (half, unit) kept in that slot
+    b_off[i] = (hu / U) * lo_delta + (row * d + 8 * (hu % U)) * 2;
+  }
+  const int nk = d / KC;
   floatx16 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  u32x4 a[D][J];
 
-  uint4 a_cur[8], a_nxt[8], b_nxt[BITEMS];
-  {
-    load_b(0, b_nxt);
+  auto issue = [&](int c, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int koff = c < nk ? c * KC * 2 : 0x40000000;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a_cur[j] = arow[j];
-    store_b(0, b_nxt);
-  }
-  __syncthreads();
-  for (int c = 0; c < nk; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nk;
-    if (more) {
-      load_b(c + 1, b_nxt);
-      const uint4* an = arow + (c + 1) * (VL_KC / 8);
+    for (int i = 0; i < IPW; ++i) vl_dma16(rb, lds0 + q * CHB + 1024 * (wave * IPW + i), b_off[i] + koff);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a_nxt[j] = an[j];
-    }
+    for (int j = 0; j < J; ++j) a[q][j] = vl_load16(ra, a_base + koff + 2 * (16 * j + 8 * h));
+  };
+  auto compute = [&](auto qc) {
+    constexpr int q = decltype(qc)::value;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 a = as_frag(a_cur[j]);
+    for (int j = 0; j < J; ++j) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[q][j]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const int row = 32 * n + (lane & 31);
-        const int u = (8 * (lane >> 5) + j) ^ (row & 15);
-        mfma32(acc[n], a, as_frag(bs[buf][row][0][u]));
-        mfma32(acc[n], a, as_frag(bs[buf][row][1][u]));
+        const char* p = &ring[q][0] + row * ROWB;
+        const int unit = 2 * j + h;
+        mfma32(acc[n], av, as_frag(*reinterpret_cast<const uint4*>(p + 16 * (unit ^ (row & 15)))));
+        mfma32(acc[n], av, as_frag(*reinterpret_cast<const uint4*>(p + 16 * ((U + unit) ^ (row & 15)))));
       }
     }
-    if (more) {
-      store_b(buf ^ 1, b_nxt);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a_cur[j] = a_nxt[j];
-    }
-    __syncthreads();
+  };
+  [&]<int... Q>(std::integer_sequence<int, Q...>) {
+    (issue(Q, std::integral_constant<int, Q>{}), ...);
+  }(std::make_integer_sequence<int, D - 1>{});
+  for (int c0 = 0; c0 < nk; c0 += D) {
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      auto step = [&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const int c = c0 + q;
+        if (c < nk) {
+          vl_wait<(D - 2) * (IPW + J), J>(a[q]);   // chunk c: its E registers and this wave's DMA
+          __syncthreads();                         // every wave's DMA of chunk c; slot (c - 1) % D free
+          issue(c + D - 1, std::integral_constant<int, (q + D - 1) % D>{});
+          compute(qc);
+        }
+      };
+      (step(std::integral_constant<int, Q>{}), ...);
+    }(std::make_integer_sequence<int, D>{});
   }
+  // the loads past the end are still outstanding: no wave leaves with a DMA
+  // into LDS in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // per column: max and sum of exp over this wave's 32 vocabulary rows
 #pragma unroll
@@ -337,14 +407,14 @@ hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void*
   auto* part = reinterpret_cast<float2*>(base + w.part);
   if (bf16) {
     const auto* hi = reinterpret_cast<const bf16_t*>(base + w.hi);
-    const auto* lo = reinterpret_cast<const bf16_t*>(base + w.lo);
+    const int lo_delta = (int)(w.lo - w.hi);
     for (int c0 = 0; c0 < w.Rp; c0 += 64) {
       if (w.Rp - c0 >= 64)
-        hipLaunchKernelGGL(vocab_lse_bf16_kernel<2>, dim3(w.nb), dim3(256), 0, s,
-                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo, c0, w.Rp, part);
+        hipLaunchKernelGGL((vocab_lse_bf16_kernel<2, 64, 4>), dim3(w.nb), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, w.Rp, part);
       else
-        hipLaunchKernelGGL(vocab_lse_bf16_kernel<1>, dim3(w.nb), dim3(256), 0, s,
-                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo, c0, w.Rp, part);
+        hipLaunchKernelGGL((vocab_lse_bf16_kernel<1, 128, 4>), dim3(w.nb), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, w.Rp, part);
     }
   } else {
     hipLaunchKernelGGL(vocab_lse_f32_kernel, dim3(w.nb), dim3(256), 0, s, reinterpret_cast<const float*>(E), V,
