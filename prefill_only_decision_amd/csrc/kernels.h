@@ -135,7 +135,7 @@ hipError_t launch_readout(bool bf16, const float* x, int d, const float* w_final
 // Workspace of the feature kernels for R distinct rows (byte offsets into
 // one device block): normalised rows hn fp32 [Rp, d], their bf16 hi / lo
 // split [Rp, d] each (bf16 models), per-block partial (max, sum) pairs
-// [nb, Rp] and lse [Rp]; Rp = R rounded up to 32.
+// [Rp, nb] and lse [Rp]; Rp = R rounded up to 32.
 struct FeatWs {
   int Rp = 0, nb = 0;
   size_t hn = 0, hi = 0, lo = 0, part = 0, lse = 0, bytes = 0;

@@ -35,7 +35,8 @@ constexpr int VL_ROWS = 32 * VL_WAVES;      // vocabulary rows per workgroup
 constexpr int VL_KC = 128;                  // k per staged chunk
 
 // 1. One workgroup per padded row; rows >= R are zero (so padded columns
-// contribute logits of 0 that the caller never reads).
+// contribute logits of 0 that the caller never reads).  Four consecutive
+// values per thread and step (d % 4 == 0).
 template <bool SPLIT>
 __global__ void __launch_bounds__(256)
 feat_norm_kernel(const float* __restrict__ x, int d, const int32_t* __restrict__ rows, int R,
@@ -45,26 +46,36 @@ feat_norm_kernel(const float* __restrict__ x, int d, const int32_t* __restrict__
   const int r = blockIdx.x;
   const long long o = (long long)r * d;
   if (r >= R) {
-    for (int i = threadIdx.x; i < d; i += 256) {
-      hn[o + i] = 0.f;
+    for (int i = 4 * threadIdx.x; i < d; i += 1024) {
+      *reinterpret_cast<float4*>(hn + o + i) = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (SPLIT) {
-        hi[o + i] = 0;
-        lo[o + i] = 0;
+        *reinterpret_cast<uint2*>(hi + o + i) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(lo + o + i) = make_uint2(0, 0);
       }
     }
     return;
   }
   const float* xr = x + (long long)rows[r] * d;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss += xr[i] * xr[i];
+  for (int i = 4 * threadIdx.x; i < d; i += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
   const float rs = rsqrtf(block_sum<4>(ss, red) / d + eps);
-  for (int i = threadIdx.x; i < d; i += 256) {
-    const float v = xr[i] * rs * w[i];
-    hn[o + i] = v;
+  for (int i = 4 * threadIdx.x; i < d; i += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    const float4 g = *reinterpret_cast<const float4*>(w + i);
+    const float e[4] = {v.x * rs * g.x, v.y * rs * g.y, v.z * rs * g.z, v.w * rs * g.w};
+    *reinterpret_cast<float4*>(hn + o + i) = make_float4(e[0], e[1], e[2], e[3]);
     if constexpr (SPLIT) {
-      const bf16_t h = f2bf(v);
-      hi[o + i] = h;
-      lo[o + i] = f2bf(v - bf2f(h));
+      bf16_t hb[4], lb[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hb[k] = f2bf(e[k]);
+        lb[k] = f2bf(e[k] - bf2f(hb[k]));
+      }
+      *reinterpret_cast<uint2*>(hi + o + i) = make_uint2(hb[0] | (uint32_t)hb[1] << 16, hb[2] | (uint32_t)hb[3] << 16);
+      *reinterpret_cast<uint2*>(lo + o + i) = make_uint2(lb[0] | (uint32_t)lb[1] << 16, lb[2] | (uint32_t)lb[3] << 16);
     }
   }
 }
@@ -155,7 +166,7 @@ __device__ __forceinline__ void vl_wait(u32x4 (&a)[J]) {
 template <int NT, int KC, int D>
 __global__ void __launch_bounds__(256, 2)
 vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* __restrict__ hi, int lo_delta,
-                      int col0, int ld_part, float2* __restrict__ part) {
+                      int col0, float2* __restrict__ part) {
   constexpr int U = KC / 8, J = KC / 16, NR = 32 * NT;
   constexpr int ROWB = 32 * U;            // LDS bytes per normalised row and chunk (hi + lo)
   constexpr int CHB = NR * ROWB;          // LDS bytes per chunk
@@ -257,7 +268,7 @@ vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* 
     float2 t = red[0][tid];
 #pragma unroll
     for (int w = 1; w < VL_WAVES; ++w) t = lse_pair(t, red[w][tid]);
-    part[(long long)blockIdx.x * ld_part + col0 + tid] = t;
+    part[(long long)(col0 + tid) * gridDim.x + blockIdx.x] = t;
   }
 }
 
@@ -266,7 +277,7 @@ vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* 
 // small).
 __global__ void __launch_bounds__(256)
 vocab_lse_f32_kernel(const float* __restrict__ E, int V, int d, const float* __restrict__ hn, int R,
-                     int ld_part, float2* __restrict__ part) {
+                     float2* __restrict__ part) {
   __shared__ float2 red[4];
   const int v = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* e = E + (long long)min(v, V - 1) * d;
@@ -291,21 +302,22 @@ vocab_lse_f32_kernel(const float* __restrict__ E, int V, int d, const float* __r
     if (threadIdx.x == 0) {
       float2 s = red[0];
       for (int w = 1; w < 4; ++w) s = lse_pair(s, red[w]);
-      part[(long long)blockIdx.x * ld_part + r] = s;
+      part[(long long)r * gridDim.x + blockIdx.x] = s;
     }
     __syncthreads();
   }
 }
 
-// 3. One workgroup per row: merge the nb partial pairs.  Thread t folds
-// blocks t, t + 256, ... in order, then a fixed butterfly and a fixed
-// cross-wave order finish; the result does not depend on timing.
+// 3. One workgroup per row: merge the row's nb partial pairs (contiguous).
+// Thread t folds blocks t, t + 256, ... in order, then a fixed butterfly and
+// a fixed cross-wave order finish; the result does not depend on timing.
 __global__ void __launch_bounds__(256)
-lse_merge_kernel(const float2* __restrict__ part, int nb, int ld_part, float* __restrict__ lse) {
+lse_merge_kernel(const float2* __restrict__ part, int nb, float* __restrict__ lse) {
   __shared__ float2 red[4];
   const int r = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float2* pr = part + (long long)r * nb;
   float2 t = make_float2(0.f, 0.f);
-  for (int b = threadIdx.x; b < nb; b += 256) t = lse_pair(t, part[(long long)b * ld_part + r]);
+  for (int b = threadIdx.x; b < nb; b += 256) t = lse_pair(t, pr[b]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     float2 u;
@@ -411,16 +423,16 @@ hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void*
     for (int c0 = 0; c0 < w.Rp; c0 += 64) {
       if (w.Rp - c0 >= 64)
         hipLaunchKernelGGL((vocab_lse_bf16_kernel<2, 64, 4>), dim3(w.nb), dim3(256), 0, s,
-                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, w.Rp, part);
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, part);
       else
         hipLaunchKernelGGL((vocab_lse_bf16_kernel<1, 128, 4>), dim3(w.nb), dim3(256), 0, s,
-                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, w.Rp, part);
+                           reinterpret_cast<const bf16_t*>(E), V, d, hi, lo_delta, c0, part);
     }
   } else {
     hipLaunchKernelGGL(vocab_lse_f32_kernel, dim3(w.nb), dim3(256), 0, s, reinterpret_cast<const float*>(E), V,
-                       d, reinterpret_cast<const float*>(base + w.hn), R, w.Rp, part);
+                       d, reinterpret_cast<const float*>(base + w.hn), R, part);
   }
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(R), dim3(256), 0, s, part, w.nb, w.Rp,
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(R), dim3(256), 0, s, part, w.nb,
                      reinterpret_cast<float*>(base + w.lse));
   return hipGetLastError();
 }
