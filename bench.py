@@ -137,6 +137,65 @@ def stored_traffic(workload):
     return rec["traffic_bytes_per_launch"] if rec.get("gemm_source_sha256") == source_digest() else None
 
 
+def features_leg(model, batch, shape, stream, args):
+    """Full-vocabulary log-probability features of every option token at
+    its question's marker row (one candidate per option, one group per
+    question), computed after the readout of the same request: the step with
+    features against the step without, and the vocabulary log-sum-exp
+    kernel against HBM bandwidth (it streams the tied embedding once per
+    launch of up to 64 distinct rows)."""
+    import torch
+    rows, toks, off, grp = [], [], [0], []
+    for j in range(batch.n_questions):
+        r = int(batch.cu_seqlens[batch.q_seq[j]]) + int(batch.q_marker[j])
+        for t in batch.options_of(j):
+            rows.append(r)
+            toks.append(int(t))
+            off.append(len(rows))
+            grp.append(j)
+    plan = model.plan(batch)
+    dp = torch.zeros(max(plan.n_options, 1), dtype=torch.float32, device="cuda")
+    dd = torch.zeros((max(plan.n_questions, 1), 6), dtype=torch.float32, device="cuda")
+    dlp = torch.zeros(len(rows), dtype=torch.float32, device="cuda")
+    dcl = torch.zeros(len(grp), dtype=torch.float32, device="cuda")
+    dcn = torch.zeros(len(grp), dtype=torch.float32, device="cuda")
+    plan.set_features(rows, toks, off, grp, dlp.data_ptr(), dcl.data_ptr(), dcn.data_ptr())
+    sp = stream.cuda_stream
+    plan.set_graph(True)
+    for _ in range(args.warmup):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    plan.set_graph(False)
+    prof = {}
+    n_prof = max(1, args.profile_steps)
+    for _ in range(n_prof):
+        for k, (n, us) in plan.profile(dp.data_ptr(), dd.data_ptr(), sp).items():
+            a, b = prof.get(k, (0, 0.0))
+            prof[k] = (a + n, b + us)
+    plan.free()
+    R = len(set(rows))
+    bf16 = shape.dtype == "bf16"
+    # bf16: one pass over the vocabulary per 64 distinct rows; fp32: one
+    launches = -(-(-(-R // 32) * 32) // 64) if bf16 else 1
+    n_v, us_v = prof["vocab_lse"]                      # one event interval per run, all passes
+    us_launch = us_v / n_v / launches
+    bytes_launch = shape.vocab * shape.d_model * (2 if bf16 else 4)   # the tied embedding, read once
+    gbps = bytes_launch / (us_launch * 1e-6) / 1e9
+    return {"targets": len(rows), "distinct_rows": R, "candidates": len(grp), "groups": int(batch.n_questions),
+            "ms_per_step_with_features": round(ms, 4),
+            "vocab_lse": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbps / HBM_PEAK_GBS, 4), "bytes_per_launch": bytes_launch,
+                          "launches_per_step": launches, "us_per_launch": round(us_launch, 2)},
+            "features_other_us_per_step": round(prof.get("features", (0, 0.0))[1] / n_prof, 2)}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-from":
         traffic_from_counters(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else "4b-single-512")
@@ -148,6 +207,8 @@ def main():
     ap.add_argument("--workload", default="4b-single-512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--no-features", action="store_true",
+                    help="skip the full-vocabulary log-prob feature leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB elementwise copy kernel (for scaling HBM counters)")
     args = ap.parse_args()
@@ -246,6 +307,8 @@ def main():
         "kernels": kernels, "roofline": roofline,
     }
     plan.free()
+    if not args.no_features:
+        out["features"] = features_leg(model, batch, shape, stream, args)
     model.free()
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)

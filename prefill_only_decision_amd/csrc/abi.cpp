@@ -532,6 +532,7 @@ int s1k_vocab_lse(int32_t dtype, const float* x, int32_t d, const float* w_final
   }
   hipError_t e = launch_feat_norm(bf16, x, d, rows, R, w_final, eps, V, ws, s);
   if (e == hipSuccess) e = launch_vocab_lse(bf16, E, V, d, R, ws, s);
+  if (e == hipSuccess) e = launch_lse_merge(bf16, V, d, R, ws, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(lse, static_cast<char*>(ws) + w.lse, 4 * (size_t)R, hipMemcpyDeviceToDevice, s);
   (void)hipFreeAsync(ws, s);

@@ -833,8 +833,10 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
     S1_TRY(launch_feat_norm(m->bf16, m->x, c.d_model, p->feat.rows, p->feat.R, m->final_norm, c.rms_eps,
                             c.vocab, p->feat_ws, s),
            "feature rows");
+    MARK(KC_FEATURES);
     S1_TRY(launch_vocab_lse(m->bf16, m->embed, c.vocab, c.d_model, p->feat.R, p->feat_ws, s), "vocabulary lse");
     MARK(KC_VOCAB_LSE);
+    S1_TRY(launch_lse_merge(m->bf16, c.vocab, c.d_model, p->feat.R, p->feat_ws, s), "lse merge");
     S1_TRY(launch_feat_targets(m->bf16, c.d_model, m->embed, c.vocab, p->feat, p->feat_logp, p->feat_cand_lp,
                                p->feat_cand_norm, p->feat_ws, s),
            "feature targets");

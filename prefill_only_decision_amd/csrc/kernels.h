@@ -160,9 +160,11 @@ struct FeatArgs {
 // Final RMSNorm of the R rows into the workspace (hn, and hi / lo for bf16).
 hipError_t launch_feat_norm(bool bf16, const float* x, int d, const int32_t* rows, int R, const float* w_final,
                             float eps, int V, void* ws, hipStream_t s);
-// lse[r] = log sum_v exp(hn[r] . E[v]) over the V rows of E, from the
-// workspace's normalised rows into its lse array.
+// Per-block partial (max, sum exp) pairs of hn[r] . E[v] over the V rows of
+// E, from the workspace's normalised rows; launch_lse_merge then forms
+// lse[r] = log sum_v exp(hn[r] . E[v]) in the workspace's lse array.
 hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void* ws, hipStream_t s);
+hipError_t launch_lse_merge(bool bf16, int V, int d, int R, void* ws, hipStream_t s);
 // Per-target logp = hn . E[token] - lse, then the candidate scores and
 // their normalisation per group (after launch_vocab_lse).
 hipError_t launch_feat_targets(bool bf16, int d, const void* E, int V, const FeatArgs& f, float* logp,

@@ -432,8 +432,14 @@ hipError_t launch_vocab_lse(bool bf16, const void* E, int V, int d, int R, void*
     hipLaunchKernelGGL(vocab_lse_f32_kernel, dim3(w.nb), dim3(256), 0, s, reinterpret_cast<const float*>(E), V,
                        d, reinterpret_cast<const float*>(base + w.hn), R, part);
   }
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(R), dim3(256), 0, s, part, w.nb,
-                     reinterpret_cast<float*>(base + w.lse));
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(bool bf16, int V, int d, int R, void* ws, hipStream_t s) {
+  const FeatWs w = feat_ws_layout(bf16, R, V, d);
+  char* base = static_cast<char*>(ws);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(R), dim3(256), 0, s, reinterpret_cast<const float2*>(base + w.part),
+                     w.nb, reinterpret_cast<float*>(base + w.lse));
   return hipGetLastError();
 }
 
@@ -477,6 +483,7 @@ hipError_t launch_features(bool bf16, const float* x, int d, const float* w_fina
   if (f.n_targets <= 0 || f.R <= 0) return hipSuccess;
   hipError_t e = launch_feat_norm(bf16, x, d, f.rows, f.R, w_final, eps, V, ws, s);
   if (e == hipSuccess) e = launch_vocab_lse(bf16, E, V, d, f.R, ws, s);
+  if (e == hipSuccess) e = launch_lse_merge(bf16, V, d, f.R, ws, s);
   if (e == hipSuccess) e = launch_feat_targets(bf16, d, E, V, f, logp, cand_lp, cand_norm, ws, s);
   return e;
 }
