@@ -105,10 +105,15 @@ __device__ __forceinline__ float2 lse_pair(float2 a, float2 b) {
 // a wait for "all but the last D - 2 groups" covers exactly the chunk about to
 // be used.  Both kinds of load are written as inline assembly: a
 // compiler-visible LDS DMA makes the compiler wait for every outstanding load
-// before any LDS read, which would empty the ring.  The wait names the
-// chunk's registers as operands, so nothing that uses them can be scheduled
-// before it; chunks past the end load from beyond the buffer's range, which
-// reads zeros without touching memory, so every group has the same size.
+// before any LDS read, which would empty the ring.  The compiler does not
+// know that these registers are written after the instruction issues, so
+// every load's destination must stay live until a wait that covers it: each
+// chunk's wait names the chunk's registers as operands (nothing that reads
+// them moves before it), every step issues a group unconditionally (chunks
+// past the end load from beyond the buffer's range, which reads zeros
+// without touching memory, so no register merges a loaded and a kept value),
+// and the final wait names every ring register, so none is reused while a
+// load past the end is still in flight.
 //
 // k order: the contraction may visit k in any order as long as both operands
 // use the same one.  Lane l (half h = l / 32) feeds MFMA step j with the
@@ -161,6 +166,16 @@ __device__ __forceinline__ void vl_wait(u32x4 (&a)[J]) {
     asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "n"(VM) : "memory");
   else
     static_assert(J == 8 || J == 4, "chunk register count");
+}
+
+// Marks the J registers as read and written here (no instruction).
+template <int J>
+__device__ __forceinline__ void vl_keep(u32x4 (&a)[J]) {
+  if constexpr (J == 8)
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                 "+v"(a[7]));
+  else
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
 
 template <int NT, int KC, int D>
@@ -242,9 +257,12 @@ vocab_lse_bf16_kernel(const bf16_t* __restrict__ E, int V, int d, const bf16_t* 
       (step(std::integral_constant<int, Q>{}), ...);
     }(std::make_integer_sequence<int, D>{});
   }
-  // the loads past the end are still outstanding: no wave leaves with a DMA
-  // into LDS in flight
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // drain the loads past the end (no wave leaves with a DMA into LDS in
+  // flight) with every ring register live across the wait
+  vl_wait<0, J>(a[0]);
+  [&]<int... Q>(std::integer_sequence<int, Q...>) {
+    (vl_keep(a[Q]), ...);
+  }(std::make_integer_sequence<int, D>{});
 
   // per column: max and sum of exp over this wave's 32 vocabulary rows
 #pragma unroll

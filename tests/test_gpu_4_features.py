@@ -39,6 +39,12 @@ def _rows(rng, n, d):
     (1000, 256, 7, 0.2),          # ragged vocabulary tail, large logits
     (129, 128, 33, 0.5),          # one row in the last block, one k chunk
     (1, 128, 2, 0.5),             # a vocabulary of one token: lse = z
+    # k-chunk counts that leave every remainder of the four-deep load ring
+    (5000, 256, 5, 0.02),         # 32-row pass, 2 chunks of 128
+    (5000, 384, 3, 0.02),         # 3 chunks
+    (5000, 384, 40, 0.02),        # 64-row pass, 6 chunks of 64
+    (5000, 640, 70, 0.02),        # 64-row pass (10 chunks) and 32-row pass (5)
+    (5000, 2688, 9, 0.02),        # 21 chunks
 ])
 def test_vocab_lse_bf16(V, d, R, std):
     torch = require_gpu()
