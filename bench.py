@@ -258,6 +258,9 @@ def main():
         return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - w0) / args.steps
 
     ms_eager, wall_eager = timed(False)
+    plan.set_invariant(True)             # row-invariant schedule, reported beside
+    ms_invariant, _ = timed(True)
+    plan.set_invariant(False)
     ms_step, wall = timed(True)          # the plan replayed as one HIP graph
     wall *= args.steps
     tokens = plan.tokens
@@ -303,6 +306,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "execution": "HIP graph replay of the plan",
         "ms_per_step_eager_launches": round(ms_eager, 4),
+        "ms_per_step_row_invariant": round(ms_invariant, 4),
         "load_s": round(t_load, 2), "weight_gen_s": round(t_gen, 2),
         "kernels": kernels, "roofline": roofline,
     }

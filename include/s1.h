@@ -209,6 +209,16 @@ void s1_plan_free(s1_plan* p);
  * fine).  Default: off.  Profiling always runs launch by launch. */
 int s1_plan_set_graph(s1_plan* p, int32_t enable);
 
+/* Row-invariant execution (enable != 0): every row's arithmetic is the same
+ * whatever else the request holds -- no K split in any projection GEMM (the
+ * tile shapes already accumulate K in one fixed order) and the chunk-parallel
+ * scan schedule in every pass -- so a sequence packed with others, run alone,
+ * or continued as a branch gives bitwise the same outputs as the plain
+ * forward of its tokens (RFC #114 comment "Plan: native OmniJev-4B v1.1":
+ * GEMM rows that do not depend on M keep batched rows order-invariant).
+ * Slower for short requests (no K split).  Default: off. */
+int s1_plan_set_invariant(s1_plan* p, int32_t enable);
+
 /* Tokens the plan processes (each prefix once plus every other sequence). */
 int64_t s1_plan_tokens(const s1_plan* p);
 

@@ -23,7 +23,7 @@ LORA_BITS = {"q": 1, "k": 2, "v": 4, "o": 8, "gate": 16, "up": 32, "down": 64}
 EXPORTS = (
     "s1_load_weights", "s1_prefill_decide", "s1_free", "s1_last_error", "s1_validate",
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
-    "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features",
+    "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs",
@@ -115,6 +115,7 @@ def load_library(path=LIB_PATH):
         "s1_plan_tokens": (i64, [vp]),
         "s1_plan_set_capture": (C.c_int, [vp, i32, vp, vp]),
         "s1_plan_set_graph": (C.c_int, [vp, i32]),
+        "s1_plan_set_invariant": (C.c_int, [vp, i32]),
         "s1_plan_set_features": (C.c_int, [vp, C.POINTER(Features), vp, vp, vp]),
         "s1_plan_profile": (C.c_int, [vp, vp, vp, vp, vp, C.POINTER(KernelTime), i32, C.POINTER(i32)]),
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -333,6 +334,9 @@ class Plan:
 
     def set_graph(self, enable=True):
         check(load_library().s1_plan_set_graph(self.handle, 1 if enable else 0))
+
+    def set_invariant(self, enable=True):
+        check(load_library().s1_plan_set_invariant(self.handle, 1 if enable else 0))
 
     def set_capture(self, rows, d_hidden_ptr):
         rows = np.ascontiguousarray(rows, dtype=np.int32)

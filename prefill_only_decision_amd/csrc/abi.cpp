@@ -199,6 +199,13 @@ int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, voi
   return rc;
 }
 
+int s1_plan_set_invariant(s1_plan* p, int32_t enable) {
+  if (!p) return set_error(S1_EINVAL, "plan is NULL");
+  p->p->invariant = enable != 0;
+  p->p->drop_graph();
+  return S1_OK;
+}
+
 int s1_plan_set_graph(s1_plan* p, int32_t enable) {
   if (!p) return set_error(S1_EINVAL, "plan is NULL");
   p->p->use_graph = enable != 0;

@@ -421,13 +421,15 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
       for (int q0 = 0; q0 < len; q0 += bq) blocks[ps].push_back({(int)k, q0});
     }
   }
-  // chunk-parallel scan when a pass has few (sequence, head) chains
+  // chunk-parallel scan when a pass has few (sequence, head) chains; the
+  // chunk lists are built for every bf16 pass, since the row-invariant mode
+  // runs every pass chunk-parallel
   std::vector<ScanSeq> chunks[2];
   std::vector<ChunkSeq> cseqs[2];
   for (int ps = 0; ps < 2; ++ps) {
     const long long chains = (long long)order[ps].size() * m->cfg.la_heads;
     p->pass[ps].chunked = m->bf16 && !order[ps].empty() && chains < 192;
-    if (!p->pass[ps].chunked) continue;
+    if (!m->bf16 || order[ps].empty()) continue;
     for (size_t k = 0; k < order[ps].size(); ++k) {
       const ScanSeq& sq = scan[ps][k];
       ChunkSeq cs{(int)chunks[ps].size(), 0, sq.s_in, sq.s_out};
@@ -676,7 +678,10 @@ namespace {
 
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
 // output (the GEMM picks the split it uses, up to this).
-int max_split(const Model* m, int M) { return M <= m->split_max_rows ? 4 : 1; }
+int max_split(const Model* m, const Plan* p, int M) {
+  if (p->invariant) return 1;     // the K order of a row must not depend on M
+  return M <= m->split_max_rows ? 4 : 1;
+}
 
 int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
   const s1_config& c = m->cfg;
@@ -714,7 +719,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
       S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s), "linear-attention in-projection");
       MARK(KC_GEMM_LA_IN);
       float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
-      if (ps.chunked)
+      if (ps.chunked || (p->invariant && ps.n_chunks > 0))
         S1_TRY(launch_scan_chunked(qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es, m->ld_qkv,
                                    m->lg, H, att, m->ld_att, ps.chunks, ps.n_chunks, ps.cseqs, ps.n_seqs,
                                    m->cstates, m->gamma, states, H, s),
@@ -759,7 +764,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     go.norm_out = xn;
     go.norm_eps = c.rms_eps;
     bool normed = false;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, T), m->splitws, s, GEMM_AUTO, &normed),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, GEMM_AUTO, &normed),
            "mixer out-projection");
     MARK(KC_GEMM_O);
     if (!normed) {
@@ -794,7 +799,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
       gd.norm_out = xn;
       gd.norm_eps = c.rms_eps;
     }
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, T), m->splitws, s, GEMM_AUTO, &xn_ready),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, GEMM_AUTO, &xn_ready),
            "FFN down");
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {

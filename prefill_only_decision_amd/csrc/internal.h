@@ -141,6 +141,9 @@ struct Plan {
   // HIP graph of the whole forward, replayed by s1_plan_run when enabled;
   // re-captured when the output or capture pointers change
   bool use_graph = false;
+  // row-invariant mode: no K split in any GEMM and the chunk-parallel scan in
+  // every pass, so a row's arithmetic does not depend on the rest of the batch
+  bool invariant = false;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   float* g_probs = nullptr;
