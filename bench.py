@@ -137,6 +137,95 @@ def stored_traffic(workload):
     return rec["traffic_bytes_per_launch"] if rec.get("gemm_source_sha256") == source_digest() else None
 
 
+SERVE_BUCKETS = tuple(range(256, 2049, 128))   # length buckets, 128 tokens apart
+
+
+def serve_leg(model, shape, stream, n_requests=48):
+    """Request replay at concurrency 1, 8 and 16 (the pages' protocol:
+    warm p50 / p95 latency, requests/s and decisions/s at predeclared
+    concurrency).  Requests are drawn like the packed 16-request workload:
+    one sequence of L ~ U[256, 2048] tokens with 1-6 questions.  At
+    concurrency 1 each request is copied into the smallest length-bucket
+    plan that holds it and its captured HIP graph is replayed (a plan built
+    per request is timed beside it); at concurrency c > 1, c requests arrive
+    together and run as one packed request (plan built per group).  Latency
+    is host wall time from arrival to the request's outputs on the host,
+    after one excluded warm-up round per mode."""
+    import numpy as np
+    import torch
+    from s1_workloads.batch import random_batch
+    rng = np.random.default_rng(2024)
+    reqs = [random_batch(shape.vocab, [int(rng.integers(256, 2049))], seed=[77, k],
+                         questions_per_seq=[int(rng.integers(1, 7))]) for k in range(n_requests)]
+    sp = stream.cuda_stream
+    max_q, max_o = 6, 64
+    cap = max_o + 2 * max_q
+    dp = torch.zeros(16 * cap, dtype=torch.float32, device="cuda")
+    dd = torch.zeros((16 * max_q, 6), dtype=torch.float32, device="cuda")
+
+    def stats(lat, total_s, n_dec):
+        lat = np.sort(np.asarray(lat) * 1e3)
+        return {"p50_ms": round(float(np.percentile(lat, 50)), 3), "p95_ms": round(float(np.percentile(lat, 95)), 3),
+                "requests_per_s": round(len(lat) / total_s, 1), "decisions_per_s": round(n_dec / total_s, 1)}
+
+    buckets = {L: model.bucket_plan(L, max_q, max_o) for L in SERVE_BUCKETS}
+    for b in buckets.values():
+        b.set_graph(True)
+
+    def one_bucket(r):
+        L = int(r.seq_lens[0])
+        plan = buckets[min(x for x in SERVE_BUCKETS if x >= L)]
+        plan.update(r)
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+        torch.cuda.synchronize()
+        _ = dp[:int(r.opt_offsets[-1])].cpu()
+
+    def one_fresh(r):
+        plan = model.plan(r)
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+        torch.cuda.synchronize()
+        _ = dp[:int(r.opt_offsets[-1])].cpu()
+        plan.free()
+
+    out = {"requests": n_requests, "request_mix": "one sequence, L ~ U[256, 2048], 1-6 questions",
+           "buckets": list(SERVE_BUCKETS)}
+    for name, fn in (("c1_bucket_graphs", one_bucket), ("c1_plan_per_request", one_fresh)):
+        for L in SERVE_BUCKETS:                      # warm-up: capture every bucket's graph once
+            fn(random_batch(shape.vocab, [L], seed=[78, L], questions_per_seq=[1]))
+        lat = []
+        t0 = time.perf_counter()
+        for r in reqs:
+            a = time.perf_counter()
+            fn(r)
+            lat.append(time.perf_counter() - a)
+        out[name] = stats(lat, time.perf_counter() - t0, sum(r.n_questions for r in reqs))
+    for b in buckets.values():
+        b.free()
+    from s1_workloads.batch import _assemble
+    for c in (8, 16):
+        groups = [reqs[i:i + c] for i in range(0, n_requests, c)]
+        lat, n_dec = [], 0
+
+        def run_group(g):
+            qs = [(k, int(r.q_marker[j]), int(r.q_type[j]), r.options_of(j)) for k, r in enumerate(g)
+                  for j in range(r.n_questions)]
+            packed = _assemble([r.tokens_of(0) for r in g], [-1] * len(g), qs)
+            plan = model.plan(packed)
+            plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+            torch.cuda.synchronize()
+            _ = dp[:int(packed.opt_offsets[-1])].cpu()
+            plan.free()
+        run_group(groups[0])                          # warm-up
+        t0 = time.perf_counter()
+        for g in groups:
+            a = time.perf_counter()
+            run_group(g)
+            lat.extend([time.perf_counter() - a] * len(g))
+            n_dec += sum(r.n_questions for r in g)
+        out[f"c{c}_packed"] = stats(lat, time.perf_counter() - t0, n_dec)
+    return out
+
+
 def features_leg(model, batch, shape, stream, args):
     """Full-vocabulary log-probability features of every option token at
     its question's marker row (one candidate per option, one group per
@@ -207,6 +296,8 @@ def main():
     ap.add_argument("--workload", default="4b-single-512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--no-serve", action="store_true",
+                    help="skip the request-replay leg (length-bucket graphs, concurrency 1 / 8 / 16)")
     ap.add_argument("--no-features", action="store_true",
                     help="skip the full-vocabulary log-prob feature leg")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -232,8 +323,9 @@ def main():
     w = make_weights(shape)
     t_gen = time.time() - t0
     T = batch.n_tokens
-    cfg = s1.make_config(shape, max_tokens=max(T, 1024), max_seqs=max(batch.n_seqs, 4),
-                         max_questions=max(batch.n_questions, 16), max_options=256, max_prefixes=4,
+    # budgets also cover the request-replay leg (16 packed requests of <= 2048 tokens)
+    cfg = s1.make_config(shape, max_tokens=max(T, 16 * 2048), max_seqs=max(batch.n_seqs, 16),
+                         max_questions=max(batch.n_questions, 96), max_options=256, max_prefixes=4,
                          max_positions=max(int(batch.seq_lens.max()) * 2, 8192))
     t0 = time.time()
     model = s1.Model(cfg, w.tensors, stream=stream)
@@ -313,6 +405,8 @@ def main():
     plan.free()
     if not args.no_features:
         out["features"] = features_leg(model, batch, shape, stream, args)
+    if not args.no_serve and shape.dtype == "bf16":
+        out["serving"] = serve_leg(model, shape, stream)
     model.free()
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)

@@ -202,6 +202,29 @@ int s1_plan_create(s1_model* m, const s1_batch* b, s1_plan** out);
 int s1_plan_run(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out, void* hip_stream);
 void s1_plan_free(s1_plan* p);
 
+/*
+ * Length buckets (RFC #114 comment "Plan: native OmniJev-4B v1.1" and the
+ * Cua-S1 issue's timing comments: graphs captured over length buckets).
+ * s1_plan_create_bucket builds a plan for one sequence of max_tokens tokens,
+ * max_questions questions and up to max_options options in all (>= 2 per
+ * question); s1_plan_update refills it with a request of one sequence (no
+ * prefix) that fits, without touching any device pointer, so a HIP graph
+ * captured from the plan is replayed as is.  The request's tokens are
+ * followed by token 0 up to max_tokens (causal mixers: padding rows never
+ * reach a request row) and its questions by two-way placeholder questions;
+ * a run writes s1_plan_questions() = max_questions decisions and
+ * s1_plan_options() <= max_options + 2 * max_questions probabilities, the
+ * request's first (size the outputs for the bound).  s1_plan_update copies synchronously and
+ * must not overlap a run of the plan.  Errors: S1_EINVAL (not a bucket plan,
+ * more than one sequence, malformed), S1_EBUDGET (the request does not fit).
+ */
+int s1_plan_create_bucket(s1_model* m, int32_t max_tokens, int32_t max_questions, int32_t max_options,
+                          s1_plan** out);
+int s1_plan_update(s1_plan* p, const s1_batch* b);
+/* Questions and option probabilities a run of the plan writes. */
+int32_t s1_plan_questions(const s1_plan* p);
+int64_t s1_plan_options(const s1_plan* p);
+
 /* Replay the plan as one HIP graph (enable != 0) instead of issuing every
  * kernel launch from the host.  The graph is captured on the first run and
  * captured again when the output or capture pointers change; the stream must

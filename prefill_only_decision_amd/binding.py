@@ -24,6 +24,7 @@ EXPORTS = (
     "s1_load_weights", "s1_prefill_decide", "s1_free", "s1_last_error", "s1_validate",
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
     "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
+    "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs",
@@ -116,6 +117,10 @@ def load_library(path=LIB_PATH):
         "s1_plan_set_capture": (C.c_int, [vp, i32, vp, vp]),
         "s1_plan_set_graph": (C.c_int, [vp, i32]),
         "s1_plan_set_invariant": (C.c_int, [vp, i32]),
+        "s1_plan_create_bucket": (C.c_int, [vp, i32, i32, i32, C.POINTER(vp)]),
+        "s1_plan_update": (C.c_int, [vp, C.POINTER(Batch)]),
+        "s1_plan_questions": (i32, [vp]),
+        "s1_plan_options": (i64, [vp]),
         "s1_plan_set_features": (C.c_int, [vp, C.POINTER(Features), vp, vp, vp]),
         "s1_plan_profile": (C.c_int, [vp, vp, vp, vp, vp, C.POINTER(KernelTime), i32, C.POINTER(i32)]),
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -292,6 +297,9 @@ class Model:
     def plan(self, batch):
         return Plan(self, batch)
 
+    def bucket_plan(self, max_tokens, max_questions, max_options):
+        return Plan(self, bucket=(max_tokens, max_questions, max_options))
+
     def free(self):
         if self.handle:
             load_library().s1_free(self.handle)
@@ -305,18 +313,32 @@ class Model:
 
 
 class Plan:
-    """Resident-input plan of one request (token ids and metadata on device)."""
+    """Resident-input plan of one request (token ids and metadata on device),
+    or, with bucket=(max_tokens, max_questions, max_options), a length-bucket
+    plan refilled by update()."""
 
-    def __init__(self, model, batch):
+    def __init__(self, model, batch=None, bucket=None):
         lib = load_library()
         self.model = model
-        cb, keep = make_batch(batch)
         h = C.c_void_p()
-        check(lib.s1_plan_create(model.handle, C.byref(cb), C.byref(h)))
-        self.handle = h
-        self.n_questions = cb.n_questions
-        self.n_options = int(np.asarray(batch.opt_offsets)[-1]) if cb.n_questions else 0
+        if bucket is not None:
+            check(lib.s1_plan_create_bucket(model.handle, int(bucket[0]), int(bucket[1]), int(bucket[2]),
+                                            C.byref(h)))
+            self.handle = h
+            self.n_questions = lib.s1_plan_questions(h)
+            self.n_options = int(bucket[2]) + 2 * int(bucket[1])   # capacity of the outputs
+        else:
+            cb, keep = make_batch(batch)
+            check(lib.s1_plan_create(model.handle, C.byref(cb), C.byref(h)))
+            self.handle = h
+            self.n_questions = cb.n_questions
+            self.n_options = int(np.asarray(batch.opt_offsets)[-1]) if cb.n_questions else 0
         self.tokens = lib.s1_plan_tokens(h)
+
+    def update(self, batch):
+        """Refill a length-bucket plan with a one-sequence request."""
+        cb, keep = make_batch(batch)
+        check(load_library().s1_plan_update(self.handle, C.byref(cb)))
 
     def run(self, d_probs_ptr, d_dec_ptr, stream=None):
         """Enqueue the forward and readout; d_* are device pointers (ints)."""

@@ -169,6 +169,30 @@ int s1_plan_create(s1_model* m, const s1_batch* b, s1_plan** out) {
   return S1_OK;
 }
 
+int s1_plan_create_bucket(s1_model* m, int32_t max_tokens, int32_t max_questions, int32_t max_options,
+                          s1_plan** out) {
+  if (!m || !out) return set_error(S1_EINVAL, "model or out is NULL");
+  Plan* p = nullptr;
+  const int rc = create_bucket_plan(m->m, max_tokens, max_questions, max_options, &p);
+  if (rc) return rc;
+  s1_plan* h = new (std::nothrow) s1_plan{p, m};
+  if (!h) {
+    delete p;
+    return set_error(S1_ENOMEM, "host allocation failed");
+  }
+  *out = h;
+  return S1_OK;
+}
+
+int s1_plan_update(s1_plan* p, const s1_batch* b) {
+  if (!p || !b) return set_error(S1_EINVAL, "plan or batch is NULL");
+  return update_bucket_plan(p->p, b);
+}
+
+int32_t s1_plan_questions(const s1_plan* p) { return p ? p->p->Q : 0; }
+
+int64_t s1_plan_options(const s1_plan* p) { return p ? p->p->total_opts : 0; }
+
 void s1_plan_free(s1_plan* p) {
   if (!p) return;
   delete p->p;

@@ -359,7 +359,7 @@ int load_model(const s1_config* cfg, const s1_tensor* tensors, int n, hipStream_
 }
 
 // ------------------------------------------------------------------ plans
-int create_plan(Model* m, const s1_batch* b, Plan** out) {
+int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
   int rc = validate_batch(&m->cfg, b);
   if (rc) return rc;
   Plan* p = new (std::nothrow) Plan();
@@ -452,7 +452,8 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
     return o;
   };
   const size_t o_ids = take(p->T * 4), o_pos = take(p->T * 4), o_qrow = take(p->Q * 4);
-  const size_t o_off = take((p->Q + 1) * 4), o_opt = take(p->total_opts * 4), o_qt = take(p->Q);
+  const size_t o_off = take((p->Q + 1) * 4), o_opt = take(std::max(p->total_opts, opts_capacity) * 4);
+  const size_t o_qt = take(p->Q);
   size_t o_scan[2], o_attn[2], o_blk[2], o_chk[2], o_cseq[2];
   for (int ps = 0; ps < 2; ++ps) {
     o_scan[ps] = take(scan[ps].size() * sizeof(ScanSeq));
@@ -511,6 +512,76 @@ int create_plan(Model* m, const s1_batch* b, Plan** out) {
     return set_error(S1_EBUDGET, "request needs more scan chunks than the workspace holds");
   }
   *out = p;
+  return S1_OK;
+}
+
+// ------------------------------------------------------ length buckets
+int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out) {
+  const s1_config& c = m->cfg;
+  if (T_b < 1 || Q_b < 1 || O_b < 2 || O_b < 2 * Q_b)
+    return set_error(S1_EINVAL, "bucket: need tokens >= 1, questions >= 1 and options >= 2 per question");
+  if (T_b > c.max_tokens || T_b > c.max_positions || Q_b > c.max_questions)
+    return set_error(S1_EBUDGET, "bucket exceeds the model's budgets");
+  // a placeholder request of the bucket's shape: token 0 everywhere, every
+  // question a two-way choice at row 0
+  std::vector<int32_t> cu = {0, T_b}, ids(T_b, 0), qs(Q_b, 0), qm(Q_b, 0), off(Q_b + 1), opt(2 * Q_b);
+  std::vector<uint8_t> qt(Q_b, S1_CHOICE);
+  for (int j = 0; j <= Q_b; ++j) off[j] = 2 * j;
+  for (int j = 0; j < Q_b; ++j) {
+    opt[2 * j] = 0;
+    opt[2 * j + 1] = 1;
+  }
+  s1_batch b{1, cu.data(), ids.data(), nullptr, Q_b, qs.data(), qm.data(), qt.data(), off.data(), opt.data()};
+  Plan* p = nullptr;
+  const int rc = create_plan(m, &b, &p, O_b);
+  if (rc) return rc;
+  p->bucket = true;
+  p->bucket_opts = O_b;
+  p->max_k = c.max_options;     // the readout's LDS is sized once, at capture
+  *out = p;
+  return S1_OK;
+}
+
+int update_bucket_plan(Plan* p, const s1_batch* b) {
+  if (!p->bucket) return set_error(S1_EINVAL, "plan was not created for a length bucket");
+  const Model* m = p->m;
+  int rc = validate_batch(&m->cfg, b);
+  if (rc) return rc;
+  if (b->n_seqs != 1 || (b->prefix_of && b->prefix_of[0] >= 0))
+    return set_error(S1_EINVAL, "a bucket takes one sequence without a prefix");
+  const int L = b->cu_seqlens[1] - b->cu_seqlens[0];
+  const int Q = b->n_questions;
+  const int nopt = Q > 0 ? b->opt_offsets[Q] : 0;
+  if (L > p->T || Q > p->Q || nopt > p->bucket_opts)
+    return set_error(S1_EBUDGET, "request exceeds the bucket (tokens, questions or options)");
+  // the request, then padding: token 0 after its end (rows past L never
+  // reach a real row: every mixer is causal), two-way placeholder questions
+  // at row 0 after its questions
+  std::vector<int32_t> ids(p->T, 0), qrow(p->Q, 0), off(p->Q + 1), opt;
+  std::vector<uint8_t> qt(p->Q, S1_CHOICE);
+  for (int t = 0; t < L; ++t) ids[t] = b->token_ids[b->cu_seqlens[0] + t];
+  opt.reserve(nopt + 2 * (p->Q - Q));
+  off[0] = 0;
+  for (int j = 0; j < p->Q; ++j) {
+    if (j < Q) {
+      qrow[j] = b->q_marker[j];
+      qt[j] = b->q_type[j];
+      for (int k = b->opt_offsets[j]; k < b->opt_offsets[j + 1]; ++k) opt.push_back(b->opt_ids[k]);
+    } else {
+      opt.push_back(0);
+      opt.push_back(1);
+    }
+    off[j + 1] = (int32_t)opt.size();
+  }
+  hipError_t e = hipMemcpy(p->ids, ids.data(), 4 * ids.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->q_row, qrow.data(), 4 * qrow.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->opt_off, off.data(), 4 * off.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->opt_ids, opt.data(), 4 * opt.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->q_type, qt.data(), qt.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "bucket update"));
+  p->total_opts = (int)opt.size();
+  p->real_T = L;
+  p->real_Q = Q;
   return S1_OK;
 }
 

@@ -144,6 +144,10 @@ struct Plan {
   // row-invariant mode: no K split in any GEMM and the chunk-parallel scan in
   // every pass, so a row's arithmetic does not depend on the rest of the batch
   bool invariant = false;
+  // length-bucket plan: created for up to T tokens, Q questions and
+  // bucket_opts options, refilled by update_bucket_plan between runs
+  bool bucket = false;
+  int bucket_opts = 0, real_T = 0, real_Q = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   float* g_probs = nullptr;
@@ -164,7 +168,9 @@ struct Plan {
 int validate_config(const s1_config* c);
 int validate_batch(const s1_config* c, const s1_batch* b);
 int load_model(const s1_config* cfg, const s1_tensor* t, int n, hipStream_t s, Model** out);
-int create_plan(Model* m, const s1_batch* b, Plan** out);
+int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity = 0);
+int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out);
+int update_bucket_plan(Plan* p, const s1_batch* b);
 int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden);
 int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp, float* d_cand_norm);
