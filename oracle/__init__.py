@@ -25,6 +25,9 @@ or fusion:
   question's marker position (Cua-S1 issue, first plan comment), and the
   answer fields (sys1rust README, "Try it": answer types and the two
   confidence numbers);
+* Gated DeltaNet (the gated delta rule with its short convolution and q/k
+  L2 normalisation), token by token and in the chunked WY form (Yang et al.
+  2024; Yang, Kautz, Hatamizadeh 2025), for shapes that ask for it;
 * language-model features: token log-probabilities normalised over the full
   vocabulary, computed chunk by chunk, and a candidate score normalised across
   the candidates of a question (RFC #114, section 4, note under the semantics
@@ -43,11 +46,13 @@ from .reference import (OracleModel, bf16_bits_to_float, round_to_bf16_bits,
                         rms_norm, rope_rotate_half, la_scan_recurrent,
                         la_scan_unrolled, la_scan_segmented, causal_attention, swiglu,
                         lora_merge, softmax, decision_fields, readout,
-                        vocab_log_probs, candidate_log_probs, prefill_decide, QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL)
+                        vocab_log_probs, candidate_log_probs, prefill_decide,
+                        l2_normalize, silu, causal_conv_silu, gdn_recurrent, gdn_chunked, QTYPE_CHOICE, QTYPE_SCORE, QTYPE_NOUL)
 
 __all__ = [
     "OracleModel", "bf16_bits_to_float", "round_to_bf16_bits", "rms_norm",
     "rope_rotate_half", "la_scan_recurrent", "la_scan_unrolled", "la_scan_segmented",
     "causal_attention", "swiglu", "lora_merge", "softmax", "decision_fields",
-    "readout", "vocab_log_probs", "candidate_log_probs", "prefill_decide", "QTYPE_CHOICE", "QTYPE_SCORE", "QTYPE_NOUL",
+    "readout", "vocab_log_probs", "candidate_log_probs", "prefill_decide",
+    "l2_normalize", "silu", "causal_conv_silu", "gdn_recurrent", "gdn_chunked", "QTYPE_CHOICE", "QTYPE_SCORE", "QTYPE_NOUL",
 ]

@@ -32,6 +32,12 @@ Readings taken where the pages are silent (tags used below):
         temperature or bias.
   (R15) LoRA targets: q, k, v, o of both mixer kinds (+ FFN gate, up, down on
         the 4B/27B shapes); the decay-gate projection is not adapted.
+  (R23) Gated DeltaNet (the layer the pages run, replacing the stand-in when
+        a shape asks for it): short causal depthwise convolution of width 4
+        on the q, k and v projections, then SiLU; q and k L2-normalised per
+        head (eps 1e-6 inside the root) and q scaled by 1/sqrt(dk); the gate
+        g of R2 as the decay; one write strength beta = sigmoid(u . w_b) per
+        (token, head); the gated delta update; no output gate or norm.
   (R21) a feature candidate scores the sum of its tokens' full-vocabulary
         log-probabilities, normalised by a log-softmax across the candidates
         of its question (the six-feature composition on top is not built).
@@ -159,6 +165,97 @@ def la_scan_segmented(q, k, v, g, S0=None, segment=512):
     for a in range(0, T, segment):
         b = min(T, a + segment)
         o[a:b], S = la_scan_unrolled(q[a:b], k[a:b], v[a:b], g[a:b], S)
+    return o, S
+
+
+def l2_normalize(x, eps=1e-6):
+    """x / sqrt(sum(x^2) + eps) over the last axis (the q / k normalisation of
+    Gated DeltaNet; the eps is reading R23)."""
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def causal_conv_silu(x, w, hist=None):
+    """Depthwise causal convolution over time, then SiLU (the short
+    convolution of Gated DeltaNet, R23):
+        y[t, c] = silu(sum_{j < W} w[c, j] * x[t - (W - 1) + j, c])
+    so w[c, W - 1] weighs the current token.  Rows before the sequence come
+    from hist [W - 1, C] (the last rows of a prefix, for a branch) or are
+    zero.  x: [T, C]; w: [C, W].  Returns (y [T, C], the last W - 1 rows of
+    the extended input, the history a continuation needs)."""
+    T, C = x.shape
+    W = w.shape[1]
+    h = np.zeros((W - 1, C), dtype=x.dtype) if hist is None else np.asarray(hist, dtype=x.dtype)
+    ext = np.concatenate([h, x], axis=0)
+    y = np.zeros_like(x)
+    for j in range(W):
+        y += w[:, j][None, :] * ext[j:j + T]
+    return silu(y), ext[T:]
+
+
+def gdn_recurrent(q, k, v, g, beta, S0=None):
+    """Gated delta rule, token by token (Yang, Kautz, Hatamizadeh, "Gated
+    Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025, the gated
+    delta update), written for a [dk, dv] state read as S^T q:
+        S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+        o_t = S_t^T q_t.
+    g_t in (0, 1] decays the state, beta_t in (0, 1) is the write strength;
+    with a unit key and beta = 1 the state then returns exactly v_t for k_t.
+    q, k: [T, H, dk]; v: [T, H, dv]; g, beta: [T, H].  Returns (o, S_T)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    S = np.zeros((H, dk, dv), dtype=q.dtype) if S0 is None else np.array(S0, dtype=q.dtype)
+    o = np.zeros((T, H, dv), dtype=q.dtype)
+    for t in range(T):
+        kS = np.einsum("hk,hkv->hv", k[t], S)                       # k_t^T S_{t-1}
+        S = g[t][:, None, None] * (S - beta[t][:, None, None] * k[t][:, :, None] * kS[:, None, :]) \
+            + beta[t][:, None, None] * k[t][:, :, None] * v[t][:, None, :]
+        o[t] = np.einsum("hkv,hk->hv", S, q[t])
+    return o, S
+
+
+def gdn_chunked(q, k, v, g, beta, S0=None, chunk=64):
+    """The gated delta rule over chunks of `chunk` tokens in the WY form
+    (Yang et al., "Parallelizing Linear Transformers with the Delta Rule over
+    Sequence Length", NeurIPS 2024, extended with the gate as in the Gated
+    DeltaNet paper).  Writing S_t = g_t S_{t-1} + k_t u_t^T with
+    u_t = beta_t (v_t - g_t S_{t-1}^T k_t), and, inside a chunk starting from
+    S_0, gamma_t = prod_{j <= t} g_j:
+        (I + L) U = diag(beta) V - diag(beta gamma) K S_0,
+            L[t, i] = beta_t (gamma_t / gamma_i) k_t . k_i  for i < t,
+        O   = diag(gamma) Q S_0 + ((Q K^T) * M) U,  M[t, i] = gamma_t / gamma_i, i <= t,
+        S_C = gamma_C S_0 + K^T diag(gamma_C / gamma) U.
+    The unit lower-triangular system is solved by forward substitution.
+    Gamma ratios are formed as exp of differences of cumulative logs (each
+    at most 1).  An exact reformulation of gdn_recurrent (the tests check one
+    against the other).  Returns (o, S_T)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dt = q.dtype
+    S = np.zeros((H, dk, dv), dtype=dt) if S0 is None else np.array(S0, dtype=dt)
+    o = np.zeros((T, H, dv), dtype=dt)
+    for a in range(0, T, chunk):
+        b = min(T, a + chunk)
+        C = b - a
+        G = np.cumsum(np.log(np.maximum(np.asarray(g[a:b], dtype=np.float64), 1e-300)), axis=0)   # [C, H]
+        tri_s = np.tril(np.ones((C, C), dtype=bool), -1)
+        tri = np.tril(np.ones((C, C), dtype=bool))
+        for h in range(H):
+            Kc, Vc, Qc = k[a:b, h], v[a:b, h], q[a:b, h]
+            Gh = G[:, h]
+            bt = np.asarray(beta[a:b, h], dtype=dt)
+            R = np.exp(np.minimum(Gh[:, None] - Gh[None, :], 0.0))                     # gamma_t / gamma_i
+            L = np.where(tri_s, bt[:, None] * R * (Kc @ Kc.T), 0.0).astype(dt)
+            rhs = bt[:, None] * Vc - (bt * np.exp(Gh))[:, None] * (Kc @ S[h])
+            U = np.zeros((C, dv), dtype=dt)
+            for t in range(C):
+                U[t] = rhs[t] - L[t, :t] @ U[:t]
+            M = np.where(tri, R, 0.0).astype(dt)
+            o[a:b, h] = np.exp(Gh)[:, None] * (Qc @ S[h]) + ((Qc @ Kc.T) * M) @ U
+            S[h] = np.exp(Gh[-1]) * S[h] + (Kc * np.exp(Gh[-1] - Gh)[:, None]).T @ U
     return o, S
 
 

@@ -239,6 +239,32 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert fails(P.test_vocab_log_probs_brute_force_loops)
     monkeypatch.undo()
 
+    monkeypatch.undo()
+
+    def gdn_delta_sign(q, k, v, g, beta, S0=None):   # adds beta k k^T S instead of removing it
+        T, H, dk = q.shape
+        S = np.zeros((H, dk, v.shape[2])) if S0 is None else np.array(S0, dtype=float)
+        o = np.zeros((T, H, v.shape[2]))
+        for t in range(T):
+            kS = np.einsum("hk,hkv->hv", k[t], S)
+            S = g[t][:, None, None] * (S + beta[t][:, None, None] * k[t][:, :, None] * kS[:, None, :]) \
+                + beta[t][:, None, None] * k[t][:, :, None] * v[t][:, None, :]
+            o[t] = np.einsum("hkv,hk->hv", S, q[t])
+        return o, S
+    monkeypatch.setattr(P.O, "gdn_recurrent", gdn_delta_sign)
+    assert fails(P.test_gdn_rewrite_under_one_key)
+    monkeypatch.undo()
+
+    real_chunked = O.gdn_chunked
+    def gdn_chunk_no_carry(q, k, v, g, beta, S0=None, chunk=64):   # drops the state between chunks
+        T = q.shape[0]
+        outs = [real_chunked(q[a:a + chunk], k[a:a + chunk], v[a:a + chunk], g[a:a + chunk],
+                             beta[a:a + chunk], S0 if a == 0 else None, chunk)[0] for a in range(0, T, chunk)]
+        return np.concatenate(outs), None
+    monkeypatch.setattr(P.O, "gdn_chunked", gdn_chunk_no_carry)
+    assert fails(P.test_gdn_chunked_equals_recurrence, 150, 64)
+    monkeypatch.undo()
+
     real_cand = O.candidate_log_probs
     def cand_over_all_groups(logp, off, grp):     # normalises across questions
         return real_cand(logp, off, np.zeros(len(grp), dtype=np.int64))

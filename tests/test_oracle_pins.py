@@ -437,3 +437,94 @@ def test_candidate_log_probs_hand_values():
     # a question with one candidate normalises to log 1 = 0
     _, n1 = O.candidate_log_probs([-3.0, -4.0], [0, 2], [5])
     assert n1[0] == 0.0
+
+
+# ------------------------------------------------------- Gated DeltaNet
+def _gdn_inputs(T, H=2, dk=8, dv=6, seed=0):
+    r = np.random.default_rng(seed)
+    q = O.l2_normalize(r.standard_normal((T, H, dk)))
+    k = O.l2_normalize(r.standard_normal((T, H, dk)))
+    v = r.standard_normal((T, H, dv))
+    g = r.uniform(0.6, 1.0, (T, H))
+    beta = r.uniform(0.05, 0.95, (T, H))
+    S0 = r.standard_normal((H, dk, dv)) * 0.3
+    return q, k, v, g, beta, S0
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 64), (7, 3), (64, 64), (150, 64), (37, 1)])
+def test_gdn_chunked_equals_recurrence(T, chunk):
+    q, k, v, g, beta, S0 = _gdn_inputs(T, seed=T)
+    o1, s1 = O.gdn_recurrent(q, k, v, g, beta, S0)
+    o2, s2 = O.gdn_chunked(q, k, v, g, beta, S0, chunk=chunk)
+    np.testing.assert_allclose(o2, o1, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s2, s1, rtol=1e-10, atol=1e-12)
+
+
+def test_gdn_without_writes_is_pure_decay():
+    q, k, v, g, beta, S0 = _gdn_inputs(20)
+    o, S = O.gdn_recurrent(q, k, v, g, np.zeros_like(beta), S0)
+    gam = np.cumprod(g, axis=0)
+    np.testing.assert_allclose(S, gam[-1][:, None, None] * S0, rtol=1e-12)
+    np.testing.assert_allclose(o, gam[:, :, None] * np.einsum("hkv,thk->thv", S0, q), rtol=1e-12, atol=1e-14)
+
+
+def test_gdn_orthonormal_keys_are_stored_exactly():
+    # g = 1, beta = 1: writing v_i under orthonormal keys k_i stores each
+    # exactly (a delta rule write replaces the value read under its key)
+    dk, dv, n = 8, 5, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:, :n].T[:, None, :]                      # [n, 1, dk]
+    v = rng.standard_normal((n, 1, dv))
+    one = np.ones((n, 1))
+    o, S = O.gdn_recurrent(k, k, v, one, one)       # query = the key just written
+    np.testing.assert_allclose(o, v, atol=1e-12)
+    np.testing.assert_allclose(np.einsum("kv,nk->nv", S[0], k[:, 0]), v[:, 0], atol=1e-12)
+
+
+def test_gdn_rewrite_under_one_key():
+    # same unit key twice: beta = 1 replaces the first value; beta = 1/2
+    # moves the stored value half way each time (closed forms)
+    dk = 4
+    kk = O.l2_normalize(rng.standard_normal(dk), eps=0.0)
+    k = np.tile(kk, (2, 1, 1))
+    v = rng.standard_normal((2, 1, 3))
+    _, S = O.gdn_recurrent(k, k, v, np.ones((2, 1)), np.ones((2, 1)))
+    np.testing.assert_allclose(S[0].T @ kk, v[1, 0], atol=1e-12)
+    vv = np.tile(v[:1], (2, 1, 1))
+    _, S = O.gdn_recurrent(k, k, vv, np.ones((2, 1)), np.full((2, 1), 0.5))
+    np.testing.assert_allclose(S[0].T @ kk, 0.75 * v[0, 0], atol=1e-12)
+
+
+def test_gdn_continuation():
+    q, k, v, g, beta, S0 = _gdn_inputs(90, seed=5)
+    o, S = O.gdn_recurrent(q, k, v, g, beta, S0)
+    oa, Sa = O.gdn_chunked(q[:41], k[:41], v[:41], g[:41], beta[:41], S0)
+    ob, Sb = O.gdn_chunked(q[41:], k[41:], v[41:], g[41:], beta[41:], Sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(Sb, S, rtol=1e-10, atol=1e-12)
+
+
+def test_causal_conv_matches_torch_and_continues():
+    T, C, W = 23, 10, 4
+    x = rng.standard_normal((T, C))
+    w = rng.standard_normal((C, W))
+    y, hist = O.causal_conv_silu(x, w)
+    xt = torch.from_numpy(x.T[None])                                 # [1, C, T]
+    ref = torch.nn.functional.conv1d(torch.nn.functional.pad(xt, (W - 1, 0)),
+                                     torch.from_numpy(w[:, None, :]), groups=C)
+    np.testing.assert_allclose(y, torch.nn.functional.silu(ref)[0].numpy().T, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(hist, x[-(W - 1):])
+    ya, ha = O.causal_conv_silu(x[:9], w)
+    yb, hb = O.causal_conv_silu(x[9:], w, ha)
+    np.testing.assert_allclose(np.concatenate([ya, yb]), y, rtol=1e-12)
+    # the current-token tap alone is a plain SiLU
+    e = np.zeros((C, W))
+    e[:, W - 1] = 1.0
+    np.testing.assert_allclose(O.causal_conv_silu(x, e)[0], x / (1 + np.exp(-x)), rtol=1e-12)
+
+
+def test_l2_normalize():
+    x = rng.standard_normal((5, 3, 16)) * 7
+    y = O.l2_normalize(x, eps=0.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(y * np.linalg.norm(x, axis=-1, keepdims=True), x, rtol=1e-12)
