@@ -88,6 +88,19 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
                         const int32_t* cu_seqlens, const float* s_init, float* s_final,
                         void* hip_stream);
 
+/* Gated DeltaNet scan (Yang, Kautz, Hatamizadeh, "Gated Delta Networks",
+ * ICLR 2025; RFC #114 section 5 for the fp32 state) over packed sequences,
+ * bf16, dk = dv = 128:
+ *   S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,
+ * in 64-token chunks in the WY form.  q, k, v elem [T, ld_qkv] with head h at
+ * columns h*128 .. h*128+127 (q and k already L2-normalised by the caller),
+ * log_g = log g and beta fp32 [T, H], o elem [T, H*128]; cu_seqlens host
+ * [n_seqs+1]; s_init / s_final optional fp32 [n_seqs, H, 128, 128] as in
+ * s1k_la_scan.  Synchronises the stream. */
+int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, const float* log_g, const float* beta,
+                 void* o, int32_t T, int32_t H, int32_t n_seqs, const int32_t* cu_seqlens, const float* s_init,
+                 float* s_final, void* hip_stream);
+
 /* Causal attention over packed sequences with grouped KV heads:
  *   o_t = sum_{s: pos_s <= pos_t} softmax_s(q_t . k_s / sqrt(hd)) v_s
  * q (elem [Tq, Hq, hd]), k, v (elem [Tkv, Hkv, hd]), o (elem [Tq, Hq, hd]).

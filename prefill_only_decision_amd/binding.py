@@ -27,7 +27,7 @@ EXPORTS = (
     "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
-    "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs",
+    "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs", "s1k_gdn_scan",
 )
 
 
@@ -134,6 +134,7 @@ def load_library(path=LIB_PATH):
         "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]),
         "s1k_readout": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "s1k_vocab_lse": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, i32, vp, vp, vp]),
+        "s1k_gdn_scan": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
         "s1k_token_logprobs": (C.c_int, [i32, vp, i32, i32, vp, f32, vp, i32, i32, vp, vp, i32, vp, vp,
                                          vp, vp, vp, vp]),
     }
@@ -480,3 +481,10 @@ def token_logprobs(dtype, x, n_rows, d, w_final, eps, E, V, rows, tokens, cand_o
     return _k("s1k_token_logprobs", dtype, C.c_void_p(x), n_rows, d, C.c_void_p(w_final), C.c_float(eps),
               C.c_void_p(E), V, len(rows), rows, tokens, len(g), off, g, C.c_void_p(logp),
               C.c_void_p(cand_logp or None), C.c_void_p(cand_norm or None), _stream(stream))
+
+
+def gdn_scan(q, k, v, ld_qkv, log_g, beta, o, T, H, cu_seqlens, s_init=None, s_final=None, stream=None):
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    return _k("s1k_gdn_scan", C.c_void_p(q), C.c_void_p(k), C.c_void_p(v), ld_qkv, C.c_void_p(log_g),
+              C.c_void_p(beta), C.c_void_p(o), T, H, len(cu) - 1, cu, C.c_void_p(s_init) if s_init else None,
+              C.c_void_p(s_final) if s_final else None, _stream(stream))

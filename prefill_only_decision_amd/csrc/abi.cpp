@@ -496,6 +496,49 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
   return dev_status(e, "s1k_la_scan_chunked");
 }
 
+int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, const float* log_g, const float* beta,
+                 void* o, int32_t T, int32_t H, int32_t n_seqs, const int32_t* cu_seqlens, const float* s_init,
+                 float* s_final, void* hip_stream) {
+  if (n_seqs < 0 || H < 1 || T < 0 || !cu_seqlens || !q || !k || !v || !log_g || !beta || !o)
+    return set_error(S1_EINVAL, "s1k_gdn_scan: unsupported arguments");
+  if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T))
+    return set_error(S1_EINVAL, "s1k_gdn_scan: cu_seqlens out of range");
+  if (n_seqs == 0) return S1_OK;
+  std::vector<ScanSeq> chunks;
+  std::vector<GdnSeq> seqs(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int a = cu_seqlens[i], len = cu_seqlens[i + 1] - a;
+    if (len < 0) return set_error(S1_EINVAL, "s1k_gdn_scan: cu_seqlens decreasing");
+    seqs[i] = {a, len, (int)chunks.size(), s_init ? i : -1, s_final ? i : -1};
+    for (int t0 = 0; t0 < len; t0 += 64) chunks.push_back({a + t0, std::min(64, len - t0), -1, -1});
+  }
+  if (chunks.empty()) return S1_OK;
+  const size_t sbytes = (size_t)n_seqs * H * 128 * 128 * sizeof(float);
+  const size_t wbytes = gdn_ws_bytes((int)chunks.size(), H);
+  const size_t b1 = chunks.size() * sizeof(ScanSeq), b2 = seqs.size() * sizeof(GdnSeq);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* dm = nullptr;
+  if (hipMalloc(&dm, al(sbytes) + al(wbytes) + al(b1) + al(b2)) != hipSuccess) {
+    (void)hipGetLastError();
+    return set_error(S1_ENOMEM, "s1k_gdn_scan: allocation failed");
+  }
+  float* st = reinterpret_cast<float*>(dm);
+  float* ws = reinterpret_cast<float*>(dm + al(sbytes));
+  auto* dch = reinterpret_cast<ScanSeq*>(dm + al(sbytes) + al(wbytes));
+  auto* dsq = reinterpret_cast<GdnSeq*>(dm + al(sbytes) + al(wbytes) + al(b1));
+  hipStream_t s = strm(hip_stream);
+  hipError_t e = hipMemcpy(dch, chunks.data(), b1, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(dsq, seqs.data(), b2, hipMemcpyHostToDevice);
+  if (e == hipSuccess && s_init) e = hipMemcpyAsync(st, s_init, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_gdn_scan(q, k, v, ld_qkv, log_g, beta, H, o, H * 128, dch, (int)chunks.size(), dsq, n_seqs, st, H,
+                        ws, s);
+  if (e == hipSuccess && s_final) e = hipMemcpyAsync(s_final, st, sbytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(dm);
+  return dev_status(e, "s1k_gdn_scan");
+}
+
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o, int32_t Hq, int32_t Hkv,
                   int32_t hd, int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len,
                   const int32_t* kv_row0, const int32_t* kv_pre_row0, const int32_t* kv_pre_len,

@@ -93,6 +93,20 @@ hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, i
 // index); `cseqs` gives each sequence's chunk range and its initial / final
 // state slots in `states`.  cstates [n_chunks][H][128][128] and gamma
 // [n_chunks][H] are workspace.
+// Gated DeltaNet scan: one sequence (rows row0 .. row0 + len - 1, chunks
+// c0 .. in the chunk list, state slots as ScanSeq).
+struct GdnSeq {
+  int row0, len, c0;
+  int s_in, s_out;
+};
+size_t gdn_ws_bytes(int n_chunks, int H);
+// q, k, v bf16 [T, ld_qkv] (head h at column h * 128), log_g and beta fp32
+// [T, ld_g]; chunks: every 64-token chunk of every sequence (row0, len);
+// ws: gdn_ws_bytes(n_chunks, H).
+hipError_t launch_gdn_scan(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
+                           const float* beta, int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
+                           const GdnSeq* seqs, int n_seqs, float* states, int H, float* ws, hipStream_t s);
+
 struct ChunkSeq {
   int c0, nc;    // chunk range
   int s_in;      // initial state slot in `states`, or -1

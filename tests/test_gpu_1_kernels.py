@@ -329,3 +329,44 @@ def test_readout(dtype):
             assert dec[j]["choice"] == f["choice"], j
         for key in ("score", "noul", "answer_confidence", "confidence", "entropy_confidence"):
             assert abs(float(dec[j][key]) - f[key]) < 1e-3 * max(1.0, abs(f[key])), (j, key)
+
+
+@pytest.mark.parametrize("H,lens,init", [(4, [1, 64, 65, 200, 640], True), (2, [1100], False), (16, [512], False)])
+def test_gdn_scan_bf16(H, lens, init):
+    """Gated DeltaNet scan against the oracle's token-by-token recurrence on
+    the same bf16 q, k, v (q and k unit vectors), gates and write strengths."""
+    torch = require_gpu()
+    log(f"gdn scan H={H} lens={lens} init={init}")
+    rng = np.random.default_rng([H, len(lens), 7])
+    T, dk = int(sum(lens)), 128
+    qk = rng.standard_normal((T, 2, H, dk))
+    qk = qk / np.linalg.norm(qk, axis=-1, keepdims=True)
+    qkv = np.concatenate([qk.reshape(T, 2 * H * dk), rng.standard_normal((T, H * dk))], axis=1)
+    bits = O.round_to_bf16_bits(qkv)
+    g = 1.0 / (1.0 + np.exp(-(rng.standard_normal((T, H)) + 2.0)))
+    lg = np.log(g).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = len(lens)
+    s0 = (rng.standard_normal((n, H, dk, dk)) * 0.1).astype(np.float32) if init else None
+    d_qkv, d_lg, d_b = dev_bits(bits), dev(lg), dev(beta)
+    d_o = torch.zeros((T, H * dk), dtype=torch.int16, device="cuda")
+    d_s0 = dev(s0) if init else None
+    d_sf = torch.zeros((n, H, dk, dk), dtype=torch.float32, device="cuda")
+    base = d_qkv.data_ptr()
+    B.gdn_scan(base, base + 2 * H * dk, base + 4 * H * dk, 3 * H * dk, d_lg.data_ptr(), d_b.data_ptr(),
+               d_o.data_ptr(), T, H, cu, d_s0.data_ptr() if init else None, d_sf.data_ptr(), stream_ptr())
+    torch.cuda.synchronize()
+    o = O.bf16_bits_to_float(host_bits(d_o)).reshape(T, H, dk)
+    sf = d_sf.cpu().numpy()
+    x = O.bf16_bits_to_float(bits).reshape(T, 3, H, dk)
+    worst_o = worst_s = 0.0
+    for i in range(n):
+        a, b = cu[i], cu[i + 1]
+        ro, rs = O.gdn_chunked(x[a:b, 0], x[a:b, 1], x[a:b, 2], np.exp(lg[a:b].astype(np.float64)),
+                               beta[a:b].astype(np.float64), s0[i].astype(np.float64) if init else None)
+        if b > a:
+            worst_o = max(worst_o, rel_l2(o[a:b], O.bf16_bits_to_float(O.round_to_bf16_bits(ro))))
+        worst_s = max(worst_s, rel_l2(sf[i], rs))
+    log(f"  rel L2 o vs rounded oracle {worst_o:.2e}, state {worst_s:.2e}")
+    assert worst_o < 1e-3 and worst_s < 1e-5
