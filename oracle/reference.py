@@ -490,6 +490,8 @@ class OracleModel:
 
     # -- mixers ----------------------------------------------------------
     def _linear(self, l, u, S0):
+        if self.s.la_kind == "gdn":
+            return self._gdn(l, u, S0)
         s = self.s
         T = u.shape[0]
         p = f"layers.{l}.la"
@@ -500,6 +502,30 @@ class OracleModel:
         g = sigmoid(self.proj(p + ".g", u))           # (R2) one gate per head
         o, S = la_scan_segmented(q, k, v, g, S0)
         return self.proj(p + ".o", self._a(o.reshape(T, s.la_heads * s.la_dv))), S
+
+    def _gdn(self, l, u, cache):
+        """Gated DeltaNet mixer (R23): projections q | k | v (the channels of
+        one depthwise causal convolution of width 4, then SiLU), the decay gate
+        g = sigmoid(u . w_g) and the write strength beta = sigmoid(u . w_b) per
+        head; q and k L2-normalised per head, q scaled by 1/sqrt(dk); the gated
+        delta rule (chunked WY form); the out-projection.  cache is None or
+        (state, the last 3 pre-convolution rows) of a prefix; returns the
+        same pair for this sequence's end."""
+        s = self.s
+        T = u.shape[0]
+        H, dk, dv = s.la_heads, s.la_dk, s.la_dv
+        p = f"layers.{l}.la"
+        u = self._a(u)
+        pre = np.concatenate([self.proj(p + ".q", u), self.proj(p + ".k", u), self.proj(p + ".v", u)], axis=1)
+        S0, hist = (None, None) if cache is None else cache
+        y, hist_out = causal_conv_silu(pre, self.W(p + ".conv"), hist)
+        q = l2_normalize(y[:, :H * dk].reshape(T, H, dk)) / math.sqrt(dk)
+        k = l2_normalize(y[:, H * dk:2 * H * dk].reshape(T, H, dk))
+        v = y[:, 2 * H * dk:].reshape(T, H, dv)
+        g = sigmoid(self.proj(p + ".g", u))
+        beta = sigmoid(self.proj(p + ".b", u))
+        o, S = gdn_chunked(self._a(q), self._a(k), self._a(v), g, beta, S0)
+        return self.proj(p + ".o", self._a(o.reshape(T, H * dv))), (S, hist_out)
 
     def _full(self, l, u, pos, prefix):
         s = self.s

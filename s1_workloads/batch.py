@@ -122,7 +122,7 @@ def make_batch(name: str) -> Batch:
     V = w.shape.vocab
     tok_rng = np.random.default_rng([w.workload_id, 1])
     lay_rng = np.random.default_rng([w.workload_id, 2])
-    if name in ("tiny-fp32", "4b-single-512"):
+    if name in ("tiny-fp32", "4b-single-512", "4b-gdn-single-512"):
         L = 128 if name == "tiny-fp32" else 512
         seqs = [tok_rng.integers(0, V, L).astype(np.int32)]
         marks = [63, 95, 127] if L == 128 else [383, 447, 511]

@@ -30,6 +30,9 @@ class ModelShape:
     rms_eps: float = 1e-6
     init_std: float = 0.02
     shape_id: int = 0        # seed component
+    la_kind: str = "gla"     # "gla": the stated gated linear-attention stand-in;
+                             # "gdn": Gated DeltaNet (short conv, L2-normalised q/k, delta rule)
+    conv_std: float = 0.5    # GDN short-convolution taps (width 4)
 
     def is_full(self, layer: int) -> bool:
         return layer % self.full_every == self.full_every - 1
@@ -46,7 +49,7 @@ class ModelShape:
         """Parameters of every projection (no embedding, no norms)."""
         d, f = self.d_model, self.ffn
         la = d * self.la_heads * (2 * self.la_dk + self.la_dv) + d * self.la_heads \
-            + self.la_heads * self.la_dv * d
+            + self.la_heads * self.la_dv * d + (d * self.la_heads if self.la_kind == "gdn" else 0)
         fa = d * self.fa_head_dim * (self.fa_q_heads + 2 * self.fa_kv_heads) \
             + self.fa_q_heads * self.fa_head_dim * d
         ffn = 3 * d * f
@@ -68,7 +71,12 @@ H27B = ModelShape(
     la_heads=40, la_dk=128, la_dv=128, fa_q_heads=40, fa_kv_heads=8, fa_head_dim=128,
     lora_rank=32, lora_alpha=64.0, lora_targets=LORA_ALL, dtype="bf16", shape_id=5)
 
-SHAPES = {s.name: s for s in (TINY, H4B, H27B)}
+H4B_GDN = ModelShape(
+    name="4b-gdn", n_layers=32, full_every=4, d_model=2560, ffn=9728, vocab=151936,
+    la_heads=16, la_dk=128, la_dv=128, fa_q_heads=16, fa_kv_heads=4, fa_head_dim=128,
+    lora_rank=32, lora_alpha=64.0, lora_targets=LORA_ALL, dtype="bf16", shape_id=6, la_kind="gdn")
+
+SHAPES = {s.name: s for s in (TINY, H4B, H27B, H4B_GDN)}
 
 
 @dataclass(frozen=True)
@@ -90,6 +98,8 @@ WORKLOADS = {w.name: w for w in (
              "4B-class bf16, 4096-token prefix + 20 branches x 64 tokens"),
     Workload("27b-single-1024", H27B, 5,
              "27B-class bf16, 1 x 1024 tokens, one choice over 10 options"),
+    Workload("4b-gdn-single-512", H4B_GDN, 6,
+             "4B-class bf16 with Gated DeltaNet layers, 1 x 512 tokens, choice(3)+score(4)+noul"),
 )}
 
 

@@ -34,6 +34,7 @@ class TensorSpec:
     name: str
     shape: Tuple[int, ...]
     kind: str            # "normal" or "ones"
+    std: float = 0.0     # normal: 0 means the shape's init_std
 
 
 def _mixer_shapes(s: ModelShape, full: bool) -> List[Tuple[str, Tuple[int, int]]]:
@@ -43,8 +44,11 @@ def _mixer_shapes(s: ModelShape, full: bool) -> List[Tuple[str, Tuple[int, int]]
         return [("q", (hq * hd, d)), ("k", (hkv * hd, d)), ("v", (hkv * hd, d)),
                 ("o", (d, hq * hd))]
     h, dk, dv = s.la_heads, s.la_dk, s.la_dv
-    return [("q", (h * dk, d)), ("k", (h * dk, d)), ("v", (h * dv, d)),
-            ("g", (h, d)), ("o", (d, h * dv))]
+    out = [("q", (h * dk, d)), ("k", (h * dk, d)), ("v", (h * dv, d)),
+           ("g", (h, d)), ("o", (d, h * dv))]
+    if s.la_kind == "gdn":
+        out.append(("b", (h, d)))          # write strength beta = sigmoid(u . w_b)
+    return out
 
 
 def tensor_specs(s: ModelShape) -> List[TensorSpec]:
@@ -57,6 +61,10 @@ def tensor_specs(s: ModelShape) -> List[TensorSpec]:
         mix = "fa" if s.is_full(l) else "la"
         for t, shp in _mixer_shapes(s, s.is_full(l)):
             specs.append(TensorSpec(f"{p}.{mix}.{t}", shp, "normal"))
+        if mix == "la" and s.la_kind == "gdn":
+            # depthwise causal convolution taps over the q | k | v channels
+            specs.append(TensorSpec(f"{p}.la.conv", (s.la_heads * (2 * s.la_dk + s.la_dv), 4), "normal",
+                                    s.conv_std))
         for t, shp in _mixer_shapes(s, s.is_full(l)):
             if t in s.lora_targets:
                 specs.append(TensorSpec(f"{p}.{mix}.{t}.lora_A", (r, shp[1]), "normal"))
@@ -88,10 +96,10 @@ class WeightSet:
         return sum(a.nbytes for a in self.tensors.values())
 
 
-def _fill_block(shape: ModelShape, tensor_index: int, block: int, out: np.ndarray):
+def _fill_block(shape: ModelShape, tensor_index: int, block: int, out: np.ndarray, std: float = 0.0):
     rng = np.random.default_rng([shape.shape_id, 0, tensor_index, block])
     tmp = rng.standard_normal(out.size, dtype=np.float32)
-    tmp *= np.float32(shape.init_std)
+    tmp *= np.float32(std or shape.init_std)
     if out.dtype == np.uint16:
         out[:] = f32_to_bf16_bits(tmp)
     else:
@@ -113,12 +121,12 @@ def make_weights(shape: ModelShape, threads: int = 0) -> WeightSet:
             continue
         flat = a.reshape(-1)
         for b in range(0, flat.size, BLOCK):
-            jobs.append((i, b // BLOCK, flat[b:b + BLOCK]))
+            jobs.append((i, b // BLOCK, flat[b:b + BLOCK], sp.std))
     if threads <= 0:
         threads = min(16, len(os.sched_getaffinity(0)))
     if threads == 1 or len(jobs) < 4:
-        for i, b, view in jobs:
-            _fill_block(shape, i, b, view)
+        for i, b, view, std in jobs:
+            _fill_block(shape, i, b, view, std)
     else:
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda j: _fill_block(shape, *j), jobs))

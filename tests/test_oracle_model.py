@@ -308,3 +308,91 @@ def test_token_log_probs_match_torch_log_softmax(tiny):
     logp, lse = m.token_log_probs(x, rows, ids[1:])
     np.testing.assert_allclose(logp, ref[rows, ids[1:]], rtol=1e-9, atol=1e-9)
     assert lse.shape == (len(ids),)
+
+
+def _torch_gdn_forward(shape, tensors, ids):
+    """Independent PyTorch formulation of a Gated DeltaNet hybrid (float64):
+    F.conv1d for the short convolution, the delta rule as a token loop."""
+    F = torch.nn.functional
+    t = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in tensors.items()}
+    s = shape
+    sc = s.lora_alpha / s.lora_rank
+
+    def lin(name, x):
+        y = F.linear(x, t[name])
+        if name + ".lora_A" in t:
+            y = y + sc * F.linear(F.linear(x, t[name + ".lora_A"]), t[name + ".lora_B"])
+        return y
+
+    def rope(a, pos):
+        hd = a.shape[-1]
+        half = hd // 2
+        z = torch.complex(a[..., :half], a[..., half:])
+        th = torch.tensor([s.rope_base ** (-(2 * i) / hd) for i in range(half)], dtype=torch.float64)
+        z = z * torch.polar(torch.ones_like(th), pos[:, None, None].double() * th)
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    T = len(ids)
+    H, dk, dv = s.la_heads, s.la_dk, s.la_dv
+    x = t["embed"][torch.from_numpy(ids.astype(np.int64))]
+    pos = torch.arange(T)
+    for l in range(s.n_layers):
+        u = F.rms_norm(x, (s.d_model,), t[f"layers.{l}.attn_norm"], eps=s.rms_eps)
+        if s.is_full(l):
+            p = f"layers.{l}.fa"
+            q = rope(lin(p + ".q", u).view(T, s.fa_q_heads, -1), pos)
+            k = rope(lin(p + ".k", u).view(T, s.fa_kv_heads, -1), pos)
+            v = lin(p + ".v", u).view(T, s.fa_kv_heads, -1)
+            rep = s.fa_q_heads // s.fa_kv_heads
+            k, v = k.repeat_interleave(rep, 1), v.repeat_interleave(rep, 1)
+            o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1),
+                                               v.transpose(0, 1), is_causal=True)
+            m = lin(p + ".o", o.transpose(0, 1).reshape(T, -1))
+        else:
+            p = f"layers.{l}.la"
+            pre = torch.cat([lin(p + ".q", u), lin(p + ".k", u), lin(p + ".v", u)], dim=1)     # [T, C]
+            w = t[p + ".conv"]                                                              # [C, 4]
+            y = F.silu(F.conv1d(F.pad(pre.T[None], (3, 0)), w[:, None, :], groups=w.shape[0])[0].T)
+            nrm = lambda a: a / torch.sqrt((a * a).sum(-1, keepdim=True) + 1e-6)
+            q = nrm(y[:, :H * dk].view(T, H, dk)) / dk ** 0.5
+            k = nrm(y[:, H * dk:2 * H * dk].view(T, H, dk))
+            v = y[:, 2 * H * dk:].view(T, H, dv)
+            g = torch.sigmoid(lin(p + ".g", u))
+            beta = torch.sigmoid(lin(p + ".b", u))
+            S = torch.zeros(H, dk, dv, dtype=torch.float64)
+            outs = []
+            eye = torch.eye(dk, dtype=torch.float64)
+            for i in range(T):
+                P = eye[None] - beta[i][:, None, None] * torch.einsum("hk,hj->hkj", k[i], k[i])
+                S = g[i][:, None, None] * torch.bmm(P, S) + beta[i][:, None, None] * torch.einsum("hk,hv->hkv", k[i], v[i])
+                outs.append(torch.einsum("hkv,hk->hv", S, q[i]))
+            m = lin(p + ".o", torch.stack(outs).reshape(T, -1))
+        y2 = x + m
+        wn = F.rms_norm(y2, (s.d_model,), t[f"layers.{l}.ffn_norm"], eps=s.rms_eps)
+        f = f"layers.{l}.ffn"
+        x = y2 + lin(f + ".down", F.silu(lin(f + ".gate", wn)) * lin(f + ".up", wn))
+    return x.numpy()
+
+
+def test_gdn_oracle_matches_independent_torch_formulation():
+    from dataclasses import replace
+    shape = replace(shape_of("tiny-fp32"), name="tiny-gdn", la_kind="gdn", shape_id=9)
+    w = make_weights(shape)
+    ids = make_batch("tiny-fp32").tokens_of(0)[:70]
+    x, _, _ = O.OracleModel(shape, w.tensors).forward(ids)
+    np.testing.assert_allclose(x, _torch_gdn_forward(shape, w.tensors, ids), rtol=1e-9, atol=1e-10)
+
+
+def test_gdn_branch_continuation_equals_plain_forward():
+    """A branch continued from the prefix's state and convolution history is
+    the plain forward of prefix + branch ([rfc114] section 5: the snapshot
+    holds the recurrent state and the convolution history)."""
+    from dataclasses import replace
+    shape = replace(shape_of("tiny-fp32"), name="tiny-gdn", la_kind="gdn", shape_id=9)
+    w = make_weights(shape)
+    m = O.OracleModel(shape, w.tensors)
+    b = random_batch(shape.vocab, [67, 2, 40], seed=3, prefix_of=[-1, 0, 0], questions_per_seq=[0, 1, 2])
+    r1 = O.prefill_decide(m, b, mode="plain")
+    r2 = O.prefill_decide(m, b, mode="continuation")
+    for j in r1["probs"]:
+        np.testing.assert_allclose(r2["probs"][j], r1["probs"][j], rtol=1e-10, atol=1e-12)
