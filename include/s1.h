@@ -46,6 +46,23 @@ enum {
 typedef enum { S1_F32 = 0, S1_BF16 = 1 } s1_dtype;
 typedef enum { S1_CHOICE = 0, S1_SCORE = 1, S1_NOUL = 2 } s1_qtype;
 
+/*
+ * Linear-attention layer kinds (s1_config.la_kind).
+ *  S1_LA_GLA: gated linear attention, S_t = g_t S_{t-1} + k_t v_t^T,
+ *    o_t = S_t^T q_t (the stand-in recurrence; RFC #114 sections 4-5 name
+ *    Gated DeltaNet without printing it).
+ *  S1_LA_GDN: Gated DeltaNet (Yang, Kautz, Hatamizadeh, ICLR 2025): the
+ *    q | k | v projections pass a depthwise causal convolution of width 4
+ *    (taps `.la.conv` [2 la_heads la_dk + la_heads la_dv, 4], the last tap on
+ *    the current token) and SiLU; q and k are L2-normalised per head (eps
+ *    1e-6 under the root), q scaled by 1/sqrt(la_dk); beta = sigmoid(u .
+ *    w_b) per head from `.la.b` [la_heads, d];
+ *    S_t = g_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T.  A branch
+ *    continues from its prefix's state and last three pre-convolution rows.
+ *    bf16 models only.
+ */
+enum { S1_LA_GLA = 0, S1_LA_GDN = 1 };
+
 /* LoRA target bits of s1_config.lora_targets. */
 enum {
   S1_LORA_Q = 1 << 0, S1_LORA_K = 1 << 1, S1_LORA_V = 1 << 2, S1_LORA_O = 1 << 3,
@@ -83,6 +100,7 @@ typedef struct {
   int32_t max_options;        /* per question */
   int32_t max_prefixes;       /* distinct prefix sequences per request */
   int64_t max_positions;      /* prefix length + branch length */
+  int32_t la_kind;            /* linear-attention layers: S1_LA_GLA or S1_LA_GDN */
 } s1_config;
 
 /*
@@ -92,7 +110,8 @@ typedef struct {
  * [out, in] (y = x W^T).  Names:
  *   embed [vocab, d] (tied: also the readout rows), final_norm [d]
  *   layers.{l}.attn_norm [d], layers.{l}.ffn_norm [d]
- *   layers.{l}.la.{q,k,v,g,o}   (linear-attention layers; g is [la_heads, d])
+ *   layers.{l}.la.{q,k,v,g,o}   (linear-attention layers; g is [la_heads, d];
+ *                                Gated DeltaNet layers also .b and .conv)
  *   layers.{l}.fa.{q,k,v,o}     (full-attention layers)
  *   layers.{l}.ffn.{gate,up,down}
  *   <projection>.lora_A [r, in] and <projection>.lora_B [out, r] for every

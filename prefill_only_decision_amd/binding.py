@@ -48,6 +48,7 @@ class Config(C.Structure):
         ("dtype", C.c_int32),
         ("max_tokens", C.c_int64), ("max_seqs", C.c_int32), ("max_questions", C.c_int32),
         ("max_options", C.c_int32), ("max_prefixes", C.c_int32), ("max_positions", C.c_int64),
+        ("la_kind", C.c_int32),
     ]
 
 
@@ -177,6 +178,7 @@ def make_config(shape, max_tokens=None, max_seqs=64, max_questions=256, max_opti
     c.max_options = int(max_options)
     c.max_prefixes = int(max_prefixes)
     c.max_positions = int(max_positions or c.max_tokens)
+    c.la_kind = 1 if getattr(shape, "la_kind", "gla") == "gdn" else 0
     return c
 
 

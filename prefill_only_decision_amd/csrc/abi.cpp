@@ -40,6 +40,9 @@ int validate_config(const s1_config* c) {
     return set_error(S1_EINVAL, "budgets must be positive (max_options >= 2)");
   if (c->max_tokens > (1LL << 30) || c->max_positions > (1LL << 24))
     return set_error(S1_EINVAL, "max_tokens or max_positions too large");
+  if (c->la_kind != S1_LA_GLA && c->la_kind != S1_LA_GDN) return set_error(S1_EINVAL, "unknown la_kind");
+  if (c->la_kind == S1_LA_GDN && c->dtype != S1_BF16)
+    return set_error(S1_EINVAL, "Gated DeltaNet layers need a bf16 model");
   if (c->d_model + c->max_options > 16384)
     return set_error(S1_EINVAL, "d_model + max_options must not exceed 16384 (readout LDS)");
   if (c->dtype == S1_BF16) {

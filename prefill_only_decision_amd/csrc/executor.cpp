@@ -177,6 +177,18 @@ class Loader {
     return S1_OK;
   }
 
+  // A small [rows, cols] tensor converted to fp32 (convolution taps).
+  int taps(const std::string& name, int rows, int cols, float** out) {
+    const void* w = nullptr;
+    int rc = fetch(name, rows, cols, &w);
+    if (rc) return rc;
+    *out = static_cast<float*>(m_->alloc((size_t)rows * cols * sizeof(float)));
+    S1_TRY(launch_to_f32(m_->bf16, w, *out, (long long)rows * cols, s_), "convolution taps");
+    S1_TRY(hipStreamSynchronize(s_), "convolution taps");
+    release();
+    return S1_OK;
+  }
+
   int norm(const std::string& name, int d, float** out) {
     const void* w = nullptr;
     int rc = fetch(name, d, -1, &w);
@@ -219,12 +231,17 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
     if ((rc = ld.norm(p + ".ffn_norm", d, &L.ffn_norm))) return rc;
     if (!L.full) {
       const std::string q = p + ".la";
-      L.n_in = 2 * H * dk + H * dv + H;
+      const bool gdn = c.la_kind == S1_LA_GDN;
+      L.n_in = 2 * H * dk + H * dv + (gdn ? 2 : 1) * H;
       L.w_in = m->alloc((size_t)L.n_in * d * m->esz);
       if ((rc = ld.projection(q + ".q", H * dk, d, tg & S1_LORA_Q, L.w_in, offset_map(H * dk, 0)))) return rc;
       if ((rc = ld.projection(q + ".k", H * dk, d, tg & S1_LORA_K, L.w_in, offset_map(H * dk, H * dk)))) return rc;
       if ((rc = ld.projection(q + ".v", H * dv, d, tg & S1_LORA_V, L.w_in, offset_map(H * dv, 2 * H * dk)))) return rc;
       if ((rc = ld.projection(q + ".g", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv)))) return rc;
+      if (gdn) {
+        if ((rc = ld.projection(q + ".b", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv + H)))) return rc;
+        if ((rc = ld.taps(q + ".conv", 2 * H * dk + H * dv, 4, &L.conv))) return rc;
+      }
       L.k_o = H * dv;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
       if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
@@ -272,6 +289,12 @@ int alloc_workspace(Model* m) {
   m->xn = m->alloc(T * d * m->esz);
   m->qkv = m->alloc(T * m->ld_qkv * m->esz);
   m->lg = static_cast<float*>(m->alloc(T * H * sizeof(float)));
+  if (c.la_kind == S1_LA_GDN) {
+    const long long Cc = 2LL * H * c.la_dk + (long long)H * c.la_dv;
+    m->beta = static_cast<float*>(m->alloc(T * H * sizeof(float)));
+    m->qkv2 = m->alloc(T * m->ld_qkv * m->esz);
+    m->conv_hist = m->alloc((size_t)std::max(1, m->n_la) * c.max_prefixes * 3 * Cc * m->esz);
+  }
   m->att = m->alloc(T * m->ld_att * m->esz);
   m->hbuf = m->alloc(T * (long long)c.ffn * m->esz);
   m->kc = m->alloc((size_t)std::max(1, m->n_fa) * T * Hkv * hd * m->esz);
@@ -283,6 +306,7 @@ int alloc_workspace(Model* m) {
     m->max_chunks = (int)((T + 63) / 64) + c.max_seqs;
     m->cstates = static_cast<float*>(m->alloc((size_t)m->max_chunks * H * c.la_dk * c.la_dv * sizeof(float)));
     m->gamma = static_cast<float*>(m->alloc((size_t)m->max_chunks * H * sizeof(float)));
+    if (c.la_kind == S1_LA_GDN) m->gdn_ws = static_cast<float*>(m->alloc(gdn_ws_bytes(m->max_chunks, H)));
   }
   m->split_max_rows = (int)std::min<long long>(T, 2048);
   m->splitws_elems = 4LL * m->split_max_rows * d;
@@ -441,6 +465,24 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
       cseqs[ps].push_back(cs);
     }
   }
+  if (m->cfg.la_kind == S1_LA_GDN)
+    for (int i = 0; i < n; ++i)
+      if (slot[i] >= 0 && b->cu_seqlens[i + 1] == b->cu_seqlens[i]) {
+        delete p;
+        return set_error(S1_EINVAL, "a prefix of a Gated DeltaNet model needs at least one token");
+      }
+  // Gated DeltaNet: every sequence with its first chunk, and each row's
+  // sequence (pass-local), for the convolution and the scan
+  std::vector<GdnSeq> gseqs[2];
+  std::vector<int32_t> rowseq[2];
+  for (int ps = 0; ps < 2 && m->cfg.la_kind == S1_LA_GDN; ++ps) {
+    rowseq[ps].assign(p->pass[ps].T, 0);
+    for (size_t k = 0; k < order[ps].size(); ++k) {
+      const ScanSeq& sq = scan[ps][k];
+      gseqs[ps].push_back({sq.row0, sq.len, cseqs[ps][k].c0, sq.s_in, sq.s_out});
+      for (int t = 0; t < sq.len; ++t) rowseq[ps][sq.row0 - p->pass[ps].r0 + t] = (int32_t)k;
+    }
+  }
   std::vector<int32_t> qrow(p->Q);
   for (int j = 0; j < p->Q; ++j) qrow[j] = row0[b->q_seq[j]] + b->q_marker[j];
 
@@ -454,13 +496,15 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
   const size_t o_ids = take(p->T * 4), o_pos = take(p->T * 4), o_qrow = take(p->Q * 4);
   const size_t o_off = take((p->Q + 1) * 4), o_opt = take(std::max(p->total_opts, opts_capacity) * 4);
   const size_t o_qt = take(p->Q);
-  size_t o_scan[2], o_attn[2], o_blk[2], o_chk[2], o_cseq[2];
+  size_t o_scan[2], o_attn[2], o_blk[2], o_chk[2], o_cseq[2], o_gseq[2], o_rseq[2];
   for (int ps = 0; ps < 2; ++ps) {
     o_scan[ps] = take(scan[ps].size() * sizeof(ScanSeq));
     o_attn[ps] = take(attn[ps].size() * sizeof(AttnSeq));
     o_blk[ps] = take(blocks[ps].size() * sizeof(AttnBlock));
     o_chk[ps] = take(chunks[ps].size() * sizeof(ScanSeq));
     o_cseq[ps] = take(cseqs[ps].size() * sizeof(ChunkSeq));
+    o_gseq[ps] = take(gseqs[ps].size() * sizeof(GdnSeq));
+    o_rseq[ps] = take(rowseq[ps].size() * sizeof(int32_t));
   }
   std::vector<char> host(off, 0);
   auto put = [&](size_t o, const void* src, size_t bytes) {
@@ -480,6 +524,8 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
     put(o_blk[ps], blocks[ps].data(), blocks[ps].size() * sizeof(AttnBlock));
     put(o_chk[ps], chunks[ps].data(), chunks[ps].size() * sizeof(ScanSeq));
     put(o_cseq[ps], cseqs[ps].data(), cseqs[ps].size() * sizeof(ChunkSeq));
+    put(o_gseq[ps], gseqs[ps].data(), gseqs[ps].size() * sizeof(GdnSeq));
+    put(o_rseq[ps], rowseq[ps].data(), rowseq[ps].size() * sizeof(int32_t));
   }
   if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
     (void)hipGetLastError();
@@ -505,6 +551,8 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
     p->pass[ps].chunks = reinterpret_cast<ScanSeq*>(dv + o_chk[ps]);
     p->pass[ps].n_chunks = (int)chunks[ps].size();
     p->pass[ps].cseqs = reinterpret_cast<ChunkSeq*>(dv + o_cseq[ps]);
+    p->pass[ps].gseqs = reinterpret_cast<GdnSeq*>(dv + o_gseq[ps]);
+    p->pass[ps].row_seq = reinterpret_cast<int32_t*>(dv + o_rseq[ps]);
   }
   if (p->pass[0].n_chunks + p->pass[1].n_chunks > 0 &&
       std::max(p->pass[0].n_chunks, p->pass[1].n_chunks) > m->max_chunks) {
@@ -787,10 +835,26 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
       g.out1 = m->lg + (size_t)r0 * H;
       g.ld1 = H;
       g.nsplit = 2 * H * dk + H * dv;
+      const bool gdn = c.la_kind == S1_LA_GDN;
+      if (gdn) {
+        g.out2 = m->beta + (size_t)r0 * H;
+        g.nsplit2 = g.nsplit + H;
+      }
       S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s), "linear-attention in-projection");
       MARK(KC_GEMM_LA_IN);
       float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
-      if (ps.chunked || (p->invariant && ps.n_chunks > 0))
+      if (gdn) {
+        char* q2 = static_cast<char*>(m->qkv2);
+        const size_t Cc = (size_t)2 * H * dk + (size_t)H * dv;
+        char* hist = static_cast<char*>(m->conv_hist) + (size_t)L.la_idx * c.max_prefixes * 3 * Cc * es;
+        S1_TRY(launch_gdn_conv(qkv, q2, m->ld_qkv, L.conv, H, r0, T, ps.row_seq, ps.gseqs, hist,
+                               1.f / sqrtf((float)dk), s),
+               "Gated DeltaNet convolution");
+        S1_TRY(launch_gdn_scan(q2, q2 + (size_t)H * dk * es, q2 + (size_t)2 * H * dk * es, m->ld_qkv, m->lg,
+                               m->beta, H, att, m->ld_att, ps.chunks, ps.n_chunks, ps.gseqs, ps.n_seqs, states, H,
+                               m->gdn_ws, s),
+               "Gated DeltaNet scan");
+      } else if (ps.chunked || (p->invariant && ps.n_chunks > 0))
         S1_TRY(launch_scan_chunked(qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es, m->ld_qkv,
                                    m->lg, H, att, m->ld_att, ps.chunks, ps.n_chunks, ps.cseqs, ps.n_seqs,
                                    m->cstates, m->gamma, states, H, s),

@@ -169,8 +169,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
             } else if constexpr (EPI == EPI_GATE) {
               if (col < g.nsplit)
                 gptr<T>(g.out0)[(long long)row * g.ld0 + col] = from_f<T>(v);
-              else
+              else if (g.out2 == nullptr || col < g.nsplit2)
                 gptr<float>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = log_sigmoid(v);
+              else
+                gptr<float>(g.out2)[(long long)row * g.ld1 + (col - g.nsplit2)] = 1.f / (1.f + __expf(-v));
             }
           }
         }

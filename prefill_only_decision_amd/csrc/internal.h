@@ -27,6 +27,7 @@ struct LayerW {
   void* w_gu = nullptr;         // gate/up interleaved in blocks of 32 rows, [2 * ffn_pad, d]
   int n_gu = 0;
   void* w_down = nullptr;       // [d, ffn]
+  float* conv = nullptr;        // Gated DeltaNet: convolution taps fp32 [3 H 128][4]
 };
 
 // Kernel families timed by s1_plan_profile.
@@ -68,6 +69,10 @@ struct Model {
   void* qkv = nullptr;          // LA: q | k | v; FA: q          [T, ld_qkv]
   int ld_qkv = 0;
   float* lg = nullptr;          // log decay gate fp32 [T, H]
+  float* beta = nullptr;        // Gated DeltaNet write strength fp32 [T, H]
+  void* qkv2 = nullptr;         // Gated DeltaNet: convolved, normalised q | k | v [T, ld_qkv]
+  void* conv_hist = nullptr;    // [n_la][max_prefixes][3][3 H 128]: prefix pre-convolution rows
+  float* gdn_ws = nullptr;      // W | Ut per (chunk, head)
   void* att = nullptr;          // mixer output [T, ld_att]
   int ld_att = 0;
   void* hbuf = nullptr;         // SwiGLU output [T, ffn]
@@ -99,6 +104,8 @@ struct PassPlan {
   ScanSeq* chunks = nullptr;    // device [n_chunks]
   int n_chunks = 0;
   ChunkSeq* cseqs = nullptr;    // device [n_seqs]
+  GdnSeq* gseqs = nullptr;      // device [n_seqs]: sequences with their first chunk
+  int32_t* row_seq = nullptr;   // device [T]: each row's sequence in gseqs
   int32_t* cap_rows = nullptr;  // device [n_cap]: rows captured in this pass
   int32_t* cap_dst = nullptr;   // device [n_cap]: index in the capture list
   int n_cap = 0;

@@ -12,7 +12,9 @@ enum Epi {
   EPI_F32 = 0,   // out0 fp32 [M, ld0]
   EPI_RESID,     // out0 fp32 [M, ld0] += C            (residual add)
   EPI_GATE,      // cols < nsplit: out0 elem [M, ld0]; cols >= nsplit:
-                 //   out1 fp32 [M, ld1] = log(sigmoid(C))   (decay gate)
+                 //   out1 fp32 [M, ld1] = log(sigmoid(C))   (decay gate);
+                 //   with out2 set, cols >= nsplit2: out2 fp32 [M, ld1] =
+                 //   sigmoid(C)                            (write strength)
   EPI_SWIGLU,    // column groups of 64 = [32 gate | 32 up]:
                  //   out0 elem [M, ld0][f] = silu(gate) * up, f < n_valid
   EPI_QKV,       // cols < nsplit: q (rope) -> out0; < nsplit2: k (rope) ->
@@ -103,6 +105,15 @@ size_t gdn_ws_bytes(int n_chunks, int H);
 // q, k, v bf16 [T, ld_qkv] (head h at column h * 128), log_g and beta fp32
 // [T, ld_g]; chunks: every 64-token chunk of every sequence (row0, len);
 // ws: gdn_ws_bytes(n_chunks, H).
+// Short convolution of the Gated DeltaNet inputs for the T rows of a pass
+// starting at row r0: y = silu(depthwise causal conv of x, width 4, taps w
+// fp32 [C][4]) over C = 3 H 128 channels (q | k | v), q and k L2-normalised
+// per head, q scaled by qscale.  row_seq[T] gives each row's sequence in
+// seqs; rows before a sequence's start come from hist[s_in] (the last three
+// pre-convolution rows of its prefix, bf16 [slots][3][C]) or are zero, and a
+// sequence with s_out >= 0 leaves its own last three rows in hist[s_out].
+hipError_t launch_gdn_conv(const void* x, void* y, int ld, const float* w, int H, int r0, int T,
+                           const int32_t* row_seq, const GdnSeq* seqs, void* hist, float qscale, hipStream_t s);
 hipError_t launch_gdn_scan(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
                            const float* beta, int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
                            const GdnSeq* seqs, int n_seqs, float* states, int H, float* ws, hipStream_t s);

@@ -20,6 +20,8 @@ import prefill_only_decision_amd as s1  # noqa: E402
 MINI = replace(shape_of("4b-single-512"), name="bf16-mini", n_layers=4, d_model=512, ffn=1024,
                vocab=4096, la_heads=4, fa_q_heads=4, fa_kv_heads=2, shape_id=77)
 
+MINI_GDN = replace(MINI, name="bf16-mini-gdn", la_kind="gdn", shape_id=78)
+
 _models = {}
 
 
@@ -68,6 +70,21 @@ def test_bf16_mini_branches():
     b = random_batch(MINI.vocab, [100, 64, 1, 65, 40], seed=9, prefix_of=[-1, 0, 0, 0, -1],
                      questions_per_seq=[0, 2, 1, 2, 1])
     _full_check(MINI, b, "bf16-mini branches")
+
+
+def test_gdn_mini_varlen_ragged():
+    # Gated DeltaNet layers (short convolution, L2-normalised q/k, delta rule)
+    b = random_batch(MINI_GDN.vocab, [300, 1, 130, 64, 257, 2], seed=18, questions_per_seq=[4, 1, 2, 1, 3, 1])
+    _full_check(MINI_GDN, b, "bf16-mini GDN varlen")
+
+
+def test_gdn_mini_branches():
+    # branches continue from the prefix's state and last three pre-convolution
+    # rows; prefixes of 100 and 2 tokens (shorter than the convolution)
+    b = random_batch(MINI_GDN.vocab, [100, 64, 1, 65, 2, 40, 3], seed=19, prefix_of=[-1, 0, 0, 0, -1, 4, 4],
+                     questions_per_seq=[0, 2, 1, 2, 0, 1, 1])
+    _full_check(MINI_GDN, b, "bf16-mini GDN branches")
+    _full_check(MINI_GDN, b, "bf16-mini GDN branches (continuation oracle)", mode="continuation")
 
 
 def test_empty_request():
