@@ -68,6 +68,32 @@ def test_4b_branch_4096x20(gpu_model_4b, oracle_4b, oracle_4b_exact):
                        stack_ref_hidden(rx, capture), label="4b-branch-4096x20")
 
 
+def test_4b_gdn_single_512():
+    """The 4B request with Gated DeltaNet linear-attention layers, every row
+    of every layer against both oracles under the full-depth gates."""
+    import copy
+    require_gpu()
+    import prefill_only_decision_amd as s1
+    shape = shape_of("4b-gdn-single-512")
+    b = make_batch("4b-gdn-single-512")
+    w = make_weights(shape)
+    cfg = s1.make_config(shape, max_tokens=1024, max_seqs=4, max_questions=16, max_options=64,
+                         max_prefixes=1, max_positions=1024)
+    model = s1.Model(cfg, w.tensors)
+    capture = {0: np.arange(512)}
+    probs, dec, hid = run_gpu(model, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
+    model.free()
+    om = O.OracleModel(shape, w.tensors, dtype=np.float32, keep_decoded=True, act="bf16")
+    t0 = time.time()
+    ref = O.prefill_decide(om, b, capture=capture)
+    log(f"oracle 4b-gdn-single-512: {time.time() - t0:.1f} s")
+    ox = copy.copy(om)
+    ox.act = "exact"
+    rx = O.prefill_decide(ox, b, capture=capture)
+    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
+                       stack_ref_hidden(rx, capture), label="4b-gdn-single-512")
+
+
 @pytest.mark.slow
 def test_27b_single_1024():
     require_gpu()
