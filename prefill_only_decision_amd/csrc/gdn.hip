@@ -118,12 +118,31 @@ gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int 
   for (int t = 0; t < C; ++t) out[t * XW + j] = x[t];
 }
 
-// Split eight floats, negated, into hi + lo bf16 operands.
+// Conversions with the packed hardware instruction (v_cvt_pk_bf16_f32,
+// round to nearest even, as f2bf for finite values).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const float2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+// v = hi + lo with hi = rne(v), lo = rne(v - hi).
+__device__ __forceinline__ void split8(const float* v, bf16x8& h, bf16x8& l) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hw[e] = cvt2(v[2 * e], v[2 * e + 1]);
+    lw[e] = cvt2(v[2 * e] - __uint_as_float(hw[e] << 16), v[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+  }
+  h = as_frag(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  l = as_frag(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
+// The same for the negated values.
 __device__ __forceinline__ void split_neg(const float* v, bf16x8& h, bf16x8& l) {
   float nv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) nv[e] = -v[e];
-  split_frag(nv, h, l);
+  split8(nv, h, l);
 }
 
 // ------------------------------------------------------------------ scan
@@ -199,11 +218,13 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
         const int d0 = q8 * 8 + 2 * e;
         const float x00 = __uint_as_float(av[e] << 16) * w0, x01 = __uint_as_float(bv[e] << 16) * w1;
         const float x10 = __uint_as_float(av[e] & 0xFFFF0000u) * w0, x11 = __uint_as_float(bv[e] & 0xFFFF0000u) * w1;
-        const bf16_t h00 = f2bf(x00), h01 = f2bf(x01), h10 = f2bf(x10), h11 = f2bf(x11);
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h00 | ((uint32_t)h01 << 16);
-        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h10 | ((uint32_t)h11 << 16);
-        *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) = pack_bf2(x00 - bf2f(h00), x01 - bf2f(h01));
-        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) = pack_bf2(x10 - bf2f(h10), x11 - bf2f(h11));
+        const uint32_t h0 = cvt2(x00, x01), h1 = cvt2(x10, x11);
+        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h0;
+        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h1;
+        *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) =
+            cvt2(x00 - __uint_as_float(h0 << 16), x01 - __uint_as_float(h0 & 0xFFFF0000u));
+        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) =
+            cvt2(x10 - __uint_as_float(h1 << 16), x11 - __uint_as_float(h1 & 0xFFFF0000u));
       }
     }
     __syncthreads();
@@ -217,7 +238,7 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
         float sv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) sv[e] = S[a][8 * hf + e];
-        split_frag(sv, shi[a][hf], slo[a][hf]);
+        split8(sv, shi[a][hf], slo[a][hf]);
       }
 
     // (1) U = Ut - W S0 for both token tiles
@@ -275,7 +296,7 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
         float uv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) uv[e] = U[st][8 * hf + e];
-        split_frag(uv, uhi[st][hf], ulo[st][hf]);
+        split8(uv, uhi[st][hf], ulo[st][hf]);
       }
 
     // (3) O = (A . D) U + exp(G_t) Q S0
@@ -308,7 +329,7 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
 #pragma unroll
         for (int e = 0; e < 8; ++e) av[e] = At[x][8 * hf + e];
         bf16x8 ahi, alo;
-        split_frag(av, ahi, alo);
+        split8(av, ahi, alo);
         mfma32(O1[tt], ahi, uhi[st][hf]);
         mfma32(O1[tt], ahi, ulo[st][hf]);
         mfma32(O1[tt], alo, uhi[st][hf]);
