@@ -106,12 +106,18 @@ gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int 
     }
     x[t] = r;
   }
+  // four partial sums per row shorten the dependent chain
 #pragma unroll
   for (int t = 1; t < C; ++t) {
-    float acc = x[t];
+    float a0 = x[t], a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < t; ++i) acc -= sL[t][i] * x[i];
-    x[t] = acc;
+    for (int i = 0; i < t; i += 4) {
+      a0 -= sL[t][i] * x[i];
+      if (i + 1 < t) a1 -= sL[t][i + 1] * x[i + 1];
+      if (i + 2 < t) a2 -= sL[t][i + 2] * x[i + 2];
+      if (i + 3 < t) a3 -= sL[t][i + 3] * x[i + 3];
+    }
+    x[t] = (a0 + a1) + (a2 + a3);
   }
   float* out = wu + ((long long)ch * H + h) * C * XW;
 #pragma unroll
@@ -378,21 +384,32 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
 }
 
 // ----------------------------------------------------------- convolution
-// One workgroup per row; thread t handles the 8-channel groups t, t + 256,
-// ...; the 16 groups of one head are 16 consecutive threads, which reduce
-// the head's sum of squares among themselves.
+// Grid (channel blocks of 256 eight-channel groups, row blocks of CONV_ROWS
+// rows of the pass). Thread t of channel block b handles group 256 b + t for
+// the block's rows, with the group's taps held in registers; the 16 groups of
+// one head are 16 consecutive threads, which reduce the head's sum of squares
+// among themselves.
+constexpr int CONV_ROWS = 4;
+
 __global__ void __launch_bounds__(256)
 gdn_conv_kernel(const bf16_t* __restrict__ x, bf16_t* __restrict__ y, int ld, const float* __restrict__ w,
-                int H, int r0, const int32_t* __restrict__ row_seq, const GdnSeq* __restrict__ seqs,
+                int H, int r0, int T, const int32_t* __restrict__ row_seq, const GdnSeq* __restrict__ seqs,
                 bf16_t* __restrict__ hist, float qscale) {
   const int Cc = 3 * H * DK, NG = Cc / 8, QKG = 2 * H * DK / 8;
-  const int r = r0 + blockIdx.x;
-  const GdnSeq sq = seqs[row_seq[blockIdx.x]];
-  const int t = r - sq.row0;
-  for (int g0 = 0; g0 < NG; g0 += 256) {
-    const int g = g0 + (int)threadIdx.x;
-    if (g0 + ((int)threadIdx.x & ~15) >= NG) continue;   // whole 16-thread group beyond the channels
-    const int c0 = 8 * g;
+  const int g = blockIdx.x * 256 + (int)threadIdx.x;
+  if (g >= NG) return;              // NG is a multiple of 16: whole 16-thread head groups leave together
+  const int c0 = 8 * g;
+  float4 tap[8];                    // taps of channels c0 .. c0 + 7
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tap[e] = *reinterpret_cast<const float4*>(w + (long long)(c0 + e) * 4);
+  const bool qk = g < QKG;
+  const float nscale = g < QKG / 2 ? qscale : 1.f;
+  for (int rr = 0; rr < CONV_ROWS; ++rr) {
+    const int pr = blockIdx.y * CONV_ROWS + rr;     // row within the pass
+    if (pr >= T) break;
+    const int r = r0 + pr;
+    const GdnSeq sq = seqs[row_seq[pr]];
+    const int t = r - sq.row0;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -407,10 +424,9 @@ gdn_conv_kernel(const bf16_t* __restrict__ x, bf16_t* __restrict__ y, int ld, co
       const uint32_t uv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float4 w0 = *reinterpret_cast<const float4*>(w + (long long)(c0 + 2 * e) * 4);
-        const float4 w1 = *reinterpret_cast<const float4*>(w + (long long)(c0 + 2 * e + 1) * 4);
-        const float wa = j == 0 ? w0.x : j == 1 ? w0.y : j == 2 ? w0.z : w0.w;
-        const float wb = j == 0 ? w1.x : j == 1 ? w1.y : j == 2 ? w1.z : w1.w;
+        const float4 ta = tap[2 * e], tb = tap[2 * e + 1];
+        const float wa = j == 0 ? ta.x : j == 1 ? ta.y : j == 2 ? ta.z : ta.w;
+        const float wb = j == 0 ? tb.x : j == 1 ? tb.y : j == 2 ? tb.z : tb.w;
         acc[2 * e] += wa * __uint_as_float(uv[e] << 16);
         acc[2 * e + 1] += wb * __uint_as_float(uv[e] & 0xFFFF0000u);
       }
@@ -421,30 +437,28 @@ gdn_conv_kernel(const bf16_t* __restrict__ x, bf16_t* __restrict__ y, int ld, co
       acc[e] = acc[e] / (1.f + __expf(-acc[e]));
       ss += acc[e] * acc[e];
     }
-    if (g0 + ((int)threadIdx.x & ~15) < QKG) {       // q or k: L2 norm over the head's 16 groups
+    if (qk) {                       // q or k: L2 norm over the head's 16 groups
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 64);
-      const float sc = rsqrtf(ss + 1e-6f) * (g < QKG / 2 ? qscale : 1.f);
+      const float sc = rsqrtf(ss + 1e-6f) * nscale;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= sc;
     }
-    if (g < NG) {
-      uint4 o;
-      o.x = pack_bf2(acc[0], acc[1]);
-      o.y = pack_bf2(acc[2], acc[3]);
-      o.z = pack_bf2(acc[4], acc[5]);
-      o.w = pack_bf2(acc[6], acc[7]);
-      *reinterpret_cast<uint4*>(y + (long long)r * ld + c0) = o;
-      if (sq.s_out >= 0) {
-        // the sequence's last three pre-convolution rows (zeros before its start)
-        const int i = t - (sq.len - 3);
-        if (i >= 0)
-          *reinterpret_cast<uint4*>(hist + ((long long)sq.s_out * 3 + i) * Cc + c0) =
-              *reinterpret_cast<const uint4*>(x + (long long)r * ld + c0);
-        if (t == 0)
-          for (int z = 0; z < 3 - sq.len; ++z)
-            *reinterpret_cast<uint4*>(hist + ((long long)sq.s_out * 3 + z) * Cc + c0) = make_uint4(0, 0, 0, 0);
-      }
+    uint4 o;
+    o.x = pack_bf2(acc[0], acc[1]);
+    o.y = pack_bf2(acc[2], acc[3]);
+    o.z = pack_bf2(acc[4], acc[5]);
+    o.w = pack_bf2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(y + (long long)r * ld + c0) = o;
+    if (sq.s_out >= 0) {
+      // the sequence's last three pre-convolution rows (zeros before its start)
+      const int hrow = t - (sq.len - 3);
+      if (hrow >= 0)
+        *reinterpret_cast<uint4*>(hist + ((long long)sq.s_out * 3 + hrow) * Cc + c0) =
+            *reinterpret_cast<const uint4*>(x + (long long)r * ld + c0);
+      if (t == 0)
+        for (int z = 0; z < 3 - sq.len; ++z)
+          *reinterpret_cast<uint4*>(hist + ((long long)sq.s_out * 3 + z) * Cc + c0) = make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -454,9 +468,10 @@ gdn_conv_kernel(const bf16_t* __restrict__ x, bf16_t* __restrict__ y, int ld, co
 hipError_t launch_gdn_conv(const void* x, void* y, int ld, const float* w, int H, int r0, int T,
                            const int32_t* row_seq, const GdnSeq* seqs, void* hist, float qscale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gdn_conv_kernel, dim3(T), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(x),
-                     reinterpret_cast<bf16_t*>(y), ld, w, H, r0, row_seq, seqs, reinterpret_cast<bf16_t*>(hist),
-                     qscale);
+  const int NG = 3 * H * DK / 8;
+  hipLaunchKernelGGL(gdn_conv_kernel, dim3((NG + 255) / 256, (T + CONV_ROWS - 1) / CONV_ROWS), dim3(256), 0, s,
+                     reinterpret_cast<const bf16_t*>(x), reinterpret_cast<bf16_t*>(y), ld, w, H, r0, T, row_seq,
+                     seqs, reinterpret_cast<bf16_t*>(hist), qscale);
   return hipGetLastError();
 }
 
