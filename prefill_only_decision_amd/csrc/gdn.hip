@@ -61,11 +61,20 @@ gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int 
     sG[lane] = G;
     sB[lane] = lane < n ? beta[(base + lane) * ldg + h] : 0.f;
   }
-  for (int c = tid; c < C * 16; c += 256) {
-    const int s = c >> 4, q8 = c & 15;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (s < n) val = *reinterpret_cast<const uint4*>(k + (base + s) * ldqkv + h * DK + q8 * 8);
-    *reinterpret_cast<uint4*>(sK + s * QP + q8 * 16) = val;
+  // rows past the chunk's end are loaded from its last row (in bounds) and
+  // replaced by zeros: the loads carry no branch and issue back to back
+  {
+    uint4 kv[C * 16 / 256];
+#pragma unroll
+    for (int i = 0; i < C * 16 / 256; ++i) {
+      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
+      kv[i] = *reinterpret_cast<const uint4*>(k + (base + min(s, n - 1)) * ldqkv + h * DK + q8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C * 16 / 256; ++i) {
+      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
+      *reinterpret_cast<uint4*>(sK + s * QP + q8 * 16) = s < n ? kv[i] : make_uint4(0, 0, 0, 0);
+    }
   }
   __syncthreads();
   // K K^T: wave w computes the 32 x 32 tile (w / 2, w % 2); exact products
@@ -94,17 +103,17 @@ gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int 
   //   rhs_t = beta_t gamma_t k_t[j] (j < DK), beta_t v_t[j - DK] (j >= DK)
   const int j = tid;
   float x[C];
+  if (j < DK) {
 #pragma unroll
-  for (int t = 0; t < C; ++t) {
-    float r = 0.f;
-    if (t < n) {
-      if (j < DK) {
-        r = sB[t] * __expf(sG[t]) * bf2f(*reinterpret_cast<const bf16_t*>(sK + t * QP + 2 * j));
-      } else {
-        r = sB[t] * bf2f(v[(base + t) * ldqkv + (long long)h * DV + (j - DK)]);
-      }
-    }
-    x[t] = r;
+    for (int t = 0; t < C; ++t)
+      x[t] = sB[t] * __expf(sG[t]) * bf2f(*reinterpret_cast<const bf16_t*>(sK + t * QP + 2 * j));
+  } else {
+    // sB is zero past the chunk's end; those rows read the last row in bounds
+    const bf16_t* vc = v + base * ldqkv + (long long)h * DV + (j - DK);
+#pragma unroll
+    for (int t = 0; t < C; ++t) x[t] = bf2f(vc[(long long)min(t, n - 1) * ldqkv]);
+#pragma unroll
+    for (int t = 0; t < C; ++t) x[t] *= sB[t];
   }
   // four partial sums per row shorten the dependent chain
 #pragma unroll
@@ -200,21 +209,41 @@ gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int 
 
     __syncthreads();
     if (wave == 0) sG[lane] = G;
-    for (int c = tid; c < C * 16; c += 256) {
-      const int s = c >> 4, q8 = c & 15;
-      uint4 qv = make_uint4(0, 0, 0, 0);
-      if (s < n) qv = *reinterpret_cast<const uint4*>(q + (base + s) * ldqkv + h * DK + q8 * 8);
-      *reinterpret_cast<uint4*>(sQ + s * QP + q8 * 16) = qv;
+    // every global load of the chunk first (rows past its end read its last
+    // row, in bounds, and are replaced by zeros), then the LDS stores
+    uint4 qv[C * 16 / 256], kav[C * 8 / 256], kbv[C * 8 / 256];
+    float4 wv4[C * (DK / 4) / 256];
+#pragma unroll
+    for (int i = 0; i < C * 16 / 256; ++i) {
+      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
+      qv[i] = *reinterpret_cast<const uint4*>(q + (base + min(s, n - 1)) * ldqkv + h * DK + q8 * 8);
     }
-    for (int c = tid; c < C * (DK / 4); c += 256) {
-      const int t = c / (DK / 4), q4 = c % (DK / 4);
-      *reinterpret_cast<float4*>(sW + t * WP + q4 * 16) = *reinterpret_cast<const float4*>(X + t * XW + 4 * q4);
+#pragma unroll
+    for (int i = 0; i < C * 8 / 256; ++i) {
+      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15;
+      kav[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p, n - 1)) * ldqkv + h * DK + q8 * 8);
+      kbv[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p + 1, n - 1)) * ldqkv + h * DK + q8 * 8);
     }
-    for (int c = tid; c < (C / 2) * 16; c += 256) {
-      const int p = c >> 4, q8 = c & 15, s0 = 2 * p, s1 = s0 + 1;
-      uint4 ka = make_uint4(0, 0, 0, 0), kb = make_uint4(0, 0, 0, 0);
-      if (s0 < n) ka = *reinterpret_cast<const uint4*>(k + (base + s0) * ldqkv + h * DK + q8 * 8);
-      if (s1 < n) kb = *reinterpret_cast<const uint4*>(k + (base + s1) * ldqkv + h * DK + q8 * 8);
+#pragma unroll
+    for (int i = 0; i < C * (DK / 4) / 256; ++i) {
+      const int c = tid + 256 * i, t = c / (DK / 4), q4 = c % (DK / 4);
+      wv4[i] = *reinterpret_cast<const float4*>(X + t * XW + 4 * q4);
+    }
+#pragma unroll
+    for (int i = 0; i < C * 16 / 256; ++i) {
+      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
+      *reinterpret_cast<uint4*>(sQ + s * QP + q8 * 16) = s < n ? qv[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C * (DK / 4) / 256; ++i) {
+      const int c = tid + 256 * i, t = c / (DK / 4), q4 = c % (DK / 4);
+      *reinterpret_cast<float4*>(sW + t * WP + q4 * 16) = wv4[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C * 8 / 256; ++i) {
+      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15, s0 = 2 * p, s1 = s0 + 1;
+      const uint4 ka = s0 < n ? kav[i] : make_uint4(0, 0, 0, 0);
+      const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(sK + s0 * QP + q8 * 16) = ka;
       *reinterpret_cast<uint4*>(sK + s1 * QP + q8 * 16) = kb;
       const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
