@@ -10,20 +10,24 @@
 // from S0, with gamma_t = prod_{j<=t} g_j (chunk-local),
 //   (I + L) U = diag(beta) V - diag(beta gamma) K S0,
 //       L[t][i] = beta_t (gamma_t / gamma_i) k_t . k_i  (i < t),
-//   O  = diag(gamma) Q S0 + (Q K^T . M) U,   M[t][i] = gamma_t / gamma_i (i <= t),
-//   S' = gamma_C S0 + (K . gamma_C / gamma)^T U.
-// U = Ut - W S0 with W = (I + L)^-1 diag(beta gamma) K and
-// Ut = (I + L)^-1 diag(beta) V, which do not depend on S0:
-//   gdn_prep_kernel   every (chunk, head) in parallel: K K^T on MFMA, L, and
-//                     W | Ut by forward substitution (one column per thread);
-//   gdn_scan_kernel   every (sequence, head) in order over its chunks: the
-//                     state stays in accumulator registers; U, O and S' on
-//                     MFMA.
-// Operands formed inside the kernels (W, U, decayed scores, the state,
-// decayed keys) are fp32 values split into bf16 hi + lo parts; products of
-// two such operands take three MFMAs (hi.hi + hi.lo + lo.hi), products with
-// a bf16 input two, so the kernels add little beyond fp32 rounding to their
-// bf16 q, k, v.
+//   O  = diag(gamma) Q S0 + A U,   A[t][i] = (gamma_t / gamma_i) q_t . k_i (i <= t),
+//   S' = gamma_C S0 + Kd^T U,      Kd = K . gamma_C / gamma.
+// With W = (I + L)^-1 diag(beta gamma) K and Ut = (I + L)^-1 diag(beta) V,
+// U = Ut - W S0, so every chunk is an affine map of its initial state:
+//   S' = M S0 + B,      M = gamma_C I - Kd^T W,          B = Kd^T Ut,
+//   O  = Qt S0 + Ol,    Qt = diag(gamma) Q - A W,        Ol = A Ut.
+//   gdn_chunk_kernel  every (chunk, head) in parallel: L and A on MFMA, W | Ut
+//                     by forward substitution (one column per thread), then M,
+//                     B, Qt and Ol on MFMA, written in the register layouts
+//                     the state kernel consumes;
+//   gdn_state_kernel  every (sequence, head, 32 value columns) in order over
+//                     its chunks: the state stays in accumulator registers,
+//                     O = Qt S + Ol and S <- M S + B, two MFMA products per
+//                     chunk and no other arithmetic.
+// Operands formed inside the kernels (W, Ut, A, decayed keys, M, Qt, the
+// state) are fp32 values split into bf16 hi + lo parts; products of two such
+// operands take three MFMAs (hi.hi + hi.lo + lo.hi), so the kernels add
+// little beyond fp32 rounding to their bf16 q, k, v.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,73 +35,165 @@ namespace s1 {
 namespace {
 
 constexpr int C = 64, DK = 128, DV = 128;
-constexpr int QP = DK * 2 + 16;    // bytes per Q / K row in LDS
-constexpr int TP = C * 2 + 16;     // bytes per decayed K^T row (hi or lo) in LDS
-constexpr int WP = DK * 4 + 16;    // bytes per W row (fp32) in LDS
-constexpr int XW = DK + DV;        // columns of W | Ut
+constexpr int QP = DK * 2 + 16;    // bytes per Q / K row in LDS (bf16)
+constexpr int LP = C + 4;          // floats per L row in LDS
+constexpr int RP = C * 2 + 16;     // bytes per row of a [.][C] bf16 operand in LDS
+// Workspace of one (chunk, head), in 16-byte units:
+//   M   A operands of M S: [row tile 4][k tile 4][half 2][hi, lo][lane 64]
+//   B   accumulator tiles of B: [row tile 4][value tile 4][lane 64][16 floats]
+//   Qt  A operands of Qt S: [token tile 2][k tile 4][half 2][hi, lo][lane 64]
+//   Ol  accumulator tiles of Ol: [token tile 2][value tile 4][lane 64][16 floats]
+constexpr int WS_M = 4 * 4 * 2 * 2 * 64, WS_B = 4 * 4 * 64 * 4, WS_Q = 2 * 4 * 2 * 2 * 64, WS_O = 2 * 4 * 64 * 4;
+constexpr int WS_CH = WS_M + WS_B + WS_Q + WS_O;
 
-// -------------------------------------------------------------- prepare
-// One workgroup (4 waves) per (chunk, head).  X = W | Ut, [C][XW] fp32.
+// Conversions with the packed hardware instruction (v_cvt_pk_bf16_f32,
+// round to nearest even, as f2bf for finite values).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const float2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+__device__ __forceinline__ float lo_half(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_half(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// v = hi + lo with hi = rne(v), lo = rne(v - hi), as two 16-byte operands.
+__device__ __forceinline__ void split8(const float* v, uint4& h, uint4& l) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hw[e] = cvt2(v[2 * e], v[2 * e + 1]);
+    lw[e] = cvt2(v[2 * e] - lo_half(hw[e]), v[2 * e + 1] - hi_half(hw[e]));
+  }
+  h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  l = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+__device__ __forceinline__ bf16x8 lds16(const char* p) { return as_frag(*reinterpret_cast<const uint4*>(p)); }
+// c += a b in split precision (hi.hi + hi.lo + lo.hi)
+__device__ __forceinline__ void mfma3(floatx16& c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+  mfma32(c, ah, bh);
+  mfma32(c, ah, bl);
+  mfma32(c, al, bh);
+}
+
+// ---------------------------------------------------------------- chunk
+// One workgroup (4 waves) per (chunk, head).
 __global__ void __launch_bounds__(256)
-gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int ldqkv,
-                const float* __restrict__ lg, const float* __restrict__ beta, int ldg,
-                const ScanSeq* __restrict__ chunks, float* __restrict__ wu, int H) {
-  __shared__ __attribute__((aligned(16))) char sK[C * QP];
-  __shared__ float sL[C][C + 1];
+gdn_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                 int ldqkv, const float* __restrict__ lg, const float* __restrict__ beta, int ldg,
+                 const ScanSeq* __restrict__ chunks, uint4* __restrict__ ws, int H) {
+  __shared__ __attribute__((aligned(16))) char sQ[C * QP];
+  // K and L first; after the solve, the rows of W^T | Ut^T (hi, then lo)
+  __shared__ __attribute__((aligned(16))) char sR[2 * (DK + DV) * RP];
+  __shared__ __attribute__((aligned(16))) char sA[2 * C * RP];     // A [t][i], hi then lo
+  __shared__ __attribute__((aligned(16))) char sKT[2 * DK * RP];   // Kd^T [d][t], hi then lo
   __shared__ float sG[C], sB[C];
+  char* const sK = sR;
+  float* const sL = reinterpret_cast<float*>(sR + C * QP);
+  char* const sXh = sR;
+  char* const sXl = sR + (DK + DV) * RP;
+  char* const sAh = sA;
+  char* const sAl = sA + C * RP;
+  char* const sKh = sKT;
+  char* const sKl = sKT + DK * RP;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, cl = lane & 31;
   const int ch = blockIdx.x, h = blockIdx.y;
   const ScanSeq cq = chunks[ch];
   const int n = cq.len;
   const long long base = cq.row0;
-  if (wave == 0) {
-    float G = lane < n ? lg[(base + lane) * ldg + h] : 0.f;
+
+  // every wave: cumulative log gate, lane = token (zero increments past the end)
+  float G = lane < n ? lg[(base + lane) * ldg + h] : 0.f;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_up(G, off, 64);
-      if (lane >= off) G += t;
-    }
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(G, off, 64);
+    if (lane >= off) G += t;
+  }
+  const float Glast = __shfl(G, 63, 64);
+  const float wK = __expf(Glast - G);
+  if (wave == 0) {
     sG[lane] = G;
     sB[lane] = lane < n ? beta[(base + lane) * ldg + h] : 0.f;
   }
-  // rows past the chunk's end are loaded from its last row (in bounds) and
-  // replaced by zeros: the loads carry no branch and issue back to back
+  // Q and K rows (rows past the end read the last row, in bounds, and are
+  // replaced by zeros), and the decayed keys transposed, hi / lo
   {
-    uint4 kv[C * 16 / 256];
+    uint4 qv[C * 16 / 256], kav[C * 8 / 256], kbv[C * 8 / 256];
 #pragma unroll
     for (int i = 0; i < C * 16 / 256; ++i) {
       const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
-      kv[i] = *reinterpret_cast<const uint4*>(k + (base + min(s, n - 1)) * ldqkv + h * DK + q8 * 8);
+      qv[i] = *reinterpret_cast<const uint4*>(q + (base + min(s, n - 1)) * ldqkv + h * DK + q8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < C * 8 / 256; ++i) {
+      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15;
+      kav[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p, n - 1)) * ldqkv + h * DK + q8 * 8);
+      kbv[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p + 1, n - 1)) * ldqkv + h * DK + q8 * 8);
     }
 #pragma unroll
     for (int i = 0; i < C * 16 / 256; ++i) {
       const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
-      *reinterpret_cast<uint4*>(sK + s * QP + q8 * 16) = s < n ? kv[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sQ + s * QP + q8 * 16) = s < n ? qv[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C * 8 / 256; ++i) {
+      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15, s0 = 2 * p, s1 = s0 + 1;
+      const uint4 ka = s0 < n ? kav[i] : make_uint4(0, 0, 0, 0);
+      const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sK + s0 * QP + q8 * 16) = ka;
+      *reinterpret_cast<uint4*>(sK + s1 * QP + q8 * 16) = kb;
+      const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
+      const uint32_t av[4] = {ka.x, ka.y, ka.z, ka.w}, bv[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d0 = q8 * 8 + 2 * e;
+        const float x00 = lo_half(av[e]) * w0, x01 = lo_half(bv[e]) * w1;
+        const float x10 = hi_half(av[e]) * w0, x11 = hi_half(bv[e]) * w1;
+        const uint32_t h0 = cvt2(x00, x01), h1 = cvt2(x10, x11);
+        *reinterpret_cast<uint32_t*>(sKh + d0 * RP + 4 * p) = h0;
+        *reinterpret_cast<uint32_t*>(sKh + (d0 + 1) * RP + 4 * p) = h1;
+        *reinterpret_cast<uint32_t*>(sKl + d0 * RP + 4 * p) = cvt2(x00 - lo_half(h0), x01 - hi_half(h0));
+        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * RP + 4 * p) = cvt2(x10 - lo_half(h1), x11 - hi_half(h1));
+      }
     }
   }
   __syncthreads();
-  // K K^T: wave w computes the 32 x 32 tile (w / 2, w % 2); exact products
-  // of bf16 inputs, fp32 accumulation
+
+  // K K^T and Q K^T: wave w takes the 32 x 32 tile (w / 2, w % 2) of both;
+  // exact products of bf16 inputs, fp32 accumulation
   {
     const int ti = wave >> 1, tj = wave & 1;
-    floatx16 acc;
+    floatx16 accL, accA;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const char* ar = sK + (32 * ti + cl) * QP + 16 * hi;
+    for (int r = 0; r < 16; ++r) {
+      accL[r] = 0.f;
+      accA[r] = 0.f;
+    }
+    const char* kr = sK + (32 * ti + cl) * QP + 16 * hi;
+    const char* qr = sQ + (32 * ti + cl) * QP + 16 * hi;
     const char* br = sK + (32 * tj + cl) * QP + 16 * hi;
 #pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks)
-      mfma32(acc, as_frag(*reinterpret_cast<const uint4*>(ar + 32 * ks)),
-             as_frag(*reinterpret_cast<const uint4*>(br + 32 * ks)));
-    // acc[r] = (K K^T)[32 ti + acc_row(r)][32 tj + cl]: L[t][i], t = row, i = column
+    for (int ks = 0; ks < DK / 16; ++ks) {
+      const bf16x8 bf = lds16(br + 32 * ks);
+      mfma32(accL, lds16(kr + 32 * ks), bf);
+      if (tj <= ti) mfma32(accA, lds16(qr + 32 * ks), bf);
+    }
+    // acc[r] = X[32 ti + acc_row(r)][32 tj + cl]: row t, column i
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * ti + acc_row(r, lane), i = 32 * tj + cl;
-      sL[t][i] = i < t ? sB[t] * __expf(sG[t] - sG[i]) * acc[r] : 0.f;
+      const float dcy = __expf(sG[t] - sG[i]);
+      sL[t * LP + i] = i < t ? sB[t] * dcy * accL[r] : 0.f;
+      const float a = i <= t ? dcy * accA[r] : 0.f;
+      const uint32_t ah = cvt2(a, 0.f);
+      const uint32_t al = cvt2(a - lo_half(ah), 0.f);
+      *reinterpret_cast<bf16_t*>(sAh + t * RP + 2 * i) = (bf16_t)(ah & 0xFFFFu);
+      *reinterpret_cast<bf16_t*>(sAl + t * RP + 2 * i) = (bf16_t)(al & 0xFFFFu);
     }
   }
   __syncthreads();
+
   // forward substitution, one column j of W | Ut per thread:
   //   X_t = rhs_t - sum_{i<t} L[t][i] X_i,
   //   rhs_t = beta_t gamma_t k_t[j] (j < DK), beta_t v_t[j - DK] (j >= DK)
@@ -121,294 +217,238 @@ gdn_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, int 
     float a0 = x[t], a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int i = 0; i < t; i += 4) {
-      a0 -= sL[t][i] * x[i];
-      if (i + 1 < t) a1 -= sL[t][i + 1] * x[i + 1];
-      if (i + 2 < t) a2 -= sL[t][i + 2] * x[i + 2];
-      if (i + 3 < t) a3 -= sL[t][i + 3] * x[i + 3];
+      a0 -= sL[t * LP + i] * x[i];
+      if (i + 1 < t) a1 -= sL[t * LP + i + 1] * x[i + 1];
+      if (i + 2 < t) a2 -= sL[t * LP + i + 2] * x[i + 2];
+      if (i + 3 < t) a3 -= sL[t * LP + i + 3] * x[i + 3];
     }
     x[t] = (a0 + a1) + (a2 + a3);
   }
-  float* out = wu + ((long long)ch * H + h) * C * XW;
+  __syncthreads();   // K and L are no longer read: their space takes W^T | Ut^T
 #pragma unroll
-  for (int t = 0; t < C; ++t) out[t * XW + j] = x[t];
-}
-
-// Conversions with the packed hardware instruction (v_cvt_pk_bf16_f32,
-// round to nearest even, as f2bf for finite values).
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-  const float2v f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-}
-// v = hi + lo with hi = rne(v), lo = rne(v - hi).
-__device__ __forceinline__ void split8(const float* v, bf16x8& h, bf16x8& l) {
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    hw[e] = cvt2(v[2 * e], v[2 * e + 1]);
-    lw[e] = cvt2(v[2 * e] - __uint_as_float(hw[e] << 16), v[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
+  for (int t8 = 0; t8 < C / 8; ++t8) {
+    uint4 xh, xl;
+    split8(x + 8 * t8, xh, xl);
+    *reinterpret_cast<uint4*>(sXh + j * RP + 16 * t8) = xh;
+    *reinterpret_cast<uint4*>(sXl + j * RP + 16 * t8) = xl;
   }
-  h = as_frag(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-  l = as_frag(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-}
-// The same for the negated values.
-__device__ __forceinline__ void split_neg(const float* v, bf16x8& h, bf16x8& l) {
-  float nv[8];
+  __syncthreads();
+
+  uint4* const wsc = ws + ((long long)ch * H + h) * WS_CH;
+  const float gC = __expf(Glast);
+  // M^T = gamma_C I - W^T Kd (tiles (wave, ti)) and P = W^T A^T (tiles
+  // (wave, tt)); the accumulator of M^T tile (j, i) holds, per lane, the A
+  // operand of M S for row tile i, k tile j, which is how it is stored
+  {
+    floatx16 accM[4], accP[2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) nv[e] = -v[e];
-  split8(nv, h, l);
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) accM[u][r] = 0.f;
+      accP[0][r] = 0.f;
+      accP[1][r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+      const int off = 32 * ks + 16 * hi;
+      const int wr = (32 * wave + cl) * RP + off;
+      const bf16x8 wh = lds16(sXh + wr), wl = lds16(sXl + wr);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const int kr = (32 * ti + cl) * RP + off;
+        mfma3(accM[ti], wh, wl, lds16(sKh + kr), lds16(sKl + kr));
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int ar = (32 * tt + cl) * RP + off;
+        mfma3(accP[tt], wh, wl, lds16(sAh + ar), lds16(sAl + ar));
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float mv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = 32 * wave + acc_row(8 * hf + e, lane), ii = 32 * ti + cl;
+          mv[e] = (jj == ii ? gC : 0.f) - accM[ti][8 * hf + e];
+        }
+        uint4 mh, ml;
+        split8(mv, mh, ml);
+        uint4* dst = wsc + (((ti * 4 + wave) * 2 + hf) * 2) * 64 + lane;
+        dst[0] = mh;
+        dst[64] = ml;
+      }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float qv[8];
+        const int t = 32 * tt + cl;
+        const float gt = __expf(sG[t]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = 32 * wave + acc_row(8 * hf + e, lane);
+          qv[e] = gt * bf2f(*reinterpret_cast<const bf16_t*>(sQ + t * QP + 2 * jj)) - accP[tt][8 * hf + e];
+        }
+        uint4 qh, ql;
+        split8(qv, qh, ql);
+        uint4* dst = wsc + WS_M + WS_B + (((tt * 4 + wave) * 2 + hf) * 2) * 64 + lane;
+        dst[0] = qh;
+        dst[64] = ql;
+      }
+  }
+  // B = Kd^T Ut (tiles (wave, value tile)) and Ol = A Ut (tiles (wave / 2,
+  // value tiles 2 (wave % 2) + 0, 1)), stored as accumulator tiles
+  {
+    floatx16 accB[4], accO[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) accB[u][r] = 0.f;
+      accO[0][r] = 0.f;
+      accO[1][r] = 0.f;
+    }
+    const int tt = wave >> 1;
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+      const int off = 32 * ks + 16 * hi;
+      const int kr = (32 * wave + cl) * RP + off, ar = (32 * tt + cl) * RP + off;
+      const bf16x8 kh = lds16(sKh + kr), kl = lds16(sKl + kr);
+      const bf16x8 ah = lds16(sAh + ar), al = lds16(sAl + ar);
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) {
+        const int ur = (DK + 32 * vt + cl) * RP + off;
+        const bf16x8 uh = lds16(sXh + ur), ul = lds16(sXl + ur);
+        mfma3(accB[vt], kh, kl, uh, ul);
+        if ((vt >> 1) == (wave & 1)) mfma3(accO[vt & 1], ah, al, uh, ul);
+      }
+    }
+    float4* const wB = reinterpret_cast<float4*>(wsc + WS_M);
+    float4* const wO = reinterpret_cast<float4*>(wsc + WS_M + WS_B + WS_Q);
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        wB[((wave * 4 + vt) * 64 + lane) * 4 + f] =
+            make_float4(accB[vt][4 * f], accB[vt][4 * f + 1], accB[vt][4 * f + 2], accB[vt][4 * f + 3]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        wO[((tt * 4 + 2 * (wave & 1) + u) * 64 + lane) * 4 + f] =
+            make_float4(accO[u][4 * f], accO[u][4 * f + 1], accO[u][4 * f + 2], accO[u][4 * f + 3]);
+  }
 }
 
-// ------------------------------------------------------------------ scan
-// One workgroup of 4 waves per (sequence, head); wave w owns value columns
-// 32 w .. 32 w + 31.  The state accumulator S[a][r] = S[32 a + acc_row(r)][32 w
-// + cl] is the B operand of Q S0 and W S0 with the contraction index permuted
-// as acc_row (Q and W are read with that permutation); U's accumulator
-// layout U[tt][r] = U[32 tt + acc_row(r)][32 w + cl] is likewise the B
-// operand of the token contractions (scores and decayed K^T are read with
-// the permutation).
-__global__ void __launch_bounds__(256)
-gdn_scan_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, int ldqkv,
-                const float* __restrict__ lg, int ldg, const float* __restrict__ wu,
-                bf16_t* __restrict__ o, int ldo, const GdnSeq* __restrict__ seqs,
-                float* __restrict__ states, int H) {
-  __shared__ __attribute__((aligned(16))) char sQ[C * QP];
-  __shared__ __attribute__((aligned(16))) char sK[C * QP];
-  __shared__ __attribute__((aligned(16))) char sKt[DK * TP];   // decayed K^T, hi
-  __shared__ __attribute__((aligned(16))) char sKl[DK * TP];   // decayed K^T, lo
-  __shared__ __attribute__((aligned(16))) char sW[C * WP];     // W rows, fp32
-  __shared__ float sG[C];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hi = lane >> 5, cl = lane & 31;
-  const int seq = blockIdx.x, h = blockIdx.y;
-  const GdnSeq sq = seqs[seq];
-  const int dv0 = wave * 32;
+// ---------------------------------------------------------------- state
+// One workgroup of 6 waves per (sequence, head, value tile of 32 columns).
+// Waves 0..3 own row tile w of the state, S_w = S[32 w .. 32 w + 31][32 vt
+// .. 32 vt + 31], and form M_w S + B_w; waves 4 and 5 form the output rows
+// 32 (w - 4) .. + 31 as Qt S + Ol.  Both are one 32 x 32 accumulator tile
+// with 16 A operands from the chunk kernel; the state is exchanged through
+// LDS each chunk as B operands (hi / lo, contraction index permuted as
+// acc_row, as the chunk kernel wrote M and Qt), double-buffered so that one
+// barrier per chunk suffices.  The operands of the next chunk, which do not
+// depend on the state, are loaded while the current one is computed.
+constexpr int ST_WAVES = 6;
 
-  floatx16 S[DK / 32];
-#pragma unroll
-  for (int a = 0; a < DK / 32; ++a)
+__global__ void __launch_bounds__(64 * ST_WAVES)
+gdn_state_kernel(const uint4* __restrict__ ws, bf16_t* __restrict__ o, int ldo, const GdnSeq* __restrict__ seqs,
+                 float* __restrict__ states, int H) {
+  __shared__ uint4 sS[2][DK / 32][2][2][64];   // [buffer][row tile][half][hi, lo][lane]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cl = lane & 31;
+  const int h = blockIdx.y, vt = blockIdx.z;
+  const GdnSeq sq = seqs[blockIdx.x];
+  const int v0 = 32 * vt;
+  if (sq.len <= 0) return;
+  const bool srow = wave < 4;
+
+  floatx16 acc;
+  if (srow) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      S[a][r] = sq.s_in >= 0
-                    ? states[(((long long)sq.s_in * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl]
-                    : 0.f;
+      acc[r] = sq.s_in >= 0
+                   ? states[(((long long)sq.s_in * H + h) * DK + 32 * wave + acc_row(r, lane)) * DV + v0 + cl]
+                   : 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = acc[8 * hf + e];
+      split8(sv, sS[0][wave][hf][0][lane], sS[0][wave][hf][1][lane]);
+    }
+  }
 
+  // this wave's 16 A operands [k tile][half][hi, lo] and accumulator start
+  auto load = [&](int ci, uint4* af, float4* cf) {
+    const uint4* const wsc = ws + ((long long)ci * H + h) * WS_CH;
+    const uint4* const A = srow ? wsc + wave * 16 * 64 : wsc + WS_M + WS_B + (wave - 4) * 16 * 64;
+    const float4* const Cs =
+        srow ? reinterpret_cast<const float4*>(wsc + WS_M) + ((wave * 4 + vt) * 64 + lane) * 4
+             : reinterpret_cast<const float4*>(wsc + WS_M + WS_B + WS_Q) + (((wave - 4) * 4 + vt) * 64 + lane) * 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) af[i] = A[i * 64 + lane];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) cf[f] = Cs[f];
+  };
+  uint4 ca[16];
+  float4 cc[4];
+  load(sq.c0, ca, cc);
+  __syncthreads();
+
+  int buf = 0;
   for (int c0 = 0, ci = sq.c0; c0 < sq.len; c0 += C, ++ci) {
     const int n = min(C, sq.len - c0);
     const long long base = (long long)sq.row0 + c0;
-    const float* X = wu + ((long long)ci * H + h) * C * XW;
-    float G = lane < n ? lg[(base + lane) * ldg + h] : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_up(G, off, 64);
-      if (lane >= off) G += t;
-    }
-    const float Glast = __shfl(G, 63, 64);
-    const float wK = __expf(Glast - G);
+    uint4 na[16];
+    float4 nc[4];
+    load(c0 + C < sq.len ? ci + 1 : ci, na, nc);
+    __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the products
 
-    __syncthreads();
-    if (wave == 0) sG[lane] = G;
-    // every global load of the chunk first (rows past its end read its last
-    // row, in bounds, and are replaced by zeros), then the LDS stores
-    uint4 qv[C * 16 / 256], kav[C * 8 / 256], kbv[C * 8 / 256];
-    float4 wv4[C * (DK / 4) / 256];
 #pragma unroll
-    for (int i = 0; i < C * 16 / 256; ++i) {
-      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
-      qv[i] = *reinterpret_cast<const uint4*>(q + (base + min(s, n - 1)) * ldqkv + h * DK + q8 * 8);
+    for (int f = 0; f < 4; ++f) {
+      acc[4 * f] = cc[f].x;
+      acc[4 * f + 1] = cc[f].y;
+      acc[4 * f + 2] = cc[f].z;
+      acc[4 * f + 3] = cc[f].w;
     }
 #pragma unroll
-    for (int i = 0; i < C * 8 / 256; ++i) {
-      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15;
-      kav[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p, n - 1)) * ldqkv + h * DK + q8 * 8);
-      kbv[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p + 1, n - 1)) * ldqkv + h * DK + q8 * 8);
-    }
+    for (int ai = 0; ai < DK / 32; ++ai)
 #pragma unroll
-    for (int i = 0; i < C * (DK / 4) / 256; ++i) {
-      const int c = tid + 256 * i, t = c / (DK / 4), q4 = c % (DK / 4);
-      wv4[i] = *reinterpret_cast<const float4*>(X + t * XW + 4 * q4);
-    }
-#pragma unroll
-    for (int i = 0; i < C * 16 / 256; ++i) {
-      const int c = tid + 256 * i, s = c >> 4, q8 = c & 15;
-      *reinterpret_cast<uint4*>(sQ + s * QP + q8 * 16) = s < n ? qv[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C * (DK / 4) / 256; ++i) {
-      const int c = tid + 256 * i, t = c / (DK / 4), q4 = c % (DK / 4);
-      *reinterpret_cast<float4*>(sW + t * WP + q4 * 16) = wv4[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C * 8 / 256; ++i) {
-      const int c = tid + 256 * i, p = c >> 4, q8 = c & 15, s0 = 2 * p, s1 = s0 + 1;
-      const uint4 ka = s0 < n ? kav[i] : make_uint4(0, 0, 0, 0);
-      const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(sK + s0 * QP + q8 * 16) = ka;
-      *reinterpret_cast<uint4*>(sK + s1 * QP + q8 * 16) = kb;
-      const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
-      const uint32_t av[4] = {ka.x, ka.y, ka.z, ka.w}, bv[4] = {kb.x, kb.y, kb.z, kb.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d0 = q8 * 8 + 2 * e;
-        const float x00 = __uint_as_float(av[e] << 16) * w0, x01 = __uint_as_float(bv[e] << 16) * w1;
-        const float x10 = __uint_as_float(av[e] & 0xFFFF0000u) * w0, x11 = __uint_as_float(bv[e] & 0xFFFF0000u) * w1;
-        const uint32_t h0 = cvt2(x00, x01), h1 = cvt2(x10, x11);
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h0;
-        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h1;
-        *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) =
-            cvt2(x00 - __uint_as_float(h0 << 16), x01 - __uint_as_float(h0 & 0xFFFF0000u));
-        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) =
-            cvt2(x10 - __uint_as_float(h1 << 16), x11 - __uint_as_float(h1 & 0xFFFF0000u));
+      for (int hf = 0; hf < 2; ++hf) {
+        const int i = (ai * 2 + hf) * 2;
+        mfma3(acc, as_frag(ca[i]), as_frag(ca[i + 1]), as_frag(sS[buf][ai][hf][0][lane]),
+              as_frag(sS[buf][ai][hf][1][lane]));
       }
-    }
-    __syncthreads();
-
-    // state operand, split once for W S0 and Q S0
-    bf16x8 shi[DK / 32][2], slo[DK / 32][2];
-#pragma unroll
-    for (int a = 0; a < DK / 32; ++a)
+    if (srow) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         float sv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = S[a][8 * hf + e];
-        split8(sv, shi[a][hf], slo[a][hf]);
+        for (int e = 0; e < 8; ++e) sv[e] = acc[8 * hf + e];
+        split8(sv, sS[buf ^ 1][wave][hf][0][lane], sS[buf ^ 1][wave][hf][1][lane]);
       }
-
-    // (1) U = Ut - W S0 for both token tiles
-    floatx16 U[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        U[tt][r] = X[(32 * tt + acc_row(r, lane)) * XW + DK + dv0 + cl];
-#pragma unroll
-      for (int a = 0; a < DK / 32; ++a)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const float* wr = reinterpret_cast<const float*>(sW + (32 * tt + cl) * WP) + 32 * a + 16 * hf + 4 * hi;
-          const float4 w0 = *reinterpret_cast<const float4*>(wr);
-          const float4 w1 = *reinterpret_cast<const float4*>(wr + 8);
-          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-          bf16x8 whi, wlo;
-          split_neg(wv, whi, wlo);
-          mfma32(U[tt], whi, shi[a][hf]);
-          mfma32(U[tt], whi, slo[a][hf]);
-          mfma32(U[tt], wlo, shi[a][hf]);
-        }
-    }
-
-    // (2) scores A^T[s][t] = k_s . q_t for s-tile st <= t-tile tt, masked and
-    // decayed by exp(G_t - G_s)
-    floatx16 At[3];   // (0,0), (0,1), (1,1)
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) At[x][r] = 0.f;
-      const char* kr = sK + (32 * st + cl) * QP + 16 * hi;
-      const char* qr = sQ + (32 * tt + cl) * QP + 16 * hi;
-#pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks)
-        mfma32(At[x], as_frag(*reinterpret_cast<const uint4*>(kr + 32 * ks)),
-               as_frag(*reinterpret_cast<const uint4*>(qr + 32 * ks)));
-      const int t = 32 * tt + cl;
-      const float Gt = sG[t];
+    } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int s = 32 * st + acc_row(r, lane);
-        At[x][r] = s <= t ? At[x][r] * __expf(Gt - sG[s]) : 0.f;
-      }
-    }
-
-    // U operand, hi / lo, shared by (3) and (4)
-    bf16x8 uhi[2][2], ulo[2][2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float uv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) uv[e] = U[st][8 * hf + e];
-        split8(uv, uhi[st][hf], ulo[st][hf]);
-      }
-
-    // (3) O = (A . D) U + exp(G_t) Q S0
-    floatx16 O1[2], O2[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        O1[tt][r] = 0.f;
-        O2[tt][r] = 0.f;
-      }
-#pragma unroll
-    for (int a = 0; a < DK / 32; ++a)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const char* qp = sQ + (32 * tt + cl) * QP + (32 * a + 16 * hf + 4 * hi) * 2;
-          const bf16x8 qf = frag_from_halves(*reinterpret_cast<const uint2*>(qp),
-                                             *reinterpret_cast<const uint2*>(qp + 16));
-          mfma32(O2[tt], qf, shi[a][hf]);
-          mfma32(O2[tt], qf, slo[a][hf]);
-        }
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      const int st = x == 2 ? 1 : 0, tt = x == 0 ? 0 : 1;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float av[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = At[x][8 * hf + e];
-        bf16x8 ahi, alo;
-        split8(av, ahi, alo);
-        mfma32(O1[tt], ahi, uhi[st][hf]);
-        mfma32(O1[tt], ahi, ulo[st][hf]);
-        mfma32(O1[tt], alo, uhi[st][hf]);
+        const int t = 32 * (wave - 4) + acc_row(r, lane);
+        if (t < n) o[(base + t) * ldo + (long long)h * DV + v0 + cl] = f2bf(acc[r]);
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int i = 0; i < 16; ++i) ca[i] = na[i];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * tt + acc_row(r, lane);
-        if (t < n) o[(base + t) * ldo + (long long)h * DV + dv0 + cl] = f2bf(O1[tt][r] + __expf(sG[t]) * O2[tt][r]);
-      }
-
-    // (4) S' = exp(G_last) S0 + (K . w)^T U, the token index permuted as
-    // acc_row on both operands
-    const float dec = __expf(Glast);
-#pragma unroll
-    for (int a = 0; a < DK / 32; ++a) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[a][r] *= dec;
-      const char* kt = sKt + (32 * a + cl) * TP;
-      const char* kl = sKl + (32 * a + cl) * TP;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int off = (32 * st + 16 * hf + 4 * hi) * 2;
-          const bf16x8 khi = frag_from_halves(*reinterpret_cast<const uint2*>(kt + off),
-                                              *reinterpret_cast<const uint2*>(kt + off + 16));
-          const bf16x8 klo = frag_from_halves(*reinterpret_cast<const uint2*>(kl + off),
-                                              *reinterpret_cast<const uint2*>(kl + off + 16));
-          mfma32(S[a], khi, uhi[st][hf]);
-          mfma32(S[a], khi, ulo[st][hf]);
-          mfma32(S[a], klo, uhi[st][hf]);
-        }
-    }
+    for (int f = 0; f < 4; ++f) cc[f] = nc[f];
+    buf ^= 1;
+    __syncthreads();
   }
 
-  if (sq.s_out >= 0) {
+  if (srow && sq.s_out >= 0) {
 #pragma unroll
-    for (int a = 0; a < DK / 32; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        states[(((long long)sq.s_out * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl] = S[a][r];
+    for (int r = 0; r < 16; ++r)
+      states[(((long long)sq.s_out * H + h) * DK + 32 * wave + acc_row(r, lane)) * DV + v0 + cl] = acc[r];
   }
 }
 
@@ -504,16 +544,18 @@ hipError_t launch_gdn_conv(const void* x, void* y, int ld, const float* w, int H
   return hipGetLastError();
 }
 
-size_t gdn_ws_bytes(int n_chunks, int H) { return (size_t)n_chunks * H * C * XW * sizeof(float); }
+size_t gdn_ws_bytes(int n_chunks, int H) { return (size_t)n_chunks * H * WS_CH * sizeof(uint4); }
 
 hipError_t launch_gdn_scan(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
                            const float* beta, int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
                            const GdnSeq* seqs, int n_seqs, float* states, int H, float* ws, hipStream_t s) {
   if (n_seqs <= 0 || H <= 0 || n_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gdn_prep_kernel, dim3(n_chunks, H), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(k),
-                     reinterpret_cast<const bf16_t*>(v), ld_qkv, log_g, beta, ld_g, chunks, ws, H);
-  hipLaunchKernelGGL(gdn_scan_kernel, dim3(n_seqs, H), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(q),
-                     reinterpret_cast<const bf16_t*>(k), ld_qkv, log_g, ld_g, ws, reinterpret_cast<bf16_t*>(o),
+  uint4* const w = reinterpret_cast<uint4*>(ws);
+  hipLaunchKernelGGL(gdn_chunk_kernel, dim3(n_chunks, H), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(q),
+                     reinterpret_cast<const bf16_t*>(k), reinterpret_cast<const bf16_t*>(v), ld_qkv, log_g, beta, ld_g,
+                     chunks, w, H);
+  hipLaunchKernelGGL(gdn_state_kernel, dim3(n_seqs, H, DV / 32), dim3(64 * ST_WAVES), 0, s, w,
+                     reinterpret_cast<bf16_t*>(o),
                      ld_o, seqs, states, H);
   return hipGetLastError();
 }
