@@ -173,18 +173,26 @@ gdn_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, con
     const char* kr = sK + (32 * ti + cl) * QP + 16 * hi;
     const char* qr = sQ + (32 * ti + cl) * QP + 16 * hi;
     const char* br = sK + (32 * tj + cl) * QP + 16 * hi;
+    // (the tile above the diagonal of Q K^T is formed too and masked below)
 #pragma unroll
     for (int ks = 0; ks < DK / 16; ++ks) {
       const bf16x8 bf = lds16(br + 32 * ks);
       mfma32(accL, lds16(kr + 32 * ks), bf);
-      if (tj <= ti) mfma32(accA, lds16(qr + 32 * ks), bf);
+      mfma32(accA, lds16(qr + 32 * ks), bf);
     }
     // acc[r] = X[32 ti + acc_row(r)][32 tj + cl]: row t, column i
+    const float Gi = sG[32 * tj + cl];
+    float Gt[16], Bt[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      Gt[r] = sG[32 * ti + acc_row(r, lane)];
+      Bt[r] = sB[32 * ti + acc_row(r, lane)];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * ti + acc_row(r, lane), i = 32 * tj + cl;
-      const float dcy = __expf(sG[t] - sG[i]);
-      sL[t * LP + i] = i < t ? sB[t] * dcy * accL[r] : 0.f;
+      const float dcy = __expf(Gt[r] - Gi);   // may overflow above the diagonal, where it is not used
+      sL[t * LP + i] = i < t ? Bt[r] * dcy * accL[r] : 0.f;
       const float a = i <= t ? dcy * accA[r] : 0.f;
       const uint32_t ah = cvt2(a, 0.f);
       const uint32_t al = cvt2(a - lo_half(ah), 0.f);
@@ -211,16 +219,28 @@ gdn_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, con
 #pragma unroll
     for (int t = 0; t < C; ++t) x[t] *= sB[t];
   }
-  // four partial sums per row shorten the dependent chain
+  // Row t of L is read from LDS (a broadcast: every thread reads the same
+  // words) while row t - 1 is applied, so the reads' latency is hidden; four
+  // partial sums per row shorten the dependent chain.
+  float4 Lr[2][C / 4];
+  Lr[1][0] = *reinterpret_cast<const float4*>(sL + 1 * LP);
 #pragma unroll
   for (int t = 1; t < C; ++t) {
+    float4* const cur = Lr[t & 1];
+    float4* const nxt = Lr[(t + 1) & 1];
+    if (t + 1 < C) {
+#pragma unroll
+      for (int q4 = 0; q4 < (t + 4) / 4; ++q4) nxt[q4] = *reinterpret_cast<const float4*>(sL + (t + 1) * LP + 4 * q4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float a0 = x[t], a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int i = 0; i < t; i += 4) {
-      a0 -= sL[t * LP + i] * x[i];
-      if (i + 1 < t) a1 -= sL[t * LP + i + 1] * x[i + 1];
-      if (i + 2 < t) a2 -= sL[t * LP + i + 2] * x[i + 2];
-      if (i + 3 < t) a3 -= sL[t * LP + i + 3] * x[i + 3];
+      const float4 c = cur[i / 4];
+      a0 -= c.x * x[i];
+      if (i + 1 < t) a1 -= c.y * x[i + 1];
+      if (i + 2 < t) a2 -= c.z * x[i + 2];
+      if (i + 3 < t) a3 -= c.w * x[i + 3];
     }
     x[t] = (a0 + a1) + (a2 + a3);
   }
