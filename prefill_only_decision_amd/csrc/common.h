@@ -44,20 +44,29 @@ __device__ __forceinline__ bf16x8 frag_from_f(const float* v) {
   u.w = pack_bf2(v[6], v[7]);
   return as_frag(u);
 }
+// Two floats -> two bf16 in one word (a low, b high) with the packed
+// hardware conversion v_cvt_pk_bf16_f32 (round to nearest even, as f2bf for
+// finite values).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const float2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+__device__ __forceinline__ float lo_half(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_half(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 // Split eight floats into hi + lo bf16 operands with v = hi + lo up to
 // 2^-16 relative: hi = rne(v), lo = rne(v - hi) (the difference is exact).
 __device__ __forceinline__ void split_frag(const float* v, bf16x8& hi, bf16x8& lo) {
-  float r[8];
-  uint32_t h[4];
+  uint32_t h[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const bf16_t a = f2bf(v[2 * e]), b = f2bf(v[2 * e + 1]);
-    h[e] = static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
-    r[2 * e] = v[2 * e] - bf2f(a);
-    r[2 * e + 1] = v[2 * e + 1] - bf2f(b);
+    h[e] = cvt2(v[2 * e], v[2 * e + 1]);
+    l[e] = cvt2(v[2 * e] - lo_half(h[e]), v[2 * e + 1] - hi_half(h[e]));
   }
   hi = as_frag(make_uint4(h[0], h[1], h[2], h[3]));
-  lo = frag_from_f(r);
+  lo = as_frag(make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 // Two 8-byte halves (4 bf16 each) -> one operand.

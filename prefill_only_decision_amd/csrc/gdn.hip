@@ -46,16 +46,6 @@ constexpr int RP = C * 2 + 16;     // bytes per row of a [.][C] bf16 operand in 
 constexpr int WS_M = 4 * 4 * 2 * 2 * 64, WS_B = 4 * 4 * 64 * 4, WS_Q = 2 * 4 * 2 * 2 * 64, WS_O = 2 * 4 * 64 * 4;
 constexpr int WS_CH = WS_M + WS_B + WS_Q + WS_O;
 
-// Conversions with the packed hardware instruction (v_cvt_pk_bf16_f32,
-// round to nearest even, as f2bf for finite values).
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-  const float2v f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-}
-__device__ __forceinline__ float lo_half(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_half(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // v = hi + lo with hi = rne(v), lo = rne(v - hi), as two 16-byte operands.
 __device__ __forceinline__ void split8(const float* v, uint4& h, uint4& l) {
   uint32_t hw[4], lw[4];

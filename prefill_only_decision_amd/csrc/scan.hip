@@ -84,44 +84,69 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();                      // previous chunk's reads of LDS are done
     if (wave == 0) sG[lane] = G;
     if (MODE == MODE_SUMMARY && tid == 0 && dvg == 0) gamma[(long long)seq * H + h] = Glast;
+    // every global load of the chunk first (rows past its end read its last
+    // row, in bounds, and are replaced by zeros), then the LDS stores
+    constexpr int QI = C * 16 / NT, KI = C * 8 / NT, VI = (C / 2) * (DVG / 8) / NT;
+    uint4 qv[MODE != MODE_SUMMARY ? QI : 1], kav[KI], kbv[KI], vav[VI], vbv[VI];
+    if constexpr (MODE != MODE_SUMMARY) {
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int c = tid + NT * i, s = c >> 4, ch = c & 15;
+        qv[i] = *reinterpret_cast<const uint4*>(q + (base + min(s, n - 1)) * ldqkv + h * DK + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int c = tid + NT * i, p = c >> 4, ch = c & 15;
+      kav[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p, n - 1)) * ldqkv + h * DK + ch * 8);
+      kbv[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p + 1, n - 1)) * ldqkv + h * DK + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8);
+      const long long col = (long long)h * DV + dvw + ch * 8;
+      vav[i] = *reinterpret_cast<const uint4*>(v + (base + min(2 * p, n - 1)) * ldqkv + col);
+      vbv[i] = *reinterpret_cast<const uint4*>(v + (base + min(2 * p + 1, n - 1)) * ldqkv + col);
+    }
     // Q rows: straight copy
-    for (int c = tid; c < C * 16 && MODE != MODE_SUMMARY; c += NT) {
-      const int s = c >> 4, ch = c & 15;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (s < n) val = *reinterpret_cast<const uint4*>(q + (base + s) * ldqkv + h * DK + ch * 8);
-      *reinterpret_cast<uint4*>(sQ + s * QP + ch * 16) = val;
+    if constexpr (MODE != MODE_SUMMARY) {
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int c = tid + NT * i, s = c >> 4, ch = c & 15;
+        *reinterpret_cast<uint4*>(sQ + s * QP + ch * 16) = s < n ? qv[i] : make_uint4(0, 0, 0, 0);
+      }
     }
     // K rows (row-major copy) and K^T scaled by the decay to the chunk end
-    for (int c = tid; c < (C / 2) * 16; c += NT) {
-      const int p = c >> 4, ch = c & 15, s0 = 2 * p, s1 = s0 + 1;
-      uint4 ka = make_uint4(0, 0, 0, 0), kb = make_uint4(0, 0, 0, 0);
-      if (s0 < n) ka = *reinterpret_cast<const uint4*>(k + (base + s0) * ldqkv + h * DK + ch * 8);
-      if (s1 < n) kb = *reinterpret_cast<const uint4*>(k + (base + s1) * ldqkv + h * DK + ch * 8);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int c = tid + NT * i, p = c >> 4, ch = c & 15, s0 = 2 * p, s1 = s0 + 1;
+      const uint4 ka = s0 < n ? kav[i] : make_uint4(0, 0, 0, 0);
+      const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(sK + s0 * QP + ch * 16) = ka;
       *reinterpret_cast<uint4*>(sK + s1 * QP + ch * 16) = kb;
-      const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
-      if (MODE == MODE_OUTPUT) continue;
-      const uint32_t a[4] = {ka.x, ka.y, ka.z, ka.w}, b[4] = {kb.x, kb.y, kb.z, kb.w};
+      if constexpr (MODE != MODE_OUTPUT) {
+        const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
+        const uint32_t a[4] = {ka.x, ka.y, ka.z, ka.w}, b[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d0 = ch * 8 + 2 * e;
-        // element d0 of tokens s0, s1 and element d0 + 1 of both
-        const float x00 = __uint_as_float(a[e] << 16) * w0, x01 = __uint_as_float(b[e] << 16) * w1;
-        const float x10 = __uint_as_float(a[e] & 0xFFFF0000u) * w0, x11 = __uint_as_float(b[e] & 0xFFFF0000u) * w1;
-        const bf16_t h00 = f2bf(x00), h01 = f2bf(x01), h10 = f2bf(x10), h11 = f2bf(x11);
-        *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h00 | ((uint32_t)h01 << 16);
-        *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h10 | ((uint32_t)h11 << 16);
-        *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) = pack_bf2(x00 - bf2f(h00), x01 - bf2f(h01));
-        *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) = pack_bf2(x10 - bf2f(h10), x11 - bf2f(h11));
+        for (int e = 0; e < 4; ++e) {
+          const int d0 = ch * 8 + 2 * e;
+          // element d0 of tokens s0, s1 and element d0 + 1 of both
+          const float x00 = lo_half(a[e]) * w0, x01 = lo_half(b[e]) * w1;
+          const float x10 = hi_half(a[e]) * w0, x11 = hi_half(b[e]) * w1;
+          const uint32_t h0 = cvt2(x00, x01), h1 = cvt2(x10, x11);
+          *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h0;
+          *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h1;
+          *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) = cvt2(x00 - lo_half(h0), x01 - hi_half(h0));
+          *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) = cvt2(x10 - lo_half(h1), x11 - hi_half(h1));
+        }
       }
     }
     // V^T for this workgroup's value columns
-    for (int c = tid; c < (C / 2) * (DVG / 8); c += NT) {
-      const int p = c / (DVG / 8), ch = c % (DVG / 8), s0 = 2 * p, s1 = s0 + 1;
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-      const long long col = (long long)h * DV + dvw + ch * 8;
-      if (s0 < n) va = *reinterpret_cast<const uint4*>(v + (base + s0) * ldqkv + col);
-      if (s1 < n) vb = *reinterpret_cast<const uint4*>(v + (base + s1) * ldqkv + col);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8), s0 = 2 * p, s1 = s0 + 1;
+      const uint4 va = s0 < n ? vav[i] : make_uint4(0, 0, 0, 0);
+      const uint4 vb = s1 < n ? vbv[i] : make_uint4(0, 0, 0, 0);
       const uint32_t a[4] = {va.x, va.y, va.z, va.w}, b[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
