@@ -45,6 +45,35 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
 /* Number of GEMM tile configurations (host-only, no device work). */
 int s1k_gemm_tile_configs(void);
 
+/* Bytes of the fragment-order copy of a bf16 weight W[N,K] (rows padded to
+ * a multiple of 32); 0 for unsupported shapes (N < 1, K not a positive
+ * multiple of 16).  Host-only. */
+int64_t s1k_frag_bytes(int32_t N, int32_t K);
+
+/* out (bf16, s1k_frag_bytes(N, K) bytes, caller-allocated device memory) =
+ * W[N,K] (bf16, row stride K) in fragment order: for each block of 32 rows
+ * nb and each step of 16 columns ks, one contiguous 1 KB block whose 16-byte
+ * chunk l holds row 32 nb + l % 32, columns 16 ks + 8 (l / 32) .. + 7 (the
+ * B operand of lane l of a 32x32x16 matrix instruction); rows past N are
+ * zero.  gate_up16 != 0 (N a multiple of 64) takes W as FFN gate/up rows
+ * interleaved in blocks of 32 ([32 gate | 32 up] per 64 rows, as the
+ * decoder stores them) and packs them interleaved in blocks of 16, the
+ * layout the SwiGLU epilogue of s1k_gemm_wfrag reads.  The weight layout of
+ * the projection GEMMs (RFC #114, section 1; the Cua-S1 issue, "mostly
+ * GEMMs" comment). */
+int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* out, void* hip_stream);
+
+/* The weight-direct GEMM: A[M,K] (bf16, row stride K) times the packed
+ * weight Wfrag (s1k_frag_pack) transposed.  swiglu = 0: out fp32 [M,N] =
+ * A W^T.  swiglu != 0 (Wfrag packed with gate_up16, N a multiple of 64):
+ * out bf16 [M, N/2][f] = silu(gate_f) * up_f, the FFN gate/up projection with
+ * its SwiGLU (RFC #114 section 1; SwiGLU FFN of the Qwen3.5-family
+ * backbone).  K must be a positive multiple of 64.  Each weight byte is read
+ * once per 128-row block of A; accumulation order over K is the same as
+ * s1k_gemm's without a K split (results are bitwise equal). */
+int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,
+                   int32_t swiglu, void* hip_stream);
+
 /* out[T,d] (elem) = x / sqrt(mean(x^2) + eps) * w for each row of x[T,d]
  * (fp32); w[d] fp32.  RMSNorm before each mixer and FFN (pre-norm blocks of
  * the Qwen3.5-family backbone the System1-Omni README names). */

@@ -25,7 +25,8 @@ EXPORTS = (
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
     "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
     "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
-    "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
+    "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_frag_bytes", "s1k_frag_pack", "s1k_gemm_wfrag",
+    "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs", "s1k_gdn_scan",
 )
@@ -127,6 +128,9 @@ def load_library(path=LIB_PATH):
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_gemm_tile_configs": (C.c_int, []),
+        "s1k_frag_bytes": (i64, [i32, i32]),
+        "s1k_frag_pack": (C.c_int, [vp, i32, i32, i32, vp, vp]),
+        "s1k_gemm_wfrag": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_rmsnorm": (C.c_int, [i32, vp, vp, vp, i32, i32, f32, vp]),
         "s1k_embed": (C.c_int, [i32, vp, vp, vp, i32, i32, vp]),
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
@@ -423,6 +427,19 @@ def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
 
 def gemm_tile_configs():
     return load_library().s1k_gemm_tile_configs()
+
+
+def frag_bytes(N, K):
+    return int(load_library().s1k_frag_bytes(N, K))
+
+
+def frag_pack(W, N, K, gate_up16, out, stream=None):
+    return _k("s1k_frag_pack", C.c_void_p(W), N, K, int(bool(gate_up16)), C.c_void_p(out), _stream(stream))
+
+
+def gemm_wfrag(A, Wfrag, out, M, N, K, swiglu=False, stream=None):
+    return _k("s1k_gemm_wfrag", C.c_void_p(A), C.c_void_p(Wfrag), C.c_void_p(out), M, N, K, int(bool(swiglu)),
+              _stream(stream))
 
 
 def rmsnorm(dtype, x, w, out, T, d, eps, stream=None):

@@ -386,6 +386,35 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
 
 int s1k_gemm_tile_configs(void) { return gemm_tile_configs(); }
 
+int64_t s1k_frag_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 16 || K % 16) return 0;
+  return (int64_t)frag_bytes(N, K);
+}
+
+int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* out, void* hip_stream) {
+  if (!W || !out || N < 1 || K < 16 || K % 16 || (gate_up16 && N % 64))
+    return set_error(S1_EINVAL, "s1k_frag_pack: unsupported arguments");
+  return dev_status(launch_frag_pack(W, N, K, K, gate_up16 != 0, out, strm(hip_stream)), "s1k_frag_pack");
+}
+
+int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,
+                   int32_t swiglu, void* hip_stream) {
+  if (!A || !Wfrag || !out || M < 0 || N < 1 || K < 64 || K % 64 || (swiglu && N % 64))
+    return set_error(S1_EINVAL, "s1k_gemm_wfrag: unsupported arguments");
+  GemmArgs g{};
+  g.A = A;
+  g.W = Wfrag;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldw = K;
+  g.out0 = out;
+  g.ld0 = swiglu ? N / 2 : N;
+  g.n_valid = N / 2;
+  return dev_status(launch_gemm_wd(swiglu ? EPI_SWIGLU : EPI_F32, g, strm(hip_stream)), "s1k_gemm_wfrag");
+}
+
 int s1k_rmsnorm(int32_t dtype, const float* x, const float* w, void* out, int32_t T, int32_t d, float eps,
                 void* hip_stream) {
   if ((dtype != S1_BF16 && dtype != S1_F32) || T < 0 || d < 4 || d % 4 || !x || !w || !out)

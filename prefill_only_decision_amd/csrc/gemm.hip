@@ -46,7 +46,10 @@ __device__ __forceinline__ float log_sigmoid(float z) {
   // log(1 / (1 + e^-z)) = -(max(-z, 0) + log1p(e^-|z|))
   return -(fmaxf(-z, 0.f) + log1pf(__expf(-fabsf(z))));
 }
-__device__ __forceinline__ float silu(float a) { return a / (1.f + __expf(-a)); }
+// silu(a) = a / (1 + e^-a), with the hardware reciprocal (1 ulp) in place of
+// an IEEE division: the epilogues run once per output with one wave per
+// SIMD, so their VALU time is not hidden.  e^-a = inf gives a * 0.
+__device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
 // Global-memory views of the epilogue's pointers: through the generic
 // pointers of GemmArgs the compiler emits flat accesses, whose results it
@@ -699,6 +702,228 @@ gemm_wide_kernel(GemmArgs g) {
   epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
 }
 
+// ----------------------------------------------- bf16 weight-direct kernel
+// For GEMMs of a few hundred rows the weights stream from HBM once while the
+// activations stay in L2, and the LDS stages of the kernels above cap how
+// many weight bytes a CU has in flight (one 57 KB stage for 256 x 192).
+// Here the weight operand bypasses LDS: the weights are stored at load time
+// in fragment order (for each 32-row block and each 16-element K step, the
+// 64 lanes' 16-byte MFMA B operands as one contiguous 1 KB block), and each
+// wave loads its own columns' fragments with coalesced 1 KB loads into a
+// register ring DK K tiles deep.  Only the activation tile goes through LDS
+// (LDS-DMA as above, NS stages of BM x 64).  The four waves split the
+// columns: a wave owns all BM rows and 32 TN columns, so no weight byte is
+// loaded twice in a workgroup.  Every load is issued unconditionally (tile
+// indices past the end are clamped to the last tile), so the number of loads
+// between an activation stage and its wait is fixed.
+template <int TM_, int TN_, int NS_, int DK_>
+struct WD {
+  static constexpr int TM = TM_, TN = TN_, NS = NS_, DK = DK_;
+  static constexpr int NWAVE = 4, NT = 256;
+  static constexpr int BK = 64, RB = 128, CH = 8, RPI = 8, SH = 1;
+  static constexpr int BM = 32 * TM, WTN = 32 * TN, BN = NWAVE * WTN;
+  static constexpr int STAGE = BM * RB;
+  static constexpr int A_INS = BM * RB / 1024 / NWAVE;   // activation DMA loads per K tile and wave
+  static constexpr int KS = BK / 16;
+  static constexpr int W_INS = KS * TN;                  // weight loads per K tile and wave
+  // loads issued after the activation DMA of tile kt + 1 when tile kt waits for it
+  static constexpr int VM_A = W_INS + (NS - 2) * (A_INS + W_INS);
+  static constexpr int VM_PRO = (NS - 1) * A_INS + DK * W_INS;
+  static_assert(A_INS * NWAVE * 1024 == BM * RB, "tile/wave mismatch");
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(VM_A < 64 && VM_PRO < 64, "vmcnt range");
+};
+
+// SwiGLU over weights packed with gate/up interleaved in blocks of 16 rows:
+// in each 32-column MFMA tile, lane column c < 16 holds gate feature f0 + c
+// and lane c + 16 its up partner, for the same 16 rows.  For each pair of
+// accumulator rows (2k, 2k + 1) one exchange between the two lanes gives the
+// gate lane the up value of row 2k and the up lane the gate value of row
+// 2k + 1, so that every lane computes and stores one output.
+template <int TM, int TN>
+__device__ __forceinline__ void epilogue_swiglu16(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0, int cn0,
+                                                  int lane) {
+  const int cl = lane & 31;
+  const bool gate_lane = cl < 16;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int cb = cn0 + 32 * j;
+    if (cb >= g.N) continue;
+    const int f = (cb >> 1) + (cl & 15);
+    const bool fok = f < g.n_valid;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rb = rm0 + 32 * i;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
+        // lane ^ 16 inside each half-wave: ds_swizzle bit mode, and 0x1F, xor 0x10
+        const float got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(gate_lane ? a1 : a0), 0x401F));
+        const float gt = gate_lane ? a0 : got, up = gate_lane ? got : a1;
+        const int row = rb + acc_row(2 * k + (gate_lane ? 0 : 1), lane);
+        if (fok && row < g.M) gptr<bf16_t>(g.out0)[(long long)row * g.ld0 + f] = f2bf(silu(gt) * up);
+      }
+      // one 32 x 32 tile at a time: bounds the values in flight
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <typename S, int EPI>
+__global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_wd_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  const GemmArgs e = pin_epilogue_args<EPI>(g);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nbm = (g.M + S::BM - 1) / S::BM, nbn = (g.N + S::BN - 1) / S::BN;
+  int tm, tn;
+  tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
+  const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const int nk = g.K / S::BK;   // >= 1: the host requires K to be a positive multiple of 64
+
+  const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
+  const int32x4 ra = buffer_rsrc(abase, (g.M - m0) * g.lda * 2);
+  const uint32_t lds0 = lds_addr(smem);
+  int va[S::A_INS];
+#pragma unroll
+  for (int i = 0; i < S::A_INS; ++i) va[i] = dma_voffset<S>(wave * S::A_INS + i, lane, g.lda);
+  auto issue_a = [&](int kt) {
+    const uint32_t st = lds0 + (kt % S::NS) * S::STAGE;
+    const int so = min(kt, nk - 1) * S::BK * 2;
+#pragma unroll
+    for (int i = 0; i < S::A_INS; ++i) dma16(ra, st + (wave * S::A_INS + i) * 1024, va[i], so);
+  };
+
+  // the wave's weight fragments: block row nb, K step ks at ((nb * ksteps + ks) * 64 + lane) * 16 bytes
+  const int ksteps = g.K >> 4, nblk = (g.N + 31) >> 5;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const gmem<u32x4>* wp[S::TN];
+#pragma unroll
+  for (int j = 0; j < S::TN; ++j) {
+    const int nb = min((n0 + wave * S::WTN) / 32 + j, nblk - 1);
+    wp[j] = gptr<u32x4>(g.W) + (long long)nb * ksteps * 64 + lane;
+  }
+  u32x4 wr[S::DK][S::KS][S::TN];
+  auto issue_w = [&](int kt, int d) {
+    const int t = min(kt, nk - 1);
+#pragma unroll
+    for (int u = 0; u < S::KS; ++u)
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j) wr[d][u][j] = wp[j][(t * S::KS + u) * 64];
+  };
+
+  const int l32 = lane & 31, h = lane >> 5;
+  const int sw = (l32 >> S::SH) & (S::CH - 1);
+  int oa[S::KS];
+#pragma unroll
+  for (int u = 0; u < S::KS; ++u) oa[u] = l32 * S::RB + (((2 * u + h) ^ sw) * 16);
+
+  floatx16 acc[S::TM][S::TN];
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8 fa[2][S::TM];
+  auto read_ops = [&](int buf, const char* st, int u) {
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) fa[buf][i] = as_frag(*reinterpret_cast<const uint4*>(st + oa[u] + i * 32 * S::RB));
+  };
+#pragma unroll
+  for (int p = 0; p < S::NS; ++p) issue_a(p);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < S::DK; ++d) issue_w(d, d);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<S::VM_PRO>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_ops(0, smem, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): nothing outstanding entering the loop
+
+  auto tile = [&](int kt, int d) {
+    const char* st = smem + (kt % S::NS) * S::STAGE;
+#pragma unroll
+    for (int u = 0; u < S::KS; ++u) {
+      if (u + 1 < S::KS) {
+        read_ops((u + 1) & 1, st, u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // activation tile kt + 1 landed (own DMA) and own reads of tile kt done;
+        // the barrier publishes the first and frees stage kt % NS for tile kt + NS
+        wait_vm_lgkm0<S::VM_A>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_a(kt + S::NS);
+        read_ops((u + 1) & 1, smem + ((kt + 1) % S::NS) * S::STAGE, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TN; ++j) mfma32(acc[i][j], fa[u & 1][i], __builtin_bit_cast(bf16x8, wr[d][u][j]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(kt + S::DK, d);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // whole groups of DK tiles without conditions (the ring slot is static and
+  // the compiler's load counts are the same on every path into the loop),
+  // then the remaining tiles
+  int kt0 = 0;
+  for (; kt0 + S::DK <= nk; kt0 += S::DK) {
+#pragma unroll
+    for (int d = 0; d < S::DK; ++d) tile(kt0 + d, d);
+  }
+#pragma unroll
+  for (int d = 0; d + 1 < S::DK; ++d)
+    if (kt0 + d < nk) tile(kt0 + d, d);
+  // no DMA may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  if constexpr (EPI == EPI_SWIGLU)
+    epilogue_swiglu16<S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane);
+  else
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
+}
+
+// Fragment-order copy of a bf16 weight W[N, K] (row stride ld): 16-byte
+// chunk ((nb * K/16 + ks) * 64 + l) holds row src(32 nb + l % 32), columns
+// 16 ks + 8 (l / 32) .. + 7; rows at or past N are zero.  With gu16 the
+// source rows are gate/up interleaved in blocks of 32 and the copy
+// interleaves them in blocks of 16 (the weight-direct SwiGLU epilogue).
+__global__ void frag_pack_kernel(const bf16_t* __restrict__ W, int N, int K, int ld, int gu16,
+                                 uint4* __restrict__ out, long long nchunks) {
+  const int ksteps = K >> 4;
+  for (long long c = blockIdx.x * (long long)blockDim.x + threadIdx.x; c < nchunks;
+       c += (long long)gridDim.x * blockDim.x) {
+    const int l = (int)(c & 63);
+    const long long rest = c >> 6;
+    const int ks = (int)(rest % ksteps);
+    const int n = (int)(rest / ksteps) * 32 + (l & 31);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n < N) {
+      int src = n;
+      if (gu16) {
+        const int feat = (n >> 5) * 16 + (n & 15);
+        src = (feat >> 5) * 64 + ((n & 16) ? 32 : 0) + (feat & 31);
+      }
+      v = *reinterpret_cast<const uint4*>(W + (long long)src * ld + ks * 16 + 8 * (l >> 5));
+    }
+    out[c] = v;
+  }
+}
+
+template <typename S, int EPI>
+hipError_t run_wd(const GemmArgs& a, hipStream_t s) {
+  const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  hipLaunchKernelGGL((gemm_wd_kernel<S, EPI>), dim3(nbm * nbn), dim3(S::NT), 0, s, a);
+  return hipGetLastError();
+}
+using CfgWD = WD<4, 3, 4, 3>;   // 128 x 384, a wave 128 x 96, four activation stages, three weight tiles ahead
+
 // Sum of split-K partial slabs in a fixed order, then the epilogue.
 template <bool RESID>
 __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, long long stride,
@@ -926,6 +1151,35 @@ hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* 
   if (split < 1) split = 1;
   return bf16 ? dispatch<bf16_t>(epi, g, split, ws, cfg, s, normed)
               : dispatch<float>(epi, g, split, ws, cfg, s, normed);
+}
+
+size_t frag_bytes(int N, int K) { return (size_t)((N + 31) / 32) * 32 * K * 2; }
+
+hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void* out, hipStream_t s) {
+  if (N <= 0 || K <= 0 || K % 16 || ld % 8) return hipErrorInvalidValue;
+  const long long nchunks = (long long)((N + 31) / 32) * (K / 16) * 64;
+  const int blocks = (int)std::min<long long>((nchunks + 255) / 256, 8192);
+  hipLaunchKernelGGL(frag_pack_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const bf16_t*>(W), N, K, ld,
+                     gu16 ? 1 : 0, static_cast<uint4*>(out), nchunks);
+  return hipGetLastError();
+}
+
+bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
+  const long long abytes = (long long)a.M * a.lda * 2;
+  return (epi == EPI_F32 || epi == EPI_RESID || epi == EPI_GATE || epi == EPI_SWIGLU) && a.K >= 64 &&
+         a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
+}
+
+hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (!gemm_wd_ok(epi, a)) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_F32: return run_wd<CfgWD, EPI_F32>(a, s);
+    case EPI_RESID: return run_wd<CfgWD, EPI_RESID>(a, s);
+    case EPI_GATE: return run_wd<CfgWD, EPI_GATE>(a, s);
+    case EPI_SWIGLU: return run_wd<CfgWD, EPI_SWIGLU>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace s1

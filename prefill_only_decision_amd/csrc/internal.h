@@ -25,6 +25,7 @@ struct LayerW {
   void* w_o = nullptr;          // [d, heads * head_dim]
   int k_o = 0;
   void* w_gu = nullptr;         // gate/up interleaved in blocks of 32 rows, [2 * ffn_pad, d]
+  void* w_gu_frag = nullptr;    // bf16: w_gu in fragment order, gate/up interleaved in blocks of 16
   int n_gu = 0;
   void* w_down = nullptr;       // [d, ffn]
   float* conv = nullptr;        // Gated DeltaNet: convolution taps fp32 [3 H 128][4]
@@ -56,6 +57,7 @@ struct Model {
   int device = 0;
   hipStream_t own_stream = nullptr;
   int ffn_pad = 0;
+  int n_cu = 256;                // compute units of the device (set at load)
   int n_la = 0, n_fa = 0;
 
   void* embed = nullptr;        // [V, d]

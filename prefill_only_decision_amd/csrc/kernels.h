@@ -57,6 +57,14 @@ struct GemmArgs {
 constexpr int GEMM_AUTO = -1;
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
                        hipStream_t s, int tile_cfg = GEMM_AUTO, bool* normed = nullptr);
+// Weight-direct GEMM (bf16): W is a fragment-order copy made by
+// launch_frag_pack (frag_bytes(N, K) bytes); K a positive multiple of 64;
+// EPI_F32, EPI_RESID, EPI_GATE, or EPI_SWIGLU over a copy packed with gu16
+// (gate/up interleaved in blocks of 16 rows).  No K split.
+size_t frag_bytes(int N, int K);
+hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void* out, hipStream_t s);
+bool gemm_wd_ok(Epi epi, const GemmArgs& a);
+hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, hipStream_t s);
 // Number of tile configurations.
 int gemm_tile_configs();
 // The K tile (elements) of the register-staged GEMM for the element type.

@@ -91,6 +91,76 @@ def test_gemm_split_is_deterministic():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+def _host_frag_pack(W, N, K):
+    """Fragment order written out with numpy: block (nb, ks) holds, for lane
+    l = 32 h + r, row 32 nb + r and columns 16 ks + 8 h .. + 7."""
+    nb = (N + 31) // 32
+    Wp = np.zeros((nb * 32, K), dtype=W.dtype)
+    Wp[:N] = W
+    return Wp.reshape(nb, 32, K // 16, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 64, 64), (77, 6160, 2560), (512, 19456, 2560), (300, 1000, 640), (130, 2560, 9728), (1000, 520, 128),
+])
+def test_gemm_wfrag(M, N, K):
+    """The weight-direct GEMM over a fragment-packed weight: the packing
+    against numpy, the product against float64 products of the same bf16
+    operands, and bitwise equality with the LDS-staged kernel without a K
+    split (same matrix instructions in the same K order)."""
+    torch = require_gpu()
+    log(f"gemm wfrag M={M} N={N} K={K}")
+    rng = np.random.default_rng([M, N, K, 11])
+    A, W = _bits(rng, (M, K)), _bits(rng, (N, K), 0.05)
+    dA, dW = dev_bits(A), dev_bits(W)
+    nbytes = B.frag_bytes(N, K)
+    assert nbytes == (N + 31) // 32 * 32 * K * 2
+    dWf = torch.full((nbytes // 2,), -1, dtype=torch.int16, device="cuda")
+    B.frag_pack(dW.data_ptr(), N, K, False, dWf.data_ptr(), stream_ptr())
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dC.data_ptr(), M, N, K, False, stream_ptr())
+    dR = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    B.gemm_cfg(B.S1_BF16, dA.data_ptr(), dW.data_ptr(), dR.data_ptr(), M, N, K, 1, 1, stream_ptr())
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dWf), _host_frag_pack(W, N, K))
+    ref = O.bf16_bits_to_float(A) @ O.bf16_bits_to_float(W).T
+    C = dC.cpu().numpy()
+    assert np.isfinite(C).all()
+    assert rel_l2(C, ref) < 1e-5
+    assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
+    assert np.array_equal(C, dR.cpu().numpy())
+
+
+@pytest.mark.parametrize("M,F,K", [(512, 9728, 2560), (77, 96, 640), (1, 32, 64), (700, 160, 128)])
+def test_gemm_wfrag_swiglu(M, F, K):
+    """Gate/up rows stored as the decoder stores them ([32 gate | 32 up] per
+    64 rows), packed with the 16-row interleave, through the SwiGLU epilogue
+    of the weight-direct GEMM: silu(x Wg^T) * (x Wu^T) within bf16 rounding
+    of the float64 result."""
+    torch = require_gpu()
+    log(f"gemm wfrag swiglu M={M} F={F} K={K}")
+    rng = np.random.default_rng([M, F, K, 12])
+    A = _bits(rng, (M, K))
+    Wg, Wu = _bits(rng, (F, K), 0.05), _bits(rng, (F, K), 0.05)
+    W = np.zeros((2 * F, K), dtype=np.uint16)
+    i = np.arange(F)
+    W[64 * (i // 32) + i % 32] = Wg
+    W[64 * (i // 32) + i % 32 + 32] = Wu
+    dA, dW = dev_bits(A), dev_bits(W)
+    dWf = torch.empty((B.frag_bytes(2 * F, K) // 2,), dtype=torch.int16, device="cuda")
+    B.frag_pack(dW.data_ptr(), 2 * F, K, True, dWf.data_ptr(), stream_ptr())
+    dH = torch.full((M, F), -1, dtype=torch.int16, device="cuda")
+    B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dH.data_ptr(), M, 2 * F, K, True, stream_ptr())
+    torch.cuda.synchronize()
+    a = O.bf16_bits_to_float(A)
+    g, u = a @ O.bf16_bits_to_float(Wg).T, a @ O.bf16_bits_to_float(Wu).T
+    ref = g / (1 + np.exp(-g)) * u
+    H = O.bf16_bits_to_float(host_bits(dH))
+    assert np.isfinite(H).all()
+    assert (np.abs(H - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max()).all()
+    assert rel_l2(H, ref) < 4e-3
+
+
 @pytest.mark.parametrize("dtype", [B.S1_BF16, B.S1_F32])
 def test_rmsnorm_and_embed(dtype):
     torch = require_gpu()
