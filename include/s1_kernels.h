@@ -68,11 +68,12 @@ int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* 
  * A W^T.  swiglu != 0 (Wfrag packed with gate_up16, N a multiple of 64):
  * out bf16 [M, N/2][f] = silu(gate_f) * up_f, the FFN gate/up projection with
  * its SwiGLU (RFC #114 section 1; SwiGLU FFN of the Qwen3.5-family
- * backbone).  K must be a positive multiple of 64.  Each weight byte is read
- * once per 128-row block of A; accumulation order over K is the same as
- * s1k_gemm's without a K split (results are bitwise equal). */
+ * backbone).  K must be a positive multiple of 64.  tile 1: workgroup tiles
+ * of 128 rows x 384 columns; tile 2: 256 x 256 (other values: S1_EINVAL).
+ * Accumulation order over K is the same as s1k_gemm's without a K split
+ * (results are bitwise equal). */
 int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,
-                   int32_t swiglu, void* hip_stream);
+                   int32_t swiglu, int32_t tile, void* hip_stream);
 
 /* out[T,d] (elem) = x / sqrt(mean(x^2) + eps) * w for each row of x[T,d]
  * (fp32); w[d] fp32.  RMSNorm before each mixer and FFN (pre-norm blocks of

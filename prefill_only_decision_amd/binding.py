@@ -130,7 +130,7 @@ def load_library(path=LIB_PATH):
         "s1k_gemm_tile_configs": (C.c_int, []),
         "s1k_frag_bytes": (i64, [i32, i32]),
         "s1k_frag_pack": (C.c_int, [vp, i32, i32, i32, vp, vp]),
-        "s1k_gemm_wfrag": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, vp]),
+        "s1k_gemm_wfrag": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_rmsnorm": (C.c_int, [i32, vp, vp, vp, i32, i32, f32, vp]),
         "s1k_embed": (C.c_int, [i32, vp, vp, vp, i32, i32, vp]),
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
@@ -437,9 +437,9 @@ def frag_pack(W, N, K, gate_up16, out, stream=None):
     return _k("s1k_frag_pack", C.c_void_p(W), N, K, int(bool(gate_up16)), C.c_void_p(out), _stream(stream))
 
 
-def gemm_wfrag(A, Wfrag, out, M, N, K, swiglu=False, stream=None):
+def gemm_wfrag(A, Wfrag, out, M, N, K, swiglu=False, tile=1, stream=None):
     return _k("s1k_gemm_wfrag", C.c_void_p(A), C.c_void_p(Wfrag), C.c_void_p(out), M, N, K, int(bool(swiglu)),
-              _stream(stream))
+              tile, _stream(stream))
 
 
 def rmsnorm(dtype, x, w, out, T, d, eps, stream=None):

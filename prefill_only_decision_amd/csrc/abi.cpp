@@ -398,8 +398,8 @@ int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* 
 }
 
 int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,
-                   int32_t swiglu, void* hip_stream) {
-  if (!A || !Wfrag || !out || M < 0 || N < 1 || K < 64 || K % 64 || (swiglu && N % 64))
+                   int32_t swiglu, int32_t tile, void* hip_stream) {
+  if (!A || !Wfrag || !out || M < 0 || N < 1 || K < 64 || K % 64 || (swiglu && N % 64) || tile < 1 || tile > 2)
     return set_error(S1_EINVAL, "s1k_gemm_wfrag: unsupported arguments");
   GemmArgs g{};
   g.A = A;
@@ -412,7 +412,7 @@ int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32
   g.out0 = out;
   g.ld0 = swiglu ? N / 2 : N;
   g.n_valid = N / 2;
-  return dev_status(launch_gemm_wd(swiglu ? EPI_SWIGLU : EPI_F32, g, strm(hip_stream)), "s1k_gemm_wfrag");
+  return dev_status(launch_gemm_wd(swiglu ? EPI_SWIGLU : EPI_F32, g, tile, strm(hip_stream)), "s1k_gemm_wfrag");
 }
 
 int s1k_rmsnorm(int32_t dtype, const float* x, const float* w, void* out, int32_t T, int32_t d, float eps,

@@ -804,15 +804,21 @@ namespace {
 
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
 // output (the GEMM picks the split it uses, up to this).
-// The FFN gate/up projection runs on the weight-direct GEMM when its tiles
-// (128 rows x 384 columns) fill the chip at most once: measured on MI355X
-// with weights out of cache, 63 us against 69 us (256 x 192 LDS tiles) for
-// the 4B shape at 512 rows.  Longer passes, which reuse each weight tile
-// over more rows, keep the LDS-staged kernels.
-bool gate_up_direct(const Model* m, const LayerW& L, int T) {
-  if (!L.w_gu_frag || T <= 0) return false;
-  const long long tiles = (long long)((T + 127) / 128) * ((L.n_gu + 383) / 384);
-  return tiles <= m->n_cu;
+// The FFN gate/up projection runs on the weight-direct GEMM.  Its launches
+// are bound by the operand stream into each CU (the same bytes per K tile
+// for both tiles, 64 KB), so the time follows the number of waves of
+// workgroups; the 256 x 256 tile does a third more work per workgroup and
+// is taken only when it needs clearly fewer waves than 128 x 384.  Measured
+// on MI355X with weights out of cache (4B shape, SwiGLU epilogue): 512 rows
+// 63-72 us (128 x 384) against 69-72 us for the LDS-staged 256 x 192 tiles;
+// 768 rows 78 us (256 x 256) against 122 us; 16,925 rows 1,473 us against
+// 1,659 us for the LDS-staged 256 x 256 tiles; 27B shape at 1,024 rows
+// 359 us (128 x 384) against 435 us.
+int gate_up_direct(const Model* m, const LayerW& L, int T) {
+  if (!L.w_gu_frag || T <= 0) return 0;
+  const long long w1 = (gemm_wd_tiles(1, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
+  const long long w2 = (gemm_wd_tiles(2, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
+  return 11 * w2 < 10 * w1 ? 2 : 1;
 }
 
 int max_split(const Model* m, const Plan* p, int M) {
@@ -935,9 +941,9 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
     gu.out0 = static_cast<char*>(m->hbuf) + (size_t)r0 * c.ffn * es;
     gu.ld0 = c.ffn;
     gu.n_valid = c.ffn;
-    if (gate_up_direct(m, L, T)) {
+    if (const int wd = gate_up_direct(m, L, T)) {
       gu.W = L.w_gu_frag;
-      S1_TRY(launch_gemm_wd(EPI_SWIGLU, gu, s), "FFN gate/up");
+      S1_TRY(launch_gemm_wd(EPI_SWIGLU, gu, wd, s), "FFN gate/up");
     } else {
       S1_TRY(launch_gemm(m->bf16, EPI_SWIGLU, gu, 1, nullptr, s), "FFN gate/up");
     }

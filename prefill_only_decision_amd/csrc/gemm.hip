@@ -922,7 +922,8 @@ hipError_t run_wd(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_wd_kernel<S, EPI>), dim3(nbm * nbn), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
-using CfgWD = WD<4, 3, 4, 3>;   // 128 x 384, a wave 128 x 96, four activation stages, three weight tiles ahead
+using CfgWD1 = WD<4, 3, 4, 3>;   // 128 x 384, a wave 128 x 96, four activation stages, three weight tiles ahead
+using CfgWD2 = WD<8, 2, 4, 3>;   // 256 x 256, a wave 256 x 64
 
 // Sum of split-K partial slabs in a fixed order, then the epilogue.
 template <bool RESID>
@@ -1170,16 +1171,26 @@ bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
          a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
 }
 
-hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_wd_ok(epi, a)) return hipErrorInvalidValue;
+template <typename S>
+hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
-    case EPI_F32: return run_wd<CfgWD, EPI_F32>(a, s);
-    case EPI_RESID: return run_wd<CfgWD, EPI_RESID>(a, s);
-    case EPI_GATE: return run_wd<CfgWD, EPI_GATE>(a, s);
-    case EPI_SWIGLU: return run_wd<CfgWD, EPI_SWIGLU>(a, s);
+    case EPI_F32: return run_wd<S, EPI_F32>(a, s);
+    case EPI_RESID: return run_wd<S, EPI_RESID>(a, s);
+    case EPI_GATE: return run_wd<S, EPI_GATE>(a, s);
+    case EPI_SWIGLU: return run_wd<S, EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+int gemm_wd_tiles(int tile, int M, int N) {
+  const int bm = tile == 2 ? CfgWD2::BM : CfgWD1::BM, bn = tile == 2 ? CfgWD2::BN : CfgWD1::BN;
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (!gemm_wd_ok(epi, a) || tile < 1 || tile > 2) return hipErrorInvalidValue;
+  return tile == 2 ? run_wd_epi<CfgWD2>(epi, a, s) : run_wd_epi<CfgWD1>(epi, a, s);
 }
 
 }  // namespace s1

@@ -63,8 +63,11 @@ hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* 
 // (gate/up interleaved in blocks of 16 rows).  No K split.
 size_t frag_bytes(int N, int K);
 hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void* out, hipStream_t s);
+// tile 1: 128 x 384 workgroup tiles (a wave 128 x 96); tile 2: 256 x 256 (a
+// wave 256 x 64).  gemm_wd_tiles gives the workgroup count.
 bool gemm_wd_ok(Epi epi, const GemmArgs& a);
-hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, hipStream_t s);
+int gemm_wd_tiles(int tile, int M, int N);
+hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s);
 // Number of tile configurations.
 int gemm_tile_configs();
 // The K tile (elements) of the register-staged GEMM for the element type.

@@ -117,18 +117,21 @@ def test_gemm_wfrag(M, N, K):
     assert nbytes == (N + 31) // 32 * 32 * K * 2
     dWf = torch.full((nbytes // 2,), -1, dtype=torch.int16, device="cuda")
     B.frag_pack(dW.data_ptr(), N, K, False, dWf.data_ptr(), stream_ptr())
-    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dC.data_ptr(), M, N, K, False, stream_ptr())
     dR = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     B.gemm_cfg(B.S1_BF16, dA.data_ptr(), dW.data_ptr(), dR.data_ptr(), M, N, K, 1, 1, stream_ptr())
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(dWf), _host_frag_pack(W, N, K))
     ref = O.bf16_bits_to_float(A) @ O.bf16_bits_to_float(W).T
-    C = dC.cpu().numpy()
-    assert np.isfinite(C).all()
-    assert rel_l2(C, ref) < 1e-5
-    assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6
-    assert np.array_equal(C, dR.cpu().numpy())
+    R = dR.cpu().numpy()
+    for tile in (1, 2):
+        dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dC.data_ptr(), M, N, K, False, tile=tile, stream=stream_ptr())
+        torch.cuda.synchronize()
+        C = dC.cpu().numpy()
+        assert np.isfinite(C).all(), tile
+        assert rel_l2(C, ref) < 1e-5, tile
+        assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6, tile
+        assert np.array_equal(C, R), tile
 
 
 @pytest.mark.parametrize("M,F,K", [(512, 9728, 2560), (77, 96, 640), (1, 32, 64), (700, 160, 128)])
@@ -149,16 +152,20 @@ def test_gemm_wfrag_swiglu(M, F, K):
     dA, dW = dev_bits(A), dev_bits(W)
     dWf = torch.empty((B.frag_bytes(2 * F, K) // 2,), dtype=torch.int16, device="cuda")
     B.frag_pack(dW.data_ptr(), 2 * F, K, True, dWf.data_ptr(), stream_ptr())
-    dH = torch.full((M, F), -1, dtype=torch.int16, device="cuda")
-    B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dH.data_ptr(), M, 2 * F, K, True, stream_ptr())
-    torch.cuda.synchronize()
     a = O.bf16_bits_to_float(A)
     g, u = a @ O.bf16_bits_to_float(Wg).T, a @ O.bf16_bits_to_float(Wu).T
     ref = g / (1 + np.exp(-g)) * u
-    H = O.bf16_bits_to_float(host_bits(dH))
-    assert np.isfinite(H).all()
-    assert (np.abs(H - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max()).all()
-    assert rel_l2(H, ref) < 4e-3
+    outs = []
+    for tile in (1, 2):
+        dH = torch.full((M, F), -1, dtype=torch.int16, device="cuda")
+        B.gemm_wfrag(dA.data_ptr(), dWf.data_ptr(), dH.data_ptr(), M, 2 * F, K, True, tile=tile, stream=stream_ptr())
+        torch.cuda.synchronize()
+        H = O.bf16_bits_to_float(host_bits(dH))
+        assert np.isfinite(H).all(), tile
+        assert (np.abs(H - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max()).all(), tile
+        assert rel_l2(H, ref) < 4e-3, tile
+        outs.append(H)
+    assert np.array_equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("dtype", [B.S1_BF16, B.S1_F32])
