@@ -1125,6 +1125,12 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
     split = split_for(t128, 240);
   } else if (t128 >= 192) {
     cfg = 1;
+  } else if (can_split && a.K >= 2048 && t128 < 128) {
+    // few output tiles (the d-wide out-projection at 512 rows: 80): a K split
+    // fills the chip, and the reduction runs fused with the residual add and
+    // the next RMSNorm in place of a separate norm (20 + 7 -> ~17 us)
+    cfg = 1;
+    split = split_for(t128, 240);
   } else {
     cfg = (epi == EPI_SWIGLU || epi == EPI_QKV) ? 4 : 3;
   }
