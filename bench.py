@@ -138,6 +138,79 @@ def stored_traffic(workload):
     return rec["traffic_bytes_per_launch"] if rec.get("gemm_source_sha256") == source_digest() else None
 
 
+def scan_roofline(shape, batch, tokens, prof, steps_p):
+    """Achieved HBM bandwidth of the linear-attention scan per step: per
+    token and layer it must read q, k, v (bf16) and the log decay (fp32) and
+    write o (bf16); per prefix and layer it writes the fp32 final state and
+    each branch reads it.  The scan is latency-bound at a few hundred tokens
+    (a few (sequence, head) chains, one 64-token chunk apart)."""
+    if shape.la_kind != "gla" or "la_scan" not in prof:
+        return None
+    H, dk, dv = shape.la_heads, shape.la_dk, shape.la_dv
+    per_token = H * (2 * dk + dv) * 2 + 4 * H + H * dv * 2
+    pre = batch.prefix_of
+    n_states = int(len(set(int(p) for p in pre if p >= 0)) + int((pre >= 0).sum()))
+    per_layer = tokens * per_token + n_states * H * dk * dv * 4
+    us = prof["la_scan"][1] / steps_p
+    gbs = per_layer * shape.n_linear / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_token_layer": per_token,
+            "bytes_per_step": per_layer * shape.n_linear, "us_per_step": round(us, 1),
+            "launches_per_step": prof["la_scan"][0] // steps_p}
+
+
+READOUT_STRESS_Q, READOUT_STRESS_K = 4096, 10
+
+
+def readout_stress_leg(shape, stream, reps=20):
+    """The decision readout at a declared stress shape (4,096 questions x 10
+    options on the model's width and vocabulary), where it moves enough
+    bytes to be measured against HBM bandwidth: the real readouts read under
+    1 MB and are latency-bound.  Bytes: each question's fp32 row, its
+    options' bf16 embedding rows and the final-norm gains."""
+    import numpy as np
+    import torch
+
+    from prefill_only_decision_amd import binding as B
+
+    Q, K, d, V = READOUT_STRESS_Q, READOUT_STRESS_K, shape.d_model, shape.vocab
+    rng = np.random.default_rng(12)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    E = (torch.randn(V, d, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    x = torch.randn(Q, d, device="cuda", generator=g)
+    wf = torch.ones(d, device="cuda")
+    rows = torch.arange(Q, dtype=torch.int32, device="cuda")
+    offs = torch.arange(0, Q * K + 1, K, dtype=torch.int32, device="cuda")
+    ids = np.concatenate([rng.choice(V, K, replace=False) for _ in range(Q)]).astype(np.int32)
+    ids = torch.from_numpy(ids).cuda()
+    qt = torch.zeros(Q, dtype=torch.uint8, device="cuda")
+    probs = torch.empty(Q * K, dtype=torch.float32, device="cuda")
+    dec = torch.empty((Q, 6), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+
+    def run():
+        B.readout(B.S1_BF16, x.data_ptr(), d, wf.data_ptr(), 1e-6, E.data_ptr(), Q, rows.data_ptr(),
+                  offs.data_ptr(), ids.data_ptr(), qt.data_ptr(), probs.data_ptr(), dec.data_ptr(), sp)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = Q * d * 4 + Q * K * d * 2 + d * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del E, x
+    torch.cuda.empty_cache()
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "questions": Q, "options_per_question": K,
+            "bytes_per_launch": nbytes, "us_per_launch": round(us, 2)}
+
+
 SERVE_BUCKETS = tuple(range(256, 2049, 128))   # length buckets, 128 tokens apart
 
 
@@ -301,6 +374,8 @@ def main():
                     help="skip the request-replay leg (length-bucket graphs, concurrency 1 / 8 / 16)")
     ap.add_argument("--no-features", action="store_true",
                     help="skip the full-vocabulary log-prob feature leg")
+    ap.add_argument("--no-readout-stress", action="store_true",
+                    help="skip the readout at the declared stress shape (4,096 questions x 10 options)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB elementwise copy kernel (for scaling HBM counters)")
     args = ap.parse_args()
@@ -388,6 +463,8 @@ def main():
                 "us_per_launch": round(avg_us, 2),
                 "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1)}
 
+    scan = scan_roofline(shape, batch, tokens, prof, steps_p)
+
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -401,7 +478,7 @@ def main():
         "ms_per_step_eager_launches": round(ms_eager, 4),
         "ms_per_step_row_invariant": round(ms_invariant, 4),
         "load_s": round(t_load, 2), "weight_gen_s": round(t_gen, 2),
-        "kernels": kernels, "roofline": roofline,
+        "kernels": kernels, "roofline": roofline, "scan": scan,
     }
     plan.free()
     if not args.no_features:
@@ -409,6 +486,8 @@ def main():
     if not args.no_serve and shape.dtype == "bf16":
         out["serving"] = serve_leg(model, shape, stream)
     model.free()
+    if not args.no_readout_stress and shape.dtype == "bf16":
+        out["readout_stress"] = readout_stress_leg(shape, stream)
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

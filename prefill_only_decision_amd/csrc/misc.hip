@@ -114,6 +114,15 @@ struct Decision {
 // (cross-lane reduction), then softmax and answer fields on wave 0.
 // (Cua-S1 issue, first plan comment: softmax over the option logits at one
 // position; sys1rust README "Try it": the answer fields.)
+// Dot product of eight bf16 values (one 16-byte chunk) with h[0..7] (fp32, LDS).
+__device__ __forceinline__ float dot8_bf16(uint4 u, const float* h) {
+  const float4 h0 = *reinterpret_cast<const float4*>(h), h1 = *reinterpret_cast<const float4*>(h + 4);
+  return __uint_as_float(u.x << 16) * h0.x + __uint_as_float(u.x & 0xFFFF0000u) * h0.y +
+         __uint_as_float(u.y << 16) * h0.z + __uint_as_float(u.y & 0xFFFF0000u) * h0.w +
+         __uint_as_float(u.z << 16) * h1.x + __uint_as_float(u.z & 0xFFFF0000u) * h1.y +
+         __uint_as_float(u.w << 16) * h1.z + __uint_as_float(u.w & 0xFFFF0000u) * h1.w;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 readout_kernel(const float* __restrict__ x, int d, const float* __restrict__ w, float eps,
@@ -142,16 +151,29 @@ readout_kernel(const float* __restrict__ x, int d, const float* __restrict__ w, 
   for (int k = wave; k < K; k += 4) {
     const T* e = E + (long long)ids[o0 + k] * d;
     float acc = 0.f;
-    for (int i = lane * 4; i < d; i += 256) {
-      float4 ev;
-      if constexpr (sizeof(T) == 2) {
-        const uint2 u = *reinterpret_cast<const uint2*>(e + i);
-        ev = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-      } else {
-        ev = *reinterpret_cast<const float4*>(e + i);
+    if (sizeof(T) == 2 && d % 8 == 0) {
+      // 16 bytes (8 values) per lane and load, four loads in flight
+      int i = lane * 8;
+      for (; i + 3 * 512 < d; i += 4 * 512) {
+        uint4 u[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) u[t] = *reinterpret_cast<const uint4*>(e + i + t * 512);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc += dot8_bf16(u[t], h + i + t * 512);
       }
-      acc += ev.x * h[i] + ev.y * h[i + 1] + ev.z * h[i + 2] + ev.w * h[i + 3];
+      for (; i < d; i += 512) acc += dot8_bf16(*reinterpret_cast<const uint4*>(e + i), h + i);
+    } else {
+      for (int i = lane * 4; i < d; i += 256) {
+        float4 ev;
+        if constexpr (sizeof(T) == 2) {
+          const uint2 u = *reinterpret_cast<const uint2*>(e + i);
+          ev = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+        } else {
+          ev = *reinterpret_cast<const float4*>(e + i);
+        }
+        acc += ev.x * h[i] + ev.y * h[i + 1] + ev.z * h[i + 2] + ev.w * h[i + 3];
+      }
     }
     acc = wave_sum(acc);
     if (lane == 0) z[k] = acc;

@@ -365,11 +365,14 @@ def test_attention_f32():
     assert _attn_case(B.S1_F32, 4, 4, 64, [(1, 0), (70, 0), (20, 30)], seed=3) < 1e-5
 
 
-@pytest.mark.parametrize("dtype", [B.S1_BF16, B.S1_F32])
-def test_readout(dtype):
+@pytest.mark.parametrize("dtype,d", [(B.S1_BF16, 2560), (B.S1_F32, 2560), (B.S1_BF16, 2568), (B.S1_BF16, 260)])
+def test_readout(dtype, d):
+    """Widths that are whole 16-byte chunks of bf16 (2560 = 5 x 512 values,
+    2568 with a ragged last pass) take the wide-load option loop; 260 the
+    8-byte one."""
     torch = require_gpu()
-    rng = np.random.default_rng(31 + dtype)
-    d, V, R = 2560, 1000, 20
+    rng = np.random.default_rng(31 + dtype + d)
+    V, R = 1000, 20
     x = (rng.standard_normal((R, d)) * 5).astype(np.float32)
     w = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
     if dtype == B.S1_BF16:
