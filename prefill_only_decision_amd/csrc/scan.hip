@@ -68,11 +68,48 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     ? states[(((long long)sq.s_in * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl]
                     : 0.f;
 
+  // Each chunk's global loads (rows past its end read its last row, in
+  // bounds, and are replaced by zeros at the LDS stores).  Four-wave
+  // workgroups issue them right after the previous chunk's LDS stores, so
+  // that they are in flight while that chunk is multiplied; with fewer waves
+  // each thread holds too many of them to keep them across the products.
+  constexpr bool PREFETCH = NW == 4;
+  constexpr int QI = C * 16 / NT, KI = C * 8 / NT, VI = (C / 2) * (DVG / 8) / NT;
+  uint4 qv[MODE != MODE_SUMMARY ? QI : 1], kav[KI], kbv[KI], vav[VI], vbv[VI];
+  float lgv = 0.f;
+  auto load_chunk = [&](int cc) {
+    const int nn = min(C, sq.len - cc);   // >= 1
+    const long long bb = (long long)sq.row0 + cc;
+    lgv = lane < nn ? lg[(bb + lane) * ldg + h] : 0.f;
+    if constexpr (MODE != MODE_SUMMARY) {
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int c = tid + NT * i, s = c >> 4, ch = c & 15;
+        qv[i] = *reinterpret_cast<const uint4*>(q + (bb + min(s, nn - 1)) * ldqkv + h * DK + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int c = tid + NT * i, p = c >> 4, ch = c & 15;
+      kav[i] = *reinterpret_cast<const uint4*>(k + (bb + min(2 * p, nn - 1)) * ldqkv + h * DK + ch * 8);
+      kbv[i] = *reinterpret_cast<const uint4*>(k + (bb + min(2 * p + 1, nn - 1)) * ldqkv + h * DK + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8);
+      const long long col = (long long)h * DV + dvw + ch * 8;
+      vav[i] = *reinterpret_cast<const uint4*>(v + (bb + min(2 * p, nn - 1)) * ldqkv + col);
+      vbv[i] = *reinterpret_cast<const uint4*>(v + (bb + min(2 * p + 1, nn - 1)) * ldqkv + col);
+    }
+  };
+  if (PREFETCH && sq.len > 0) load_chunk(0);
+
   for (int c0 = 0; c0 < sq.len; c0 += C) {
+    if constexpr (!PREFETCH) load_chunk(c0);
     const int n = min(C, sq.len - c0);
     const long long base = (long long)sq.row0 + c0;
     // chunk-local cumulative log-gate, redundantly in every wave
-    float G = lane < n ? lg[(base + lane) * ldg + h] : 0.f;
+    float G = lgv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float t = __shfl_up(G, off, 64);
@@ -84,30 +121,6 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();                      // previous chunk's reads of LDS are done
     if (wave == 0) sG[lane] = G;
     if (MODE == MODE_SUMMARY && tid == 0 && dvg == 0) gamma[(long long)seq * H + h] = Glast;
-    // every global load of the chunk first (rows past its end read its last
-    // row, in bounds, and are replaced by zeros), then the LDS stores
-    constexpr int QI = C * 16 / NT, KI = C * 8 / NT, VI = (C / 2) * (DVG / 8) / NT;
-    uint4 qv[MODE != MODE_SUMMARY ? QI : 1], kav[KI], kbv[KI], vav[VI], vbv[VI];
-    if constexpr (MODE != MODE_SUMMARY) {
-#pragma unroll
-      for (int i = 0; i < QI; ++i) {
-        const int c = tid + NT * i, s = c >> 4, ch = c & 15;
-        qv[i] = *reinterpret_cast<const uint4*>(q + (base + min(s, n - 1)) * ldqkv + h * DK + ch * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int c = tid + NT * i, p = c >> 4, ch = c & 15;
-      kav[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p, n - 1)) * ldqkv + h * DK + ch * 8);
-      kbv[i] = *reinterpret_cast<const uint4*>(k + (base + min(2 * p + 1, n - 1)) * ldqkv + h * DK + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8);
-      const long long col = (long long)h * DV + dvw + ch * 8;
-      vav[i] = *reinterpret_cast<const uint4*>(v + (base + min(2 * p, n - 1)) * ldqkv + col);
-      vbv[i] = *reinterpret_cast<const uint4*>(v + (base + min(2 * p + 1, n - 1)) * ldqkv + col);
-    }
     // Q rows: straight copy
     if constexpr (MODE != MODE_SUMMARY) {
 #pragma unroll
@@ -155,6 +168,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         *reinterpret_cast<uint32_t*>(sVt + (d0 + 1) * TP + 4 * p) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
       }
     }
+    if (PREFETCH && c0 + C < sq.len) load_chunk(c0 + C);
     __syncthreads();
 
     const char* vrow = sVt + (wave * 32 + cl) * TP;
