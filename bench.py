@@ -159,6 +159,58 @@ def scan_roofline(shape, batch, tokens, prof, steps_p):
             "launches_per_step": prof["la_scan"][0] // steps_p}
 
 
+def measure_peaks(stream, reps=5):
+    """Achievable peaks on this GPU, in the same job: a register-resident
+    bf16 matrix-instruction loop (two four-wave workgroups per CU, eight
+    independent accumulators per wave) and a 1 GiB streaming copy (bytes
+    read + bytes written over the time)."""
+    import torch
+
+    from prefill_only_decision_amd import binding as B
+
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sp = stream.cuda_stream
+    seed = torch.randint(-2 ** 15, 2 ** 15, (1024,), dtype=torch.int16, device="cuda")
+    seed = torch.where((seed & 0x7F80) == 0x7F80, seed & ~0x4000, seed)   # no inf / nan patterns
+    blocks, iters = 2 * n_cu, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t = timed(lambda: B.mfma_peak(seed.data_ptr(), blocks, iters, out.data_ptr(), sp))
+    flops = blocks * 4 * 8 * iters * 2 * 32 * 32 * 16
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    tc = timed(lambda: B.stream_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, sp))
+    sink = torch.empty(1024, dtype=torch.int32, device="cuda")
+    tr = timed(lambda: B.stream_read(src.data_ptr(), COPY_BYTES, sink.data_ptr(), sp))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(flops / t / 1e12, 1), "hbm_copy_gbs": round(2 * COPY_BYTES / tc / 1e9, 1),
+            "hbm_read_gbs": round(COPY_BYTES / tr / 1e9, 1),
+            "mfma_probe": f"{blocks} workgroups x 4 waves x 8 x {iters} v_mfma_f32_32x32x16_bf16 on registers",
+            "copy_probe": f"{COPY_BYTES} bytes read + written, 16-byte non-temporal accesses",
+            "read_probe": f"{COPY_BYTES} bytes read, same accesses", "cus": n_cu}
+
+
+def add_measured_fraction(obj, peaks, key):
+    """Fraction of the measured peak: the MFMA loop for MFMA-bound kernels;
+    for HBM-bound kernels (mostly reads) the faster of the copy and the
+    read-only stream."""
+    if obj and peaks:
+        peak = peaks[key] if key != "hbm" else max(peaks["hbm_copy_gbs"], peaks["hbm_read_gbs"])
+        obj["frac_of_measured_peak"] = round(obj["achieved"] / peak, 4)
+
+
 READOUT_STRESS_Q, READOUT_STRESS_K = 4096, 10
 
 
@@ -374,6 +426,8 @@ def main():
                     help="skip the request-replay leg (length-bucket graphs, concurrency 1 / 8 / 16)")
     ap.add_argument("--no-features", action="store_true",
                     help="skip the full-vocabulary log-prob feature leg")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (MFMA loop, 1 GiB copy)")
     ap.add_argument("--no-readout-stress", action="store_true",
                     help="skip the readout at the declared stress shape (4,096 questions x 10 options)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -488,6 +542,13 @@ def main():
     model.free()
     if not args.no_readout_stress and shape.dtype == "bf16":
         out["readout_stress"] = readout_stress_leg(shape, stream)
+    peaks = None if args.no_peaks else measure_peaks(stream)
+    if peaks:
+        out["peaks"] = peaks
+        add_measured_fraction(out["roofline"], peaks, "mfma_bf16_tflops")
+        add_measured_fraction(out["scan"], peaks, "hbm")
+        add_measured_fraction(out.get("readout_stress"), peaks, "hbm")
+        add_measured_fraction((out.get("features") or {}).get("vocab_lse"), peaks, "hbm")
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)

@@ -45,6 +45,22 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
 /* Number of GEMM tile configurations (host-only, no device work). */
 int s1k_gemm_tile_configs(void);
 
+/* Achievable-peak probes (not on the decision path; they state each
+ * kernel's roofline fraction against what the GPU in use delivers, beside
+ * the datasheet figures).  s1k_mfma_peak: `blocks` workgroups of four
+ * waves; each wave issues 8 * iters bf16 32x32x16 matrix instructions on
+ * register operands (2 * 32 * 32 * 16 flop each) built from seed (device,
+ * 2048 bytes, any bf16 bit patterns); out (device, blocks * 256 floats)
+ * receives per-lane sums so the work is not elided.  s1k_stream_copy: dst =
+ * src over `bytes` (a multiple of 16; device buffers of that size, not
+ * overlapping), 16-byte non-temporal accesses.  s1k_stream_read: reads
+ * `bytes` (a multiple of 16) of src with the same accesses; sink (device,
+ * 4096 bytes) is written only when a lane's xor of what it read equals a
+ * fixed pattern. */
+int s1k_mfma_peak(const void* seed, int32_t blocks, int32_t iters, float* out, void* hip_stream);
+int s1k_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream);
+int s1k_stream_read(const void* src, int64_t bytes, void* sink, void* hip_stream);
+
 /* Bytes of the fragment-order copy of a bf16 weight W[N,K] (rows padded to
  * a multiple of 32); 0 for unsupported shapes (N < 1, K not a positive
  * multiple of 16).  Host-only. */

@@ -26,6 +26,7 @@ EXPORTS = (
     "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
     "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_frag_bytes", "s1k_frag_pack", "s1k_gemm_wfrag",
+    "s1k_mfma_peak", "s1k_stream_copy", "s1k_stream_read",
     "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
     "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs", "s1k_gdn_scan",
@@ -129,6 +130,9 @@ def load_library(path=LIB_PATH):
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_gemm_tile_configs": (C.c_int, []),
         "s1k_frag_bytes": (i64, [i32, i32]),
+        "s1k_mfma_peak": (C.c_int, [vp, i32, i32, vp, vp]),
+        "s1k_stream_copy": (C.c_int, [vp, vp, i64, vp]),
+        "s1k_stream_read": (C.c_int, [vp, i64, vp, vp]),
         "s1k_frag_pack": (C.c_int, [vp, i32, i32, i32, vp, vp]),
         "s1k_gemm_wfrag": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_rmsnorm": (C.c_int, [i32, vp, vp, vp, i32, i32, f32, vp]),
@@ -427,6 +431,18 @@ def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
 
 def gemm_tile_configs():
     return load_library().s1k_gemm_tile_configs()
+
+
+def mfma_peak(seed, blocks, iters, out, stream=None):
+    return _k("s1k_mfma_peak", C.c_void_p(seed), blocks, iters, C.c_void_p(out), _stream(stream))
+
+
+def stream_copy(src, dst, nbytes, stream=None):
+    return _k("s1k_stream_copy", C.c_void_p(src), C.c_void_p(dst), nbytes, _stream(stream))
+
+
+def stream_read(src, nbytes, sink, stream=None):
+    return _k("s1k_stream_read", C.c_void_p(src), nbytes, C.c_void_p(sink), _stream(stream))
 
 
 def frag_bytes(N, K):

@@ -386,6 +386,21 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
 
 int s1k_gemm_tile_configs(void) { return gemm_tile_configs(); }
 
+int s1k_mfma_peak(const void* seed, int32_t blocks, int32_t iters, float* out, void* hip_stream) {
+  if (!seed || !out || blocks < 1 || iters < 1) return set_error(S1_EINVAL, "s1k_mfma_peak: unsupported arguments");
+  return dev_status(launch_mfma_peak(seed, blocks, iters, out, strm(hip_stream)), "s1k_mfma_peak");
+}
+
+int s1k_stream_copy(const void* src, void* dst, int64_t bytes, void* hip_stream) {
+  if (!src || !dst || bytes < 0 || bytes % 16) return set_error(S1_EINVAL, "s1k_stream_copy: unsupported arguments");
+  return dev_status(launch_stream_copy(src, dst, bytes, strm(hip_stream)), "s1k_stream_copy");
+}
+
+int s1k_stream_read(const void* src, int64_t bytes, void* sink, void* hip_stream) {
+  if (!src || !sink || bytes < 0 || bytes % 16) return set_error(S1_EINVAL, "s1k_stream_read: unsupported arguments");
+  return dev_status(launch_stream_read(src, bytes, sink, strm(hip_stream)), "s1k_stream_read");
+}
+
 int64_t s1k_frag_bytes(int32_t N, int32_t K) {
   if (N < 1 || K < 16 || K % 16) return 0;
   return (int64_t)frag_bytes(N, K);

@@ -73,6 +73,16 @@ int gemm_tile_configs();
 // The K tile (elements) of the register-staged GEMM for the element type.
 int gemm_k_tile(bool bf16);
 
+// --------------------------------------------------- achievable peaks
+// blocks workgroups of four waves, each wave 8 * iters bf16 32x32x16 matrix
+// instructions on registers (out: blocks * 256 floats); a copy of `bytes`
+// (multiple of 16) from src to dst, non-temporal.
+hipError_t launch_mfma_peak(const void* seed, int blocks, int iters, float* out, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, long long bytes, hipStream_t s);
+// Reads `bytes` (multiple of 16) of src; sink: 4096 bytes, written only when
+// a lane's xor of what it read equals a fixed pattern.
+hipError_t launch_stream_read(const void* src, long long bytes, void* sink, hipStream_t s);
+
 // ------------------------------------------------------------ elementwise
 hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
                         hipStream_t s);

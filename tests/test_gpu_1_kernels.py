@@ -450,3 +450,27 @@ def test_gdn_scan_bf16(H, lens, init):
         worst_s = max(worst_s, rel_l2(sf[i], rs))
     log(f"  rel L2 o vs rounded oracle {worst_o:.2e}, state {worst_s:.2e}")
     assert worst_o < 1e-3 and worst_s < 1e-5
+
+
+def test_peak_probes():
+    """The achievable-peak probes behind the benchmark's measured fractions:
+    the copy is exact (ragged length: past the last full group of four
+    accesses per thread), the read leaves the sink untouched for data whose
+    xor misses its pattern, and the matrix loop equals iters x 8 products of
+    its operands on every lane of a tile."""
+    torch = require_gpu()
+    nbytes = (1 << 20) + 48
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    B.stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream_ptr())
+    sink = torch.full((1024,), 7, dtype=torch.int32, device="cuda")
+    B.stream_read(src.data_ptr(), nbytes, sink.data_ptr(), stream_ptr())
+    # seed: A = all ones, B = all ones (bf16 0x3F80): each 32x32x16 product adds 16
+    seed = torch.full((1024,), 0x3F80, dtype=torch.int16, device="cuda")
+    out = torch.empty(2 * 256, dtype=torch.float32, device="cuda")
+    B.mfma_peak(seed.data_ptr(), 2, 3, out.data_ptr(), stream_ptr())
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert (sink == 7).all()
+    # every lane sums 8 accumulators x 16 rows, each 3 x 16
+    assert (out == 8 * 16 * 3 * 16).all()
