@@ -386,10 +386,13 @@ hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int 
   const auto* kk = reinterpret_cast<const bf16_t*>(k);
   const auto* vv = reinterpret_cast<const bf16_t*>(v);
   auto* oo = reinterpret_cast<bf16_t*>(o);
-  // four waves per (chunk, head), one per 32 value columns, sharing the
-  // chunk's Q / K / K^T tiles (measured faster than one-wave workgroups that
-  // each stage them, also at 8 chunks x 16 heads)
-  const int nw = 4;
+  // one wave per 32 value columns; the waves of a workgroup share the
+  // chunk's Q / K / K^T tiles.  Four waves per (chunk, head) when there are
+  // enough (chunk, head) pairs to fill the chip; below that two workgroups of
+  // two waves each (8 chunks x 16 heads: 29.8 against 31.0 us per layer for
+  // the three launches; one-wave workgroups, which each stage the tiles,
+  // 35.1 us)
+  const int nw = (long long)n_chunks * H >= 256 ? 4 : 2;
   hipError_t e = launch_mode<MODE_SUMMARY>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates,
                                            H, gamma, nw, s);
   if (e != hipSuccess) return e;
