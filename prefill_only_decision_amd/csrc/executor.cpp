@@ -826,7 +826,7 @@ int max_split(const Model* m, const Plan* p, int M) {
   return M <= m->split_max_rows ? 4 : 1;
 }
 
-int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
+int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s) {
   const s1_config& c = m->cfg;
   const int d = c.d_model, H = c.la_heads, dk = c.la_dk, dv = c.la_dv;
   const int Hq = c.fa_q_heads, Hkv = c.fa_kv_heads, hd = c.fa_head_dim;
@@ -838,7 +838,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, hipStream_t s) {
   char* qkv = static_cast<char*>(m->qkv);
   char* att = static_cast<char*>(m->att);
   const long long kvld = (long long)Hkv * hd;
-  bool xn_ready = false;   // xn already holds this layer's normalised input
+  bool xn_ready = xn_first;   // xn already holds this layer's normalised input
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     if (!xn_ready) {
@@ -982,7 +982,14 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
   const s1_config& c = m->cfg;
   if (p->T == 0) return S1_OK;
   if (m->prof) m->prof->begin(s);
-  S1_TRY(launch_embed(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, s), "embedding");
+  // the gather writes the first layer's normalised input too when the row fits the fused kernel
+  const bool fused = c.n_layers > 0 && c.d_model % 4 == 0 && c.d_model <= 16384;
+  if (fused)
+    S1_TRY(launch_embed_norm(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, m->layers[0].attn_norm, m->xn,
+                             c.rms_eps, s),
+           "embedding and first norm");
+  else
+    S1_TRY(launch_embed(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, s), "embedding");
   MARK(KC_EMBED);
   for (int ps = 0; ps < p->n_passes; ++ps)
     if (p->pass[ps].n_cap)
@@ -990,7 +997,7 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
                                 p->pass[ps].n_cap, p->cap_out, s),
              "capture");
   for (int ps = 0; ps < p->n_passes; ++ps) {
-    const int rc = run_pass(m, p, p->pass[ps], s);
+    const int rc = run_pass(m, p, p->pass[ps], fused, s);
     if (rc) return rc;
   }
   if (p->Q > 0)

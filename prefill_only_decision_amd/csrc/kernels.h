@@ -88,6 +88,10 @@ hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, 
                         hipStream_t s);
 hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
                           float eps, hipStream_t s);
+// x = E[ids] (fp32) and xn = RMSNorm(x) * w (elem), T rows of width d
+// (d % 4 == 0, d <= 16384; else hipErrorInvalidValue).
+hipError_t launch_embed_norm(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
+                             const float* w, void* xn, float eps, hipStream_t s);
 // out[dst_row(o)] = W[o] + scale * B[o] A ; row_map may be NULL (identity);
 // dst rows are out_ld elements apart.  W, A, B may be fp32 or bf16 (same as
 // out); A == NULL means no adapter.

@@ -54,6 +54,38 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, out + row * d);
 }
 
+// Embedding gather fused with the first layer's input RMSNorm: x[t] =
+// E[ids[t]] (fp32) and xn[t] = RMSNorm(x[t]) * w, one workgroup of 256
+// threads per row, the row in registers (the same arithmetic as
+// rmsnorm_kernel on the gathered row).
+template <typename T>
+__global__ void __launch_bounds__(256) embed_norm_kernel(const int32_t* __restrict__ ids, const T* __restrict__ E,
+                                                         float* __restrict__ x, int d, const float* __restrict__ w,
+                                                         T* __restrict__ xn, float eps) {
+  __shared__ float red[4];
+  const long long row = blockIdx.x;
+  const T* src = E + (long long)ids[row] * d;
+  float* dst = x + row * d;
+  float4 v[RMS_MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < RMS_MAXV; ++k) {
+    const int c = (k * 256 + (int)threadIdx.x) * 4;
+    if (c >= d) break;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(src + c);
+      v[k] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    } else {
+      v[k] = *reinterpret_cast<const float4*>(src + c);
+    }
+    *reinterpret_cast<float4*>(dst + c) = v[k];
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+  }
+  ss = block_sum<4>(ss, red);
+  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, xn + row * d);
+}
+
 // ---------------------------------------------------------------- merge
 // out[map(o)] = W[o] + scale * (B[o] . A[:, i]); fp32 arithmetic, one rounding.
 template <typename T>
@@ -234,6 +266,19 @@ hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, 
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(T), dim3(256), 0, s, ids,
                        reinterpret_cast<const float*>(E), x, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
+                            const float* w, void* xn, float eps, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d % 4 || d > 4 * 256 * RMS_MAXV) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL(embed_norm_kernel<bf16_t>, dim3(T), dim3(256), 0, s, ids,
+                       reinterpret_cast<const bf16_t*>(E), x, d, w, reinterpret_cast<bf16_t*>(xn), eps);
+  else
+    hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(T), dim3(256), 0, s, ids,
+                       reinterpret_cast<const float*>(E), x, d, w, reinterpret_cast<float*>(xn), eps);
   return hipGetLastError();
 }
 
