@@ -55,6 +55,31 @@ def test_gemm_config_count_and_validation(lib):
         assert e.value.code == -1   # S1_EINVAL
 
 
+def test_frag_bytes_and_packed_gemm_validation(lib):
+    # the fragment-order copy pads rows to whole 32-row blocks: 1 KB per
+    # block and 16-column step
+    assert s1.binding.frag_bytes(19456, 2560) == 19456 * 2560 * 2
+    assert s1.binding.frag_bytes(6160, 2560) == 6176 * 2560 * 2
+    assert s1.binding.frag_bytes(1, 16) == 32 * 16 * 2
+    for n, k in ((0, 64), (64, 0), (64, 8), (64, 24)):
+        assert s1.binding.frag_bytes(n, k) == 0
+    # shapes the weight-direct GEMM does not take are rejected on the host
+    bad = [dict(M=4, N=64, K=32), dict(M=4, N=64, K=100), dict(M=4, N=96, K=64, swiglu=True),
+           dict(M=4, N=64, K=64, tile=0), dict(M=4, N=64, K=64, tile=4), dict(M=-1, N=64, K=64)]
+    for kw in bad:
+        with pytest.raises(s1.binding.S1Error) as e:
+            s1.binding.gemm_wfrag(16, 16, 16, **kw)
+        assert e.value.code == -1, kw
+    with pytest.raises(s1.binding.S1Error):
+        s1.binding.frag_pack(16, 96, 64, True, 16)     # gate/up packing needs N % 64 == 0
+    for args in ((16, 0, 16), (16, 32, 8), (16, 32, -16)):   # null destination, ragged, negative
+        with pytest.raises(s1.binding.S1Error) as e:
+            s1.binding.stream_copy(*args)
+        assert e.value.code == -1, args
+    with pytest.raises(s1.binding.S1Error):
+        s1.binding.mfma_peak(16, 0, 1, 16)
+
+
 def _cfg(name="4b-single-512", **kw):
     return s1.make_config(shape_of(name), **kw)
 
