@@ -769,6 +769,48 @@ __device__ __forceinline__ void epilogue_swiglu16(const GemmArgs& g, floatx16 (&
   }
 }
 
+// The same SwiGLU outputs staged through LDS (free once the main loop has
+// drained) and written as whole 16-byte chunks of each output row: a tile's
+// BN / 2 features of one row are contiguous in the output.  Needs ld0 and
+// n_valid multiples of 8 and the tile's first feature 16-byte aligned.
+template <typename S>
+__device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx16 (&acc)[S::TM][S::TN], int m0,
+                                                      int n0, int wave, int lane, char* smem) {
+  constexpr int FT = S::BN / 2;                   // features per tile
+  constexpr int PITCH = FT * 2 + 16;              // bytes per staged row
+  constexpr int CPR = FT * 2 / 16;                // 16-byte chunks per row
+  static_assert(S::BM * PITCH <= S::NS * S::STAGE, "staging must fit the operand stages");
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const int cl = lane & 31;
+  const bool gate_lane = cl < 16;
+  __syncthreads();                                // every wave is done reading the stages
+#pragma unroll
+  for (int j = 0; j < S::TN; ++j) {
+    const int fl = wave * (S::WTN / 2) + 16 * j + (cl & 15);
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
+        const float got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(gate_lane ? a1 : a0), 0x401F));
+        const float gt = gate_lane ? a0 : got, up = gate_lane ? got : a1;
+        const int rl = 32 * i + acc_row(2 * k + (gate_lane ? 0 : 1), lane);
+        *reinterpret_cast<bf16_t*>(smem + rl * PITCH + 2 * fl) = f2bf(silu(gt) * up);
+      }
+    }
+  }
+  __syncthreads();
+  const int f0 = n0 >> 1;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < S::BM * CPR; c += S::NT) {
+    const int rl = c / CPR, ch = c % CPR;
+    const int row = m0 + rl, f = f0 + ch * 8;
+    if (row < g.M && f < g.n_valid)
+      *reinterpret_cast<gmem<u32x4v>*>(gptr<bf16_t>(g.out0) + (long long)row * g.ld0 + f) =
+          *reinterpret_cast<const u32x4v*>(smem + rl * PITCH + ch * 16);
+  }
+}
+
 template <typename S, int EPI>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wd_kernel(GemmArgs g) {
@@ -883,8 +925,12 @@ gemm_wd_kernel(GemmArgs g) {
     if (kt0 + d < nk) tile(kt0 + d, d);
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  if constexpr (EPI == EPI_SWIGLU)
-    epilogue_swiglu16<S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane);
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (e.ld0 % 8 == 0 && e.n_valid % 8 == 0)
+      epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
+    else
+      epilogue_swiglu16<S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane);
+  }
   else
     epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
 }
