@@ -815,7 +815,7 @@ namespace {
 // 1,659 us for the LDS-staged 256 x 256 tiles; 27B shape at 1,024 rows
 // 359 us (128 x 384) against 435 us.
 int gate_up_direct(const Model* m, const LayerW& L, int T) {
-  if (!L.w_gu_frag || T <= 0) return 0;
+  if (!L.w_gu_frag || T <= 0 || m->cfg.ffn % 8) return 0;   // SwiGLU rows written in 16-byte chunks
   const long long w1 = (gemm_wd_tiles(1, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
   const long long w2 = (gemm_wd_tiles(2, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
   return 11 * w2 < 10 * w1 ? 2 : 1;

@@ -739,40 +739,11 @@ struct WD {
 // and lane c + 16 its up partner, for the same 16 rows.  For each pair of
 // accumulator rows (2k, 2k + 1) one exchange between the two lanes gives the
 // gate lane the up value of row 2k and the up lane the gate value of row
-// 2k + 1, so that every lane computes and stores one output.
-template <int TM, int TN>
-__device__ __forceinline__ void epilogue_swiglu16(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0, int cn0,
-                                                  int lane) {
-  const int cl = lane & 31;
-  const bool gate_lane = cl < 16;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int cb = cn0 + 32 * j;
-    if (cb >= g.N) continue;
-    const int f = (cb >> 1) + (cl & 15);
-    const bool fok = f < g.n_valid;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int rb = rm0 + 32 * i;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
-        // lane ^ 16 inside each half-wave: ds_swizzle bit mode, and 0x1F, xor 0x10
-        const float got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(gate_lane ? a1 : a0), 0x401F));
-        const float gt = gate_lane ? a0 : got, up = gate_lane ? got : a1;
-        const int row = rb + acc_row(2 * k + (gate_lane ? 0 : 1), lane);
-        if (fok && row < g.M) gptr<bf16_t>(g.out0)[(long long)row * g.ld0 + f] = f2bf(silu(gt) * up);
-      }
-      // one 32 x 32 tile at a time: bounds the values in flight
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
-// The same SwiGLU outputs staged through LDS (free once the main loop has
-// drained) and written as whole 16-byte chunks of each output row: a tile's
-// BN / 2 features of one row are contiguous in the output.  Needs ld0 and
-// n_valid multiples of 8 and the tile's first feature 16-byte aligned.
+// 2k + 1, so that every lane computes one output.  The outputs are staged
+// through LDS (free once the main loop has drained) and written as whole
+// 16-byte chunks of each output row: a tile's BN / 2 features of one row are
+// contiguous in the output.  Needs ld0 and n_valid multiples of 8 (the host
+// checks) and the tile's first feature 16-byte aligned.
 template <typename S>
 __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx16 (&acc)[S::TM][S::TN], int m0,
                                                       int n0, int wave, int lane, char* smem) {
@@ -925,12 +896,8 @@ gemm_wd_kernel(GemmArgs g) {
     if (kt0 + d < nk) tile(kt0 + d, d);
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  if constexpr (EPI == EPI_SWIGLU) {
-    if (e.ld0 % 8 == 0 && e.n_valid % 8 == 0)
-      epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
-    else
-      epilogue_swiglu16<S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane);
-  }
+  if constexpr (EPI == EPI_SWIGLU)
+    epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
   else
     epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
 }
@@ -1219,8 +1186,9 @@ hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void
 
 bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
   const long long abytes = (long long)a.M * a.lda * 2;
-  return (epi == EPI_F32 || epi == EPI_RESID || epi == EPI_GATE || epi == EPI_SWIGLU) && a.K >= 64 &&
-         a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
+  return (epi == EPI_F32 || epi == EPI_RESID || epi == EPI_GATE ||
+          (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) &&
+         a.K >= 64 && a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
 }
 
 template <typename S>
