@@ -273,7 +273,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
     }
     if ((rc = ld.projection(f + ".gate", F, d, tg & S1_LORA_GATE, L.w_gu, mg))) return rc;
     if ((rc = ld.projection(f + ".up", F, d, tg & S1_LORA_UP, L.w_gu, mu))) return rc;
-    if (m->bf16 && d % 64 == 0) {   // the weight-direct GEMM's copy (few-row passes)
+    if (m->bf16 && d % 64 == 0 && F % 8 == 0) {   // the weight-direct GEMM's copy
       L.w_gu_frag = m->alloc(frag_bytes(L.n_gu, d));
       S1_TRY(launch_frag_pack(L.w_gu, L.n_gu, d, d, true, L.w_gu_frag, s), "pack gate/up");
     }
