@@ -704,8 +704,10 @@ gemm_wide_kernel(GemmArgs g) {
 
 // ----------------------------------------------- bf16 weight-direct kernel
 // For GEMMs of a few hundred rows the weights stream from HBM once while the
-// activations stay in L2, and the LDS stages of the kernels above cap how
-// many weight bytes a CU has in flight (one 57 KB stage for 256 x 192).
+// activations stay in L2, and the launch is bound by the operand stream into
+// each CU.  Measured on MI355X at the FFN gate/up shape, LDS-DMA staging of
+// both operands (the kernels above) delivers about 33 GB/s per CU and this
+// kernel about 42 GB/s, whatever the number of active CUs.
 // Here the weight operand bypasses LDS: the weights are stored at load time
 // in fragment order (for each 32-row block and each 16-element K step, the
 // 64 lanes' 16-byte MFMA B operands as one contiguous 1 KB block), and each
@@ -1186,17 +1188,14 @@ hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void
 
 bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
   const long long abytes = (long long)a.M * a.lda * 2;
-  return (epi == EPI_F32 || epi == EPI_RESID || epi == EPI_GATE ||
-          (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) &&
-         a.K >= 64 && a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
+  return (epi == EPI_F32 || (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) && a.K >= 64 &&
+         a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
 }
 
 template <typename S>
 hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_F32: return run_wd<S, EPI_F32>(a, s);
-    case EPI_RESID: return run_wd<S, EPI_RESID>(a, s);
-    case EPI_GATE: return run_wd<S, EPI_GATE>(a, s);
     case EPI_SWIGLU: return run_wd<S, EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
