@@ -802,8 +802,6 @@ int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp,
 
 namespace {
 
-// Largest K split the workspace allows for an M-row GEMM with a d-wide
-// output (the GEMM picks the split it uses, up to this).
 // The FFN gate/up projection runs on the weight-direct GEMM.  Its launches
 // are bound by the operand stream into each CU (the same bytes per K tile
 // for both tiles, 64 KB), so the time follows the number of waves of
@@ -821,6 +819,8 @@ int gate_up_direct(const Model* m, const LayerW& L, int T) {
   return 11 * w2 < 10 * w1 ? 2 : 1;
 }
 
+// Largest K split the workspace allows for an M-row GEMM with a d-wide
+// output (the GEMM picks the split it uses, up to this).
 int max_split(const Model* m, const Plan* p, int M) {
   if (p->invariant) return 1;     // the K order of a row must not depend on M
   return M <= m->split_max_rows ? 4 : 1;
