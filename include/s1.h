@@ -136,7 +136,8 @@ typedef struct {
  *    linear-attention state, and its token j has position len(prefix) + j
  *    (RFC #114 section 4 "Branching" and section 5: encode the common prefix
  *    once; every branch starts from the same immutable snapshot).  A prefix
- *    must itself have prefix_of == -1.  Sequences never see each other
+ *    must itself have prefix_of == -1 and carries no questions (S1_EINVAL:
+ *    it is encoded once for its branches).  Sequences never see each other
  *    otherwise.
  *  Question q reads token q_marker[q] (0-based, inside sequence q_seq[q]) and
  *    has options opt_ids[opt_offsets[q] .. opt_offsets[q+1]-1], K >= 2 of
@@ -271,6 +272,22 @@ int64_t s1_plan_tokens(const s1_plan* p);
  * memory) by the next s1_plan_run calls.  n_rows = 0 switches capture off.
  */
 int s1_plan_set_capture(s1_plan* p, int32_t n_rows, const int32_t* rows, float* d_hidden);
+
+/*
+ * Layer-local inputs (a test hook for per-layer parity, RFC #114 section 6:
+ * compare the selected hidden rows of every stage).  Before layer l runs,
+ * residual-stream row rows[j] (a packed token index of the request, each
+ * listed at most once) is replaced by d_src[(l * n_rows + j) * d_model ..]
+ * (fp32, device memory, n_layers * n_rows * d_model floats) and the layer's
+ * normalised input is recomputed from the replaced stream, so that every
+ * layer runs from caller-supplied inputs instead of its predecessor's
+ * output.  Rows not listed keep the path's own values; list every row of
+ * a sequence (and of its prefix) whose outputs are compared.  With capture
+ * on, captured layer l + 1 is then layer l's output from the replaced
+ * input.  n_rows = 0 switches it off.  Errors: S1_EINVAL (NULL, range,
+ * duplicates), S1_ENOMEM, S1_EDEVICE.
+ */
+int s1_plan_set_layer_inputs(s1_plan* p, int32_t n_rows, const int32_t* rows, const float* d_src);
 
 /*
  * Full-vocabulary language-model features (RFC #114, section 4, note under

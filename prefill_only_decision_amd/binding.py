@@ -25,6 +25,7 @@ EXPORTS = (
     "s1_plan_create", "s1_plan_run", "s1_plan_free", "s1_plan_tokens", "s1_plan_set_capture",
     "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
     "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
+    "s1_plan_set_layer_inputs",
     "s1k_gemm", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_frag_bytes", "s1k_frag_pack", "s1k_gemm_wfrag",
     "s1k_mfma_peak", "s1k_stream_copy", "s1k_stream_read",
     "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
@@ -118,6 +119,7 @@ def load_library(path=LIB_PATH):
         "s1_plan_free": (None, [vp]),
         "s1_plan_tokens": (i64, [vp]),
         "s1_plan_set_capture": (C.c_int, [vp, i32, vp, vp]),
+        "s1_plan_set_layer_inputs": (C.c_int, [vp, i32, vp, vp]),
         "s1_plan_set_graph": (C.c_int, [vp, i32]),
         "s1_plan_set_invariant": (C.c_int, [vp, i32]),
         "s1_plan_create_bucket": (C.c_int, [vp, i32, i32, i32, C.POINTER(vp)]),
@@ -376,6 +378,15 @@ class Plan:
         check(load_library().s1_plan_set_capture(self.handle, len(rows),
                                                  rows.ctypes.data_as(C.c_void_p),
                                                  C.c_void_p(d_hidden_ptr)))
+
+    def set_layer_inputs(self, rows, d_src_ptr):
+        """Before every layer l, replace the residual rows `rows` (packed
+        token indices) by d_src[l, j, :] (fp32 device memory [n_layers,
+        len(rows), d_model]); empty rows switch it off."""
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        check(load_library().s1_plan_set_layer_inputs(self.handle, len(rows),
+                                                      rows.ctypes.data_as(C.c_void_p),
+                                                      C.c_void_p(d_src_ptr)))
 
     def set_features(self, rows, tokens, cand_offsets, cand_group, d_logp_ptr, d_cand_logp_ptr=0,
                      d_cand_norm_ptr=0):

@@ -101,6 +101,9 @@ int validate_batch(const s1_config* c, const s1_batch* b) {
     const std::string at = " (question " + std::to_string(j) + ")";
     const int s = b->q_seq[j];
     if (s < 0 || s >= n) return set_error(S1_EINVAL, "q_seq out of range" + at);
+    // a prefix is encoded once for its branches and answers nothing itself
+    // (its questions belong to the branches that continue it)
+    if (is_prefix[s]) return set_error(S1_EINVAL, "a question on a prefix sequence" + at);
     if (b->q_marker[j] < 0 || b->q_marker[j] >= len(s)) return set_error(S1_EINVAL, "marker outside its sequence" + at);
     if (b->q_type[j] > S1_NOUL) return set_error(S1_EINVAL, "unknown question type" + at);
     const int K = b->opt_offsets[j + 1] - b->opt_offsets[j];
@@ -207,6 +210,11 @@ int64_t s1_plan_tokens(const s1_plan* p) { return p ? p->p->T : 0; }
 int s1_plan_set_capture(s1_plan* p, int32_t n_rows, const int32_t* rows, float* d_hidden) {
   if (!p) return set_error(S1_EINVAL, "plan is NULL");
   return set_capture(p->p, n_rows, rows, d_hidden);
+}
+
+int s1_plan_set_layer_inputs(s1_plan* p, int32_t n_rows, const int32_t* rows, const float* d_src) {
+  if (!p) return set_error(S1_EINVAL, "plan is NULL");
+  return set_layer_inputs(p->p, n_rows, rows, d_src);
 }
 
 int s1_plan_set_features(s1_plan* p, const s1_features* f, float* d_logp, float* d_cand_logp,

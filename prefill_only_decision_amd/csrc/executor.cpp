@@ -89,6 +89,7 @@ Plan::~Plan() {
   drop_graph();
   if (dev) (void)hipFree(dev);
   if (cap_dev) (void)hipFree(cap_dev);
+  if (inj_dev) (void)hipFree(inj_dev);
   if (feat_dev) (void)hipFree(feat_dev);
 }
 
@@ -575,7 +576,8 @@ int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out) {
   const s1_config& c = m->cfg;
   if (T_b < 1 || Q_b < 1 || O_b < 2 || O_b < 2 * Q_b)
     return set_error(S1_EINVAL, "bucket: need tokens >= 1, questions >= 1 and options >= 2 per question");
-  if (T_b > c.max_tokens || T_b > c.max_positions || Q_b > c.max_questions)
+  if (c.vocab < 2) return set_error(S1_EINVAL, "bucket: placeholder questions need a vocabulary of >= 2 ids");
+  if (T_b > c.max_tokens || T_b > c.max_positions || Q_b > c.max_questions || O_b > (1 << 28) - 2 * Q_b)
     return set_error(S1_EBUDGET, "bucket exceeds the model's budgets");
   // a placeholder request of the bucket's shape: token 0 everywhere, every
   // question a two-way choice at row 0
@@ -587,11 +589,15 @@ int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out) {
     opt[2 * j + 1] = 1;
   }
   s1_batch b{1, cu.data(), ids.data(), nullptr, Q_b, qs.data(), qm.data(), qt.data(), off.data(), opt.data()};
+  // the option slot holds a request's O_b options plus two placeholder
+  // options for every question slot it leaves unused
+  const int cap = O_b + 2 * Q_b;
   Plan* p = nullptr;
-  const int rc = create_plan(m, &b, &p, O_b);
+  const int rc = create_plan(m, &b, &p, cap);
   if (rc) return rc;
   p->bucket = true;
   p->bucket_opts = O_b;
+  p->opts_cap = cap;
   p->max_k = c.max_options;     // the readout's LDS is sized once, at capture
   *out = p;
   return S1_OK;
@@ -628,6 +634,7 @@ int update_bucket_plan(Plan* p, const s1_batch* b) {
     }
     off[j + 1] = (int32_t)opt.size();
   }
+  if ((int)opt.size() > p->opts_cap) return set_error(S1_EBUDGET, "bucket: options exceed the plan's option slot");
   hipError_t e = hipMemcpy(p->ids, ids.data(), 4 * ids.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(p->q_row, qrow.data(), 4 * qrow.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(p->opt_off, off.data(), 4 * off.size(), hipMemcpyHostToDevice);
@@ -678,6 +685,51 @@ int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
   }
   p->n_cap = n_rows;
   p->cap_out = d_hidden;
+  return S1_OK;
+}
+
+int set_layer_inputs(Plan* p, int n_rows, const int32_t* rows, const float* d_src) {
+  p->drop_graph();
+  if (p->inj_dev) {
+    (void)hipFree(p->inj_dev);
+    p->inj_dev = nullptr;
+  }
+  p->n_inj = 0;
+  p->inj_src = nullptr;
+  for (auto& ps : p->pass) ps.n_inj = 0;
+  if (n_rows <= 0) return S1_OK;
+  if (rows == nullptr || d_src == nullptr) return set_error(S1_EINVAL, "layer-input rows or buffer is NULL");
+  std::vector<int32_t> lists[2][2];   // [pass][rows | index]
+  std::vector<char> seen(p->T, 0);
+  for (int j = 0; j < n_rows; ++j) {
+    if (rows[j] < 0 || rows[j] >= p->T) return set_error(S1_EINVAL, "layer-input row out of range");
+    if (seen[rows[j]]) return set_error(S1_EINVAL, "layer-input row listed twice");
+    seen[rows[j]] = 1;
+    const int r = p->row_of[rows[j]];
+    const int ps = p->pass_of_row[r];
+    lists[ps][0].push_back(r);
+    lists[ps][1].push_back(j);
+  }
+  if (hipMalloc(&p->inj_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
+    (void)hipGetLastError();
+    p->inj_dev = nullptr;
+    return set_error(S1_ENOMEM, "device allocation for layer inputs failed");
+  }
+  int32_t* d = static_cast<int32_t*>(p->inj_dev);
+  for (int ps = 0; ps < 2; ++ps) {
+    const int k = (int)lists[ps][0].size();
+    if (k) {
+      if (hipMemcpy(d, lists[ps][0].data(), 4 * k, hipMemcpyHostToDevice) != hipSuccess ||
+          hipMemcpy(d + k, lists[ps][1].data(), 4 * k, hipMemcpyHostToDevice) != hipSuccess)
+        return set_error(S1_EDEVICE, "copy layer-input rows");
+    }
+    p->pass[ps].inj_rows = d;
+    p->pass[ps].inj_idx = d + k;
+    p->pass[ps].n_inj = k;
+    d += 2 * k;
+  }
+  p->n_inj = n_rows;
+  p->inj_src = d_src;
   return S1_OK;
 }
 
@@ -841,6 +893,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
   bool xn_ready = xn_first;   // xn already holds this layer's normalised input
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
+    if (ps.n_inj) {   // replaced layer inputs: the rows, then their norm
+      S1_TRY(launch_gather_rows(p->inj_src + (size_t)l * p->n_inj * d, d, ps.inj_idx, ps.inj_rows, ps.n_inj,
+                                m->x, s),
+             "layer inputs");
+      xn_ready = false;
+    }
     if (!xn_ready) {
       S1_TRY(launch_rmsnorm(m->bf16, x, L.attn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
       MARK(KC_RMSNORM);
@@ -1028,7 +1086,8 @@ namespace s1 {
 // Capture the forward of a plan into a HIP graph on stream s (it must not be
 // the null stream) and replay it.  Only kernel launches are recorded.
 int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
-  if (p->gexec && (p->g_probs != d_probs || p->g_dec != d_dec || p->g_cap != p->cap_out)) p->drop_graph();
+  if (p->gexec && (p->g_probs != d_probs || p->g_dec != d_dec || p->g_cap != p->cap_out || p->g_inj != p->inj_src))
+    p->drop_graph();
   if (!p->gexec) {
     hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "begin graph capture"));
@@ -1051,6 +1110,7 @@ int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s
     p->g_probs = d_probs;
     p->g_dec = d_dec;
     p->g_cap = p->cap_out;
+    p->g_inj = p->inj_src;
   }
   const hipError_t e = hipGraphLaunch(p->gexec, s);
   if (e != hipSuccess) return set_error(S1_EDEVICE, hip_msg(e, "graph launch"));

@@ -111,6 +111,9 @@ struct PassPlan {
   int32_t* cap_rows = nullptr;  // device [n_cap]: rows captured in this pass
   int32_t* cap_dst = nullptr;   // device [n_cap]: index in the capture list
   int n_cap = 0;
+  int32_t* inj_rows = nullptr;  // device [n_inj]: rows whose layer inputs are replaced in this pass
+  int32_t* inj_idx = nullptr;   // device [n_inj]: index in the caller's row list
+  int n_inj = 0;
 };
 
 // Host form of a feature request, validated: distinct rows (internal row
@@ -147,6 +150,11 @@ struct Plan {
   int n_cap = 0;
   void* dev = nullptr;          // one device block for the arrays above
   void* cap_dev = nullptr;      // device block for capture row lists
+  // layer-input replacement (test hook): before layer l, row list entry j
+  // takes inj_src[(l * n_inj + j) * d]
+  const float* inj_src = nullptr;
+  int n_inj = 0;
+  void* inj_dev = nullptr;
   // HIP graph of the whole forward, replayed by s1_plan_run when enabled;
   // re-captured when the output or capture pointers change
   bool use_graph = false;
@@ -157,11 +165,13 @@ struct Plan {
   // bucket_opts options, refilled by update_bucket_plan between runs
   bool bucket = false;
   int bucket_opts = 0, real_T = 0, real_Q = 0;
+  int opts_cap = 0;             // option ids the device slot holds (bucket plans)
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   float* g_probs = nullptr;
   void* g_dec = nullptr;
   float* g_cap = nullptr;
+  const float* g_inj = nullptr;
   // full-vocabulary log-probability features, computed after the readout by
   // every run when set
   void* feat_dev = nullptr;     // metadata + workspace
@@ -182,6 +192,7 @@ int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out);
 int update_bucket_plan(Plan* p, const s1_batch* b);
 int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden);
+int set_layer_inputs(Plan* p, int n_rows, const int32_t* rows, const float* d_src);
 int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp, float* d_cand_norm);
 int run_plan_graph(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);
 

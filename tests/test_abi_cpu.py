@@ -128,6 +128,7 @@ def test_empty_request_is_valid():
     ("prefix_self", -1, "is invalid"),
     ("too_many_prefixes", -4, "max_prefixes"),
     ("q_seq_oob", -1, "q_seq out of range"),
+    ("question_on_prefix", -1, "a question on a prefix sequence"),
 ])
 def test_validation_errors(case, code, needle):
     cfg = _cfg("tiny-fp32", max_tokens=1024, max_options=16, max_prefixes=1)
@@ -165,6 +166,8 @@ def test_validation_errors(case, code, needle):
         b.prefix_of = np.array([-1, 1, -1], np.int32)
     elif case == "too_many_prefixes":
         b = random_batch(4096, [30, 20, 10, 5], seed=5, prefix_of=[-1, 0, -1, 2])
+    elif case == "question_on_prefix":     # sequence 0 holds two questions
+        b.prefix_of = np.array([-1, 0, -1], np.int32)
     elif case == "q_seq_oob":
         b.q_seq = b.q_seq.copy()
         b.q_seq[0] = 3
