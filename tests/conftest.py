@@ -48,20 +48,10 @@ def gpu_model_4b(weights_4b):
 
 
 @pytest.fixture(scope="session")
-def oracle_4b(weights_4b):
+def oracle_4b_exact(weights_4b):
+    """The float32 oracle of the 4B shape without activation rounding."""
     import numpy as np
     import oracle
     from s1_workloads import shape_of
-    return _get("o4b", lambda: oracle.OracleModel(shape_of("4b-single-512"), weights_4b.tensors,
-                                                   dtype=np.float32, keep_decoded=True, act="bf16"))
-
-
-@pytest.fixture(scope="session")
-def oracle_4b_exact(weights_4b, oracle_4b):
-    """The same model without activation rounding (shares decoded weights)."""
-    import copy
-    def make():
-        ox = copy.copy(oracle_4b)
-        ox.act = "exact"
-        return ox
-    return _get("o4bx", make)
+    return _get("o4bx", lambda: oracle.OracleModel(shape_of("4b-single-512"), weights_4b.tensors,
+                                                    dtype=np.float32, keep_decoded=True))

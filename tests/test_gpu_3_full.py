@@ -1,8 +1,16 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times (resident-input plans on the same model budgets).  The 4B
-single request is compared on every row of every layer; the packed and
-branched workloads on sampled sequences and rows the oracle computes one by
-one; the 27B request at its marker row and sampled rows."""
+benchmark times (resident-input plans on the same model budgets), against
+the float32 oracle without activation rounding, under the fixed gates of
+tests/parity.py (RFC #114 section 6, "Validation and acceptance"):
+  - every layer, run from the oracle's input to it, within 1e-2 relative L2
+    of the oracle's output of that layer (every row of the single requests;
+    marker rows and seeded samples of every sequence of the packed and
+    branched workloads);
+  - every question's probabilities within 0.039 of the oracle end to end
+    (the pages' bf16-against-float32 allowance), no choice flip where the
+    oracle's margin >= 0.02;
+  - end-to-end per-layer drift and the count of questions beyond 1e-2 are
+    printed (not gated: bf16 rounding amplified through depth)."""
 import time
 
 import numpy as np
@@ -11,67 +19,82 @@ import pytest
 import oracle as O
 from s1_workloads import make_batch, make_weights, shape_of
 from tests.gpu_util import log, require_gpu
-from tests.parity import compare_full_depth, oracle_rows, run_gpu, stack_ref_hidden
+from tests.parity import (DEPTH_PROB_TOL, decision_gate, end_to_end_drift, layer_local_gate, oracle_rows,
+                          ref_rows, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
 
-def test_4b_single_512(gpu_model_4b, oracle_4b, oracle_4b_exact):
+def _oracle(om, b, seqs, mode="plain"):
+    """The oracle over `seqs`, every row captured, one sequence at a time
+    (progress printed).  In continuation mode a prefix is computed once."""
+    t0 = time.time()
+    out = {"probs": {}, "fields": {}, "hidden": {}}
+    if mode == "continuation":
+        r = O.prefill_decide(om, b, mode=mode, capture={i: np.arange(int(b.seq_lens[i])) for i in seqs}, seqs=seqs)
+        log(f"  oracle, {len(seqs)} sequences ({int(sum(b.seq_lens[i] for i in seqs))} tokens): "
+            f"{time.time() - t0:.1f} s")
+        return r
+    for i in seqs:
+        r = O.prefill_decide(om, b, mode=mode, capture={i: np.arange(int(b.seq_lens[i]))}, seqs=[i])
+        for k in out:
+            out[k].update(r[k])
+        log(f"  oracle sequence {i} ({int(b.seq_lens[i])} tokens): {time.time() - t0:.1f} s")
+    return out
+
+
+def _sample(b, i, rng, n):
+    L = int(b.seq_lens[i])
+    marks = b.q_marker[b.q_seq == i].tolist()
+    return np.unique(np.concatenate([marks, rng.choice(L, min(n, L), replace=False), [0, L - 1]])).astype(int)
+
+
+def _check(model, shape, b, om, label, cap, mode="plain"):
+    seqs = sorted(cap)
+    ref = _oracle(om, b, seqs, mode)
+    probs, dec, hid = run_gpu(model, b, oracle_rows(b, cap), shape.n_layers, shape.d_model)
+    drift = end_to_end_drift(hid, ref_rows(ref, cap))
+    log(f"{label}: end-to-end rel L2 per layer (not gated) " + " ".join(f"{x:.1e}" for x in drift))
+    qs = [j for j in range(b.n_questions) if int(b.q_seq[j]) in cap]
+    res = decision_gate(b, probs, dec, ref, DEPTH_PROB_TOL, questions=qs, label=label)
+    res["layers"] = layer_local_gate(model, b, ref, seqs, cap, shape.n_layers, shape.d_model, label=label)
+    return res
+
+
+def test_4b_single_512(gpu_model_4b, oracle_4b_exact):
     shape = shape_of("4b-single-512")
     b = make_batch("4b-single-512")
-    capture = {0: np.arange(512)}
-    probs, dec, hid = run_gpu(gpu_model_4b, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
-    t0 = time.time()
-    ref = O.prefill_decide(oracle_4b, b, capture=capture)
-    log(f"oracle 4b-single-512: {time.time() - t0:.1f} s")
-    rx = O.prefill_decide(oracle_4b_exact, b, capture=capture)
-    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
-                       stack_ref_hidden(rx, capture), label="4b-single-512")
+    _check(gpu_model_4b, shape, b, oracle_4b_exact, "4b-single-512", {0: np.arange(512)})
 
 
-def test_4b_varlen_16_sampled(gpu_model_4b, oracle_4b, oracle_4b_exact):
+def test_4b_varlen_16_every_question(gpu_model_4b, oracle_4b_exact):
+    """All 16 requests: every question under the decision gate; the
+    layer-local gate on the marker rows and 16 seeded rows of every
+    sequence (every row of every sequence is replaced by the oracle's)."""
     shape = shape_of("4b-varlen-16")
     b = make_batch("4b-varlen-16")
-    sample = [9, 4, 15]          # 256, 694 and 826 tokens; 15 is the last in the pack
     rng = np.random.default_rng(3)
-    capture = {}
-    for i in sample:
-        L = int(b.seq_lens[i])
-        marks = b.q_marker[b.q_seq == i].tolist()
-        capture[i] = np.unique(np.concatenate([marks, rng.choice(L, 24, replace=False), [0, L - 1]]))
-    probs, dec, hid = run_gpu(gpu_model_4b, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
-    t0 = time.time()
-    ref = O.prefill_decide(oracle_4b, b, capture=capture, seqs=sample)
-    log(f"oracle 4b-varlen-16 (3 sequences): {time.time() - t0:.1f} s")
-    rx = O.prefill_decide(oracle_4b_exact, b, capture=capture, seqs=sample)
-    qs = [j for j in range(b.n_questions) if b.q_seq[j] in sample]
-    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
-                       stack_ref_hidden(rx, capture), questions=qs, label="4b-varlen-16 sampled")
-    # every question: a probability vector with consistent fields
-    for j in range(b.n_questions):
-        lo, hi = b.opt_offsets[j], b.opt_offsets[j + 1]
-        assert abs(probs[lo:hi].sum() - 1.0) < 1e-5 and (probs[lo:hi] >= 0).all()
+    cap = {i: _sample(b, i, rng, 16) for i in range(b.n_seqs)}
+    res = _check(gpu_model_4b, shape, b, oracle_4b_exact, "4b-varlen-16", cap)
+    assert res["questions"] == b.n_questions
 
 
-def test_4b_branch_4096x20(gpu_model_4b, oracle_4b, oracle_4b_exact):
+def test_4b_branch_4096x20(gpu_model_4b, oracle_4b_exact):
+    """The prefix and all 20 branches (every question); the oracle continues
+    each branch from the prefix's cache (equal to the plain forward of
+    prefix + branch, pinned on the CPU)."""
     shape = shape_of("4b-branch-4096x20")
     b = make_batch("4b-branch-4096x20")
-    capture = {0: np.array([0, 1, 2047, 4095])}
+    rng = np.random.default_rng(4)
+    cap = {0: np.unique(np.concatenate([[0, 1, 2047, 4095], rng.choice(4096, 60, replace=False)]))}
     for i in range(1, 21):
-        capture[i] = np.array([0, 31, 63])
-    probs, dec, hid = run_gpu(gpu_model_4b, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
-    t0 = time.time()
-    ref = O.prefill_decide(oracle_4b, b, mode="continuation", capture=capture)
-    log(f"oracle 4b-branch-4096x20: {time.time() - t0:.1f} s")
-    rx = O.prefill_decide(oracle_4b_exact, b, mode="continuation", capture=capture)
-    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
-                       stack_ref_hidden(rx, capture), label="4b-branch-4096x20")
+        cap[i] = np.array([0, 31, 63])
+    _check(gpu_model_4b, shape, b, oracle_4b_exact, "4b-branch-4096x20", cap, mode="continuation")
 
 
 def test_4b_gdn_single_512():
     """The 4B request with Gated DeltaNet linear-attention layers, every row
-    of every layer against both oracles under the full-depth gates."""
-    import copy
+    of every layer."""
     require_gpu()
     import prefill_only_decision_amd as s1
     shape = shape_of("4b-gdn-single-512")
@@ -80,18 +103,11 @@ def test_4b_gdn_single_512():
     cfg = s1.make_config(shape, max_tokens=1024, max_seqs=4, max_questions=16, max_options=64,
                          max_prefixes=1, max_positions=1024)
     model = s1.Model(cfg, w.tensors)
-    capture = {0: np.arange(512)}
-    probs, dec, hid = run_gpu(model, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
-    model.free()
-    om = O.OracleModel(shape, w.tensors, dtype=np.float32, keep_decoded=True, act="bf16")
-    t0 = time.time()
-    ref = O.prefill_decide(om, b, capture=capture)
-    log(f"oracle 4b-gdn-single-512: {time.time() - t0:.1f} s")
-    ox = copy.copy(om)
-    ox.act = "exact"
-    rx = O.prefill_decide(ox, b, capture=capture)
-    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
-                       stack_ref_hidden(rx, capture), label="4b-gdn-single-512")
+    om = O.OracleModel(shape, w.tensors, dtype=np.float32, keep_decoded=True)
+    try:
+        _check(model, shape, b, om, "4b-gdn-single-512", {0: np.arange(512)})
+    finally:
+        model.free()
 
 
 @pytest.mark.slow
@@ -107,14 +123,8 @@ def test_27b_single_1024():
     model = s1.Model(cfg, w.tensors)
     b = make_batch("27b-single-1024")
     rng = np.random.default_rng(5)
-    capture = {0: np.unique(np.concatenate([[0, 1023], rng.choice(1024, 14, replace=False)]))}
-    probs, dec, hid = run_gpu(model, b, oracle_rows(b, capture), shape.n_layers, shape.d_model)
-    model.free()
-    t0 = time.time()
-    om = O.OracleModel(shape, w.tensors, dtype=np.float32, act="bf16")
-    ref = O.prefill_decide(om, b, capture=capture)
-    log(f"oracle 27b-single-1024: {time.time() - t0:.1f} s")
-    om.act = "exact"
-    rx = O.prefill_decide(om, b, capture=capture)
-    compare_full_depth(b, probs, dec, ref, rx, hid, stack_ref_hidden(ref, capture),
-                       stack_ref_hidden(rx, capture), label="27b-single-1024")
+    om = O.OracleModel(shape, w.tensors, dtype=np.float32)
+    try:
+        _check(model, shape, b, om, "27b-single-1024", {0: _sample(b, 0, rng, 62)})
+    finally:
+        model.free()
