@@ -168,16 +168,16 @@ def test_branches_equal_plain_forward_bitwise(gpu_model_4b):
 
 def test_invariant_mode_against_oracle(gpu_model_4b, oracle_4b_exact):
     """The row-invariant schedule under the fixed gates against the float32
-    oracle: every layer from the oracle's input within 1e-2, probabilities
-    within 0.039 end to end, no choice flip where the margin >= 0.02."""
+    oracle: every layer from the oracle's input within 1e-2 and its readout
+    within 1e-2, no choice flip where the margin >= 0.02 end to end."""
     require_gpu()
     from s1_workloads import make_batch, shape_of
-    from tests.parity import DEPTH_PROB_TOL, decision_gate, layer_local_gate, run_gpu
+    from tests.parity import decision_gate, layer_local_gate, run_gpu
     shape = shape_of("4b-single-512")
     b = make_batch("4b-single-512")
     cap = {0: np.arange(512)}
     ref = O.prefill_decide(oracle_4b_exact, b, capture=cap)
     probs, dec, _ = run_gpu(gpu_model_4b, b, invariant=True)
-    decision_gate(b, probs, dec, ref, DEPTH_PROB_TOL, label="4b-single-512 row-invariant")
+    decision_gate(b, probs, dec, ref, None, label="4b-single-512 row-invariant end to end")
     layer_local_gate(gpu_model_4b, b, ref, [0], cap, shape.n_layers, shape.d_model,
                      label="4b-single-512 row-invariant", invariant=True)
