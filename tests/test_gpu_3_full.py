@@ -7,12 +7,11 @@ tests/parity.py (RFC #114 section 6, "Validation and acceptance"):
     marker rows and seeded samples of every sequence of the packed and
     branched workloads);
   - the readout of that run (last layer from the oracle's input) within
-    1e-2 of the oracle's probabilities for every compared question;
-  - end to end, no choice flip where the oracle's margin >= 0.02, for
-    every compared question;
-  - end-to-end per-layer drift and probabilities are printed with the
-    counts of questions beyond 1e-2 and 0.039 (not gated: the oracle with
-    bf16 operands drifts from the float oracle the same way)."""
+    1e-2 of the oracle's probabilities, and no choice flip where the
+    oracle's margin >= 0.02, for every compared question;
+  - end-to-end per-layer drift, probabilities and choice flips are printed
+    with the counts of questions beyond 1e-2 and 0.039 (not gated: the
+    oracle with bf16 operands drifts from the float oracle the same way)."""
 import time
 
 import numpy as np

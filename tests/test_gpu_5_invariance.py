@@ -168,8 +168,9 @@ def test_branches_equal_plain_forward_bitwise(gpu_model_4b):
 
 def test_invariant_mode_against_oracle(gpu_model_4b, oracle_4b_exact):
     """The row-invariant schedule under the fixed gates against the float32
-    oracle: every layer from the oracle's input within 1e-2 and its readout
-    within 1e-2, no choice flip where the margin >= 0.02 end to end."""
+    oracle: every layer from the oracle's input within 1e-2, its readout
+    within 1e-2 with no choice flip where the margin >= 0.02; end-to-end
+    answers printed."""
     require_gpu()
     from s1_workloads import make_batch, shape_of
     from tests.parity import decision_gate, layer_local_gate, run_gpu

@@ -2,9 +2,10 @@
 bucket, refilled with each request that fits (the graph-over-length-buckets
 fast path of the Cua-S1 issue's timing comments and RFC #114's plan).  Every
 refilled request's answers are held to the float32 oracle under the fixed
-gates of tests/parity.py (no choice flip where the oracle's margin >= 0.02
-end to end), and one request runs layer by layer from the oracle's inputs
-through the bucket's graph (1e-2 per layer and in its readout).  Under
+gates of tests/parity.py: one request runs layer by layer from the
+oracle's inputs through the bucket's graph (1e-2 per layer, its readout
+within 1e-2 and no choice flip where the oracle's margin >= 0.02); every
+request's end-to-end answers are printed against the oracle.  Under
 the row-invariant schedule a refilled bucket also answers bit for bit like a
 plan built for the request."""
 import numpy as np
