@@ -184,26 +184,54 @@ typedef struct {
 typedef struct s1_model s1_model;
 typedef struct s1_plan s1_plan;
 
-/* Copy, merge (W' = W + (alpha/r) B A, fp32 arithmetic, one rounding to the
- * model dtype) and lay out the weights on the current HIP device; allocate the
- * workspace for the budgets in cfg.  Errors: S1_EINVAL (shape, names,
- * missing tensors), S1_ENOMEM, S1_EDEVICE.  *out is set only on success. */
+/* Load a model: the executor owns the weights and device buffers from here
+ * until s1_free (RFC #114, section 2, "Ownership and serving interface").
+ * Copies the caller's tensors, merges each adapter into its projection,
+ * W' = W + (alpha/r) B A in fp32 with one rounding to the model dtype (the
+ * rank-32 / alpha-64 adapter merged into BF16 weights: RFC #114 section 1;
+ * merged at load: Cua-S1 issue #10, plan comment, step 3), lays the weights
+ * out for the kernels (gate/up interleaved, RoPE pairs permuted) and
+ * allocates the workspace for the budgets in cfg on the current HIP device.
+ * tensors: n_tensors caller-owned entries (host, or device with on_device),
+ * read during the call only.  hip_stream: the stream the copies and merges
+ * run on (NULL: the library's own).  Errors, with nothing left allocated:
+ * S1_EINVAL (config, names, shapes, dtypes, missing tensors), S1_ENOMEM,
+ * S1_EDEVICE.  *out is set only on success. */
 int s1_load_weights(const s1_config* cfg, const s1_tensor* tensors, int32_t n_tensors,
                     void* hip_stream, s1_model** out);
 
-/* Answer every question of the request.  probs[sum K] receives the option
- * probabilities in question order, out[n_questions] the answer fields; both
- * host memory.  timing may be NULL.  Synchronous: returns once the outputs
- * are written.  Includes the host-to-device copy of the request and the
- * device-to-host copy of the results. */
+/* Answer every question of the request from one prefill pass (System1-Omni
+ * README, introduction: decisions from a single forward pass, no decoding;
+ * Cua-S1 issue #10, plan comment: a softmax over the answer-option logits).
+ * Input is token ids (Cua-S1 issue #10, last comment), per-question marker
+ * positions and option-token id lists (s1_batch); the readout runs only at
+ * the marker rows (sys1rust README, "How it works") and fills the answer
+ * fields of sys1rust README "Try it" (s1_decision).  probs[sum K] receives
+ * the option probabilities in question order, out[n_questions] the fields;
+ * both host memory, caller-owned.  timing may be NULL (its wall_us covers the
+ * whole call, including the host-to-device copy of the request and the
+ * device-to-host copy of the results; device_us the device work alone).
+ * Synchronous: returns once the outputs are written.  The request is
+ * validated on the host before any device work (RFC #114 section 2:
+ * validate counts, lengths and budgets before dispatch, explicit errors):
+ * S1_EINVAL (malformed, ids out of range, K < 2, noul K != 2, a marker
+ * outside its sequence, bad prefix links, a question on a prefix), S1_EBUDGET
+ * (beyond a load-time budget), both with nothing enqueued; S1_EDEVICE after
+ * the stream has been synchronised (resource ownership kept until device work
+ * finishes, RFC #114 section 2); S1_ENOMEM.  Device memory: a block owned
+ * by the model, grown only when a request needs more than every earlier one
+ * (no allocation in the steady state).  One call per model at a time. */
 int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision* out,
                       s1_timing* timing, void* hip_stream);
 
-/* Free the model and its device memory.  NULL is a no-op.  The caller must
- * not have a call in flight on the model. */
+/* Free the model and all its device memory, after the device is idle (RFC
+ * #114 section 2: ownership until device work finishes).  NULL is a no-op.
+ * The caller must not have a call in flight on the model. */
 void s1_free(s1_model* m);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none): the explicit
+ * error of RFC #114 section 2.  The pointer stays valid until the next call
+ * on this thread. */
 const char* s1_last_error(void);
 
 /* Validate a request against a config, on the host only (no device work,

@@ -156,11 +156,34 @@ int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, co
  * kv_pre_len[i] ..); query j has position kv_pre_len[i] + j.  All five
  * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd <= 128.
  * block_rows: queries per workgroup, 0 to choose by size as the decoder
- * does; bf16 accepts 32, 64 or 128, fp32 64. */
+ * does; bf16 accepts 32, 64 or 128, fp32 64.  piece (bf16 only): 0 runs every
+ * query block over its whole key range in one workgroup; a positive multiple
+ * of 64 cuts the keys at multiples of it into pieces run by separate
+ * workgroups and merged in key order, and lets consecutive sequences that
+ * share prefix rows (same kv_pre_row0 and kv_pre_len, contiguous query rows)
+ * sweep the prefix keys once for all their queries (RFC #114 section 5:
+ * branches share one prefix snapshot); -1 chooses the piece by size as the
+ * decoder does.  Query rows of different sequences must not overlap. */
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o,
                   int32_t Hq, int32_t Hkv, int32_t hd, int32_t n_seqs, const int32_t* q_row0,
                   const int32_t* q_len, const int32_t* kv_row0, const int32_t* kv_pre_row0,
-                  const int32_t* kv_pre_len, int32_t block_rows, void* hip_stream);
+                  const int32_t* kv_pre_len, int32_t block_rows, int32_t piece, void* hip_stream);
+
+/* The launch plan s1k_attention (and the decoder) would use, on the host
+ * only (no device work; usable without a GPU), for checking its coverage.
+ * Inputs as s1k_attention (host arrays).  On return blocks[5 * i ..] =
+ * (sequence, first query, first key, key end, piece ordinal or -1) for
+ * i < *n_blocks, where sequences n_seqs .. *n_seqs_out - 1 are the shared
+ * prefix entries whose (q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len) go
+ * to shared[5 * (i - n_seqs) ..]; row_np[r - row_lo] the pieces of query
+ * row r, with row_lo the smallest query row.  Capacities: max_blocks
+ * blocks, max_shared shared entries, max_rows rows; S1_EINVAL when any is
+ * exceeded. */
+int s1k_attention_plan(int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len, const int32_t* kv_row0,
+                       const int32_t* kv_pre_row0, const int32_t* kv_pre_len, int32_t Hq, int32_t block_rows,
+                       int32_t piece, int32_t n_cu, int32_t max_blocks, int32_t* blocks, int32_t* n_blocks,
+                       int32_t max_shared, int32_t* shared, int32_t* n_seqs_out, int32_t max_rows,
+                       int32_t* row_np, int32_t* piece_out);
 
 /* Decision readout for Q questions: h = RMSNorm(x[rows[j]]; w_final),
  * z_k = h . E[opt_k], p = softmax(z) over the question's options, and the

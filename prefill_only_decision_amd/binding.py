@@ -30,7 +30,7 @@ EXPORTS = (
     "s1k_mfma_peak", "s1k_stream_copy", "s1k_stream_read",
     "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
-    "s1k_attention", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs", "s1k_gdn_scan",
+    "s1k_attention", "s1k_attention_plan", "s1k_readout", "s1k_vocab_lse", "s1k_token_logprobs", "s1k_gdn_scan",
 )
 
 
@@ -142,7 +142,9 @@ def load_library(path=LIB_PATH):
         "s1k_lora_merge": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, f32, vp]),
         "s1k_la_scan": (C.c_int, [i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
         "s1k_la_scan_chunked": (C.c_int, [vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
-        "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]),
+        "s1k_attention": (C.c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, i32, vp]),
+        "s1k_attention_plan": (C.c_int, [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32,
+                                         vp, vp]),
         "s1k_readout": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "s1k_vocab_lse": (C.c_int, [i32, vp, i32, vp, f32, vp, i32, i32, vp, vp, vp]),
         "s1k_gdn_scan": (C.c_int, [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -500,10 +502,27 @@ def la_scan_chunked(q, k, v, ld_qkv, log_g, o, T, H, cu_seqlens, s_init=None, s_
 
 
 def attention(dtype, q, k, v, o, Hq, Hkv, hd, q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len,
-              stream=None, block_rows=0):
+              stream=None, block_rows=0, piece=0):
     arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len)]
     return _k("s1k_attention", dtype, C.c_void_p(q), C.c_void_p(k), C.c_void_p(v), C.c_void_p(o),
-              Hq, Hkv, hd, len(arrs[0]), *arrs, block_rows, _stream(stream))
+              Hq, Hkv, hd, len(arrs[0]), *arrs, block_rows, piece, _stream(stream))
+
+
+def attention_plan(q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len, Hq, block_rows=128, piece=-1, n_cu=256):
+    """The attention launch plan on the host: (blocks int32 [n, 5] = (seq,
+    q0, k_lo, k_hi, part), shared-prefix entries int32 [m, 5], row pieces
+    from the smallest query row, chosen piece)."""
+    arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (q_row0, q_len, kv_row0, kv_pre_row0, kv_pre_len)]
+    n = len(arrs[0])
+    rows = int(max([r + l for r, l in zip(arrs[0], arrs[1]) if l > 0], default=0)) + 1
+    cap = 4096 + 64 * (rows + 1)
+    blocks = np.zeros((cap, 5), np.int32)
+    shared = np.zeros((max(n, 1), 5), np.int32)
+    row_np = np.zeros(max(rows, 1), np.int32)
+    nb, ns, pc = C.c_int32(), C.c_int32(), C.c_int32()
+    _k("s1k_attention_plan", n, *arrs, Hq, block_rows, piece, n_cu, cap, blocks, C.byref(nb), len(shared), shared,
+       C.byref(ns), len(row_np), row_np, C.byref(pc))
+    return blocks[:nb.value].copy(), shared[:ns.value - n].copy(), row_np, pc.value
 
 
 def readout(dtype, x, d, w_final, eps, E, Q, rows, opt_offsets, opt_ids, q_type, probs, decisions,

@@ -1,4 +1,5 @@
 // C ABI of the library: argument validation, error reporting, entry points.
+#include <algorithm>
 #include <chrono>
 #include <cstring>
 #include <string>
@@ -296,36 +297,31 @@ int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision*
   int rc = validate_batch(&m->m->cfg, b);
   if (rc) return rc;
   if (b->n_questions > 0 && (!probs || !out)) return set_error(S1_EINVAL, "output arrays are NULL");
-  hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : m->m->own_stream;
+  Model* mm = m->m;
+  hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : mm->own_stream;
+  for (hipEvent_t& e : mm->decide_ev)
+    if (!e && hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      return set_error(S1_EDEVICE, "event creation failed");
+    }
+  const int nopt = b->n_questions > 0 ? b->opt_offsets[b->n_questions] : 0;
+  const size_t pbytes = ((size_t)nopt * sizeof(float) + 15) / 16 * 16;
+  // the plan and the results share the model's reusable device block
   Plan* p = nullptr;
-  rc = create_plan(m->m, b, &p);
+  rc = create_plan(mm, b, &p, 0, true, pbytes + (size_t)b->n_questions * sizeof(s1_decision) + 16);
   if (rc) return rc;
-  const int Q = p->Q, nopt = p->total_opts;
-  void* dout = nullptr;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  double dev_us = 0.0;
-  const size_t bytes = (size_t)nopt * sizeof(float) + (size_t)Q * sizeof(s1_decision) + 16;
+  const int Q = p->Q;
   auto fail = [&](int code, const std::string& msg) {
     (void)hipStreamSynchronize(s);
-    if (dout) (void)hipFree(dout);
-    if (e0) (void)hipEventDestroy(e0);
-    if (e1) (void)hipEventDestroy(e1);
     delete p;
-    return code == S1_OK ? S1_OK : (msg.empty() ? code : set_error(code, msg));
+    return msg.empty() ? code : set_error(code, msg);
   };
-  if (hipMalloc(&dout, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    dout = nullptr;
-    return fail(S1_ENOMEM, "device allocation for results failed");
-  }
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
-    return fail(S1_EDEVICE, "event creation failed");
-  float* dprobs = static_cast<float*>(dout);
-  s1_decision* ddec = reinterpret_cast<s1_decision*>(static_cast<char*>(dout) + ((size_t)nopt * 4 + 15) / 16 * 16);
-  if (hipEventRecord(e0, s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
-  rc = run_plan(m->m, p, dprobs, ddec, s);
+  float* dprobs = static_cast<float*>(p->extra);
+  s1_decision* ddec = reinterpret_cast<s1_decision*>(static_cast<char*>(p->extra) + pbytes);
+  if (hipEventRecord(mm->decide_ev[0], s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
+  rc = run_plan(mm, p, dprobs, ddec, s);
   if (rc) return fail(rc, "");
-  if (hipEventRecord(e1, s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
+  if (hipEventRecord(mm->decide_ev[1], s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
   if (Q > 0) {
     if (hipMemcpyAsync(probs, dprobs, (size_t)nopt * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipMemcpyAsync(out, ddec, (size_t)Q * sizeof(s1_decision), hipMemcpyDeviceToHost, s) != hipSuccess)
@@ -334,9 +330,9 @@ int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision*
   const hipError_t se = hipStreamSynchronize(s);
   if (se != hipSuccess) return fail(S1_EDEVICE, hip_msg(se, "device work failed"));
   float ms = 0.f;
-  if (hipEventElapsedTime(&ms, e0, e1) == hipSuccess) dev_us = ms * 1000.0;
+  const double dev_us = hipEventElapsedTime(&ms, mm->decide_ev[0], mm->decide_ev[1]) == hipSuccess ? ms * 1000.0 : 0.0;
   const long long T = p->T;
-  fail(S1_OK, "");
+  delete p;
   if (timing) {
     timing->tokens_processed = T;
     timing->device_us = dev_us;
@@ -597,39 +593,109 @@ int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, co
 int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, void* o, int32_t Hq, int32_t Hkv,
                   int32_t hd, int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len,
                   const int32_t* kv_row0, const int32_t* kv_pre_row0, const int32_t* kv_pre_len,
-                  int32_t block_rows, void* hip_stream) {
+                  int32_t block_rows, int32_t piece, void* hip_stream) {
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || Hq < 1 || Hkv < 1 || Hq % Hkv || n_seqs < 0 || !q || !k ||
       !v || !o || (bf16 && hd != 128) || (!bf16 && (hd < 1 || hd > 128)) ||
       (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)) ||
-      (block_rows != 0 && !attn_block_rows_valid(bf16, block_rows)))
+      (block_rows != 0 && !attn_block_rows_valid(bf16, block_rows)) || (!bf16 && piece != 0) ||
+      (piece > 0 && piece % 64))
     return set_error(S1_EINVAL, "s1k_attention: unsupported arguments");
-  for (int i = 0; i < n_seqs; ++i)
-    if (q_len[i] < 0 || kv_pre_len[i] < 0) return set_error(S1_EINVAL, "s1k_attention: negative length");
-  std::vector<AttnSeq> seqs(n_seqs);
-  std::vector<AttnBlock> blocks;
-  const int bq = block_rows ? block_rows : attn_block_rows(bf16, q_len, n_seqs, Hq);
+  int row_lo = 0, row_hi = 0;
   for (int i = 0; i < n_seqs; ++i) {
-    seqs[i] = {q_row0[i], q_len[i], kv_row0[i], kv_pre_row0[i], kv_pre_len[i]};
-    for (int q0 = 0; q0 < q_len[i]; q0 += bq) blocks.push_back({i, q0});
+    if (q_len[i] < 0 || kv_pre_len[i] < 0 || q_row0[i] < 0) return set_error(S1_EINVAL, "s1k_attention: negative length");
+    if (q_len[i] == 0) continue;
+    row_lo = row_hi > row_lo ? std::min(row_lo, q_row0[i]) : q_row0[i];
+    row_hi = std::max(row_hi, q_row0[i] + q_len[i]);
   }
-  if (blocks.empty()) return S1_OK;
+  std::vector<AttnSeq> seqs(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) seqs[i] = {q_row0[i], q_len[i], kv_row0[i], kv_pre_row0[i], kv_pre_len[i]};
+  const int bq = block_rows ? block_rows : attn_block_rows(bf16, q_len, n_seqs, Hq);
+  int n_cu = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  AttnPlanHost ap;
+  plan_attention(seqs.data(), n_seqs, row_lo, row_hi - row_lo, Hq, bq, piece, n_cu, &ap);
+  if (ap.blocks.empty()) return S1_OK;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o_ = off;
+    off += (bytes + 255) / 256 * 256;
+    return o_;
+  };
+  const size_t o_s = take(ap.seqs.size() * sizeof(AttnSeq)), o_b = take(ap.blocks.size() * sizeof(AttnBlock));
+  const size_t o_rs = take(ap.row_slot.size() * 4), o_rn = take(ap.row_np.size() * 4);
+  const size_t o_c = take(ap.comb_rows.size() * 4), o_po = take((size_t)ap.slots * Hq * hd * 4);
+  const size_t o_pm = take((size_t)ap.slots * Hq * 8);
   void* dm = nullptr;
-  const size_t b1 = seqs.size() * sizeof(AttnSeq), b2 = blocks.size() * sizeof(AttnBlock);
-  if (hipMalloc(&dm, b1 + b2 + 256) != hipSuccess) {
+  if (hipMalloc(&dm, off + 256) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_attention: allocation failed");
   }
-  auto* ds = static_cast<AttnSeq*>(dm);
-  auto* db = reinterpret_cast<AttnBlock*>(static_cast<char*>(dm) + (b1 + 255) / 256 * 256);
-  hipError_t e = hipMemcpy(ds, seqs.data(), b1, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(db, blocks.data(), b2, hipMemcpyHostToDevice);
+  char* d = static_cast<char*>(dm);
+  AttnPartials part;
+  part.row_slot = reinterpret_cast<const int32_t*>(d + o_rs);
+  part.row_np = reinterpret_cast<const int32_t*>(d + o_rn);
+  part.row_base = row_lo;
+  part.pO = reinterpret_cast<float*>(d + o_po);
+  part.pML = reinterpret_cast<float2*>(d + o_pm);
+  hipError_t e = hipMemcpy(d + o_s, ap.seqs.data(), ap.seqs.size() * sizeof(AttnSeq), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(d + o_b, ap.blocks.data(), ap.blocks.size() * sizeof(AttnBlock), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !ap.row_slot.empty()) {
+    e = hipMemcpy(d + o_rs, ap.row_slot.data(), ap.row_slot.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(d + o_rn, ap.row_np.data(), ap.row_np.size() * 4, hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess && !ap.comb_rows.empty())
+    e = hipMemcpy(d + o_c, ap.comb_rows.data(), ap.comb_rows.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess)
-    e = launch_attention(bf16, q, Hq * hd, k, v, Hkv * hd, o, Hq * hd, ds, db, (int)blocks.size(), Hq, Hkv,
-                         hd, bq, strm(hip_stream));
+    e = launch_attention(bf16, q, Hq * hd, k, v, Hkv * hd, o, Hq * hd, reinterpret_cast<AttnSeq*>(d + o_s),
+                         reinterpret_cast<AttnBlock*>(d + o_b), (int)ap.blocks.size(), Hq, Hkv, hd, bq, part,
+                         strm(hip_stream));
+  if (e == hipSuccess)
+    e = launch_attn_combine(reinterpret_cast<int32_t*>(d + o_c), (int)ap.comb_rows.size(), part, o, Hq * hd, Hq,
+                            strm(hip_stream));
   if (e == hipSuccess) e = hipStreamSynchronize(strm(hip_stream));
   (void)hipFree(dm);
   return dev_status(e, "s1k_attention");
+}
+
+int s1k_attention_plan(int32_t n_seqs, const int32_t* q_row0, const int32_t* q_len, const int32_t* kv_row0,
+                       const int32_t* kv_pre_row0, const int32_t* kv_pre_len, int32_t Hq, int32_t block_rows,
+                       int32_t piece, int32_t n_cu, int32_t max_blocks, int32_t* blocks, int32_t* n_blocks,
+                       int32_t max_shared, int32_t* shared, int32_t* n_seqs_out, int32_t max_rows,
+                       int32_t* row_np, int32_t* piece_out) {
+  if (n_seqs < 0 || Hq < 1 || n_cu < 1 || (piece > 0 && piece % 64) || !attn_block_rows_valid(true, block_rows) ||
+      (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)) || !blocks || !n_blocks ||
+      !shared || !n_seqs_out || !row_np || !piece_out)
+    return set_error(S1_EINVAL, "s1k_attention_plan: bad arguments");
+  int row_lo = 0, row_hi = 0;
+  std::vector<AttnSeq> seqs(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    if (q_len[i] < 0 || kv_pre_len[i] < 0 || q_row0[i] < 0) return set_error(S1_EINVAL, "s1k_attention_plan: negative length");
+    seqs[i] = {q_row0[i], q_len[i], kv_row0[i], kv_pre_row0[i], kv_pre_len[i]};
+    if (q_len[i] == 0) continue;
+    row_lo = row_hi > row_lo ? std::min(row_lo, q_row0[i]) : q_row0[i];
+    row_hi = std::max(row_hi, q_row0[i] + q_len[i]);
+  }
+  AttnPlanHost ap;
+  plan_attention(seqs.data(), n_seqs, row_lo, row_hi - row_lo, Hq, block_rows, piece, n_cu, &ap);
+  if ((int)ap.blocks.size() > max_blocks || (int)ap.seqs.size() - n_seqs > max_shared || row_hi - row_lo > max_rows)
+    return set_error(S1_EINVAL, "s1k_attention_plan: capacity exceeded");
+  for (size_t i = 0; i < ap.blocks.size(); ++i) {
+    const AttnBlock& b = ap.blocks[i];
+    const int32_t v[5] = {b.seq, b.q0, b.k_lo, b.k_hi, b.part};
+    std::memcpy(blocks + 5 * i, v, sizeof(v));
+  }
+  *n_blocks = (int)ap.blocks.size();
+  for (size_t i = n_seqs; i < ap.seqs.size(); ++i) {
+    const AttnSeq& a = ap.seqs[i];
+    const int32_t v[5] = {a.q_row0, a.len, a.kv_row0, a.kv_pre_row0, a.kv_pre_len};
+    std::memcpy(shared + 5 * (i - n_seqs), v, sizeof(v));
+  }
+  *n_seqs_out = (int)ap.seqs.size();
+  for (int r = 0; r < row_hi - row_lo; ++r) row_np[r] = ap.row_np[r];
+  *piece_out = ap.piece;
+  return S1_OK;
 }
 
 int s1k_readout(int32_t dtype, const float* x, int32_t d, const float* w_final, float eps, const void* E,

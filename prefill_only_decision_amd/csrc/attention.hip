@@ -13,6 +13,16 @@
 // is a permutation of the key index that the B operand of the second product
 // accepts as-is, provided V^T is read with the same key permutation.  Running
 // max and sum are fp32; exp2 with log2(e) folded into the scale.
+//
+// Split keys: a workgroup may cover only a piece [k_lo, k_hi) of its
+// queries' keys (pieces cut at fixed key positions, so a query's pieces do
+// not depend on the other sequences) and then writes its running max, sum
+// and unnormalised O; attn_combine_kernel merges a row's pieces in piece
+// order.  This lets short requests fill the chip, and lets the branches of a
+// prefix read the prefix keys once for all their queries (RFC #114 section 5:
+// every branch attends to the same immutable prefix snapshot).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,7 +42,8 @@ __global__ void __launch_bounds__(NWQ * 64)
 attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ k,
                  const bf16_t* __restrict__ v, int ldkv, bf16_t* __restrict__ o, int ldo,
                  const AttnSeq* __restrict__ seqs, const AttnBlock* __restrict__ blocks, int Hq,
-                 int Hkv, float scale_log2) {
+                 int Hkv, float scale_log2, const int32_t* __restrict__ row_slot, int row_base,
+                 float* __restrict__ pO, float2* __restrict__ pML) {
   constexpr int BQ = 32 * NWQ, NT = 64 * NWQ;
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   char* sK = smem;
@@ -42,10 +53,11 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
   const AttnBlock blk = blocks[blockIdx.x];
   const AttnSeq sq = seqs[blk.seq];
   const int n_pre = sq.kv_pre_len, n_kv = n_pre + sq.len;
+  const int k_lo = blk.k_lo, k_hi = min(blk.k_hi, n_kv);
   const int qw0 = blk.q0 + wave * 32;
   const bool wave_active = qw0 < sq.len;
-  const int kv_end = n_pre + min(blk.q0 + BQ, sq.len);          // keys any query of the WG sees
-  const int wave_kv_end = n_pre + min(qw0 + 32, sq.len);         // keys this wave sees
+  const int kv_end = min(k_hi, n_pre + min(blk.q0 + BQ, sq.len));   // keys any query of the WG sees
+  const int wave_kv_end = min(k_hi, n_pre + min(qw0 + 32, sq.len));  // keys this wave sees
   const int qi = qw0 + (lane & 31);
   const int hi = lane >> 5;
 
@@ -107,8 +119,8 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
       }
     }
   };
-  if (kv_end > 0) load_block(0);
-  for (int j0 = 0; j0 < kv_end; j0 += BKV) {
+  if (kv_end > k_lo) load_block(k_lo);
+  for (int j0 = k_lo; j0 < kv_end; j0 += BKV) {
     __syncthreads();   // the previous block's LDS reads are done
     store_block();
     if (j0 + BKV < kv_end) load_block(j0 + BKV);
@@ -131,20 +143,23 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + 32 * t + acc_row(r, lane);
-        const bool vis = (j <= n_pre + qi) && (j < n_kv);
+        const bool vis = (j <= n_pre + qi) && (j < k_hi);
         const float val = vis ? s[t][r] * scale_log2 : -INFINITY;
         s[t][r] = val;
         mx = fmaxf(mx, val);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    // a query that has seen no key of this piece yet keeps (max, sum, O) =
+    // (-inf, 0, 0): the reference point 0 keeps alpha and p finite (0)
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[t][r] - m_new);
+        const float p = exp2f(s[t][r] - m_use);
         s[t][r] = p;
         ps += p;
       }
@@ -174,9 +189,24 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
     }
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (blk.part >= 0) {   // one piece of the keys: (max, sum, unnormalised O) to its slot
+    const int qq = qw0 + (lane & 31);
+    if (!wave_active || qq >= sq.len) return;
+    const int row = sq.q_row0 + qq;
+    const long long slot = (long long)(row_slot[row - row_base] + blk.part) * Hq + h;
+    float* dst = pO + slot * HD;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g + 4 * hi) =
+            make_float4(oacc[dt][4 * g], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2], oacc[dt][4 * g + 3]);
+    if (hi == 0) pML[slot] = make_float2(m_run, l_tot);
+    return;
+  }
   // normalise and stage O through LDS for coalesced row stores
   __syncthreads();
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
   char* so = smem + wave * 32 * OPITCH;
 #pragma unroll
@@ -197,6 +227,36 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
       *reinterpret_cast<uint4*>(o + (long long)(sq.q_row0 + qq) * ldo + h * HD + ch * 8) =
           *reinterpret_cast<const uint4*>(so + row * OPITCH + ch * 16);
   }
+}
+
+// Merge a row's key pieces: with M the largest piece max, o = sum_p
+// 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, pieces in order (a piece that saw
+// no key has m = -inf and weight 0).  One wave per (row, head), two output
+// columns per lane.
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(const int32_t* __restrict__ rows, int n_rows, const int32_t* __restrict__ row_slot,
+                    const int32_t* __restrict__ row_np, int row_base, const float* __restrict__ pO,
+                    const float2* __restrict__ pML, bf16_t* __restrict__ o, int ldo, int Hq) {
+  const int lane = threadIdx.x & 63;
+  const long long gw = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= (long long)n_rows * Hq) return;
+  const int ri = (int)(gw / Hq), h = (int)(gw % Hq);
+  const int row = rows[ri];
+  const int base = row_slot[row - row_base], np = row_np[row - row_base];
+  float M = -INFINITY;
+  for (int pc = 0; pc < np; ++pc) M = fmaxf(M, pML[(long long)(base + pc) * Hq + h].x);
+  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int pc = 0; pc < np; ++pc) {
+    const long long slot = (long long)(base + pc) * Hq + h;
+    const float2 ml = pML[slot];
+    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+    const float2 val = *reinterpret_cast<const float2*>(pO + slot * HD + 2 * lane);
+    L += w * ml.y;
+    a0 += w * val.x;
+    a1 += w * val.y;
+  }
+  const float inv = 1.f / L;
+  *reinterpret_cast<uint32_t*>(o + (long long)row * ldo + h * HD + 2 * lane) = pack_bf2(a0 * inv, a1 * inv);
 }
 
 // fp32 path (small models): one wave per query, online softmax over keys,
@@ -253,10 +313,110 @@ int attn_block_rows(bool bf16, const int* lens, int n, int Hq) {
   return bf16 ? 128 : BQ32;
 }
 
+namespace {
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// The pieces [lo, hi) of the keys [k0, k_end), cut at multiples of piece.
+template <typename F>
+int for_pieces(int k0, int k_end, int piece, F f) {
+  int n = 0;
+  for (int lo = k0; lo < k_end;) {
+    const int hi = std::min(k_end, (lo / piece + 1) * piece);
+    f(lo, hi, n++);
+    lo = hi;
+  }
+  return n;
+}
+
+}  // namespace
+
+void plan_attention(const AttnSeq* in, int n, int row_base, int n_rows, int Hq, int bq, int piece, int n_cu,
+                    AttnPlanHost* out) {
+  AttnPlanHost& P = *out;
+  P = AttnPlanHost();
+  P.seqs.assign(in, in + n);
+  P.row_slot.assign(std::max(n_rows, 0), -1);
+  P.row_np.assign(std::max(n_rows, 0), 1);
+  if (piece < 0) {
+    // key blocks (64 keys) per workgroup chain without a split, and their sum
+    long long total = 0;
+    int longest = 0;
+    bool prefix = false;
+    for (int i = 0; i < n; ++i) {
+      prefix |= in[i].kv_pre_len > 0 && in[i].len > 0;
+      for (int q0 = 0; q0 < in[i].len; q0 += bq) {
+        const int kb = cdiv(in[i].kv_pre_len + std::min(q0 + bq, in[i].len), 64);
+        total += kb;
+        longest = std::max(longest, kb);
+      }
+    }
+    total *= Hq;
+    const long long target = std::max<long long>(2, (total + 2LL * n_cu - 1) / (2LL * n_cu));
+    if (longest <= target && !prefix) {
+      piece = 0;
+    } else {
+      long long pb = 2;
+      while (pb * 2 <= target) pb *= 2;
+      piece = (int)(64 * pb);
+    }
+  }
+  P.piece = piece;
+  auto assign_rows = [&](int row0, int nq, int np) {
+    for (int r = row0; r < row0 + nq; ++r) {
+      P.row_slot[r - row_base] = P.slots;
+      P.row_np[r - row_base] = np;
+      P.slots += np;
+      P.comb_rows.push_back(r);
+    }
+  };
+  for (int i = 0; i < n;) {
+    const AttnSeq& a = in[i];
+    if (piece > 0 && a.kv_pre_len > 0 && a.len > 0) {
+      // the run of sequences continuing this prefix with contiguous query rows
+      int j = i, rows = a.len;
+      while (j + 1 < n && in[j + 1].kv_pre_len == a.kv_pre_len && in[j + 1].kv_pre_row0 == a.kv_pre_row0 &&
+             in[j + 1].q_row0 == in[j].q_row0 + in[j].len && in[j + 1].len > 0) {
+        ++j;
+        rows += in[j].len;
+      }
+      const int Pn = a.kv_pre_len;
+      const int npre = cdiv(Pn, piece);
+      const int g = (int)P.seqs.size();
+      P.seqs.push_back({a.q_row0, rows, a.q_row0, a.kv_pre_row0, Pn});
+      for (int q0 = 0; q0 < rows; q0 += bq)
+        for_pieces(0, Pn, piece, [&](int lo, int hi, int ord) { P.blocks.push_back({g, q0, lo, hi, ord}); });
+      for (int k = i; k <= j; ++k)
+        for (int q0 = 0; q0 < in[k].len; q0 += bq) {
+          const int nq = std::min(bq, in[k].len - q0);
+          const int nown = for_pieces(Pn, Pn + q0 + nq, piece, [&](int lo, int hi, int ord) {
+            P.blocks.push_back({k, q0, lo, hi, npre + ord});
+          });
+          assign_rows(in[k].q_row0 + q0, nq, npre + nown);
+        }
+      i = j + 1;
+      continue;
+    }
+    for (int q0 = 0; q0 < a.len; q0 += bq) {
+      const int nq = std::min(bq, a.len - q0);
+      const int k_end = a.kv_pre_len + q0 + nq;
+      if (piece <= 0 || k_end <= piece) {
+        P.blocks.push_back({i, q0, 0, a.kv_pre_len + a.len, -1});
+        continue;
+      }
+      const int np = for_pieces(0, k_end, piece, [&](int lo, int hi, int ord) {
+        P.blocks.push_back({i, q0, lo, hi, ord});
+      });
+      assign_rows(a.q_row0 + q0, nq, np);
+    }
+    ++i;
+  }
+}
+
 hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, const void* v,
                             int ld_kv, void* o, int ld_o, const AttnSeq* seqs,
                             const AttnBlock* blocks, int n_blocks, int Hq, int Hkv, int hd, int block_rows,
-                            hipStream_t s) {
+                            const AttnPartials& part, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   if (Hkv <= 0 || Hq % Hkv != 0 || !attn_block_rows_valid(bf16, block_rows)) return hipErrorInvalidValue;
   const dim3 grid(n_blocks, Hq);
@@ -269,13 +429,13 @@ hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, c
     auto* oo = reinterpret_cast<bf16_t*>(o);
     if (block_rows == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
-                         blocks, Hq, Hkv, sl2);
+                         blocks, Hq, Hkv, sl2, part.row_slot, part.row_base, part.pO, part.pML);
     else if (block_rows == 64)
       hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
-                         blocks, Hq, Hkv, sl2);
+                         blocks, Hq, Hkv, sl2, part.row_slot, part.row_base, part.pO, part.pML);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
-                         blocks, Hq, Hkv, sl2);
+                         blocks, Hq, Hkv, sl2, part.row_slot, part.row_base, part.pO, part.pML);
   } else {
     if (hd > 128) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
@@ -283,6 +443,16 @@ hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, c
                        ld_kv, reinterpret_cast<float*>(o), ld_o, seqs, blocks, Hq, Hkv, hd,
                        1.f / sqrtf((float)hd));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const int32_t* rows, int n_rows, const AttnPartials& part, void* o, int ld_o,
+                               int Hq, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  const long long waves = (long long)n_rows * Hq;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, rows, n_rows,
+                     part.row_slot, part.row_np, part.row_base, part.pO, part.pML, reinterpret_cast<bf16_t*>(o),
+                     ld_o, Hq);
   return hipGetLastError();
 }
 

@@ -63,6 +63,9 @@ void Profiler::mark(int c, hipStream_t s) {
 
 Model::~Model() {
   delete prof;
+  for (hipEvent_t e : decide_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (decide_dev) (void)hipFree(decide_dev);
   for (void* p : allocs) (void)hipFree(p);
   if (own_stream) (void)hipStreamDestroy(own_stream);
 }
@@ -87,7 +90,7 @@ void Plan::drop_graph() {
 
 Plan::~Plan() {
   drop_graph();
-  if (dev) (void)hipFree(dev);
+  if (dev && dev_owned) (void)hipFree(dev);
   if (cap_dev) (void)hipFree(cap_dev);
   if (inj_dev) (void)hipFree(inj_dev);
   if (feat_dev) (void)hipFree(feat_dev);
@@ -391,7 +394,7 @@ int load_model(const s1_config* cfg, const s1_tensor* tensors, int n, hipStream_
 }
 
 // ------------------------------------------------------------------ plans
-int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
+int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity, bool model_block, size_t extra_bytes) {
   int rc = validate_batch(&m->cfg, b);
   if (rc) return rc;
   Plan* p = new (std::nothrow) Plan();
@@ -409,9 +412,11 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
   int n_slots = 0;
   for (int i = 0; i < n; ++i)
     if (pre(i) >= 0 && slot[pre(i)] < 0) slot[pre(i)] = n_slots++;
-  // internal order: pass A (non-branches) then pass B (branches)
+  // internal order: pass A (non-branches) then pass B (branches, those of
+  // one prefix next to each other so that they can share its key sweep)
   std::vector<int> order[2];
   for (int i = 0; i < n; ++i) order[pre(i) >= 0 ? 1 : 0].push_back(i);
+  std::stable_sort(order[1].begin(), order[1].end(), [&](int a, int c) { return slot[pre(a)] < slot[pre(c)]; });
   std::vector<int> row0(n, 0);
   p->row_of.assign(p->T, 0);
   p->pass_of_row.assign(p->T, 0);
@@ -436,10 +441,12 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
     p->pass[ps].n_seqs = (int)order[ps].size();
   }
   std::vector<ScanSeq> scan[2];
-  std::vector<AttnSeq> attn[2];
-  std::vector<AttnBlock> blocks[2];
+  // attention: the split plan (keys cut into pieces, branch prefixes shared)
+  // for the default schedule, the unsplit one for the row-invariant mode
+  AttnPlanHost aplan[2], aplan_inv[2];
   for (int ps = 0; ps < 2; ++ps) {
     std::vector<int> lens;
+    std::vector<AttnSeq> attn;
     for (const int i : order[ps]) lens.push_back(b->cu_seqlens[i + 1] - b->cu_seqlens[i]);
     const int bq = attn_block_rows(m->bf16, lens.data(), (int)lens.size(), m->cfg.fa_q_heads);
     p->pass[ps].attn_rows = bq;
@@ -449,9 +456,11 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
       const int pi = pre(i);
       const int P = pi >= 0 ? b->cu_seqlens[pi + 1] - b->cu_seqlens[pi] : 0;
       scan[ps].push_back({row0[i], len, pi >= 0 ? slot[pi] : -1, slot[i]});
-      attn[ps].push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
-      for (int q0 = 0; q0 < len; q0 += bq) blocks[ps].push_back({(int)k, q0});
+      attn.push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
     }
+    const int r0 = p->pass[ps].r0, Tp = p->pass[ps].T, Hq = m->cfg.fa_q_heads;
+    plan_attention(attn.data(), (int)attn.size(), r0, Tp, Hq, bq, m->bf16 ? -1 : 0, m->n_cu, &aplan[ps]);
+    plan_attention(attn.data(), (int)attn.size(), r0, Tp, Hq, bq, 0, m->n_cu, &aplan_inv[ps]);
   }
   // chunk-parallel scan when a pass has few (sequence, head) chains; the
   // chunk lists are built for every bf16 pass, since the row-invariant mode
@@ -505,16 +514,29 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
   const size_t o_off = take((p->Q + 1) * 4), o_opt = take(std::max(p->total_opts, opts_capacity) * 4);
   const size_t o_qt = take(p->Q);
   size_t o_scan[2], o_attn[2], o_blk[2], o_chk[2], o_cseq[2], o_gseq[2], o_rseq[2];
+  size_t o_blki[2], o_rslot[2], o_rnp[2], o_comb[2], o_pO[2], o_pML[2];
+  const int Hq = m->cfg.fa_q_heads, hd = m->cfg.fa_head_dim;
   for (int ps = 0; ps < 2; ++ps) {
+    const AttnPlanHost& ap = aplan[ps];
     o_scan[ps] = take(scan[ps].size() * sizeof(ScanSeq));
-    o_attn[ps] = take(attn[ps].size() * sizeof(AttnSeq));
-    o_blk[ps] = take(blocks[ps].size() * sizeof(AttnBlock));
+    o_attn[ps] = take(ap.seqs.size() * sizeof(AttnSeq));
+    o_blk[ps] = take(ap.blocks.size() * sizeof(AttnBlock));
+    o_blki[ps] = take(aplan_inv[ps].blocks.size() * sizeof(AttnBlock));
+    o_rslot[ps] = take(ap.row_slot.size() * 4);
+    o_rnp[ps] = take(ap.row_np.size() * 4);
+    o_comb[ps] = take(ap.comb_rows.size() * 4);
     o_chk[ps] = take(chunks[ps].size() * sizeof(ScanSeq));
     o_cseq[ps] = take(cseqs[ps].size() * sizeof(ChunkSeq));
     o_gseq[ps] = take(gseqs[ps].size() * sizeof(GdnSeq));
     o_rseq[ps] = take(rowseq[ps].size() * sizeof(int32_t));
   }
-  std::vector<char> host(off, 0);
+  const size_t host_bytes = off;   // partial results need no upload
+  for (int ps = 0; ps < 2; ++ps) {
+    o_pO[ps] = take((size_t)aplan[ps].slots * Hq * hd * 4);
+    o_pML[ps] = take((size_t)aplan[ps].slots * Hq * 8);
+  }
+  const size_t o_extra = take(extra_bytes);
+  std::vector<char> host(host_bytes, 0);
   auto put = [&](size_t o, const void* src, size_t bytes) {
     if (bytes) std::memcpy(host.data() + o, src, bytes);
   };
@@ -528,23 +550,48 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
   }
   for (int ps = 0; ps < 2; ++ps) {
     put(o_scan[ps], scan[ps].data(), scan[ps].size() * sizeof(ScanSeq));
-    put(o_attn[ps], attn[ps].data(), attn[ps].size() * sizeof(AttnSeq));
-    put(o_blk[ps], blocks[ps].data(), blocks[ps].size() * sizeof(AttnBlock));
+    const AttnPlanHost& ap = aplan[ps];
+    put(o_attn[ps], ap.seqs.data(), ap.seqs.size() * sizeof(AttnSeq));
+    put(o_blk[ps], ap.blocks.data(), ap.blocks.size() * sizeof(AttnBlock));
+    put(o_blki[ps], aplan_inv[ps].blocks.data(), aplan_inv[ps].blocks.size() * sizeof(AttnBlock));
+    put(o_rslot[ps], ap.row_slot.data(), ap.row_slot.size() * 4);
+    put(o_rnp[ps], ap.row_np.data(), ap.row_np.size() * 4);
+    put(o_comb[ps], ap.comb_rows.data(), ap.comb_rows.size() * 4);
     put(o_chk[ps], chunks[ps].data(), chunks[ps].size() * sizeof(ScanSeq));
     put(o_cseq[ps], cseqs[ps].data(), cseqs[ps].size() * sizeof(ChunkSeq));
     put(o_gseq[ps], gseqs[ps].data(), gseqs[ps].size() * sizeof(GdnSeq));
     put(o_rseq[ps], rowseq[ps].data(), rowseq[ps].size() * sizeof(int32_t));
   }
-  if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
+  if (model_block) {
+    // the model's block, grown only when this request needs more; the
+    // previous call synchronised its stream, so nothing still reads it
+    if (m->decide_bytes < off) {
+      if (m->decide_dev) (void)hipFree(m->decide_dev);
+      m->decide_dev = nullptr;
+      m->decide_bytes = 0;
+      const size_t want = std::max<size_t>(off, 1 << 20);
+      if (hipMalloc(&m->decide_dev, want) != hipSuccess) {
+        (void)hipGetLastError();
+        m->decide_dev = nullptr;
+        delete p;
+        return set_error(S1_ENOMEM, "device allocation for the request failed");
+      }
+      m->decide_bytes = want;
+    }
+    p->dev = m->decide_dev;
+    p->dev_owned = false;
+  } else if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
     (void)hipGetLastError();
+    p->dev = nullptr;
     delete p;
     return set_error(S1_ENOMEM, "device allocation for the plan failed");
   }
-  if (hipMemcpy(p->dev, host.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMemcpy(p->dev, host.data(), host_bytes, hipMemcpyHostToDevice) != hipSuccess) {
     delete p;
     return set_error(S1_EDEVICE, "copy plan to device");
   }
   char* dv = static_cast<char*>(p->dev);
+  p->extra = dv + o_extra;
   p->ids = reinterpret_cast<int32_t*>(dv + o_ids);
   p->pos = reinterpret_cast<int32_t*>(dv + o_pos);
   p->q_row = reinterpret_cast<int32_t*>(dv + o_qrow);
@@ -555,7 +602,16 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity) {
     p->pass[ps].scan = reinterpret_cast<ScanSeq*>(dv + o_scan[ps]);
     p->pass[ps].attn = reinterpret_cast<AttnSeq*>(dv + o_attn[ps]);
     p->pass[ps].blocks = reinterpret_cast<AttnBlock*>(dv + o_blk[ps]);
-    p->pass[ps].n_blocks = (int)blocks[ps].size();
+    p->pass[ps].n_blocks = (int)aplan[ps].blocks.size();
+    p->pass[ps].blocks_inv = reinterpret_cast<AttnBlock*>(dv + o_blki[ps]);
+    p->pass[ps].n_blocks_inv = (int)aplan_inv[ps].blocks.size();
+    p->pass[ps].comb_rows = reinterpret_cast<int32_t*>(dv + o_comb[ps]);
+    p->pass[ps].n_comb = (int)aplan[ps].comb_rows.size();
+    p->pass[ps].attn_part.row_slot = reinterpret_cast<int32_t*>(dv + o_rslot[ps]);
+    p->pass[ps].attn_part.row_np = reinterpret_cast<int32_t*>(dv + o_rnp[ps]);
+    p->pass[ps].attn_part.row_base = p->pass[ps].r0;
+    p->pass[ps].attn_part.pO = reinterpret_cast<float*>(dv + o_pO[ps]);
+    p->pass[ps].attn_part.pML = reinterpret_cast<float2*>(dv + o_pML[ps]);
     p->pass[ps].chunks = reinterpret_cast<ScanSeq*>(dv + o_chk[ps]);
     p->pass[ps].n_chunks = (int)chunks[ps].size();
     p->pass[ps].cseqs = reinterpret_cast<ChunkSeq*>(dv + o_cseq[ps]);
@@ -962,9 +1018,14 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       g.rope = m->rope;
       S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s), "attention QKV projection");
       MARK(KC_GEMM_FA_QKV);
+      const bool split = !p->invariant;
       S1_TRY(launch_attention(m->bf16, qkv, m->ld_qkv, kc, vc, (int)kvld, att, m->ld_att, ps.attn,
-                              ps.blocks, ps.n_blocks, Hq, Hkv, hd, ps.attn_rows, s),
+                              split ? ps.blocks : ps.blocks_inv, split ? ps.n_blocks : ps.n_blocks_inv, Hq, Hkv,
+                              hd, ps.attn_rows, ps.attn_part, s),
              "attention");
+      if (split && ps.n_comb)
+        S1_TRY(launch_attn_combine(ps.comb_rows, ps.n_comb, ps.attn_part, att, m->ld_att, Hq, s),
+               "attention combine");
       MARK(KC_ATTENTION);
     }
     GemmArgs go{};

@@ -88,6 +88,12 @@ struct Model {
   long long splitws_elems = 0;
   int split_max_rows = 0;
 
+  // s1_prefill_decide's plan and result block, kept from call to call and
+  // grown when a request needs more (no allocation in the steady state),
+  // and its two timing events
+  void* decide_dev = nullptr;
+  size_t decide_bytes = 0;
+  hipEvent_t decide_ev[2] = {nullptr, nullptr};
   Profiler* prof = nullptr;     // set only during s1_plan_profile
   std::vector<void*> allocs;
   ~Model();
@@ -99,8 +105,13 @@ struct PassPlan {
   int n_seqs = 0;
   ScanSeq* scan = nullptr;      // device [n_seqs]
   AttnSeq* attn = nullptr;      // device [n_seqs]
-  AttnBlock* blocks = nullptr;  // device [n_blocks]
+  AttnBlock* blocks = nullptr;  // device [n_blocks]: keys split into pieces, prefixes shared
   int n_blocks = 0;
+  AttnBlock* blocks_inv = nullptr;  // device: one workgroup per query block (row-invariant mode)
+  int n_blocks_inv = 0;
+  int32_t* comb_rows = nullptr; // device [n_comb]: rows whose pieces are merged
+  int n_comb = 0;
+  AttnPartials attn_part;       // partial results of the split attention
   int attn_rows = 0;            // queries per attention workgroup
   bool chunked = false;         // scan runs chunk-parallel (few chains)
   ScanSeq* chunks = nullptr;    // device [n_chunks]
@@ -149,6 +160,8 @@ struct Plan {
   float* cap_out = nullptr;     // device [(n_layers + 1) * n_cap * d]
   int n_cap = 0;
   void* dev = nullptr;          // one device block for the arrays above
+  bool dev_owned = true;        // false: the model's reusable block (s1_prefill_decide)
+  void* extra = nullptr;        // extra_bytes requested at creation, after the arrays
   void* cap_dev = nullptr;      // device block for capture row lists
   // layer-input replacement (test hook): before layer l, row list entry j
   // takes inj_src[(l * n_inj + j) * d]
@@ -187,7 +200,10 @@ struct Plan {
 int validate_config(const s1_config* c);
 int validate_batch(const s1_config* c, const s1_batch* b);
 int load_model(const s1_config* cfg, const s1_tensor* t, int n, hipStream_t s, Model** out);
-int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity = 0);
+// model_block: place the plan's device arrays (and extra_bytes more, at
+// p->extra) in the model's reusable block instead of a new allocation.
+int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity = 0, bool model_block = false,
+                size_t extra_bytes = 0);
 int create_bucket_plan(Model* m, int T_b, int Q_b, int O_b, Plan** out);
 int update_bucket_plan(Plan* p, const s1_batch* b);
 int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace s1 {
 
 // ---------------------------------------------------------------- GEMM
@@ -162,18 +164,57 @@ struct AttnSeq {
   int kv_pre_len;   // prefix keys (positions 0 ..); queries start at this position
 };
 struct AttnBlock {
-  int seq;
+  int seq;          // index into the sequence table
   int q0;           // first query (within the sequence) of this block
+  int k_lo, k_hi;   // the keys this workgroup reads, [k_lo, k_hi) in the sequence's key
+                    // order (prefix keys first); the causal mask applies within
+  int part;         // -1: the block's whole key range, O is written; else the ordinal
+                    // of this key piece: (m, l, unnormalised O) go to a partial slot
 };
 // Queries per attention workgroup for sequences of these lengths: bf16 takes
 // the largest of 128, 64, 32 that still gives 512 workgroups over Hq heads
 // (else 32); fp32 uses 64.
 int attn_block_rows(bool bf16, const int* lens, int n, int Hq);
 bool attn_block_rows_valid(bool bf16, int rows);
+
+// Launch plan of one attention pass whose query rows lie in [row_base,
+// row_base + n_rows).  piece == 0: one workgroup per query block over its
+// whole causal key range (no partial results).  piece > 0 (a multiple of
+// 64): keys are cut at multiples of `piece`, each query block's pieces run
+// as separate workgroups writing partial (max, sum, O) triples that a
+// combine kernel merges in piece order, and consecutive sequences that
+// continue the same prefix with contiguous query rows share one sweep of the
+// prefix keys (all their queries see every prefix key).  piece < 0: the
+// piece is chosen from the key blocks per workgroup chain against the chip
+// (n_cu compute units), or no split when the chains are already short and
+// no sequence has prefix keys.
+struct AttnPlanHost {
+  std::vector<AttnSeq> seqs;        // the input sequences, then one entry per shared prefix
+  std::vector<AttnBlock> blocks;
+  std::vector<int32_t> row_slot;    // [n_rows]: first partial slot of a row (-1: written directly)
+  std::vector<int32_t> row_np;      // [n_rows]: the row's pieces
+  std::vector<int32_t> comb_rows;   // rows (absolute) the combine kernel writes
+  int slots = 0;                    // partial slots, each Hq x (128 + 2) floats
+  int piece = 0;
+};
+void plan_attention(const AttnSeq* seqs, int n, int row_base, int n_rows, int Hq, int bq, int piece, int n_cu,
+                    AttnPlanHost* out);
+// Partial results of split attention: pO fp32 [slots][Hq][hd], pML (max in
+// log2 units, sum) [slots][Hq]; row_slot indexed by row - row_base.
+struct AttnPartials {
+  const int32_t* row_slot = nullptr;
+  const int32_t* row_np = nullptr;
+  int row_base = 0;
+  float* pO = nullptr;
+  float2* pML = nullptr;
+};
 hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, const void* v,
                             int ld_kv, void* o, int ld_o, const AttnSeq* seqs,
                             const AttnBlock* blocks, int n_blocks, int Hq, int Hkv, int hd, int block_rows,
-                            hipStream_t s);
+                            const AttnPartials& part, hipStream_t s);
+// Merge the partial results of the listed rows in piece order into o (bf16).
+hipError_t launch_attn_combine(const int32_t* rows, int n_rows, const AttnPartials& part, void* o, int ld_o,
+                               int Hq, hipStream_t s);
 
 // ---------------------------------------------------------------- readout
 hipError_t launch_readout(bool bf16, const float* x, int d, const float* w_final, float eps,

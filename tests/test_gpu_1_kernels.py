@@ -323,8 +323,10 @@ def test_scan_f32():
         assert rel_l2(d_sf.cpu().numpy()[i], rs) < 1e-5
 
 
-def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0):
-    """seqs: list of (q_len, prefix_len)."""
+def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0, piece=0, shared=False):
+    """seqs: list of (q_len, prefix_len).  shared: every sequence continues
+    one prefix (the first sequence's prefix_len rows), as the branches of a
+    request do."""
     torch = require_gpu()
     rng = np.random.default_rng(seed)
     Tq = sum(s[0] for s in seqs)
@@ -344,9 +346,9 @@ def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0):
     for (L, P) in seqs:
         q_row0.append(rq); q_len.append(L); kv_row0.append(rq); pre_row0.append(rp); pre_len.append(P)
         rq += L
-        rp += P
+        rp += 0 if shared else P
     B.attention(dtype, dq.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), do.data_ptr(), Hq, Hkv, hd,
-                q_row0, q_len, kv_row0, pre_row0, pre_len, stream_ptr(), block_rows=block_rows)
+                q_row0, q_len, kv_row0, pre_row0, pre_len, stream_ptr(), block_rows=block_rows, piece=piece)
     torch.cuda.synchronize()
     got = O.bf16_bits_to_float(host_bits(do)) if dtype == B.S1_BF16 else do.cpu().numpy().astype(np.float64)
     worst = worst_el = 0.0
@@ -367,8 +369,8 @@ def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0):
         unit = 2.0 ** -9 if dtype == B.S1_BF16 else 1e-5
         bound = unit * (vmax + 2.0 * np.abs(ref)) + 1e-6
         worst_el = max(worst_el, float((np.abs(got[a:a + L] - ref) / bound).max()))
-    log(f"attention dtype={dtype} rows/workgroup={block_rows or 'auto'} seqs={seqs}: rel L2 {worst:.2e}, "
-        f"element-wise excess {worst_el:.2f}")
+    log(f"attention dtype={dtype} rows/workgroup={block_rows or 'auto'} piece={piece} shared={shared} "
+        f"seqs={seqs}: rel L2 {worst:.2e}, element-wise excess {worst_el:.2f}")
     assert worst_el <= 1.0, worst_el
     return worst
 
@@ -380,6 +382,27 @@ def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0):
 ])
 def test_attention_bf16(seqs, block_rows):
     assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=len(seqs), block_rows=block_rows) < 1e-2
+
+
+@pytest.mark.parametrize("piece", [128, 256, -1])
+@pytest.mark.parametrize("seqs", [
+    [(1, 0), (100, 0), (128, 0), (129, 0), (300, 0), (512, 0)],
+    [(64, 200), (1, 70), (130, 4096)],
+])
+def test_attention_bf16_split_keys(seqs, piece):
+    """Keys cut into pieces run by separate workgroups and merged in order,
+    against the same definition and element-wise bound."""
+    assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=len(seqs) + 7, piece=piece) < 1e-2
+
+
+@pytest.mark.parametrize("piece", [128, 1024, -1])
+@pytest.mark.parametrize("P,lens", [(4096, [64] * 5), (100, [64, 1, 65, 130]), (257, [3, 200])])
+def test_attention_bf16_shared_prefix(P, lens, piece):
+    """Branches of one prefix: one sweep of the prefix keys for all their
+    queries (prefix lengths off the 64-key grid included), merged with each
+    branch's own causal keys."""
+    seqs = [(L, P) for L in lens]
+    assert _attn_case(B.S1_BF16, 16, 4, 128, seqs, seed=P + len(lens), piece=piece, shared=True) < 1e-2
 
 
 def test_attention_bf16_gqa5():
