@@ -6,7 +6,10 @@ every layer, readout) through the library's resident-input plan: token ids
 and metadata already sit in device memory when the timed region starts.
 Prints one JSON line with the throughput (prefill tokens/s), ms per request,
 the dominant kernel's roofline fraction (HIP events recorded by the library
-on the launch stream) and the CPU oracle's throughput on a bounded sample.
+on the launch stream), the attention and scan fractions, the boundary call
+s1_prefill_decide (host arrays in and out) timed per call, the same figures
+for the 16-request and branched workloads on the same weights, and the CPU
+oracle's throughput on the whole request.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -46,31 +49,139 @@ def gemm_flops(shape, T):
     }
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, weights, batch, budget_s=30.0):
-    """Time the CPU oracle (float32 mode) on a bounded sample of the request:
-    the first sequence's prefill over as many whole layers as fit the budget,
-    scaled to all layers."""
+    """The CPU oracle as it stands (float32 mode, numpy's BLAS on the host
+    cores) timed on the whole request, end to end: prefill_decide over every
+    layer and the readout, the per-layer weight decode included.  One
+    warm-up, then the median of three runs, or fewer runs when one takes
+    more than a third of the budget."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
     om = oracle.OracleModel(shape, weights.tensors, dtype=np.float32)
-    ids = batch.tokens_of(0)
-    # time the first n layers, doubling n while the budget allows
-    n_done, t_used, n = 0, 0.0, 1
-    while True:
+    times = []
+    t0 = time.time()
+    oracle.prefill_decide(om, batch)
+    warm = time.time() - t0
+    n_runs = 3 if warm * 3 <= budget_s else 1
+    for _ in range(n_runs):
         t0 = time.time()
-        om.forward(ids, n_layers=n)
-        n_done, t_used = n, time.time() - t0
-        if n == shape.n_layers or t_used * 2.2 > budget_s:
-            break
-        n = min(shape.n_layers, 2 * n)
-    per_layer = t_used / n_done
-    full = per_layer * shape.n_layers
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": len(ids) / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float32 oracle forward of the {len(ids)}-token request over {n_done} of "
-                      f"{shape.n_layers} layers ({t_used:.1f} s), scaled to all layers; "
-                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+        oracle.prefill_decide(om, batch)
+        times.append(time.time() - t0)
+    med = float(np.median(times))
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas")
+    return {"value": batch.n_tokens / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "ms_per_request": round(med * 1e3 / requests_in(batch), 1),
+            "sample": f"float32 oracle prefill_decide of the whole {batch.n_tokens}-token request "
+                      f"({batch.n_questions} questions), median of {n_runs} after one warm-up "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s); {len(os.sched_getaffinity(0))} host cores "
+                      f"visible",
+            "cpu": cpu_model(), "blas": blas or "unknown"}
+
+
+def decide_leg(model, batch, warmup=2, timed=20):
+    """s1_prefill_decide, host arrays in and out (the boundary call): wall
+    time per call from entry to return with the results on the host, the
+    copies of the request and the results included, and the device time of
+    the same calls (HIP events inside the call)."""
+    import numpy as np
+    for _ in range(warmup):
+        model.decide(batch)
+    wall, dev = [], []
+    for _ in range(timed):
+        _, _, t = model.decide(batch)
+        wall.append(t["wall_us"] / 1e3)
+        dev.append(t["device_us"] / 1e3)
+    wall = np.asarray(wall)
+    med = float(np.median(wall))
+    return {"calls": timed, "warmup": warmup, "wall_ms_median": round(med, 4),
+            "wall_ms_p95": round(float(np.percentile(wall, 95)), 4), "wall_ms_mean": round(float(wall.mean()), 4),
+            "wall_ms_min": round(float(wall.min()), 4), "device_ms_median": round(float(np.median(dev)), 4),
+            "tokens_per_s_at_median": round(batch.n_tokens / (med / 1e3), 1)}
+
+
+def attention_flops(shape, batch):
+    """Algorithmic attention flops per step: 4 Hq hd per visible (query, key)
+    pair (the causal half, a branch's prefix keys included), every full
+    layer."""
+    pre = batch.prefix_of
+    pairs = 0
+    for i in range(batch.n_seqs):
+        L = int(batch.seq_lens[i])
+        P = int(batch.seq_lens[pre[i]]) if pre[i] >= 0 else 0
+        pairs += L * (L + 1) // 2 + P * L
+    return 4 * shape.fa_q_heads * shape.fa_head_dim * pairs * shape.n_full
+
+
+def attention_roofline(shape, batch, prof, steps_p):
+    if "attention" not in prof:
+        return None
+    fl = attention_flops(shape, batch)
+    us = prof["attention"][1] / steps_p
+    tf = fl / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_step": fl, "us_per_step": round(us, 1),
+            "launches_per_step": prof["attention"][0] // steps_p}
+
+
+def workload_leg(model, name, args, stream):
+    """Another workload of the same shape on the loaded model: the plan
+    replayed as a HIP graph (tokens/s, ms/request), per-kernel times, the
+    attention and scan rooflines, and the boundary call's wall time."""
+    import torch
+    from s1_workloads import make_batch, shape_of
+    shape = shape_of(name)
+    batch = make_batch(name)
+    plan = model.plan(batch)
+    dp = torch.zeros(max(plan.n_options, 1), dtype=torch.float32, device="cuda")
+    dd = torch.zeros((max(plan.n_questions, 1), 6), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+    plan.set_graph(True)
+    steps = max(3, args.steps // 2)
+    for _ in range(2):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        plan.run(dp.data_ptr(), dd.data_ptr(), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    plan.set_graph(False)
+    prof = {}
+    n_prof = 2
+    for _ in range(n_prof):
+        for k, (n, us) in plan.profile(dp.data_ptr(), dd.data_ptr(), sp).items():
+            a, b = prof.get(k, (0, 0.0))
+            prof[k] = (a + n, b + us)
+    tokens = plan.tokens
+    plan.free()
+    reqs = requests_in(batch)
+    gemm_us = sum(prof[k][1] for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+                  if k in prof) / n_prof
+    all_gemm_flops = 2 * tokens * shape.linear_params()
+    return {"tokens_per_step": int(tokens), "requests_per_step": reqs, "questions_per_step": int(batch.n_questions),
+            "steps": steps, "ms_per_step": round(ms, 3), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "ms_per_request": round(ms / reqs, 3),
+            "kernels": {k: {"launches_per_step": n // n_prof, "us_per_step": round(us / n_prof, 1)}
+                        for k, (n, us) in sorted(prof.items())},
+            "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1),
+            "attention": attention_roofline(shape, batch, prof, n_prof),
+            "scan": scan_roofline(shape, batch, tokens, prof, n_prof),
+            "prefill_decide": decide_leg(model, batch, warmup=2, timed=max(5, args.steps // 2))}
 
 
 GEMM_SOURCE = os.path.join(ROOT, "prefill_only_decision_amd", "csrc", "gemm.hip")
@@ -430,6 +541,8 @@ def main():
                     help="skip the achievable-peak probes (MFMA loop, 1 GiB copy)")
     ap.add_argument("--no-readout-stress", action="store_true",
                     help="skip the readout at the declared stress shape (4,096 questions x 10 options)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="with the 4B single request, skip the 16-request and branched workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB elementwise copy kernel (for scaling HBM counters)")
     args = ap.parse_args()
@@ -454,7 +567,7 @@ def main():
     t_gen = time.time() - t0
     T = batch.n_tokens
     # budgets also cover the request-replay leg (16 packed requests of <= 2048 tokens)
-    cfg = s1.make_config(shape, max_tokens=max(T, 16 * 2048), max_seqs=max(batch.n_seqs, 16),
+    cfg = s1.make_config(shape, max_tokens=max(T, 16 * 2048), max_seqs=max(batch.n_seqs, 32),
                          max_questions=max(batch.n_questions, 96), max_options=256, max_prefixes=4,
                          max_positions=max(int(batch.seq_lens.max()) * 2, 8192))
     t0 = time.time()
@@ -518,6 +631,16 @@ def main():
                 "all_gemms_tflops": round(all_gemm_flops / (gemm_us * 1e-6) / 1e12, 1)}
 
     scan = scan_roofline(shape, batch, tokens, prof, steps_p)
+    attn = attention_roofline(shape, batch, prof, steps_p)
+    gemm_fracs = {}
+    for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_gate_up", "gemm_down"):
+        if k in prof and flops.get(k):
+            n_k, us_k = prof[k]
+            tf = flops[k] * (n_k // steps_p) / (us_k / steps_p * 1e-6) / 1e12
+            gemm_fracs[k] = {"tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                             "us_per_launch": round(us_k / n_k, 2)}
+    roofline["all_gemms_frac"] = round(roofline["all_gemms_tflops"] / BF16_PEAK_TFLOPS, 4)
+    roofline["per_gemm"] = gemm_fracs
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -532,9 +655,13 @@ def main():
         "ms_per_step_eager_launches": round(ms_eager, 4),
         "ms_per_step_row_invariant": round(ms_invariant, 4),
         "load_s": round(t_load, 2), "weight_gen_s": round(t_gen, 2),
-        "kernels": kernels, "roofline": roofline, "scan": scan,
+        "kernels": kernels, "roofline": roofline, "scan": scan, "attention": attn,
     }
     plan.free()
+    out["prefill_decide"] = decide_leg(model, batch, warmup=2, timed=args.steps)
+    if args.workload == "4b-single-512" and not args.no_other_workloads:
+        out["other_workloads"] = {n: workload_leg(model, n, args, stream)
+                                  for n in ("4b-varlen-16", "4b-branch-4096x20")}
     if not args.no_features:
         out["features"] = features_leg(model, batch, shape, stream, args)
     if not args.no_serve and shape.dtype == "bf16":

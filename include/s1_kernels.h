@@ -117,7 +117,7 @@ int s1k_lora_merge(int32_t dtype, const void* W, const void* A, const void* B, v
  * o (elem [T, H*dv]).  cu_seqlens (host, n_seqs + 1).  s_init (fp32
  * [n_seqs, H, dk, dv] or NULL = zero start) and s_final (same shape or NULL)
  * hold each sequence's initial and final state.  bf16 needs dk = dv = 128;
- * fp32 needs dk, dv <= 128.  The recurrent state stays fp32 (RFC #114
+ * fp32 needs dk, dv in {64, 128}.  The recurrent state stays fp32 (RFC #114
  * section 5: FP32 recurrent state). */
 int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int32_t ld_qkv,
                 const float* log_g, void* o, int32_t T, int32_t H, int32_t dk, int32_t dv,
@@ -154,7 +154,7 @@ int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, co
  * kv_pre_len[i] prefix rows starting at kv_pre_row0[i] (positions 0 ..) and
  * then its own q_len[i] rows starting at kv_row0[i] (positions
  * kv_pre_len[i] ..); query j has position kv_pre_len[i] + j.  All five
- * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd <= 128.
+ * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd 64 or 128.
  * block_rows: queries per workgroup, 0 to choose by size as the decoder
  * does; bf16 accepts 32, 64 or 128, fp32 64.  piece (bf16 only): 0 runs every
  * query block over its whole key range in one workgroup; a positive multiple

@@ -54,8 +54,8 @@ int validate_config(const s1_config* c) {
   } else {
     if (c->fa_head_dim != 64 && c->fa_head_dim != 128)
       return set_error(S1_EINVAL, "fp32 models need fa_head_dim 64 or 128");
-    if (c->la_dk > 128 || c->la_dv > 128 || 256 % c->la_dv || c->la_dk % (256 / c->la_dv))
-      return set_error(S1_EINVAL, "fp32 models need la_dv dividing 256 and la_dk <= 128");
+    if ((c->la_dk != 64 && c->la_dk != 128) || (c->la_dv != 64 && c->la_dv != 128))
+      return set_error(S1_EINVAL, "fp32 models need la_dk and la_dv of 64 or 128");
     if (c->d_model % 4 || c->ffn % 4 || (c->la_heads * c->la_dv) % 4)
       return set_error(S1_EINVAL, "fp32 models need d_model, ffn, la_heads*la_dv multiples of 4");
   }
@@ -464,7 +464,7 @@ int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int3
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || n_seqs < 0 || H < 1 || !cu_seqlens || !q || !k || !v ||
       !log_g || !o || (bf16 && (dk != 128 || dv != 128)) ||
-      (!bf16 && (dk > 128 || dv > 128 || 256 % dv || dk % (256 / dv))))
+      (!bf16 && ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))))
     return set_error(S1_EINVAL, "s1k_la_scan: unsupported arguments");
   if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T))
     return set_error(S1_EINVAL, "s1k_la_scan: cu_seqlens out of range");
@@ -596,7 +596,7 @@ int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, vo
                   int32_t block_rows, int32_t piece, void* hip_stream) {
   const bool bf16 = dtype == S1_BF16;
   if ((dtype != S1_BF16 && dtype != S1_F32) || Hq < 1 || Hkv < 1 || Hq % Hkv || n_seqs < 0 || !q || !k ||
-      !v || !o || (bf16 && hd != 128) || (!bf16 && (hd < 1 || hd > 128)) ||
+      !v || !o || (bf16 && hd != 128) || (!bf16 && hd != 64 && hd != 128) ||
       (n_seqs > 0 && (!q_row0 || !q_len || !kv_row0 || !kv_pre_row0 || !kv_pre_len)) ||
       (block_rows != 0 && !attn_block_rows_valid(bf16, block_rows)) || (!bf16 && piece != 0) ||
       (piece > 0 && piece % 64))

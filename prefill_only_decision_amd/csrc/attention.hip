@@ -259,43 +259,96 @@ attn_combine_kernel(const int32_t* __restrict__ rows, int n_rows, const int32_t*
   *reinterpret_cast<uint32_t*>(o + (long long)row * ldo + h * HD + 2 * lane) = pack_bf2(a0 * inv, a1 * inv);
 }
 
-// fp32 path (small models): one wave per query, online softmax over keys,
-// lanes over the head dimension (hd <= 128).
-constexpr int BQ32 = 64;
+// fp32 path (small models).  A workgroup owns 64 queries of one head; four
+// threads share a query, each holding a quarter of its head dimensions.
+// Keys and values stream through LDS in blocks of 64; per block every
+// thread forms its query's 64 scores (partial dot products over its quarter,
+// summed across the four threads), takes the block maximum once, rescales
+// its output quarter once and accumulates p v for the block's keys.
+constexpr int BQ32 = 64, BK32 = 64;
+template <int HD32>
 __global__ void __launch_bounds__(256)
 attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ k,
                 const float* __restrict__ v, int ldkv, float* __restrict__ o, int ldo,
                 const AttnSeq* __restrict__ seqs, const AttnBlock* __restrict__ blocks, int Hq,
-                int Hkv, int hd, float scale) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = blockIdx.y;
-  const int kvh = h / (Hq / Hkv);
+                int Hkv, float scale_log2) {
+  constexpr int QD = HD32 / 4;                  // dimensions per thread
+  constexpr int KP = HD32 + 4;                  // LDS row pitch (floats)
+  __shared__ __attribute__((aligned(16))) float sK[BK32 * KP];
+  __shared__ __attribute__((aligned(16))) float sV[BK32 * KP];
+  const int tid = threadIdx.x, h = blockIdx.y, kvh = h / (Hq / Hkv);
+  const int qloc = tid >> 2, sub = tid & 3;
   const AttnBlock blk = blocks[blockIdx.x];
   const AttnSeq sq = seqs[blk.seq];
-  const int n_pre = sq.kv_pre_len;
-  const int qend = min(blk.q0 + BQ32, sq.len);
-  for (int qi = blk.q0 + wave; qi < qend; qi += 4) {
-    const float* qp = q + (long long)(sq.q_row0 + qi) * ldq + h * hd;
-    const float q0 = lane < hd ? qp[lane] : 0.f;
-    const float q1 = lane + 64 < hd ? qp[lane + 64] : 0.f;
-    float m = -INFINITY, l = 0.f, a0 = 0.f, a1 = 0.f;
-    const int nvis = n_pre + qi + 1;
-    for (int j = 0; j < nvis; ++j) {
-      const long long row = j < n_pre ? (long long)sq.kv_pre_row0 + j : (long long)sq.kv_row0 + (j - n_pre);
-      const float* kp = k + row * ldkv + kvh * hd;
-      const float* vp = v + row * ldkv + kvh * hd;
-      const float k0 = lane < hd ? kp[lane] : 0.f, k1 = lane + 64 < hd ? kp[lane + 64] : 0.f;
-      const float sc = wave_sum(q0 * k0 + q1 * k1) * scale;
-      const float mn = fmaxf(m, sc);
-      const float al = __expf(m - mn), p = __expf(sc - mn);
-      l = l * al + p;
-      a0 = a0 * al + p * (lane < hd ? vp[lane] : 0.f);
-      a1 = a1 * al + p * (lane + 64 < hd ? vp[lane + 64] : 0.f);
-      m = mn;
+  const int n_pre = sq.kv_pre_len, n_kv = n_pre + sq.len;
+  const int qi = blk.q0 + qloc;
+  const bool active = qi < sq.len;
+  const int kv_end = n_pre + min(blk.q0 + BQ32, sq.len);
+  float qr[QD], acc[QD];
+  {
+    const float* qp = q + (long long)(sq.q_row0 + min(qi, sq.len - 1)) * ldq + h * HD32 + sub * QD;
+#pragma unroll
+    for (int d = 0; d < QD; d += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(qp + d);
+      qr[d] = t.x; qr[d + 1] = t.y; qr[d + 2] = t.z; qr[d + 3] = t.w;
     }
-    float* op = o + (long long)(sq.q_row0 + qi) * ldo + h * hd;
-    if (lane < hd) op[lane] = a0 / l;
-    if (lane + 64 < hd) op[lane + 64] = a1 / l;
   }
+#pragma unroll
+  for (int d = 0; d < QD; ++d) acc[d] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int j0 = 0; j0 < kv_end; j0 += BK32) {
+    __syncthreads();   // the previous block's reads are done
+    constexpr int F4 = BK32 * HD32 / 4;
+    for (int c = tid; c < F4; c += 256) {
+      const int key = c / (HD32 / 4), d4 = (c % (HD32 / 4)) * 4;
+      const int j = j0 + key;
+      float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
+      if (j < n_kv) {
+        const long long row = j < n_pre ? (long long)sq.kv_pre_row0 + j : (long long)sq.kv_row0 + (j - n_pre);
+        kv4 = *reinterpret_cast<const float4*>(k + row * ldkv + kvh * HD32 + d4);
+        vv4 = *reinterpret_cast<const float4*>(v + row * ldkv + kvh * HD32 + d4);
+      }
+      *reinterpret_cast<float4*>(sK + key * KP + d4) = kv4;
+      *reinterpret_cast<float4*>(sV + key * KP + d4) = vv4;
+    }
+    __syncthreads();
+    float sc[BK32];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < BK32; ++kk) {
+      const float* kr = sK + kk * KP + sub * QD;
+      float part = 0.f;
+#pragma unroll
+      for (int d = 0; d < QD; ++d) part = fmaf(qr[d], kr[d], part);
+      part += __shfl_xor(part, 1, 64);
+      part += __shfl_xor(part, 2, 64);
+      const int j = j0 + kk;
+      const float val = (j <= n_pre + qi && j < n_kv) ? part * scale_log2 : -INFINITY;
+      sc[kk] = val;
+      mx = fmaxf(mx, val);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < QD; ++d) acc[d] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < BK32; ++kk) {
+      const float p = exp2f(sc[kk] - m_use);
+      l_run += p;
+      const float* vr = sV + kk * KP + sub * QD;
+#pragma unroll
+      for (int d = 0; d < QD; ++d) acc[d] = fmaf(p, vr[d], acc[d]);
+    }
+    m_run = m_new;
+  }
+  if (!active) return;
+  const float inv = 1.f / l_run;
+  float* op = o + (long long)(sq.q_row0 + qi) * ldo + h * HD32 + sub * QD;
+#pragma unroll
+  for (int d = 0; d < QD; d += 4)
+    *reinterpret_cast<float4*>(op + d) = make_float4(acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv);
 }
 
 }  // namespace
@@ -437,11 +490,19 @@ hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, c
       hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
                          blocks, Hq, Hkv, sl2, part.row_slot, part.row_base, part.pO, part.pML);
   } else {
-    if (hd > 128) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, reinterpret_cast<const float*>(q),
-                       ld_q, reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v),
-                       ld_kv, reinterpret_cast<float*>(o), ld_o, seqs, blocks, Hq, Hkv, hd,
-                       1.f / sqrtf((float)hd));
+    const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
+    const auto* qq = reinterpret_cast<const float*>(q);
+    const auto* kk = reinterpret_cast<const float*>(k);
+    const auto* vv = reinterpret_cast<const float*>(v);
+    auto* oo = reinterpret_cast<float*>(o);
+    if (hd == 64)
+      hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(256), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs, blocks,
+                         Hq, Hkv, sl2);
+    else if (hd == 128)
+      hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
+                         blocks, Hq, Hkv, sl2);
+    else
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

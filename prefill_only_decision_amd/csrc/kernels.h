@@ -47,6 +47,7 @@ struct GemmArgs {
   const float* norm_w;
   void* norm_out;
   float norm_eps;
+  int staged;            // set by launch_gemm: bf16 outputs staged through LDS
 };
 
 // Runs the GEMM.  tile_cfg >= 0 picks a tile configuration (0 .. 

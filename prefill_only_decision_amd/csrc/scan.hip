@@ -289,53 +289,96 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
-// fp32 path (small models): the recurrence token by token.  One workgroup
-// per (sequence, head); each thread owns state elements of one value column.
+// fp32 path (small models): the chunked form of the recurrence.  One
+// workgroup per (sequence, head) walks the sequence in chunks of 32 tokens;
+// thread t owns value column t % DV and state rows t / DV + IST u of the
+// fp32 state.  Per chunk, with G_t the chunk-local cumulative log gate:
+//   A[t][s] = (q_t . k_s) exp(G_t - G_s) for s <= t      (LDS)
+//   O[t] = A V + exp(G_t) q_t S0                           (q_t S0 summed over the IST threads of a column)
+//   S0 <- exp(G_last) S0 + sum_s exp(G_last - G_s) k_s v_s^T
+// Every decay is the exponential of a difference, at most 1.
+template <int DK, int DV>
 __global__ void __launch_bounds__(256)
 scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const float* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
                 float* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
-                float* __restrict__ states, int H, int dk, int dv) {
-  __shared__ float sq_[128], sk_[128], sv_[128], part[256];
-  __shared__ float sg;
+                float* __restrict__ states, int H) {
+  constexpr int CC = 32;
+  constexpr int IST = 256 / DV, NI = DK / IST;
+  __shared__ float sQ[CC][DK + 1], sK[CC][DK + 1], sV[CC][DV + 1], sA[CC][CC + 1];
+  __shared__ float sQS[IST][CC][DV + 1];
+  __shared__ float sG[CC];
   const int tid = threadIdx.x, seq = blockIdx.x, h = blockIdx.y;
   const ScanSeq sq = seqs[seq];
-  const int j = tid % dv, i0 = tid / dv, istep = 256 / dv, ni = dk / istep;
-  float Sr[128];
-  for (int u = 0; u < ni; ++u) {
-    const int i = i0 + u * istep;
-    Sr[u] = sq.s_in >= 0 ? states[(((long long)sq.s_in * H + h) * dk + i) * dv + j] : 0.f;
+  const int col = tid % DV, i0 = tid / DV;
+  float S[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u)
+    S[u] = sq.s_in >= 0 ? states[(((long long)sq.s_in * H + h) * DK + i0 + u * IST) * DV + col] : 0.f;
+  for (int c0 = 0; c0 < sq.len; c0 += CC) {
+    const int n = min(CC, sq.len - c0);
+    const long long base = (long long)sq.row0 + c0;
+    __syncthreads();   // the previous chunk's reads of LDS are done
+    for (int e = tid; e < CC * DK; e += 256) {
+      const int t = e / DK, d = e % DK;
+      sQ[t][d] = t < n ? q[(base + t) * ldqkv + h * DK + d] : 0.f;
+      sK[t][d] = t < n ? k[(base + t) * ldqkv + h * DK + d] : 0.f;
+    }
+    for (int e = tid; e < CC * DV; e += 256) {
+      const int t = e / DV, d = e % DV;
+      sV[t][d] = t < n ? v[(base + t) * ldqkv + h * DV + d] : 0.f;
+    }
+    if (tid == 0) {
+      float g = 0.f;
+      for (int t = 0; t < CC; ++t) {
+        g += t < n ? lg[(base + t) * ldg + h] : 0.f;
+        sG[t] = g;
+      }
+    }
+    __syncthreads();
+    // decayed scores of the chunk, s <= t
+    for (int e = tid; e < CC * CC; e += 256) {
+      const int t = e / CC, s2 = e % CC;
+      float a = 0.f;
+      if (s2 <= t && t < n) {
+#pragma unroll 8
+        for (int d = 0; d < DK; ++d) a = fmaf(sQ[t][d], sK[s2][d], a);
+        a *= __expf(sG[t] - sG[s2]);
+      }
+      sA[t][s2] = a;
+    }
+    // q_t S0 over this thread's state rows
+    for (int t = 0; t < n; ++t) {
+      float part = 0.f;
+#pragma unroll
+      for (int u = 0; u < NI; ++u) part = fmaf(sQ[t][i0 + u * IST], S[u], part);
+      sQS[i0][t][col] = part;
+    }
+    __syncthreads();
+    for (int t = i0; t < n; t += IST) {
+      float inter = 0.f;
+#pragma unroll
+      for (int x = 0; x < IST; ++x) inter += sQS[x][t][col];
+      float intra = 0.f;
+      for (int s2 = 0; s2 <= t; ++s2) intra = fmaf(sA[t][s2], sV[s2][col], intra);
+      o[(base + t) * ldo + h * DV + col] = intra + __expf(sG[t]) * inter;
+    }
+    // the state leaving the chunk
+    const float Gl = sG[n - 1];
+    const float dec = __expf(Gl);
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      float acc = dec * S[u];
+      const int kr = i0 + u * IST;
+      for (int s2 = 0; s2 < n; ++s2) acc = fmaf(__expf(Gl - sG[s2]) * sK[s2][kr], sV[s2][col], acc);
+      S[u] = acc;
+    }
   }
-  for (int t = 0; t < sq.len; ++t) {
-    const long long row = (long long)sq.row0 + t;
-    __syncthreads();
-    if (tid < dk) {
-      sq_[tid] = q[row * ldqkv + h * dk + tid];
-      sk_[tid] = k[row * ldqkv + h * dk + tid];
-    }
-    if (tid < dv) sv_[tid] = v[row * ldqkv + h * dv + tid];
-    if (tid == 0) sg = __expf(lg[row * ldg + h]);
-    __syncthreads();
-    float acc = 0.f;
-    const float g = sg, vj = sv_[j];
-    for (int u = 0; u < ni; ++u) {
-      const int i = i0 + u * istep;
-      Sr[u] = g * Sr[u] + sk_[i] * vj;
-      acc += Sr[u] * sq_[i];
-    }
-    part[tid] = acc;
-    __syncthreads();
-    if (tid < dv) {
-      float s = 0.f;
-      for (int x = 0; x < istep; ++x) s += part[x * dv + tid];
-      o[row * ldo + h * dv + tid] = s;
-    }
+  if (sq.s_out >= 0) {
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      states[(((long long)sq.s_out * H + h) * DK + i0 + u * IST) * DV + col] = S[u];
   }
-  if (sq.s_out >= 0)
-    for (int u = 0; u < ni; ++u) {
-      const int i = i0 + u * istep;
-      states[(((long long)sq.s_out * H + h) * dk + i) * dv + j] = Sr[u];
-    }
 }
 
 // Scan of chunk states across the chunks of each sequence, elementwise over
@@ -418,11 +461,24 @@ hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, i
     return launch_mode<MODE_FULL>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, seqs, n_seqs, states, H, nullptr,
                                   chains >= 256 ? 4 : (chains >= 128 ? 2 : 1), s);
   } else {
-    if (dk > 128 || dv > 128 || 256 % dv != 0 || dk % (256 / dv) != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(scan_f32_kernel, dim3(n_seqs, H), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
-                       reinterpret_cast<const float*>(v), ld_qkv, log_g, ld_g,
-                       reinterpret_cast<float*>(o), ld_o, seqs, states, H, dk, dv);
+    const auto* qq = reinterpret_cast<const float*>(q);
+    const auto* kk = reinterpret_cast<const float*>(k);
+    const auto* vv = reinterpret_cast<const float*>(v);
+    auto* oo = reinterpret_cast<float*>(o);
+    if (dk == 64 && dv == 64)
+      hipLaunchKernelGGL((scan_f32_kernel<64, 64>), dim3(n_seqs, H), dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g,
+                         ld_g, oo, ld_o, seqs, states, H);
+    else if (dk == 128 && dv == 128)
+      hipLaunchKernelGGL((scan_f32_kernel<128, 128>), dim3(n_seqs, H), dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g,
+                         ld_g, oo, ld_o, seqs, states, H);
+    else if (dk == 128 && dv == 64)
+      hipLaunchKernelGGL((scan_f32_kernel<128, 64>), dim3(n_seqs, H), dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g,
+                         ld_g, oo, ld_o, seqs, states, H);
+    else if (dk == 64 && dv == 128)
+      hipLaunchKernelGGL((scan_f32_kernel<64, 128>), dim3(n_seqs, H), dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g,
+                         ld_g, oo, ld_o, seqs, states, H);
+    else
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
