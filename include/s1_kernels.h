@@ -42,6 +42,18 @@ int s1k_gemm(int32_t dtype, const void* A, const void* W, float* C, int32_t M, i
 int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
                  int32_t K, int32_t split_k, int32_t tile_cfg, void* hip_stream);
 
+/* s1k_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and results, with the split-K partial sums in a file-scope
+ * device array of S1K_NOALLOC_SCRATCH_BYTES per GPU (held until the process
+ * ends) instead of a per-call workspace; it calls no allocator.  S1_EINVAL
+ * when split_k * M * N * 4 exceeds that size.  Every call on one GPU shares
+ * its array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller. */
+#define S1K_NOALLOC_SCRATCH_BYTES (32u << 20)
+int s1k_gemm_noalloc(int32_t dtype, const void* A, const void* W, float* C, int32_t M, int32_t N,
+                     int32_t K, int32_t split_k, void* hip_stream);
+
 /* Number of GEMM tile configurations (host-only, no device work). */
 int s1k_gemm_tile_configs(void);
 

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libs1.so")
-SOURCES = ["abi.cpp", "executor.cpp", "gemm.hip", "attention.hip", "scan.hip", "misc.hip", "vocab.hip", "gdn.hip", "peak.hip"]
+SOURCES = ["abi.cpp", "executor.cpp", "gemm.hip", "attention.hip", "scan.hip", "misc.hip", "vocab.hip", "gdn.hip", "peak.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
