@@ -1,6 +1,8 @@
 // C ABI of the library: argument validation, error reporting, entry points.
 #include <algorithm>
 #include <chrono>
+#include <cstdlib>
+#include <mutex>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -22,6 +24,48 @@ int set_error(int code, const std::string& msg) {
 
 std::string hip_msg(hipError_t e, const char* what) {
   return std::string(what) + ": " + hipGetErrorString(e);
+}
+
+namespace {
+std::mutex g_alloc_mu;
+std::string g_alloc_env;   // the hook's value when the count started
+long long g_alloc_count = 0;
+
+// True when the S1_TEST_FAIL_ALLOC hook says this allocation fails.
+bool injected_failure() {
+  std::lock_guard<std::mutex> lock(g_alloc_mu);
+  const char* e = std::getenv("S1_TEST_FAIL_ALLOC");
+  const std::string v = e ? e : "";
+  if (v != g_alloc_env) {
+    g_alloc_env = v;
+    g_alloc_count = 0;
+  }
+  if (v.empty()) return false;
+  const long long n = std::atoll(v.c_str());
+  return ++g_alloc_count == n;
+}
+}  // namespace
+
+hipError_t dev_alloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (injected_failure()) return hipErrorOutOfMemory;
+  const hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+  }
+  return e;
+}
+
+hipError_t dev_alloc_async(void** p, size_t bytes, hipStream_t s) {
+  *p = nullptr;
+  if (injected_failure()) return hipErrorOutOfMemory;
+  const hipError_t e = hipMallocAsync(p, bytes, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+  }
+  return e;
 }
 
 int validate_config(const s1_config* c) {
@@ -368,7 +412,7 @@ int gemm_entry(int32_t dtype, const void* A, const void* W, float* C, int32_t M,
   g.ld0 = N;
   float* ws = nullptr;
   if (split_k > 1) {
-    if (hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)split_k * M * N * sizeof(float) + 256, strm(hip_stream)) != hipSuccess)
+    if (dev_alloc_async(reinterpret_cast<void**>(&ws), (size_t)split_k * M * N * sizeof(float) + 256, strm(hip_stream)) != hipSuccess)
       return set_error(S1_ENOMEM, "s1k_gemm: workspace allocation failed");
   }
   const hipError_t e = launch_gemm(bf16, EPI_F32, g, split_k, ws, strm(hip_stream), tile_cfg);
@@ -479,7 +523,8 @@ int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int3
   float* st = nullptr;
   ScanSeq* dseq = nullptr;
   hipStream_t s = strm(hip_stream);
-  if (hipMalloc(&st, sbytes) != hipSuccess || hipMalloc(&dseq, seqs.size() * sizeof(ScanSeq)) != hipSuccess) {
+  if (dev_alloc(reinterpret_cast<void**>(&st), sbytes) != hipSuccess ||
+      dev_alloc(reinterpret_cast<void**>(&dseq), seqs.size() * sizeof(ScanSeq)) != hipSuccess) {
     (void)hipGetLastError();
     if (st) (void)hipFree(st);
     return set_error(S1_ENOMEM, "s1k_la_scan: allocation failed");
@@ -524,7 +569,7 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
                        nc * sizeof(ScanSeq) + cseqs.size() * sizeof(ChunkSeq) + 1024;
   char* buf = nullptr;
   hipStream_t s = strm(hip_stream);
-  if (hipMalloc(&buf, bytes) != hipSuccess) {
+  if (dev_alloc(reinterpret_cast<void**>(&buf), bytes) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_la_scan_chunked: allocation failed");
   }
@@ -569,7 +614,7 @@ int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, co
   const size_t b1 = chunks.size() * sizeof(ScanSeq), b2 = seqs.size() * sizeof(GdnSeq);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   char* dm = nullptr;
-  if (hipMalloc(&dm, al(sbytes) + al(wbytes) + al(b1) + al(b2)) != hipSuccess) {
+  if (dev_alloc(reinterpret_cast<void**>(&dm), al(sbytes) + al(wbytes) + al(b1) + al(b2)) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_gdn_scan: allocation failed");
   }
@@ -628,7 +673,7 @@ int s1k_attention(int32_t dtype, const void* q, const void* k, const void* v, vo
   const size_t o_c = take(ap.comb_rows.size() * 4), o_po = take((size_t)ap.slots * Hq * hd * 4);
   const size_t o_pm = take((size_t)ap.slots * Hq * 8);
   void* dm = nullptr;
-  if (hipMalloc(&dm, off + 256) != hipSuccess) {
+  if (dev_alloc(&dm, off + 256) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_attention: allocation failed");
   }
@@ -721,7 +766,7 @@ int s1k_vocab_lse(int32_t dtype, const float* x, int32_t d, const float* w_final
   hipStream_t s = strm(hip_stream);
   const FeatWs w = feat_ws_layout(bf16, R, V, d);
   void* ws = nullptr;
-  if (hipMallocAsync(&ws, w.bytes, s) != hipSuccess) {
+  if (dev_alloc_async(&ws, w.bytes, s) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_vocab_lse: allocation failed");
   }
@@ -751,7 +796,7 @@ int s1k_token_logprobs(int32_t dtype, const float* x, int32_t n_rows, int32_t d,
   const FeatWs w = feat_ws_layout(bf16, (int)h.rows.size(), V, d);
   const size_t meta = h.meta_bytes();
   void* dm = nullptr;
-  if (hipMalloc(&dm, meta + w.bytes) != hipSuccess) {
+  if (dev_alloc(&dm, meta + w.bytes) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "s1k_token_logprobs: allocation failed");
   }

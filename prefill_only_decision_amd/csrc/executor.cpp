@@ -73,10 +73,7 @@ Model::~Model() {
 void* Model::alloc(size_t bytes) {
   void* p = nullptr;
   if (bytes == 0) bytes = 256;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    throw std::bad_alloc();
-  }
+  if (dev_alloc(&p, bytes) != hipSuccess) throw std::bad_alloc();
   allocs.push_back(p);
   return p;
 }
@@ -139,7 +136,7 @@ class Loader {
       return S1_OK;
     }
     void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
+    if (dev_alloc(&p, bytes) != hipSuccess) {
       (void)hipGetLastError();
       return set_error(S1_ENOMEM, "device allocation for '" + name + "' failed");
     }
@@ -165,7 +162,7 @@ class Loader {
     }
     int* dmap = nullptr;
     if (!map.empty()) {
-      if (hipMalloc(&dmap, map.size() * sizeof(int)) != hipSuccess) {
+      if (dev_alloc(reinterpret_cast<void**>(&dmap), map.size() * sizeof(int)) != hipSuccess) {
         (void)hipGetLastError();
         return set_error(S1_ENOMEM, "device allocation failed");
       }
@@ -570,7 +567,7 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity, bool
       m->decide_dev = nullptr;
       m->decide_bytes = 0;
       const size_t want = std::max<size_t>(off, 1 << 20);
-      if (hipMalloc(&m->decide_dev, want) != hipSuccess) {
+      if (dev_alloc(&m->decide_dev, want) != hipSuccess) {
         (void)hipGetLastError();
         m->decide_dev = nullptr;
         delete p;
@@ -580,7 +577,7 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity, bool
     }
     p->dev = m->decide_dev;
     p->dev_owned = false;
-  } else if (hipMalloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
+  } else if (dev_alloc(&p->dev, std::max<size_t>(off, 256)) != hipSuccess) {
     (void)hipGetLastError();
     p->dev = nullptr;
     delete p;
@@ -722,7 +719,7 @@ int set_capture(Plan* p, int n_rows, const int32_t* rows, float* d_hidden) {
     lists[ps][0].push_back(r);
     lists[ps][1].push_back(j);
   }
-  if (hipMalloc(&p->cap_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
+  if (dev_alloc(&p->cap_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
     (void)hipGetLastError();
     return set_error(S1_ENOMEM, "device allocation for capture failed");
   }
@@ -766,7 +763,7 @@ int set_layer_inputs(Plan* p, int n_rows, const int32_t* rows, const float* d_sr
     lists[ps][0].push_back(r);
     lists[ps][1].push_back(j);
   }
-  if (hipMalloc(&p->inj_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
+  if (dev_alloc(&p->inj_dev, 8 * (size_t)n_rows + 512) != hipSuccess) {
     (void)hipGetLastError();
     p->inj_dev = nullptr;
     return set_error(S1_ENOMEM, "device allocation for layer inputs failed");
@@ -885,7 +882,7 @@ int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp,
   if (rc) return rc;
   const FeatWs w = feat_ws_layout(m->bf16, (int)h.rows.size(), c.vocab, c.d_model);
   const size_t meta = h.meta_bytes();
-  if (hipMalloc(&p->feat_dev, meta + w.bytes + 256) != hipSuccess) {
+  if (dev_alloc(&p->feat_dev, meta + w.bytes + 256) != hipSuccess) {
     (void)hipGetLastError();
     p->feat_dev = nullptr;
     return set_error(S1_ENOMEM, "device allocation for features failed");

@@ -15,6 +15,15 @@ namespace s1 {
 int set_error(int code, const std::string& msg);
 std::string hip_msg(hipError_t e, const char* what);
 
+// Device allocation, used by every allocating path of the library.  Test
+// hook (forced from the host, no device fault involved): with
+// S1_TEST_FAIL_ALLOC=n (or n@tag) in the environment, the n-th allocation
+// counted from the last change of that variable's text fails as if the
+// device were out of memory, so that every ENOMEM cleanup path can be
+// exercised; a new tag restarts the count for the same n.
+hipError_t dev_alloc(void** p, size_t bytes);
+hipError_t dev_alloc_async(void** p, size_t bytes, hipStream_t s);
+
 struct LayerW {
   bool full = false;
   int la_idx = -1, fa_idx = -1;

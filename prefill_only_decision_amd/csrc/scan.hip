@@ -305,9 +305,14 @@ scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 float* __restrict__ states, int H) {
   constexpr int CC = 32;
   constexpr int IST = 256 / DV, NI = DK / IST;
-  __shared__ float sQ[CC][DK + 1], sK[CC][DK + 1], sV[CC][DV + 1], sA[CC][CC + 1];
+  constexpr int QF = CC * DK / 4 / 256, VF = CC * DV / 4 / 256;   // float4 loads per thread
+  static_assert(QF >= 1 && VF >= 1 && QF * 1024 == CC * DK && VF * 1024 == CC * DV, "chunk / thread mismatch");
+  __shared__ __attribute__((aligned(16))) float sQ[CC][DK + 4];
+  __shared__ __attribute__((aligned(16))) float sK[CC][DK + 4];
+  __shared__ __attribute__((aligned(16))) float sV[CC][DV + 4];
+  __shared__ float sA[CC][CC + 1];
   __shared__ float sQS[IST][CC][DV + 1];
-  __shared__ float sG[CC];
+  __shared__ float sG[CC], sEG[CC], sW[CC];
   const int tid = threadIdx.x, seq = blockIdx.x, h = blockIdx.y;
   const ScanSeq sq = seqs[seq];
   const int col = tid % DV, i0 = tid / DV;
@@ -315,34 +320,72 @@ scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
   for (int u = 0; u < NI; ++u)
     S[u] = sq.s_in >= 0 ? states[(((long long)sq.s_in * H + h) * DK + i0 + u * IST) * DV + col] : 0.f;
+  // the chunk's q, k, v and log gates are loaded into registers one chunk
+  // ahead (rows past the sequence read its last row and are zeroed at the
+  // LDS stores)
+  float4 qv[QF], kv[QF], vv[VF];
+  float lgv = 0.f;
+  auto load_chunk = [&](int c0) {
+    const int n = min(CC, sq.len - c0);
+    const long long base = (long long)sq.row0 + c0;
+#pragma unroll
+    for (int x = 0; x < QF; ++x) {
+      const int e = tid + 256 * x, t = e / (DK / 4), d4 = (e % (DK / 4)) * 4;
+      const long long row = base + min(t, n - 1);
+      qv[x] = *reinterpret_cast<const float4*>(q + row * ldqkv + h * DK + d4);
+      kv[x] = *reinterpret_cast<const float4*>(k + row * ldqkv + h * DK + d4);
+    }
+#pragma unroll
+    for (int x = 0; x < VF; ++x) {
+      const int e = tid + 256 * x, t = e / (DV / 4), d4 = (e % (DV / 4)) * 4;
+      vv[x] = *reinterpret_cast<const float4*>(v + (base + min(t, n - 1)) * ldqkv + h * DV + d4);
+    }
+    lgv = tid < n ? lg[(base + tid) * ldg + h] : 0.f;
+  };
+  if (sq.len > 0) load_chunk(0);
   for (int c0 = 0; c0 < sq.len; c0 += CC) {
     const int n = min(CC, sq.len - c0);
     const long long base = (long long)sq.row0 + c0;
     __syncthreads();   // the previous chunk's reads of LDS are done
-    for (int e = tid; e < CC * DK; e += 256) {
-      const int t = e / DK, d = e % DK;
-      sQ[t][d] = t < n ? q[(base + t) * ldqkv + h * DK + d] : 0.f;
-      sK[t][d] = t < n ? k[(base + t) * ldqkv + h * DK + d] : 0.f;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int x = 0; x < QF; ++x) {
+      const int e = tid + 256 * x, t = e / (DK / 4), d4 = (e % (DK / 4)) * 4;
+      *reinterpret_cast<float4*>(&sQ[t][d4]) = t < n ? qv[x] : z;
+      *reinterpret_cast<float4*>(&sK[t][d4]) = t < n ? kv[x] : z;
     }
-    for (int e = tid; e < CC * DV; e += 256) {
-      const int t = e / DV, d = e % DV;
-      sV[t][d] = t < n ? v[(base + t) * ldqkv + h * DV + d] : 0.f;
+#pragma unroll
+    for (int x = 0; x < VF; ++x) {
+      const int e = tid + 256 * x, t = e / (DV / 4), d4 = (e % (DV / 4)) * 4;
+      *reinterpret_cast<float4*>(&sV[t][d4]) = t < n ? vv[x] : z;
     }
-    if (tid == 0) {
-      float g = 0.f;
-      for (int t = 0; t < CC; ++t) {
-        g += t < n ? lg[(base + t) * ldg + h] : 0.f;
-        sG[t] = g;
+    if (tid < 64) {   // wave 0: cumulative log gate, its exponential, the decay to the chunk end
+      float g = lgv;
+#pragma unroll
+      for (int off = 1; off < CC; off <<= 1) {
+        const float t = __shfl_up(g, off, 64);
+        if (tid >= off) g += t;
+      }
+      const float gl = __shfl(g, n - 1, 64);
+      if (tid < CC) {
+        sG[tid] = g;
+        sEG[tid] = __expf(g);
+        sW[tid] = tid < n ? __expf(gl - g) : 0.f;
       }
     }
+    if (c0 + CC < sq.len) load_chunk(c0 + CC);
     __syncthreads();
     // decayed scores of the chunk, s <= t
     for (int e = tid; e < CC * CC; e += 256) {
       const int t = e / CC, s2 = e % CC;
       float a = 0.f;
       if (s2 <= t && t < n) {
-#pragma unroll 8
-        for (int d = 0; d < DK; ++d) a = fmaf(sQ[t][d], sK[s2][d], a);
+#pragma unroll
+        for (int d = 0; d < DK; d += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(&sQ[t][d]);
+          const float4 y = *reinterpret_cast<const float4*>(&sK[s2][d]);
+          a = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, a))));
+        }
         a *= __expf(sG[t] - sG[s2]);
       }
       sA[t][s2] = a;
@@ -361,17 +404,16 @@ scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
       for (int x = 0; x < IST; ++x) inter += sQS[x][t][col];
       float intra = 0.f;
       for (int s2 = 0; s2 <= t; ++s2) intra = fmaf(sA[t][s2], sV[s2][col], intra);
-      o[(base + t) * ldo + h * DV + col] = intra + __expf(sG[t]) * inter;
+      o[(base + t) * ldo + h * DV + col] = intra + sEG[t] * inter;
     }
     // the state leaving the chunk
-    const float Gl = sG[n - 1];
-    const float dec = __expf(Gl);
+    const float dec = __expf(sG[n - 1]);
 #pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      float acc = dec * S[u];
-      const int kr = i0 + u * IST;
-      for (int s2 = 0; s2 < n; ++s2) acc = fmaf(__expf(Gl - sG[s2]) * sK[s2][kr], sV[s2][col], acc);
-      S[u] = acc;
+    for (int u = 0; u < NI; ++u) S[u] *= dec;
+    for (int s2 = 0; s2 < n; ++s2) {
+      const float wv = sW[s2] * sV[s2][col];
+#pragma unroll
+      for (int u = 0; u < NI; ++u) S[u] = fmaf(sK[s2][i0 + u * IST], wv, S[u]);
     }
   }
   if (sq.s_out >= 0) {
