@@ -1,5 +1,6 @@
 // C ABI of the library: argument validation, error reporting, entry points.
 #include <algorithm>
+#include <climits>
 #include <chrono>
 #include <cstdlib>
 #include <mutex>
@@ -552,20 +553,25 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
   if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T) return set_error(S1_EINVAL, "s1k_la_scan_chunked: cu_seqlens out of range");
   std::vector<ScanSeq> chunks;
   std::vector<ChunkSeq> cseqs;
+  int max_nc = 0;
   for (int i = 0; i < n_seqs; ++i) {
     const int len = cu_seqlens[i + 1] - cu_seqlens[i];
     if (len < 0) return set_error(S1_EINVAL, "s1k_la_scan_chunked: cu_seqlens decreasing");
-    ChunkSeq cs{(int)chunks.size(), 0, s_init ? i : -1, s_final ? i : -1};
+    // final states go to slots of their own (n_seqs + i): in the two-launch
+    // schedule one workgroup writes a sequence's final state while others
+    // still read its initial one
+    ChunkSeq cs{(int)chunks.size(), 0, s_init ? i : -1, s_final ? n_seqs + i : -1};
     for (int t0 = 0; t0 < len; t0 += 64) {
       const int id = (int)chunks.size();
       chunks.push_back({cu_seqlens[i] + t0, std::min(64, len - t0), id, id});
       ++cs.nc;
     }
+    max_nc = std::max(max_nc, cs.nc == 0 && cs.s_out >= 0 ? INT_MAX : cs.nc);
     cseqs.push_back(cs);
   }
   const size_t E = 128 * 128;
   const size_t nc = std::max<size_t>(1, chunks.size());
-  const size_t bytes = nc * H * E * 4 + nc * H * 4 + (size_t)n_seqs * H * E * 4 +
+  const size_t bytes = nc * H * E * 4 + nc * H * 4 + (size_t)2 * n_seqs * H * E * 4 +
                        nc * sizeof(ScanSeq) + cseqs.size() * sizeof(ChunkSeq) + 1024;
   char* buf = nullptr;
   hipStream_t s = strm(hip_stream);
@@ -577,7 +583,7 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
   float* gam = cst + nc * H * E;
   float* st = gam + nc * H + 64;
   st = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(st) + 255) & ~uintptr_t(255));
-  ScanSeq* dch = reinterpret_cast<ScanSeq*>(st + (size_t)n_seqs * H * E);
+  ScanSeq* dch = reinterpret_cast<ScanSeq*>(st + (size_t)2 * n_seqs * H * E);
   ChunkSeq* dcs = reinterpret_cast<ChunkSeq*>(dch + nc);
   hipError_t e = hipMemcpy(dch, chunks.data(), chunks.size() * sizeof(ScanSeq), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(dcs, cseqs.data(), cseqs.size() * sizeof(ChunkSeq), hipMemcpyHostToDevice);
@@ -585,8 +591,9 @@ int s1k_la_scan_chunked(const void* q, const void* k, const void* v, int32_t ld_
   if (e == hipSuccess && s_init) e = hipMemcpyAsync(st, s_init, sbytes, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_scan_chunked(q, k, v, ld_qkv, log_g, H, o, H * 128, dch, (int)chunks.size(), dcs, n_seqs, cst,
-                            gam, st, H, s);
-  if (e == hipSuccess && s_final) e = hipMemcpyAsync(s_final, st, sbytes, hipMemcpyDeviceToDevice, s);
+                            gam, st, H, s, max_nc);
+  if (e == hipSuccess && s_final)
+    e = hipMemcpyAsync(s_final, st + (size_t)n_seqs * H * E, sbytes, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(buf);
   return dev_status(e, "s1k_la_scan_chunked");

@@ -9,6 +9,7 @@
 // only at the questions' marker rows (sys1rust README, "How it works": the
 // head runs only at the positions the answer reads).
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <map>
 #include <new>
@@ -476,6 +477,8 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity, bool
         chunks[ps].push_back({sq.row0 + t0, std::min(64, sq.len - t0), id, id});
         ++cs.nc;
       }
+      // an empty sequence that keeps a state needs the separate state scan
+      p->pass[ps].max_nc = std::max(p->pass[ps].max_nc, cs.nc == 0 && cs.s_out >= 0 ? INT_MAX : cs.nc);
       cseqs[ps].push_back(cs);
     }
   }
@@ -992,7 +995,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       } else if (ps.chunked || (p->invariant && ps.n_chunks > 0))
         S1_TRY(launch_scan_chunked(qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es, m->ld_qkv,
                                    m->lg, H, att, m->ld_att, ps.chunks, ps.n_chunks, ps.cseqs, ps.n_seqs,
-                                   m->cstates, m->gamma, states, H, s),
+                                   m->cstates, m->gamma, states, H, s, ps.max_nc),
                "linear-attention scan (chunk-parallel)");
       else
         S1_TRY(launch_scan(m->bf16, qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es,

@@ -122,7 +122,8 @@ hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, i
 // `chunks` lists every chunk of up to 64 tokens (its s_in / s_out are its own
 // index); `cseqs` gives each sequence's chunk range and its initial / final
 // state slots in `states`.  cstates [n_chunks][H][128][128] and gamma
-// [n_chunks][H] are workspace.
+// [n_chunks][H] are workspace.  max_nc: the most chunks of one sequence
+// (chooses between two and three launches; the results are the same).
 // Gated DeltaNet scan: one sequence (rows row0 .. row0 + len - 1, chunks
 // c0 .. in the chunk list, state slots as ScanSeq).
 struct GdnSeq {
@@ -154,7 +155,7 @@ struct ChunkSeq {
 hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
                                int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
                                const ChunkSeq* cseqs, int n_cseqs, float* cstates, float* gamma,
-                               float* states, int H, hipStream_t s);
+                               float* states, int H, hipStream_t s, int max_nc);
 
 // -------------------------------------------------------------- attention
 struct AttnSeq {

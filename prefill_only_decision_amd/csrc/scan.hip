@@ -30,26 +30,39 @@ constexpr int C = 64, DK = 128, DV = 128;
 constexpr int QP = DK * 2 + 16;   // bytes per Q / K row in LDS
 constexpr int TP = C * 2 + 16;    // bytes per K^T / V^T row in LDS
 
+// Byte offset of K^T / V^T row d in LDS: 16 bytes of padding after every 16
+// rows.  The transposing stores of one instruction hit rows 8 apart (one
+// element pair of many 16-byte load chunks), which without it share a bank;
+// the reads of the products take 16 consecutive rows at a time, which the
+// padding leaves at the same relative addresses.
+__device__ __forceinline__ int trow(int d) { return d * TP + (d >> 4) * 16; }
+constexpr int trows_bytes(int rows) { return rows * TP + (rows / 16) * 16; }
+
 // MODE_FULL: the recurrence over whole sequences.  MODE_SUMMARY: one chunk
 // per entry from a zero state; writes only the chunk's state contribution and
 // its total log-decay.  MODE_OUTPUT: one chunk per entry from the state
-// entering it; writes only the outputs.
-enum { MODE_FULL = 0, MODE_SUMMARY = 1, MODE_OUTPUT = 2 };
+// entering it; writes only the outputs.  MODE_FOLD: MODE_OUTPUT that first
+// forms its entering state from the contributions of its sequence's earlier
+// chunks (S <- exp(gamma) S + dS in chunk order, the same operations as
+// chunk_state_scan_kernel), and whose last chunk writes the sequence's final
+// state: two launches in place of three for short sequences.
+enum { MODE_FULL = 0, MODE_SUMMARY = 1, MODE_OUTPUT = 2, MODE_FOLD = 3 };
 
 template <int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64)
 scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                  const bf16_t* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
                  bf16_t* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
-                 float* __restrict__ states, int H, float* __restrict__ gamma) {
+                 float* __restrict__ states, int H, float* __restrict__ gamma,
+                 const ChunkSeq* __restrict__ cseqs, int n_cseqs, float* __restrict__ seq_states) {
   constexpr int NT = NW * 64;
   constexpr int DVG = 32 * NW;        // value columns per workgroup
   constexpr int NDVG = DV / DVG;      // workgroups per (sequence, head)
   __shared__ __attribute__((aligned(16))) char sQ[C * QP];
   __shared__ __attribute__((aligned(16))) char sK[C * QP];
-  __shared__ __attribute__((aligned(16))) char sKt[DK * TP];     // decayed K^T, hi part
-  __shared__ __attribute__((aligned(16))) char sKl[DK * TP];     // decayed K^T, lo part
-  __shared__ __attribute__((aligned(16))) char sVt[DVG * TP];
+  __shared__ __attribute__((aligned(16))) char sKt[trows_bytes(DK)];     // decayed K^T, hi part
+  __shared__ __attribute__((aligned(16))) char sKl[trows_bytes(DK)];     // decayed K^T, lo part
+  __shared__ __attribute__((aligned(16))) char sVt[trows_bytes(DVG)];
   __shared__ float sG[C];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -60,13 +73,37 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int dv0 = dvw + wave * 32;    // first value column of this wave
 
   floatx16 S[DK / 32];                // S[a][r] = S[32a + acc_row(r)][dv0 + cl]
+  auto st_at = [&](float* base, long long slot, int a, int r) {
+    return base + ((slot * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl;
+  };
+  ChunkSeq cs{0, 0, -1, -1};
+  if constexpr (MODE == MODE_FOLD) {
+    // this chunk's sequence: the last entry whose first chunk is at or before it
+    int lo = 0, hi2 = n_cseqs - 1;
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (cseqs[mid].c0 <= seq) lo = mid;
+      else hi2 = mid - 1;
+    }
+    cs = cseqs[lo];
 #pragma unroll
-  for (int a = 0; a < DK / 32; ++a)
+    for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      S[a][r] = (MODE != MODE_SUMMARY && sq.s_in >= 0)
-                    ? states[(((long long)sq.s_in * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl]
-                    : 0.f;
+      for (int r = 0; r < 16; ++r) S[a][r] = cs.s_in >= 0 ? *st_at(seq_states, cs.s_in, a, r) : 0.f;
+    for (int c = cs.c0; c < seq; ++c) {
+      const float g = __expf(gamma[(long long)c * H + h]);
+#pragma unroll
+      for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[a][r] = fmaf(g, S[a][r], *st_at(states, c, a, r));
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        S[a][r] = (MODE != MODE_SUMMARY && sq.s_in >= 0) ? *st_at(states, sq.s_in, a, r) : 0.f;
+  }
 
   // Each chunk's global loads (rows past its end read its last row, in
   // bounds, and are replaced by zeros at the LDS stores).  Four-wave
@@ -137,7 +174,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(sK + s0 * QP + ch * 16) = ka;
       *reinterpret_cast<uint4*>(sK + s1 * QP + ch * 16) = kb;
-      if constexpr (MODE != MODE_OUTPUT) {
+      if constexpr (MODE != MODE_OUTPUT && MODE != MODE_FOLD) {
         const float w0 = __shfl(wK, s0, 64), w1 = __shfl(wK, s1, 64);
         const uint32_t a[4] = {ka.x, ka.y, ka.z, ka.w}, b[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
@@ -147,10 +184,11 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           const float x00 = lo_half(a[e]) * w0, x01 = lo_half(b[e]) * w1;
           const float x10 = hi_half(a[e]) * w0, x11 = hi_half(b[e]) * w1;
           const uint32_t h0 = cvt2(x00, x01), h1 = cvt2(x10, x11);
-          *reinterpret_cast<uint32_t*>(sKt + d0 * TP + 4 * p) = h0;
-          *reinterpret_cast<uint32_t*>(sKt + (d0 + 1) * TP + 4 * p) = h1;
-          *reinterpret_cast<uint32_t*>(sKl + d0 * TP + 4 * p) = cvt2(x00 - lo_half(h0), x01 - hi_half(h0));
-          *reinterpret_cast<uint32_t*>(sKl + (d0 + 1) * TP + 4 * p) = cvt2(x10 - lo_half(h1), x11 - hi_half(h1));
+          const int r0 = trow(d0) + 4 * p, r1 = trow(d0 + 1) + 4 * p;
+          *reinterpret_cast<uint32_t*>(sKt + r0) = h0;
+          *reinterpret_cast<uint32_t*>(sKt + r1) = h1;
+          *reinterpret_cast<uint32_t*>(sKl + r0) = cvt2(x00 - lo_half(h0), x01 - hi_half(h0));
+          *reinterpret_cast<uint32_t*>(sKl + r1) = cvt2(x10 - lo_half(h1), x11 - hi_half(h1));
         }
       }
     }
@@ -164,14 +202,14 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d0 = ch * 8 + 2 * e;
-        *reinterpret_cast<uint32_t*>(sVt + d0 * TP + 4 * p) = (a[e] & 0xFFFFu) | (b[e] << 16);
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 1) * TP + 4 * p) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sVt + trow(d0) + 4 * p) = (a[e] & 0xFFFFu) | (b[e] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + trow(d0 + 1) + 4 * p) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
       }
     }
     if (PREFETCH && c0 + C < sq.len) load_chunk(c0 + C);
     __syncthreads();
 
-    const char* vrow = sVt + (wave * 32 + cl) * TP;
+    const char* vrow = sVt + trow(wave * 32 + cl);
     if constexpr (MODE != MODE_SUMMARY) {
     // (a) score tiles A^T[s][t] = k_s . q_t for s-tile st <= t-tile tt
     floatx16 At[3];   // (0,0), (0,1), (1,1)
@@ -260,15 +298,15 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
 
     }  // MODE != MODE_SUMMARY
-    if constexpr (MODE != MODE_OUTPUT) {
+    if constexpr (MODE != MODE_OUTPUT && MODE != MODE_FOLD) {
     // (c) S = exp(G_last) S + (K . w)^T V
     const float dec = __expf(Glast);
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[a][r] *= dec;
-      const char* kt = sKt + (32 * a + cl) * TP + 16 * hi;
-      const char* kl = sKl + (32 * a + cl) * TP + 16 * hi;
+      const char* kt = sKt + trow(32 * a + cl) + 16 * hi;
+      const char* kl = sKl + trow(32 * a + cl) + 16 * hi;
       const char* vt = vrow + 16 * hi;
 #pragma unroll
       for (int ks = 0; ks < C / 16; ++ks) {
@@ -280,12 +318,19 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }  // MODE != MODE_OUTPUT
   }
 
-  if (MODE != MODE_OUTPUT && sq.s_out >= 0) {
+  if constexpr (MODE == MODE_FOLD) {
+    if (seq == cs.c0 + cs.nc - 1 && cs.s_out >= 0) {   // the sequence's final state
+      const float g = __expf(gamma[(long long)seq * H + h]);
+#pragma unroll
+      for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) *st_at(seq_states, cs.s_out, a, r) = fmaf(g, S[a][r], *st_at(states, seq, a, r));
+    }
+  } else if (MODE != MODE_OUTPUT && sq.s_out >= 0) {
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        states[(((long long)sq.s_out * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl] = S[a][r];
+      for (int r = 0; r < 16; ++r) *st_at(states, sq.s_out, a, r) = S[a][r];
   }
 }
 
@@ -439,7 +484,7 @@ chunk_state_scan_kernel(const ChunkSeq* __restrict__ cseqs, const float* __restr
     float* slot = cstates + ((long long)c * H + h) * E + e;
     const float d = *slot;
     *slot = sv;
-    sv = __expf(gamma[(long long)c * H + h]) * sv + d;
+    sv = fmaf(__expf(gamma[(long long)c * H + h]), sv, d);
   }
   if (cs.s_out >= 0) states[((long long)cs.s_out * H + h) * E + e] = sv;
 }
@@ -447,16 +492,17 @@ chunk_state_scan_kernel(const ChunkSeq* __restrict__ cseqs, const float* __restr
 template <int MODE>
 hipError_t launch_mode(const bf16_t* qq, const bf16_t* kk, const bf16_t* vv, int ld_qkv, const float* log_g,
                        int ld_g, bf16_t* oo, int ld_o, const ScanSeq* seqs, int n_seqs, float* states, int H,
-                       float* gamma, int nw, hipStream_t s) {
+                       float* gamma, int nw, hipStream_t s, const ChunkSeq* cseqs = nullptr, int n_cseqs = 0,
+                       float* seq_states = nullptr) {
   if (nw == 4)
     hipLaunchKernelGGL((scan_bf16_kernel<4, MODE>), dim3(n_seqs * 1, H), dim3(256), 0, s, qq, kk, vv, ld_qkv,
-                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma, cseqs, n_cseqs, seq_states);
   else if (nw == 2)
     hipLaunchKernelGGL((scan_bf16_kernel<2, MODE>), dim3(n_seqs * 2, H), dim3(128), 0, s, qq, kk, vv, ld_qkv,
-                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma, cseqs, n_cseqs, seq_states);
   else
     hipLaunchKernelGGL((scan_bf16_kernel<1, MODE>), dim3(n_seqs * 4, H), dim3(64), 0, s, qq, kk, vv, ld_qkv,
-                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma);
+                       log_g, ld_g, oo, ld_o, seqs, states, H, gamma, cseqs, n_cseqs, seq_states);
   return hipGetLastError();
 }
 
@@ -465,7 +511,7 @@ hipError_t launch_mode(const bf16_t* qq, const bf16_t* kk, const bf16_t* vv, int
 hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int ld_qkv, const float* log_g,
                                int ld_g, void* o, int ld_o, const ScanSeq* chunks, int n_chunks,
                                const ChunkSeq* cseqs, int n_cseqs, float* cstates, float* gamma,
-                               float* states, int H, hipStream_t s) {
+                               float* states, int H, hipStream_t s, int max_nc) {
   if (n_chunks <= 0 || H <= 0) return hipSuccess;
   const auto* qq = reinterpret_cast<const bf16_t*>(q);
   const auto* kk = reinterpret_cast<const bf16_t*>(k);
@@ -481,6 +527,13 @@ hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int 
   hipError_t e = launch_mode<MODE_SUMMARY>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates,
                                            H, gamma, nw, s);
   if (e != hipSuccess) return e;
+  // sequences of up to FOLD_MAX chunks: each output workgroup folds its
+  // predecessors' contributions itself (up to FOLD_MAX - 1 state slices read
+  // per workgroup) in place of a separate scan over the chunk states
+  constexpr int FOLD_MAX = 16;
+  if (max_nc <= FOLD_MAX)
+    return launch_mode<MODE_FOLD>(qq, kk, vv, ld_qkv, log_g, ld_g, oo, ld_o, chunks, n_chunks, cstates, H, gamma,
+                                  nw, s, cseqs, n_cseqs, states);
   hipLaunchKernelGGL(chunk_state_scan_kernel, dim3(DK * DV / 256, n_cseqs * H), dim3(256), 0, s, cseqs, gamma,
                      cstates, states, H);
   e = hipGetLastError();
