@@ -168,7 +168,7 @@ int s1k_gdn_scan(const void* q, const void* k, const void* v, int32_t ld_qkv, co
  * kv_pre_len[i] ..); query j has position kv_pre_len[i] + j.  All five
  * arrays are host int32 [n_seqs].  bf16 needs hd = 128; fp32 hd 64 or 128.
  * block_rows: queries per workgroup, 0 to choose by size as the decoder
- * does; bf16 accepts 32, 64 or 128, fp32 64.  piece (bf16 only): 0 runs every
+ * does; bf16 accepts 32, 64 or 128, fp32 16.  piece (bf16 only): 0 runs every
  * query block over its whole key range in one workgroup; a positive multiple
  * of 64 cuts the keys at multiples of it into pieces run by separate
  * workgroups and merged in key order, and lets consecutive sequences that

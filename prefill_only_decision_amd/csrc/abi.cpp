@@ -514,30 +514,32 @@ int s1k_la_scan(int32_t dtype, const void* q, const void* k, const void* v, int3
   if (n_seqs > 0 && (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] > T))
     return set_error(S1_EINVAL, "s1k_la_scan: cu_seqlens out of range");
   if (n_seqs == 0) return S1_OK;
-  // one state buffer: initial states copied in, final states copied out
+  // one state buffer: initial states copied into slots 0 .. n_seqs - 1, final
+  // states written to slots n_seqs .. 2 n_seqs - 1 (the fp32 short-sequence
+  // kernel writes a final state while other workgroups read the initial one)
   std::vector<ScanSeq> seqs(n_seqs);
+  int max_len = 0;
   for (int i = 0; i < n_seqs; ++i) {
     if (cu_seqlens[i + 1] < cu_seqlens[i]) return set_error(S1_EINVAL, "s1k_la_scan: cu_seqlens decreasing");
-    seqs[i] = {cu_seqlens[i], cu_seqlens[i + 1] - cu_seqlens[i], s_init ? i : -1, -1};
+    seqs[i] = {cu_seqlens[i], cu_seqlens[i + 1] - cu_seqlens[i], s_init ? i : -1, s_final ? n_seqs + i : -1};
+    max_len = std::max(max_len, seqs[i].len);
   }
   const size_t sbytes = (size_t)n_seqs * H * dk * dv * sizeof(float);
   float* st = nullptr;
   ScanSeq* dseq = nullptr;
   hipStream_t s = strm(hip_stream);
-  if (dev_alloc(reinterpret_cast<void**>(&st), sbytes) != hipSuccess ||
+  if (dev_alloc(reinterpret_cast<void**>(&st), 2 * sbytes) != hipSuccess ||
       dev_alloc(reinterpret_cast<void**>(&dseq), seqs.size() * sizeof(ScanSeq)) != hipSuccess) {
     (void)hipGetLastError();
     if (st) (void)hipFree(st);
     return set_error(S1_ENOMEM, "s1k_la_scan: allocation failed");
   }
-  // the kernel reads slot s_in and writes slot s_out of the same buffer; with
-  // s_in == s_out == i the read happens before the write in the same workgroup
-  for (auto& q2 : seqs) q2.s_out = s_final ? (int)(&q2 - seqs.data()) : -1;
   hipError_t e = hipMemcpy(dseq, seqs.data(), seqs.size() * sizeof(ScanSeq), hipMemcpyHostToDevice);
   if (e == hipSuccess && s_init) e = hipMemcpyAsync(st, s_init, sbytes, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
-    e = launch_scan(bf16, q, k, v, ld_qkv, log_g, H, o, H * dv, dseq, n_seqs, st, H, dk, dv, s);
-  if (e == hipSuccess && s_final) e = hipMemcpyAsync(s_final, st, sbytes, hipMemcpyDeviceToDevice, s);
+    e = launch_scan(bf16, q, k, v, ld_qkv, log_g, H, o, H * dv, dseq, n_seqs, st, H, dk, dv, s, max_len);
+  if (e == hipSuccess && s_final)
+    e = hipMemcpyAsync(s_final, reinterpret_cast<char*>(st) + sbytes, sbytes, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(st);
   (void)hipFree(dseq);

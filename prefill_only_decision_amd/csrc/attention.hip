@@ -259,13 +259,16 @@ attn_combine_kernel(const int32_t* __restrict__ rows, int n_rows, const int32_t*
   *reinterpret_cast<uint32_t*>(o + (long long)row * ldo + h * HD + 2 * lane) = pack_bf2(a0 * inv, a1 * inv);
 }
 
-// fp32 path (small models).  A workgroup owns 64 queries of one head; four
-// threads share a query, each holding a quarter of its head dimensions.
-// Keys and values stream through LDS in blocks of 64; per block every
-// thread forms its query's 64 scores (partial dot products over its quarter,
-// summed across the four threads), takes the block maximum once, rescales
-// its output quarter once and accumulates p v for the block's keys.
-constexpr int BQ32 = 64, BK32 = 64;
+// fp32 path (small models).  A workgroup owns 16 queries of one head and
+// 16 threads share a query: four quarters of its head dimensions times four
+// key groups.  Keys and values stream through LDS in blocks of 64; key group
+// g takes keys g, g + 4, ... of each block (so that the causal cut leaves
+// the groups balanced) and keeps its own running maximum, sum and output
+// quarter, with scores from partial dot products summed across the four
+// dimension quarters.  The four groups are merged at the end with lane
+// exchanges.  Sixteen threads per query (not four) give the few queries of
+// a small request four times as many waves.
+constexpr int BQ32 = 16, BK32 = 64;
 template <int HD32>
 __global__ void __launch_bounds__(256)
 attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ k,
@@ -274,10 +277,11 @@ attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ 
                 int Hkv, float scale_log2) {
   constexpr int QD = HD32 / 4;                  // dimensions per thread
   constexpr int KP = HD32 + 4;                  // LDS row pitch (floats)
+  constexpr int KPG = BK32 / 4;                 // keys per group and block
   __shared__ __attribute__((aligned(16))) float sK[BK32 * KP];
   __shared__ __attribute__((aligned(16))) float sV[BK32 * KP];
   const int tid = threadIdx.x, h = blockIdx.y, kvh = h / (Hq / Hkv);
-  const int qloc = tid >> 2, sub = tid & 3;
+  const int qloc = tid >> 4, kg = (tid >> 2) & 3, sub = tid & 3;
   const AttnBlock blk = blocks[blockIdx.x];
   const AttnSeq sq = seqs[blk.seq];
   const int n_pre = sq.kv_pre_len, n_kv = n_pre + sq.len;
@@ -312,10 +316,11 @@ attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ 
       *reinterpret_cast<float4*>(sV + key * KP + d4) = vv4;
     }
     __syncthreads();
-    float sc[BK32];
+    float sc[KPG];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < BK32; ++kk) {
+    for (int i = 0; i < KPG; ++i) {
+      const int kk = kg + 4 * i;
       const float* kr = sK + kk * KP + sub * QD;
       float part = 0.f;
 #pragma unroll
@@ -324,7 +329,7 @@ attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ 
       part += __shfl_xor(part, 2, 64);
       const int j = j0 + kk;
       const float val = (j <= n_pre + qi && j < n_kv) ? part * scale_log2 : -INFINITY;
-      sc[kk] = val;
+      sc[i] = val;
       mx = fmaxf(mx, val);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -334,17 +339,31 @@ attn_f32_kernel(const float* __restrict__ q, int ldq, const float* __restrict__ 
 #pragma unroll
     for (int d = 0; d < QD; ++d) acc[d] *= alpha;
 #pragma unroll
-    for (int kk = 0; kk < BK32; ++kk) {
-      const float p = exp2f(sc[kk] - m_use);
+    for (int i = 0; i < KPG; ++i) {
+      const float p = exp2f(sc[i] - m_use);
       l_run += p;
-      const float* vr = sV + kk * KP + sub * QD;
+      const float* vr = sV + (kg + 4 * i) * KP + sub * QD;
 #pragma unroll
       for (int d = 0; d < QD; ++d) acc[d] = fmaf(p, vr[d], acc[d]);
     }
     m_run = m_new;
   }
-  if (!active) return;
-  const float inv = 1.f / l_run;
+  // merge the four key groups (lanes 4 and 8 apart)
+  float m_all = fmaxf(m_run, __shfl_xor(m_run, 4, 64));
+  m_all = fmaxf(m_all, __shfl_xor(m_all, 8, 64));
+  const float f = m_run == -INFINITY ? 0.f : exp2f(m_run - m_all);
+  float l = l_run * f;
+  l += __shfl_xor(l, 4, 64);
+  l += __shfl_xor(l, 8, 64);
+#pragma unroll
+  for (int d = 0; d < QD; ++d) {
+    float a = acc[d] * f;
+    a += __shfl_xor(a, 4, 64);
+    a += __shfl_xor(a, 8, 64);
+    acc[d] = a;
+  }
+  if (!active || kg != 0) return;
+  const float inv = 1.f / l;
   float* op = o + (long long)(sq.q_row0 + qi) * ldo + h * HD32 + sub * QD;
 #pragma unroll
   for (int d = 0; d < QD; d += 4)

@@ -454,6 +454,7 @@ int create_plan(Model* m, const s1_batch* b, Plan** out, int opts_capacity, bool
       const int pi = pre(i);
       const int P = pi >= 0 ? b->cu_seqlens[pi + 1] - b->cu_seqlens[pi] : 0;
       scan[ps].push_back({row0[i], len, pi >= 0 ? slot[pi] : -1, slot[i]});
+      p->pass[ps].max_len = std::max(p->pass[ps].max_len, len);
       attn.push_back({row0[i], len, row0[i], pi >= 0 ? row0[pi] : 0, P});
     }
     const int r0 = p->pass[ps].r0, Tp = p->pass[ps].T, Hq = m->cfg.fa_q_heads;
@@ -934,6 +935,11 @@ int max_split(const Model* m, const Plan* p, int M) {
   return M <= m->split_max_rows ? 4 : 1;
 }
 
+// GEMM configuration: chosen by shape, except that the row-invariant mode
+// keeps fp32 GEMMs on the one configuration whose K order does not depend on
+// the number of rows (bf16 configurations all share one K order).
+int gemm_cfg(const Model* m, const Plan* p) { return p->invariant && !m->bf16 ? 0 : GEMM_AUTO; }
+
 int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s) {
   const s1_config& c = m->cfg;
   const int d = c.d_model, H = c.la_heads, dk = c.la_dk, dv = c.la_dv;
@@ -978,7 +984,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
         g.out2 = m->beta + (size_t)r0 * H;
         g.nsplit2 = g.nsplit + H;
       }
-      S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s), "linear-attention in-projection");
+      S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s, gemm_cfg(m, p)), "linear-attention in-projection");
       MARK(KC_GEMM_LA_IN);
       float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
       if (gdn) {
@@ -999,7 +1005,8 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
                "linear-attention scan (chunk-parallel)");
       else
         S1_TRY(launch_scan(m->bf16, qkv, qkv + (size_t)H * dk * es, qkv + (size_t)2 * H * dk * es,
-                           m->ld_qkv, m->lg, H, att, m->ld_att, ps.scan, ps.n_seqs, states, H, dk, dv, s),
+                           m->ld_qkv, m->lg, H, att, m->ld_att, ps.scan, ps.n_seqs, states, H, dk, dv, s,
+                           p->invariant ? INT_MAX : ps.max_len),   // one fp32 schedule in the row-invariant mode
                "linear-attention scan");
       MARK(KC_LA_SCAN);
     } else {
@@ -1016,7 +1023,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       g.head_dim = hd;
       g.pos = p->pos + r0;
       g.rope = m->rope;
-      S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s), "attention QKV projection");
+      S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s, gemm_cfg(m, p)), "attention QKV projection");
       MARK(KC_GEMM_FA_QKV);
       const bool split = !p->invariant;
       S1_TRY(launch_attention(m->bf16, qkv, m->ld_qkv, kc, vc, (int)kvld, att, m->ld_att, ps.attn,
@@ -1042,7 +1049,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     go.norm_out = xn;
     go.norm_eps = c.rms_eps;
     bool normed = false;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, GEMM_AUTO, &normed),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &normed),
            "mixer out-projection");
     MARK(KC_GEMM_O);
     if (!normed) {
@@ -1064,7 +1071,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       gu.W = L.w_gu_frag;
       S1_TRY(launch_gemm_wd(EPI_SWIGLU, gu, wd, s), "FFN gate/up");
     } else {
-      S1_TRY(launch_gemm(m->bf16, EPI_SWIGLU, gu, 1, nullptr, s), "FFN gate/up");
+      S1_TRY(launch_gemm(m->bf16, EPI_SWIGLU, gu, 1, nullptr, s, gemm_cfg(m, p)), "FFN gate/up");
     }
     MARK(KC_GEMM_GATE_UP);
     GemmArgs gd{};
@@ -1082,7 +1089,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       gd.norm_out = xn;
       gd.norm_eps = c.rms_eps;
     }
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, GEMM_AUTO, &xn_ready),
+    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &xn_ready),
            "FFN down");
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {

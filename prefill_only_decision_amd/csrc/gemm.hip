@@ -1121,6 +1121,95 @@ splitk_resid_norm_kernel(const float* __restrict__ ws, int split, long long stri
   write_normed_row<T, 256, RN_MAXV>(v, ss, N, eps, w, nout + row * N);
 }
 
+// ----------------------------------------------- fp32 kernel for few tiles
+// fp32 GEMMs whose 128 x 128 tiles would leave most of the chip idle (the
+// small fp32 model at a few hundred rows).  A workgroup owns a 32 x 64
+// output tile and its four waves take consecutive quarters of the 16-element
+// K blocks of its K range.  Operands go from global memory straight into
+// MFMA registers: a lane loads eight consecutive K elements of its A row and
+// of its two W rows (two float4 each), and k-step j of a block contracts
+// elements j (lanes 0-31) and 8 + j (lanes 32-63), the same permutation of
+// K for both operands.  The next block's loads are issued before the current
+// block's products.  Waves 1-3 leave their partial tiles in LDS, wave 0 adds
+// them in wave order and runs the epilogue.  The K partition depends on K
+// (and the split) only.
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_f32_ks_kernel(GemmArgs g) {
+  __shared__ float red[3][32][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cl = lane & 31, hi = lane >> 5;
+  const int nbm = (g.M + 31) / 32;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = (t % nbm) * 32, n0 = (t / nbm) * 64;
+  const int kbeg = blockIdx.y * g.k_split, kend = min(g.K, kbeg + g.k_split);
+  const int nkb = kend > kbeg ? (kend - kbeg + 15) / 16 : 0;
+  const int kb0 = (nkb * wave) / 4, kb1 = (nkb * (wave + 1)) / 4;
+  const float* pa = static_cast<const float*>(g.A) + (long long)min(m0 + cl, g.M - 1) * g.lda + kbeg + 8 * hi;
+  const float* pw0 = static_cast<const float*>(g.W) + (long long)min(n0 + cl, g.N - 1) * g.ldw + kbeg + 8 * hi;
+  const float* pw1 = static_cast<const float*>(g.W) + (long long)min(n0 + 32 + cl, g.N - 1) * g.ldw + kbeg + 8 * hi;
+  const int klim = kend - kbeg - 8 * hi;   // elements of this lane's half-block still inside the K range
+  floatx16 acc[1][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][j][r] = 0.f;
+  // ops[0..1]: A, ops[2..3]: W rows n0 + cl, ops[4..5]: W rows n0 + 32 + cl
+  auto load = [&](int kb, float4 (&ops)[6]) {
+    const int k = kb * 16;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool in = k + 4 * q + 4 <= klim;   // K % 4 == 0: a float4 is wholly in or out
+      ops[q] = in ? *reinterpret_cast<const float4*>(pa + k + 4 * q) : z;
+      ops[2 + q] = in ? *reinterpret_cast<const float4*>(pw0 + k + 4 * q) : z;
+      ops[4 + q] = in ? *reinterpret_cast<const float4*>(pw1 + k + 4 * q) : z;
+    }
+  };
+  auto el = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
+  float4 cur[6], nxt[6];
+  if (kb0 < kb1) load(kb0, cur);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    if (kb + 1 < kb1) load(kb + 1, nxt);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = el(cur[j >> 2], j & 3);
+      mfma32(acc[0][0], a, el(cur[2 + (j >> 2)], j & 3));
+      mfma32(acc[0][1], a, el(cur[4 + (j >> 2)], j & 3));
+    }
+#pragma unroll
+    for (int q = 0; q < 6; ++q) cur[q] = nxt[q];
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave - 1][16 * j + r][lane] = acc[0][j][r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[0][j][r] += red[w][16 * j + r][lane];
+  epilogue<float, EPI, 1, 2>(g, acc, m0, n0, lane, blockIdx.y);
+}
+
+// Whether the fp32 few-tile kernel can run the launch (16-byte aligned
+// operand rows, K a multiple of 4).
+inline bool f32_ks_ok(const GemmArgs& a) {
+  return a.K % 4 == 0 && a.lda % 4 == 0 && a.ldw % 4 == 0 && reinterpret_cast<uintptr_t>(a.A) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.W) % 16 == 0;
+}
+
+template <int EPI>
+hipError_t run_f32_ks(const GemmArgs& a, int split, hipStream_t s) {
+  const int nbm = (a.M + 31) / 32, nbn = (a.N + 63) / 64;
+  hipLaunchKernelGGL((gemm_f32_ks_kernel<EPI>), dim3(nbm * nbn, split), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int EPI>
 hipError_t run_reg(const GemmArgs& a, int split, hipStream_t s) {
   constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
@@ -1162,8 +1251,14 @@ inline bool lds_ok(const GemmArgs& a) {
          abytes < (1LL << 31) && wbytes < (1LL << 31);
 }
 
+// Internal configuration: the fp32 few-tile kernel (chosen by shape only).
+constexpr int CFG_F32_FEW = 64;
+
 template <typename T, int EPI>
 hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
+  if constexpr (sizeof(T) == 4) {
+    if (cfg == CFG_F32_FEW && f32_ks_ok(a)) return run_f32_ks<EPI>(a, split, s);
+  }
   if constexpr (sizeof(T) == 2) {
     constexpr bool PAIR = EPI == EPI_SWIGLU || EPI == EPI_QKV;
     if (cfg > 0 && lds_ok(a)) {
@@ -1242,6 +1337,17 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
   const bool long_k = a.K >= 6144 && can_split;
   split = 1;
   if (!bf16) {
+    // fewer 128 x 128 tiles than CUs: 32 x 64 tiles with the K range split
+    // over the four waves of a workgroup (and over workgroups up to about
+    // one per CU for the fp32 outputs); the row-invariant mode asks for
+    // configuration 0 explicitly
+    const long long tf = (long long)((a.M + 31) / 32) * ((a.N + 63) / 64);
+    if (t128 < 256) {
+      cfg = CFG_F32_FEW;
+      if (can_split)
+        while (split < max_split && tf * (split + 1) <= 256 && a.K / (64 * (split + 1)) >= 2) ++split;
+      return;
+    }
     cfg = 0;
     if (can_split)
       while (split < max_split && t128 * (split + 1) <= 320 && a.K / (32 * (split + 1)) >= 4) ++split;

@@ -127,6 +127,7 @@ struct PassPlan {
   int n_chunks = 0;
   ChunkSeq* cseqs = nullptr;    // device [n_seqs]
   int max_nc = 0;               // most chunks of one sequence (INT_MAX: an empty one keeps a state)
+  int max_len = 0;              // longest sequence of the pass
   GdnSeq* gseqs = nullptr;      // device [n_seqs]: sequences with their first chunk
   int32_t* row_seq = nullptr;   // device [T]: each row's sequence in gseqs
   int32_t* cap_rows = nullptr;  // device [n_cap]: rows captured in this pass

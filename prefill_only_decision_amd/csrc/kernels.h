@@ -117,7 +117,7 @@ struct ScanSeq {
 };
 hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
                        const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
-                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s);
+                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s, int max_len);
 // Chunk-parallel form for few (sequence, head) chains (bf16, dk = dv = 128):
 // `chunks` lists every chunk of up to 64 tokens (its s_in / s_out are its own
 // index); `cseqs` gives each sequence's chunk range and its initial / final
@@ -175,7 +175,7 @@ struct AttnBlock {
 };
 // Queries per attention workgroup for sequences of these lengths: bf16 takes
 // the largest of 128, 64, 32 that still gives 512 workgroups over Hq heads
-// (else 32); fp32 uses 64.
+// (else 32); fp32 uses 16.
 int attn_block_rows(bool bf16, const int* lens, int n, int Hq);
 bool attn_block_rows_valid(bool bf16, int rows);
 

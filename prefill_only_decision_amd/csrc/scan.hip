@@ -468,6 +468,233 @@ scan_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   }
 }
 
+// fp32 path for short sequences (at most QMAX tokens): the chunked form with
+// the whole sequence as one chunk, so that no workgroup waits for another.
+// A workgroup owns 32 query rows [b, b + n) of one (sequence, head):
+//   o_t = sum_{s <= t} (q_t . k_s) exp(G_t - G_s) v_s + exp(G_t) q_t S0,
+// over key blocks of 32 staged in LDS.  The log-gate sums are taken from b:
+// R(x) = G_x - G_b, forward over the rows and backward over the earlier
+// keys, so the exponent G_t - G_s = R(t) - R(s) is formed from short sums
+// where the decay is not negligible.  One more workgroup per (sequence,
+// head) writes the final state, S = exp(G_last) S0 + sum_s exp(G_last - G_s)
+// k_s v_s^T, with the sums taken backward from the last token.  Initial and
+// final states must be different slots.
+constexpr int QMAX = 512;
+
+// R(x) for x = -1 .. b + n - 1 into r[x + 1] (r holds lg_x at x + 1 on entry,
+// anything at 0): backward sums from b, forward sums from b.  256 threads.
+__device__ __forceinline__ void log_gate_sums(float* r, int b, int n, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // backward: u_i = lg_{b - i}, i = 0..b; R(b - 1 - i) = -(u_0 + .. + u_i)
+  const int i0 = 2 * tid;
+  const float u0 = i0 <= b ? r[b - i0 + 1] : 0.f, u1 = i0 + 1 <= b ? r[b - i0] : 0.f;
+  // forward (wave 0): R(b + i) = lg_{b+1} + .. + lg_{b+i}
+  float f = (wave == 0 && lane >= 1 && lane < n) ? r[b + lane + 1] : 0.f;
+  float t = u0 + u1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float x = __shfl_up(t, off, 64);
+    if (lane >= off) t += x;
+  }
+  if (lane == 63) red[wave] = t;
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const float x = __shfl_up(f, off, 64);
+      if (lane >= off) f += x;
+    }
+  }
+  __syncthreads();   // every entry of r has been read
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += red[w];
+  const float p1 = base + t, p0 = p1 - u1;   // inclusive sums through u_{i0 + 1}, u_{i0}
+  if (i0 <= b) r[b - i0] = -p0;
+  if (i0 + 1 <= b) r[b - i0 - 1] = -p1;
+  if (wave == 0 && lane < n) r[b + lane + 1] = f;
+  __syncthreads();
+}
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(256)
+scan_f32_whole_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                      const float* __restrict__ v, int ldqkv, const float* __restrict__ lg, int ldg,
+                      float* __restrict__ o, int ldo, const ScanSeq* __restrict__ seqs,
+                      float* __restrict__ states, int H, int nqb) {
+  constexpr int QB = 32, KB = 32, CPT = DV / 8;   // columns per thread (rows x column groups = 32 x 8)
+  __shared__ __attribute__((aligned(16))) float sQ[QB][DK + 4];
+  __shared__ __attribute__((aligned(16))) float sK[KB][DK + 4];
+  __shared__ __attribute__((aligned(16))) float sV[KB][DV + 4];
+  __shared__ float sA[QB][KB + 1];
+  __shared__ float sR[QMAX + 1];
+  __shared__ float red[4];
+  const int tid = threadIdx.x, h = blockIdx.y;
+  const int seq = blockIdx.x / (nqb + 1), j = blockIdx.x % (nqb + 1);
+  const ScanSeq sq = seqs[seq];
+  const int L = sq.len, nq = (L + QB - 1) / QB;
+  const long long qoff = (long long)h * DK, voff = (long long)h * DV;
+  const long long sbase = (long long)h * DK * DV;
+  if (j < nq) {
+    const int b = j * QB, n = min(QB, L - b), span = b + n;   // keys 0 .. span - 1
+    for (int x = tid; x < span; x += 256) sR[x + 1] = lg[(long long)(sq.row0 + x) * ldg + h];
+    for (int e = tid; e < QB * DK / 4; e += 256) {
+      const int t = e / (DK / 4), d4 = (e % (DK / 4)) * 4;
+      *reinterpret_cast<float4*>(&sQ[t][d4]) =
+          t < n ? *reinterpret_cast<const float4*>(q + (long long)(sq.row0 + b + t) * ldqkv + qoff + d4)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    log_gate_sums(sR, b, n, red);
+    const int t = tid >> 3, cg = tid & 7;   // query row t, columns 8 u + cg ... (scores), cg * CPT .. (outputs)
+    const float Rt = sR[min(b + t, span - 1) + 1];
+    float acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < span; s0 += KB) {
+      const int nk = min(KB, span - s0);
+      __syncthreads();   // the previous key block's reads are done
+      for (int e = tid; e < KB * DK / 4; e += 256) {
+        const int r = e / (DK / 4), d4 = (e % (DK / 4)) * 4;
+        *reinterpret_cast<float4*>(&sK[r][d4]) =
+            r < nk ? *reinterpret_cast<const float4*>(k + (long long)(sq.row0 + s0 + r) * ldqkv + qoff + d4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      for (int e = tid; e < KB * DV / 4; e += 256) {
+        const int r = e / (DV / 4), d4 = (e % (DV / 4)) * 4;
+        *reinterpret_cast<float4*>(&sV[r][d4]) =
+            r < nk ? *reinterpret_cast<const float4*>(v + (long long)(sq.row0 + s0 + r) * ldqkv + voff + d4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+      // decayed scores of row t against keys 8 u + cg
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int d = 0; d < DK; d += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&sQ[t][d]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 y = *reinterpret_cast<const float4*>(&sK[8 * u + cg][d]);
+          sc[u] = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, sc[u]))));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = 8 * u + cg, sa = s0 + sl;
+        sA[t][sl] = (sl < nk && sa <= b + t && t < n) ? sc[u] * __expf(Rt - sR[sa + 1]) : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int sl = 0; sl < KB; ++sl) {
+        const float a = sA[t][sl];
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4) {
+          const float4 y = *reinterpret_cast<const float4*>(&sV[sl][cg * CPT + c]);
+          acc[c] = fmaf(a, y.x, acc[c]);
+          acc[c + 1] = fmaf(a, y.y, acc[c + 1]);
+          acc[c + 2] = fmaf(a, y.z, acc[c + 2]);
+          acc[c + 3] = fmaf(a, y.w, acc[c + 3]);
+        }
+      }
+    }
+    if (sq.s_in >= 0) {   // exp(G_t) q_t S0, S0 staged 32 rows at a time in sK's place
+      float qs[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) qs[c] = 0.f;
+      const float* S0 = states + (long long)sq.s_in * H * DK * DV + sbase;
+      for (int k0 = 0; k0 < DK; k0 += KB) {
+        __syncthreads();
+        for (int e = tid; e < KB * DV / 4; e += 256) {
+          const int r = e / (DV / 4), d4 = (e % (DV / 4)) * 4;
+          *reinterpret_cast<float4*>(&sV[r][d4]) = *reinterpret_cast<const float4*>(S0 + (long long)(k0 + r) * DV + d4);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r = 0; r < KB; ++r) {
+          const float a = sQ[t][k0 + r];
+#pragma unroll
+          for (int c = 0; c < CPT; c += 4) {
+            const float4 y = *reinterpret_cast<const float4*>(&sV[r][cg * CPT + c]);
+            qs[c] = fmaf(a, y.x, qs[c]);
+            qs[c + 1] = fmaf(a, y.y, qs[c + 1]);
+            qs[c + 2] = fmaf(a, y.z, qs[c + 2]);
+            qs[c + 3] = fmaf(a, y.w, qs[c + 3]);
+          }
+        }
+      }
+      const float e0 = __expf(Rt - sR[0]);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(e0, qs[c], acc[c]);
+    }
+    if (t < n) {
+      float* orow = o + (long long)(sq.row0 + b + t) * ldo + voff + cg * CPT;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) orow[c] = acc[c];
+    }
+  } else if (j == nqb && sq.s_out >= 0) {
+    // final state: thread (row group rg, column group cg) owns rows rg + RG m
+    constexpr int NCG = DV / 8, RG = 256 / NCG, RPT = DK / RG;
+    const int rg = tid / NCG, cg = tid % NCG;
+    const int b = L - 1;   // sums backward from the last token (b = -1: no tokens)
+    for (int x = tid; x < L; x += 256) sR[x + 1] = lg[(long long)(sq.row0 + x) * ldg + h];
+    __syncthreads();
+    if (L > 0) log_gate_sums(sR, b, 1, red);
+    else if (tid == 0) sR[0] = 0.f;
+    __syncthreads();
+    float acc[RPT][8];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[m][c] = 0.f;
+    for (int s0 = 0; s0 < L; s0 += KB) {
+      const int nk = min(KB, L - s0);
+      __syncthreads();
+      for (int e = tid; e < KB * DK / 4; e += 256) {
+        const int r = e / (DK / 4), d4 = (e % (DK / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < nk) {
+          // decay from token s0 + r to the end: exp(G_last - G_s) = exp(-R(s))
+          const float w = __expf(-sR[s0 + r + 1]);
+          x = *reinterpret_cast<const float4*>(k + (long long)(sq.row0 + s0 + r) * ldqkv + qoff + d4);
+          x.x *= w; x.y *= w; x.z *= w; x.w *= w;
+        }
+        *reinterpret_cast<float4*>(&sK[r][d4]) = x;
+      }
+      for (int e = tid; e < KB * DV / 4; e += 256) {
+        const int r = e / (DV / 4), d4 = (e % (DV / 4)) * 4;
+        *reinterpret_cast<float4*>(&sV[r][d4]) =
+            r < nk ? *reinterpret_cast<const float4*>(v + (long long)(sq.row0 + s0 + r) * ldqkv + voff + d4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int r = 0; r < KB; ++r) {
+        const float4 y0 = *reinterpret_cast<const float4*>(&sV[r][cg * 8]);
+        const float4 y1 = *reinterpret_cast<const float4*>(&sV[r][cg * 8 + 4]);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+          const float a = sK[r][rg + RG * m];
+          acc[m][0] = fmaf(a, y0.x, acc[m][0]);
+          acc[m][1] = fmaf(a, y0.y, acc[m][1]);
+          acc[m][2] = fmaf(a, y0.z, acc[m][2]);
+          acc[m][3] = fmaf(a, y0.w, acc[m][3]);
+          acc[m][4] = fmaf(a, y1.x, acc[m][4]);
+          acc[m][5] = fmaf(a, y1.y, acc[m][5]);
+          acc[m][6] = fmaf(a, y1.z, acc[m][6]);
+          acc[m][7] = fmaf(a, y1.w, acc[m][7]);
+        }
+      }
+    }
+    const float e0 = __expf(-sR[0]);   // exp(G_last): the decay of the initial state
+    const float* S0 = sq.s_in >= 0 ? states + (long long)sq.s_in * H * DK * DV + sbase : nullptr;
+    float* S1 = states + (long long)sq.s_out * H * DK * DV + sbase;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const long long rowo = (long long)(rg + RG * m) * DV + cg * 8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) S1[rowo + c] = S0 ? fmaf(e0, S0[rowo + c], acc[m][c]) : acc[m][c];
+    }
+  }
+}
+
 // Scan of chunk states across the chunks of each sequence, elementwise over
 // the [dk, dv] state: S_enter[c] = exp(gamma[c-1]) S_enter[c-1] + dS[c-1],
 // starting from the sequence's initial state.  cstates holds dS[c] on entry
@@ -544,7 +771,7 @@ hipError_t launch_scan_chunked(const void* q, const void* k, const void* v, int 
 
 hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, int ld_qkv,
                        const float* log_g, int ld_g, void* o, int ld_o, const ScanSeq* seqs,
-                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s) {
+                       int n_seqs, float* states, int H, int dk, int dv, hipStream_t s, int max_len) {
   if (n_seqs <= 0 || H <= 0) return hipSuccess;
   if (bf16) {
     if (dk != DK || dv != DV) return hipErrorInvalidValue;
@@ -560,6 +787,20 @@ hipError_t launch_scan(bool bf16, const void* q, const void* k, const void* v, i
     const auto* kk = reinterpret_cast<const float*>(k);
     const auto* vv = reinterpret_cast<const float*>(v);
     auto* oo = reinterpret_cast<float*>(o);
+    if (max_len <= QMAX && ld_qkv % 4 == 0) {
+      const int nqb = (max_len + 31) / 32;
+      const dim3 grid(n_seqs * (nqb + 1), H);
+#define S1_WHOLE(DKV, DVV)                                                                                   \
+  hipLaunchKernelGGL((scan_f32_whole_kernel<DKV, DVV>), grid, dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g, ld_g, \
+                     oo, ld_o, seqs, states, H, nqb)
+      if (dk == 64 && dv == 64) S1_WHOLE(64, 64);
+      else if (dk == 128 && dv == 128) S1_WHOLE(128, 128);
+      else if (dk == 128 && dv == 64) S1_WHOLE(128, 64);
+      else if (dk == 64 && dv == 128) S1_WHOLE(64, 128);
+      else return hipErrorInvalidValue;
+#undef S1_WHOLE
+      return hipGetLastError();
+    }
     if (dk == 64 && dv == 64)
       hipLaunchKernelGGL((scan_f32_kernel<64, 64>), dim3(n_seqs, H), dim3(256), 0, s, qq, kk, vv, ld_qkv, log_g,
                          ld_g, oo, ld_o, seqs, states, H);

@@ -62,19 +62,32 @@ def test_gemm_bf16_every_tile_config(M, N, K, split):
         assert np.abs(C - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6, cfg
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 1408, 256), (100, 256, 688), (5, 772, 256)])
-def test_gemm_f32(M, N, K):
+@pytest.mark.parametrize("M,N,K,split", [
+    (128, 1408, 256, 1), (100, 256, 688, 3), (5, 772, 256, 1), (77, 132, 100, 2), (33, 65, 36, 1),
+    (600, 1000, 256, 1), (2100, 2100, 64, 1),
+])
+def test_gemm_f32(M, N, K, split):
+    """fp32 GEMMs: the shape's own choice (the few-tile kernel with the K
+    range split over waves, and over workgroups up to `split`; the 128 x 128
+    kernel for many tiles) and configuration 0, on ragged
+    M, N and K, against float64 products."""
     torch = require_gpu()
-    log(f"gemm f32 M={M} N={N} K={K}")
     rng = np.random.default_rng([M, N, K, 32])
     A = rng.standard_normal((M, K)).astype(np.float32)
     W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
-    dC = torch.empty((M, N), dtype=torch.float32, device="cuda")
     dA, dW = dev(A), dev(W)
-    B.gemm(B.S1_F32, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, 1, stream_ptr())
-    torch.cuda.synchronize()
     ref = A.astype(np.float64) @ W.astype(np.float64).T
-    assert rel_l2(dC.cpu().numpy(), ref) < 1e-5
+    for cfg in (None, 0):
+        log(f"gemm f32 M={M} N={N} K={K} split={split} cfg={cfg}")
+        dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        if cfg is None:
+            B.gemm(B.S1_F32, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, split, stream_ptr())
+        else:
+            B.gemm_cfg(B.S1_F32, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K, split, cfg, stream_ptr())
+        torch.cuda.synchronize()
+        C = dC.cpu().numpy()
+        assert np.isfinite(C).all(), cfg
+        assert rel_l2(C, ref) < 1e-5, cfg
 
 
 def test_gemm_split_is_deterministic():
@@ -298,29 +311,44 @@ def test_scan_bf16_chunk_parallel(H, lens, init):
     _scan_case(H, lens, seed=H + len(lens), with_init=init, chunked=True)
 
 
-def test_scan_f32():
+@pytest.mark.parametrize("H,dk,dv,lens", [
+    (4, 64, 64, [1, 50, 77]), (2, 128, 128, [0, 33, 300]), (3, 128, 64, [512, 31]), (2, 64, 128, [600, 5]),
+])
+def test_scan_f32(H, dk, dv, lens):
+    """fp32 scan against the float64 recurrence, with initial and final
+    states: batches whose longest sequence has at most 512 tokens run the
+    whole-sequence kernel (one chunk per sequence, all rows in parallel),
+    longer ones the sequential chunked kernel; an empty sequence passes its
+    initial state through."""
     torch = require_gpu()
-    rng = np.random.default_rng(21)
-    H, dk, lens = 4, 64, [1, 50, 77]
+    log(f"scan f32 H={H} dk={dk} dv={dv} lens={lens}")
+    rng = np.random.default_rng([21, H, dk, dv, len(lens)])
     T = sum(lens)
-    qkv = rng.standard_normal((T, 3 * H * dk)).astype(np.float32)
+    n = len(lens)
+    ld = H * (2 * dk + dv)
+    qkv = rng.standard_normal((T, ld)).astype(np.float32)
     lg = np.log(1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    s0 = rng.standard_normal((3, H, dk, dk)).astype(np.float32)
+    s0 = rng.standard_normal((n, H, dk, dv)).astype(np.float32)
     d_qkv, d_lg, d_s0 = dev(qkv), dev(lg), dev(s0)
-    d_o = torch.zeros((T, H * dk), dtype=torch.float32, device="cuda")
+    d_o = torch.zeros((T, H * dv), dtype=torch.float32, device="cuda")
     d_sf = torch.zeros_like(d_s0)
     base = d_qkv.data_ptr()
-    B.la_scan(B.S1_F32, base, base + 4 * H * dk, base + 8 * H * dk, 3 * H * dk, d_lg.data_ptr(), d_o.data_ptr(),
-              T, H, dk, dk, cu, d_s0.data_ptr(), d_sf.data_ptr(), stream_ptr())
+    B.la_scan(B.S1_F32, base, base + 4 * H * dk, base + 8 * H * dk, ld, d_lg.data_ptr(), d_o.data_ptr(),
+              T, H, dk, dv, cu, d_s0.data_ptr(), d_sf.data_ptr(), stream_ptr())
     torch.cuda.synchronize()
-    q = qkv.reshape(T, 3, H, dk).astype(np.float64)
-    for i in range(3):
+    x = qkv.astype(np.float64)
+    qa = x[:, :H * dk].reshape(T, H, dk)
+    ka = x[:, H * dk:2 * H * dk].reshape(T, H, dk)
+    va = x[:, 2 * H * dk:].reshape(T, H, dv)
+    out, sf = d_o.cpu().numpy().reshape(T, H, dv), d_sf.cpu().numpy()
+    for i in range(n):
         a, b = cu[i], cu[i + 1]
-        ro, rs = O.la_scan_recurrent(q[a:b, 0], q[a:b, 1], q[a:b, 2], np.exp(lg[a:b].astype(np.float64)),
+        ro, rs = O.la_scan_recurrent(qa[a:b], ka[a:b], va[a:b], np.exp(lg[a:b].astype(np.float64)),
                                      s0[i].astype(np.float64))
-        assert rel_l2(d_o.cpu().numpy()[a:b].reshape(-1, H, dk), ro) < 1e-5
-        assert rel_l2(d_sf.cpu().numpy()[i], rs) < 1e-5
+        if b > a:
+            assert rel_l2(out[a:b], ro) < 1e-5, i
+        assert rel_l2(sf[i], rs) < 1e-5, i
 
 
 def _attn_case(dtype, Hq, Hkv, hd, seqs, seed, block_rows=0, piece=0, shared=False):
@@ -410,8 +438,11 @@ def test_attention_bf16_gqa5():
     assert _attn_case(B.S1_BF16, 40, 8, 128, [(200, 0), (33, 17)], seed=40) < 1e-2
 
 
-def test_attention_f32():
-    assert _attn_case(B.S1_F32, 4, 4, 64, [(1, 0), (70, 0), (20, 30)], seed=3) < 1e-5
+@pytest.mark.parametrize("Hq,Hkv,hd,seqs", [
+    (4, 4, 64, [(1, 0), (70, 0), (20, 30)]), (8, 2, 128, [(130, 0), (17, 100), (64, 0)]),
+])
+def test_attention_f32(Hq, Hkv, hd, seqs):
+    assert _attn_case(B.S1_F32, Hq, Hkv, hd, seqs, seed=3 + hd) < 1e-5
 
 
 @pytest.mark.parametrize("dtype,d", [(B.S1_BF16, 2560), (B.S1_F32, 2560), (B.S1_BF16, 2568), (B.S1_BF16, 260)])
