@@ -38,6 +38,26 @@ constexpr int TP = C * 2 + 16;    // bytes per K^T / V^T row in LDS
 __device__ __forceinline__ int trow(int d) { return d * TP + (d >> 4) * 16; }
 constexpr int trows_bytes(int rows) { return rows * TP + (rows / 16) * 16; }
 
+// Raw buffer over `bytes` bytes from `base`: loads at or past the end read
+// zero and stores there are dropped (the range check covers the per-lane
+// offset, which is where every offset that needs checking goes).  Buffer
+// addressing keeps the per-lane offsets in 32-bit registers computed once
+// and the per-access constants in scalar offsets.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(rsrc_t r, int voff) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ float ldf(rsrc_t r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void stf(float x, rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+
 // MODE_FULL: the recurrence over whole sequences.  MODE_SUMMARY: one chunk
 // per entry from a zero state; writes only the chunk's state contribution and
 // its total log-decay.  MODE_OUTPUT: one chunk per entry from the state
@@ -63,7 +83,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __attribute__((aligned(16))) char sKt[trows_bytes(DK)];     // decayed K^T, hi part
   __shared__ __attribute__((aligned(16))) char sKl[trows_bytes(DK)];     // decayed K^T, lo part
   __shared__ __attribute__((aligned(16))) char sVt[trows_bytes(DVG)];
-  __shared__ float sG[C];
+  __shared__ float sG[C], sEG[C];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, cl = lane & 31;
@@ -72,10 +92,88 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int dvw = dvg * DVG;          // first value column of the workgroup
   const int dv0 = dvw + wave * 32;    // first value column of this wave
 
-  floatx16 S[DK / 32];                // S[a][r] = S[32a + acc_row(r)][dv0 + cl]
-  auto st_at = [&](float* base, long long slot, int a, int r) {
-    return base + ((slot * H + h) * DK + 32 * a + acc_row(r, lane)) * DV + dv0 + cl;
+  // Each chunk's global loads, through buffers that end at the chunk's last
+  // row: rows past it read zero.  Four-wave workgroups issue them right
+  // after the previous chunk's LDS stores, so that they are in flight while
+  // that chunk is multiplied; with fewer waves each thread holds too many of
+  // them to keep them across the products.  The first chunk's loads are
+  // issued before the entering state is read (the output modes' only chunk:
+  // its loads overlap the state loads).
+  constexpr bool PREFETCH = NW == 4 || MODE == MODE_OUTPUT || MODE == MODE_FOLD;
+  constexpr int QI = C * 16 / NT, KI = C * 8 / NT, VI = (C / 2) * (DVG / 8) / NT;
+  uint4 qv[MODE != MODE_SUMMARY ? QI : 1], kav[KI], kbv[KI], vav[VI], vbv[VI];
+  const int ldb = ldqkv * 2;          // bytes per q/k/v row
+  int qo[MODE != MODE_SUMMARY ? QI : 1], ko[KI], vo[VI];   // chunk-relative byte offsets (rows 2p for k, v)
+#pragma unroll
+  for (int i = 0; i < QI; ++i) {
+    const int c = tid + NT * i;
+    if constexpr (MODE != MODE_SUMMARY) qo[i] = (c >> 4) * ldb + (h * DK + (c & 15) * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int c = tid + NT * i;
+    ko[i] = 2 * (c >> 4) * ldb + (h * DK + (c & 15) * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int c = tid + NT * i;
+    vo[i] = 2 * (c / (DVG / 8)) * ldb + (h * DV + dvw + (c % (DVG / 8)) * 8) * 2;
+  }
+  float lgv = 0.f;
+  auto load_chunk = [&](int cc) {
+    const int nn = min(C, sq.len - cc);   // >= 1
+    const long long bb = (long long)sq.row0 + cc;
+    lgv = ldf(make_rsrc(lg + bb * ldg, nn * ldg * 4), (lane * ldg + h) * 4, 0);
+    if constexpr (MODE != MODE_SUMMARY) {
+      const rsrc_t rq = make_rsrc(q + bb * ldqkv, nn * ldb);
+#pragma unroll
+      for (int i = 0; i < QI; ++i) qv[i] = ld16(rq, qo[i]);
+    }
+    const rsrc_t rk = make_rsrc(k + bb * ldqkv, nn * ldb);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      kav[i] = ld16(rk, ko[i]);
+      kbv[i] = ld16(rk, ko[i] + ldb);
+    }
+    const rsrc_t rv = make_rsrc(v + bb * ldqkv, nn * ldb);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      vav[i] = ld16(rv, vo[i]);
+      vbv[i] = ld16(rv, vo[i] + ldb);
+    }
   };
+  if (PREFETCH && sq.len > 0) load_chunk(0);
+
+  floatx16 S[DK / 32];                // S[a][r] = S[32a + acc_row(r)][dv0 + cl]
+  // state slabs [DK][DV] fp32 per (slot, head): lane part of the offset, and
+  // the constant part of element (a, r)
+  const int st_lane = (4 * hi * DV + dv0 + cl) * 4;
+  auto st_soff = [](int a, int r) { return (32 * a + 8 * (r >> 2) + (r & 3)) * DV * 4; };
+  // chunk slots (the chunk-parallel modes' `states`) hold the state in the
+  // accumulator order instead: [32-column block][a][r / 4][lane][r % 4], so
+  // that a lane's four consecutive accumulators are one 16-byte access
+  const int fr_lane = ((dv0 / 32) * (DK / 32) * 4 * 256 + lane * 4) * 4;
+  auto fr_soff = [](int a, int rq) { return (a * 4 + rq) * 1024; };
+  auto ld_frag = [&](rsrc_t rs, floatx16 (&X)[DK / 32]) {
+    uint4 u[DK / 32][4];
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, fr_lane, fr_soff(a, rq), 0);
+        u[a][rq] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        X[a][4 * rq] = __uint_as_float(u[a][rq].x);
+        X[a][4 * rq + 1] = __uint_as_float(u[a][rq].y);
+        X[a][4 * rq + 2] = __uint_as_float(u[a][rq].z);
+        X[a][4 * rq + 3] = __uint_as_float(u[a][rq].w);
+      }
+  };
+  auto slab = [&](const float* base, long long slot) { return make_rsrc(base + (slot * H + h) * DK * DV, DK * DV * 4); };
   ChunkSeq cs{0, 0, -1, -1};
   if constexpr (MODE == MODE_FOLD) {
     // this chunk's sequence: the last entry whose first chunk is at or before it
@@ -86,60 +184,47 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       else hi2 = mid - 1;
     }
     cs = cseqs[lo];
-#pragma unroll
-    for (int a = 0; a < DK / 32; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[a][r] = cs.s_in >= 0 ? *st_at(seq_states, cs.s_in, a, r) : 0.f;
-    for (int c = cs.c0; c < seq; ++c) {
-      const float g = __expf(gamma[(long long)c * H + h]);
+    if (cs.s_in >= 0) {
+      const rsrc_t rs = slab(seq_states, cs.s_in);
 #pragma unroll
       for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[a][r] = fmaf(g, S[a][r], *st_at(states, c, a, r));
+        for (int r = 0; r < 16; ++r) S[a][r] = ldf(rs, st_lane, st_soff(a, r));
+    } else {
+#pragma unroll
+      for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[a][r] = 0.f;
     }
+    // the next predecessor's contribution is loaded while the current one is added
+    floatx16 dA[DK / 32], dB[DK / 32];
+    if (cs.c0 < seq) ld_frag(slab(states, cs.c0), dA);
+    for (int c = cs.c0; c < seq; ++c) {
+      const float g = __expf(gamma[(long long)c * H + h]);
+      if (c + 1 < seq) ld_frag(slab(states, c + 1), dB);
+#pragma unroll
+      for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[a][r] = fmaf(g, S[a][r], dA[a][r]);
+          dA[a][r] = dB[a][r];
+        }
+    }
+  } else if (MODE == MODE_OUTPUT) {
+    ld_frag(slab(states, sq.s_in), S);   // the state entering the chunk
+  } else if (MODE == MODE_FULL && sq.s_in >= 0) {
+    const rsrc_t rs = slab(states, sq.s_in);
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[a][r] = ldf(rs, st_lane, st_soff(a, r));
   } else {
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        S[a][r] = (MODE != MODE_SUMMARY && sq.s_in >= 0) ? *st_at(states, sq.s_in, a, r) : 0.f;
+      for (int r = 0; r < 16; ++r) S[a][r] = 0.f;
   }
 
-  // Each chunk's global loads (rows past its end read its last row, in
-  // bounds, and are replaced by zeros at the LDS stores).  Four-wave
-  // workgroups issue them right after the previous chunk's LDS stores, so
-  // that they are in flight while that chunk is multiplied; with fewer waves
-  // each thread holds too many of them to keep them across the products.
-  constexpr bool PREFETCH = NW == 4;
-  constexpr int QI = C * 16 / NT, KI = C * 8 / NT, VI = (C / 2) * (DVG / 8) / NT;
-  uint4 qv[MODE != MODE_SUMMARY ? QI : 1], kav[KI], kbv[KI], vav[VI], vbv[VI];
-  float lgv = 0.f;
-  auto load_chunk = [&](int cc) {
-    const int nn = min(C, sq.len - cc);   // >= 1
-    const long long bb = (long long)sq.row0 + cc;
-    lgv = lane < nn ? lg[(bb + lane) * ldg + h] : 0.f;
-    if constexpr (MODE != MODE_SUMMARY) {
-#pragma unroll
-      for (int i = 0; i < QI; ++i) {
-        const int c = tid + NT * i, s = c >> 4, ch = c & 15;
-        qv[i] = *reinterpret_cast<const uint4*>(q + (bb + min(s, nn - 1)) * ldqkv + h * DK + ch * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int c = tid + NT * i, p = c >> 4, ch = c & 15;
-      kav[i] = *reinterpret_cast<const uint4*>(k + (bb + min(2 * p, nn - 1)) * ldqkv + h * DK + ch * 8);
-      kbv[i] = *reinterpret_cast<const uint4*>(k + (bb + min(2 * p + 1, nn - 1)) * ldqkv + h * DK + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8);
-      const long long col = (long long)h * DV + dvw + ch * 8;
-      vav[i] = *reinterpret_cast<const uint4*>(v + (bb + min(2 * p, nn - 1)) * ldqkv + col);
-      vbv[i] = *reinterpret_cast<const uint4*>(v + (bb + min(2 * p + 1, nn - 1)) * ldqkv + col);
-    }
-  };
-  if (PREFETCH && sq.len > 0) load_chunk(0);
 
   for (int c0 = 0; c0 < sq.len; c0 += C) {
     if constexpr (!PREFETCH) load_chunk(c0);
@@ -156,22 +241,24 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const float wK = __expf(Glast - G);   // decay from token `lane` to the chunk end
 
     __syncthreads();                      // previous chunk's reads of LDS are done
-    if (wave == 0) sG[lane] = G;
+    if (wave == 0) {
+      sG[lane] = G;
+      sEG[lane] = __expf(G);
+    }
     if (MODE == MODE_SUMMARY && tid == 0 && dvg == 0) gamma[(long long)seq * H + h] = Glast;
     // Q rows: straight copy
     if constexpr (MODE != MODE_SUMMARY) {
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int c = tid + NT * i, s = c >> 4, ch = c & 15;
-        *reinterpret_cast<uint4*>(sQ + s * QP + ch * 16) = s < n ? qv[i] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(sQ + s * QP + ch * 16) = qv[i];
       }
     }
     // K rows (row-major copy) and K^T scaled by the decay to the chunk end
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int c = tid + NT * i, p = c >> 4, ch = c & 15, s0 = 2 * p, s1 = s0 + 1;
-      const uint4 ka = s0 < n ? kav[i] : make_uint4(0, 0, 0, 0);
-      const uint4 kb = s1 < n ? kbv[i] : make_uint4(0, 0, 0, 0);
+      const uint4 ka = kav[i], kb = kbv[i];
       *reinterpret_cast<uint4*>(sK + s0 * QP + ch * 16) = ka;
       *reinterpret_cast<uint4*>(sK + s1 * QP + ch * 16) = kb;
       if constexpr (MODE != MODE_OUTPUT && MODE != MODE_FOLD) {
@@ -196,8 +283,7 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int c = tid + NT * i, p = c / (DVG / 8), ch = c % (DVG / 8), s0 = 2 * p, s1 = s0 + 1;
-      const uint4 va = s0 < n ? vav[i] : make_uint4(0, 0, 0, 0);
-      const uint4 vb = s1 < n ? vbv[i] : make_uint4(0, 0, 0, 0);
+      const uint4 va = vav[i], vb = vbv[i];
       const uint32_t a[4] = {va.x, va.y, va.z, va.w}, b[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -286,16 +372,20 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         mfma32(O1[tt], alo, vf);
       }
     }
+    {
+      // rows at or past n are dropped by the buffer's range check
+      const rsrc_t ro = make_rsrc(o + base * ldo, n * ldo * 2);
+      const int olane = (4 * hi * ldo + h * DV + dv0 + cl) * 2;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * tt + acc_row(r, lane);
-        if (t < n) {
-          const float val = O1[tt][r] + __expf(sG[t]) * O2[tt][r];
-          o[(base + t) * ldo + (long long)h * DV + dv0 + cl] = f2bf(val);
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * tt + acc_row(r, lane);
+          const float val = O1[tt][r] + sEG[t] * O2[tt][r];
+          __builtin_amdgcn_raw_buffer_store_b16(f2bf(val), ro, olane + (32 * tt + 8 * (r >> 2) + (r & 3)) * ldo * 2,
+                                                0, 0);
         }
-      }
+    }
 
     }  // MODE != MODE_SUMMARY
     if constexpr (MODE != MODE_OUTPUT && MODE != MODE_FOLD) {
@@ -321,16 +411,32 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   if constexpr (MODE == MODE_FOLD) {
     if (seq == cs.c0 + cs.nc - 1 && cs.s_out >= 0) {   // the sequence's final state
       const float g = __expf(gamma[(long long)seq * H + h]);
+      floatx16 dS[DK / 32];
+      ld_frag(slab(states, seq), dS);
+      const rsrc_t rs = slab(seq_states, cs.s_out);
 #pragma unroll
       for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) *st_at(seq_states, cs.s_out, a, r) = fmaf(g, S[a][r], *st_at(states, seq, a, r));
+        for (int r = 0; r < 16; ++r) stf(fmaf(g, S[a][r], dS[a][r]), rs, st_lane, st_soff(a, r));
     }
-  } else if (MODE != MODE_OUTPUT && sq.s_out >= 0) {
+  } else if (MODE == MODE_SUMMARY) {   // the chunk's contribution, in accumulator order
+    const rsrc_t rs = slab(states, sq.s_out);
 #pragma unroll
     for (int a = 0; a < DK / 32; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) *st_at(states, sq.s_out, a, r) = S[a][r];
+      for (int rq = 0; rq < 4; ++rq) {
+        const uint4 u = make_uint4(__float_as_uint(S[a][4 * rq]), __float_as_uint(S[a][4 * rq + 1]),
+                                   __float_as_uint(S[a][4 * rq + 2]), __float_as_uint(S[a][4 * rq + 3]));
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0)), u), rs, fr_lane,
+            fr_soff(a, rq), 0);
+      }
+  } else if (MODE == MODE_FULL && sq.s_out >= 0) {
+    const rsrc_t rs = slab(states, sq.s_out);
+#pragma unroll
+    for (int a = 0; a < DK / 32; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stf(S[a][r], rs, st_lane, st_soff(a, r));
   }
 }
 
@@ -698,22 +804,40 @@ scan_f32_whole_kernel(const float* __restrict__ q, const float* __restrict__ k,
 // Scan of chunk states across the chunks of each sequence, elementwise over
 // the [dk, dv] state: S_enter[c] = exp(gamma[c-1]) S_enter[c-1] + dS[c-1],
 // starting from the sequence's initial state.  cstates holds dS[c] on entry
-// and S_enter[c] on exit; the final state goes to the sequence's slot.
+// and S_enter[c] on exit, in the accumulator order of the chunk kernels; the
+// initial and final states are in the sequence slots' row-major order.
 __global__ void __launch_bounds__(256)
 chunk_state_scan_kernel(const ChunkSeq* __restrict__ cseqs, const float* __restrict__ gamma,
                         float* __restrict__ cstates, float* __restrict__ states, int H) {
   const int sidx = blockIdx.y / H, h = blockIdx.y % H;
   const ChunkSeq cs = cseqs[sidx];
   constexpr int E = DK * DV;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  float sv = cs.s_in >= 0 ? states[((long long)cs.s_in * H + h) * E + e] : 0.f;
-  for (int c = cs.c0; c < cs.c0 + cs.nc; ++c) {
-    float* slot = cstates + ((long long)c * H + h) * E + e;
-    const float d = *slot;
-    *slot = sv;
-    sv = fmaf(__expf(gamma[(long long)c * H + h]), sv, d);
+  const int e = blockIdx.x * 256 + threadIdx.x;   // index in the chunk slots' accumulator order
+  // the same element in the sequence states' row-major order
+  const int r3 = e & 3, lane = (e >> 2) & 63, rq = (e >> 8) & 3, a = (e >> 10) & 3, cb = e >> 12;
+  const int rm = (32 * a + 8 * rq + 4 * (lane >> 5) + r3) * DV + 32 * cb + (lane & 31);
+  float sv = cs.s_in >= 0 ? states[((long long)cs.s_in * H + h) * E + rm] : 0.f;
+  // eight chunks at a time: their loads are issued together, then the
+  // recurrence steps through them in order
+  constexpr int G8 = 8;
+  const int cend = cs.c0 + cs.nc;
+  for (int c0 = cs.c0; c0 < cend; c0 += G8) {
+    float d[G8], gm[G8];
+#pragma unroll
+    for (int i = 0; i < G8; ++i) {
+      const int c = min(c0 + i, cend - 1);
+      d[i] = cstates[((long long)c * H + h) * E + e];
+      gm[i] = gamma[(long long)c * H + h];
+    }
+#pragma unroll
+    for (int i = 0; i < G8; ++i) {
+      if (c0 + i < cend) {
+        cstates[((long long)(c0 + i) * H + h) * E + e] = sv;
+        sv = fmaf(__expf(gm[i]), sv, d[i]);
+      }
+    }
   }
-  if (cs.s_out >= 0) states[((long long)cs.s_out * H + h) * E + e] = sv;
+  if (cs.s_out >= 0) states[((long long)cs.s_out * H + h) * E + rm] = sv;
 }
 
 template <int MODE>
