@@ -3,7 +3,7 @@
  *
  * A decision model answers closed questions from one prefill pass, with no
  * decoding (System1-Omni README, introduction; Cua-S1 4B 0.2 issue #10, first
- * plan comment: one forward pass and a softmax over the answer-option logits).
+ * plan comment: a single pass, then a softmax over the option logits).
  * The model is a hybrid decoder -- gated linear-attention layers and full
  * causal-attention layers, 3:1 -- with a LoRA adapter merged into the weights
  * at load (RFC #114 "Native Rust/CUDA support for OmniJev-4B v1.1", sections

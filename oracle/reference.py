@@ -331,8 +331,8 @@ def decision_fields(p, qtype):
 def readout(h_row, w_final, e_rows, eps, qtype):
     """Decision readout of one question: final RMSNorm of the marker row,
     option logits z_k = h . E[opt_k] against the tied embedding rows, softmax
-    over the K option logits only ([cua-issue] first plan comment: one forward
-    pass and a softmax over the answer-letter logits; [rfc114-plan]: the head
+    over the K option logits only ([cua-issue] first plan comment: the answer
+    is read from the option logits of a single pass; [rfc114-plan]: the head
     stays bf16 and is cast to fp32 before the softmax -- here the whole
     readout runs in the oracle's float type).  Returns (p, fields)."""
     h = rms_norm(h_row[None, :], w_final, eps)[0]
