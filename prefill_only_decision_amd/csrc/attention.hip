@@ -34,11 +34,18 @@ constexpr int HD = 128, BKV = 64;
 constexpr int KPITCH = HD * 2 + 16;   // bytes per K row in LDS
 constexpr int VPITCH = BKV * 2 + 8;   // bytes per V^T row in LDS
 constexpr int OPITCH = HD * 2 + 16;   // bytes per output row in LDS
-constexpr int LDS_BYTES = BKV * KPITCH + HD * VPITCH;
+// V^T row d sits at d * VPITCH plus 16 bytes per 32 rows before it: the
+// transposing stores of one instruction hit rows 8 apart, which the padding
+// spreads over the banks; a read takes 32 consecutive rows of one group.
+constexpr int vt_row(int d) { return d * VPITCH + (d >> 5) * 16; }
+constexpr int LDS_BYTES = BKV * KPITCH + HD * VPITCH + (HD / 32) * 16;
 static_assert(4 * 32 * OPITCH <= LDS_BYTES, "output staging must fit");
 
+// Four-wave workgroups are held to two waves per SIMD (all accumulators in
+// VGPRs, no spills): two workgroups share a CU, so one's barriers and block
+// staging overlap the other's products.
 template <int NWQ>
-__global__ void __launch_bounds__(NWQ * 64)
+__global__ void __launch_bounds__(NWQ * 64) __attribute__((amdgpu_waves_per_eu(NWQ == 4 ? 2 : 1, 2)))
 attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict__ k,
                  const bf16_t* __restrict__ v, int ldkv, bf16_t* __restrict__ o, int ldo,
                  const AttnSeq* __restrict__ seqs, const AttnBlock* __restrict__ blocks, int Hq,
@@ -114,8 +121,8 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d0 = ch * 8 + 2 * e;
-        *reinterpret_cast<uint32_t*>(sVt + d0 * VPITCH + 4 * kp) = (a[e] & 0xFFFFu) | (b[e] << 16);
-        *reinterpret_cast<uint32_t*>(sVt + (d0 + 1) * VPITCH + 4 * kp) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(sVt + vt_row(d0) + 4 * kp) = (a[e] & 0xFFFFu) | (b[e] << 16);
+        *reinterpret_cast<uint32_t*>(sVt + vt_row(d0 + 1) + 4 * kp) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
       }
     }
   };
@@ -180,7 +187,7 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
         const int kb = (32 * t + 16 * hf + 4 * hi) * 2;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
-          const char* vr = sVt + (32 * dt + (lane & 31)) * VPITCH + kb;
+          const char* vr = sVt + vt_row(32 * dt + (lane & 31)) + kb;
           const bf16x8 vf = frag_from_halves(*reinterpret_cast<const uint2*>(vr),
                                              *reinterpret_cast<const uint2*>(vr + 16));
           mfma32(oacc[dt], vf, pf);
