@@ -170,15 +170,35 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
             } else if constexpr (EPI == EPI_PARTIAL) {
               gptr<float>(g.out0)[split_idx * g.split_stride + (long long)row * g.ld0 + col] = v;
             } else if constexpr (EPI == EPI_GATE) {
+              // gate columns raw here, finished by the wave's loop below
               if (col < g.nsplit)
                 gptr<T>(g.out0)[(long long)row * g.ld0 + col] = from_f<T>(v);
               else if (g.out2 == nullptr || col < g.nsplit2)
-                gptr<float>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = log_sigmoid(v);
+                gptr<float>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = v;
               else
-                gptr<float>(g.out2)[(long long)row * g.ld1 + (col - g.nsplit2)] = 1.f / (1.f + __expf(-v));
+                gptr<float>(g.out2)[(long long)row * g.ld1 + (col - g.nsplit2)] = v;
             }
           }
         }
+      }
+    }
+  }
+  if constexpr (EPI == EPI_GATE) {
+    // the nonlinearity of the wave's gate columns, once per element in a
+    // small loop (unrolled over every accumulator it costs the main loop of
+    // the largest tiles registers); the wave's own raw stores are complete
+    // after vmcnt(0)
+    const int g0 = max(cn0, g.nsplit), ngc = min(cn0 + 32 * TN, g.N) - g0;
+    if (ngc > 0) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      for (int e = lane; e < 32 * TM * ngc; e += 64) {
+        const int row = rm0 + e / ngc, col = g0 + e % ngc;
+        if (row >= g.M) continue;
+        const bool beta = g.out2 != nullptr && col >= g.nsplit2;
+        gmem<float>* p = beta ? gptr<float>(g.out2) + (long long)row * g.ld1 + (col - g.nsplit2)
+                              : gptr<float>(g.out1) + (long long)row * g.ld1 + (col - g.nsplit);
+        const float v = *p;
+        *p = beta ? 1.f / (1.f + __expf(-v)) : log_sigmoid(v);
       }
     }
   }
@@ -242,29 +262,48 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
       }
     }
   } else {   // EPI_GATE
+    // nsplit is a multiple of 32, so each 32-column block is all q|k|v
+    // (staged as bf16) or all gate columns; the gate columns are written raw
+    // here and finished by the small loop below: with the nonlinearity
+    // unrolled over every accumulator the epilogue's code and registers
+    // spilled into the main loop of the largest tiles
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int cll = wc0 + 32 * j + cl, col = n0 + cll;
+      const int cbl = wc0 + 32 * j, cb = n0 + cbl;
+      const int cll = cbl + cl, col = cb + cl;
+      if (cb < g.nsplit) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int rbl = wr0 + 32 * i;
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = rbl + acc_row(r, lane), row = m0 + rl;
-          const float v = acc[i][j][r];
-          if (col < g.nsplit) {
-            put(rl, cll, v);
-          } else if (col < g.N && row < g.M) {
-            if (g.out2 == nullptr || col < g.nsplit2)
-              gptr<float>(g.out1)[(long long)row * g.ld1 + (col - g.nsplit)] = log_sigmoid(v);
-            else
-              gptr<float>(g.out2)[(long long)row * g.ld1 + (col - g.nsplit2)] = 1.f / (1.f + __expf(-v));
+          for (int r = 0; r < 16; ++r) put(wr0 + 32 * i + acc_row(r, lane), cll, acc[i][j][r]);
+      } else if (col < g.N) {
+        gmem<float>* dst = (g.out2 != nullptr && col >= g.nsplit2) ? gptr<float>(g.out2) + (col - g.nsplit2)
+                                                                  : gptr<float>(g.out1) + (col - g.nsplit);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wr0 + 32 * i + acc_row(r, lane);
+            if (row < g.M) dst[(long long)row * g.ld1] = acc[i][j][r];
           }
-        }
       }
     }
   }
-  __syncthreads();
+  __syncthreads();   // staged rows complete; raw gate values visible to the workgroup
+  if constexpr (EPI == EPI_GATE) {
+    if (n0 + BN > g.nsplit) {
+      const int g0 = max(n0, g.nsplit), ngc = min(n0 + BN, g.N) - g0;
+      for (int e = threadIdx.x; e < BM * ngc; e += NT) {
+        const int row = m0 + e / ngc, col = g0 + e % ngc;
+        if (row >= g.M) continue;
+        const bool beta = g.out2 != nullptr && col >= g.nsplit2;
+        gmem<float>* p = beta ? gptr<float>(g.out2) + (long long)row * g.ld1 + (col - g.nsplit2)
+                              : gptr<float>(g.out1) + (long long)row * g.ld1 + (col - g.nsplit);
+        const float v = *p;
+        *p = beta ? 1.f / (1.f + __expf(-v)) : log_sigmoid(v);
+      }
+    }
+  }
   constexpr int CPR = BN / 8;                     // 16-byte chunks per row
   const int lim = EPI == EPI_GATE ? min(g.N, g.nsplit) : g.N;
 #pragma unroll 4
@@ -286,7 +325,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 
 // Whether a launch can use epilogue_staged (16-byte aligned destinations).
 __host__ __device__ inline bool staged_ok(int epi, const GemmArgs& g) {
-  if (epi == EPI_GATE) return g.ld0 % 8 == 0 && g.nsplit % 8 == 0;
+  if (epi == EPI_GATE) return g.ld0 % 8 == 0 && g.nsplit % 32 == 0;
   if (epi == EPI_QKV) return g.ld0 % 8 == 0 && g.ld1 % 8 == 0 && g.ld2 % 8 == 0 && g.nsplit % 8 == 0 &&
                              g.nsplit2 % 8 == 0 && g.N % 8 == 0;
   return false;
@@ -524,7 +563,7 @@ __device__ __forceinline__ T pin_sgpr(T v) {
 template <int EPI>
 __device__ __forceinline__ GemmArgs pin_epilogue_args(const GemmArgs& g) {
   GemmArgs e = g;
-  if constexpr (EPI == EPI_QKV) return e;
+  if constexpr (EPI == EPI_QKV || EPI == EPI_GATE) return e;
   e.M = pin_sgpr(g.M);
   e.N = pin_sgpr(g.N);
   e.out0 = pin_sgpr(g.out0);
@@ -815,15 +854,25 @@ gemm_wide_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   tile(nk - 1, std::true_type{});
-  if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_GATE) {
+    // only the staged form: the host runs unaligned gate launches on the
+    // other kernels (with both forms compiled in, these 256 x 256 tiles
+    // spilled registers inside the main loop)
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
-    if (g.staged) {
-      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                              S::NS * S::STAGE);
-      return;
+    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                            S::NS * S::STAGE);
+    return;
+  } else {
+    if constexpr (EPI == EPI_QKV) {
+      static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
+      if (g.staged) {
+        epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane,
+                                                                smem, S::NS * S::STAGE);
+        return;
+      }
     }
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   }
-  epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
 }
 
 // ----------------------------------------------- bf16 weight-direct kernel
@@ -1269,8 +1318,11 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
           if constexpr (!PAIR) return run_lds<Cfg3, EPI>(a, split, s);
           break;
         case 4: return run_lds<Cfg4, EPI>(a, split, s);
-        case 5: return run_wide<Cfg5, EPI>(a, split, s);
-        case 6: return run_wide<Cfg6, EPI>(a, split, s);
+        case 5:
+        case 6:
+          // the wide kernels' gate epilogue is the staged one only
+          if (EPI == EPI_GATE && !a.staged) return run_lds<Cfg1, EPI>(a, split, s);
+          return cfg == 5 ? run_wide<Cfg5, EPI>(a, split, s) : run_wide<Cfg6, EPI>(a, split, s);
         default: break;
       }
     }
