@@ -724,14 +724,15 @@ gemm_lds_kernel(GemmArgs g) {
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   if (nk > 0) tile(nk - 1, std::true_type{});
   if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
+    // bf16 q|k|v outputs: only the staged form is compiled here (the host
+    // runs unaligned launches on the register-staged kernel); both forms in
+    // one kernel cost registers and code in the main loop
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
-    if (g.staged) {
-      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                              S::NS * S::STAGE);
-      return;
-    }
+    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                            S::NS * S::STAGE);
+  } else {
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   }
-  epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
 }
 
 // ------------------------------------------------- bf16 wide-wave kernel
@@ -854,23 +855,14 @@ gemm_wide_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   tile(nk - 1, std::true_type{});
-  if constexpr (EPI == EPI_GATE) {
-    // only the staged form: the host runs unaligned gate launches on the
-    // other kernels (with both forms compiled in, these 256 x 256 tiles
-    // spilled registers inside the main loop)
+  if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
+    // only the staged form, as in the LDS kernels (with both forms compiled
+    // in, the gate epilogue spilled registers into the main loop of these
+    // 256 x 256 tiles)
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
     epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
                                                             S::NS * S::STAGE);
-    return;
   } else {
-    if constexpr (EPI == EPI_QKV) {
-      static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
-      if (g.staged) {
-        epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane,
-                                                                smem, S::NS * S::STAGE);
-        return;
-      }
-    }
     epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   }
 }
@@ -1310,7 +1302,8 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
   }
   if constexpr (sizeof(T) == 2) {
     constexpr bool PAIR = EPI == EPI_SWIGLU || EPI == EPI_QKV;
-    if (cfg > 0 && lds_ok(a)) {
+    constexpr bool STAGED_ONLY = EPI == EPI_GATE || EPI == EPI_QKV;   // see the kernels' epilogues
+    if (cfg > 0 && lds_ok(a) && (!STAGED_ONLY || a.staged)) {
       switch (cfg) {
         case 1: return run_lds<Cfg1, EPI>(a, split, s);
         case 2: return run_lds<Cfg2, EPI>(a, split, s);
@@ -1318,11 +1311,8 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
           if constexpr (!PAIR) return run_lds<Cfg3, EPI>(a, split, s);
           break;
         case 4: return run_lds<Cfg4, EPI>(a, split, s);
-        case 5:
-        case 6:
-          // the wide kernels' gate epilogue is the staged one only
-          if (EPI == EPI_GATE && !a.staged) return run_lds<Cfg1, EPI>(a, split, s);
-          return cfg == 5 ? run_wide<Cfg5, EPI>(a, split, s) : run_wide<Cfg6, EPI>(a, split, s);
+        case 5: return run_wide<Cfg5, EPI>(a, split, s);
+        case 6: return run_wide<Cfg6, EPI>(a, split, s);
         default: break;
       }
     }
