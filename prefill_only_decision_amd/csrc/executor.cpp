@@ -281,6 +281,10 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
     }
     L.w_down = m->alloc((size_t)d * F * m->esz);
     if ((rc = ld.projection(f + ".down", d, F, tg & S1_LORA_DOWN, L.w_down, {}))) return rc;
+    if (m->bf16 && F % 64 == 0) {   // the weight-direct copy for the down GEMM at many rows
+      L.w_down_frag = m->alloc(frag_bytes(d, F));
+      S1_TRY(launch_frag_pack(L.w_down, d, F, F, false, L.w_down_frag, s), "pack down");
+    }
   }
   return S1_OK;
 }
@@ -928,6 +932,15 @@ int gate_up_direct(const Model* m, const LayerW& L, int T) {
   return 11 * w2 < 10 * w1 ? 2 : 1;
 }
 
+// The down projection on the weight-direct kernel (256 x 256 tiles) when it
+// runs without a K split and its tiles fill the chip at least once: its
+// weights bypass LDS as in the gate/up GEMM.  Measured on MI355X at 16,925
+// rows (4B shape): see the design notes' kernel table.  Same K order as the
+// LDS kernels, so rows stay bitwise independent of M.
+bool down_direct(const Model* m, const LayerW& L, int T, int split) {
+  return L.w_down_frag && split == 1 && gemm_wd_tiles(2, T, m->cfg.d_model) >= m->n_cu;
+}
+
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
 // output (the GEMM picks the split it uses, up to this).
 int max_split(const Model* m, const Plan* p, int M) {
@@ -1089,8 +1102,14 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       gd.norm_out = xn;
       gd.norm_eps = c.rms_eps;
     }
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &xn_ready),
-           "FFN down");
+    if (down_direct(m, L, T, max_split(m, p, T))) {
+      gd.W = L.w_down_frag;
+      S1_TRY(launch_gemm_wd(EPI_RESID, gd, 2, s), "FFN down");
+      xn_ready = false;
+    } else {
+      S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &xn_ready),
+             "FFN down");
+    }
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {
       S1_TRY(launch_gather_rows(m->x, d, ps.cap_rows, ps.cap_dst, ps.n_cap,

@@ -1464,14 +1464,15 @@ hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void
 
 bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
   const long long abytes = (long long)a.M * a.lda * 2;
-  return (epi == EPI_F32 || (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) && a.K >= 64 &&
-         a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
+  return (epi == EPI_F32 || epi == EPI_RESID || (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) &&
+         a.K >= 64 && a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
 }
 
 template <typename S>
 hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_F32: return run_wd<S, EPI_F32>(a, s);
+    case EPI_RESID: return run_wd<S, EPI_RESID>(a, s);
     case EPI_SWIGLU: return run_wd<S, EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
