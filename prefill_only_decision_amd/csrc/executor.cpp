@@ -220,6 +220,15 @@ std::vector<int> offset_map(int n, int base) {
   return v;
 }
 
+// Fragment-order copy of a bf16 weight [N, K] for the weight-direct GEMM
+// (K a multiple of 64); nothing for fp32 models or other K.
+int pack_direct(Model* m, const void* W, int N, int K, void** out, hipStream_t s) {
+  if (!m->bf16 || K % 64) return S1_OK;
+  *out = m->alloc(frag_bytes(N, K));
+  S1_TRY(launch_frag_pack(W, N, K, K, false, *out, s), "pack a weight for the weight-direct GEMM");
+  return S1_OK;
+}
+
 int load_layers(Model* m, Loader& ld, hipStream_t s) {
   const s1_config& c = m->cfg;
   const int d = c.d_model, F = c.ffn, H = c.la_heads, dk = c.la_dk, dv = c.la_dv;
@@ -281,10 +290,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
     }
     L.w_down = m->alloc((size_t)d * F * m->esz);
     if ((rc = ld.projection(f + ".down", d, F, tg & S1_LORA_DOWN, L.w_down, {}))) return rc;
-    if (m->bf16 && F % 64 == 0) {   // the weight-direct copy for the down GEMM at many rows
-      L.w_down_frag = m->alloc(frag_bytes(d, F));
-      S1_TRY(launch_frag_pack(L.w_down, d, F, F, false, L.w_down_frag, s), "pack down");
-    }
+    if ((rc = pack_direct(m, L.w_down, d, F, &L.w_down_frag, s))) return rc;
   }
   return S1_OK;
 }
@@ -933,12 +939,13 @@ int gate_up_direct(const Model* m, const LayerW& L, int T) {
 }
 
 // The down projection on the weight-direct kernel (256 x 256 tiles) when it
-// runs without a K split and its tiles fill the chip at least once: its
-// weights bypass LDS as in the gate/up GEMM.  Measured on MI355X at 16,925
-// rows (4B shape): see the design notes' kernel table.  Same K order as the
-// LDS kernels, so rows stay bitwise independent of M.
-bool down_direct(const Model* m, const LayerW& L, int T, int split) {
-  return L.w_down_frag && split == 1 && gemm_wd_tiles(2, T, m->cfg.d_model) >= m->n_cu;
+// runs without a K split and its tiles fill the chip at least once: the
+// weights bypass LDS as in the gate/up GEMM (4B shape, 16,925 rows, on
+// MI355X: 930 -> 817 us; the out-projection, K = 2,048, gained nothing:
+// 270 against 275 us).  Same K order as the LDS kernels, so rows stay
+// bitwise independent of M.
+bool residual_direct(const Model* m, const void* frag, int T, int split) {
+  return frag && split == 1 && gemm_wd_tiles(2, T, m->cfg.d_model) >= m->n_cu;
 }
 
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
@@ -1102,7 +1109,7 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       gd.norm_out = xn;
       gd.norm_eps = c.rms_eps;
     }
-    if (down_direct(m, L, T, max_split(m, p, T))) {
+    if (residual_direct(m, L.w_down_frag, T, max_split(m, p, T))) {
       gd.W = L.w_down_frag;
       S1_TRY(launch_gemm_wd(EPI_RESID, gd, 2, s), "FFN down");
       xn_ready = false;
