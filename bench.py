@@ -43,7 +43,8 @@ def gemm_flops(shape, T):
     return {
         "gemm_la_in": 2 * T * d * (2 * H * dk + H * dv + H),
         "gemm_fa_qkv": 2 * T * d * (Hq + 2 * Hkv) * hd,
-        "gemm_o": None,  # mixed K (linear and full layers); not used for the roofline
+        # per launch averaged over the layers (K = H dv on linear layers, Hq hd on full ones)
+        "gemm_o": 2 * T * d * (shape.n_linear * H * dv + shape.n_full * Hq * hd) / shape.n_layers,
         "gemm_gate_up": 2 * T * d * 2 * F,
         "gemm_down": 2 * T * F * d,
     }
@@ -633,7 +634,7 @@ def main():
     scan = scan_roofline(shape, batch, tokens, prof, steps_p)
     attn = attention_roofline(shape, batch, prof, steps_p)
     gemm_fracs = {}
-    for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_gate_up", "gemm_down"):
+    for k in ("gemm_la_in", "gemm_fa_qkv", "gemm_o", "gemm_gate_up", "gemm_down"):
         if k in prof and flops.get(k):
             n_k, us_k = prof[k]
             tf = flops[k] * (n_k // steps_p) / (us_k / steps_p * 1e-6) / 1e12
