@@ -1133,33 +1133,63 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, lo
 // Split-K reduction into a residual row, fused with the RMSNorm of the
 // updated row: one workgroup per row, partial slabs summed in a fixed order.
 constexpr int RN_MAXV = 16;   // N <= 4 * 256 * RN_MAXV
-template <typename T>
+template <typename T, int MAXV>
 __global__ void __launch_bounds__(256)
 splitk_resid_norm_kernel(const float* __restrict__ ws, int split, long long stride, float* __restrict__ out,
                          int N, int ld, const float* __restrict__ w, T* __restrict__ nout, float eps) {
   __shared__ float red[4];
   const long long row = blockIdx.x;
-  float4 v[RN_MAXV];
+  // every load of the row first (partials of up to SPLIT_MAX splits and the
+  // residual), then the sums in split order: one memory round trip
+  constexpr int SPLIT_MAX = 4;
+  float4 part[MAXV][SPLIT_MAX], v[MAXV];
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int c = (k * 256 + (int)threadIdx.x) * 4;
+    if (c < N) {
+      const long long src = row * N + c;
+#pragma unroll
+      for (int z = 0; z < SPLIT_MAX; ++z)
+        if (z < split) part[k][z] = *reinterpret_cast<const float4*>(ws + z * stride + src);
+      v[k] = *reinterpret_cast<const float4*>(out + row * ld + c);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < RN_MAXV; ++k) {
+  for (int k = 0; k < MAXV; ++k) {
     const int c = (k * 256 + (int)threadIdx.x) * 4;
     if (c >= N) break;
-    const long long src = row * N + c;
-    float4 t = *reinterpret_cast<const float4*>(ws + src);
-    for (int z = 1; z < split; ++z) {
-      const float4 p = *reinterpret_cast<const float4*>(ws + z * stride + src);
-      t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
-    }
-    float4* d = reinterpret_cast<float4*>(out + row * ld + c);
-    float4 o = *d;
+    float4 t = part[k][0];
+#pragma unroll
+    for (int z = 1; z < SPLIT_MAX; ++z)
+      if (z < split) {
+        t.x += part[k][z].x; t.y += part[k][z].y; t.z += part[k][z].z; t.w += part[k][z].w;
+      }
+    float4 o = v[k];
     o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
-    *d = o;
+    *reinterpret_cast<float4*>(out + row * ld + c) = o;
     v[k] = o;
     ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
   }
   ss = block_sum<4>(ss, red);
-  write_normed_row<T, 256, RN_MAXV>(v, ss, N, eps, w, nout + row * N);
+  write_normed_row<T, 256, MAXV>(v, ss, N, eps, w, nout + row * N);
+}
+
+// the smallest row-register count that holds N columns (N <= 4 * 256 * RN_MAXV)
+template <typename T>
+hipError_t launch_splitk_resid_norm(const GemmArgs& a, const float* ws, int split, long long stride, hipStream_t s) {
+  const int nv = (a.N + 1023) / 1024;
+#define S1_RN(V)                                                                                              \
+  hipLaunchKernelGGL((splitk_resid_norm_kernel<T, V>), dim3(a.M), dim3(256), 0, s, ws, split, stride,          \
+                     reinterpret_cast<float*>(a.out0), a.N, a.ld0, a.norm_w, reinterpret_cast<T*>(a.norm_out),  \
+                     a.norm_eps)
+  if (nv <= 2) S1_RN(2);
+  else if (nv <= 3) S1_RN(3);
+  else if (nv <= 5) S1_RN(5);
+  else if (nv <= 8) S1_RN(8);
+  else S1_RN(RN_MAXV);
+#undef S1_RN
+  return hipGetLastError();
 }
 
 // ----------------------------------------------- fp32 kernel for few tiles
@@ -1330,12 +1360,9 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
     p.split_stride = (long long)a.M * a.N;
     hipError_t e = run_cfg<T, EPI_PARTIAL>(p, split, cfg, s);
     if (e != hipSuccess) return e;
-    if (epi == EPI_RESID && a.norm_w && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV) {
-      hipLaunchKernelGGL(splitk_resid_norm_kernel<T>, dim3(a.M), dim3(256), 0, s, ws, split, p.split_stride,
-                         reinterpret_cast<float*>(a.out0), a.N, a.ld0, a.norm_w,
-                         reinterpret_cast<T*>(a.norm_out), a.norm_eps);
+    if (epi == EPI_RESID && a.norm_w && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV && split <= 4) {
       if (normed) *normed = true;
-      return hipGetLastError();
+      return launch_splitk_resid_norm<T>(a, ws, split, p.split_stride, s);
     }
     const long long n4 = (long long)a.M * (a.N / 4);
     const int blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
