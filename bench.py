@@ -231,8 +231,8 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
            "copy_bytes": COPY_BYTES, "copy_fetch_bytes": round(c_f), "copy_write_bytes": round(c_w),
            "gemm_source_sha256": source_digest(),
            "commands": [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c.lower()} -o run -f csv -- python3 bench.py "
-                        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-serve --no-peaks --no-readout-stress --profile-steps 1 "
-                        f"--calibrate-copy"
+                        f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline --no-serve --no-peaks "
+                        f"--no-readout-stress --no-other-workloads --profile-steps 1 --calibrate-copy"
                         for c in ("FETCH_SIZE", "WRITE_SIZE")]}
     rec["traffic_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     with open(traffic_file(workload), "w") as f:
