@@ -254,6 +254,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
         if ((rc = ld.taps(q + ".conv", 2 * H * dk + H * dv, 4, &L.conv))) return rc;
       }
       L.k_o = H * dv;
+      if ((rc = pack_direct(m, L.w_in, L.n_in, d, &L.w_in_frag, s))) return rc;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
       if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
     } else {
@@ -270,6 +271,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
       if ((rc = ld.projection(q + ".v", Hkv * hd, d, tg & S1_LORA_V, L.w_in,
                               offset_map(Hkv * hd, (Hq + Hkv) * hd)))) return rc;
       L.k_o = Hq * hd;
+      if ((rc = pack_direct(m, L.w_in, L.n_in, d, &L.w_in_frag, s))) return rc;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
       if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
     }
@@ -948,6 +950,13 @@ bool residual_direct(const Model* m, const void* frag, int T, int split) {
   return frag && split == 1 && gemm_wd_tiles(2, T, m->cfg.d_model) >= m->n_cu;
 }
 
+// The mixer in-projections (linear-attention q|k|v|gate, attention q|k|v)
+// on the weight-direct kernel's 256 x 256 tiles when those fill the chip,
+// with the staged bf16 epilogue.  Same K order as the LDS kernels.
+bool in_direct(const Model* m, const LayerW& L, int T) {
+  return L.w_in_frag && gemm_wd_tiles(2, T, L.n_in) >= m->n_cu;
+}
+
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
 // output (the GEMM picks the split it uses, up to this).
 int max_split(const Model* m, const Plan* p, int M) {
@@ -1004,7 +1013,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
         g.out2 = m->beta + (size_t)r0 * H;
         g.nsplit2 = g.nsplit + H;
       }
-      S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s, gemm_cfg(m, p)), "linear-attention in-projection");
+      if (in_direct(m, L, T) && gemm_wd_ok(EPI_GATE, g)) {
+        g.W = L.w_in_frag;
+        S1_TRY(launch_gemm_wd(EPI_GATE, g, 2, s), "linear-attention in-projection");
+      } else {
+        S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s, gemm_cfg(m, p)), "linear-attention in-projection");
+      }
       MARK(KC_GEMM_LA_IN);
       float* states = m->states + (size_t)L.la_idx * c.max_prefixes * H * dk * dv;
       if (gdn) {
@@ -1043,7 +1057,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       g.head_dim = hd;
       g.pos = p->pos + r0;
       g.rope = m->rope;
-      S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s, gemm_cfg(m, p)), "attention QKV projection");
+      if (in_direct(m, L, T) && gemm_wd_ok(EPI_QKV, g)) {
+        g.W = L.w_in_frag;
+        S1_TRY(launch_gemm_wd(EPI_QKV, g, 2, s), "attention QKV projection");
+      } else {
+        S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s, gemm_cfg(m, p)), "attention QKV projection");
+      }
       MARK(KC_GEMM_FA_QKV);
       const bool split = !p->invariant;
       S1_TRY(launch_attention(m->bf16, qkv, m->ld_qkv, kc, vc, (int)kvld, att, m->ld_att, ps.attn,

@@ -1065,6 +1065,9 @@ gemm_wd_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
   if constexpr (EPI == EPI_SWIGLU)
     epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
+  else if constexpr (EPI == EPI_GATE || EPI == EPI_QKV)
+    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
+                                                            S::NS * S::STAGE);
   else
     epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
 }
@@ -1491,7 +1494,8 @@ hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void
 
 bool gemm_wd_ok(Epi epi, const GemmArgs& a) {
   const long long abytes = (long long)a.M * a.lda * 2;
-  return (epi == EPI_F32 || epi == EPI_RESID || (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0)) &&
+  return (epi == EPI_F32 || epi == EPI_RESID || (epi == EPI_SWIGLU && a.ld0 % 8 == 0 && a.n_valid % 8 == 0) ||
+          ((epi == EPI_GATE || epi == EPI_QKV) && staged_ok(epi, a))) &&
          a.K >= 64 && a.K % 64 == 0 && a.lda % 8 == 0 && abytes < (1LL << 31);
 }
 
@@ -1501,6 +1505,13 @@ hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
     case EPI_F32: return run_wd<S, EPI_F32>(a, s);
     case EPI_RESID: return run_wd<S, EPI_RESID>(a, s);
     case EPI_SWIGLU: return run_wd<S, EPI_SWIGLU>(a, s);
+    case EPI_GATE:
+    case EPI_QKV:
+      // bf16 q|k|v outputs staged through the activation stages: the
+      // 256 x 256 tile only (the 128 x 384 tile's stages are too small)
+      if constexpr (S::BM * S::BN * 2 <= S::NS * S::STAGE)
+        return epi == EPI_GATE ? run_wd<S, EPI_GATE>(a, s) : run_wd<S, EPI_QKV>(a, s);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

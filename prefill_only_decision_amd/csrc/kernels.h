@@ -62,9 +62,10 @@ hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* 
                        hipStream_t s, int tile_cfg = GEMM_AUTO, bool* normed = nullptr);
 // Weight-direct GEMM (bf16): W is a fragment-order copy made by
 // launch_frag_pack (frag_bytes(N, K) bytes); K a positive multiple of 64;
-// EPI_F32, EPI_RESID, or EPI_SWIGLU over a copy packed with gu16 (gate/up
-// interleaved in blocks of 16 rows; ld0 and n_valid multiples of 8).  No K
-// split.
+// EPI_F32, EPI_RESID, EPI_SWIGLU over a copy packed with gu16 (gate/up
+// interleaved in blocks of 16 rows; ld0 and n_valid multiples of 8), or,
+// with tile 2 only, EPI_GATE / EPI_QKV on destinations the staged epilogue
+// accepts.  No K split.
 size_t frag_bytes(int N, int K);
 hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void* out, hipStream_t s);
 // tile 1: 128 x 384 workgroup tiles (a wave 128 x 96); tile 2: 256 x 256 (a
