@@ -300,14 +300,16 @@ int s1_plan_profile(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out,
   if (p->owner != m) return set_error(S1_EINVAL, "plan belongs to another model");
   Model* mm = m->m;
   hipStream_t s = hip_stream ? static_cast<hipStream_t>(hip_stream) : mm->own_stream;
-  if (!mm->prof) mm->prof = new (std::nothrow) Profiler();
-  if (!mm->prof || mm->prof->reserve(16 * mm->cfg.n_layers + 64) != S1_OK)
+  if (!mm->prof_store) mm->prof_store = new (std::nothrow) Profiler();
+  if (!mm->prof_store || mm->prof_store->reserve(16 * mm->cfg.n_layers + 64) != S1_OK)
     return set_error(S1_EDEVICE, "profiler events");
+  // events are recorded during this run only (other runs, graph captures
+  // included, record none)
+  Profiler* pr = mm->prof_store;
+  mm->prof = pr;
   int rc = run_plan(mm, p->p, d_probs, d_out, s);
-  Profiler* pr = mm->prof;
   mm->prof = nullptr;
   const hipError_t se = hipStreamSynchronize(s);
-  mm->prof = pr;
   if (rc) return rc;
   if (se != hipSuccess) return set_error(S1_EDEVICE, hip_msg(se, "profiled run"));
   if (pr->overflow) return set_error(S1_EDEVICE, "profiler ran out of events");
@@ -333,6 +335,25 @@ int s1_plan_profile(s1_model* m, s1_plan* p, float* d_probs, s1_decision* d_out,
   }
   *n_out = k;
   return S1_OK;
+}
+
+// Everything of a batch that decides its plan's device layout and launch
+// arguments: sequence lengths, prefixes, questions (sequence, type, marker)
+// and option counts.  Token and option ids are contents.
+static std::vector<long long> decide_signature(const s1_batch* b) {
+  std::vector<long long> v;
+  const int n = b->n_seqs, Q = b->n_questions;
+  v.push_back(n);
+  for (int i = 0; i <= n; ++i) v.push_back(b->cu_seqlens[i]);
+  for (int i = 0; i < n; ++i) v.push_back(b->prefix_of ? b->prefix_of[i] : -1);
+  v.push_back(Q);
+  for (int j = 0; j < Q; ++j) {
+    v.push_back(b->q_seq[j]);
+    v.push_back(b->q_type[j]);
+    v.push_back(b->q_marker[j]);
+    v.push_back(b->opt_offsets[j + 1] - b->opt_offsets[j]);
+  }
+  return v;
 }
 
 int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision* out,
@@ -363,9 +384,53 @@ int s1_prefill_decide(s1_model* m, const s1_batch* b, float* probs, s1_decision*
   };
   float* dprobs = static_cast<float*>(p->extra);
   s1_decision* ddec = reinterpret_cast<s1_decision*>(static_cast<char*>(p->extra) + pbytes);
+  // the batch's structure: a repeat of the previous call's runs as a HIP graph
+  std::vector<long long> sig = decide_signature(b);
+  sig.push_back(reinterpret_cast<long long>(mm->decide_dev));
+  sig.push_back((long long)mm->decide_bytes);
+  const bool repeat = sig == mm->decide_sig;
+  if (!repeat) {
+    mm->drop_decide_graph();
+    mm->decide_sig = sig;
+    mm->decide_eager = false;
+  }
   if (hipEventRecord(mm->decide_ev[0], s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
-  rc = run_plan(mm, p, dprobs, ddec, s);
-  if (rc) return fail(rc, "");
+  if (repeat && !mm->decide_gexec && !mm->decide_eager) {   // second call of this structure: capture it
+    // a stream that cannot be captured (or a failed instantiation) leaves
+    // this structure on eager launches
+    hipGraph_t g = nullptr;
+    hipGraphExec_t x = nullptr;
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      rc = run_plan(mm, p, dprobs, ddec, s);
+      e = hipStreamEndCapture(s, &g);
+      if (rc) {
+        if (g) (void)hipGraphDestroy(g);
+        mm->decide_sig.clear();
+        return fail(rc, "");
+      }
+      if (e == hipSuccess) e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    }
+    if (e == hipSuccess) {
+      mm->decide_graph = g;
+      mm->decide_gexec = x;
+    } else {
+      (void)hipGetLastError();
+      if (g) (void)hipGraphDestroy(g);
+      mm->decide_eager = true;
+    }
+  }
+  if (mm->decide_gexec) {
+    const hipError_t e = hipGraphLaunch(mm->decide_gexec, s);
+    if (e != hipSuccess) {
+      mm->drop_decide_graph();
+      mm->decide_sig.clear();
+      return fail(S1_EDEVICE, hip_msg(e, "graph launch"));
+    }
+  } else {
+    rc = run_plan(mm, p, dprobs, ddec, s);
+    if (rc) return fail(rc, "");
+  }
   if (hipEventRecord(mm->decide_ev[1], s) != hipSuccess) return fail(S1_EDEVICE, "event record failed");
   if (Q > 0) {
     if (hipMemcpyAsync(probs, dprobs, (size_t)nopt * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||

@@ -62,8 +62,16 @@ void Profiler::mark(int c, hipStream_t s) {
   cls[used++] = c;
 }
 
+void Model::drop_decide_graph() {
+  if (decide_gexec) (void)hipGraphExecDestroy(decide_gexec);
+  if (decide_graph) (void)hipGraphDestroy(decide_graph);
+  decide_gexec = nullptr;
+  decide_graph = nullptr;
+}
+
 Model::~Model() {
-  delete prof;
+  drop_decide_graph();
+  delete prof_store;
   for (hipEvent_t e : decide_ev)
     if (e) (void)hipEventDestroy(e);
   if (decide_dev) (void)hipFree(decide_dev);

@@ -105,7 +105,18 @@ struct Model {
   void* decide_dev = nullptr;
   size_t decide_bytes = 0;
   hipEvent_t decide_ev[2] = {nullptr, nullptr};
-  Profiler* prof = nullptr;     // set only during s1_plan_profile
+  // s1_prefill_decide replays a HIP graph when a batch repeats the previous
+  // call's structure (everything but the token and option ids): the plan's
+  // device layout in decide_dev is then the same, so only its contents are
+  // uploaded again.  decide_sig is that structure (with the block's address
+  // and size); the graph is captured on the second call of a structure.
+  std::vector<long long> decide_sig;
+  hipGraph_t decide_graph = nullptr;
+  hipGraphExec_t decide_gexec = nullptr;
+  bool decide_eager = false;    // this structure could not be captured
+  void drop_decide_graph();
+  Profiler* prof = nullptr;     // set only during s1_plan_profile's run
+  Profiler* prof_store = nullptr;   // its events, kept between profiled runs
   std::vector<void*> allocs;
   ~Model();
   void* alloc(size_t bytes);    // throws std::bad_alloc on failure

@@ -128,6 +128,30 @@ def test_host_path_equals_plan_path():
     assert t["tokens"] == 181
 
 
+def test_host_path_replays_repeated_structures():
+    """The boundary call replays a captured HIP graph when a batch repeats
+    the previous call's structure (lengths, prefixes, questions, markers,
+    option counts) with new token and option ids: every call must answer
+    like a plan built for its batch, and another structure in between must
+    not reuse the graph."""
+    model, _ = _model(MINI)
+    base = random_batch(MINI.vocab, [150, 31, 20], seed=15, prefix_of=[-1, 0, -1])
+    other = random_batch(MINI.vocab, [90, 40], seed=16)
+    rng = np.random.default_rng(17)
+
+    def refill(b):
+        opt = np.concatenate([rng.choice(MINI.vocab, int(b.opt_offsets[j + 1] - b.opt_offsets[j]), replace=False)
+                              for j in range(b.n_questions)]).astype(np.int32)
+        return replace(b, token_ids=rng.integers(0, MINI.vocab, b.token_ids.shape[0]).astype(np.int32),
+                       opt_ids=opt)
+
+    for k, b in enumerate([base, refill(base), refill(base), other, refill(base), refill(base)]):
+        p1, d1, _ = run_gpu(model, b)
+        p2, d2, _ = model.decide(b)
+        log(f"call {k}: {int((p1 != p2).sum())} probabilities differ from a plan of the batch")
+        assert np.array_equal(p1, p2) and np.array_equal(d1, d2), k
+
+
 def test_option_and_question_permutation():
     model, _ = _model(MINI)
     b = random_batch(MINI.vocab, [180, 77], seed=14, questions_per_seq=[3, 2])
