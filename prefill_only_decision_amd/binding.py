@@ -26,7 +26,7 @@ EXPORTS = (
     "s1_plan_profile", "s1_plan_set_graph", "s1_plan_set_features", "s1_plan_set_invariant",
     "s1_plan_create_bucket", "s1_plan_update", "s1_plan_questions", "s1_plan_options",
     "s1_plan_set_layer_inputs",
-    "s1k_gemm", "s1k_gemm_noalloc", "s1k_gemm_cfg", "s1k_gemm_tile_configs", "s1k_frag_bytes", "s1k_frag_pack", "s1k_gemm_wfrag",
+    "s1k_gemm", "s1k_gemm_noalloc", "s1k_gemm_cfg", "s1k_gemm_resid_norm", "s1k_gemm_tile_configs", "s1k_frag_bytes", "s1k_frag_pack", "s1k_gemm_wfrag",
     "s1k_mfma_peak", "s1k_stream_copy", "s1k_stream_read",
     "s1k_rmsnorm", "s1k_embed", "s1k_lora_merge", "s1k_la_scan",
     "s1k_la_scan_chunked",
@@ -131,6 +131,7 @@ def load_library(path=LIB_PATH):
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_gemm_noalloc": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
+        "s1k_gemm_resid_norm": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
         "s1k_gemm_tile_configs": (C.c_int, []),
         "s1k_frag_bytes": (i64, [i32, i32]),
         "s1k_mfma_peak": (C.c_int, [vp, i32, i32, vp, vp]),
@@ -446,6 +447,11 @@ def gemm_noalloc(dtype, A, W, Cout, M, N, K, split_k=1, stream=None):
 def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
     return _k("s1k_gemm_cfg", dtype, C.c_void_p(A), C.c_void_p(W), C.c_void_p(Cout), M, N, K, split_k, cfg,
               _stream(stream))
+
+
+def gemm_resid_norm(A, W, x, M, N, K, split_k, cfg, eps, hb, rs, stream=None):
+    return _k("s1k_gemm_resid_norm", C.c_void_p(A), C.c_void_p(W), C.c_void_p(x), M, N, K, split_k, cfg,
+              C.c_float(eps), C.c_void_p(hb), C.c_void_p(rs), _stream(stream))
 
 
 def gemm_tile_configs():

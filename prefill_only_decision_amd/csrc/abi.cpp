@@ -498,6 +498,45 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
   return gemm_entry(dtype, A, W, C, M, N, K, split_k, tile_cfg, hip_stream);
 }
 
+int s1k_gemm_resid_norm(const void* A, const void* W, float* x, int32_t M, int32_t N, int32_t K,
+                        int32_t split_k, int32_t tile_cfg, float eps, void* hb, float* rs, void* hip_stream) {
+  if (M < 0 || N < 1 || N > 8192 || K < 8 || K % 8 || split_k < 1 || (split_k > 1 && (N % 4 || K % 64)) || !A ||
+      !W || !x || !hb || !rs || tile_cfg < GEMM_AUTO || tile_cfg >= gemm_tile_configs())
+    return set_error(S1_EINVAL, "s1k_gemm_resid_norm: unsupported arguments");
+  if (M == 0) return S1_OK;
+  const hipStream_t s = strm(hip_stream);
+  const int ld = (M + 31) / 32 * 32, nt = (M / 32 + 2 + 3) / 4 * 4;   // 16-byte aligned split workspace
+  const size_t parts = (size_t)((N + 31) / 32) * ld * sizeof(float);
+  const size_t split_bytes = split_k > 1 ? (size_t)split_k * M * N * sizeof(float) : 0;
+  char* ws = nullptr;
+  if (dev_alloc_async(reinterpret_cast<void**>(&ws), parts + nt * sizeof(unsigned) + split_bytes + 256, s) !=
+      hipSuccess)
+    return set_error(S1_ENOMEM, "s1k_gemm_resid_norm: workspace allocation failed");
+  GemmArgs g{};
+  g.A = A;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldw = K;
+  g.out0 = x;
+  g.ld0 = N;
+  g.norm_out = hb;
+  g.norm_eps = eps;
+  g.rs_out = rs;
+  g.ss_parts = reinterpret_cast<float*>(ws);
+  g.ss_ld = ld;
+  g.tickets = reinterpret_cast<unsigned*>(ws + parts);
+  float* sws = split_k > 1 ? reinterpret_cast<float*>(ws + parts + nt * sizeof(unsigned)) : nullptr;
+  hipError_t e = hipMemsetAsync(g.tickets, 0, nt * sizeof(unsigned), s);
+  bool normed = false;
+  if (e == hipSuccess) e = launch_gemm(true, EPI_RESID, g, split_k, sws, s, tile_cfg, &normed);
+  (void)hipFreeAsync(ws, s);
+  if (e == hipSuccess && !normed) return set_error(S1_EINVAL, "s1k_gemm_resid_norm: shape not supported");
+  return dev_status(e, "s1k_gemm_resid_norm");
+}
+
 int s1k_gemm_tile_configs(void) { return gemm_tile_configs(); }
 
 int s1k_mfma_peak(const void* seed, int32_t blocks, int32_t iters, float* out, void* hip_stream) {

@@ -121,11 +121,31 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // RMSNorm of one row held as float4 pieces v[k] (columns 4 (k * NT + tid)
 // ...): out = v * r * w with r = 1 / sqrt(ss / d + eps), ss the row's sum of
-// squares.
+// squares.  Deferred form (w == NULL): out = v rounded to T and *rs = r, the
+// scale the next GEMM applies to its accumulators (the gain is in its W).
 template <typename T, int NT, int MAXV>
 __device__ __forceinline__ void write_normed_row(const float4 (&v)[MAXV], float ss, int d, float eps,
-                                                 const float* __restrict__ w, T* __restrict__ o) {
+                                                 const float* __restrict__ w, T* __restrict__ o,
+                                                 float* __restrict__ rs = nullptr) {
   const float r = rsqrtf(ss / d + eps);
+  if (w == nullptr) {
+    if (threadIdx.x == 0) *rs = r;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int c = (k * NT + (int)threadIdx.x) * 4;
+      if (c >= d) break;
+      const float4 x = v[k];
+      if constexpr (sizeof(T) == 2) {
+        uint2 u;
+        u.x = pack_bf2(x.x, x.y);
+        u.y = pack_bf2(x.z, x.w);
+        *reinterpret_cast<uint2*>(o + c) = u;
+      } else {
+        *reinterpret_cast<float4*>(o + c) = x;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < MAXV; ++k) {
     const int c = (k * NT + (int)threadIdx.x) * 4;

@@ -158,7 +158,7 @@ class Loader {
   // Merge the adapter of `name` (if it is a target) into its rows of dst,
   // row o of the [out, in] source going to dst row map[o] (or base + o).
   int projection(const std::string& name, int out_dim, int in_dim, bool target, void* dst,
-                 const std::vector<int>& map) {
+                 const std::vector<int>& map, const float* gain = nullptr) {
     const void* w = nullptr;
     const void* a = nullptr;
     const void* b = nullptr;
@@ -180,7 +180,7 @@ class Loader {
     }
     const float scale = target ? m_->cfg.lora_alpha / (float)r : 0.f;
     S1_TRY(launch_merge(m_->bf16, w, target ? a : nullptr, target ? b : nullptr, dst, out_dim, in_dim,
-                        r, scale, dmap, s_),
+                        r, scale, dmap, s_, gain),
            "LoRA merge");
     S1_TRY(hipStreamSynchronize(s_), "LoRA merge");
     release();
@@ -248,17 +248,23 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
     const std::string p = "layers." + std::to_string(l);
     if ((rc = ld.norm(p + ".attn_norm", d, &L.attn_norm))) return rc;
     if ((rc = ld.norm(p + ".ffn_norm", d, &L.ffn_norm))) return rc;
+    // with the deferred norm the gains scale the consuming weights' columns
+    const float* ga = m->fold ? L.attn_norm : nullptr;
+    const float* gf = m->fold ? L.ffn_norm : nullptr;
     if (!L.full) {
       const std::string q = p + ".la";
       const bool gdn = c.la_kind == S1_LA_GDN;
       L.n_in = 2 * H * dk + H * dv + (gdn ? 2 : 1) * H;
       L.w_in = m->alloc((size_t)L.n_in * d * m->esz);
-      if ((rc = ld.projection(q + ".q", H * dk, d, tg & S1_LORA_Q, L.w_in, offset_map(H * dk, 0)))) return rc;
-      if ((rc = ld.projection(q + ".k", H * dk, d, tg & S1_LORA_K, L.w_in, offset_map(H * dk, H * dk)))) return rc;
-      if ((rc = ld.projection(q + ".v", H * dv, d, tg & S1_LORA_V, L.w_in, offset_map(H * dv, 2 * H * dk)))) return rc;
-      if ((rc = ld.projection(q + ".g", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv)))) return rc;
+      if ((rc = ld.projection(q + ".q", H * dk, d, tg & S1_LORA_Q, L.w_in, offset_map(H * dk, 0), ga))) return rc;
+      if ((rc = ld.projection(q + ".k", H * dk, d, tg & S1_LORA_K, L.w_in, offset_map(H * dk, H * dk), ga)))
+        return rc;
+      if ((rc = ld.projection(q + ".v", H * dv, d, tg & S1_LORA_V, L.w_in, offset_map(H * dv, 2 * H * dk), ga)))
+        return rc;
+      if ((rc = ld.projection(q + ".g", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv), ga))) return rc;
       if (gdn) {
-        if ((rc = ld.projection(q + ".b", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv + H)))) return rc;
+        if ((rc = ld.projection(q + ".b", H, d, false, L.w_in, offset_map(H, 2 * H * dk + H * dv + H), ga)))
+          return rc;
         if ((rc = ld.taps(q + ".conv", 2 * H * dk + H * dv, 4, &L.conv))) return rc;
       }
       L.k_o = H * dv;
@@ -274,10 +280,10 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
         for (int i = 0; i < hd; ++i) mq[h * hd + i] = h * hd + rope_perm(i, hd);
       for (int h = 0; h < Hkv; ++h)
         for (int i = 0; i < hd; ++i) mk[h * hd + i] = Hq * hd + h * hd + rope_perm(i, hd);
-      if ((rc = ld.projection(q + ".q", Hq * hd, d, tg & S1_LORA_Q, L.w_in, mq))) return rc;
-      if ((rc = ld.projection(q + ".k", Hkv * hd, d, tg & S1_LORA_K, L.w_in, mk))) return rc;
+      if ((rc = ld.projection(q + ".q", Hq * hd, d, tg & S1_LORA_Q, L.w_in, mq, ga))) return rc;
+      if ((rc = ld.projection(q + ".k", Hkv * hd, d, tg & S1_LORA_K, L.w_in, mk, ga))) return rc;
       if ((rc = ld.projection(q + ".v", Hkv * hd, d, tg & S1_LORA_V, L.w_in,
-                              offset_map(Hkv * hd, (Hq + Hkv) * hd)))) return rc;
+                              offset_map(Hkv * hd, (Hq + Hkv) * hd), ga))) return rc;
       L.k_o = Hq * hd;
       if ((rc = pack_direct(m, L.w_in, L.n_in, d, &L.w_in_frag, s))) return rc;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
@@ -292,8 +298,8 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
       mg[i] = 64 * (i / 32) + (i % 32);
       mu[i] = mg[i] + 32;
     }
-    if ((rc = ld.projection(f + ".gate", F, d, tg & S1_LORA_GATE, L.w_gu, mg))) return rc;
-    if ((rc = ld.projection(f + ".up", F, d, tg & S1_LORA_UP, L.w_gu, mu))) return rc;
+    if ((rc = ld.projection(f + ".gate", F, d, tg & S1_LORA_GATE, L.w_gu, mg, gf))) return rc;
+    if ((rc = ld.projection(f + ".up", F, d, tg & S1_LORA_UP, L.w_gu, mu, gf))) return rc;
     if (m->bf16 && d % 64 == 0 && F % 8 == 0) {   // the weight-direct GEMM's copy
       L.w_gu_frag = m->alloc(frag_bytes(L.n_gu, d));
       S1_TRY(launch_frag_pack(L.w_gu, L.n_gu, d, d, true, L.w_gu_frag, s), "pack gate/up");
@@ -334,6 +340,15 @@ int alloc_workspace(Model* m) {
     m->gamma = static_cast<float*>(m->alloc((size_t)m->max_chunks * H * sizeof(float)));
     if (c.la_kind == S1_LA_GDN) m->gdn_ws = static_cast<float*>(m->alloc(gdn_ws_bytes(m->max_chunks, H)));
   }
+  if (m->fold) {
+    m->ss_ld = (int)((T + 31) / 32 * 32);
+    m->rstd = static_cast<float*>(m->alloc(T * sizeof(float)));
+    m->ssq = static_cast<float*>(m->alloc((size_t)((d + 31) / 32) * m->ss_ld * sizeof(float)));
+    const size_t nt = (size_t)(T + 31) / 32 + 1;   // row blocks of the smallest tile
+    m->tickets = static_cast<unsigned int*>(m->alloc(nt * sizeof(unsigned int)));
+    if (hipMemset(m->tickets, 0, nt * sizeof(unsigned int)) != hipSuccess)
+      return set_error(S1_EDEVICE, "clear the row-block tickets");
+  }
   m->split_max_rows = (int)std::min<long long>(T, 2048);
   m->splitws_elems = 4LL * m->split_max_rows * d;
   m->splitws = static_cast<float*>(m->alloc(m->splitws_elems * sizeof(float)));
@@ -359,6 +374,9 @@ int load_model(const s1_config* cfg, const s1_tensor* tensors, int n, hipStream_
   m->bf16 = cfg->dtype == S1_BF16;
   m->esz = m->bf16 ? 2 : 4;
   m->ffn_pad = (cfg->ffn + 31) / 32 * 32;
+  // the deferred RMSNorm: bf16 rows that the fused norm kernels hold (d % 4,
+  // d <= 16,384) with at most 256 partial sums of 32 columns
+  m->fold = m->bf16 && cfg->d_model % 32 == 0 && cfg->d_model <= 256 * 32;
   if (hipGetDevice(&m->device) != hipSuccess) {
     delete m;
     return set_error(S1_EDEVICE, "no HIP device");
@@ -990,6 +1008,18 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
   char* att = static_cast<char*>(m->att);
   const long long kvld = (long long)Hkv * hd;
   bool xn_ready = xn_first;   // xn already holds this layer's normalised input
+  // the deferred norm: the consumers' row scales, and what a residual GEMM
+  // needs to produce them
+  float* rstd = m->fold ? m->rstd + r0 : nullptr;
+  auto defer_norm = [&](GemmArgs& a) {
+    a.rs_out = rstd;
+    a.ss_parts = m->ssq + r0;
+    a.ss_ld = m->ss_ld;
+    a.tickets = m->tickets;
+  };
+  auto norm_pass = [&](const float* gain) {   // a norm that no GEMM epilogue produced
+    return launch_rmsnorm(m->bf16, x, m->fold ? nullptr : gain, xn, T, d, c.rms_eps, s, rstd);
+  };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = m->layers[l];
     if (ps.n_inj) {   // replaced layer inputs: the rows, then their norm
@@ -999,11 +1029,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       xn_ready = false;
     }
     if (!xn_ready) {
-      S1_TRY(launch_rmsnorm(m->bf16, x, L.attn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+      S1_TRY(norm_pass(L.attn_norm), "rmsnorm");
       MARK(KC_RMSNORM);
     }
     GemmArgs g{};
     g.A = xn;
+    g.row_scale = rstd;
     g.M = T;
     g.K = d;
     g.lda = d;
@@ -1092,19 +1123,21 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     go.K = L.k_o;
     go.out0 = x;
     go.ld0 = d;
-    go.norm_w = L.ffn_norm;
+    go.norm_w = m->fold ? nullptr : L.ffn_norm;
     go.norm_out = xn;
     go.norm_eps = c.rms_eps;
+    if (m->fold) defer_norm(go);
     bool normed = false;
     S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &normed),
            "mixer out-projection");
     MARK(KC_GEMM_O);
     if (!normed) {
-      S1_TRY(launch_rmsnorm(m->bf16, x, L.ffn_norm, xn, T, d, c.rms_eps, s), "rmsnorm");
+      S1_TRY(norm_pass(L.ffn_norm), "rmsnorm");
       MARK(KC_RMSNORM);
     }
     GemmArgs gu{};
     gu.A = xn;
+    gu.row_scale = rstd;
     gu.lda = d;
     gu.W = L.w_gu;
     gu.ldw = d;
@@ -1131,15 +1164,18 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     gd.K = c.ffn;
     gd.out0 = x;
     gd.ld0 = d;
-    if (l + 1 < c.n_layers) {   // the next layer's input norm, fused when the GEMM splits K
-      gd.norm_w = m->layers[l + 1].attn_norm;
+    // the next layer's input norm: fused into the K split's reduction, or
+    // deferred (its statistics from this GEMM's epilogue)
+    if (l + 1 < c.n_layers) {
+      gd.norm_w = m->fold ? nullptr : m->layers[l + 1].attn_norm;
       gd.norm_out = xn;
       gd.norm_eps = c.rms_eps;
+      if (m->fold) defer_norm(gd);
     }
     if (residual_direct(m, L.w_down_frag, T, max_split(m, p, T))) {
       gd.W = L.w_down_frag;
       S1_TRY(launch_gemm_wd(EPI_RESID, gd, 2, s), "FFN down");
-      xn_ready = false;
+      xn_ready = gd.rs_out != nullptr;
     } else {
       S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &xn_ready),
              "FFN down");
@@ -1164,8 +1200,9 @@ int run_plan(Model* m, Plan* p, float* d_probs, void* d_dec, hipStream_t s) {
   // the gather writes the first layer's normalised input too when the row fits the fused kernel
   const bool fused = c.n_layers > 0 && c.d_model % 4 == 0 && c.d_model <= 16384;
   if (fused)
-    S1_TRY(launch_embed_norm(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, m->layers[0].attn_norm, m->xn,
-                             c.rms_eps, s),
+    S1_TRY(launch_embed_norm(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model,
+                             m->fold ? nullptr : m->layers[0].attn_norm, m->xn, c.rms_eps, s,
+                             m->fold ? m->rstd : nullptr),
            "embedding and first norm");
   else
     S1_TRY(launch_embed(m->bf16, p->ids, m->embed, m->x, p->T, c.d_model, s), "embedding");

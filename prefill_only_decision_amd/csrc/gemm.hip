@@ -20,6 +20,7 @@
 // columns later, i.e. in the neighbouring MFMA tile at the same register.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -51,6 +52,12 @@ __device__ __forceinline__ float log_sigmoid(float z) {
 // SIMD, so their VALU time is not hidden.  e^-a = inf gives a * 0.
 __device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
+// The rotate-half pair (a1, a2) by (cos, sin), with the multiply-adds
+// written out: left to contraction, kernels of different tiles could fuse
+// different products and round a row differently.
+__device__ __forceinline__ float rope_lo(float a1, float a2, float2 cs) { return fmaf(a1, cs.x, -(a2 * cs.y)); }
+__device__ __forceinline__ float rope_hi(float a1, float a2, float2 cs) { return fmaf(a2, cs.x, a1 * cs.y); }
+
 // Global-memory views of the epilogue's pointers: through the generic
 // pointers of GemmArgs the compiler emits flat accesses, whose results it
 // must wait for with vmcnt(0) and lgkmcnt(0) (flat operations may complete
@@ -66,15 +73,237 @@ __device__ __forceinline__ const gmem<T>* gptr(const void* p) {
   return (const gmem<T>*)p;
 }
 
+// ------------------------------------------- deferred RMSNorm (bf16 model)
+// The pre-norm before a projection, x / rms(x) * gain, is split between the
+// GEMM that updates the residual x and the GEMM that consumes it: the gain
+// multiplies the consumer's weight columns (folded in at load), the consumer
+// reads x rounded to bf16 and multiplies each accumulator row by 1 / rms of
+// its row; the producer's epilogue writes that bf16 copy and the 1 / rms.
+// No separate norm pass reads and writes the rows.
+//
+// The sum of squares of a row is taken in one fixed tree whatever the tile
+// configuration (so a row's scale does not depend on the number of rows):
+// each aligned block of 32 columns is summed as a butterfly (pairs of columns
+// c, c ^ 16, then c ^ 8, ... c ^ 1), the blocks as a pairwise tree over
+// aligned groups of 2^k blocks, missing blocks past N being zero.
+
+// Exchange with lane ^ M inside each half-wave (ds_swizzle, bit mode).
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+
+// v[r]: one value per accumulator row r of a 32 x 32 MFMA tile, column lane &
+// 31.  Sums each row over the 32 columns of its half-wave (reduce-scatter:
+// each exchange halves the values a lane keeps) and returns in lanes 2q and
+// 2q + 1 the sum for accumulator row r = q & 15 (row acc_row(r, lane)).
+__device__ __forceinline__ float half_wave_row_sum(float (&v)[16], int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool b = lane & 16;
+    const float keep = b ? v[k + 8] : v[k], send = b ? v[k] : v[k + 8];
+    v[k] = keep + swz_xor<16>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool b = lane & 8;
+    const float keep = b ? v[k + 4] : v[k], send = b ? v[k] : v[k + 4];
+    v[k] = keep + swz_xor<8>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const bool b = lane & 4;
+    const float keep = b ? v[k + 2] : v[k], send = b ? v[k] : v[k + 2];
+    v[k] = keep + swz_xor<4>(send);
+  }
+  {
+    const bool b = lane & 2;
+    const float keep = b ? v[1] : v[0], send = b ? v[0] : v[1];
+    v[0] = keep + swz_xor<2>(send);
+  }
+  return v[0] + swz_xor<1>(v[0]);
+}
+
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&v)[N]) {
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int u = 0; u + w < N; u += 2 * w) v[u] += v[u + w];
+  return v[0];
+}
+
+// Residual epilogue: out0 (fp32) += the tile.  With the deferred norm
+// (bf16, rs_out set) it also writes the updated rows rounded to bf16 and,
+// per row and aligned group of TG = 2^k column blocks (TG the largest power
+// of two dividing TN), the partial sum of squares, to
+// ss_parts[(cn0 / 32 / TG + group) * ss_ld + row].  Each 32 x 32 tile's
+// squares are summed while its values are in registers; no lane skips the
+// exchanges (columns past N count as zero).
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): the
+// accumulator indices stay compile-time constants however large the body
+// (a loop the unroller declines to unroll indexes the accumulators at run
+// time and moves them to scratch memory).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
+
+template <typename T, int TM, int TN>
+__device__ __forceinline__ void epilogue_resid(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0, int cn0,
+                                               int lane) {
+  constexpr int TG = TN & -TN;
+  const int cl = lane & 31;
+  bool defer = false;
+  if constexpr (sizeof(T) == 2) defer = g.rs_out != nullptr;
+  gmem<float>* out = gptr<float>(g.out0);
+  static_for<TM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int rb = rm0 + 32 * i;
+    float part[TN];
+    static_for<TN>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int col = cn0 + 32 * j + cl;
+      const bool cok = col < g.N;
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = min(rb + acc_row(r, lane), g.M - 1);
+        v[r] = cok ? out[(long long)row * g.ld0 + col] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rb + acc_row(r, lane);
+        v[r] += acc[i][j][r];
+        if (cok && row < g.M) out[(long long)row * g.ld0 + col] = v[r];
+      }
+      if (defer) {
+        gmem<bf16_t>* hb = gptr<bf16_t>(g.norm_out);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb + acc_row(r, lane);
+          if (cok && row < g.M) hb[(long long)row * g.N + col] = f2bf(v[r]);
+          v[r] = cok ? __fmul_rn(v[r], v[r]) : 0.f;
+        }
+        part[j] = half_wave_row_sum(v, lane);
+      }
+    });
+    if (defer) {
+      const int row = rb + acc_row((lane >> 1) & 15, lane);
+#pragma unroll
+      for (int q = 0; q < TN / TG; ++q) {
+        float sg[TG];
+#pragma unroll
+        for (int u = 0; u < TG; ++u) sg[u] = part[q * TG + u];
+        const float t = tree_sum(sg);
+        // only groups with a column before N: their slots exist ([N / 32]
+        // rows).  Device-scope stores (coherent across the XCDs' L2s): the
+        // row block's last workgroup, possibly on another XCD, reads them.
+        if ((lane & 1) == 0 && row < g.M && cn0 + 32 * TG * q < g.N)
+          __hip_atomic_store(g.ss_parts + (long long)((cn0 >> 5) / TG + q) * g.ss_ld + row, t, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  });
+}
+
+// After the epilogue of a residual tile with the deferred norm: the last
+// workgroup to finish row block tm (one ticket per column tile) turns the
+// block's partial sums into rs_out.  The partial sums travel as device-scope
+// stores and loads (no cache of one XCD holds a stale copy); every wave waits
+// for its own stores to complete before the workgroup barrier that precedes
+// the ticket, so a workgroup's ticket is taken only after all its partial
+// sums are visible.  Nothing waits on another workgroup.  The slots are
+// summed as aligned 16-slot pairwise trees, then a pairwise tree over those:
+// for any slot width this is the fixed tree above, zero-padded.  Every
+// thread of the workgroup calls this (it has barriers).
+template <int BM, int NT, int TG>
+__device__ __forceinline__ void resid_norm_finish(const GemmArgs& g, int m0, int tm, int nbn) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(g.tickets + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old + 1 == (unsigned)nbn;
+    if (last) __hip_atomic_store(g.tickets + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // for the next launch
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int ns = (g.N + 32 * TG - 1) / (32 * TG);
+  for (int t = threadIdx.x; t < BM; t += NT) {
+    const int row = m0 + t;
+    if (row >= g.M) break;
+    float* p = g.ss_parts + row;
+    // 16 groups of 16 slots; the groups' tree is built as a binary counter
+    // (lv[k]: the pending left subtree of 2^k groups)
+    float lv[4] = {0.f, 0.f, 0.f, 0.f}, total = 0.f;
+#pragma unroll 1
+    for (int q = 0; q < 16; ++q) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = 0.f;
+      if (16 * q < ns) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (16 * q + k < ns)
+            v[k] = __hip_atomic_load(p + (long long)(16 * q + k) * g.ss_ld, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float x = tree_sum(v);
+      if (q & 1) {
+        x = lv[0] + x;
+        if (q & 2) {
+          x = lv[1] + x;
+          if (q & 4) {
+            x = lv[2] + x;
+            if (q & 8) total = lv[3] + x;
+            else lv[3] = x;
+          } else {
+            lv[2] = x;
+          }
+        } else {
+          lv[1] = x;
+        }
+      } else {
+        lv[0] = x;
+      }
+    }
+    gptr<float>(g.rs_out)[row] = rsqrtf(total / g.N + g.norm_eps);
+  }
+}
+
+// Consumer side: the scale of row m0 + tid (tid < BM; 1 without row_scale),
+// loaded at kernel entry so that its latency hides under the operand loads,
+// stored to LDS after the main loop; the epilogues multiply each accumulator
+// by its row's scale where they read it (a separate pass over the
+// accumulators costs the largest tiles registers).
+template <int BM>
+__device__ __forceinline__ float row_scale_load(const GemmArgs& g, int m0) {
+  if (g.row_scale == nullptr) return 1.f;
+  return gptr<float>(g.row_scale)[min(m0 + min((int)threadIdx.x, BM - 1), g.M - 1)];
+}
+template <int BM>
+__device__ __forceinline__ void row_scale_store(float rsv, float* rsl) {
+  if (threadIdx.x < BM) rsl[threadIdx.x] = rsv;
+  __syncthreads();
+}
+constexpr bool scaled_epi(int epi) { return epi == EPI_SWIGLU || epi == EPI_GATE || epi == EPI_QKV; }
+
 // Loads an epilogue needs (the residual, positions, RoPE factors) are issued
 // for a whole 32-row MFMA tile before its stores: a store to the output may
 // alias a later load as far as the compiler knows, so element-by-element
 // read-modify-write would wait for the memory latency once per element.
 template <typename T, int EPI, int TM, int TN>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0,
-                                         int cn0, int lane, int split_idx) {
+                                         int cn0, int lane, int split_idx, const float* rsw = nullptr) {
   const int cl = lane & 31;
-  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+  // row scale of accumulator r of MFMA row block i (rsw: LDS, the wave's first row)
+  auto scl = [&](int i, int r) { return rsw != nullptr ? rsw[32 * i + acc_row(r, lane)] : 1.f; };
+  if constexpr (EPI == EPI_RESID) {
+    epilogue_resid<T, TM, TN>(g, acc, rm0, cn0, lane);
+  } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
     static_assert(TN % 2 == 0, "pair epilogues need both MFMA tiles of a 64-column block in the wave");
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
@@ -89,8 +318,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = rb + acc_row(r, lane);
+            const float sc = scl(i, r);
             if (row < g.M)
-              gptr<T>(g.out0)[(long long)row * g.ld0 + f] = from_f<T>(silu(acc[i][j][r]) * acc[i][j + 1][r]);
+              gptr<T>(g.out0)[(long long)row * g.ld0 + f] =
+                  from_f<T>(silu(acc[i][j][r] * sc) * (acc[i][j + 1][r] * sc));
           }
         } else if (cb < g.nsplit2) {
           // rotate-half pair (d, d + hd/2): permuted to columns (cb+cl, cb+32+cl)
@@ -120,10 +351,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
           for (int r = 0; r < 16; ++r) {
             const int row = rb + acc_row(r, lane);
             if (row >= g.M) continue;
-            const float a1 = acc[i][j][r], a2 = acc[i][j + 1][r];
+            const float sc = scl(i, r);
+            const float a1 = acc[i][j][r] * sc, a2 = acc[i][j + 1][r] * sc;
             const long long off = (long long)row * ld + base;
-            dst[off + cl] = from_f<T>(a1 * cs[r].x - a2 * cs[r].y);
-            dst[off + 32 + cl] = from_f<T>(a2 * cs[r].x + a1 * cs[r].y);
+            dst[off + cl] = from_f<T>(rope_lo(a1, a2, cs[r]));
+            dst[off + 32 + cl] = from_f<T>(rope_hi(a1, a2, cs[r]));
           }
         } else {
           gmem<T>* dst = gptr<T>(g.out2);
@@ -132,8 +364,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
             const int row = rb + acc_row(r, lane);
             if (row >= g.M) continue;
             const long long off = (long long)row * g.ld2 + (cb - g.nsplit2);
-            dst[off + cl] = from_f<T>(acc[i][j][r]);
-            if (cb + 32 < g.N) dst[off + 32 + cl] = from_f<T>(acc[i][j + 1][r]);
+            const float sc = scl(i, r);
+            dst[off + cl] = from_f<T>(acc[i][j][r] * sc);
+            if (cb + 32 < g.N) dst[off + 32 + cl] = from_f<T>(acc[i][j + 1][r] * sc);
           }
         }
       }
@@ -146,25 +379,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int rb = rm0 + 32 * i;
-        if constexpr (EPI == EPI_RESID) {
-          gmem<float>* out = gptr<float>(g.out0);
-          float prev[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = min(rb + acc_row(r, lane), g.M - 1);
-            prev[r] = out[(long long)row * g.ld0 + col];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rb + acc_row(r, lane);
-            if (row < g.M) out[(long long)row * g.ld0 + col] = prev[r] + acc[i][j][r];
-          }
-        } else {
+        {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = rb + acc_row(r, lane);
             if (row >= g.M) continue;
-            const float v = acc[i][j][r];
+            float v = acc[i][j][r];
+            if constexpr (EPI == EPI_GATE) v *= scl(i, r);
             if constexpr (EPI == EPI_F32) {
               gptr<float>(g.out0)[(long long)row * g.ld0 + col] = v;
             } else if constexpr (EPI == EPI_PARTIAL) {
@@ -215,7 +436,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
 // ld2, nsplit and nsplit2 multiples of 8); the caller checks.
 template <int EPI, int TM, int TN, int BM, int BN, int NT>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m0, int n0,
-                                                int wr0, int wc0, int lane, char* smem, int smem_bytes) {
+                                                int wr0, int wc0, int lane, char* smem, int smem_bytes,
+                                                const float* rsl) {
   constexpr int PP = BN * 2 + 16;
   const int pitch = BM * PP <= smem_bytes ? PP : BN * 2;   // pad the rows when the stages allow
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
@@ -247,16 +469,16 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = rbl + acc_row(r, lane);
-            const float a1 = acc[i][j][r], a2 = acc[i][j + 1][r];
-            put(rl, cbl + cl, a1 * cs[r].x - a2 * cs[r].y);
-            put(rl, cbl + 32 + cl, a2 * cs[r].x + a1 * cs[r].y);
+            const float a1 = acc[i][j][r] * rsl[rl], a2 = acc[i][j + 1][r] * rsl[rl];
+            put(rl, cbl + cl, rope_lo(a1, a2, cs[r]));
+            put(rl, cbl + 32 + cl, rope_hi(a1, a2, cs[r]));
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = rbl + acc_row(r, lane);
-            put(rl, cbl + cl, acc[i][j][r]);
-            put(rl, cbl + 32 + cl, acc[i][j + 1][r]);
+            put(rl, cbl + cl, acc[i][j][r] * rsl[rl]);
+            put(rl, cbl + 32 + cl, acc[i][j + 1][r] * rsl[rl]);
           }
         }
       }
@@ -275,7 +497,10 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) put(wr0 + 32 * i + acc_row(r, lane), cll, acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) {
+            const int rl = wr0 + 32 * i + acc_row(r, lane);
+            put(rl, cll, acc[i][j][r] * rsl[rl]);
+          }
       } else if (col < g.N) {
         gmem<float>* dst = (g.out2 != nullptr && col >= g.nsplit2) ? gptr<float>(g.out2) + (col - g.nsplit2)
                                                                   : gptr<float>(g.out1) + (col - g.nsplit);
@@ -283,8 +508,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wr0 + 32 * i + acc_row(r, lane);
-            if (row < g.M) dst[(long long)row * g.ld1] = acc[i][j][r];
+            const int rl = wr0 + 32 * i + acc_row(r, lane);
+            if (m0 + rl < g.M) dst[(long long)(m0 + rl) * g.ld1] = acc[i][j][r] * rsl[rl];
           }
       }
     }
@@ -446,13 +671,16 @@ __global__ void __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(BM * BN <= 128 * 128 ? 2 : 1, 2)))
 gemm_kernel(GemmArgs g) {
   typedef GemmShape<T, BM, BN, WM, WN> S;
+  static_assert(BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(16))) char smem[2 * S::STAGE];
+  __shared__ float rsl[scaled_epi(EPI) ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int nbm = (g.M + BM - 1) / BM;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int m0 = (t % nbm) * BM, n0 = (t / nbm) * BN;
+  const float rsv = scaled_epi(EPI) ? row_scale_load<BM>(g, m0) : 1.f;
   const int kb = blockIdx.y * g.k_split;
   TileCtx c;
   c.ke = min(g.K, kb + g.k_split);
@@ -481,7 +709,12 @@ gemm_kernel(GemmArgs g) {
   const int brow = wn * S::WTN + (lane & 31);
   const int khalf = (lane >> 5) * Frag<T>::LANE_K * (int)sizeof(T);
   mainloop<T, S, BM, true>(acc, c, smem, tid, kb, nk, arow, brow, khalf);
-  epilogue<T, EPI, S::TM, S::TN>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
+  if constexpr (scaled_epi(EPI)) row_scale_store<BM>(rsv, rsl);
+  epilogue<T, EPI, S::TM, S::TN>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                 scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
+  if constexpr (EPI == EPI_RESID && sizeof(T) == 2) {
+    if (g.rs_out != nullptr) resid_norm_finish<BM, S::NT, (S::TN & -S::TN)>(g, m0, t % nbm, (g.N + BN - 1) / BN);
+  }
 }
 
 // ------------------------------------------------------- bf16 LDS-DMA kernel
@@ -613,7 +846,9 @@ template <typename S, int EPI>
 __global__ void __launch_bounds__(S::NT)
 __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 gemm_lds_kernel(GemmArgs g) {
+  static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -622,6 +857,7 @@ gemm_lds_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = ke > kb ? (ke - kb) / S::BK : 0;
@@ -723,15 +959,20 @@ gemm_lds_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   if (nk > 0) tile(nk - 1, std::true_type{});
+  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
   if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
     // bf16 q|k|v outputs: only the staged form is compiled here (the host
     // runs unaligned launches on the register-staged kernel); both forms in
     // one kernel cost registers and code in the main loop
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
     epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE);
+                                                            S::NS * S::STAGE, rsl);
   } else {
-    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                        scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
+  }
+  if constexpr (EPI == EPI_RESID) {
+    if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
   }
 }
 
@@ -763,7 +1004,9 @@ struct W4 {
 template <typename S, int EPI>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wide_kernel(GemmArgs g) {
+  static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -772,6 +1015,7 @@ gemm_wide_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = (ke - kb) / S::BK;   // >= 1: the host gives every split a K tile
@@ -855,15 +1099,20 @@ gemm_wide_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   tile(nk - 1, std::true_type{});
+  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
   if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
     // only the staged form, as in the LDS kernels (with both forms compiled
     // in, the gate epilogue spilled registers into the main loop of these
     // 256 x 256 tiles)
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
     epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE);
+                                                            S::NS * S::STAGE, rsl);
   } else {
-    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                        scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
+  }
+  if constexpr (EPI == EPI_RESID) {
+    if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
   }
 }
 
@@ -913,7 +1162,7 @@ struct WD {
 // checks) and the tile's first feature 16-byte aligned.
 template <typename S>
 __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx16 (&acc)[S::TM][S::TN], int m0,
-                                                      int n0, int wave, int lane, char* smem) {
+                                                      int n0, int wave, int lane, char* smem, const float* rsl) {
   constexpr int FT = S::BN / 2;                   // features per tile
   constexpr int PITCH = FT * 2 + 16;              // bytes per staged row
   constexpr int CPR = FT * 2 / 16;                // 16-byte chunks per row
@@ -929,7 +1178,8 @@ __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx1
     for (int i = 0; i < S::TM; ++i) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
+        const float a0 = acc[i][j][2 * k] * rsl[32 * i + acc_row(2 * k, lane)];
+        const float a1 = acc[i][j][2 * k + 1] * rsl[32 * i + acc_row(2 * k + 1, lane)];
         const float got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(gate_lane ? a1 : a0), 0x401F));
         const float gt = gate_lane ? a0 : got, up = gate_lane ? got : a1;
         const int rl = 32 * i + acc_row(2 * k + (gate_lane ? 0 : 1), lane);
@@ -952,7 +1202,9 @@ __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx1
 template <typename S, int EPI>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wd_kernel(GemmArgs g) {
+  static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
+  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -960,6 +1212,7 @@ gemm_wd_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
+  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
   const int nk = g.K / S::BK;   // >= 1: the host requires K to be a positive multiple of 64
 
   const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
@@ -1063,13 +1316,17 @@ gemm_wd_kernel(GemmArgs g) {
     if (kt0 + d < nk) tile(kt0 + d, d);
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
   if constexpr (EPI == EPI_SWIGLU)
-    epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
+    epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem, rsl);
   else if constexpr (EPI == EPI_GATE || EPI == EPI_QKV)
     epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE);
+                                                            S::NS * S::STAGE, rsl);
   else
     epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
+  if constexpr (EPI == EPI_RESID) {
+    if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
+  }
 }
 
 // Fragment-order copy of a bf16 weight W[N, K] (row stride ld): 16-byte
@@ -1134,12 +1391,15 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, lo
 }
 
 // Split-K reduction into a residual row, fused with the RMSNorm of the
-// updated row: one workgroup per row, partial slabs summed in a fixed order.
+// updated row (or its deferred form when w is NULL: the row rounded to T and
+// its 1 / rms to rs): one workgroup per row, partial slabs summed in a fixed
+// order.
 constexpr int RN_MAXV = 16;   // N <= 4 * 256 * RN_MAXV
 template <typename T, int MAXV>
 __global__ void __launch_bounds__(256)
 splitk_resid_norm_kernel(const float* __restrict__ ws, int split, long long stride, float* __restrict__ out,
-                         int N, int ld, const float* __restrict__ w, T* __restrict__ nout, float eps) {
+                         int N, int ld, const float* __restrict__ w, T* __restrict__ nout, float eps,
+                         float* __restrict__ rs) {
   __shared__ float red[4];
   const long long row = blockIdx.x;
   // every load of the row first (partials of up to SPLIT_MAX splits and the
@@ -1175,7 +1435,7 @@ splitk_resid_norm_kernel(const float* __restrict__ ws, int split, long long stri
     ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
   }
   ss = block_sum<4>(ss, red);
-  write_normed_row<T, 256, MAXV>(v, ss, N, eps, w, nout + row * N);
+  write_normed_row<T, 256, MAXV>(v, ss, N, eps, w, nout + row * N, rs ? rs + row : nullptr);
 }
 
 // the smallest row-register count that holds N columns (N <= 4 * 256 * RN_MAXV)
@@ -1185,7 +1445,7 @@ hipError_t launch_splitk_resid_norm(const GemmArgs& a, const float* ws, int spli
 #define S1_RN(V)                                                                                              \
   hipLaunchKernelGGL((splitk_resid_norm_kernel<T, V>), dim3(a.M), dim3(256), 0, s, ws, split, stride,          \
                      reinterpret_cast<float*>(a.out0), a.N, a.ld0, a.norm_w, reinterpret_cast<T*>(a.norm_out),  \
-                     a.norm_eps)
+                     a.norm_eps, a.rs_out)
   if (nv <= 2) S1_RN(2);
   else if (nv <= 3) S1_RN(3);
   else if (nv <= 5) S1_RN(5);
@@ -1363,7 +1623,7 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
     p.split_stride = (long long)a.M * a.N;
     hipError_t e = run_cfg<T, EPI_PARTIAL>(p, split, cfg, s);
     if (e != hipSuccess) return e;
-    if (epi == EPI_RESID && a.norm_w && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV && split <= 4) {
+    if (epi == EPI_RESID && (a.norm_w || a.rs_out) && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV && split <= 4) {
       if (normed) *normed = true;
       return launch_splitk_resid_norm<T>(a, ws, split, p.split_stride, s);
     }
@@ -1379,7 +1639,9 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
   }
   switch (epi) {
     case EPI_F32: return run_cfg<T, EPI_F32>(a, 1, cfg, s);
-    case EPI_RESID: return run_cfg<T, EPI_RESID>(a, 1, cfg, s);
+    case EPI_RESID:
+      if (normed && a.rs_out) *normed = true;   // the deferred norm in the epilogue
+      return run_cfg<T, EPI_RESID>(a, 1, cfg, s);
     case EPI_GATE:
     case EPI_QKV: {
       GemmArgs r = a;
@@ -1461,12 +1723,24 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
 
 int gemm_k_tile(bool bf16) { return bf16 ? 64 : 32; }
 
+// Arguments of the deferred RMSNorm (bf16 only): the row scale on the
+// scaled epilogues; on EPI_RESID the bf16 copy, the scale output and, for
+// the form without a K split, the partial sums (at most 256 slots of 32
+// columns per row, rows a multiple of 32 apart) and the tickets.
+bool deferred_norm_ok(bool bf16, Epi epi, const GemmArgs& a) {
+  if (a.row_scale && (!bf16 || !(epi == EPI_SWIGLU || epi == EPI_GATE || epi == EPI_QKV))) return false;
+  if (a.rs_out == nullptr) return true;
+  return bf16 && epi == EPI_RESID && a.norm_out && a.ss_parts && a.tickets && a.N <= 256 * 32 &&
+         a.ss_ld >= a.M && a.ss_ld % 32 == 0;
+}
+
 int gemm_tile_configs() { return N_CFG; }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws, hipStream_t s,
                        int cfg, bool* normed) {
   if (normed) *normed = false;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (!deferred_norm_ok(bf16, epi, a)) return hipErrorInvalidValue;
   GemmArgs g = a;
   if (split < 1) split = 1;
   if (cfg < 0) auto_plan(bf16, epi, a, ws ? split : 1, cfg, split);
@@ -1523,7 +1797,7 @@ int gemm_wd_tiles(int tile, int M, int N) {
 
 hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_wd_ok(epi, a) || tile < 1 || tile > 2) return hipErrorInvalidValue;
+  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || tile < 1 || tile > 2) return hipErrorInvalidValue;
   return tile == 2 ? run_wd_epi<CfgWD2>(epi, a, s) : run_wd_epi<CfgWD1>(epi, a, s);
 }
 

@@ -78,7 +78,16 @@ struct Model {
 
   // workspace, sized for cfg budgets
   float* x = nullptr;           // residual stream fp32 [T, d]
-  void* xn = nullptr;           // normalised activations [T, d]
+  void* xn = nullptr;           // normalised activations [T, d]; with the deferred norm: x rounded to bf16
+  // Deferred RMSNorm (bf16 models): the pre-norm gains are folded into the
+  // columns of the in-projection and gate/up weights, the GEMMs that update
+  // x write xn = bf16(x) and rstd = 1 / rms of each row, and the consuming
+  // GEMMs scale their accumulator rows by rstd.
+  bool fold = false;
+  float* rstd = nullptr;        // [T]
+  float* ssq = nullptr;         // partial sums of squares [d / 32][ss_ld]
+  int ss_ld = 0;
+  unsigned int* tickets = nullptr;   // one per row block, zero between launches
   void* qkv = nullptr;          // LA: q | k | v; FA: q          [T, ld_qkv]
   int ld_qkv = 0;
   float* lg = nullptr;          // log decay gate fp32 [T, H]

@@ -48,6 +48,22 @@ struct GemmArgs {
   void* norm_out;
   float norm_eps;
   int staged;            // set by launch_gemm: bf16 outputs staged through LDS
+  // EPI_SWIGLU, EPI_GATE, EPI_QKV (bf16): when row_scale is set, the
+  // accumulators of row r are multiplied by row_scale[r] before the epilogue
+  // (the 1 / rms of an RMSNorm whose gain has been folded into W).
+  const float* row_scale;
+  // EPI_RESID (bf16) with rs_out set: the RMSNorm of the updated rows is left
+  // to the next GEMM: norm_out (bf16, row stride N) = the updated row rounded
+  // to bf16 and rs_out[r] = 1 / sqrt(mean(row^2) + norm_eps), norm_w unused.
+  // Without a K split the epilogue writes the rows' sums of squares over
+  // aligned groups of 32 * 2^k columns to ss_parts ([N / 32][ss_ld] floats,
+  // ss_ld a multiple of 32) and the last workgroup to finish a row block (by
+  // `tickets`, one counter per row block, zero between launches) sums them
+  // in a fixed tree order that does not depend on the tile configuration.
+  float* rs_out;
+  float* ss_parts;
+  int ss_ld;
+  unsigned int* tickets;
 };
 
 // Runs the GEMM.  tile_cfg >= 0 picks a tile configuration (0 .. 
@@ -56,7 +72,8 @@ struct GemmArgs {
 // the largest K split allowed (1 without a workspace).  With split > 1
 // (EPI_F32 or EPI_RESID only) partial tiles go to `ws` (split * M * N
 // floats) and a reduction kernel applies the epilogue in a fixed order.
-// `normed` (optional) reports whether the fused RMSNorm ran.
+// `normed` (optional) reports whether the fused RMSNorm (or, with rs_out, its
+// deferred form) ran.
 constexpr int GEMM_AUTO = -1;
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
                        hipStream_t s, int tile_cfg = GEMM_AUTO, bool* normed = nullptr);
@@ -91,18 +108,22 @@ hipError_t launch_stream_read(const void* src, long long bytes, void* sink, hipS
 // ------------------------------------------------------------ elementwise
 hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
                         hipStream_t s);
+// out = RMSNorm(x) * w.  With w == NULL and rs set (the deferred form): out
+// = x rounded to the element type and rs[t] = 1 / sqrt(mean(x[t]^2) + eps).
 hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
-                          float eps, hipStream_t s);
+                          float eps, hipStream_t s, float* rs = nullptr);
 // x = E[ids] (fp32) and xn = RMSNorm(x) * w (elem), T rows of width d
-// (d % 4 == 0, d <= 16384; else hipErrorInvalidValue).
+// (d % 4 == 0, d <= 16384; else hipErrorInvalidValue); w == NULL with rs:
+// the deferred form as launch_rmsnorm.
 hipError_t launch_embed_norm(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
-                             const float* w, void* xn, float eps, hipStream_t s);
-// out[dst_row(o)] = W[o] + scale * B[o] A ; row_map may be NULL (identity);
-// dst rows are out_ld elements apart.  W, A, B may be fp32 or bf16 (same as
-// out); A == NULL means no adapter.
+                             const float* w, void* xn, float eps, hipStream_t s, float* rs = nullptr);
+// out[dst_row(o)] = (W[o] + scale * B[o] A) * gain ; row_map may be NULL
+// (identity); gain (fp32 [in_dim], an RMSNorm gain folded into the columns)
+// may be NULL.  W, A, B may be fp32 or bf16 (same as out); A == NULL means
+// no adapter.  fp32 arithmetic, one rounding.
 hipError_t launch_merge(bool bf16, const void* W, const void* A, const void* B, void* out,
                         int out_dim, int in_dim, int rank, float scale, const int* row_map,
-                        hipStream_t s);
+                        hipStream_t s, const float* gain = nullptr);
 hipError_t launch_to_f32(bool bf16, const void* in, float* out, long long n, hipStream_t s);
 hipError_t launch_rope_table(float2* table, int max_pos, int head_dim, double base,
                              hipStream_t s);

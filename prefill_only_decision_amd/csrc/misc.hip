@@ -33,11 +33,13 @@ __global__ void embed_kernel(const int32_t* __restrict__ ids, const T* __restric
 // -------------------------------------------------------------- rmsnorm
 // out = x / sqrt(mean(x^2) + eps) * w, one workgroup of 256 threads per row;
 // the row stays in registers between the sum of squares and the scaling
-// (d <= 4 * 256 * RMS_MAXV).
+// (d <= 4 * 256 * RMS_MAXV).  w == NULL: the deferred form (out = x rounded,
+// rs[row] = 1 / sqrt(mean(x^2) + eps)).
 constexpr int RMS_MAXV = 16;
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                                                      T* __restrict__ out, int d, float eps) {
+                                                      T* __restrict__ out, int d, float eps,
+                                                      float* __restrict__ rs) {
   __shared__ float red[4];
   const long long row = blockIdx.x;
   const float* xr = x + row * d;
@@ -51,17 +53,17 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   ss = block_sum<4>(ss, red);
-  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, out + row * d);
+  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, out + row * d, rs ? rs + row : nullptr);
 }
 
 // Embedding gather fused with the first layer's input RMSNorm: x[t] =
 // E[ids[t]] (fp32) and xn[t] = RMSNorm(x[t]) * w, one workgroup of 256
 // threads per row, the row in registers (the same arithmetic as
-// rmsnorm_kernel on the gathered row).
+// rmsnorm_kernel on the gathered row, the deferred form when w == NULL).
 template <typename T>
 __global__ void __launch_bounds__(256) embed_norm_kernel(const int32_t* __restrict__ ids, const T* __restrict__ E,
                                                          float* __restrict__ x, int d, const float* __restrict__ w,
-                                                         T* __restrict__ xn, float eps) {
+                                                         T* __restrict__ xn, float eps, float* __restrict__ rs) {
   __shared__ float red[4];
   const long long row = blockIdx.x;
   const T* src = E + (long long)ids[row] * d;
@@ -83,15 +85,16 @@ __global__ void __launch_bounds__(256) embed_norm_kernel(const int32_t* __restri
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   ss = block_sum<4>(ss, red);
-  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, xn + row * d);
+  write_normed_row<T, 256, RMS_MAXV>(v, ss, d, eps, w, xn + row * d, rs ? rs + row : nullptr);
 }
 
 // ---------------------------------------------------------------- merge
-// out[map(o)] = W[o] + scale * (B[o] . A[:, i]); fp32 arithmetic, one rounding.
+// out[map(o)] = (W[o] + scale * (B[o] . A[:, i])) * gain[i] (gain optional);
+// fp32 arithmetic, one rounding.
 template <typename T>
 __global__ void merge_kernel(const T* __restrict__ W, const T* __restrict__ A,
                              const T* __restrict__ B, T* __restrict__ out, int in_dim, int rank,
-                             float scale, const int* __restrict__ row_map) {
+                             float scale, const int* __restrict__ row_map, const float* __restrict__ gain) {
   __shared__ float sb[64];
   const int o = blockIdx.x;
   if (A != nullptr && threadIdx.x < rank) sb[threadIdx.x] = to_f<T>(B[(long long)o * rank + threadIdx.x]);
@@ -106,6 +109,7 @@ __global__ void merge_kernel(const T* __restrict__ W, const T* __restrict__ A,
       for (int j = 0; j < rank; ++j) ba = fmaf(sb[j], to_f<T>(A[(long long)j * in_dim + i]), ba);
       v += scale * ba;
     }
+    if (gain != nullptr) v *= gain[i];
     orow[i] = from_f<T>(v);
   }
 }
@@ -270,34 +274,34 @@ hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, 
 }
 
 hipError_t launch_embed_norm(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
-                            const float* w, void* xn, float eps, hipStream_t s) {
+                            const float* w, void* xn, float eps, hipStream_t s, float* rs) {
   if (T <= 0) return hipSuccess;
-  if (d % 4 || d > 4 * 256 * RMS_MAXV) return hipErrorInvalidValue;
+  if (d % 4 || d > 4 * 256 * RMS_MAXV || (w == nullptr && rs == nullptr)) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(embed_norm_kernel<bf16_t>, dim3(T), dim3(256), 0, s, ids,
-                       reinterpret_cast<const bf16_t*>(E), x, d, w, reinterpret_cast<bf16_t*>(xn), eps);
+                       reinterpret_cast<const bf16_t*>(E), x, d, w, reinterpret_cast<bf16_t*>(xn), eps, rs);
   else
     hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(T), dim3(256), 0, s, ids,
-                       reinterpret_cast<const float*>(E), x, d, w, reinterpret_cast<float*>(xn), eps);
+                       reinterpret_cast<const float*>(E), x, d, w, reinterpret_cast<float*>(xn), eps, rs);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
-                          float eps, hipStream_t s) {
+                          float eps, hipStream_t s, float* rs) {
   if (T <= 0) return hipSuccess;
-  if (d % 4 || d > 4 * 256 * RMS_MAXV) return hipErrorInvalidValue;
+  if (d % 4 || d > 4 * 256 * RMS_MAXV || (w == nullptr && rs == nullptr)) return hipErrorInvalidValue;
   if (bf16)
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(T), dim3(256), 0, s, x, w,
-                       reinterpret_cast<bf16_t*>(out), d, eps);
+                       reinterpret_cast<bf16_t*>(out), d, eps, rs);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(T), dim3(256), 0, s, x, w,
-                       reinterpret_cast<float*>(out), d, eps);
+                       reinterpret_cast<float*>(out), d, eps, rs);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(bool bf16, const void* W, const void* A, const void* B, void* out,
                         int out_dim, int in_dim, int rank, float scale, const int* row_map,
-                        hipStream_t s) {
+                        hipStream_t s, const float* gain) {
   if (out_dim <= 0 || in_dim <= 0) return hipSuccess;
   if (A != nullptr && (rank <= 0 || rank > 64)) return hipErrorInvalidValue;
   const dim3 grid(out_dim, std::max(1, std::min(8, (in_dim + 1023) / 1024)));
@@ -305,12 +309,12 @@ hipError_t launch_merge(bool bf16, const void* W, const void* A, const void* B, 
     hipLaunchKernelGGL(merge_kernel<bf16_t>, grid, dim3(256), 0, s,
                        reinterpret_cast<const bf16_t*>(W), reinterpret_cast<const bf16_t*>(A),
                        reinterpret_cast<const bf16_t*>(B), reinterpret_cast<bf16_t*>(out), in_dim,
-                       rank, scale, row_map);
+                       rank, scale, row_map, gain);
   else
     hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s,
                        reinterpret_cast<const float*>(W), reinterpret_cast<const float*>(A),
                        reinterpret_cast<const float*>(B), reinterpret_cast<float*>(out), in_dim,
-                       rank, scale, row_map);
+                       rank, scale, row_map, gain);
   return hipGetLastError();
 }
 
