@@ -58,18 +58,22 @@ int s1k_gemm_noalloc(int32_t dtype, const void* A, const void* W, float* C, int3
  * (pre-norm blocks of the Qwen3.5-family backbone the System1-Omni README
  * names; RFC #114 section 3, RMSNorm before each mixer and FFN), bf16:
  * x[M,N] (fp32, in/out, device) += A[M,K] W[N,K]^T (A, W bf16, device);
- * hb[M,N] (bf16, device) = the updated x rounded to bf16; rs[M] (fp32,
- * device) = 1 / sqrt(mean(x_row^2) + eps).  The projection that consumes the
- * norm multiplies its accumulator rows by rs, the norm gain being folded
- * into its weight columns, so that no separate norm pass reads the rows.
- * tile_cfg: -1 (chosen by shape) or as s1k_gemm_cfg; split_k >= 1 K splits
- * (as s1k_gemm_cfg; K % 64 == 0 and N % 4 == 0 when split_k > 1).  Without
- * a K split a row's sum of squares is taken in one fixed order whatever
- * tile_cfg and M, so rs is bitwise the same for a row in any launch.
- * N <= 8192, K % 8 == 0.  Allocates its workspace per call.  S1_EINVAL on
- * other arguments. */
+ * rs[M] (fp32, device) = 1 / sqrt(mean(x_row^2) + eps); hb[M,N] (bf16,
+ * device) = the updated x rounded to bf16 (*form = 2, the launch ran without
+ * a K split: the projection that consumes the norm multiplies its
+ * accumulator rows by rs) or x * rs rounded to bf16 (*form = 1, a K split's
+ * reduction, which holds whole rows).  Either way the norm gain is folded
+ * into the consuming weight columns, so that no separate norm pass reads the
+ * rows.  form: host int, may be NULL.
+ * tile_cfg: -1 (configuration and split chosen by shape, at most split_k) or
+ * as s1k_gemm_cfg (exactly split_k K splits, K % 64 == 0 and N % 4 == 0 when
+ * split_k > 1).  Without a K split a row's sum of squares is taken in one
+ * fixed order whatever tile_cfg and M, so rs is bitwise the same for a row
+ * in any such launch.  N <= 8192, K % 8 == 0.  Allocates its workspace per
+ * call.  S1_EINVAL on other arguments. */
 int s1k_gemm_resid_norm(const void* A, const void* W, float* x, int32_t M, int32_t N, int32_t K,
-                        int32_t split_k, int32_t tile_cfg, float eps, void* hb, float* rs, void* hip_stream);
+                        int32_t split_k, int32_t tile_cfg, float eps, void* hb, float* rs, int32_t* form,
+                        void* hip_stream);
 
 /* Number of GEMM tile configurations (host-only, no device work). */
 int s1k_gemm_tile_configs(void);

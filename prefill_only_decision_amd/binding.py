@@ -131,7 +131,7 @@ def load_library(path=LIB_PATH):
         "s1k_gemm": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
         "s1k_gemm_cfg": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "s1k_gemm_noalloc": (C.c_int, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
-        "s1k_gemm_resid_norm": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
+        "s1k_gemm_resid_norm": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp]),
         "s1k_gemm_tile_configs": (C.c_int, []),
         "s1k_frag_bytes": (i64, [i32, i32]),
         "s1k_mfma_peak": (C.c_int, [vp, i32, i32, vp, vp]),
@@ -450,8 +450,11 @@ def gemm_cfg(dtype, A, W, Cout, M, N, K, split_k, cfg, stream=None):
 
 
 def gemm_resid_norm(A, W, x, M, N, K, split_k, cfg, eps, hb, rs, stream=None):
-    return _k("s1k_gemm_resid_norm", C.c_void_p(A), C.c_void_p(W), C.c_void_p(x), M, N, K, split_k, cfg,
-              C.c_float(eps), C.c_void_p(hb), C.c_void_p(rs), _stream(stream))
+    """Returns the form of hb: 1 = x * rs (a K split ran), 2 = x itself."""
+    form = C.c_int32(0)
+    _k("s1k_gemm_resid_norm", C.c_void_p(A), C.c_void_p(W), C.c_void_p(x), M, N, K, split_k, cfg,
+       C.c_float(eps), C.c_void_p(hb), C.c_void_p(rs), C.byref(form), _stream(stream))
+    return form.value
 
 
 def gemm_tile_configs():

@@ -499,7 +499,8 @@ int s1k_gemm_cfg(int32_t dtype, const void* A, const void* W, float* C, int32_t 
 }
 
 int s1k_gemm_resid_norm(const void* A, const void* W, float* x, int32_t M, int32_t N, int32_t K,
-                        int32_t split_k, int32_t tile_cfg, float eps, void* hb, float* rs, void* hip_stream) {
+                        int32_t split_k, int32_t tile_cfg, float eps, void* hb, float* rs, int32_t* form,
+                        void* hip_stream) {
   if (M < 0 || N < 1 || N > 8192 || K < 8 || K % 8 || split_k < 1 || (split_k > 1 && (N % 4 || K % 64)) || !A ||
       !W || !x || !hb || !rs || tile_cfg < GEMM_AUTO || tile_cfg >= gemm_tile_configs())
     return set_error(S1_EINVAL, "s1k_gemm_resid_norm: unsupported arguments");
@@ -530,10 +531,11 @@ int s1k_gemm_resid_norm(const void* A, const void* W, float* x, int32_t M, int32
   g.tickets = reinterpret_cast<unsigned*>(ws + parts);
   float* sws = split_k > 1 ? reinterpret_cast<float*>(ws + parts + nt * sizeof(unsigned)) : nullptr;
   hipError_t e = hipMemsetAsync(g.tickets, 0, nt * sizeof(unsigned), s);
-  bool normed = false;
+  int normed = NORM_NONE;
   if (e == hipSuccess) e = launch_gemm(true, EPI_RESID, g, split_k, sws, s, tile_cfg, &normed);
   (void)hipFreeAsync(ws, s);
-  if (e == hipSuccess && !normed) return set_error(S1_EINVAL, "s1k_gemm_resid_norm: shape not supported");
+  if (e == hipSuccess && normed == NORM_NONE) return set_error(S1_EINVAL, "s1k_gemm_resid_norm: shape not supported");
+  if (e == hipSuccess && form) *form = normed;
   return dev_status(e, "s1k_gemm_resid_norm");
 }
 

@@ -121,8 +121,8 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // RMSNorm of one row held as float4 pieces v[k] (columns 4 (k * NT + tid)
 // ...): out = v * r * w with r = 1 / sqrt(ss / d + eps), ss the row's sum of
-// squares.  Deferred form (w == NULL): out = v rounded to T and *rs = r, the
-// scale the next GEMM applies to its accumulators (the gain is in its W).
+// squares.  With w == NULL (the gain folded into the next GEMM's weights):
+// out = v * r and *rs = r.
 template <typename T, int NT, int MAXV>
 __device__ __forceinline__ void write_normed_row(const float4 (&v)[MAXV], float ss, int d, float eps,
                                                  const float* __restrict__ w, T* __restrict__ o,
@@ -137,11 +137,11 @@ __device__ __forceinline__ void write_normed_row(const float4 (&v)[MAXV], float 
       const float4 x = v[k];
       if constexpr (sizeof(T) == 2) {
         uint2 u;
-        u.x = pack_bf2(x.x, x.y);
-        u.y = pack_bf2(x.z, x.w);
+        u.x = pack_bf2(x.x * r, x.y * r);
+        u.y = pack_bf2(x.z * r, x.w * r);
         *reinterpret_cast<uint2*>(o + c) = u;
       } else {
-        *reinterpret_cast<float4*>(o + c) = x;
+        *reinterpret_cast<float4*>(o + c) = make_float4(x.x * r, x.y * r, x.z * r, x.w * r);
       }
     }
     return;

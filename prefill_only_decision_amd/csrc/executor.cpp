@@ -1008,8 +1008,12 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
   char* att = static_cast<char*>(m->att);
   const long long kvld = (long long)Hkv * hd;
   bool xn_ready = xn_first;   // xn already holds this layer's normalised input
-  // the deferred norm: the consumers' row scales, and what a residual GEMM
-  // needs to produce them
+  // the deferred norm (gains folded into the consuming weights): xn holds
+  // either the normalised rows without the gain (from a kernel that had
+  // whole rows: the embedding gather, a K split's reduction, a norm pass) or,
+  // after a residual GEMM without a K split, the rows themselves, which the
+  // consuming GEMM scales by rstd (xn_scaled)
+  bool xn_scaled = false;
   float* rstd = m->fold ? m->rstd + r0 : nullptr;
   auto defer_norm = [&](GemmArgs& a) {
     a.rs_out = rstd;
@@ -1031,10 +1035,11 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     if (!xn_ready) {
       S1_TRY(norm_pass(L.attn_norm), "rmsnorm");
       MARK(KC_RMSNORM);
+      xn_scaled = false;
     }
     GemmArgs g{};
     g.A = xn;
-    g.row_scale = rstd;
+    g.row_scale = xn_scaled ? rstd : nullptr;
     g.M = T;
     g.K = d;
     g.lda = d;
@@ -1127,17 +1132,17 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     go.norm_out = xn;
     go.norm_eps = c.rms_eps;
     if (m->fold) defer_norm(go);
-    bool normed = false;
+    int normed = NORM_NONE;
     S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &normed),
            "mixer out-projection");
     MARK(KC_GEMM_O);
-    if (!normed) {
+    if (normed == NORM_NONE) {
       S1_TRY(norm_pass(L.ffn_norm), "rmsnorm");
       MARK(KC_RMSNORM);
     }
     GemmArgs gu{};
     gu.A = xn;
-    gu.row_scale = rstd;
+    gu.row_scale = normed == NORM_DEFERRED ? rstd : nullptr;
     gu.lda = d;
     gu.W = L.w_gu;
     gu.ldw = d;
@@ -1175,10 +1180,13 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     if (residual_direct(m, L.w_down_frag, T, max_split(m, p, T))) {
       gd.W = L.w_down_frag;
       S1_TRY(launch_gemm_wd(EPI_RESID, gd, 2, s), "FFN down");
-      xn_ready = gd.rs_out != nullptr;
+      xn_ready = xn_scaled = gd.rs_out != nullptr;   // without a K split: the rows and their scales
     } else {
-      S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &xn_ready),
+      int nd = NORM_NONE;
+      S1_TRY(launch_gemm(m->bf16, EPI_RESID, gd, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &nd),
              "FFN down");
+      xn_ready = nd != NORM_NONE;
+      xn_scaled = nd == NORM_DEFERRED;
     }
     MARK(KC_GEMM_DOWN);
     if (ps.n_cap) {

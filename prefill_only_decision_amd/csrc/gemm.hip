@@ -19,8 +19,8 @@
 // rows are permuted at load so that the partner column sits exactly 32
 // columns later, i.e. in the neighbouring MFMA tile at the same register.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
-#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -140,57 +140,109 @@ __device__ __forceinline__ float tree_sum(float (&v)[N]) {
 // ss_parts[(cn0 / 32 / TG + group) * ss_ld + row].  Each 32 x 32 tile's
 // squares are summed while its values are in registers; no lane skips the
 // exchanges (columns past N count as zero).
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): the
-// accumulator indices stay compile-time constants however large the body
-// (a loop the unroller declines to unroll indexes the accumulators at run
-// time and moves them to scratch memory).
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-  }(std::make_integer_sequence<int, N>{});
+// Sums over the 32 columns of each half-wave for TN tiles at once, one
+// exchange level for all tiles before the next (independent chains
+// interleave); the same reduce-scatter as half_wave_row_sum.
+template <int TN>
+__device__ __forceinline__ void half_wave_row_sums(float (&v)[TN][16], float (&out)[TN], int lane) {
+  const bool b16 = lane & 16, b8 = lane & 8, b4 = lane & 4, b2 = lane & 2;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float keep = b16 ? v[j][k + 8] : v[j][k], send = b16 ? v[j][k] : v[j][k + 8];
+      v[j][k] = keep + swz_xor<16>(send);
+    }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float keep = b8 ? v[j][k + 4] : v[j][k], send = b8 ? v[j][k] : v[j][k + 4];
+      v[j][k] = keep + swz_xor<8>(send);
+    }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float keep = b4 ? v[j][k + 2] : v[j][k], send = b4 ? v[j][k] : v[j][k + 2];
+      v[j][k] = keep + swz_xor<4>(send);
+    }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const float keep = b2 ? v[j][1] : v[j][0], send = b2 ? v[j][0] : v[j][1];
+    v[j][0] = keep + swz_xor<2>(send);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) out[j] = v[j][0] + swz_xor<1>(v[j][0]);
 }
 
+// Residual epilogue: out0 (fp32) += the tile.  The rows are addressed
+// through a buffer resource over rows rm0 .. M - 1: loads past the end read
+// zero and stores past it are dropped, so no access is predicated and a row
+// block's loads (all its column tiles) are issued together before its stores.
+// With the deferred norm (bf16, rs_out set) it also writes the updated rows
+// rounded to bf16 (staged in LDS when `stage` is given) and, per row and
+// aligned group of TG = 2^k column blocks (TG the largest power of two
+// dividing TN), the partial sum of squares, to ss_parts[(cn0 / 32 / TG +
+// group) * ss_ld + row]; columns past N count as zero.
 template <typename T, int TM, int TN>
 __device__ __forceinline__ void epilogue_resid(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0, int cn0,
-                                               int lane) {
+                                               int lane, char* stage = nullptr, int pitch = 0, int wr0 = 0,
+                                               int wc0 = 0) {
   constexpr int TG = TN & -TN;
   const int cl = lane & 31;
   bool defer = false;
   if constexpr (sizeof(T) == 2) defer = g.rs_out != nullptr;
-  gmem<float>* out = gptr<float>(g.out0);
-  static_for<TM>([&](auto ic) {
-    constexpr int i = decltype(ic)::value;
+  const int nrow = max(0, g.M - rm0);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<float*>(g.out0) + (long long)rm0 * g.ld0, (short)0, nrow * g.ld0 * 4, 0x00020000);
+  // byte offsets: this lane's row and column parts (a column past N is sent
+  // out of range)
+  const int lrow = 4 * (lane >> 5) * g.ld0 * 4;
+  int coff[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) coff[j] = cn0 + 32 * j + cl < g.N ? lrow + (cn0 + 32 * j + cl) * 4 : INT_MIN;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
     const int rb = rm0 + 32 * i;
-    float part[TN];
-    static_for<TN>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const int col = cn0 + 32 * j + cl;
-      const bool cok = col < g.N;
-      float v[16];
+    float v[TN][16];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        v[j][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rx, coff[j] + (32 * i + 8 * (r >> 2) + (r & 3)) * g.ld0 * 4, 0, 0));
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = min(rb + acc_row(r, lane), g.M - 1);
-        v[r] = cok ? out[(long long)row * g.ld0 + col] : 0.f;
+        v[j][r] += acc[i][j][r];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j][r]), rx,
+                                              coff[j] + (32 * i + 8 * (r >> 2) + (r & 3)) * g.ld0 * 4, 0, 0);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb + acc_row(r, lane);
-        v[r] += acc[i][j][r];
-        if (cok && row < g.M) out[(long long)row * g.ld0 + col] = v[r];
-      }
-      if (defer) {
-        gmem<bf16_t>* hb = gptr<bf16_t>(g.norm_out);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rb + acc_row(r, lane);
-          if (cok && row < g.M) hb[(long long)row * g.N + col] = f2bf(v[r]);
-          v[r] = cok ? __fmul_rn(v[r], v[r]) : 0.f;
-        }
-        part[j] = half_wave_row_sum(v, lane);
-      }
-    });
     if (defer) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cn0 + 32 * j + cl;
+        const bool cok = col < g.N;
+        if (stage != nullptr) {   // the bf16 copy staged for whole-row 16-byte stores
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<bf16_t*>(stage + (wr0 + 32 * i + acc_row(r, lane)) * pitch +
+                                       2 * (wc0 + 32 * j + cl)) = f2bf(v[j][r]);
+        } else {
+          gmem<bf16_t>* hb = gptr<bf16_t>(g.norm_out);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, lane);
+            if (cok && row < g.M) hb[(long long)row * g.N + col] = f2bf(v[j][r]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[j][r] = cok ? __fmul_rn(v[j][r], v[j][r]) : 0.f;
+      }
+      float part[TN];
+      half_wave_row_sums<TN>(v, part, lane);
       const int row = rb + acc_row((lane >> 1) & 15, lane);
 #pragma unroll
       for (int q = 0; q < TN / TG; ++q) {
@@ -206,7 +258,7 @@ __device__ __forceinline__ void epilogue_resid(const GemmArgs& g, floatx16 (&acc
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  });
+  }
 }
 
 // After the epilogue of a residual tile with the deferred norm: the last
@@ -274,20 +326,57 @@ __device__ __forceinline__ void resid_norm_finish(const GemmArgs& g, int m0, int
   }
 }
 
+// The residual epilogue of a BM x BN workgroup tile whose operand stages
+// (smem_bytes) are free: with the deferred norm the bf16 copy of the updated
+// rows goes through LDS and out as 16-byte chunks of whole rows (written
+// from the accumulators every store would be 2 bytes per lane, half a cache
+// line of two rows per wave store).  Every thread calls this.
+template <int TM, int TN, int BM, int BN, int NT>
+__device__ __forceinline__ void epilogue_resid_tile(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m0, int n0,
+                                                    int wr0, int wc0, int lane, char* smem, int smem_bytes) {
+  constexpr int PP = BN * 2 + 16;
+  const int pitch = BM * PP <= smem_bytes ? PP : BN * 2;
+  const bool stage = g.rs_out != nullptr && g.N % 8 == 0 && BM * BN * 2 <= smem_bytes;
+  if (stage) {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): no operand DMA still lands in the stages
+    __syncthreads();                      // every wave is done reading the stages
+  }
+  epilogue_resid<bf16_t, TM, TN>(g, acc, m0 + wr0, n0 + wc0, lane, stage ? smem : nullptr, pitch, wr0, wc0);
+  if (!stage) return;
+  __syncthreads();
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int CPR = BN / 8;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < BM * CPR; c += NT) {
+    const int rl = c / CPR, ch = c % CPR;
+    const int row = m0 + rl, col = n0 + ch * 8;
+    if (row >= g.M || col >= g.N) continue;
+    *reinterpret_cast<gmem<u32x4v>*>(gptr<bf16_t>(g.norm_out) + (long long)row * g.N + col) =
+        *reinterpret_cast<const u32x4v*>(smem + rl * pitch + ch * 16);
+  }
+}
+
 // Consumer side: the scale of row m0 + tid (tid < BM; 1 without row_scale),
 // loaded at kernel entry so that its latency hides under the operand loads,
 // stored to LDS after the main loop; the epilogues multiply each accumulator
 // by its row's scale where they read it (a separate pass over the
 // accumulators costs the largest tiles registers).
+// The load is issued whether or not there is a row scale (from the operand A
+// when there is none, always in range: M rows of at least two bf16): a load
+// on one path only leaves the compiler's wait counting at the main loop's
+// head imprecise, and it then waits more inside the loop.
 template <int BM>
 __device__ __forceinline__ float row_scale_load(const GemmArgs& g, int m0) {
-  if (g.row_scale == nullptr) return 1.f;
-  return gptr<float>(g.row_scale)[min(m0 + min((int)threadIdx.x, BM - 1), g.M - 1)];
+  const bool has = g.row_scale != nullptr;
+  const float* p = has ? g.row_scale : static_cast<const float*>(g.A);
+  const float v = gptr<float>(p)[min(m0 + min((int)threadIdx.x, BM - 1), g.M - 1)];
+  return has ? v : 1.f;
 }
 template <int BM>
-__device__ __forceinline__ void row_scale_store(float rsv, float* rsl) {
+__device__ __forceinline__ const float* row_scale_store(float rsv, float* rsl) {
   if (threadIdx.x < BM) rsl[threadIdx.x] = rsv;
   __syncthreads();
+  return rsl;
 }
 constexpr bool scaled_epi(int epi) { return epi == EPI_SWIGLU || epi == EPI_GATE || epi == EPI_QKV; }
 
@@ -295,12 +384,13 @@ constexpr bool scaled_epi(int epi) { return epi == EPI_SWIGLU || epi == EPI_GATE
 // for a whole 32-row MFMA tile before its stores: a store to the output may
 // alias a later load as far as the compiler knows, so element-by-element
 // read-modify-write would wait for the memory latency once per element.
-template <typename T, int EPI, int TM, int TN>
+template <typename T, int EPI, int TM, int TN, bool RS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][TN], int rm0,
                                          int cn0, int lane, int split_idx, const float* rsw = nullptr) {
   const int cl = lane & 31;
-  // row scale of accumulator r of MFMA row block i (rsw: LDS, the wave's first row)
-  auto scl = [&](int i, int r) { return rsw != nullptr ? rsw[32 * i + acc_row(r, lane)] : 1.f; };
+  // RS: the row scale of accumulator r of MFMA row block i (rsw: LDS, the
+  // wave's first row); without it the factor is the constant 1 and folds away
+  auto scl = [&](int i, int r) { return RS ? rsw[32 * i + acc_row(r, lane)] : 1.f; };
   if constexpr (EPI == EPI_RESID) {
     epilogue_resid<T, TM, TN>(g, acc, rm0, cn0, lane);
   } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
@@ -434,10 +524,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, floatx16 (&acc)[TM][
 // on MI355X).  The fp32 decay-gate columns (and write strengths) still go
 // straight from the lanes.  Needs 16-byte aligned destinations (ld0, ld1,
 // ld2, nsplit and nsplit2 multiples of 8); the caller checks.
-template <int EPI, int TM, int TN, int BM, int BN, int NT>
+template <int EPI, int TM, int TN, int BM, int BN, int NT, bool RS = false>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&acc)[TM][TN], int m0, int n0,
                                                 int wr0, int wc0, int lane, char* smem, int smem_bytes,
-                                                const float* rsl) {
+                                                const float* rsl = nullptr) {
   constexpr int PP = BN * 2 + 16;
   const int pitch = BM * PP <= smem_bytes ? PP : BN * 2;   // pad the rows when the stages allow
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
@@ -447,6 +537,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
   auto put = [&](int rl, int cll, float v) {
     *reinterpret_cast<bf16_t*>(smem + rl * pitch + 2 * cll) = f2bf(v);
   };
+  // RS: the row scale of tile-local row rl (LDS); otherwise the constant 1
+  auto scl = [&](int rl) { return RS ? rsl[rl] : 1.f; };
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
@@ -469,7 +561,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = rbl + acc_row(r, lane);
-            const float a1 = acc[i][j][r] * rsl[rl], a2 = acc[i][j + 1][r] * rsl[rl];
+            const float sc = scl(rl);
+            const float a1 = acc[i][j][r] * sc, a2 = acc[i][j + 1][r] * sc;
             put(rl, cbl + cl, rope_lo(a1, a2, cs[r]));
             put(rl, cbl + 32 + cl, rope_hi(a1, a2, cs[r]));
           }
@@ -477,8 +570,9 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = rbl + acc_row(r, lane);
-            put(rl, cbl + cl, acc[i][j][r] * rsl[rl]);
-            put(rl, cbl + 32 + cl, acc[i][j + 1][r] * rsl[rl]);
+            const float sc = scl(rl);
+            put(rl, cbl + cl, acc[i][j][r] * sc);
+            put(rl, cbl + 32 + cl, acc[i][j + 1][r] * sc);
           }
         }
       }
@@ -499,7 +593,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int rl = wr0 + 32 * i + acc_row(r, lane);
-            put(rl, cll, acc[i][j][r] * rsl[rl]);
+            put(rl, cll, acc[i][j][r] * scl(rl));
           }
       } else if (col < g.N) {
         gmem<float>* dst = (g.out2 != nullptr && col >= g.nsplit2) ? gptr<float>(g.out2) + (col - g.nsplit2)
@@ -508,8 +602,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& g, floatx16 (&ac
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int rl = wr0 + 32 * i + acc_row(r, lane);
-            if (m0 + rl < g.M) dst[(long long)(m0 + rl) * g.ld1] = acc[i][j][r] * rsl[rl];
+            const int row = m0 + wr0 + 32 * i + acc_row(r, lane);
+            if (row < g.M) dst[(long long)row * g.ld1] = acc[i][j][r] * scl(row - m0);
           }
       }
     }
@@ -666,21 +760,21 @@ __device__ __forceinline__ void mainloop(floatx16 (&acc)[S::TM][S::TN], const Ti
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, int EPI, bool RS = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(BM * BN <= 128 * 128 ? 2 : 1, 2)))
 gemm_kernel(GemmArgs g) {
   typedef GemmShape<T, BM, BN, WM, WN> S;
   static_assert(BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(16))) char smem[2 * S::STAGE];
-  __shared__ float rsl[scaled_epi(EPI) ? BM : 1];
+  __shared__ float rsl[RS ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int nbm = (g.M + BM - 1) / BM;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int m0 = (t % nbm) * BM, n0 = (t / nbm) * BN;
-  const float rsv = scaled_epi(EPI) ? row_scale_load<BM>(g, m0) : 1.f;
+  const float rsv = RS ? row_scale_load<BM>(g, m0) : 1.f;
   const int kb = blockIdx.y * g.k_split;
   TileCtx c;
   c.ke = min(g.K, kb + g.k_split);
@@ -709,9 +803,11 @@ gemm_kernel(GemmArgs g) {
   const int brow = wn * S::WTN + (lane & 31);
   const int khalf = (lane >> 5) * Frag<T>::LANE_K * (int)sizeof(T);
   mainloop<T, S, BM, true>(acc, c, smem, tid, kb, nk, arow, brow, khalf);
-  if constexpr (scaled_epi(EPI)) row_scale_store<BM>(rsv, rsl);
-  epilogue<T, EPI, S::TM, S::TN>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
-                                 scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
+  if constexpr (RS)
+    epilogue<T, EPI, S::TM, S::TN, true>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                         row_scale_store<BM>(rsv, rsl) + wm * S::WTM);
+  else
+    epilogue<T, EPI, S::TM, S::TN>(g, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   if constexpr (EPI == EPI_RESID && sizeof(T) == 2) {
     if (g.rs_out != nullptr) resid_norm_finish<BM, S::NT, (S::TN & -S::TN)>(g, m0, t % nbm, (g.N + BN - 1) / BN);
   }
@@ -781,6 +877,34 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
 
+// As dma16, 4 bytes per lane (lane l's at lds + 4 l).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(int32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The row scales of rows m0 .. m0 + BM - 1 (BM a multiple of 64) into LDS by
+// LDS-DMA at kernel entry, ahead of the operand loads: no register is held
+// through the main loop for them.  Waves 0 .. BM / 64 - 1 load 64 rows each;
+// rows past M read zero.  row_scale_sync, after the main loop, waits for the
+// wave's own DMA and meets the other waves.
+template <int BM>
+__device__ __forceinline__ void row_scale_dma(const GemmArgs& g, int m0, const float* rsl, int wave, int lane) {
+  static_assert(BM % 64 == 0, "whole waves of rows");
+  if (g.row_scale == nullptr || wave * 64 >= BM) return;
+  const int32x4 r = buffer_rsrc(g.row_scale + m0, (g.M - m0) * 4);
+  dma4(r, lds_addr(reinterpret_cast<const char*>(rsl)) + wave * 256, (wave * 64 + lane) * 4, 0);
+}
+__device__ __forceinline__ const float* row_scale_sync(const float* rsl) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  return rsl;
+}
+
 // The epilogue's arguments, loaded into SGPRs at kernel entry.  Left to the
 // compiler, these kernel-argument loads are placed just before the main loop
 // and are still outstanding when it starts; the waitcnt pass then has to
@@ -842,13 +966,13 @@ __device__ __forceinline__ int dma_voffset(int b, int lane, int ld) {
   return r * ld * 2 + c * 16;
 }
 
-template <typename S, int EPI>
+template <typename S, int EPI, bool RS = false>
 __global__ void __launch_bounds__(S::NT)
 __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 gemm_lds_kernel(GemmArgs g) {
   static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -857,7 +981,7 @@ gemm_lds_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
+  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = ke > kb ? (ke - kb) / S::BK : 0;
@@ -959,20 +1083,26 @@ gemm_lds_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   if (nk > 0) tile(nk - 1, std::true_type{});
-  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
   if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
     // bf16 q|k|v outputs: only the staged form is compiled here (the host
     // runs unaligned launches on the register-staged kernel); both forms in
     // one kernel cost registers and code in the main loop
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
-    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE, rsl);
-  } else {
-    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
-                                        scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
-  }
-  if constexpr (EPI == EPI_RESID) {
+    if constexpr (RS)
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT, true>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane,
+                                                                    smem, S::NS * S::STAGE, row_scale_sync(rsl));
+    else
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                              S::NS * S::STAGE);
+  } else if constexpr (EPI == EPI_RESID) {
+    epilogue_resid_tile<S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                           S::NS * S::STAGE);
     if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
+  } else if constexpr (RS) {
+    epilogue<bf16_t, EPI, S::TM, S::TN, true>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                              row_scale_sync(rsl) + wm * S::WTM);
+  } else {
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   }
 }
 
@@ -1001,12 +1131,12 @@ struct W4 {
   static_assert(INS * (NS - 1) < 64, "vmcnt range");
 };
 
-template <typename S, int EPI>
+template <typename S, int EPI, bool RS = false>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wide_kernel(GemmArgs g) {
   static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1015,7 +1145,7 @@ gemm_wide_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
+  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = (ke - kb) / S::BK;   // >= 1: the host gives every split a K tile
@@ -1099,20 +1229,26 @@ gemm_wide_kernel(GemmArgs g) {
   };
   for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::false_type{});
   tile(nk - 1, std::true_type{});
-  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
   if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
     // only the staged form, as in the LDS kernels (with both forms compiled
     // in, the gate epilogue spilled registers into the main loop of these
     // 256 x 256 tiles)
     static_assert(S::BM * S::BN * 2 <= S::NS * S::STAGE, "the staged output tile must fit the operand stages");
-    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE, rsl);
-  } else {
-    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
-                                        scaled_epi(EPI) ? rsl + wm * S::WTM : nullptr);
-  }
-  if constexpr (EPI == EPI_RESID) {
+    if constexpr (RS)
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT, true>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane,
+                                                                    smem, S::NS * S::STAGE, row_scale_sync(rsl));
+    else
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                              S::NS * S::STAGE);
+  } else if constexpr (EPI == EPI_RESID) {
+    epilogue_resid_tile<S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, wm * S::WTM, wn * S::WTN, lane, smem,
+                                                           S::NS * S::STAGE);
     if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
+  } else if constexpr (RS) {
+    epilogue<bf16_t, EPI, S::TM, S::TN, true>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y,
+                                              row_scale_sync(rsl) + wm * S::WTM);
+  } else {
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, lane, blockIdx.y);
   }
 }
 
@@ -1160,9 +1296,10 @@ struct WD {
 // 16-byte chunks of each output row: a tile's BN / 2 features of one row are
 // contiguous in the output.  Needs ld0 and n_valid multiples of 8 (the host
 // checks) and the tile's first feature 16-byte aligned.
-template <typename S>
+template <typename S, bool RS = false>
 __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx16 (&acc)[S::TM][S::TN], int m0,
-                                                      int n0, int wave, int lane, char* smem, const float* rsl) {
+                                                      int n0, int wave, int lane, char* smem,
+                                                      const float* rsl = nullptr) {
   constexpr int FT = S::BN / 2;                   // features per tile
   constexpr int PITCH = FT * 2 + 16;              // bytes per staged row
   constexpr int CPR = FT * 2 / 16;                // 16-byte chunks per row
@@ -1178,8 +1315,9 @@ __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx1
     for (int i = 0; i < S::TM; ++i) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a0 = acc[i][j][2 * k] * rsl[32 * i + acc_row(2 * k, lane)];
-        const float a1 = acc[i][j][2 * k + 1] * rsl[32 * i + acc_row(2 * k + 1, lane)];
+        // RS: each value times its row's scale (LDS); otherwise times the constant 1
+        const float a0 = acc[i][j][2 * k] * (RS ? rsl[32 * i + acc_row(2 * k, lane)] : 1.f);
+        const float a1 = acc[i][j][2 * k + 1] * (RS ? rsl[32 * i + acc_row(2 * k + 1, lane)] : 1.f);
         const float got = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(gate_lane ? a1 : a0), 0x401F));
         const float gt = gate_lane ? a0 : got, up = gate_lane ? got : a1;
         const int rl = 32 * i + acc_row(2 * k + (gate_lane ? 0 : 1), lane);
@@ -1199,12 +1337,12 @@ __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx1
   }
 }
 
-template <typename S, int EPI>
+template <typename S, int EPI, bool RS = false>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wd_kernel(GemmArgs g) {
   static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ float rsl[scaled_epi(EPI) ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1212,7 +1350,7 @@ gemm_wd_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  const float rsv = scaled_epi(EPI) ? row_scale_load<S::BM>(g, m0) : 1.f;
+  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
   const int nk = g.K / S::BK;   // >= 1: the host requires K to be a positive multiple of 64
 
   const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
@@ -1316,17 +1454,25 @@ gemm_wd_kernel(GemmArgs g) {
     if (kt0 + d < nk) tile(kt0 + d, d);
   // no DMA may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-  if constexpr (scaled_epi(EPI)) row_scale_store<S::BM>(rsv, rsl);
-  if constexpr (EPI == EPI_SWIGLU)
-    epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem, rsl);
-  else if constexpr (EPI == EPI_GATE || EPI == EPI_QKV)
-    epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
-                                                            S::NS * S::STAGE, rsl);
-  else
-    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
-  if constexpr (EPI == EPI_RESID) {
-    if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
+  if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (RS)
+      epilogue_swiglu16_lds<S, true>(e, acc, m0, n0, wave, lane, smem, row_scale_sync(rsl));
+    else
+      epilogue_swiglu16_lds<S>(e, acc, m0, n0, wave, lane, smem);
+  } else if constexpr (EPI == EPI_GATE || EPI == EPI_QKV) {
+    if constexpr (RS)
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT, true>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
+                                                                    S::NS * S::STAGE, row_scale_sync(rsl));
+    else
+      epilogue_staged<EPI, S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
+                                                              S::NS * S::STAGE);
   }
+  else if constexpr (EPI == EPI_RESID) {
+    epilogue_resid_tile<S::TM, S::TN, S::BM, S::BN, S::NT>(e, acc, m0, n0, 0, wave * S::WTN, lane, smem,
+                                                           S::NS * S::STAGE);
+    if (g.rs_out != nullptr) resid_norm_finish<S::BM, S::NT, (S::TN & -S::TN)>(g, m0, tm, nbn);
+  } else
+    epilogue<bf16_t, EPI, S::TM, S::TN>(e, acc, m0, n0 + wave * S::WTN, lane, 0);
 }
 
 // Fragment-order copy of a bf16 weight W[N, K] (row stride ld): 16-byte
@@ -1359,6 +1505,12 @@ __global__ void frag_pack_kernel(const bf16_t* __restrict__ W, int N, int K, int
 template <typename S, int EPI>
 hipError_t run_wd(const GemmArgs& a, hipStream_t s) {
   const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  if constexpr (scaled_epi(EPI)) {
+    if (a.row_scale != nullptr) {
+      hipLaunchKernelGGL((gemm_wd_kernel<S, EPI, true>), dim3(nbm * nbn), dim3(S::NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_wd_kernel<S, EPI>), dim3(nbm * nbn), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
@@ -1391,9 +1543,8 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, int split, lo
 }
 
 // Split-K reduction into a residual row, fused with the RMSNorm of the
-// updated row (or its deferred form when w is NULL: the row rounded to T and
-// its 1 / rms to rs): one workgroup per row, partial slabs summed in a fixed
-// order.
+// updated row (without the gain when w is NULL, the 1 / rms then also to
+// rs): one workgroup per row, partial slabs summed in a fixed order.
 constexpr int RN_MAXV = 16;   // N <= 4 * 256 * RN_MAXV
 template <typename T, int MAXV>
 __global__ void __launch_bounds__(256)
@@ -1548,6 +1699,13 @@ template <typename T, int EPI>
 hipError_t run_reg(const GemmArgs& a, int split, hipStream_t s) {
   constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
   const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+  if constexpr (scaled_epi(EPI) && sizeof(T) == 2) {
+    if (a.row_scale != nullptr) {
+      hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI, true>), dim3(nbm * nbn, split), dim3(WM * WN * 64), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI>), dim3(nbm * nbn, split), dim3(WM * WN * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -1555,6 +1713,12 @@ hipError_t run_reg(const GemmArgs& a, int split, hipStream_t s) {
 template <typename S, int EPI>
 hipError_t run_lds(const GemmArgs& a, int split, hipStream_t s) {
   const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  if constexpr (scaled_epi(EPI)) {
+    if (a.row_scale != nullptr) {
+      hipLaunchKernelGGL((gemm_lds_kernel<S, EPI, true>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_lds_kernel<S, EPI>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
@@ -1562,6 +1726,12 @@ hipError_t run_lds(const GemmArgs& a, int split, hipStream_t s) {
 template <typename S, int EPI>
 hipError_t run_wide(const GemmArgs& a, int split, hipStream_t s) {
   const int nbm = (a.M + S::BM - 1) / S::BM, nbn = (a.N + S::BN - 1) / S::BN;
+  if constexpr (scaled_epi(EPI)) {
+    if (a.row_scale != nullptr) {
+      hipLaunchKernelGGL((gemm_wide_kernel<S, EPI, true>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_wide_kernel<S, EPI>), dim3(nbm * nbn, split), dim3(S::NT), 0, s, a);
   return hipGetLastError();
 }
@@ -1614,7 +1784,7 @@ hipError_t run_cfg(const GemmArgs& a, int split, int cfg, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, hipStream_t s, bool* normed) {
+hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, hipStream_t s, int* normed) {
   if (split > 1) {
     if (epi != EPI_F32 && epi != EPI_RESID) return hipErrorInvalidValue;
     GemmArgs p = a;
@@ -1624,7 +1794,7 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
     hipError_t e = run_cfg<T, EPI_PARTIAL>(p, split, cfg, s);
     if (e != hipSuccess) return e;
     if (epi == EPI_RESID && (a.norm_w || a.rs_out) && a.N % 4 == 0 && a.N <= 4 * 256 * RN_MAXV && split <= 4) {
-      if (normed) *normed = true;
+      if (normed) *normed = NORM_ROWS;   // the reduction has whole rows: normalised there (without the gain when deferred)
       return launch_splitk_resid_norm<T>(a, ws, split, p.split_stride, s);
     }
     const long long n4 = (long long)a.M * (a.N / 4);
@@ -1640,7 +1810,7 @@ hipError_t dispatch(Epi epi, const GemmArgs& a, int split, float* ws, int cfg, h
   switch (epi) {
     case EPI_F32: return run_cfg<T, EPI_F32>(a, 1, cfg, s);
     case EPI_RESID:
-      if (normed && a.rs_out) *normed = true;   // the deferred norm in the epilogue
+      if (normed && a.rs_out) *normed = NORM_DEFERRED;   // the rows and their scales from the epilogue
       return run_cfg<T, EPI_RESID>(a, 1, cfg, s);
     case EPI_GATE:
     case EPI_QKV: {
@@ -1723,6 +1893,11 @@ void auto_plan(bool bf16, Epi epi, const GemmArgs& a, int max_split, int& cfg, i
 
 int gemm_k_tile(bool bf16) { return bf16 ? 64 : 32; }
 
+// The residual epilogue addresses out0 through a 32-bit buffer range.
+bool resid_rows_ok(Epi epi, const GemmArgs& a) {
+  return epi != EPI_RESID || (long long)a.M * a.ld0 * 4 < (1LL << 31);
+}
+
 // Arguments of the deferred RMSNorm (bf16 only): the row scale on the
 // scaled epilogues; on EPI_RESID the bf16 copy, the scale output and, for
 // the form without a K split, the partial sums (at most 256 slots of 32
@@ -1737,10 +1912,10 @@ bool deferred_norm_ok(bool bf16, Epi epi, const GemmArgs& a) {
 int gemm_tile_configs() { return N_CFG; }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws, hipStream_t s,
-                       int cfg, bool* normed) {
-  if (normed) *normed = false;
+                       int cfg, int* normed) {
+  if (normed) *normed = NORM_NONE;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!deferred_norm_ok(bf16, epi, a)) return hipErrorInvalidValue;
+  if (!deferred_norm_ok(bf16, epi, a) || !resid_rows_ok(epi, a)) return hipErrorInvalidValue;
   GemmArgs g = a;
   if (split < 1) split = 1;
   if (cfg < 0) auto_plan(bf16, epi, a, ws ? split : 1, cfg, split);
@@ -1797,7 +1972,8 @@ int gemm_wd_tiles(int tile, int M, int N) {
 
 hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || tile < 1 || tile > 2) return hipErrorInvalidValue;
+  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || !resid_rows_ok(epi, a) || tile < 1 || tile > 2)
+    return hipErrorInvalidValue;
   return tile == 2 ? run_wd_epi<CfgWD2>(epi, a, s) : run_wd_epi<CfgWD1>(epi, a, s);
 }
 

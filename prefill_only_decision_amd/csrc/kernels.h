@@ -52,10 +52,12 @@ struct GemmArgs {
   // accumulators of row r are multiplied by row_scale[r] before the epilogue
   // (the 1 / rms of an RMSNorm whose gain has been folded into W).
   const float* row_scale;
-  // EPI_RESID (bf16) with rs_out set: the RMSNorm of the updated rows is left
-  // to the next GEMM: norm_out (bf16, row stride N) = the updated row rounded
-  // to bf16 and rs_out[r] = 1 / sqrt(mean(row^2) + norm_eps), norm_w unused.
-  // Without a K split the epilogue writes the rows' sums of squares over
+  // EPI_RESID (bf16) with rs_out set: the RMSNorm gain is left to the next
+  // GEMM (folded into its weights), norm_w unused; rs_out[r] = 1 /
+  // sqrt(mean(row^2) + norm_eps).  With a K split the reduction writes the
+  // normalised rows (row * rs_out, bf16) to norm_out (row stride N); without
+  // one the rows rounded to bf16, and the next GEMM scales its accumulator
+  // rows by rs_out.  Without a K split the epilogue writes the rows' sums of squares over
   // aligned groups of 32 * 2^k columns to ss_parts ([N / 32][ss_ld] floats,
   // ss_ld a multiple of 32) and the last workgroup to finish a row block (by
   // `tickets`, one counter per row block, zero between launches) sums them
@@ -72,11 +74,16 @@ struct GemmArgs {
 // the largest K split allowed (1 without a workspace).  With split > 1
 // (EPI_F32 or EPI_RESID only) partial tiles go to `ws` (split * M * N
 // floats) and a reduction kernel applies the epilogue in a fixed order.
-// `normed` (optional) reports whether the fused RMSNorm (or, with rs_out, its
-// deferred form) ran.
+// `normed` (optional) reports what an EPI_RESID launch left in norm_out.
+enum NormOut {
+  NORM_NONE = 0,       // nothing: the norm was not fused
+  NORM_ROWS = 1,       // the normalised rows (times norm_w; without a gain when rs_out is set): the
+                       // K split's reduction had whole rows
+  NORM_DEFERRED = 2,   // the rows rounded to bf16 and rs_out: the consumer scales its rows
+};
 constexpr int GEMM_AUTO = -1;
 hipError_t launch_gemm(bool bf16, Epi epi, const GemmArgs& a, int split, float* ws,
-                       hipStream_t s, int tile_cfg = GEMM_AUTO, bool* normed = nullptr);
+                       hipStream_t s, int tile_cfg = GEMM_AUTO, int* normed = nullptr);
 // Weight-direct GEMM (bf16): W is a fragment-order copy made by
 // launch_frag_pack (frag_bytes(N, K) bytes); K a positive multiple of 64;
 // EPI_F32, EPI_RESID, EPI_SWIGLU over a copy packed with gu16 (gate/up
@@ -108,13 +115,14 @@ hipError_t launch_stream_read(const void* src, long long bytes, void* sink, hipS
 // ------------------------------------------------------------ elementwise
 hipError_t launch_embed(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
                         hipStream_t s);
-// out = RMSNorm(x) * w.  With w == NULL and rs set (the deferred form): out
-// = x rounded to the element type and rs[t] = 1 / sqrt(mean(x[t]^2) + eps).
+// out = RMSNorm(x) * w.  With w == NULL and rs set (the gain folded into the
+// next GEMM's weights): out = x * rs[t] (no gain) and rs[t] = 1 / sqrt(mean(
+// x[t]^2) + eps).
 hipError_t launch_rmsnorm(bool bf16, const float* x, const float* w, void* out, int T, int d,
                           float eps, hipStream_t s, float* rs = nullptr);
 // x = E[ids] (fp32) and xn = RMSNorm(x) * w (elem), T rows of width d
 // (d % 4 == 0, d <= 16384; else hipErrorInvalidValue); w == NULL with rs:
-// the deferred form as launch_rmsnorm.
+// no gain, as launch_rmsnorm.
 hipError_t launch_embed_norm(bool bf16, const int32_t* ids, const void* E, float* x, int T, int d,
                              const float* w, void* xn, float eps, hipStream_t s, float* rs = nullptr);
 // out[dst_row(o)] = (W[o] + scale * B[o] A) * gain ; row_map may be NULL

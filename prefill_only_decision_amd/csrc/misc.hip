@@ -33,8 +33,8 @@ __global__ void embed_kernel(const int32_t* __restrict__ ids, const T* __restric
 // -------------------------------------------------------------- rmsnorm
 // out = x / sqrt(mean(x^2) + eps) * w, one workgroup of 256 threads per row;
 // the row stays in registers between the sum of squares and the scaling
-// (d <= 4 * 256 * RMS_MAXV).  w == NULL: the deferred form (out = x rounded,
-// rs[row] = 1 / sqrt(mean(x^2) + eps)).
+// (d <= 4 * 256 * RMS_MAXV).  w == NULL: no gain (it is folded into the next
+// GEMM's weights) and rs[row] = 1 / sqrt(mean(x^2) + eps).
 constexpr int RMS_MAXV = 16;
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,

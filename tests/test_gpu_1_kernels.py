@@ -67,11 +67,12 @@ def test_gemm_bf16_every_tile_config(M, N, K, split):
 def test_gemm_resid_norm(M, N, K):
     """The residual projection that leaves its RMSNorm to the next GEMM
     (s1k_gemm_resid_norm), in every tile configuration and with a K split:
-    x += A W^T against float64 products of the same operands; hb the updated
-    x rounded to bf16 (bitwise); rs * x against the oracle's rms_norm of the
-    same updated x (gain 1) element by element; without a K split, rs bitwise
-    the same in every configuration and for a row whatever M (one summation
-    order, whatever the tile widths), N ragged against the tiles."""
+    x += A W^T against float64 products of the same operands; rs * x against
+    the oracle's rms_norm of the same updated x (gain 1) element by element;
+    hb bitwise the updated x rounded to bf16 (without a K split) or x * rs
+    rounded (with one); without a K split, rs bitwise the same in every
+    configuration and for a row whatever M (one summation order, whatever the
+    tile widths), N ragged against the tiles."""
     torch = require_gpu()
     rng = np.random.default_rng([M, N, K, 11])
     A, W = _bits(rng, (M, K)), _bits(rng, (N, K), 0.05)
@@ -81,24 +82,28 @@ def test_gemm_resid_norm(M, N, K):
     ref = x0.astype(np.float64) + O.bf16_bits_to_float(A) @ O.bf16_bits_to_float(W).T
     runs = [(cfg, 1) for cfg in [-1] + list(range(B.gemm_tile_configs()))]
     if N % 4 == 0 and K % 64 == 0 and K >= 128:
-        runs.append((-1, 2))
+        runs += [(-1, 2), (1, 2)]
     first = None
     for cfg, split in runs:
         log(f"gemm resid norm cfg={cfg} split={split} M={M} N={N} K={K}")
         dx = dev(x0.copy())
         dh = torch.zeros((M, N), dtype=torch.int16, device="cuda")
         drs = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
-        B.gemm_resid_norm(dA.data_ptr(), dW.data_ptr(), dx.data_ptr(), M, N, K, split, cfg, eps, dh.data_ptr(),
-                          drs.data_ptr(), stream_ptr())
+        form = B.gemm_resid_norm(dA.data_ptr(), dW.data_ptr(), dx.data_ptr(), M, N, K, split, cfg, eps,
+                                 dh.data_ptr(), drs.data_ptr(), stream_ptr())
         torch.cuda.synchronize()
         x, hb, rs = dx.cpu().numpy(), host_bits(dh), drs.cpu().numpy()
+        # without a K split the rows and their scales; an explicit configuration splits as asked
+        if split == 1 or cfg >= 0:
+            assert form == (2 if split == 1 else 1), (cfg, split, form)
         assert np.isfinite(x).all() and np.isfinite(rs).all(), (cfg, split)
         assert np.abs(x - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-6, (cfg, split)
-        assert np.array_equal(hb, f32_to_bf16_bits(x)), (cfg, split)
+        want_hb = x if form == 2 else (x * rs[:, None]).astype(np.float32)
+        assert np.array_equal(hb, f32_to_bf16_bits(want_hb)), (cfg, split)
         want = O.rms_norm(x.astype(np.float64), np.ones(N), eps)
         got = x.astype(np.float64) * rs[:, None].astype(np.float64)
         assert np.abs(got - want).max() <= 4e-6 * np.abs(want).max(), (cfg, split)
-        if split == 1:
+        if form == 2:
             if first is None:
                 first = rs.copy()
             assert np.array_equal(rs.view(np.uint32), first.view(np.uint32)), (cfg, "rs differs between configurations")
