@@ -214,7 +214,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
             if r["Counter_Name"] != counter:
                 continue
             name, kib = r["Kernel_Name"], float(r["Counter_Value"])
-            if re.search(r"gemm_\w+_kernel<.*, 3>\(s1::GemmArgs\)", name):
+            if re.search(r"gemm_\w+_kernel<.*, 3(, (true|false))?>\(s1::GemmArgs\)", name):
                 gemm.append(kib * 1024)
             elif "elementwise" in name and kib * 1024 > COPY_BYTES / 2:
                 copy.append(kib * 1024)

@@ -12,7 +12,9 @@
 // registers and feed O^T += V^T P^T directly: the accumulator layout of S^T
 // is a permutation of the key index that the B operand of the second product
 // accepts as-is, provided V^T is read with the same key permutation.  Running
-// max and sum are fp32; exp2 with log2(e) folded into the scale.
+// max and sum are fp32; exp2 with log2(e) folded into the scale, applied in
+// one multiply-add per score; the reference max moves only when a block
+// raises it by more than 2^8 (no rescale of O in most blocks).
 //
 // Split keys: a workgroup may cover only a piece [k_lo, k_hi) of its
 // queries' keys (pieces cut at fixed key positions, so a query's pieces do
@@ -22,6 +24,7 @@
 // prefix read the prefix keys once for all their queries (RFC #114 section 5:
 // every branch attends to the same immutable prefix snapshot).
 #include <algorithm>
+#include <climits>
 
 #include "common.h"
 #include "kernels.h"
@@ -55,9 +58,12 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   char* sK = smem;
   char* sVt = smem + BKV * KPITCH;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = blockIdx.y;
+  // the heads of one block are adjacent in launch order (blocks come
+  // heaviest first, so the whole launch runs longest work first)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x % Hq;
   const int kvh = h / (Hq / Hkv);
-  const AttnBlock blk = blocks[blockIdx.x];
+  const AttnBlock blk = blocks[blockIdx.x / Hq];
   const AttnSeq sq = seqs[blk.seq];
   const int n_pre = sq.kv_pre_len, n_kv = n_pre + sq.len;
   const int k_lo = blk.k_lo, k_hi = min(blk.k_hi, n_kv);
@@ -144,46 +150,64 @@ attn_bf16_kernel(const bf16_t* __restrict__ q, int ldq, const bf16_t* __restrict
       for (int ks = 0; ks < HD / 16; ++ks)
         mfma32(s[t], as_frag(*reinterpret_cast<const uint4*>(kr + 32 * ks)), qf[ks]);
     }
+    // raw scores; keys a query must not see become -inf.  A block that every
+    // query of the wave sees whole (the causal cut and the piece end both lie
+    // past it) skips the mask: the values are the same either way.
     float mx = -INFINITY;
+    if (j0 + BKV <= n_pre + qw0 + 1 && j0 + BKV <= k_hi) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * t + acc_row(r, lane);
-        const bool vis = (j <= n_pre + qi) && (j < k_hi);
-        const float val = vis ? s[t][r] * scale_log2 : -INFINITY;
-        s[t][r] = val;
-        mx = fmaxf(mx, val);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    // a query that has seen no key of this piece yet keeps (max, sum, O) =
-    // (-inf, 0, 0): the reference point 0 keeps alpha and p finite (0)
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * t + acc_row(r, lane);
+          const bool vis = (j <= n_pre + qi) && (j < k_hi);
+          s[t][r] = vis ? s[t][r] : -INFINITY;
+          mx = fmaxf(mx, s[t][r]);
+        }
+    }
+    // the block's largest scaled score (rounding is monotonic, so this is
+    // the largest of the scaled scores); both halves of the wave hold the
+    // same queries
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    // Lazy rescaling: the reference point m_run moves only when the block's
+    // maximum exceeds it by more than 2^8, so p = 2^(s - m_run) <= 256 and
+    // the running sums stay exact relative to their reference.  A query that
+    // has seen no key of this piece yet keeps (m, l, O) = (-inf, 0, 0).  The
+    // rescale runs for the whole wave when any of its queries needs it;
+    // others multiply by exactly 1.
+    const bool grow = mx > m_run + 8.f;
+    if (__ballot(grow) != 0) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float ps = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[t][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -m_use));
         s[t][r] = p;
         ps += p;
       }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    l_run += ps;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[t][8 * hf + e];
-        const bf16x8 pf = frag_from_f(pv);
+        const int e0 = 8 * hf;
+        const bf16x8 pf = as_frag(make_uint4(cvt2(s[t][e0], s[t][e0 + 1]), cvt2(s[t][e0 + 2], s[t][e0 + 3]),
+                                             cvt2(s[t][e0 + 4], s[t][e0 + 5]), cvt2(s[t][e0 + 6], s[t][e0 + 7])));
         const int kb = (32 * t + 16 * hf + 4 * hi) * 2;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt) {
@@ -490,6 +514,15 @@ void plan_attention(const AttnSeq* in, int n, int row_base, int n_rows, int Hq, 
     }
     ++i;
   }
+  // heaviest workgroups first (the 64-key blocks each sweeps), so that the
+  // long causal blocks do not start last and leave CUs idle at the end
+  auto cost = [&](const AttnBlock& b) {
+    const AttnSeq& q = P.seqs[b.seq];
+    const int end = std::min(b.k_hi, q.kv_pre_len + std::min(b.q0 + bq, q.len));
+    return end > b.k_lo ? cdiv(end - b.k_lo, 64) : 0;
+  };
+  std::stable_sort(P.blocks.begin(), P.blocks.end(),
+                   [&](const AttnBlock& x, const AttnBlock& y) { return cost(x) > cost(y); });
 }
 
 hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, const void* v,
@@ -498,8 +531,9 @@ hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, c
                             const AttnPartials& part, hipStream_t s) {
   if (n_blocks <= 0) return hipSuccess;
   if (Hkv <= 0 || Hq % Hkv != 0 || !attn_block_rows_valid(bf16, block_rows)) return hipErrorInvalidValue;
-  const dim3 grid(n_blocks, Hq);
+  if ((long long)n_blocks * Hq > INT_MAX) return hipErrorInvalidValue;
   if (bf16) {
+    const dim3 grid(n_blocks * Hq);   // block-major, heads adjacent
     if (hd != HD) return hipErrorInvalidValue;
     const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
     const auto* qq = reinterpret_cast<const bf16_t*>(q);
@@ -516,6 +550,7 @@ hipError_t launch_attention(bool bf16, const void* q, int ld_q, const void* k, c
       hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, s, qq, ld_q, kk, vv, ld_kv, oo, ld_o, seqs,
                          blocks, Hq, Hkv, sl2, part.row_slot, part.row_base, part.pO, part.pML);
   } else {
+    const dim3 grid(n_blocks, Hq);
     const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
     const auto* qq = reinterpret_cast<const float*>(q);
     const auto* kk = reinterpret_cast<const float*>(k);

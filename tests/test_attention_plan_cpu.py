@@ -3,7 +3,8 @@ visible (query, key) pair is covered by exactly one workgroup, every row's
 piece ordinals are 0 .. n-1 exactly once, pieces are cut at fixed key
 positions (multiples of the piece), shared prefix sweeps serve only
 sequences that continue that prefix, and the unsplit plan is one workgroup
-per query block over its whole causal range."""
+per query block over its whole causal range; workgroups come heaviest
+first."""
 from collections import defaultdict
 
 import numpy as np
@@ -72,6 +73,18 @@ def _check(seqs, bq, piece, n_cu=256):
         else:
             assert sorted(ps) == list(range(len(ps))) and row_np[r - row_lo] == len(ps), (r, ps)
     assert sum(cover.values()) == sum(pre_len[i] + t + 1 for r, (i, t) in owner.items())
+    # workgroups are launched heaviest first: the 64-key blocks each sweeps
+    # never increase along the plan
+    def sweeps(b):
+        seq, q0, k_lo, k_hi, _ = b
+        if seq < n:
+            L, P = q_len[seq], pre_len[seq]
+        else:
+            L, P = shared[seq - n][1], shared[seq - n][4]
+        end = min(k_hi, P + min(q0 + bq, L))
+        return -(-(end - k_lo) // 64) if end > k_lo else 0
+    w = [sweeps(b) for b in blocks]
+    assert all(a >= b for a, b in zip(w, w[1:])), w
     return blocks, shared, chosen
 
 
@@ -103,8 +116,9 @@ def test_unsplit_plan_is_one_workgroup_per_query_block():
     seqs = _seqs([(300, 0), (64, 200)])
     blocks, shared, chosen = _check(seqs, 128, 0)
     assert chosen == 0 and len(shared) == 0
-    assert [tuple(b) for b in blocks] == [(0, 0, 0, 300, -1), (0, 128, 0, 300, -1), (0, 256, 0, 300, -1),
-                                          (1, 0, 0, 264, -1)]
+    # heaviest first: 5, 5, 4 and 2 blocks of 64 keys, ties in plan order
+    assert [tuple(b) for b in blocks] == [(0, 256, 0, 300, -1), (1, 0, 0, 264, -1), (0, 128, 0, 300, -1),
+                                          (0, 0, 0, 300, -1)]
 
 
 def test_auto_piece_fills_the_chip_for_one_short_request():
