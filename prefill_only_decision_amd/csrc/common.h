@@ -15,16 +15,20 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bfloat16, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+// Two floats -> two bf16 in one word (a low, b high) with the packed
+// hardware conversion v_cvt_pk_bf16_f32: round to nearest, ties to even
+// (inputs are finite).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const float2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
-}
+// float -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ bf16_t f2bf(float f) { return static_cast<bf16_t>(cvt2(f, 0.f)); }
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return cvt2(lo, hi); }
 
 // Element conversions used by templated kernels (T = bf16_t or float).
 template <typename T> __device__ __forceinline__ float to_f(T v);
@@ -43,15 +47,6 @@ __device__ __forceinline__ bf16x8 frag_from_f(const float* v) {
   u.z = pack_bf2(v[4], v[5]);
   u.w = pack_bf2(v[6], v[7]);
   return as_frag(u);
-}
-// Two floats -> two bf16 in one word (a low, b high) with the packed
-// hardware conversion v_cvt_pk_bf16_f32 (round to nearest even, as f2bf for
-// finite values).
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-typedef float float2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-  const float2v f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 __device__ __forceinline__ float lo_half(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_half(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
