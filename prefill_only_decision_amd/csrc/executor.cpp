@@ -950,20 +950,23 @@ int set_features(Plan* p, const s1_features* f, float* d_logp, float* d_cand_lp,
 namespace {
 
 // The FFN gate/up projection runs on the weight-direct GEMM.  Its launches
-// are bound by the operand stream into each CU (the same bytes per K tile
-// for both tiles, 64 KB), so the time follows the number of waves of
-// workgroups; the 256 x 256 tile does a third more work per workgroup and
-// is taken only when it needs clearly fewer waves than 128 x 384.  Measured
-// on MI355X with weights out of cache (4B shape, SwiGLU epilogue): 512 rows
-// 63-72 us (128 x 384) against 69-72 us for the LDS-staged 256 x 192 tiles;
-// 768 rows 78 us (256 x 256) against 122 us; 16,925 rows 1,473 us against
-// 1,659 us for the LDS-staged 256 x 256 tiles; 27B shape at 1,024 rows
-// 359 us (128 x 384) against 435 us.
+// are bound by the operand stream into each CU (BM + BN operand rows per K
+// step: 512 for 128 x 384 and 256 x 256, 448 for 192 x 256), so the time
+// follows the number of waves of workgroups times that panel; the
+// 256 x 256 tile does a third more work per workgroup and is taken only
+// when it needs clearly fewer waves than 128 x 384, and 192 x 256 when it
+// streams fewer rows in all (one wave of 228 workgroups at 512 rows).
+// Measured on MI355X with weights out of cache (4B shape, SwiGLU epilogue):
+// 512 rows 63-72 us (128 x 384) against 69-72 us for the LDS-staged
+// 256 x 192 tiles; 768 rows 78 us (256 x 256) against 122 us; 16,925 rows
+// 1,473 us against 1,659 us for the LDS-staged 256 x 256 tiles; 27B shape at
+// 1,024 rows 359 us (128 x 384) against 435 us.
 int gate_up_direct(const Model* m, const LayerW& L, int T) {
   if (!L.w_gu_frag || T <= 0 || m->cfg.ffn % 8) return 0;   // SwiGLU rows written in 16-byte chunks
-  const long long w1 = (gemm_wd_tiles(1, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
-  const long long w2 = (gemm_wd_tiles(2, T, L.n_gu) + m->n_cu - 1) / m->n_cu;
-  return 11 * w2 < 10 * w1 ? 2 : 1;
+  auto waves = [&](int t) { return (gemm_wd_tiles(t, T, L.n_gu) + m->n_cu - 1) / m->n_cu; };
+  const long long w1 = waves(1), w2 = waves(2), w3 = waves(3);
+  const int t = 11 * w2 < 10 * w1 ? 2 : 1;
+  return w3 * gemm_wd_panel(3) < (t == 2 ? w2 : w1) * gemm_wd_panel(t) ? 3 : t;
 }
 
 // The down projection on the weight-direct kernel (256 x 256 tiles) when it

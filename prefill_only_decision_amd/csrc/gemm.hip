@@ -1516,6 +1516,7 @@ hipError_t run_wd(const GemmArgs& a, hipStream_t s) {
 }
 using CfgWD1 = WD<4, 3, 4, 3>;   // 128 x 384, a wave 128 x 96, four activation stages, three weight tiles ahead
 using CfgWD2 = WD<8, 2, 4, 3>;   // 256 x 256, a wave 256 x 64
+using CfgWD3 = WD<6, 2, 4, 3>;   // 192 x 256, a wave 192 x 64
 
 // Sum of split-K partial slabs in a fixed order, then the epilogue.
 template <bool RESID>
@@ -1966,14 +1967,24 @@ hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 int gemm_wd_tiles(int tile, int M, int N) {
-  const int bm = tile == 2 ? CfgWD2::BM : CfgWD1::BM, bn = tile == 2 ? CfgWD2::BN : CfgWD1::BN;
+  const int bm = tile == 2 ? CfgWD2::BM : tile == 3 ? CfgWD3::BM : CfgWD1::BM;
+  const int bn = tile == 2 ? CfgWD2::BN : tile == 3 ? CfgWD3::BN : CfgWD1::BN;
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+int gemm_wd_panel(int tile) {
+  return tile == 2 ? CfgWD2::BM + CfgWD2::BN : tile == 3 ? CfgWD3::BM + CfgWD3::BN : CfgWD1::BM + CfgWD1::BN;
 }
 
 hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || !resid_rows_ok(epi, a) || tile < 1 || tile > 2)
+  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || !resid_rows_ok(epi, a) || tile < 1 || tile > 3)
     return hipErrorInvalidValue;
+  if (tile == 3) {   // built for the SwiGLU and fp32 epilogues
+    if (epi == EPI_SWIGLU) return run_wd<CfgWD3, EPI_SWIGLU>(a, s);
+    if (epi == EPI_F32) return run_wd<CfgWD3, EPI_F32>(a, s);
+    return hipErrorInvalidValue;
+  }
   return tile == 2 ? run_wd_epi<CfgWD2>(epi, a, s) : run_wd_epi<CfgWD1>(epi, a, s);
 }
 
