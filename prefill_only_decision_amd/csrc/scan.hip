@@ -87,7 +87,17 @@ scan_bf16_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi = lane >> 5, cl = lane & 31;
-  const int seq = blockIdx.x / NDVG, dvg = blockIdx.x % NDVG, h = blockIdx.y;
+  // The chunk modes take their (chunk, head) in head-major order through
+  // the XCD remap, so that each XCD runs a contiguous run of heads: the
+  // chunk states a head's summary workgroups write are read by its fold
+  // workgroups on the same XCD, out of that XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if constexpr (MODE != MODE_FULL) {
+    const int t = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    by = t / gridDim.x;
+    bx = t - by * gridDim.x;
+  }
+  const int seq = bx / NDVG, dvg = bx % NDVG, h = by;
   const ScanSeq sq = seqs[seq];
   const int dvw = dvg * DVG;          // first value column of the workgroup
   const int dv0 = dvw + wave * 32;    // first value column of this wave
