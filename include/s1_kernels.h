@@ -118,8 +118,8 @@ int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* 
  * out bf16 [M, N/2][f] = silu(gate_f) * up_f, the FFN gate/up projection with
  * its SwiGLU (RFC #114 section 1; SwiGLU FFN of the Qwen3.5-family
  * backbone).  K must be a positive multiple of 64.  tile 1: workgroup tiles
- * of 128 rows x 384 columns; tile 2: 256 x 256; tile 3: 192 x 256 (other
- * values: S1_EINVAL).
+ * of 128 rows x 384 columns; tile 2: 256 x 256; tile 3: 192 x 256; tile
+ * 4: 224 x 256 (other values: S1_EINVAL).
  * Accumulation order over K is the same as s1k_gemm's without a K split
  * (results are bitwise equal). */
 int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,

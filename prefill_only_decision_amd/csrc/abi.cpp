@@ -569,7 +569,7 @@ int s1k_frag_pack(const void* W, int32_t N, int32_t K, int32_t gate_up16, void* 
 
 int s1k_gemm_wfrag(const void* A, const void* Wfrag, void* out, int32_t M, int32_t N, int32_t K,
                    int32_t swiglu, int32_t tile, void* hip_stream) {
-  if (!A || !Wfrag || !out || M < 0 || N < 1 || K < 64 || K % 64 || (swiglu && N % 64) || tile < 1 || tile > 3)
+  if (!A || !Wfrag || !out || M < 0 || N < 1 || K < 64 || K % 64 || (swiglu && N % 64) || tile < 1 || tile > 4)
     return set_error(S1_EINVAL, "s1k_gemm_wfrag: unsupported arguments");
   GemmArgs g{};
   g.A = A;

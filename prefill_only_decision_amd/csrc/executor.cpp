@@ -9,6 +9,7 @@
 // only at the questions' marker rows (sys1rust README, "How it works": the
 // head runs only at the positions the answer reads).
 #include <algorithm>
+#include <initializer_list>
 #include <climits>
 #include <cstring>
 #include <map>
@@ -969,21 +970,43 @@ int gate_up_direct(const Model* m, const LayerW& L, int T) {
   return w3 * gemm_wd_panel(3) < (t == 2 ? w2 : w1) * gemm_wd_panel(t) ? 3 : t;
 }
 
-// The down projection on the weight-direct kernel (256 x 256 tiles) when it
-// runs without a K split and its tiles fill the chip at least once: the
-// weights bypass LDS as in the gate/up GEMM (4B shape, 16,925 rows, on
-// MI355X: 930 -> 817 us; the out-projection, K = 2,048, gained nothing:
-// 270 against 275 us).  Same K order as the LDS kernels, so rows stay
-// bitwise independent of M.
-bool residual_direct(const Model* m, const void* frag, int T, int split) {
-  return frag && split == 1 && gemm_wd_tiles(2, T, m->cfg.d_model) >= m->n_cu;
+// Of the weight-direct tiles given (earlier ones preferred on ties), the one
+// with the fewest waves of workgroups times operand rows per K step: the
+// operand stream into each CU bounds these launches, and a last wave that
+// leaves CUs idle costs a whole wave.  16,925 rows: 224 x 256 tiles take the
+// d-wide down projection in 2.97 waves where 256 x 256 take 2.62, rounded up
+// to 3 (1,440 against 1,536 rows per K step), and the attention QKV in 3.6
+// against 3.1 (4 waves either way, 480 against 512 rows).
+int wd_pick(const Model* m, int T, int N, std::initializer_list<int> tiles) {
+  int best = 0;
+  long long cost = LLONG_MAX;
+  for (int t : tiles) {
+    const long long c = (gemm_wd_tiles(t, T, N) + m->n_cu - 1) / m->n_cu * gemm_wd_panel(t);
+    if (c < cost) {
+      cost = c;
+      best = t;
+    }
+  }
+  return best;
+}
+
+// The down projection on the weight-direct kernel (256 x 256 or 224 x 256
+// tiles) when it runs without a K split and its tiles fill the chip at least
+// once: the weights bypass LDS as in the gate/up GEMM (4B shape, 16,925
+// rows, on MI355X: 930 -> 817 us; the out-projection, K = 2,048, gained
+// nothing: 270 against 275 us).  Same K order as the LDS kernels, so rows
+// stay bitwise independent of M.  0: not on the weight-direct kernel.
+int residual_direct(const Model* m, const void* frag, int T, int split) {
+  if (!frag || split != 1 || gemm_wd_tiles(2, T, m->cfg.d_model) < m->n_cu) return 0;
+  return wd_pick(m, T, m->cfg.d_model, {2, 4});
 }
 
 // The mixer in-projections (linear-attention q|k|v|gate, attention q|k|v)
-// on the weight-direct kernel's 256 x 256 tiles when those fill the chip,
-// with the staged bf16 epilogue.  Same K order as the LDS kernels.
-bool in_direct(const Model* m, const LayerW& L, int T) {
-  return L.w_in_frag && gemm_wd_tiles(2, T, L.n_in) >= m->n_cu;
+// on the weight-direct kernel's 256 x 256 or 224 x 256 tiles when those fill
+// the chip, with the staged bf16 epilogue.  Same K order as the LDS kernels.
+int in_direct(const Model* m, const LayerW& L, int T) {
+  if (!L.w_in_frag || gemm_wd_tiles(2, T, L.n_in) < m->n_cu) return 0;
+  return wd_pick(m, T, L.n_in, {2, 4});
 }
 
 // Largest K split the workspace allows for an M-row GEMM with a d-wide
@@ -1060,9 +1083,9 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
         g.out2 = m->beta + (size_t)r0 * H;
         g.nsplit2 = g.nsplit + H;
       }
-      if (in_direct(m, L, T) && gemm_wd_ok(EPI_GATE, g)) {
+      if (const int wt = in_direct(m, L, T); wt && gemm_wd_ok(EPI_GATE, g)) {
         g.W = L.w_in_frag;
-        S1_TRY(launch_gemm_wd(EPI_GATE, g, 2, s), "linear-attention in-projection");
+        S1_TRY(launch_gemm_wd(EPI_GATE, g, wt, s), "linear-attention in-projection");
       } else {
         S1_TRY(launch_gemm(m->bf16, EPI_GATE, g, 1, nullptr, s, gemm_cfg(m, p)), "linear-attention in-projection");
       }
@@ -1104,9 +1127,9 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       g.head_dim = hd;
       g.pos = p->pos + r0;
       g.rope = m->rope;
-      if (in_direct(m, L, T) && gemm_wd_ok(EPI_QKV, g)) {
+      if (const int wt = in_direct(m, L, T); wt && gemm_wd_ok(EPI_QKV, g)) {
         g.W = L.w_in_frag;
-        S1_TRY(launch_gemm_wd(EPI_QKV, g, 2, s), "attention QKV projection");
+        S1_TRY(launch_gemm_wd(EPI_QKV, g, wt, s), "attention QKV projection");
       } else {
         S1_TRY(launch_gemm(m->bf16, EPI_QKV, g, 1, nullptr, s, gemm_cfg(m, p)), "attention QKV projection");
       }
@@ -1180,9 +1203,9 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
       gd.norm_eps = c.rms_eps;
       if (m->fold) defer_norm(gd);
     }
-    if (residual_direct(m, L.w_down_frag, T, max_split(m, p, T))) {
+    if (const int wt = residual_direct(m, L.w_down_frag, T, max_split(m, p, T))) {
       gd.W = L.w_down_frag;
-      S1_TRY(launch_gemm_wd(EPI_RESID, gd, 2, s), "FFN down");
+      S1_TRY(launch_gemm_wd(EPI_RESID, gd, wt, s), "FFN down");
       xn_ready = xn_scaled = gd.rs_out != nullptr;   // without a K split: the rows and their scales
     } else {
       int nd = NORM_NONE;

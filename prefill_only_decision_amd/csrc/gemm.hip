@@ -887,17 +887,21 @@ __device__ __forceinline__ void dma4(int32x4 rsrc, uint32_t lds, int voff, int s
 }
 #pragma clang diagnostic pop
 
-// The row scales of rows m0 .. m0 + BM - 1 (BM a multiple of 64) into LDS by
-// LDS-DMA at kernel entry, ahead of the operand loads: no register is held
-// through the main loop for them.  Waves 0 .. BM / 64 - 1 load 64 rows each;
-// rows past M read zero.  row_scale_sync, after the main loop, waits for the
-// wave's own DMA and meets the other waves.
-template <int BM>
+// The row scales of rows m0 .. m0 + BM - 1 into LDS by LDS-DMA at kernel
+// entry, ahead of the operand loads: no register is held through the main
+// loop for them.  Blocks of 64 rows go to waves in turn (the LDS array holds
+// BM rounded up to 64: rows past the tile are loaded and not used); rows past
+// M read zero.  row_scale_sync, after the main loop, waits for the wave's own
+// DMA and meets the other waves.
+constexpr int rsl_rows(int bm) { return (bm + 63) / 64 * 64; }
+template <int BM, int NW = 4>
 __device__ __forceinline__ void row_scale_dma(const GemmArgs& g, int m0, const float* rsl, int wave, int lane) {
-  static_assert(BM % 64 == 0, "whole waves of rows");
-  if (g.row_scale == nullptr || wave * 64 >= BM) return;
+  if (g.row_scale == nullptr) return;
   const int32x4 r = buffer_rsrc(g.row_scale + m0, (g.M - m0) * 4);
-  dma4(r, lds_addr(reinterpret_cast<const char*>(rsl)) + wave * 256, (wave * 64 + lane) * 4, 0);
+#pragma unroll
+  for (int b = 0; b < rsl_rows(BM) / 64; b += NW)
+    if (b + wave < rsl_rows(BM) / 64)
+      dma4(r, lds_addr(reinterpret_cast<const char*>(rsl)) + (b + wave) * 256, ((b + wave) * 64 + lane) * 4, 0);
 }
 __device__ __forceinline__ const float* row_scale_sync(const float* rsl) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -972,7 +976,7 @@ __attribute__((amdgpu_waves_per_eu(S::OCC, S::OCC)))
 gemm_lds_kernel(GemmArgs g) {
   static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? rsl_rows(S::BM) : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -981,7 +985,7 @@ gemm_lds_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
+  if constexpr (RS) row_scale_dma<S::BM, S::NWAVE>(g, m0, rsl, wave, lane);
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = ke > kb ? (ke - kb) / S::BK : 0;
@@ -1136,7 +1140,7 @@ __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1
 gemm_wide_kernel(GemmArgs g) {
   static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? rsl_rows(S::BM) : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1145,7 +1149,7 @@ gemm_wide_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
+  if constexpr (RS) row_scale_dma<S::BM, S::NWAVE>(g, m0, rsl, wave, lane);
   const int kb = blockIdx.y * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
   const int nk = (ke - kb) / S::BK;   // >= 1: the host gives every split a K tile
@@ -1340,9 +1344,8 @@ __device__ __forceinline__ void epilogue_swiglu16_lds(const GemmArgs& g, floatx1
 template <typename S, int EPI, bool RS = false>
 __global__ void __launch_bounds__(S::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_wd_kernel(GemmArgs g) {
-  static_assert(S::BM <= S::NT, "one row scale per thread");
   __shared__ __attribute__((aligned(1024))) char smem[S::NS * S::STAGE];
-  __shared__ __attribute__((aligned(16))) float rsl[RS ? S::BM : 1];
+  __shared__ __attribute__((aligned(16))) float rsl[RS ? rsl_rows(S::BM) : 1];
   const GemmArgs e = pin_epilogue_args<EPI>(g);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1350,7 +1353,7 @@ gemm_wd_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords<8>(xcd_remap(blockIdx.x, gridDim.x), nbm, nbn, tm, tn);
   const int m0 = tm * S::BM, n0 = tn * S::BN;
-  if constexpr (RS) row_scale_dma<S::BM>(g, m0, rsl, wave, lane);
+  if constexpr (RS) row_scale_dma<S::BM, S::NWAVE>(g, m0, rsl, wave, lane);
   const int nk = g.K / S::BK;   // >= 1: the host requires K to be a positive multiple of 64
 
   const char* abase = reinterpret_cast<const char*>(g.A) + (long long)m0 * g.lda * 2;
@@ -1517,6 +1520,7 @@ hipError_t run_wd(const GemmArgs& a, hipStream_t s) {
 using CfgWD1 = WD<4, 3, 4, 3>;   // 128 x 384, a wave 128 x 96, four activation stages, three weight tiles ahead
 using CfgWD2 = WD<8, 2, 4, 3>;   // 256 x 256, a wave 256 x 64
 using CfgWD3 = WD<6, 2, 4, 3>;   // 192 x 256, a wave 192 x 64
+using CfgWD4 = WD<7, 2, 4, 3>;   // 224 x 256, a wave 224 x 64 (288 rows spill registers)
 
 // Sum of split-K partial slabs in a fixed order, then the epilogue.
 template <bool RESID>
@@ -1966,25 +1970,39 @@ hipError_t run_wd_epi(Epi epi, const GemmArgs& a, hipStream_t s) {
   }
 }
 
+namespace {
+int wd_dims(int tile, int& bn) {
+  switch (tile) {
+    case 2: bn = CfgWD2::BN; return CfgWD2::BM;
+    case 3: bn = CfgWD3::BN; return CfgWD3::BM;
+    case 4: bn = CfgWD4::BN; return CfgWD4::BM;
+    default: bn = CfgWD1::BN; return CfgWD1::BM;
+  }
+}
+}  // namespace
+
 int gemm_wd_tiles(int tile, int M, int N) {
-  const int bm = tile == 2 ? CfgWD2::BM : tile == 3 ? CfgWD3::BM : CfgWD1::BM;
-  const int bn = tile == 2 ? CfgWD2::BN : tile == 3 ? CfgWD3::BN : CfgWD1::BN;
+  int bn = 0;
+  const int bm = wd_dims(tile, bn);
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 int gemm_wd_panel(int tile) {
-  return tile == 2 ? CfgWD2::BM + CfgWD2::BN : tile == 3 ? CfgWD3::BM + CfgWD3::BN : CfgWD1::BM + CfgWD1::BN;
+  int bn = 0;
+  const int bm = wd_dims(tile, bn);
+  return bm + bn;
 }
 
 hipError_t launch_gemm_wd(Epi epi, const GemmArgs& a, int tile, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || !resid_rows_ok(epi, a) || tile < 1 || tile > 3)
+  if (!gemm_wd_ok(epi, a) || !deferred_norm_ok(true, epi, a) || !resid_rows_ok(epi, a) || tile < 1 || tile > 4)
     return hipErrorInvalidValue;
   if (tile == 3) {   // built for the SwiGLU and fp32 epilogues
     if (epi == EPI_SWIGLU) return run_wd<CfgWD3, EPI_SWIGLU>(a, s);
     if (epi == EPI_F32) return run_wd<CfgWD3, EPI_F32>(a, s);
     return hipErrorInvalidValue;
   }
+  if (tile == 4) return run_wd_epi<CfgWD4>(epi, a, s);
   return tile == 2 ? run_wd_epi<CfgWD2>(epi, a, s) : run_wd_epi<CfgWD1>(epi, a, s);
 }
 

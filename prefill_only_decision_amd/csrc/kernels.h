@@ -94,8 +94,9 @@ size_t frag_bytes(int N, int K);
 hipError_t launch_frag_pack(const void* W, int N, int K, int ld, bool gu16, void* out, hipStream_t s);
 // tile 1: 128 x 384 workgroup tiles (a wave 128 x 96); tile 2: 256 x 256 (a
 // wave 256 x 64); tile 3: 192 x 256 (a wave 192 x 64; EPI_SWIGLU and EPI_F32
-// only).  gemm_wd_tiles gives the workgroup count, gemm_wd_panel the
-// operand rows a workgroup streams per K step (BM + BN).
+// only); tile 4: 224 x 256 (a wave 224 x 64).  gemm_wd_tiles gives the
+// workgroup count, gemm_wd_panel the operand rows a workgroup streams per K
+// step (BM + BN).
 bool gemm_wd_ok(Epi epi, const GemmArgs& a);
 int gemm_wd_tiles(int tile, int M, int N);
 int gemm_wd_panel(int tile);

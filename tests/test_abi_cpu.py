@@ -65,7 +65,7 @@ def test_frag_bytes_and_packed_gemm_validation(lib):
         assert s1.binding.frag_bytes(n, k) == 0
     # shapes the weight-direct GEMM does not take are rejected on the host
     bad = [dict(M=4, N=64, K=32), dict(M=4, N=64, K=100), dict(M=4, N=96, K=64, swiglu=True),
-           dict(M=4, N=64, K=64, tile=0), dict(M=4, N=64, K=64, tile=4), dict(M=-1, N=64, K=64)]
+           dict(M=4, N=64, K=64, tile=0), dict(M=4, N=64, K=64, tile=5), dict(M=-1, N=64, K=64)]
     for kw in bad:
         with pytest.raises(s1.binding.S1Error) as e:
             s1.binding.gemm_wfrag(16, 16, 16, **kw)
