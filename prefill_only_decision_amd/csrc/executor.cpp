@@ -272,6 +272,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
       if ((rc = pack_direct(m, L.w_in, L.n_in, d, &L.w_in_frag, s))) return rc;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
       if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
+      if ((rc = pack_direct(m, L.w_o, d, L.k_o, &L.w_o_frag, s))) return rc;
     } else {
       const std::string q = p + ".fa";
       L.n_in = (Hq + 2 * Hkv) * hd;
@@ -289,6 +290,7 @@ int load_layers(Model* m, Loader& ld, hipStream_t s) {
       if ((rc = pack_direct(m, L.w_in, L.n_in, d, &L.w_in_frag, s))) return rc;
       L.w_o = m->alloc((size_t)d * L.k_o * m->esz);
       if ((rc = ld.projection(q + ".o", d, L.k_o, tg & S1_LORA_O, L.w_o, {}))) return rc;
+      if ((rc = pack_direct(m, L.w_o, d, L.k_o, &L.w_o_frag, s))) return rc;
     }
     const std::string f = p + ".ffn";
     L.n_gu = 2 * m->ffn_pad;
@@ -1159,8 +1161,16 @@ int run_pass(Model* m, Plan* p, const PassPlan& ps, bool xn_first, hipStream_t s
     go.norm_eps = c.rms_eps;
     if (m->fold) defer_norm(go);
     int normed = NORM_NONE;
-    S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &normed),
-           "mixer out-projection");
+    if (const int wt = residual_direct(m, L.w_o_frag, T, max_split(m, p, T)); wt == 4) {
+      // only on the 224 x 256 tiles: at K = 2,048 the 256 x 256 weight-direct
+      // tiles gained nothing over the LDS-staged ones
+      go.W = L.w_o_frag;
+      S1_TRY(launch_gemm_wd(EPI_RESID, go, wt, s), "mixer out-projection");
+      normed = go.rs_out ? NORM_DEFERRED : NORM_NONE;
+    } else {
+      S1_TRY(launch_gemm(m->bf16, EPI_RESID, go, max_split(m, p, T), m->splitws, s, gemm_cfg(m, p), &normed),
+             "mixer out-projection");
+    }
     MARK(KC_GEMM_O);
     if (normed == NORM_NONE) {
       S1_TRY(norm_pass(L.ffn_norm), "rmsnorm");

@@ -36,6 +36,7 @@ struct LayerW {
   void* w_gu = nullptr;         // gate/up interleaved in blocks of 32 rows, [2 * ffn_pad, d]
   void* w_gu_frag = nullptr;    // bf16: w_gu in fragment order, gate/up interleaved in blocks of 16
   void* w_down_frag = nullptr;  // bf16: w_down in fragment order (the down GEMM at many rows)
+  void* w_o_frag = nullptr;     // bf16: w_o in fragment order (the out-projection at many rows)
   void* w_in_frag = nullptr;    // bf16: w_in in fragment order (the in-projection at many rows)
   int n_gu = 0;
   void* w_down = nullptr;       // [d, ffn]
